@@ -1,0 +1,273 @@
+"""Plain, slow CPU oracle of self-indexing compressed-key decode attention.
+
+TEST INFRASTRUCTURE: only the tests, the smoke check and the benchmark's
+CPU-baseline leg use this module.  It shares no code with the HIP path.
+
+Source of the method: the web summary of "Self-Indexing KVCache: Predicting
+Sparse Attention from Compressed Keys" (arXiv 2603.14224), technical summary.
+Citations below name its sections: §1 (problem), §2 (methodology),
+§2.1 items 1-4 (core components), §3 (contributions).  The summary prints no
+equations, so every formula here is the plainest reading of that prose; the
+readings are marked READING and listed in the design notes.
+
+Precision: every score, logit, softmax and weighted sum is fp64.  Two
+reductions are fp32 on purpose, because their exact bits decide the sign
+codes and are required to match bit for bit: the per-channel mean and the
+per-token scale, each summed by an adjacent-pair binary tree (READING: the
+summary fixes no summation order; this one is written down here and the GPU
+reproduces it).  bf16 inputs are uint16 bit patterns, decoded exactly.
+
+Pins (tests/test_oracle_pins.py checks each function against something other
+than itself): tree order (hand-computed leaves), mean (fp64 mean within the
+tree error bound), codes (hand-derived layout fixture, brute-force bits,
+entropy balance), scale (least-squares optimality, round trip), lookup table
+(all 16 sign vertices enumerated, exact identity with the dequantised dot
+product), top-k (brute-force sort, heapq), attention (dense softmax attention
+through torch's fp64 SDPA when every token is kept, q = 0, one dominant
+token), decode step (planted-token recall).  No function is left unpinned.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+HEAD_DIM = 128          # D: the only head size of the evaluated models (Llama-3.1-8B, Qwen2.5-14B)
+N_SINK = 64             # §2.1 item 3: 64 full-precision sink tokens kept at prefill
+SUB_DIM = 4             # §2.1 item 1: keys are split into 4-dimensional sub-vectors
+N_SUB = HEAD_DIM // SUB_DIM
+N_PATTERNS = 16         # §2.1 item 1: a sub-vector's sign pattern picks one of 16 clusters
+CODE_BYTES = HEAD_DIM // 8
+
+
+# --------------------------------------------------------------------------- #
+# bf16 and fixed-order fp32 helpers
+# --------------------------------------------------------------------------- #
+def bf16_to_f32(bits) -> np.ndarray:
+    """Exact decode of bf16 bit patterns (uint16) to float32."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def tree_sum_f32(x, axis: int = -1) -> np.ndarray:
+    """Adjacent-pair binary-tree sum in float32 along ``axis``.
+
+    The leaves are padded with +0.0 up to the next power of two P; then, level
+    by level, element i of the next level is fl32(x[2i] + x[2i+1]).  Padding to
+    any larger power of two gives the same value (the extra subtrees are +0.0
+    and are added last).
+    """
+    x = np.moveaxis(np.asarray(x, dtype=np.float32), axis, -1)
+    n = x.shape[-1]
+    p = 1
+    while p < n:
+        p *= 2
+    if p != n:
+        pad = np.zeros(x.shape[:-1] + (p - n,), np.float32)
+        x = np.concatenate([x, pad], axis=-1)
+    while x.shape[-1] > 1:
+        x = x[..., 0::2] + x[..., 1::2]
+    return x[..., 0]
+
+
+# --------------------------------------------------------------------------- #
+# Prefill compression: §2.1 items 1 and 3
+# --------------------------------------------------------------------------- #
+def channel_mean(k_bits, n_tokens: int) -> np.ndarray:
+    """Per-channel mean of the keys that get quantised (§2.1 item 1, entropy-aware
+    normalisation: subtract the channel mean so that + and - signs balance).
+
+    READING: the mean runs over the non-sink tokens t in [64, N) of the same
+    (batch, KV head); sink rows are stored in full precision (§2.1 item 3) and
+    do not enter it.  Sum: ``tree_sum_f32`` over the token axis with the sink
+    rows and the rows past N replaced by +0.0; then one correctly rounded fp32
+    division by fl32(N - 64).
+
+    k_bits: [..., >=N, 128] bf16 bits.  Returns float32 [..., 128].
+    """
+    if n_tokens <= N_SINK:
+        raise ValueError("need more than 64 tokens")
+    x = bf16_to_f32(np.asarray(k_bits)[..., :n_tokens, :]).copy()
+    x[..., :N_SINK, :] = np.float32(0.0)
+    s = tree_sum_f32(x, axis=-2)
+    return (s / np.float32(n_tokens - N_SINK)).astype(np.float32)
+
+
+def sign_bits(k_bits, mu) -> np.ndarray:
+    """Sign of each normalised channel as a bit: 1 iff fp32(k_c) < mu_c (§2.1 item 1,
+    sign-based 1-bit VQ).  A tie (k_c == mu_c, also -0 vs +0) gives bit 0, i.e. sign +1.
+    Returns bool [..., T, 128]."""
+    x = bf16_to_f32(k_bits)
+    return x < np.asarray(mu, np.float32)[..., None, :]
+
+
+def pack_codes(bits) -> np.ndarray:
+    """READING (layout): bit c of a token's 16-byte code is channel c, least
+    significant bit first: byte c // 8, bit c % 8.  Hence the 4-bit pattern of
+    sub-vector j (channels 4j..4j+3) is nibble j, low nibble first, with bit i
+    of the pattern = channel 4j + i."""
+    return np.packbits(np.asarray(bits, bool), axis=-1, bitorder="little")
+
+
+def token_scale(k_bits, mu) -> np.ndarray:
+    """Per-token scale alpha_t = mean_c |fp32(k_c) - mu_c| (READING: the summary gives
+    no scale; 1 bit per dimension plus one per-token scale, with the mean absolute
+    deviation, the least-squares optimum for a fixed sign vector).
+
+    Sum: ``tree_sum_f32`` over the 128 channels of |fl32(k_c - mu_c)|; then an
+    exact multiplication by 2^-7.  Returns float32 [..., T]."""
+    x = bf16_to_f32(k_bits)
+    a = np.abs(x - np.asarray(mu, np.float32)[..., None, :]).astype(np.float32)
+    return (tree_sum_f32(a, axis=-1) * np.float32(2.0 ** -7)).astype(np.float32)
+
+
+def encode(k_bits, n_tokens: int) -> dict:
+    """Prefill compression of one cache (§2.1 items 1 and 3).
+
+    k_bits: [B, H, >=N, 128] bf16 bits.  Returns mu [B,H,128] f32, codes
+    [B,H,N,16] u8 (written for every token, sinks included, for a uniform
+    layout), alpha [B,H,N] f32 and k_sink [B,H,64,128] (bf16 bits, the first 64
+    rows copied unchanged: READING, sinks are the initial positions)."""
+    k_bits = np.asarray(k_bits)
+    mu = channel_mean(k_bits, n_tokens)
+    rows = k_bits[..., :n_tokens, :]
+    return {
+        "mu": mu,
+        "codes": pack_codes(sign_bits(rows, mu)),
+        "alpha": token_scale(rows, mu),
+        "k_sink": np.array(k_bits[..., :N_SINK, :], dtype=np.uint16),
+    }
+
+
+def encode_rows(k_bits, mu) -> dict:
+    """Codes and scales of rows appended after prefill, with the channel mean
+    frozen (READING: the mean is computed once at prefill)."""
+    return {"codes": pack_codes(sign_bits(k_bits, mu)), "alpha": token_scale(k_bits, mu)}
+
+
+def dequantize(codes, alpha, mu) -> np.ndarray:
+    """Reconstructed key k^_c = fl32(mu_c + alpha * v_c), v_c = +1 for bit 0 and -1
+    for bit 1 (§2.1 item 1: the code doubles as the quantised key).  alpha*v is
+    exact, so this is one rounding.  Returns float32 [..., T, 128]."""
+    bits = np.unpackbits(np.asarray(codes, np.uint8), axis=-1, bitorder="little")
+    v = (1.0 - 2.0 * bits).astype(np.float32)
+    return (np.asarray(mu, np.float32)[..., None, :]
+            + np.asarray(alpha, np.float32)[..., :, None] * v).astype(np.float32)
+
+
+# --------------------------------------------------------------------------- #
+# Decode retrieval: §2.1 item 2 (compressed-domain top-k by LUT-GEMV)
+# --------------------------------------------------------------------------- #
+def centres() -> np.ndarray:
+    """The 16 centre vectors of a 4-dim sub-vector (READING: the sign vertices;
+    the per-token scale carries the magnitude).  Row p, element i: +1 if bit i
+    of p is 0 else -1.  Shape [16, 4], fp64."""
+    p = np.arange(N_PATTERNS)[:, None]
+    i = np.arange(SUB_DIM)[None, :]
+    return np.where((p >> i) & 1, -1.0, 1.0)
+
+
+def group_query(q_bits, n_kv_heads: int) -> np.ndarray:
+    """Selection query of each KV head: the sum of its query group (READING:
+    grouped-query attention with contiguous groups, heads h*G..h*G+G-1, selection
+    per KV head by the group's summed score).  q_bits [B,Hq,128] -> fp64 [B,Hkv,128]."""
+    q = bf16_to_f32(q_bits).astype(np.float64)
+    b, hq, d = q.shape
+    return q.reshape(b, n_kv_heads, hq // n_kv_heads, d).sum(axis=2)
+
+
+def query_lut(qbar) -> np.ndarray:
+    """§2.1 item 2: split the query like the key and dot each 4-dim piece with the
+    16 centres.  qbar [..., 128] -> LUT [..., 32, 16] fp64."""
+    qs = np.asarray(qbar, np.float64).reshape(qbar.shape[:-1] + (N_SUB, SUB_DIM))
+    return qs @ centres().T
+
+
+def code_nibbles(codes) -> np.ndarray:
+    """Cluster index of every sub-vector: nibble j of the code. [..., 16] -> [..., 32]."""
+    c = np.asarray(codes, np.uint8)
+    lo = c & 0x0F
+    hi = c >> 4
+    return np.stack([lo, hi], axis=-1).reshape(c.shape[:-1] + (N_SUB,))
+
+
+def lut_scores(lut, codes, alpha) -> np.ndarray:
+    """§2.1 item 2: score a token by looking up each sub-vector's cluster in the
+    query's table and accumulating, all in the quantised domain:
+    s_t = alpha_t * sum_j LUT[j, nibble_j(code_t)].  fp64.
+
+    This is q.(k^ - mu) for the dequantised key; the term q.mu is the same for
+    every token and does not change the ranking, so it is left out.
+    lut [32,16]; codes [T,16]; alpha [T] -> [T]."""
+    nib = code_nibbles(codes).astype(np.intp)
+    acc = np.asarray(lut)[np.arange(N_SUB)[None, :], nib].sum(axis=-1)
+    return np.asarray(alpha, np.float64) * acc
+
+
+def select_topk(scores, k: int, first_token: int = N_SINK) -> np.ndarray:
+    """Top-k tokens by score (§2.1 item 2).  scores[i] belongs to token
+    first_token + i.  Order: larger score first, ties to the smaller position
+    (READING); the result is returned in ascending token order."""
+    s = np.asarray(scores, np.float64)
+    if not 1 <= k <= s.size:
+        raise ValueError("need 1 <= k <= number of candidates")
+    t = np.arange(s.size)
+    order = np.lexsort((t, -s))
+    return np.sort(order[:k]).astype(np.int64) + first_token
+
+
+# --------------------------------------------------------------------------- #
+# Sparse attention over top-k plus sinks: §2.1 items 3 and 4
+# --------------------------------------------------------------------------- #
+def sparse_attention(q_bits_group, idx, k_sink_bits, codes, alpha, mu, v_bits,
+                     sm_scale: float) -> np.ndarray:
+    """Attention of the G query heads of one KV head over S = {0..63} U idx
+    (§2.1 item 3: sinks always kept in full precision; item 4: keys dequantised
+    inside the attention).  Keys: bf16 sink rows for t < 64, else k^_t (fp32,
+    ``dequantize``).  Values: the bf16 V rows, unmodified (READING).  Logits
+    (q_g . kappa_t) * sm_scale; softmax over S; output sum_t p_t V_t.  No mask:
+    a decoding query sees every cached token.  fp64, returned as float32 [G,128].
+
+    q_bits_group [G,128]; idx [k] (token positions >= 64); k_sink_bits [64,128];
+    codes [N,16], alpha [N], mu [128], v_bits [N,128] of that KV head."""
+    idx = np.asarray(idx, np.int64)
+    q = bf16_to_f32(q_bits_group).astype(np.float64)
+    kap = np.concatenate([bf16_to_f32(k_sink_bits).astype(np.float64),
+                          dequantize(np.asarray(codes)[idx], np.asarray(alpha)[idx],
+                                     mu).astype(np.float64)], axis=0)
+    rows = np.concatenate([np.arange(N_SINK, dtype=np.int64), idx])
+    vals = bf16_to_f32(np.asarray(v_bits)[rows]).astype(np.float64)
+    logits = (kap @ q.T) * float(sm_scale)                      # [|S|, G]
+    logits -= logits.max(axis=0, keepdims=True)
+    p = np.exp(logits)
+    p /= p.sum(axis=0, keepdims=True)
+    return (p.T @ vals).astype(np.float32)
+
+
+def head_scores(q_bits, codes, alpha, b: int, h: int, n_kv_heads: int,
+                n_tokens: int) -> np.ndarray:
+    """Selection scores of the candidates t in [64, N) of one (batch, KV head)."""
+    qbar = group_query(q_bits[b:b + 1], n_kv_heads)[0, h]
+    return lut_scores(query_lut(qbar), codes[N_SINK:n_tokens], alpha[N_SINK:n_tokens])
+
+
+def decode_step(q_bits, cache: dict, v_bits, top_k: int, sm_scale: float,
+                n_tokens: int, heads=None) -> dict:
+    """One decode step: LUT scores -> top-k -> sparse attention, per (b, KV head).
+
+    cache: ``encode`` output (codes/alpha indexed by token).  v_bits [B,H,>=N,128].
+    heads: optional list of (b, h) pairs to compute (others left zero / -1).
+    Returns idx [B,H,k] int64 and out [B,Hq,128] float32."""
+    q_bits = np.asarray(q_bits)
+    b_n, hq, _ = q_bits.shape
+    n_kv = cache["mu"].shape[1]
+    g = hq // n_kv
+    idx = np.full((b_n, n_kv, top_k), -1, np.int64)
+    out = np.zeros((b_n, hq, HEAD_DIM), np.float32)
+    pairs = heads if heads is not None else [(b, h) for b in range(b_n) for h in range(n_kv)]
+    for b, h in pairs:
+        s = head_scores(q_bits, cache["codes"][b, h], cache["alpha"][b, h], b, h, n_kv, n_tokens)
+        sel = select_topk(s, top_k)
+        idx[b, h] = sel
+        out[b, h * g:(h + 1) * g] = sparse_attention(
+            q_bits[b, h * g:(h + 1) * g], sel, cache["k_sink"][b, h], cache["codes"][b, h],
+            cache["alpha"][b, h], cache["mu"][b, h], v_bits[b, h], sm_scale)
+    return {"idx": idx, "out": out}

@@ -1,0 +1,322 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Page: "Self-Indexing KVCache: Predicting Sparse Attention from Compressed Keys"
+(web summary, technical part), sections cited as §2.1 item n.  Hand-derived
+values live in tests/golden/hand_cases.json.  Each test is built so that a
+plausible slip in the oracle (dropped term, wrong sign or index, transposed
+operand, wrong bit order, wrong reduction order) makes it fail.
+"""
+
+import heapq
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import sikv_synth as S
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")))
+
+
+def _bf16(x):
+    return S.f32_to_bf16_bits(np.asarray(x, np.float32))
+
+
+def _rand_keys(rng, n, mu_scale=2.0, h=1):
+    mu = rng.normal(0, mu_scale, (h, 1, 128)).astype(np.float32)
+    return _bf16(mu + rng.standard_normal((h, n, 128)).astype(np.float32))
+
+
+# ----------------------------------------------------------------- tree / mean
+def test_tree_order_golden():
+    g = GOLD["tree_order"]
+    got = O.tree_sum_f32(np.array(g["leaves"], np.float32))
+    assert float(got) == g["expected"]
+    seq = np.float32(0)
+    for v in g["leaves"]:
+        seq = np.float32(seq + np.float32(v))
+    assert float(seq) == g["sequential_would_give"] != g["expected"]
+
+
+def test_tree_padding_is_neutral():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal(37).astype(np.float32)
+    a = O.tree_sum_f32(x)
+    b = O.tree_sum_f32(np.concatenate([x, np.zeros(64 - 37, np.float32)]))
+    c = O.tree_sum_f32(np.concatenate([x, np.zeros(256 - 37, np.float32)]))
+    assert a == b == c
+    # integers: exact, so the tree must give the true sum
+    xi = rng.integers(-1000, 1000, 1000).astype(np.float32)
+    assert float(O.tree_sum_f32(xi)) == float(xi.astype(np.int64).sum())
+
+
+@pytest.mark.parametrize("n", [65, 100, 1000, 4096, 5003])
+def test_channel_mean_vs_fp64(n):
+    rng = np.random.default_rng(n)
+    k = _rand_keys(rng, n)
+    mu = O.channel_mean(k, n)[0]
+    x = S.bf16_bits_to_f32(k[0, 64:n]).astype(np.float64)
+    ref = x.mean(axis=0)
+    levels = math.ceil(math.log2(n)) + 1
+    bound = levels * 2.0 ** -24 * np.abs(x).sum(axis=0) / (n - 64) + 2.0 ** -24 * np.abs(ref)
+    assert np.all(np.abs(mu - ref) <= bound)
+
+
+def test_channel_mean_ignores_sinks_and_tail():
+    rng = np.random.default_rng(2)
+    k = _rand_keys(rng, 600)
+    mu = O.channel_mean(k, 500)
+    k2 = k.copy()
+    k2[:, :64] = _bf16(np.full((1, 64, 128), 1e4))
+    k2[:, 500:] = _bf16(np.full((1, 100, 128), -1e4))
+    assert np.array_equal(mu, O.channel_mean(k2, 500))
+
+
+# ----------------------------------------------------------------- codes / scale
+def _layout_row():
+    g = GOLD["code_layout"]
+    row = np.full(128, g["other_value"], np.float32)
+    row[g["negative_channels"]] = g["negative_value"]
+    bits = _bf16(row)
+    bits[g["zero_channels_pos"]] = 0x0000
+    bits[g["zero_channels_neg"]] = 0x8000
+    return bits[None, :], np.full(128, g["mu"], np.float32)
+
+
+def test_code_layout_golden():
+    g = GOLD["code_layout"]
+    k, mu = _layout_row()
+    code = O.pack_codes(O.sign_bits(k, mu))[0]
+    assert code.tobytes().hex() == g["expected_code_hex"]
+    nib = O.code_nibbles(code)
+    for j, v in g["expected_nibbles"].items():
+        assert nib[int(j)] == v
+    assert float(O.token_scale(k, mu)[0]) == g["expected_alpha"]
+
+
+def test_codes_bruteforce_bits():
+    rng = np.random.default_rng(3)
+    k = _rand_keys(rng, 70)[0]
+    mu = O.channel_mean(k[None], 70)[0]
+    codes = O.pack_codes(O.sign_bits(k, mu))
+    x = S.bf16_bits_to_f32(k)
+    for t in range(0, 70, 7):
+        for c in range(128):
+            byte = int(codes[t, c // 8])
+            assert ((byte >> (c % 8)) & 1) == (1 if float(x[t, c]) < float(mu[c]) else 0)
+        for j in range(32):
+            pat = sum((1 << i) for i in range(4) if float(x[t, 4 * j + i]) < float(mu[4 * j + i]))
+            assert O.code_nibbles(codes[t])[j] == pat
+
+
+def test_entropy_balance():
+    """§2.1 item 1: subtracting the channel mean balances the signs.  With mean
+    offsets N(0,2) the raw sign rate of channel c is Phi(-m_c); after centring it
+    is close to 1/2 for every channel."""
+    rng = np.random.default_rng(4)
+    n = 20000
+    m = rng.normal(0, math.sqrt(2), 128).astype(np.float32)
+    k = _bf16(m[None, :] + rng.standard_normal((n, 128)).astype(np.float32))
+    mu = O.channel_mean(k[None], n)[0]
+    rate = O.sign_bits(k[64:], mu).mean(axis=0)
+    assert np.all(np.abs(rate - 0.5) < 0.02)
+    raw = O.sign_bits(k[64:], np.zeros(128, np.float32)).mean(axis=0)
+    phi = 0.5 * (1 + np.vectorize(math.erf)(-m / math.sqrt(2)))
+    assert np.all(np.abs(raw - phi) < 0.02)
+    assert np.abs(raw - 0.5).max() > 0.3
+
+
+def test_scale_is_least_squares_optimum():
+    rng = np.random.default_rng(5)
+    k = _rand_keys(rng, 300)[0]
+    mu = O.channel_mean(k[None], 300)[0]
+    alpha = O.token_scale(k, mu).astype(np.float64)
+    kt = S.bf16_bits_to_f32(k).astype(np.float64) - mu.astype(np.float64)
+    sgn = np.where(O.sign_bits(k, mu), -1.0, 1.0)
+    for eps in (1e-3, -1e-3):
+        e0 = ((kt - alpha[:, None] * sgn) ** 2).sum(axis=1)
+        e1 = ((kt - (alpha * (1 + eps))[:, None] * sgn) ** 2).sum(axis=1)
+        assert np.all(e1 > e0)
+    fs = np.array([math.fsum(np.abs(np.float32(S.bf16_bits_to_f32(k[t])) - mu).astype(np.float64))
+                   for t in range(300)]) / 128
+    assert np.allclose(alpha, fs, rtol=1e-6, atol=0)
+
+
+def test_round_trip():
+    """§2.1 item 1 (dual use): re-encoding the reconstructed keys against the same
+    mean gives the same codes, and the scale back to within rounding."""
+    rng = np.random.default_rng(6)
+    k = _rand_keys(rng, 400)[0]
+    mu = O.channel_mean(k[None], 400)[0]
+    codes = O.pack_codes(O.sign_bits(k, mu))
+    alpha = O.token_scale(k, mu)
+    khat = O.dequantize(codes, alpha, mu)
+    bits2 = khat < mu[None, :]
+    assert np.array_equal(O.pack_codes(bits2), codes)
+    alpha2 = np.abs(khat - mu[None, :]).astype(np.float64).mean(axis=1)
+    assert np.allclose(alpha2, alpha, rtol=1e-5, atol=0)
+
+
+def test_dequantize_values():
+    k, mu = _layout_row()
+    codes = O.pack_codes(O.sign_bits(k, mu))
+    khat = O.dequantize(codes, np.array([0.5], np.float32), mu + np.float32(2.0))
+    g = GOLD["code_layout"]
+    expect = np.full(128, 2.5, np.float32)
+    expect[g["negative_channels"]] = 1.5
+    assert np.array_equal(khat[0], expect)
+
+
+def test_encode_layout_and_sinks():
+    rng = np.random.default_rng(7)
+    k = _rand_keys(rng, 300, h=2)[None]           # [1,2,300,128]
+    enc = O.encode(k, 260)
+    assert enc["codes"].shape == (1, 2, 260, 16) and enc["alpha"].shape == (1, 2, 260)
+    assert np.array_equal(enc["k_sink"], k[:, :, :64])
+    app = O.encode_rows(k[:, :, 260:], enc["mu"])
+    full = O.encode_rows(k[:, :, :300], enc["mu"])
+    assert np.array_equal(app["codes"], full["codes"][:, :, 260:])
+    assert np.array_equal(full["codes"][:, :, :260], enc["codes"])
+
+
+# ----------------------------------------------------------------- LUT / scores
+def test_lut_golden_subvector():
+    g = GOLD["lut_subvector"]
+    q = np.zeros(128)
+    q[:4] = g["q_piece"]
+    lut = O.query_lut(q)
+    for p, v in g["expected"].items():
+        assert lut[0, int(p)] == v
+    assert np.all(lut[1:] == 0)
+
+
+def test_lut_enumerates_all_sign_vertices():
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal(128)
+    lut = O.query_lut(q)
+    for j in range(32):
+        for signs in itertools.product((1.0, -1.0), repeat=4):
+            p = sum((1 << i) for i, s in enumerate(signs) if s < 0)
+            assert lut[j, p] == pytest.approx(float(np.dot(q[4 * j:4 * j + 4], signs)), abs=1e-12)
+
+
+def test_lut_score_identity():
+    """LUT score plus q.mu equals the plain dot product of the group's queries with
+    the reconstructed key (computed without any table) to fp64 rounding."""
+    rng = np.random.default_rng(9)
+    B, Hq, Hkv, N = 2, 6, 2, 500
+    q = _bf16(rng.standard_normal((B, Hq, 128)))
+    k = _bf16(rng.normal(0, 1.5, (B, Hkv, 1, 128)) + rng.standard_normal((B, Hkv, N, 128)))
+    enc = O.encode(k, N)
+    G = Hq // Hkv
+    qf = S.bf16_bits_to_f32(q).astype(np.float64)
+    for b in range(B):
+        for h in range(Hkv):
+            s = O.head_scores(q, enc["codes"][b, h], enc["alpha"][b, h], b, h, Hkv, N)
+            bits = np.unpackbits(enc["codes"][b, h, 64:N], axis=-1, bitorder="little")
+            khat = (enc["mu"][b, h].astype(np.float64)[None, :]
+                    + enc["alpha"][b, h, 64:N].astype(np.float64)[:, None] * (1.0 - 2.0 * bits))
+            direct = sum(khat @ qf[b, h * G + g] for g in range(G))
+            qmu = sum(float(qf[b, h * G + g] @ enc["mu"][b, h].astype(np.float64)) for g in range(G))
+            assert np.allclose(s + qmu, direct, rtol=1e-12, atol=1e-10)
+
+
+def test_group_query_is_contiguous():
+    q = np.zeros((1, 8, 128), np.uint16)
+    q[0, 5] = _bf16(np.ones(128))
+    qb = O.group_query(q, 2)             # G = 4: heads 4..7 -> KV head 1
+    assert np.all(qb[0, 0] == 0) and np.all(qb[0, 1] == 1)
+
+
+# ----------------------------------------------------------------- top-k
+def test_topk_golden_ties():
+    g = GOLD["topk_ties"]
+    got = O.select_topk(np.array(g["scores"]), g["k"], g["first_token"])
+    assert got.tolist() == g["expected_idx"]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_bruteforce(seed):
+    rng = np.random.default_rng(seed)
+    m = int(rng.integers(1, 13))
+    s = np.round(rng.standard_normal(m), 1)            # rounding forces ties
+    for k in range(1, m + 1):
+        brute = sorted(range(m), key=lambda i: (-s[i], i))[:k]
+        assert O.select_topk(s, k).tolist() == sorted(i + 64 for i in brute)
+
+
+def test_topk_heapq():
+    rng = np.random.default_rng(11)
+    s = rng.standard_normal(5000)
+    got = O.select_topk(s, 300)
+    ref = sorted(i + 64 for i in heapq.nlargest(300, range(5000), key=lambda i: s[i]))
+    assert got.tolist() == ref
+
+
+# ----------------------------------------------------------------- attention
+def _small_cache(seed, B=1, Hq=4, Hkv=2, N=300):
+    rng = np.random.default_rng(seed)
+    q = _bf16(rng.standard_normal((B, Hq, 128)))
+    k = _bf16(rng.normal(0, 1.5, (B, Hkv, 1, 128)) + rng.standard_normal((B, Hkv, N, 128)))
+    v = _bf16(rng.standard_normal((B, Hkv, N, 128)))
+    return q, k, v, O.encode(k, N)
+
+
+def test_attention_all_tokens_equals_dense_sdpa():
+    """With k = N - 64 the sparse path is dense softmax attention over
+    [K_sink; K^] (checked through torch's fp64 scaled_dot_product_attention)."""
+    q, k, v, enc = _small_cache(12)
+    N, G, sm = 300, 2, 1 / math.sqrt(128)
+    res = O.decode_step(q, enc, v, N - 64, sm, N)
+    for h in range(2):
+        kap = np.concatenate([S.bf16_bits_to_f32(enc["k_sink"][0, h]),
+                              O.dequantize(enc["codes"][0, h, 64:], enc["alpha"][0, h, 64:],
+                                           enc["mu"][0, h])]).astype(np.float64)
+        qq = torch.tensor(S.bf16_bits_to_f32(q[0, h * G:(h + 1) * G]), dtype=torch.float64)
+        kk = torch.tensor(kap)[None].expand(G, -1, -1)
+        vv = torch.tensor(S.bf16_bits_to_f32(v[0, h]).astype(np.float64))[None].expand(G, -1, -1)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qq[:, None, :], kk, vv, scale=sm)[:, 0].numpy()
+        assert np.allclose(res["out"][0, h * G:(h + 1) * G], ref, rtol=1e-6, atol=1e-7)
+        assert res["idx"][0, h].tolist() == list(range(64, N))
+
+
+def test_attention_zero_query_is_mean_of_attended_values():
+    q, k, v, enc = _small_cache(13)
+    q[:] = 0
+    res = O.decode_step(q, enc, v, 50, 0.088, 300)
+    for h in range(2):
+        rows = np.concatenate([np.arange(64), res["idx"][0, h]])
+        ref = S.bf16_bits_to_f32(v[0, h, rows]).astype(np.float64).mean(axis=0)
+        assert np.allclose(res["out"][0, 2 * h], ref, rtol=1e-6, atol=1e-7)
+
+
+def test_attention_one_dominant_token():
+    q, k, v, enc = _small_cache(14, Hq=1, Hkv=1)
+    qf = S.bf16_bits_to_f32(q[0, 0]).astype(np.float64)
+    # make candidate 200 equal to a large multiple of q: its reconstructed key
+    # points along q's signs with a huge scale
+    row = np.sign(qf) * -1e3
+    k2 = k.copy()
+    k2[0, 0, 200] = _bf16(row)
+    enc2 = O.encode(k2, 300)
+    # flip: the stored code of token 200 has all signs opposite to q -> tiny score;
+    # attend with -q so token 200 dominates
+    qn = _bf16(-S.bf16_bits_to_f32(q))
+    res = O.decode_step(qn, enc2, v, 5, 1.0, 300)
+    assert 200 in res["idx"][0, 0].tolist()
+    assert np.allclose(res["out"][0, 0], S.bf16_bits_to_f32(v[0, 0, 200]), rtol=0, atol=1e-6)
+
+
+def test_planted_recall_tiny():
+    """On the tiny workload every planted token scores into the top 256."""
+    w = S.WORKLOADS["tiny_4k"]
+    d = S.draw(w)
+    enc = O.encode(d["K"], w.n_tokens)
+    res = O.decode_step(d["q"], enc, d["V"], w.top_k, 1 / math.sqrt(128), w.n_tokens)
+    assert set(d["planted"][0, 0].tolist()) <= set(res["idx"][0, 0].tolist())
