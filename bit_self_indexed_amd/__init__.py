@@ -1,0 +1,268 @@
+"""Python binding of libsikv.so: self-indexing compressed-key decode attention on gfx950.
+
+Thin ctypes layer with the same names as the C ABI (include/sikv.h).  It only
+marshals arguments: torch supplies device memory and the current stream, and
+every step of the computation runs in the library's HIP kernels.  There is no
+CPU fallback: if the library is missing or fails to load, importing this
+package raises.
+
+Method: "Self-Indexing KVCache: Predicting Sparse Attention from Compressed
+Keys" (web summary, technical part, §2.1 items 1-4).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # first: the library then binds to the HIP runtime torch has loaded
+
+from . import _abi
+
+HEAD_DIM = 128
+N_SINK = 64
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsikv.so")
+
+OP_ENCODE, OP_SCORE_TOPK, OP_SPARSE_ATTN, OP_DECODE_STEP = 0, 1, 2, 3
+
+
+class SikvError(RuntimeError):
+    """A libsikv call returned a non-zero status."""
+
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {status_str(status)} (status {status})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m bit_self_indexed_amd.build` "
+            "(the HIP library is required, there is no fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    _abi.declare(lib)
+    if lib.sikv_abi_version() != _abi.ABI_VERSION:
+        raise ImportError("libsikv.so ABI version mismatch; rebuild it")
+    if lib.sikv_desc_size() != ctypes.sizeof(_abi.CacheDesc):
+        raise ImportError("libsikv.so cache descriptor layout mismatch; rebuild it")
+    return lib
+
+
+lib = _load()
+
+
+def status_str(status: int) -> str:
+    return lib.sikv_status_str(int(status)).decode()
+
+
+def _check(status: int, call: str) -> None:
+    if status != 0:
+        raise SikvError(status, call)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _bits(t: torch.Tensor) -> torch.Tensor:
+    """bf16 tensors are passed as their bit patterns; uint16/int16 pass through."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16)
+    if t.dtype in (torch.int16, torch.uint16):
+        return t
+    raise TypeError(f"expected bfloat16 (or its uint16 bits), got {t.dtype}")
+
+
+def _strides_rows(t: torch.Tensor, name: str):
+    """Strides (b, h, t) in elements of a [B, H, T, 128] tensor with unit channel stride."""
+    if t.dim() != 4 or t.shape[-1] != HEAD_DIM or t.stride(-1) != 1:
+        raise ValueError(f"{name} must be [B, H, T, 128] with contiguous channels")
+    return t.stride(0), t.stride(1), t.stride(2)
+
+
+class Workspace:
+    """Caller-owned device scratch, grown on demand (256-byte aligned)."""
+
+    def __init__(self, device):
+        self.device = torch.device(device)
+        self.buf = None
+
+    def get(self, nbytes: int):
+        if nbytes == 0:
+            return None, 0
+        if self.buf is None or self.buf.numel() < nbytes + 256:
+            self.buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
+        base = self.buf.data_ptr()
+        off = (-base) % 256
+        return ctypes.c_void_p(base + off), self.buf.numel() - off
+
+
+class Cache:
+    """The compressed key cache of one layer plus a reference to its value cache.
+
+    codes uint8 [B,Hkv,cap,16], alpha fp32 [B,Hkv,cap], mu fp32 [B,Hkv,128],
+    k_sink bf16 [B,Hkv,64,128] are owned here; ``v`` (bf16 [B,Hkv,>=cap,128],
+    unit channel stride) is only referenced.
+    """
+
+    def __init__(self, batch: int, n_kv_heads: int, capacity: int, device="cuda",
+                 v: torch.Tensor | None = None):
+        dev = torch.device(device)
+        self.batch, self.n_kv_heads, self.capacity = batch, n_kv_heads, capacity
+        self.n_tokens = 0
+        self.codes = torch.zeros((batch, n_kv_heads, capacity, 16), dtype=torch.uint8, device=dev)
+        self.alpha = torch.zeros((batch, n_kv_heads, capacity), dtype=torch.float32, device=dev)
+        self.mu = torch.zeros((batch, n_kv_heads, HEAD_DIM), dtype=torch.float32, device=dev)
+        self.k_sink = torch.zeros((batch, n_kv_heads, N_SINK, HEAD_DIM), dtype=torch.bfloat16,
+                                  device=dev)
+        self.v = v
+        self.ws = Workspace(dev)
+
+    @property
+    def device(self):
+        return self.codes.device
+
+    def desc(self) -> _abi.CacheDesc:
+        d = _abi.CacheDesc()
+        d.batch, d.n_kv_heads, d.head_dim = self.batch, self.n_kv_heads, HEAD_DIM
+        d.capacity, d.n_tokens, d.n_sink = self.capacity, self.n_tokens, N_SINK
+        d.codes = self.codes.data_ptr()
+        d.alpha = self.alpha.data_ptr()
+        d.mu = self.mu.data_ptr()
+        d.k_sink = self.k_sink.data_ptr()
+        if self.v is not None:
+            sb, sh, st = _strides_rows(self.v, "v")
+            d.v = self.v.data_ptr()
+            d.v_stride_b, d.v_stride_h, d.v_stride_t = sb, sh, st
+        d.codebook = None
+        return d
+
+
+def workspace_bytes(op: int, cache: Cache, n_q_heads: int = 1, top_k: int = 1) -> int:
+    d = cache.desc()
+    return int(lib.sikv_workspace_bytes(op, ctypes.byref(d), n_q_heads, top_k))
+
+
+def sikv_encode(cache: Cache, k: torch.Tensor, t_begin: int = 0, t_end: int | None = None,
+                recompute_mu: bool = True) -> None:
+    """Compress keys of tokens [t_begin, t_end) (k holds exactly those rows).
+    recompute_mu=True: prefill of the whole cache (t_begin 0, sets n_tokens);
+    False: append with the frozen mean (raises n_tokens to t_end)."""
+    kb = _bits(k)
+    if t_end is None:
+        t_end = t_begin + kb.shape[2]
+    sb, sh, st = _strides_rows(kb, "k")
+    if recompute_mu:
+        cache.n_tokens = t_end
+    d = cache.desc()
+    need = int(lib.sikv_workspace_bytes(OP_ENCODE, ctypes.byref(d), 1, 1)) if recompute_mu else 0
+    ws, wsn = cache.ws.get(need)
+    _check(lib.sikv_encode(ctypes.byref(d), kb.data_ptr(), sb, sh, st, t_begin, t_end,
+                           1 if recompute_mu else 0, ws, wsn, _stream(cache.device)),
+           "sikv_encode")
+    if not recompute_mu:
+        cache.n_tokens = max(cache.n_tokens, t_end)
+
+
+def sikv_score_topk(cache: Cache, q: torch.Tensor, top_k: int, idx: torch.Tensor | None = None,
+                    scores: torch.Tensor | None = None) -> torch.Tensor:
+    qb = _bits(q).contiguous()
+    n_q = qb.shape[1]
+    d = cache.desc()
+    if idx is None:
+        idx = torch.empty((cache.batch, cache.n_kv_heads, top_k), dtype=torch.int32,
+                          device=cache.device)
+    need = int(lib.sikv_workspace_bytes(OP_SCORE_TOPK, ctypes.byref(d), n_q, top_k))
+    ws, wsn = cache.ws.get(need)
+    _check(lib.sikv_score_topk(ctypes.byref(d), qb.data_ptr(), n_q, top_k, idx.data_ptr(),
+                               _ptr(scores), ws, wsn, _stream(cache.device)), "sikv_score_topk")
+    return idx
+
+
+def sikv_sparse_attn(cache: Cache, q: torch.Tensor, idx: torch.Tensor,
+                     sm_scale: float | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    qb = _bits(q).contiguous()
+    n_q = qb.shape[1]
+    top_k = idx.shape[-1]
+    sm = 1.0 / math.sqrt(HEAD_DIM) if sm_scale is None else float(sm_scale)
+    if out is None:
+        out = torch.empty((cache.batch, n_q, HEAD_DIM), dtype=torch.float32, device=cache.device)
+    d = cache.desc()
+    need = int(lib.sikv_workspace_bytes(OP_SPARSE_ATTN, ctypes.byref(d), n_q, top_k))
+    ws, wsn = cache.ws.get(need)
+    idx = idx.contiguous()
+    _check(lib.sikv_sparse_attn(ctypes.byref(d), qb.data_ptr(), n_q, idx.data_ptr(), top_k,
+                                ctypes.c_float(sm), out.data_ptr(), ws, wsn, _stream(cache.device)),
+           "sikv_sparse_attn")
+    return out
+
+
+def sikv_decode_step(cache: Cache, q: torch.Tensor, top_k: int, sm_scale: float | None = None,
+                     idx_out: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    qb = _bits(q).contiguous()
+    n_q = qb.shape[1]
+    sm = 1.0 / math.sqrt(HEAD_DIM) if sm_scale is None else float(sm_scale)
+    if out is None:
+        out = torch.empty((cache.batch, n_q, HEAD_DIM), dtype=torch.float32, device=cache.device)
+    d = cache.desc()
+    need = int(lib.sikv_workspace_bytes(OP_DECODE_STEP, ctypes.byref(d), n_q, top_k))
+    ws, wsn = cache.ws.get(need)
+    _check(lib.sikv_decode_step(ctypes.byref(d), qb.data_ptr(), n_q, top_k, ctypes.c_float(sm),
+                                _ptr(idx_out), out.data_ptr(), ws, wsn, _stream(cache.device)),
+           "sikv_decode_step")
+    return out
+
+
+def sikv_dense_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    sm_scale: float | None = None, out: torch.Tensor | None = None,
+                    ws: Workspace | None = None) -> torch.Tensor:
+    """Dense bf16 decode attention over every token (the comparator)."""
+    qb, kb, vb = _bits(q).contiguous(), _bits(k), _bits(v)
+    B, n_q = qb.shape[0], qb.shape[1]
+    Hkv, N = kb.shape[1], kb.shape[2]
+    ksb, ksh, kst = _strides_rows(kb, "k")
+    vsb, vsh, vst = _strides_rows(vb, "v")
+    sm = 1.0 / math.sqrt(HEAD_DIM) if sm_scale is None else float(sm_scale)
+    if out is None:
+        out = torch.empty((B, n_q, HEAD_DIM), dtype=torch.float32, device=q.device)
+    ws = ws or Workspace(q.device)
+    w, wn = ws.get(int(lib.sikv_dense_workspace_bytes(B, Hkv, n_q, N)))
+    _check(lib.sikv_dense_attn(B, Hkv, n_q, N, qb.data_ptr(), kb.data_ptr(), ksb, ksh, kst,
+                               vb.data_ptr(), vsb, vsh, vst, ctypes.c_float(sm), out.data_ptr(),
+                               w, wn, _stream(q.device)), "sikv_dense_attn")
+    return out
+
+
+def sikv_stream_copy(dst: torch.Tensor, src: torch.Tensor) -> None:
+    n = src.numel() * src.element_size()
+    _check(lib.sikv_stream_copy(dst.data_ptr(), src.data_ptr(), n, _stream(src.device)),
+           "sikv_stream_copy")
+
+
+# ----------------------------------------------------------------- kernel timing
+def timing_enable(on: bool = True) -> None:
+    _check(lib.sikv_timing_enable(1 if on else 0), "sikv_timing_enable")
+
+
+def timing_reset() -> None:
+    _check(lib.sikv_timing_reset(), "sikv_timing_reset")
+
+
+def timing_read() -> dict:
+    """{kernel name: (launches, total ms)} since the last reset."""
+    res = {}
+    for i in range(lib.sikv_timing_count()):
+        n = ctypes.c_int64()
+        ms = ctypes.c_double()
+        _check(lib.sikv_timing_read(i, ctypes.byref(n), ctypes.byref(ms)), "sikv_timing_read")
+        res[lib.sikv_timing_name(i).decode()] = (int(n.value), float(ms.value))
+    return res
+
+
+def debug_force_exact_select(on: bool) -> None:
+    _check(lib.sikv_debug_force_exact_select(1 if on else 0), "sikv_debug_force_exact_select")

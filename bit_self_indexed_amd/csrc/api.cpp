@@ -1,0 +1,474 @@
+// Host side of the C ABI declared in include/sikv.h: argument validation,
+// workspace planning and the launch sequences of each call.  Nothing here
+// allocates device memory or synchronises a stream.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <mutex>
+#include <vector>
+
+#include "../../include/sikv.h"
+#include "sikv_internal.h"
+
+namespace {
+
+using namespace sikv;
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxChunks = 4096;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline bool misaligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) != 0; }
+
+// ------------------------------------------------------------------ plans
+struct EncodePlan {
+  int nblk;
+  size_t bytes;
+};
+
+struct ScorePlan {
+  int chunk, n_chunks;
+  size_t off_tau, off_cnt, off_ckey, off_ct, off_pkey, off_pt, bytes;
+};
+
+struct AttnPlan {
+  int split, n_splits;
+  size_t off_o, off_ml, bytes;
+};
+
+struct DecodePlan {
+  ScorePlan sp;
+  AttnPlan ap;
+  size_t off_idx, off_score, off_attn, bytes;
+};
+
+EncodePlan plan_encode(const sikv_cache_desc* c) {
+  EncodePlan p;
+  p.nblk = (int)cdiv(c->n_tokens, 256);
+  p.bytes = align_up((size_t)c->batch * c->n_kv_heads * p.nblk * kD * sizeof(float));
+  return p;
+}
+
+// Tile of the score kernel: 256*U candidates per block, the largest U in
+// {8,4,2,1} that still gives >= 1024 blocks (4 per CU), widened if the tile
+// count would exceed what the select kernel keeps in LDS.
+bool plan_score(const sikv_cache_desc* c, ScorePlan* p) {
+  const int64_t BH = (int64_t)c->batch * c->n_kv_heads;
+  const int64_t n = (int64_t)c->n_tokens - kSink;
+  int U = 1;
+  for (int u : {8, 4, 2}) {
+    if (BH * cdiv(n, 256 * u) >= 1024) {
+      U = u;
+      break;
+    }
+  }
+  while (cdiv(n, 256 * U) > kMaxChunks && U < 16) U *= 2;
+  if (cdiv(n, 256 * U) > kMaxChunks) return false;
+  p->chunk = 256 * U;
+  p->n_chunks = (int)cdiv(n, p->chunk);
+  const size_t cap = (size_t)BH * p->n_chunks * p->chunk;
+  size_t o = 0;
+  p->off_tau = o;  o += align_up((size_t)BH * sizeof(float));
+  p->off_cnt = o;  o += align_up((size_t)BH * p->n_chunks * sizeof(int32_t));
+  p->off_ckey = o; o += align_up(cap * sizeof(uint32_t));
+  p->off_ct = o;   o += align_up(cap * sizeof(int32_t));
+  p->off_pkey = o; o += align_up(cap * sizeof(uint32_t));
+  p->off_pt = o;   o += align_up(cap * sizeof(int32_t));
+  p->bytes = o;
+  return true;
+}
+
+// Entries of the attended list (64 sinks + k) per block: the largest of
+// 256/128/64 that still gives >= 1024 blocks.
+void plan_attn(const sikv_cache_desc* c, int n_q_heads, int top_k, AttnPlan* p) {
+  const int64_t BH = (int64_t)c->batch * c->n_kv_heads;
+  const int64_t L = (int64_t)kSink + top_k;
+  int split = 256;
+  while (split > 64 && BH * cdiv(L, split) < 1024) split /= 2;
+  p->split = split;
+  p->n_splits = (int)cdiv(L, split);
+  const size_t rows = (size_t)c->batch * n_q_heads * p->n_splits;
+  p->off_o = 0;
+  p->off_ml = align_up(rows * kD * sizeof(float));
+  p->bytes = p->off_ml + align_up(rows * 2 * sizeof(float));
+}
+
+bool plan_decode(const sikv_cache_desc* c, int n_q_heads, int top_k, DecodePlan* p) {
+  if (!plan_score(c, &p->sp)) return false;
+  plan_attn(c, n_q_heads, top_k, &p->ap);
+  p->off_idx = 0;
+  p->off_score = align_up((size_t)c->batch * c->n_kv_heads * top_k * sizeof(int32_t));
+  p->off_attn = p->off_score + p->sp.bytes;
+  p->bytes = p->off_attn + p->ap.bytes;
+  return true;
+}
+
+// ------------------------------------------------------------------ validation
+sikv_status check_desc(const sikv_cache_desc* c) {
+  if (c == nullptr) return SIKV_ERR_INVALID_ARG;
+  if (c->head_dim != kD || c->n_sink != kSink || c->codebook != nullptr) return SIKV_ERR_UNSUPPORTED;
+  if (c->batch < 1 || c->n_kv_heads < 1 || (int64_t)c->batch * c->n_kv_heads > 65535)
+    return SIKV_ERR_INVALID_ARG;
+  if (c->n_tokens <= kSink || c->capacity < c->n_tokens) return SIKV_ERR_INVALID_ARG;
+  if (!c->codes || !c->alpha || !c->mu || !c->k_sink) return SIKV_ERR_INVALID_ARG;
+  if (misaligned(c->codes, 16) || misaligned(c->alpha, 4) || misaligned(c->mu, 16) ||
+      misaligned(c->k_sink, 16))
+    return SIKV_ERR_INVALID_ARG;
+  return SIKV_OK;
+}
+
+bool bad_strides(int64_t sb, int64_t sh, int64_t st) {
+  return sb < 0 || sh < 0 || st < 0 || (sb % 8) || (sh % 8) || (st % 8);
+}
+
+sikv_status check_v(const sikv_cache_desc* c) {
+  if (c->v == nullptr || misaligned(c->v, 16) || bad_strides(c->v_stride_b, c->v_stride_h, c->v_stride_t))
+    return SIKV_ERR_INVALID_ARG;
+  return SIKV_OK;
+}
+
+sikv_status check_query(const sikv_cache_desc* c, const uint16_t* q, int n_q_heads, int top_k) {
+  if (q == nullptr || misaligned(q, 16)) return SIKV_ERR_INVALID_ARG;
+  if (n_q_heads < 1 || n_q_heads % c->n_kv_heads) return SIKV_ERR_INVALID_ARG;
+  if (n_q_heads / c->n_kv_heads > kMaxGroup) return SIKV_ERR_UNSUPPORTED;
+  if (top_k < 1 || top_k > c->n_tokens - kSink) return SIKV_ERR_INVALID_ARG;
+  return SIKV_OK;
+}
+
+sikv_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return SIKV_OK;
+  if (ws == nullptr || misaligned(ws, kAlign) || ws_bytes < need) return SIKV_ERR_WORKSPACE;
+  return SIKV_OK;
+}
+
+#define SIKV_TRY(expr)                               \
+  do {                                               \
+    if ((expr) != hipSuccess) return SIKV_ERR_HIP;   \
+  } while (0)
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+std::atomic<int> g_force_exact{0};
+
+sikv_status run_score_topk(const sikv_cache_desc* c, const uint16_t* q, int n_q_heads, int top_k,
+                           int32_t* idx, float* scores_opt, void* ws, const ScorePlan& sp,
+                           hipStream_t s) {
+  const int B = c->batch, Hkv = c->n_kv_heads;
+  float* tau = at<float>(ws, sp.off_tau);
+  int32_t* cnt = at<int32_t>(ws, sp.off_cnt);
+  uint32_t* ckey = at<uint32_t>(ws, sp.off_ckey);
+  int32_t* ct = at<int32_t>(ws, sp.off_ct);
+  uint32_t* pkey = at<uint32_t>(ws, sp.off_pkey);
+  int32_t* pt = at<int32_t>(ws, sp.off_pt);
+  SIKV_TRY(launch_sample(q, n_q_heads, B, Hkv, c->codes, c->alpha, c->capacity, c->n_tokens,
+                         top_k, g_force_exact.load(std::memory_order_relaxed), tau, s));
+  SIKV_TRY(launch_score(q, n_q_heads, B, Hkv, c->codes, c->alpha, c->capacity, c->n_tokens, tau,
+                        sp.chunk, sp.n_chunks, ckey, ct, cnt, scores_opt, s));
+  SIKV_TRY(launch_select(q, n_q_heads, B, Hkv, c->codes, c->alpha, c->capacity, c->n_tokens, top_k,
+                         sp.chunk, sp.n_chunks, ckey, ct, cnt, pkey, pt, idx, s));
+  return SIKV_OK;
+}
+
+sikv_status run_attn(const sikv_cache_desc* c, const uint16_t* q, int n_q_heads,
+                     const int32_t* idx, int top_k, float sm_scale, float* out, void* ws,
+                     const AttnPlan& ap, hipStream_t s) {
+  float* po = at<float>(ws, ap.off_o);
+  float* pml = at<float>(ws, ap.off_ml);
+  SIKV_TRY(launch_attn(q, n_q_heads, c->batch, c->n_kv_heads, c->codes, c->alpha, c->mu, c->k_sink,
+                       c->v, c->v_stride_b, c->v_stride_h, c->v_stride_t, c->capacity, c->n_tokens, idx, top_k,
+                       sm_scale, ap.split, ap.n_splits, po, pml, s));
+  SIKV_TRY(launch_combine(po, pml, c->batch * n_q_heads, ap.n_splits, out, s));
+  return SIKV_OK;
+}
+
+// ------------------------------------------------------------------ timing
+std::mutex g_tmu;
+std::atomic<int> g_timing{0};
+struct Pending {
+  int kid;
+  hipEvent_t e0, e1;
+};
+std::vector<Pending> g_pending;
+std::vector<hipEvent_t> g_pool;
+double g_ms[KID_COUNT];
+int64_t g_cnt[KID_COUNT];
+const char* const g_names[KID_COUNT] = {"mu_partial", "mu_final", "codes", "sample",
+                                        "score",      "select",   "attn",  "combine",
+                                        "dense",      "copy"};
+
+hipEvent_t take_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+sikv_status drain_pending() {
+  sikv_status st = SIKV_OK;
+  for (auto& p : g_pending) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(p.e1) != hipSuccess || hipEventElapsedTime(&ms, p.e0, p.e1) != hipSuccess)
+      st = SIKV_ERR_HIP;
+    else {
+      g_ms[p.kid] += ms;
+      g_cnt[p.kid] += 1;
+    }
+    g_pool.push_back(p.e0);
+    g_pool.push_back(p.e1);
+  }
+  g_pending.clear();
+  return st;
+}
+
+}  // namespace
+
+namespace sikv {
+void timing_events(int kernel_id, hipEvent_t* start, hipEvent_t* stop) {
+  *start = *stop = nullptr;
+  if (!g_timing.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> lk(g_tmu);
+  hipEvent_t a = take_event(), b = take_event();
+  if (!a || !b) {
+    if (a) g_pool.push_back(a);
+    if (b) g_pool.push_back(b);
+    return;
+  }
+  g_pending.push_back({kernel_id, a, b});
+  *start = a;
+  *stop = b;
+}
+}  // namespace sikv
+
+// ================================================================== C ABI
+extern "C" {
+
+sikv_status sikv_encode(const sikv_cache_desc* c, const uint16_t* k, int64_t k_stride_b,
+                        int64_t k_stride_h, int64_t k_stride_t, int32_t t_begin, int32_t t_end,
+                        int32_t recompute_mu, void* ws, size_t ws_bytes, void* stream) {
+  sikv_status st = check_desc(c);
+  if (st != SIKV_OK) return st;
+  if (k == nullptr || misaligned(k, 16) || bad_strides(k_stride_b, k_stride_h, k_stride_t))
+    return SIKV_ERR_INVALID_ARG;
+  if (recompute_mu != 0 && recompute_mu != 1) return SIKV_ERR_INVALID_ARG;
+  if (t_begin < 0 || t_end <= t_begin || t_end > c->capacity) return SIKV_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (recompute_mu) {
+    if (t_begin != 0 || t_end != c->n_tokens) return SIKV_ERR_INVALID_ARG;
+    const EncodePlan p = plan_encode(c);
+    st = check_ws(ws, ws_bytes, p.bytes);
+    if (st != SIKV_OK) return st;
+    float* partial = static_cast<float*>(ws);
+    SIKV_TRY(launch_mu_partial(k, k_stride_b, k_stride_h, k_stride_t, c->batch, c->n_kv_heads,
+                               c->n_tokens, partial, p.nblk, s));
+    SIKV_TRY(launch_mu_final(partial, c->batch * c->n_kv_heads, p.nblk, c->n_tokens, c->mu, s));
+  }
+  SIKV_TRY(launch_codes(k, k_stride_b, k_stride_h, k_stride_t, c->batch, c->n_kv_heads, t_begin,
+                        t_end, c->capacity, c->mu, c->codes, c->alpha, c->k_sink, s));
+  return SIKV_OK;
+}
+
+sikv_status sikv_score_topk(const sikv_cache_desc* c, const uint16_t* q, int32_t n_q_heads,
+                            int32_t top_k, int32_t* idx, float* scores_opt, void* ws,
+                            size_t ws_bytes, void* stream) {
+  sikv_status st = check_desc(c);
+  if (st != SIKV_OK) return st;
+  st = check_query(c, q, n_q_heads, top_k);
+  if (st != SIKV_OK) return st;
+  if (idx == nullptr || misaligned(idx, 4) || misaligned(scores_opt, 4)) return SIKV_ERR_INVALID_ARG;
+  ScorePlan sp;
+  if (!plan_score(c, &sp)) return SIKV_ERR_UNSUPPORTED;
+  st = check_ws(ws, ws_bytes, sp.bytes);
+  if (st != SIKV_OK) return st;
+  return run_score_topk(c, q, n_q_heads, top_k, idx, scores_opt, ws, sp,
+                        static_cast<hipStream_t>(stream));
+}
+
+sikv_status sikv_sparse_attn(const sikv_cache_desc* c, const uint16_t* q, int32_t n_q_heads,
+                             const int32_t* idx, int32_t top_k, float sm_scale, float* out,
+                             void* ws, size_t ws_bytes, void* stream) {
+  sikv_status st = check_desc(c);
+  if (st != SIKV_OK) return st;
+  st = check_query(c, q, n_q_heads, top_k);
+  if (st != SIKV_OK) return st;
+  st = check_v(c);
+  if (st != SIKV_OK) return st;
+  if (idx == nullptr || misaligned(idx, 4) || out == nullptr || misaligned(out, 4))
+    return SIKV_ERR_INVALID_ARG;
+  if (!std::isfinite(sm_scale)) return SIKV_ERR_INVALID_ARG;
+  AttnPlan ap;
+  plan_attn(c, n_q_heads, top_k, &ap);
+  st = check_ws(ws, ws_bytes, ap.bytes);
+  if (st != SIKV_OK) return st;
+  return run_attn(c, q, n_q_heads, idx, top_k, sm_scale, out, ws, ap,
+                  static_cast<hipStream_t>(stream));
+}
+
+sikv_status sikv_decode_step(const sikv_cache_desc* c, const uint16_t* q, int32_t n_q_heads,
+                             int32_t top_k, float sm_scale, int32_t* idx_out_opt, float* out,
+                             void* ws, size_t ws_bytes, void* stream) {
+  sikv_status st = check_desc(c);
+  if (st != SIKV_OK) return st;
+  st = check_query(c, q, n_q_heads, top_k);
+  if (st != SIKV_OK) return st;
+  st = check_v(c);
+  if (st != SIKV_OK) return st;
+  if (out == nullptr || misaligned(out, 4) || misaligned(idx_out_opt, 4)) return SIKV_ERR_INVALID_ARG;
+  if (!std::isfinite(sm_scale)) return SIKV_ERR_INVALID_ARG;
+  DecodePlan dp;
+  if (!plan_decode(c, n_q_heads, top_k, &dp)) return SIKV_ERR_UNSUPPORTED;
+  st = check_ws(ws, ws_bytes, dp.bytes);
+  if (st != SIKV_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* idx = idx_out_opt ? idx_out_opt : at<int32_t>(ws, dp.off_idx);
+  st = run_score_topk(c, q, n_q_heads, top_k, idx, nullptr, at<char>(ws, dp.off_score), dp.sp, s);
+  if (st != SIKV_OK) return st;
+  return run_attn(c, q, n_q_heads, idx, top_k, sm_scale, out, at<char>(ws, dp.off_attn), dp.ap, s);
+}
+
+size_t sikv_workspace_bytes(int32_t op, const sikv_cache_desc* c, int32_t n_q_heads,
+                            int32_t top_k) {
+  if (check_desc(c) != SIKV_OK) return 0;
+  switch (op) {
+    case SIKV_OP_ENCODE:
+      return plan_encode(c).bytes;
+    case SIKV_OP_SCORE_TOPK: {
+      if (check_query(c, reinterpret_cast<const uint16_t*>(kAlign), n_q_heads, top_k) != SIKV_OK)
+        return 0;
+      ScorePlan sp;
+      return plan_score(c, &sp) ? sp.bytes : 0;
+    }
+    case SIKV_OP_SPARSE_ATTN: {
+      if (check_query(c, reinterpret_cast<const uint16_t*>(kAlign), n_q_heads, top_k) != SIKV_OK)
+        return 0;
+      AttnPlan ap;
+      plan_attn(c, n_q_heads, top_k, &ap);
+      return ap.bytes;
+    }
+    case SIKV_OP_DECODE_STEP: {
+      if (check_query(c, reinterpret_cast<const uint16_t*>(kAlign), n_q_heads, top_k) != SIKV_OK)
+        return 0;
+      DecodePlan dp;
+      return plan_decode(c, n_q_heads, top_k, &dp) ? dp.bytes : 0;
+    }
+    default:
+      return 0;
+  }
+}
+
+const char* sikv_status_str(sikv_status s) {
+  switch (s) {
+    case SIKV_OK:
+      return "ok";
+    case SIKV_ERR_INVALID_ARG:
+      return "invalid argument (null or misaligned pointer, bad size or range)";
+    case SIKV_ERR_UNSUPPORTED:
+      return "unsupported (head_dim must be 128, 64 sinks, 1..8 query heads per KV head, no codebook)";
+    case SIKV_ERR_WORKSPACE:
+      return "workspace missing, not 256-byte aligned, or smaller than sikv_workspace_bytes";
+    case SIKV_ERR_HIP:
+      return "HIP kernel launch or runtime call failed";
+    default:
+      return "unknown status";
+  }
+}
+
+int32_t sikv_abi_version(void) { return SIKV_ABI_VERSION; }
+size_t sikv_desc_size(void) { return sizeof(sikv_cache_desc); }
+
+size_t sikv_dense_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads,
+                                  int32_t n_tokens) {
+  if (batch < 1 || n_kv_heads < 1 || n_q_heads < 1 || n_tokens < 1 || n_q_heads % n_kv_heads)
+    return 0;
+  const int64_t BH = (int64_t)batch * n_kv_heads;
+  const int64_t per_head = cdiv(1024, BH);
+  int64_t split = cdiv(cdiv(n_tokens, per_head), 256) * 256;
+  if (split < 256) split = 256;
+  const int64_t n_splits = cdiv(n_tokens, split);
+  const size_t rows = (size_t)batch * n_q_heads * n_splits;
+  return align_up(rows * kD * sizeof(float)) + align_up(rows * 2 * sizeof(float));
+}
+
+sikv_status sikv_dense_attn(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads, int32_t n_tokens,
+                            const uint16_t* q, const uint16_t* k, int64_t k_stride_b,
+                            int64_t k_stride_h, int64_t k_stride_t, const uint16_t* v,
+                            int64_t v_stride_b, int64_t v_stride_h, int64_t v_stride_t,
+                            float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream) {
+  if (batch < 1 || n_kv_heads < 1 || n_q_heads < 1 || n_tokens < 1 || n_q_heads % n_kv_heads ||
+      (int64_t)batch * n_kv_heads > 65535)
+    return SIKV_ERR_INVALID_ARG;
+  if (n_q_heads / n_kv_heads > kMaxGroup) return SIKV_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !out || misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) ||
+      misaligned(out, 4) || bad_strides(k_stride_b, k_stride_h, k_stride_t) ||
+      bad_strides(v_stride_b, v_stride_h, v_stride_t) || !std::isfinite(sm_scale))
+    return SIKV_ERR_INVALID_ARG;
+  const size_t need = sikv_dense_workspace_bytes(batch, n_kv_heads, n_q_heads, n_tokens);
+  sikv_status st = check_ws(ws, ws_bytes, need);
+  if (st != SIKV_OK) return st;
+  const int64_t BH = (int64_t)batch * n_kv_heads;
+  const int64_t per_head = cdiv(1024, BH);
+  int64_t split = cdiv(cdiv(n_tokens, per_head), 256) * 256;
+  if (split < 256) split = 256;
+  const int n_splits = (int)cdiv(n_tokens, split);
+  const size_t rows = (size_t)batch * n_q_heads * n_splits;
+  float* po = static_cast<float*>(ws);
+  float* pml = at<float>(ws, align_up(rows * kD * sizeof(float)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SIKV_TRY(launch_dense(q, n_q_heads, batch, n_kv_heads, n_tokens, k, k_stride_b, k_stride_h,
+                        k_stride_t, v, v_stride_b, v_stride_h, v_stride_t, sm_scale, (int)split,
+                        n_splits, po, pml, s));
+  SIKV_TRY(launch_combine(po, pml, batch * n_q_heads, n_splits, out, s));
+  return SIKV_OK;
+}
+
+sikv_status sikv_stream_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (!dst || !src || bytes == 0 || bytes % 16 || misaligned(dst, 16) || misaligned(src, 16))
+    return SIKV_ERR_INVALID_ARG;
+  SIKV_TRY(launch_copy(dst, src, bytes, static_cast<hipStream_t>(stream)));
+  return SIKV_OK;
+}
+
+sikv_status sikv_timing_enable(int32_t on) {
+  g_timing.store(on ? 1 : 0);
+  return SIKV_OK;
+}
+
+sikv_status sikv_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  sikv_status st = drain_pending();
+  for (int i = 0; i < KID_COUNT; ++i) {
+    g_ms[i] = 0.0;
+    g_cnt[i] = 0;
+  }
+  return st;
+}
+
+int32_t sikv_timing_count(void) { return KID_COUNT; }
+
+const char* sikv_timing_name(int32_t id) {
+  return (id >= 0 && id < KID_COUNT) ? g_names[id] : "unknown";
+}
+
+sikv_status sikv_timing_read(int32_t id, int64_t* launches, double* total_ms) {
+  if (id < 0 || id >= KID_COUNT || !launches || !total_ms) return SIKV_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(g_tmu);
+  sikv_status st = drain_pending();
+  *launches = g_cnt[id];
+  *total_ms = g_ms[id];
+  return st;
+}
+
+sikv_status sikv_debug_force_exact_select(int32_t on) {
+  g_force_exact.store(on ? 1 : 0);
+  return SIKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,177 @@
+// Prefill / append compression of the key cache (gfx950).
+//
+// "Self-Indexing KVCache: Predicting Sparse Attention from Compressed Keys",
+// technical summary §2.1 item 1: keys are centred by their channel mean
+// (entropy-aware normalisation), then every channel contributes its sign as one
+// bit, so each 4-dim sub-vector lands in one of 16 clusters; §2.1 item 3: the
+// format is token-wise and the 64 first tokens stay in full precision.
+//
+// Bit-exactness: the mean and the per-token scale are sums whose rounding
+// decides the codes, so both follow one fixed order, the adjacent-pair binary
+// tree in fp32 (mean: over the token axis with sink rows and rows past N as
+// +0.0, padded to a power of two; scale: over the 128 channels).  Every
+// blocking below is an aligned power-of-two split of that tree.
+#include <hip/hip_ext.h>
+
+#include "sikv_internal.h"
+
+namespace sikv {
+
+namespace {
+
+__device__ __forceinline__ float chan(const uint4& w, int c) {
+  const uint32_t x = (c >> 1) == 0 ? w.x : (c >> 1) == 1 ? w.y : (c >> 1) == 2 ? w.z : w.w;
+  return (c & 1) ? bf16hi(x) : bf16lo(x);
+}
+
+// Pairwise tree over 16 leaves (one aligned 16-leaf subtree).
+__device__ __forceinline__ float tree16(const float* l) {
+  const float a0 = l[0] + l[1], a1 = l[2] + l[3], a2 = l[4] + l[5], a3 = l[6] + l[7];
+  const float a4 = l[8] + l[9], a5 = l[10] + l[11], a6 = l[12] + l[13], a7 = l[14] + l[15];
+  const float b0 = a0 + a1, b1 = a2 + a3, b2 = a4 + a5, b3 = a6 + a7;
+  return (b0 + b1) + (b2 + b3);
+}
+
+// Mean, stage 1: one block per (256-token tile, b*h).  Thread (rs, cg) owns the
+// aligned 16-row group rs of the tile and channels 8cg..8cg+7; its 16-leaf
+// subtree is summed in registers, then the 16 group sums are combined by the
+// tree's top 4 levels.  Leaves outside [64, N) are +0.0 (never loaded).
+__global__ __launch_bounds__(256) void mu_partial_kernel(const uint16_t* __restrict__ k, int64_t sb,
+                                                         int64_t sh, int64_t st, int Hkv,
+                                                         int n_tokens, float* __restrict__ partial,
+                                                         int nblk) {
+  __shared__ float red[16][kD + 1];
+  const int bh = blockIdx.y, b = bh / Hkv, h = bh - b * Hkv;
+  const int tid = threadIdx.x, cg = tid & 15, rs = tid >> 4;
+  const int t0 = blockIdx.x * 256 + rs * 16;
+  const uint16_t* base = k + (int64_t)b * sb + (int64_t)h * sh + cg * 8;
+  uint4 w[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int t = t0 + i;
+    w[i] = (t >= kSink && t < n_tokens) ? *reinterpret_cast<const uint4*>(base + (int64_t)t * st)
+                                        : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    float l[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) l[i] = chan(w[i], c);
+    red[rs][cg * 8 + c] = tree16(l);
+  }
+  __syncthreads();
+  if (tid < kD) {
+    float l[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) l[r] = red[r][tid];
+    partial[((int64_t)bh * nblk + blockIdx.x) * kD + tid] = tree16(l);
+  }
+}
+
+// Mean, stage 2: one block per b*h, one thread per channel.  The tile sums are
+// the leaves of the remaining levels (padded with +0.0 to a power of two) and
+// are reduced by a binary counter: leaf i is merged with the pending subtree of
+// each level where i has a trailing 1 bit, which is exactly the pairwise tree.
+__global__ __launch_bounds__(128) void mu_final_kernel(const float* __restrict__ partial, int nblk,
+                                                       int n_tokens, float* __restrict__ mu) {
+  __shared__ float stk[32][kD];
+  const int bh = blockIdx.x, c = threadIdx.x;
+  int n2 = 1, levels = 0;
+  while (n2 < nblk) {
+    n2 <<= 1;
+    ++levels;
+  }
+  const float* p = partial + (int64_t)bh * nblk * kD + c;
+  for (int i = 0; i < n2; ++i) {
+    float x = (i < nblk) ? p[(int64_t)i * kD] : 0.0f;
+    int lvl = 0;
+    for (unsigned ii = (unsigned)i; ii & 1u; ii >>= 1) {
+      x = stk[lvl][c] + x;
+      ++lvl;
+    }
+    stk[lvl][c] = x;
+  }
+  mu[(int64_t)bh * kD + c] = __fdiv_rn(stk[levels][c], (float)(n_tokens - kSink));
+}
+
+// Codes, scales and sink copy: one block per (128-token tile, b*h); 16 lanes per
+// 256-byte key row, 8 channels (one code byte) per lane, 8 rows per thread.
+// bit c = (k_c < mu_c); scale = tree(|fl(k_c - mu_c)|) * 2^-7 where the lane's 8
+// channels form an aligned subtree and the xor butterfly over lanes 1,2,4,8 forms
+// the top levels (each lane ends with the same bits).
+__global__ __launch_bounds__(256) void codes_kernel(const uint16_t* __restrict__ k, int64_t sb,
+                                                    int64_t sh, int64_t st, int Hkv, int t_begin,
+                                                    int t_end, int capacity,
+                                                    const float* __restrict__ mu,
+                                                    uint8_t* __restrict__ codes,
+                                                    float* __restrict__ alpha,
+                                                    uint16_t* __restrict__ k_sink) {
+  const int bh = blockIdx.y, b = bh / Hkv, h = bh - b * Hkv;
+  const int tid = threadIdx.x, cg = tid & 15, rs = tid >> 4;
+  const int tb = t_begin + blockIdx.x * 128;
+  float m[8];
+  {
+    const float4 m0 = *reinterpret_cast<const float4*>(mu + (int64_t)bh * kD + cg * 8);
+    const float4 m1 = *reinterpret_cast<const float4*>(mu + (int64_t)bh * kD + cg * 8 + 4);
+    m[0] = m0.x; m[1] = m0.y; m[2] = m0.z; m[3] = m0.w;
+    m[4] = m1.x; m[5] = m1.y; m[6] = m1.z; m[7] = m1.w;
+  }
+  const uint16_t* base = k + (int64_t)b * sb + (int64_t)h * sh + cg * 8;
+  uint4 w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int t = tb + i * 16 + rs;
+    w[i] = (t < t_end) ? *reinterpret_cast<const uint4*>(base + (int64_t)(t - t_begin) * st)
+                       : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int t = tb + i * 16 + rs;
+    uint32_t byte = 0;
+    float a[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float x = chan(w[i], c);
+      byte |= (x < m[c] ? 1u : 0u) << c;
+      a[c] = fabsf(x - m[c]);
+    }
+    float s = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);
+    s += __shfl_xor(s, 8);
+    const uint32_t v16 = byte | (__shfl_down(byte, 1, 16) << 8);
+    const uint32_t v32 = v16 | (__shfl_down(v16, 2, 16) << 16);
+    if (t < t_end) {
+      const int64_t row = (int64_t)bh * capacity + t;
+      if ((cg & 3) == 0) *reinterpret_cast<uint32_t*>(codes + row * kCodeBytes + cg) = v32;
+      if (cg == 0) alpha[row] = s * 0.0078125f;
+      if (t < kSink)
+        *reinterpret_cast<uint4*>(k_sink + ((int64_t)bh * kSink + t) * kD + cg * 8) = w[i];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mu_partial(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
+                             int n_tokens, float* partial, int nblk, hipStream_t s) {
+  return launch_k(KID_MU_PARTIAL, mu_partial_kernel, dim3(nblk, B * Hkv), dim3(256), 0, s, k, sb,
+                  sh, st, Hkv, n_tokens, partial, nblk);
+}
+
+hipError_t launch_mu_final(const float* partial, int BH, int nblk, int n_tokens, float* mu,
+                           hipStream_t s) {
+  return launch_k(KID_MU_FINAL, mu_final_kernel, dim3(BH), dim3(kD), 0, s, partial, nblk,
+                  n_tokens, mu);
+}
+
+hipError_t launch_codes(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
+                        int t_begin, int t_end, int capacity, const float* mu, uint8_t* codes,
+                        float* alpha, uint16_t* k_sink, hipStream_t s) {
+  const int tiles = (t_end - t_begin + 127) / 128;
+  return launch_k(KID_CODES, codes_kernel, dim3(tiles, B * Hkv), dim3(256), 0, s, k, sb, sh, st,
+                  Hkv, t_begin, t_end, capacity, mu, codes, alpha, k_sink);
+}
+
+}  // namespace sikv

@@ -1,0 +1,221 @@
+/*
+ * sikv.h - C ABI of the self-indexing compressed-key decode path (gfx950 / MI355X).
+ *
+ * The method: "Self-Indexing KVCache: Predicting Sparse Attention from
+ * Compressed Keys" (web summary of arXiv 2603.14224, technical part).  Keys are
+ * normalised by their channel mean, split into 4-dim sub-vectors and sign-coded
+ * (one of 16 clusters per sub-vector, 1 bit per channel) plus one fp32 scale per
+ * token (§2.1 item 1).  A decoding query builds a 16-entry table per sub-vector
+ * and scores every cached token by table look-up and accumulation (LUT-GEMV),
+ * then keeps the top-k (§2.1 item 2).  Attention runs over the top-k plus 64
+ * full-precision sink tokens, with the keys dequantised inside the kernel
+ * (§2.1 items 3 and 4).
+ *
+ * Conventions shared by every call
+ *   - Pointers named in the cache descriptor and the arguments are DEVICE
+ *     pointers (hipMalloc'd or torch CUDA tensors) unless stated otherwise; the
+ *     descriptor itself and the workspace size query live in HOST memory.
+ *   - bf16 values are passed as uint16_t bit patterns.
+ *   - Ownership: every buffer belongs to the caller.  The library never
+ *     allocates, frees or keeps device memory; scratch comes from the caller's
+ *     workspace (size from sikv_workspace_bytes, 256-byte aligned start).
+ *   - Asynchrony: every call only enqueues kernels on `stream` (a hipStream_t;
+ *     NULL = the null stream) and returns.  Buffers must stay valid until the
+ *     stream has run the work.  No call synchronises.
+ *   - Errors: arguments are validated on the host before anything is launched;
+ *     an invalid call returns a negative status and launches nothing.  A failed
+ *     launch returns SIKV_ERR_HIP.  Faults inside kernels surface at the
+ *     caller's next synchronisation.  No C++ exception crosses this ABI.
+ *   - Shapes: head_dim 128 and 64 sinks only (SIKV_ERR_UNSUPPORTED otherwise);
+ *     query heads per KV head (G = n_q_heads / n_kv_heads) from 1 to 8, query
+ *     head h*G+g belongs to KV head h.
+ *   - Thread safety: calls keep no state between them (except the optional
+ *     kernel-timing facility at the end of this file) and may run concurrently
+ *     on different streams with disjoint buffers.
+ */
+#ifndef SIKV_H
+#define SIKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SIKV_ABI_VERSION 1
+#define SIKV_HEAD_DIM 128
+#define SIKV_N_SINK 64
+#define SIKV_MAX_GROUP 8
+
+typedef int32_t sikv_status;
+#define SIKV_OK 0
+#define SIKV_ERR_INVALID_ARG (-1) /* null/misaligned pointer, bad size or range   */
+#define SIKV_ERR_UNSUPPORTED (-2) /* valid but outside v1 (head_dim, sinks, G)     */
+#define SIKV_ERR_WORKSPACE (-3)   /* workspace missing, misaligned or too small    */
+#define SIKV_ERR_HIP (-4)         /* a kernel launch or HIP runtime call failed    */
+
+/* op codes of sikv_workspace_bytes */
+#define SIKV_OP_ENCODE 0
+#define SIKV_OP_SCORE_TOPK 1
+#define SIKV_OP_SPARSE_ATTN 2
+#define SIKV_OP_DECODE_STEP 3
+
+/*
+ * The compressed cache of one layer (caller-owned device arrays), described in
+ * host memory.  Index order [b][h][t][...] with b < batch, h < n_kv_heads,
+ * t < capacity.  Layout (§2.1 item 3: token-wise, so any token can be fetched
+ * on its own):
+ *   codes  uint8 [B][Hkv][capacity][16]: bit c of a token's code (byte c/8,
+ *          bit c%8, least significant first) is 1 iff its key channel c is
+ *          below the channel mean; nibble j (low nibble first) is the cluster
+ *          of sub-vector j (channels 4j..4j+3, bit i = channel 4j+i).  16-byte
+ *          aligned.
+ *   alpha  fp32 [B][Hkv][capacity]: per-token scale, mean |k_c - mu_c|.
+ *   mu     fp32 [B][Hkv][128]: channel mean of the non-sink prefill keys.
+ *   k_sink bf16 [B][Hkv][64][128]: the first 64 key rows, unquantised.
+ *   v      bf16 value cache, element (b,h,t,c) at v[b*v_stride_b + h*v_stride_h
+ *          + t*v_stride_t + c] (strides in elements, multiples of 8; rows
+ *          16-byte aligned).  Only read.
+ *   codebook  reserved for data-derived cluster centres; must be NULL.
+ * n_tokens (N) is the number of valid tokens of every sequence (64 < N <=
+ * capacity); candidates for top-k are the tokens 64..N-1.
+ */
+typedef struct sikv_cache_desc {
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t capacity;
+  int32_t n_tokens;
+  int32_t n_sink;
+  uint8_t *codes;
+  float *alpha;
+  float *mu;
+  uint16_t *k_sink;
+  const uint16_t *v;
+  int64_t v_stride_b;
+  int64_t v_stride_h;
+  int64_t v_stride_t;
+  const float *codebook;
+} sikv_cache_desc;
+
+/*
+ * sikv_encode - compress keys into the cache (§2.1 item 1: channel-mean
+ * normalisation, then sign codes of 4-dim sub-vectors; §2.1 item 3: the 64
+ * sink rows kept in full precision at prefill).
+ *   k            bf16 keys of tokens t_begin..t_end-1: element (b,h,t,c) at
+ *                k[b*k_stride_b + h*k_stride_h + (t - t_begin)*k_stride_t + c]
+ *                (strides in elements, multiples of 8; k 16-byte aligned).
+ *   recompute_mu 1: prefill.  Requires t_begin == 0 and t_end == n_tokens; mu
+ *                is recomputed from tokens 64..N-1 (fixed adjacent-pair fp32
+ *                tree over the token axis, then one rounded division), then
+ *                codes and alpha are written for tokens 0..N-1 and k_sink for
+ *                0..63.  Needs workspace (SIKV_OP_ENCODE).
+ *                0: append.  mu is kept; codes and alpha are written for
+ *                t_begin..t_end-1 (t_end <= capacity; rows below 64 also go to
+ *                k_sink).  The caller then raises n_tokens.  Needs no workspace.
+ *   alpha is the adjacent-pair fp32 tree of |fl(k_c - mu_c)| over the 128
+ *   channels times 2^-7.  Results are bit-identical to that definition.
+ */
+sikv_status sikv_encode(const sikv_cache_desc *cache, const uint16_t *k, int64_t k_stride_b,
+                        int64_t k_stride_h, int64_t k_stride_t, int32_t t_begin, int32_t t_end,
+                        int32_t recompute_mu, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * sikv_score_topk - compressed-domain retrieval (§2.1 item 2).  For every KV
+ * head h the selection query is the sum of its G query heads; its table holds,
+ * per sub-vector j and pattern p, the dot product of the query's 4 channels
+ * with the sign vertex p (+1 for bit 0, -1 for bit 1).  The score of token t is
+ * alpha_t * sum_j LUT[j][nibble_j(code_t)] (fp32), and the top_k tokens of
+ * 64..N-1 with the largest scores (ties: smaller t) are written to idx.
+ *   q          bf16 [B][n_q_heads][128], contiguous.
+ *   top_k      1..N-64.
+ *   idx        int32 [B][Hkv][top_k], ascending token positions.
+ *   scores_opt NULL, or fp32 [B][Hkv][capacity]: receives every candidate's
+ *              score (test hook; entries t < 64 and t >= N untouched).
+ */
+sikv_status sikv_score_topk(const sikv_cache_desc *cache, const uint16_t *q, int32_t n_q_heads,
+                            int32_t top_k, int32_t *idx, float *scores_opt, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/*
+ * sikv_sparse_attn - attention over the 64 sinks plus the selected tokens,
+ * dequantisation fused in (§2.1 items 3 and 4).  For query head g of KV head
+ * h and S = {0..63} U idx[b][h]: key_t = k_sink row (t < 64) or
+ * mu + alpha_t * v(code_t); logit = sm_scale * q_g . key_t; softmax over S;
+ * out = sum_t p_t V_t.  fp32 arithmetic, fp32 output.
+ *   idx  int32 [B][Hkv][top_k], distinct positions in 64..N-1 (any order;
+ *        ascending is fastest).  Not checked on the device.
+ *   out  fp32 [B][n_q_heads][128].
+ */
+sikv_status sikv_sparse_attn(const sikv_cache_desc *cache, const uint16_t *q, int32_t n_q_heads,
+                             const int32_t *idx, int32_t top_k, float sm_scale, float *out,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * sikv_decode_step - sikv_score_topk followed by sikv_sparse_attn on the same
+ * stream.  The current token must already be in the cache (sikv_encode with
+ * recompute_mu = 0).  idx_out_opt: NULL, or int32 [B][Hkv][top_k] to receive
+ * the selection.
+ */
+sikv_status sikv_decode_step(const sikv_cache_desc *cache, const uint16_t *q, int32_t n_q_heads,
+                             int32_t top_k, float sm_scale, int32_t *idx_out_opt, float *out,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes needed by `op` (SIKV_OP_*) for this cache and call shape.
+ * Host only, launches nothing.  Returns 0 for an invalid combination. */
+size_t sikv_workspace_bytes(int32_t op, const sikv_cache_desc *cache, int32_t n_q_heads,
+                            int32_t top_k);
+
+/* Static description of a status code; never NULL. */
+const char *sikv_status_str(sikv_status status);
+
+int32_t sikv_abi_version(void);
+size_t sikv_desc_size(void);
+
+/*
+ * Measurement helpers (not part of the method).
+ *
+ * sikv_dense_attn - dense bf16 decode attention over all N tokens of an
+ * unquantised cache (the comparator the method is measured against): for query
+ * head g of KV head h, softmax(sm_scale * q_g . K_t) over t < N, times V.
+ * K and V bf16 with the stride scheme of sikv_cache_desc; q bf16
+ * [B][n_q_heads][128]; out fp32 [B][n_q_heads][128].  Workspace from
+ * sikv_dense_workspace_bytes.
+ */
+sikv_status sikv_dense_attn(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads,
+                            int32_t n_tokens, const uint16_t *q, const uint16_t *k,
+                            int64_t k_stride_b, int64_t k_stride_h, int64_t k_stride_t,
+                            const uint16_t *v, int64_t v_stride_b, int64_t v_stride_h,
+                            int64_t v_stride_t, float sm_scale, float *out, void *ws,
+                            size_t ws_bytes, void *stream);
+size_t sikv_dense_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads,
+                                  int32_t n_tokens);
+
+/* Plain device copy of `bytes` (multiple of 16, both pointers 16-byte
+ * aligned): the reference kernel for bandwidth and traffic-counter scaling. */
+sikv_status sikv_stream_copy(void *dst, const void *src, size_t bytes, void *stream);
+
+/*
+ * Kernel timing (process-wide, for benchmarks).  While enabled, every kernel
+ * the library launches is bracketed by HIP events recorded with the launch
+ * itself; sikv_timing_read synchronises on them and returns, per kernel id
+ * (0 <= id < sikv_timing_count()), the number of launches and their summed
+ * duration in milliseconds since the last reset.  Not meant for concurrent use
+ * from several threads.
+ */
+sikv_status sikv_timing_enable(int32_t on);
+sikv_status sikv_timing_reset(void);
+int32_t sikv_timing_count(void);
+const char *sikv_timing_name(int32_t id);
+sikv_status sikv_timing_read(int32_t id, int64_t *launches, double *total_ms);
+
+/* Test hook: when on, score_topk ignores its sampled threshold and always
+ * takes its exact whole-head selection path (same result, slower). */
+sikv_status sikv_debug_force_exact_select(int32_t on);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SIKV_H */

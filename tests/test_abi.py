@@ -1,0 +1,172 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/sikv.h declares, its descriptor layout matches, and host-side argument
+validation rejects bad calls before anything is launched.
+
+Every call below is invalid by construction (it fails a host check), so no
+kernel is ever launched and the fake device addresses are never dereferenced.
+"""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sikv.h")
+
+sk = pytest.importorskip("bit_self_indexed_amd")
+from bit_self_indexed_amd import _abi  # noqa: E402
+
+lib = sk.lib
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = 0, -1, -2, -3, -4
+FAKE = 0x10000000  # 256-byte aligned fake device address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^[a-z_0-9 ]+\**\s*\**(sikv_\w+)\(", text, re.M)))
+
+
+def test_header_functions_are_exported_and_declared():
+    names = declared_functions()
+    assert "sikv_encode" in names and "sikv_decode_step" in names
+    assert set(names) == set(_abi.SIGNATURES)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_desc_layout():
+    assert lib.sikv_abi_version() == _abi.ABI_VERSION
+    assert lib.sikv_desc_size() == C.sizeof(_abi.CacheDesc) == 96
+    offs = {f[0]: getattr(_abi.CacheDesc, f[0]).offset for f in _abi.CacheDesc._fields_}
+    assert offs["codes"] == 24 and offs["v"] == 56 and offs["v_stride_t"] == 80
+    assert offs["codebook"] == 88
+
+
+def test_status_strings():
+    for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, HIP):
+        s = lib.sikv_status_str(code).decode()
+        assert s and s != "unknown status"
+    assert lib.sikv_status_str(-99).decode() == "unknown status"
+
+
+def desc(**kw):
+    d = _abi.CacheDesc()
+    d.batch, d.n_kv_heads, d.head_dim, d.capacity, d.n_tokens, d.n_sink = 2, 2, 128, 1000, 900, 64
+    d.codes, d.alpha, d.mu, d.k_sink = FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000
+    d.v, d.v_stride_b, d.v_stride_h, d.v_stride_t = FAKE + 0x400000, 2 * 1000 * 128, 1000 * 128, 128
+    d.codebook = None
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def score(d, q=FAKE, hq=4, k=16, idx=FAKE, ws=None, wsn=0):
+    return lib.sikv_score_topk(C.byref(d), q, hq, k, idx, None, ws, wsn, None)
+
+
+def test_workspace_sizes():
+    d = desc()
+    assert lib.sikv_workspace_bytes(0, C.byref(d), 1, 1) > 0
+    s1 = lib.sikv_workspace_bytes(1, C.byref(d), 4, 16)
+    s2 = lib.sikv_workspace_bytes(2, C.byref(d), 4, 16)
+    s3 = lib.sikv_workspace_bytes(3, C.byref(d), 4, 16)
+    assert s1 > 0 and s2 > 0 and s3 >= s1 + s2
+    assert lib.sikv_workspace_bytes(1, C.byref(d), 3, 16) == 0          # Hq % Hkv
+    assert lib.sikv_workspace_bytes(1, C.byref(d), 4, 837) == 0         # k > N - 64
+    assert lib.sikv_workspace_bytes(9, C.byref(d), 4, 16) == 0          # bad op
+    assert lib.sikv_workspace_bytes(1, None, 4, 16) == 0
+    big = desc(capacity=600000, n_tokens=524288, batch=1, n_kv_heads=8)
+    assert lib.sikv_workspace_bytes(3, C.byref(big), 40, 4096) > 0
+    assert lib.sikv_dense_workspace_bytes(4, 8, 32, 131072) > 0
+    assert lib.sikv_dense_workspace_bytes(4, 8, 30, 131072) == 0
+
+
+@pytest.mark.parametrize("field,value,expect", [
+    ("head_dim", 64, UNSUPPORTED),
+    ("n_sink", 32, UNSUPPORTED),
+    ("codebook", FAKE, UNSUPPORTED),
+    ("n_tokens", 64, INVALID),
+    ("n_tokens", 1001, INVALID),
+    ("batch", 0, INVALID),
+    ("codes", None, INVALID),
+    ("codes", FAKE + 8, INVALID),
+    ("mu", FAKE + 4, INVALID),
+    ("alpha", FAKE + 2, INVALID),
+])
+def test_descriptor_validation(field, value, expect):
+    d = desc(**{field: value})
+    assert score(d) == expect
+
+
+def test_query_validation():
+    d = desc()
+    assert score(d, q=None) == INVALID
+    assert score(d, q=FAKE + 2) == INVALID
+    assert score(d, hq=3) == INVALID           # not a multiple of Hkv
+    assert score(d, hq=18) == UNSUPPORTED      # G = 9
+    assert score(d, k=0) == INVALID
+    assert score(d, k=837) == INVALID          # N - 64 = 836
+    assert score(d, idx=None) == INVALID
+    assert score(d) == WORKSPACE               # no workspace
+    need = lib.sikv_workspace_bytes(1, C.byref(d), 4, 16)
+    assert score(d, ws=FAKE, wsn=need - 1) == WORKSPACE
+    assert score(d, ws=FAKE + 64, wsn=need) == WORKSPACE   # misaligned
+
+
+def test_attention_and_decode_validation():
+    d = desc()
+    nd = desc(v=None)
+    sd = desc(v_stride_t=100)
+    f = C.c_float
+    for dd in (nd, sd):
+        assert lib.sikv_sparse_attn(C.byref(dd), FAKE, 4, FAKE, 16, f(0.088), FAKE, FAKE, 1 << 30,
+                                    None) == INVALID
+        assert lib.sikv_decode_step(C.byref(dd), FAKE, 4, 16, f(0.088), None, FAKE, FAKE, 1 << 30,
+                                    None) == INVALID
+    assert lib.sikv_sparse_attn(C.byref(d), FAKE, 4, FAKE, 16, f(float("nan")), FAKE, FAKE,
+                                1 << 30, None) == INVALID
+    assert lib.sikv_sparse_attn(C.byref(d), FAKE, 4, None, 16, f(0.088), FAKE, FAKE, 1 << 30,
+                                None) == INVALID
+    assert lib.sikv_decode_step(C.byref(d), FAKE, 4, 16, f(0.088), None, None, FAKE, 1 << 30,
+                                None) == INVALID
+    need = lib.sikv_workspace_bytes(3, C.byref(d), 4, 16)
+    assert lib.sikv_decode_step(C.byref(d), FAKE, 4, 16, f(0.088), None, FAKE, FAKE, need - 256,
+                                None) == WORKSPACE
+
+
+def test_encode_validation():
+    d = desc()
+    e = lib.sikv_encode
+    assert e(C.byref(d), None, 0, 0, 128, 0, 900, 1, FAKE, 1 << 30, None) == INVALID
+    assert e(C.byref(d), FAKE + 2, 0, 0, 128, 0, 900, 1, FAKE, 1 << 30, None) == INVALID
+    assert e(C.byref(d), FAKE, 0, 0, 100, 0, 900, 1, FAKE, 1 << 30, None) == INVALID  # stride
+    assert e(C.byref(d), FAKE, 0, 0, 128, 1, 900, 1, FAKE, 1 << 30, None) == INVALID  # t_begin
+    assert e(C.byref(d), FAKE, 0, 0, 128, 0, 899, 1, FAKE, 1 << 30, None) == INVALID  # t_end != N
+    assert e(C.byref(d), FAKE, 0, 0, 128, 0, 900, 2, FAKE, 1 << 30, None) == INVALID
+    assert e(C.byref(d), FAKE, 0, 0, 128, 0, 900, 1, None, 0, None) == WORKSPACE
+    assert e(C.byref(d), FAKE, 0, 0, 128, 900, 1001, 0, None, 0, None) == INVALID     # > capacity
+    assert e(C.byref(d), FAKE, 0, 0, 128, 900, 900, 0, None, 0, None) == INVALID      # empty
+
+
+def test_dense_and_copy_validation():
+    f = C.c_float
+    assert lib.sikv_dense_attn(1, 2, 3, 100, FAKE, FAKE, 0, 0, 128, FAKE, 0, 0, 128, f(0.1), FAKE,
+                               FAKE, 1 << 30, None) == INVALID
+    assert lib.sikv_dense_attn(1, 1, 9, 100, FAKE, FAKE, 0, 0, 128, FAKE, 0, 0, 128, f(0.1), FAKE,
+                               FAKE, 1 << 30, None) == UNSUPPORTED
+    assert lib.sikv_dense_attn(1, 1, 4, 100, FAKE, FAKE, 0, 0, 128, FAKE, 0, 0, 128, f(0.1), FAKE,
+                               None, 0, None) == WORKSPACE
+    assert lib.sikv_stream_copy(FAKE, FAKE, 17, None) == INVALID
+    assert lib.sikv_stream_copy(None, FAKE, 16, None) == INVALID
+
+
+def test_timing_facility_without_launches():
+    assert lib.sikv_timing_count() >= 10
+    names = [lib.sikv_timing_name(i).decode() for i in range(lib.sikv_timing_count())]
+    assert "score" in names and "attn" in names
+    assert lib.sikv_timing_reset() == OK
+    n, ms = C.c_int64(), C.c_double()
+    assert lib.sikv_timing_read(0, C.byref(n), C.byref(ms)) == OK and n.value == 0
+    assert lib.sikv_timing_read(99, C.byref(n), C.byref(ms)) == INVALID
