@@ -1,0 +1,331 @@
+"""Benchmark of the self-indexing compressed-key decode path on one MI355X.
+
+A step is one decode step of one layer: append-encode of the current token
+(its key row, frozen channel mean) then sikv_decode_step (selection-query LUT,
+LUT-GEMV score of every cached token, exact top-k, fused dequant attention
+over sinks + top-k).  Steps rotate over --layers independent layer caches so
+that the working set (layers x ~174 MB at 128K context) is far larger than
+the 256 MB Infinity Cache: every step reads its cache from HBM, as in a real
+multi-layer decode.  Each layer's step is captured once in a HIP graph and
+replayed (eager timing is reported too).
+
+Prints one JSON line (see `report`).  Inputs are seeded synthetic data of the
+evaluated models' decode-layer shapes; no weights or datasets.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "cached tokens scored/s + decode-step µs at 128K ctx; % of HBM roofline"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=400)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", default="long_128k")
+    p.add_argument("--layers", type=int, default=8)
+    p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-dense", action="store_true", help="skip the dense bf16 comparator")
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    return p.parse_args()
+
+
+# ----------------------------------------------------------------------------- bytes
+def algorithmic_bytes(w, kernel: str) -> float:
+    """Bytes the method must move per launch of `kernel` (reads + writes)."""
+    BH = w.batch * w.n_kv_heads
+    n = w.n_tokens - 64
+    k = w.top_k
+    if kernel == "score":           # 16-byte code + 4-byte scale per candidate
+        return 20.0 * BH * n
+    if kernel == "attn":            # idx + code + scale + V row per selected token,
+        per_head = k * (4 + 16 + 4 + 256) + 64 * 512 + 512     # sinks K+V, mean
+        return BH * per_head + w.batch * w.n_q_heads * 256       # queries
+    if kernel == "select":          # selection written
+        return 4.0 * BH * k
+    if kernel == "codes":           # append: one key row in, code + scale out
+        return BH * (256 + 20.0)
+    if kernel == "step":
+        return (algorithmic_bytes(w, "score") + algorithmic_bytes(w, "attn")
+                + algorithmic_bytes(w, "select") + algorithmic_bytes(w, "codes")
+                + w.batch * w.n_q_heads * 512)                   # output fp32
+    raise KeyError(kernel)
+
+
+def source_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, "bit_self_indexed_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+        ent = data["kernels"][kernel]
+        if ent.get("source_hash") != source_hash(ent["sources"]):
+            return None
+        return float(ent["hbm_bytes_per_launch"])
+    except Exception:  # malformed summary: report nothing rather than a wrong number
+        return None
+
+
+# ----------------------------------------------------------------------------- CPU
+def cpu_baseline(w, d, budget_s: float):
+    """The oracle as it stands, single-threaded BLAS, timed on a bounded sample of
+    (batch, KV head) pairs at the full context length."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:
+        threadpool_limits = None
+    pairs = [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)]
+    done, t_dec = 0, 0.0
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    try:
+        for b, h in pairs:
+            e = O.encode(d["K"][b:b + 1, h:h + 1], w.n_tokens)
+            enc = {k: v[0, 0] for k, v in e.items()}
+            t0 = time.perf_counter()
+            s = O.head_scores(d["q"], enc["codes"], enc["alpha"], b, h, w.n_kv_heads, w.n_tokens)
+            sel = O.select_topk(s, w.top_k)
+            G = w.group
+            O.sparse_attention(d["q"][b, h * G:(h + 1) * G], sel, enc["k_sink"], enc["codes"],
+                               enc["alpha"], enc["mu"], d["V"][b, h], 1 / math.sqrt(128))
+            t_dec += time.perf_counter() - t0
+            done += 1
+            if t_dec >= budget_s:
+                break
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    return {
+        "value": done * (w.n_tokens - 64) / t_dec,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} of {len(pairs)} (batch, KV head) pairs of {w.name} at full N="
+                  f"{w.n_tokens}: LUT scores + top-k + sparse attention, {t_dec:.1f} s; "
+                  f"encode untimed",
+    }
+
+
+# ----------------------------------------------------------------------------- main
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the path shards by (batch, KV head) with no communication; see the design "
+              f"notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_self_indexed_amd as sk
+    import sikv_synth as S
+
+    w = S.WORKLOADS[args.config]
+    dev = torch.device("cuda:0")
+    log(f"workload {w.name}: {w.description}")
+    t0 = time.time()
+    d = S.draw(w)
+    log(f"inputs drawn in {time.time() - t0:.1f}s")
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    K = up(d["K"])
+    q_all = up(d["q"])
+    N = w.n_tokens
+    L = args.layers
+    sm = 1.0 / math.sqrt(128)
+    caches, outs, idxs = [], [], []
+    stream = torch.cuda.current_stream(dev)
+    for layer in range(L):
+        V = up(d["V"])
+        c = sk.Cache(w.batch, w.n_kv_heads, N, device=dev, v=V)
+        sk.sikv_encode(c, K[:, :, :N - 1])                     # prefill (mean frozen here)
+        caches.append(c)
+        outs.append(torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev))
+        idxs.append(torch.empty((w.batch, w.n_kv_heads, w.top_k), dtype=torch.int32, device=dev))
+        if layer == 0:
+            log("layer 0 cache encoded")
+    torch.cuda.synchronize()
+    k_new = K[:, :, N - 1:N]
+
+    def step(layer):
+        c = caches[layer]
+        sk.sikv_encode(c, k_new, t_begin=N - 1, recompute_mu=False)
+        sk.sikv_decode_step(c, q_all, w.top_k, sm, idx_out=idxs[layer], out=outs[layer])
+
+    for i in range(max(args.warmup, L)):
+        step(i % L)
+    torch.cuda.synchronize()
+    log("warm-up done")
+
+    # eager timing
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(args.steps):
+        step(i % L)
+    ev1.record()
+    torch.cuda.synchronize()
+    eager_ms = ev0.elapsed_time(ev1) / args.steps
+
+    # graph timing
+    graph_ms = None
+    if not args.no_graph:
+        graphs = []
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for layer in range(L):
+                step(layer)
+        torch.cuda.synchronize()
+        for layer in range(L):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(layer)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        ref_out = outs[0].clone()
+        for i in range(args.warmup):
+            graphs[i % L].replay()
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(args.steps):
+            graphs[i % L].replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        graph_ms = ev0.elapsed_time(ev1) / args.steps
+        if not torch.equal(ref_out, outs[0]):
+            raise RuntimeError("graph replay output differs from the eager step")
+        log(f"eager {eager_ms * 1e3:.1f} us/step, graph {graph_ms * 1e3:.1f} us/step")
+    ms = graph_ms if graph_ms is not None else eager_ms
+
+    # per-kernel durations (event-bracketed launches, eager, same rotation)
+    sk.timing_reset()
+    sk.timing_enable(True)
+    for i in range(args.steps):
+        step(i % L)
+    torch.cuda.synchronize()
+    kt = sk.timing_read()
+    sk.timing_enable(False)
+    kern_us = {name: 1e3 * tot / n for name, (n, tot) in kt.items() if n}
+    per_step_us = {name: 1e3 * tot / args.steps for name, (n, tot) in kt.items() if n}
+    dominant = max(("score", "attn"), key=lambda n: per_step_us.get(n, 0.0))
+    dom_bytes = algorithmic_bytes(w, dominant)
+    achieved = dom_bytes / (kern_us[dominant] * 1e-6) / 1e9
+    traffic = measured_traffic(dominant, w.name)
+    log("kernel avg us:", {k: round(v, 2) for k, v in kern_us.items()})
+
+    # prefill encode (1 layer, full K), for context
+    sk.timing_reset()
+    sk.timing_enable(True)
+    enc_c = sk.Cache(w.batch, w.n_kv_heads, N, device=dev, v=None)
+    for _ in range(3):
+        sk.sikv_encode(enc_c, K)
+    torch.cuda.synchronize()
+    et = sk.timing_read()
+    sk.timing_enable(False)
+    enc_us = sum(1e3 * tot / 3 for name, (n, tot) in et.items() if name in ("mu_partial", "mu_final", "codes") and n)
+    del enc_c
+
+    # dense bf16 comparator over the same (uncompressed) cache
+    dense_us = None
+    if not args.no_dense:
+        Vd = caches[0].v
+        ws = sk.Workspace(dev)
+        out_d = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            sk.sikv_dense_attn(q_all, K, Vd, sm, out=out_d, ws=ws)
+        torch.cuda.synchronize()
+        reps = 20
+        ev0.record()
+        for _ in range(reps):
+            sk.sikv_dense_attn(q_all, K, Vd, sm, out=out_d, ws=ws)
+        ev1.record()
+        torch.cuda.synchronize()
+        dense_us = ev0.elapsed_time(ev1) * 1e3 / reps
+        log(f"dense bf16 {dense_us:.1f} us")
+
+    cpu = None
+    if not args.no_cpu:
+        log("timing the CPU oracle")
+        cpu = cpu_baseline(w, d, args.cpu_seconds)
+
+    step_us = ms * 1e3
+    scored = w.batch * w.n_kv_heads * (w.n_tokens - 64)
+    report = {
+        "metric": METRIC,
+        "value": scored / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads,
+            "n_kv_heads": w.n_kv_heads, "head_dim": 128, "n_tokens": w.n_tokens,
+            "top_k": w.top_k, "n_sink": 64, "layers_rotated": L,
+            "timing": "hip graph replay" if graph_ms is not None else "eager",
+        },
+        "decode_step_us": step_us,
+        "decode_step_us_eager": eager_ms * 1e3,
+        "step_algorithmic_bytes": algorithmic_bytes(w, "step"),
+        "step_hbm_frac": algorithmic_bytes(w, "step") / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "kernel_avg_us": kern_us,
+        "score_topk_us": sum(kern_us.get(n, 0.0) for n in ("sample", "score", "select")),
+        "score_topk_hbm_frac": (algorithmic_bytes(w, "score") + algorithmic_bytes(w, "select"))
+        / (sum(kern_us.get(n, 0.0) for n in ("sample", "score", "select")) * 1e-6) / 1e9
+        / HBM_PEAK_GBS,
+        "encode_prefill_us": enc_us,
+        "dense_bf16_us": dense_us,
+        "speedup_vs_dense": (dense_us / step_us) if dense_us else None,
+        "roofline": {
+            "kernel": dominant,
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(report), flush=True)
+
+
+if __name__ == "__main__":
+    main()
