@@ -229,6 +229,20 @@ def main():
         log(f"eager {eager_ms * 1e3:.1f} us/step, graph {graph_ms * 1e3:.1f} us/step")
     ms = graph_ms if graph_ms is not None else eager_ms
 
+    # reference copy of a known size (bandwidth; scales hardware traffic counters)
+    copy_bytes = 512 << 20
+    src = torch.empty(copy_bytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    sk.sikv_stream_copy(dst, src)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(5):
+        sk.sikv_stream_copy(dst, src)
+    ev1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * copy_bytes * 5 / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    del src, dst
+
     # per-kernel durations (event-bracketed launches, eager, same rotation)
     sk.timing_reset()
     sk.timing_enable(True)
@@ -306,11 +320,12 @@ def main():
         "step_algorithmic_bytes": algorithmic_bytes(w, "step"),
         "step_hbm_frac": algorithmic_bytes(w, "step") / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "kernel_avg_us": kern_us,
-        "score_topk_us": sum(kern_us.get(n, 0.0) for n in ("sample", "score", "select")),
+        "score_topk_us": sum(kern_us.get(n, 0.0) for n in ("prep", "score", "select")),
         "score_topk_hbm_frac": (algorithmic_bytes(w, "score") + algorithmic_bytes(w, "select"))
-        / (sum(kern_us.get(n, 0.0) for n in ("sample", "score", "select")) * 1e-6) / 1e9
+        / (sum(kern_us.get(n, 0.0) for n in ("prep", "score", "select")) * 1e-6) / 1e9
         / HBM_PEAK_GBS,
         "encode_prefill_us": enc_us,
+        "copy_kernel_gbs": copy_gbs,
         "dense_bf16_us": dense_us,
         "speedup_vs_dense": (dense_us / step_us) if dense_us else None,
         "roofline": {

@@ -16,7 +16,7 @@ namespace {
 using namespace sikv;
 
 constexpr size_t kAlign = 256;
-constexpr int kMaxChunks = 4096;
+constexpr int kMaxChunks = 2048;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -30,12 +30,13 @@ struct EncodePlan {
 
 struct ScorePlan {
   int chunk, n_chunks;
-  size_t off_tau, off_cnt, off_ckey, off_ct, off_pkey, off_pt, bytes;
+  size_t off_tau, off_cnt, off_ckey, off_ct, off_pkey, off_pt, off_tab, off_inv, off_lut, off_qmu;
+  size_t bytes;
 };
 
 struct AttnPlan {
   int split, n_splits;
-  size_t off_o, off_ml, bytes;
+  size_t off_o, off_ml, off_lut, off_qmu, bytes;
 };
 
 struct DecodePlan {
@@ -54,7 +55,7 @@ EncodePlan plan_encode(const sikv_cache_desc* c) {
 // Tile of the score kernel: 256*U candidates per block, the largest U in
 // {8,4,2,1} that still gives >= 1024 blocks (4 per CU), widened if the tile
 // count would exceed what the select kernel keeps in LDS.
-bool plan_score(const sikv_cache_desc* c, ScorePlan* p) {
+bool plan_score(const sikv_cache_desc* c, int n_q_heads, ScorePlan* p) {
   const int64_t BH = (int64_t)c->batch * c->n_kv_heads;
   const int64_t n = (int64_t)c->n_tokens - kSink;
   int U = 1;
@@ -76,12 +77,17 @@ bool plan_score(const sikv_cache_desc* c, ScorePlan* p) {
   p->off_ct = o;   o += align_up(cap * sizeof(int32_t));
   p->off_pkey = o; o += align_up(cap * sizeof(uint32_t));
   p->off_pt = o;   o += align_up(cap * sizeof(int32_t));
+  p->off_tab = o;  o += align_up((size_t)BH * kLut * sizeof(int32_t));
+  p->off_inv = o;  o += align_up((size_t)BH * sizeof(float));
+  p->off_lut = o;  o += align_up((size_t)c->batch * n_q_heads * kLut * sizeof(float));
+  p->off_qmu = o;  o += align_up((size_t)c->batch * n_q_heads * sizeof(float));
   p->bytes = o;
   return true;
 }
 
 // Entries of the attended list (64 sinks + k) per block: the largest of
-// 256/128/64 that still gives >= 1024 blocks.
+// 256/128/64 that still gives >= 1024 blocks.  Workspace: split partials (o,
+// max, sum) and, for a standalone call, the query heads' tables.
 void plan_attn(const sikv_cache_desc* c, int n_q_heads, int top_k, AttnPlan* p) {
   const int64_t BH = (int64_t)c->batch * c->n_kv_heads;
   const int64_t L = (int64_t)kSink + top_k;
@@ -92,11 +98,13 @@ void plan_attn(const sikv_cache_desc* c, int n_q_heads, int top_k, AttnPlan* p) 
   const size_t rows = (size_t)c->batch * n_q_heads * p->n_splits;
   p->off_o = 0;
   p->off_ml = align_up(rows * kD * sizeof(float));
-  p->bytes = p->off_ml + align_up(rows * 2 * sizeof(float));
+  p->off_lut = p->off_ml + align_up(rows * 2 * sizeof(float));
+  p->off_qmu = p->off_lut + align_up((size_t)c->batch * n_q_heads * kLut * sizeof(float));
+  p->bytes = p->off_qmu + align_up((size_t)c->batch * n_q_heads * sizeof(float));
 }
 
 bool plan_decode(const sikv_cache_desc* c, int n_q_heads, int top_k, DecodePlan* p) {
-  if (!plan_score(c, &p->sp)) return false;
+  if (!plan_score(c, n_q_heads, &p->sp)) return false;
   plan_attn(c, n_q_heads, top_k, &p->ap);
   p->off_idx = 0;
   p->off_score = align_up((size_t)c->batch * c->n_kv_heads * top_k * sizeof(int32_t));
@@ -155,6 +163,8 @@ T* at(void* ws, size_t off) {
 
 std::atomic<int> g_force_exact{0};
 
+// prep (tables + threshold) -> score -> select.  The prep kernel also leaves the
+// query heads' attention tables in the workspace for a following attention.
 sikv_status run_score_topk(const sikv_cache_desc* c, const uint16_t* q, int n_q_heads, int top_k,
                            int32_t* idx, float* scores_opt, void* ws, const ScorePlan& sp,
                            hipStream_t s) {
@@ -165,23 +175,39 @@ sikv_status run_score_topk(const sikv_cache_desc* c, const uint16_t* q, int n_q_
   int32_t* ct = at<int32_t>(ws, sp.off_ct);
   uint32_t* pkey = at<uint32_t>(ws, sp.off_pkey);
   int32_t* pt = at<int32_t>(ws, sp.off_pt);
-  SIKV_TRY(launch_sample(q, n_q_heads, B, Hkv, c->codes, c->alpha, c->capacity, c->n_tokens,
-                         top_k, g_force_exact.load(std::memory_order_relaxed), tau, s));
-  SIKV_TRY(launch_score(q, n_q_heads, B, Hkv, c->codes, c->alpha, c->capacity, c->n_tokens, tau,
+  int32_t* tab = at<int32_t>(ws, sp.off_tab);
+  float* inv = at<float>(ws, sp.off_inv);
+  const int mode = g_force_exact.load(std::memory_order_relaxed) ? 2 : 1;
+  SIKV_TRY(launch_prep(q, n_q_heads, B, Hkv, c->mu, c->codes, c->alpha, c->capacity, c->n_tokens,
+                       top_k, mode, tab, inv, at<float>(ws, sp.off_lut), at<float>(ws, sp.off_qmu),
+                       tau, s));
+  SIKV_TRY(launch_score(B, Hkv, c->codes, c->alpha, c->capacity, c->n_tokens, tab, inv, tau,
                         sp.chunk, sp.n_chunks, ckey, ct, cnt, scores_opt, s));
-  SIKV_TRY(launch_select(q, n_q_heads, B, Hkv, c->codes, c->alpha, c->capacity, c->n_tokens, top_k,
+  SIKV_TRY(launch_select(B, Hkv, c->codes, c->alpha, c->capacity, c->n_tokens, tab, inv, top_k,
                          sp.chunk, sp.n_chunks, ckey, ct, cnt, pkey, pt, idx, s));
   return SIKV_OK;
 }
 
+// Attention (+ split merge).  att_lut / att_qmu: the query heads' tables, built
+// here by a prep launch when the caller has none (standalone call).
 sikv_status run_attn(const sikv_cache_desc* c, const uint16_t* q, int n_q_heads,
                      const int32_t* idx, int top_k, float sm_scale, float* out, void* ws,
-                     const AttnPlan& ap, hipStream_t s) {
+                     const AttnPlan& ap, const float* att_lut, const float* att_qmu,
+                     hipStream_t s) {
   float* po = at<float>(ws, ap.off_o);
   float* pml = at<float>(ws, ap.off_ml);
-  SIKV_TRY(launch_attn(q, n_q_heads, c->batch, c->n_kv_heads, c->codes, c->alpha, c->mu, c->k_sink,
-                       c->v, c->v_stride_b, c->v_stride_h, c->v_stride_t, c->capacity, c->n_tokens, idx, top_k,
-                       sm_scale, ap.split, ap.n_splits, po, pml, s));
+  if (att_lut == nullptr) {
+    float* lut = at<float>(ws, ap.off_lut);
+    float* qmu = at<float>(ws, ap.off_qmu);
+    SIKV_TRY(launch_prep(q, n_q_heads, c->batch, c->n_kv_heads, c->mu, c->codes, c->alpha,
+                         c->capacity, c->n_tokens, top_k, 0, nullptr, nullptr, lut, qmu, nullptr,
+                         s));
+    att_lut = lut;
+    att_qmu = qmu;
+  }
+  SIKV_TRY(launch_attn(q, n_q_heads, c->batch, c->n_kv_heads, c->codes, c->alpha, c->k_sink, c->v,
+                       c->v_stride_b, c->v_stride_h, c->v_stride_t, c->capacity, c->n_tokens, idx,
+                       top_k, att_lut, att_qmu, sm_scale, ap.split, ap.n_splits, po, pml, s));
   SIKV_TRY(launch_combine(po, pml, c->batch * n_q_heads, ap.n_splits, out, s));
   return SIKV_OK;
 }
@@ -197,7 +223,7 @@ std::vector<Pending> g_pending;
 std::vector<hipEvent_t> g_pool;
 double g_ms[KID_COUNT];
 int64_t g_cnt[KID_COUNT];
-const char* const g_names[KID_COUNT] = {"mu_partial", "mu_final", "codes", "sample",
+const char* const g_names[KID_COUNT] = {"mu_partial", "mu_final", "codes", "prep",
                                         "score",      "select",   "attn",  "combine",
                                         "dense",      "copy"};
 
@@ -285,7 +311,7 @@ sikv_status sikv_score_topk(const sikv_cache_desc* c, const uint16_t* q, int32_t
   if (st != SIKV_OK) return st;
   if (idx == nullptr || misaligned(idx, 4) || misaligned(scores_opt, 4)) return SIKV_ERR_INVALID_ARG;
   ScorePlan sp;
-  if (!plan_score(c, &sp)) return SIKV_ERR_UNSUPPORTED;
+  if (!plan_score(c, n_q_heads, &sp)) return SIKV_ERR_UNSUPPORTED;
   st = check_ws(ws, ws_bytes, sp.bytes);
   if (st != SIKV_OK) return st;
   return run_score_topk(c, q, n_q_heads, top_k, idx, scores_opt, ws, sp,
@@ -308,7 +334,7 @@ sikv_status sikv_sparse_attn(const sikv_cache_desc* c, const uint16_t* q, int32_
   plan_attn(c, n_q_heads, top_k, &ap);
   st = check_ws(ws, ws_bytes, ap.bytes);
   if (st != SIKV_OK) return st;
-  return run_attn(c, q, n_q_heads, idx, top_k, sm_scale, out, ws, ap,
+  return run_attn(c, q, n_q_heads, idx, top_k, sm_scale, out, ws, ap, nullptr, nullptr,
                   static_cast<hipStream_t>(stream));
 }
 
@@ -329,9 +355,11 @@ sikv_status sikv_decode_step(const sikv_cache_desc* c, const uint16_t* q, int32_
   if (st != SIKV_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t* idx = idx_out_opt ? idx_out_opt : at<int32_t>(ws, dp.off_idx);
-  st = run_score_topk(c, q, n_q_heads, top_k, idx, nullptr, at<char>(ws, dp.off_score), dp.sp, s);
+  char* wsc = at<char>(ws, dp.off_score);
+  st = run_score_topk(c, q, n_q_heads, top_k, idx, nullptr, wsc, dp.sp, s);
   if (st != SIKV_OK) return st;
-  return run_attn(c, q, n_q_heads, idx, top_k, sm_scale, out, at<char>(ws, dp.off_attn), dp.ap, s);
+  return run_attn(c, q, n_q_heads, idx, top_k, sm_scale, out, at<char>(ws, dp.off_attn), dp.ap,
+                  at<float>(wsc, dp.sp.off_lut), at<float>(wsc, dp.sp.off_qmu), s);
 }
 
 size_t sikv_workspace_bytes(int32_t op, const sikv_cache_desc* c, int32_t n_q_heads,
@@ -344,7 +372,7 @@ size_t sikv_workspace_bytes(int32_t op, const sikv_cache_desc* c, int32_t n_q_he
       if (check_query(c, reinterpret_cast<const uint16_t*>(kAlign), n_q_heads, top_k) != SIKV_OK)
         return 0;
       ScorePlan sp;
-      return plan_score(c, &sp) ? sp.bytes : 0;
+      return plan_score(c, n_q_heads, &sp) ? sp.bytes : 0;
     }
     case SIKV_OP_SPARSE_ATTN: {
       if (check_query(c, reinterpret_cast<const uint16_t*>(kAlign), n_q_heads, top_k) != SIKV_OK)

@@ -7,12 +7,17 @@
 // decoding the keys; the top-k tokens are then selected.
 //
 // Three kernels per decode step, all exact:
-//   sample  - one block per (b, h): scores a fixed, evenly spaced sample of the
-//             candidates and takes a conservative threshold tau below the
-//             expected k-th score (the whole candidate set when it is small);
+//   prep    - one block per (b, h): builds the selection query's table (the
+//             16-entry table of each 4-dim sub-vector, in int32 fixed point so
+//             that a token's 32 look-ups are summed exactly with 3-input integer
+//             adds), the attention tables of the G query heads and their q.mu;
+//             then scores a fixed, evenly spaced sample of the candidates and
+//             takes a conservative threshold tau below the expected k-th score
+//             (the whole candidate set when it is small);
 //   score   - the HBM stream: 16-byte code + 4-byte scale per token, one lane per
-//             token, table in LDS; tokens with score >= tau are written, in token
-//             order, to a per-tile slot (no atomics, no global sort);
+//             token, 2 KB table in LDS (16-entry look-ups never conflict in the
+//             LDS banks); tokens with score >= tau are written, in token order,
+//             to a per-tile slot (no atomics);
 //   select  - one block per (b, h): radix select of the exact k-th largest over
 //             the candidates, then an ordered compaction (ascending positions,
 //             ties to the smaller position).  If fewer than k candidates passed
@@ -26,15 +31,16 @@ namespace sikv {
 
 namespace {
 
-constexpr int kSampleMax = 4096;     // sampled candidates per head
-constexpr int kSampleRun = 256;      // contiguous tokens per sample stratum
-constexpr int kSelectLds = 12288;    // candidates kept in LDS by select
-constexpr int kMaxChunks = 4096;
+constexpr int kSampleMax = 4096;   // sampled candidates per head
+constexpr int kSampleRun = 256;    // contiguous tokens per sample stratum
+constexpr int kSelectLds = 16384;  // candidates kept in LDS by select
+constexpr int kMaxChunks = 2048;
+constexpr int kSubMax = 1024;
 
 // ------------------------------------------------------------------ block helpers
-// Exclusive prefix sum of one int per thread over the block (blockDim multiple
-// of 64, at most 1024).  tmp: LDS, >= 17 ints.  Returns the exclusive sum and
-// writes the block total to *total.  Contains barriers.
+// Exclusive prefix sum of one int per thread over the block (blockDim a multiple
+// of 64, at most 1024).  tmp: LDS, >= 17 ints.  Returns the exclusive sum and the
+// block total.  Three barriers.
 __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
@@ -46,14 +52,16 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
   }
   if (lane == 63) tmp[wave] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int w = 0; w < nw; ++w) {
-      const int c = tmp[w];
-      tmp[w] = run;
-      run += c;
+  if (wave == 0) {
+    const int t = lane < nw ? tmp[lane] : 0;
+    int y = t;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const int z = __shfl_up(y, o);
+      if (lane >= o) y += z;
     }
-    tmp[16] = run;
+    if (lane < nw) tmp[lane] = y - t;
+    if (lane == nw - 1) tmp[16] = y;
   }
   __syncthreads();
   const int r = tmp[wave] + x - v;
@@ -100,194 +108,311 @@ struct Kth {
   int need;      // keys equal to it that belong to the top k (>= 1)
 };
 
-// k-th largest of n keys (1 <= k <= n) held at `keys` (LDS or global), all in
-// [lo, hi].  Radix select on key - lo, 11-bit digits from the highest bit that
-// varies, LDS histograms.  hist: LDS >= 2048 uint32; tmp: LDS >= 20 ints.
-__device__ Kth block_kth_largest(const uint32_t* keys, int n, int k, uint32_t lo, uint32_t hi,
-                                 uint32_t* hist, int* tmp) {
+// One radix round: among the keys whose bits of (key - lo) above `top` equal
+// those of `prefix`, histogram the next digit (<= 11 bits, ending at `shift`)
+// and find the digit holding the k-th largest of them.  hist: LDS >= 2048;
+// tmp: LDS >= 24 ints.  Returns (digit, count in larger digits, count in it).
+struct Round {
+  int digit, above, count, shift;
+};
+
+__device__ __forceinline__ Round block_round(const uint32_t* keys, int n, int k, uint32_t lo,
+                                             int top, uint32_t prefix, uint32_t* hist, int* tmp) {
+  const int width = top < 11 ? top : 11;
+  const int shift = top - width;
+  const int nb = 1 << width;
+  for (int i = threadIdx.x; i < nb; i += blockDim.x) hist[i] = 0u;
+  __syncthreads();
+  const uint64_t want = (uint64_t)prefix >> top;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const uint32_t r = keys[i] - lo;
+    if (((uint64_t)r >> top) == want) atomicAdd(&hist[(r >> shift) & (uint32_t)(nb - 1)], 1u);
+  }
+  __syncthreads();
+  const int per = (nb + blockDim.x - 1) / blockDim.x;
+  const int d0 = threadIdx.x * per;
+  int cnt = 0;
+  for (int d = d0; d < d0 + per && d < nb; ++d) cnt += (int)hist[d];
+  int total;
+  int pre = block_excl_scan(cnt, tmp, &total);
+  const int x = total - k;  // ascending rank of the k-th largest among the matched
+  for (int d = d0; d < d0 + per && d < nb; ++d) {
+    const int c = (int)hist[d];
+    if (pre <= x && x < pre + c) {
+      tmp[18] = d;
+      tmp[19] = total - (pre + c);
+      tmp[20] = c;
+    }
+    pre += c;
+  }
+  __syncthreads();
+  const Round r{tmp[18], tmp[19], tmp[20], shift};
+  __syncthreads();
+  return r;
+}
+
+// Exact k-th largest of n keys in [lo, hi] (1 <= k <= n).  The first round runs
+// over all keys; the keys of its boundary digit (usually few) are then copied to
+// `sub` (LDS) and the remaining rounds run over them only.
+__device__ Kth block_kth(const uint32_t* keys, int n, int k, uint32_t lo, uint32_t hi,
+                         uint32_t* hist, int* tmp, uint32_t* sub, int* scount) {
   const uint32_t span = hi - lo;
   int top = span ? 32 - __clz(span) : 0;
   uint32_t prefix = 0;
   int need = k, above = 0;
+  const uint32_t* src = keys;
+  int ns = n;
+  bool first = true;
   while (top > 0) {
-    const int width = top < 11 ? top : 11;
-    const int shift = top - width;
-    const int nb = 1 << width;
-    for (int i = threadIdx.x; i < nb; i += blockDim.x) hist[i] = 0u;
-    __syncthreads();
-    const uint64_t want = (uint64_t)prefix >> top;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-      const uint32_t r = keys[i] - lo;
-      if (((uint64_t)r >> top) == want) atomicAdd(&hist[(r >> shift) & (uint32_t)(nb - 1)], 1u);
-    }
-    __syncthreads();
-    // Bins of this thread: a contiguous run, scanned in ascending digit order.
-    const int per = (nb + blockDim.x - 1) / blockDim.x;
-    const int d0 = threadIdx.x * per;
-    int cnt = 0;
-    for (int d = d0; d < d0 + per && d < nb; ++d) cnt += (int)hist[d];
-    int total;
-    int pre = block_excl_scan(cnt, tmp, &total);
-    // The digit holding the element of ascending rank x = total - need.
-    const int x = total - need;
-    for (int d = d0; d < d0 + per && d < nb; ++d) {
-      const int c = (int)hist[d];
-      if (pre <= x && x < pre + c) {
-        tmp[18] = d;
-        tmp[19] = total - (pre + c);  // elements in larger digits
+    const Round r = block_round(src, ns, need, lo, top, prefix, hist, tmp);
+    above += r.above;
+    need -= r.above;
+    prefix |= (uint32_t)r.digit << r.shift;
+    top = r.shift;
+    if (first && top > 0 && r.count <= kSubMax) {
+      if (threadIdx.x == 0) *scount = 0;
+      __syncthreads();
+      const uint64_t want = (uint64_t)prefix >> top;
+      for (int i = threadIdx.x; i < ns; i += blockDim.x) {
+        const uint32_t key = src[i];
+        if (((uint64_t)(key - lo) >> top) == want) sub[atomicAdd(scount, 1)] = key;
       }
-      pre += c;
+      __syncthreads();
+      src = sub;
+      ns = r.count;
     }
-    __syncthreads();
-    const int dsel = tmp[18];
-    above += tmp[19];
-    need -= tmp[19];
-    prefix |= (uint32_t)dsel << shift;
-    top = shift;
-    __syncthreads();
+    first = false;
   }
   return Kth{lo + prefix, above, need};
 }
 
-// Writes the selected positions of keys[0..n) (in list order, which is ascending
-// position) to out: every key > kth, and the first `need` keys == kth.
-__device__ void block_emit_selected(const uint32_t* keys, const int32_t* pos, int n, int k, Kth r,
-                                    int32_t* __restrict__ out, int* tmp) {
-  int run_gt = 0, run_eq = 0;
-  for (int base = 0; base < n; base += blockDim.x) {
-    const int i = base + threadIdx.x;
-    int gt = 0, eq = 0;
-    if (i < n) {
-      const uint32_t kk = keys[i];
-      gt = kk > r.key;
-      eq = kk == r.key;
-    }
-    int total;
-    const int ex = block_excl_scan((gt << 16) | eq, tmp, &total);
-    const int gt_before = run_gt + (ex >> 16);
-    const int eq_before = run_eq + (ex & 0xffff);
-    const int p = gt_before + min(eq_before, r.need);
-    if ((gt || (eq && eq_before < r.need)) && p < k) out[p] = pos[i];
-    run_gt += total >> 16;
-    run_eq += total & 0xffff;
+// Writes the positions of the selected keys (all keys > kth, then the first
+// `need` keys == kth in list order) to out, in list order (= ascending
+// position).  Each thread owns a contiguous run of the list.
+__device__ void block_emit(const uint32_t* keys, const int32_t* pos, int n, int k, Kth r,
+                           int32_t* __restrict__ out, int* tmp) {
+  const int per = (n + blockDim.x - 1) / blockDim.x;
+  const int i0 = threadIdx.x * per, i1 = min(n, i0 + per);
+  int gt = 0, eq = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t kk = keys[i];
+    gt += kk > r.key;
+    eq += kk == r.key;
+  }
+  int tg, te;
+  const int gt_before = block_excl_scan(gt, tmp, &tg);
+  int eq_before = block_excl_scan(eq, tmp, &te);
+  int o = gt_before + min(eq_before, r.need);
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t kk = keys[i];
+    bool take = kk > r.key;
+    if (kk == r.key) take = eq_before++ < r.need;
+    if (take && o < k) out[o++] = pos[i];
   }
 }
 
-// ------------------------------------------------------------------ sample
-__global__ __launch_bounds__(1024) void sample_kernel(const uint16_t* __restrict__ q, int n_q_heads,
-                                                      int Hkv, int G, const uint8_t* __restrict__ codes,
-                                                      const float* __restrict__ alpha, int capacity,
-                                                      int n_tokens, int rank, int force_exact,
-                                                      float* __restrict__ tau) {
-  __shared__ float qbar[kD];
-  __shared__ float lut[kLut];
+// Copies the selection table of one head from global memory into LDS (2 KB).
+// No barrier.
+__device__ __forceinline__ void load_itab(const int* __restrict__ gtab, int* itab) {
+  const int4* src = reinterpret_cast<const int4*>(gtab);
+  int4* dst = reinterpret_cast<int4*>(itab);
+  for (int i = threadIdx.x; i < kLut / 4; i += blockDim.x) dst[i] = src[i];
+}
+
+// ------------------------------------------------------------------ prep
+// mode 0: attention tables only (sel_tab and tau unused); 1: all tables +
+// sampled threshold; 2: all tables + tau = +inf (forces the exact whole-head
+// selection).
+__global__ __launch_bounds__(1024) void prep_kernel(
+    const uint16_t* __restrict__ q, int n_q_heads, int Hkv, int G, const float* __restrict__ mu,
+    const uint8_t* __restrict__ codes, const float* __restrict__ alpha, int capacity, int n_tokens,
+    int rank, int mode, int* __restrict__ sel_lut, float* __restrict__ sel_inv,
+    float* __restrict__ att_lut, float* __restrict__ att_qmu, float* __restrict__ tau) {
+  __shared__ float qv[kMaxGroup + 1][kD];  // q_g, then the selection query (sum)
+  __shared__ int itab[kLut];
+  __shared__ float red_a[16];
   __shared__ uint32_t keys[kSampleMax];
   __shared__ uint32_t hist[2048];
+  __shared__ uint32_t sub[kSubMax];
   __shared__ int tmp[32];
   __shared__ uint32_t mm[32];
+  __shared__ int scount;
   const int bh = blockIdx.x, b = bh / Hkv, h = bh - b * Hkv;
-  if (force_exact) {
-    if (threadIdx.x == 0) tau[bh] = __uint_as_float(0x7f800000u);  // +inf: nothing passes
-    return;
-  }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = n_tokens - kSink;
   const bool full = n <= kSampleMax;
   const int m = full ? n : kSampleMax;
-  if (!full && rank > m) {  // threshold would sit below every sample: keep all
-    if (threadIdx.x == 0) tau[bh] = __uint_as_float(0xff800000u);
+  const bool sample = mode == 1 && (full || rank <= m);
+  const int64_t row0 = (int64_t)bh * capacity;
+
+  // Sample loads first (consumed after the tables are built).
+  constexpr int kPer = kSampleMax / 1024;
+  uint4 c[kPer];
+  float a[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = tid + u * 1024;
+    c[u] = make_uint4(0u, 0u, 0u, 0u);
+    a[u] = 0.0f;
+    if (sample && i < m) {
+      int t;
+      if (full) {
+        t = kSink + i;
+      } else {
+        const int st = i / kSampleRun;
+        const int start = (int)(((int64_t)st * (n - kSampleRun)) / (kSampleMax / kSampleRun - 1));
+        t = kSink + start + (i - st * kSampleRun);
+      }
+      c[u] = *reinterpret_cast<const uint4*>(codes + (row0 + t) * kCodeBytes);
+      a[u] = alpha[row0 + t];
+    }
+  }
+  // Queries of the group and their sum (fp32, g ascending).
+  const uint16_t* qb = q + ((int64_t)b * n_q_heads + (int64_t)h * G) * kD;
+  for (int i = tid; i < G * kD; i += blockDim.x)
+    qv[i / kD][i % kD] = __uint_as_float((uint32_t)qb[i] << 16);
+  __syncthreads();
+  if (tid < kD) {
+    float s = qv[0][tid];
+    for (int g = 1; g < G; ++g) s += qv[g][tid];
+    qv[kMaxGroup][tid] = s;
+  }
+  // Attention tables of the G query heads and their q.mu.
+  const int64_t hq0 = (int64_t)b * n_q_heads + (int64_t)h * G;
+  for (int i = tid; i < G * kLut; i += blockDim.x)
+    att_lut[hq0 * kLut + i] = lut_entry(qv[i / kLut], i % kLut);
+  for (int g = wave; g < G; g += (int)(blockDim.x >> 6)) {
+    const float* mb = mu + (int64_t)bh * kD;
+    float d = fmaf(qv[g][lane], mb[lane], qv[g][lane + 64] * mb[lane + 64]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) d += __shfl_xor(d, o);
+    if (lane == 0) att_qmu[hq0 + g] = d;
+  }
+  __syncthreads();
+  if (mode == 0) return;
+  // Selection table in fixed point: A = sum_c |qbar_c| = m * 2^x (m in [0.5, 1)),
+  // scale 2^(30 - x) so that any sum of 32 entries stays below 2^30 in magnitude.
+  if (wave == 0) {
+    float v = fabsf(qv[kMaxGroup][lane]) + fabsf(qv[kMaxGroup][lane + 64]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    if (lane == 0) red_a[0] = v;
+  }
+  __syncthreads();
+  int ex = 0;
+  if (red_a[0] > 0.0f) {
+    frexpf(red_a[0], &ex);
+    ex = 30 - ex;
+  }
+  for (int e = tid; e < kLut; e += blockDim.x) {
+    const int v = (int)rintf(ldexpf(lut_entry(qv[kMaxGroup], e), ex));
+    itab[e] = v;
+    sel_lut[(int64_t)bh * kLut + e] = v;
+  }
+  const float inv = ldexpf(1.0f, -ex);
+  if (tid == 0) sel_inv[bh] = inv;
+  __syncthreads();
+  if (mode == 2) {
+    if (tid == 0) tau[bh] = __uint_as_float(0x7f800000u);  // +inf: nothing passes
     return;
   }
-  build_selection_lut(q, b, h, n_q_heads, G, qbar, lut);
-  const int64_t row0 = (int64_t)bh * capacity;
+  if (!sample) {  // threshold would sit below every sample: keep all
+    if (tid == 0) tau[bh] = __uint_as_float(0xff800000u);
+    return;
+  }
   uint32_t lo = 0xffffffffu, hi = 0u;
-  for (int i = threadIdx.x; i < m; i += blockDim.x) {
-    int t;
-    if (full) {
-      t = kSink + i;
-    } else {
-      const int sidx = i / kSampleRun;
-      const int start = (int)(((int64_t)sidx * (n - kSampleRun)) / (kSampleMax / kSampleRun - 1));
-      t = kSink + start + (i - sidx * kSampleRun);
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = tid + u * 1024;
+    if (i < m) {
+      const uint32_t key = score_key(selection_score(itab, inv, c[u], a[u]));
+      keys[i] = key;
+      lo = min(lo, key);
+      hi = max(hi, key);
     }
-    const uint4 c = *reinterpret_cast<const uint4*>(codes + (row0 + t) * kCodeBytes);
-    const uint32_t key = score_key(selection_score(lut, c, alpha[row0 + t]));
-    keys[i] = key;
-    lo = min(lo, key);
-    hi = max(hi, key);
   }
   block_minmax(lo, hi, mm, &lo, &hi);
-  const Kth kt = block_kth_largest(keys, m, rank, lo, hi, hist, tmp);
-  if (threadIdx.x == 0) tau[bh] = key_score(kt.key);
+  const Kth kt = block_kth(keys, m, rank, lo, hi, hist, tmp, sub, &scount);
+  if (tid == 0) tau[bh] = key_score(kt.key);
 }
 
 // ------------------------------------------------------------------ score
-// One block per (tile of 256*U candidates, b*h); lane <-> token.  All code and
-// scale loads of the tile are issued before the table is built.
+// One block per (tile of 256*U candidates, b*h); lane <-> token.  Tile base
+// pointers are block-uniform, so every load is a 32-bit lane offset from a
+// scalar base; full tiles load without bounds checks.
 template <int U>
 __global__ __launch_bounds__(256) void score_kernel(
-    const uint16_t* __restrict__ q, int n_q_heads, int Hkv, int G, const uint8_t* __restrict__ codes,
-    const float* __restrict__ alpha, int capacity, int n_tokens, const float* __restrict__ tau,
-    int n_chunks, uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_t,
-    int32_t* __restrict__ chunk_count, float* __restrict__ scores_opt) {
-  __shared__ float qbar[kD];
-  __shared__ float lut[kLut];
-  __shared__ int wcnt[U][4];
+    const uint8_t* __restrict__ codes, const float* __restrict__ alpha, int capacity,
+    int n_tokens, const int* __restrict__ sel_lut, const float* __restrict__ sel_inv,
+    const float* __restrict__ tau, int n_chunks, uint32_t* __restrict__ cand_key,
+    int32_t* __restrict__ cand_t, int32_t* __restrict__ chunk_count,
+    float* __restrict__ scores_opt) {
+  __shared__ int itab[kLut];
+  __shared__ int wcnt[U * 4];
   constexpr int kChunk = 256 * U;
-  const int bh = blockIdx.y, b = bh / Hkv, h = bh - b * Hkv;
+  const int bh = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = kSink + blockIdx.x * kChunk;
-  const int64_t row0 = (int64_t)bh * capacity;
+  const int64_t row0 = (int64_t)bh * capacity + t0;
+  const uint4* __restrict__ cb = reinterpret_cast<const uint4*>(codes) + row0;
+  const float* __restrict__ ab = alpha + row0;
+  const int2 tv = reinterpret_cast<const int2*>(sel_lut + (int64_t)bh * kLut)[tid];
+  const int lim = n_tokens - t0;  // tokens of this tile that exist
   uint4 c[U];
   float a[U];
+  if (lim >= kChunk) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int t = t0 + u * 256 + tid;
-    if (t < n_tokens) {
-      c[u] = *reinterpret_cast<const uint4*>(codes + (row0 + t) * kCodeBytes);
-      a[u] = alpha[row0 + t];
-    } else {
-      c[u] = make_uint4(0u, 0u, 0u, 0u);
-      a[u] = 0.0f;
+    for (int u = 0; u < U; ++u) {
+      c[u] = cb[u * 256 + tid];
+      a[u] = ab[u * 256 + tid];
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = u * 256 + tid;
+      c[u] = i < lim ? cb[i] : make_uint4(0u, 0u, 0u, 0u);
+      a[u] = i < lim ? ab[i] : 0.0f;
     }
   }
-  build_selection_lut(q, b, h, n_q_heads, G, qbar, lut);
+  reinterpret_cast<int2*>(itab)[tid] = tv;
+  const float inv = sel_inv[bh];
   const float th = tau[bh];
+  __syncthreads();
   uint64_t mask[U];
   uint32_t key[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int t = t0 + u * 256 + tid;
-    const float s = selection_score(lut, c[u], a[u]);
-    const bool valid = t < n_tokens;
-    if (scores_opt != nullptr && valid) scores_opt[row0 + t] = s;
+    const int i = u * 256 + tid;
+    const float s = selection_score(itab, inv, c[u], a[u]);
+    if (scores_opt != nullptr && i < lim) scores_opt[row0 + i] = s;
     key[u] = score_key(s);
-    mask[u] = __ballot(valid && s >= th);
-    if (lane == 0) wcnt[u][wave] = __popcll(mask[u]);
+    mask[u] = __ballot(i < lim && s >= th);
+    if (lane == 0) wcnt[u * 4 + wave] = __popcll(mask[u]);
   }
   __syncthreads();
   int run = 0;
   const int64_t slot = ((int64_t)bh * n_chunks + blockIdx.x) * kChunk;
+  uint32_t* __restrict__ kout = cand_key + slot;
+  int32_t* __restrict__ tout = cand_t + slot;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    int off = run;
-    for (int w = 0; w < 4; ++w) {
-      const int cw = wcnt[u][w];
-      if (w < wave) off += cw;
-      run += cw;
-    }
+    const int4 w4 = reinterpret_cast<const int4*>(wcnt)[u];
+    const int before = (wave > 0 ? w4.x : 0) + (wave > 1 ? w4.y : 0) + (wave > 2 ? w4.z : 0);
     if ((mask[u] >> lane) & 1ull) {
-      const int p = off + ballot_rank(mask[u]);
-      cand_key[slot + p] = key[u];
-      cand_t[slot + p] = t0 + u * 256 + tid;
+      const int p = run + before + ballot_rank(mask[u]);
+      kout[p] = key[u];
+      tout[p] = t0 + u * 256 + tid;
     }
+    run += (w4.x + w4.y) + (w4.z + w4.w);
   }
   if (tid == 0) chunk_count[(int64_t)bh * n_chunks + blockIdx.x] = run;
 }
 
 // ------------------------------------------------------------------ select
 __global__ __launch_bounds__(1024) void select_kernel(
-    const uint16_t* __restrict__ q, int n_q_heads, int Hkv, int G, const uint8_t* __restrict__ codes,
-    const float* __restrict__ alpha, int capacity, int n_tokens, int top_k, int chunk, int n_chunks,
+    const uint8_t* __restrict__ codes, const float* __restrict__ alpha, int capacity,
+    int n_tokens, const int* __restrict__ sel_lut, const float* __restrict__ sel_inv, int top_k,
+    int chunk, int n_chunks,
     const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_t,
     const int32_t* __restrict__ chunk_count, uint32_t* __restrict__ comp_key,
     int32_t* __restrict__ comp_t, int32_t* __restrict__ idx) {
@@ -295,12 +420,12 @@ __global__ __launch_bounds__(1024) void select_kernel(
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t lkey[kSelectLds];
   __shared__ int32_t lpos[kSelectLds];
-  __shared__ float qbar[kD];
-  __shared__ float lut[kLut];
+  __shared__ uint32_t sub[kSubMax];
   __shared__ int tmp[32];
   __shared__ uint32_t mm[32];
-  const int bh = blockIdx.x, b = bh / Hkv, h = bh - b * Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  __shared__ int scount;
+  const int bh = blockIdx.x;
+  const int tid = threadIdx.x;
   const int n = n_tokens - kSink;
   int32_t* out = idx + (int64_t)bh * top_k;
   if (top_k >= n) {  // every candidate is kept
@@ -309,62 +434,92 @@ __global__ __launch_bounds__(1024) void select_kernel(
   }
   // Tile counts -> offsets of each tile's candidates in the ordered list.
   {
-    const int per = (n_chunks + blockDim.x - 1) / blockDim.x;
+    const int per = (n_chunks + blockDim.x - 1) / blockDim.x;  // <= 2
     const int c0 = tid * per;
-    int s = 0;
-    for (int ci = c0; ci < c0 + per && ci < n_chunks; ++ci)
-      s += chunk_count[(int64_t)bh * n_chunks + ci];
+    int cs[2] = {0, 0};
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (j < per && c0 + j < n_chunks) cs[j] = chunk_count[(int64_t)bh * n_chunks + c0 + j];
     int total;
-    int pre = block_excl_scan(s, tmp, &total);
-    for (int ci = c0; ci < c0 + per && ci < n_chunks; ++ci) {
-      off[ci] = pre;
-      pre += chunk_count[(int64_t)bh * n_chunks + ci];
-    }
+    int pre = block_excl_scan(cs[0] + cs[1], tmp, &total);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (j < per && c0 + j < n_chunks) {
+        off[c0 + j] = pre;
+        pre += cs[j];
+      }
     if (tid == 0) off[n_chunks] = total;
     __syncthreads();
   }
-  int C = off[n_chunks];
+  const int C = off[n_chunks];
   const int64_t cbase = (int64_t)bh * n_chunks * chunk;
-  const uint32_t* keys;
-  const int32_t* pos;
   uint32_t lo = 0xffffffffu, hi = 0u;
   if (C < top_k) {
-    // Exact path over the whole head: rescore every candidate, in order.
-    build_selection_lut(q, b, h, n_q_heads, G, qbar, lut);
+    // Exact path over the whole head: rescore every candidate with the same
+    // table and arithmetic as the score kernel, in order.
+    int* itab = reinterpret_cast<int*>(lkey);  // the LDS list is unused here
+    load_itab(sel_lut + (int64_t)bh * kLut, itab);
+    const float inv = sel_inv[bh];
+    __syncthreads();
     const int64_t row0 = (int64_t)bh * capacity;
     for (int i = tid; i < n; i += blockDim.x) {
       const int t = kSink + i;
       const uint4 c = *reinterpret_cast<const uint4*>(codes + (row0 + t) * kCodeBytes);
-      const uint32_t key = score_key(selection_score(lut, c, alpha[row0 + t]));
+      const uint32_t key = score_key(selection_score(itab, inv, c, alpha[row0 + t]));
       comp_key[cbase + i] = key;
       comp_t[cbase + i] = t;
       lo = min(lo, key);
       hi = max(hi, key);
     }
-    C = n;
-    keys = comp_key + cbase;
-    pos = comp_t + cbase;
-  } else {
-    const bool in_lds = C <= kSelectLds;
-    uint32_t* dk = in_lds ? lkey : comp_key + cbase;
-    int32_t* dp = in_lds ? lpos : comp_t + cbase;
-    for (int ci = wave; ci < n_chunks; ci += nw) {
-      const int o = off[ci], cnt = off[ci + 1] - o;
-      const int64_t src = cbase + (int64_t)ci * chunk;
-      for (int j = lane; j < cnt; j += 64) {
-        const uint32_t key = cand_key[src + j];
-        dk[o + j] = key;
-        dp[o + j] = cand_t[src + j];
-        lo = min(lo, key);
-        hi = max(hi, key);
+    block_minmax(lo, hi, mm, &lo, &hi);
+    const Kth r = block_kth(comp_key + cbase, n, top_k, lo, hi, hist, tmp, sub, &scount);
+    block_emit(comp_key + cbase, comp_t + cbase, n, top_k, r, out, tmp);
+    return;
+  }
+  // Gather the candidates into one ordered list: element i lives in the tile
+  // ci with off[ci] <= i < off[ci + 1] (binary search), 8 loads in flight per
+  // thread.
+  const bool in_lds = C <= kSelectLds;
+  uint32_t* dk = in_lds ? lkey : comp_key + cbase;
+  int32_t* dp = in_lds ? lpos : comp_t + cbase;
+  for (int base = 0; base < C; base += 8 * (int)blockDim.x) {
+    uint32_t kk[8];
+    int32_t tt[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * blockDim.x + tid;
+      kk[u] = 0u;
+      tt[u] = 0;
+      if (i < C) {
+        int l = 0, r = n_chunks;
+        while (r - l > 1) {
+          const int mid = (l + r) >> 1;
+          if (off[mid] <= i) l = mid; else r = mid;
+        }
+        const int64_t src = cbase + (int64_t)l * chunk + (i - off[l]);
+        kk[u] = cand_key[src];
+        tt[u] = cand_t[src];
       }
     }
-    keys = dk;
-    pos = dp;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * blockDim.x + tid;
+      if (i < C) {
+        dk[i] = kk[u];
+        dp[i] = tt[u];
+        lo = min(lo, kk[u]);
+        hi = max(hi, kk[u]);
+      }
+    }
   }
   block_minmax(lo, hi, mm, &lo, &hi);  // its barriers also publish the copies
-  const Kth r = block_kth_largest(keys, C, top_k, lo, hi, hist, tmp);
-  block_emit_selected(keys, pos, C, top_k, r, out, tmp);
+  if (in_lds) {
+    const Kth r = block_kth(lkey, C, top_k, lo, hi, hist, tmp, sub, &scount);
+    block_emit(lkey, lpos, C, top_k, r, out, tmp);
+  } else {
+    const Kth r = block_kth(comp_key + cbase, C, top_k, lo, hi, hist, tmp, sub, &scount);
+    block_emit(comp_key + cbase, comp_t + cbase, C, top_k, r, out, tmp);
+  }
 }
 
 }  // namespace
@@ -374,32 +529,36 @@ __global__ __launch_bounds__(1024) void select_kernel(
 // score).  Otherwise the expected rank of the k-th score in the sample plus five
 // standard deviations and a small floor, so that fewer than k tokens pass only
 // with negligible probability; the select kernel handles that case exactly anyway.
-hipError_t launch_sample(const uint16_t* q, int n_q_heads, int B, int Hkv, const uint8_t* codes,
-                         const float* alpha, int capacity, int n_tokens, int top_k, int force_exact,
-                         float* tau, hipStream_t s) {
+hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const float* mu,
+                       const uint8_t* codes, const float* alpha, int capacity, int n_tokens,
+                       int top_k, int mode, int* sel_lut, float* sel_inv, float* att_lut,
+                       float* att_qmu, float* tau, hipStream_t s) {
   const int n = n_tokens - kSink;
-  int rank;
-  if (n <= kSampleMax) {
-    rank = top_k;
-  } else {
-    const double e = (double)top_k * kSampleMax / (double)n;
-    double r = e + 5.0 * __builtin_sqrt(e) + 8.0;
-    rank = r > kSampleMax ? kSampleMax + 1 : (int)r + 1;
+  int rank = 1;
+  if (mode == 1) {
+    if (n <= kSampleMax) {
+      rank = top_k;
+    } else {
+      const double e = (double)top_k * kSampleMax / (double)n;
+      const double r = e + 5.0 * __builtin_sqrt(e) + 8.0;
+      rank = r > kSampleMax ? kSampleMax + 1 : (int)r + 1;
+    }
   }
-  return launch_k(KID_SAMPLE, sample_kernel, dim3(B * Hkv), dim3(1024), 0, s, q, n_q_heads, Hkv,
-                  n_q_heads / Hkv, codes, alpha, capacity, n_tokens, rank, force_exact, tau);
+  return launch_k(KID_PREP, prep_kernel, dim3(B * Hkv), dim3(1024), 0, s, q, n_q_heads, Hkv,
+                  n_q_heads / Hkv, mu, codes, alpha, capacity, n_tokens, rank, mode, sel_lut,
+                  sel_inv, att_lut, att_qmu, tau);
 }
 
-hipError_t launch_score(const uint16_t* q, int n_q_heads, int B, int Hkv, const uint8_t* codes,
-                        const float* alpha, int capacity, int n_tokens, const float* tau,
-                        int chunk, int n_chunks, uint32_t* cand_key, int32_t* cand_t,
-                        int32_t* chunk_count, float* scores_opt, hipStream_t s) {
+hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha, int capacity,
+                        int n_tokens, const int* sel_lut, const float* sel_inv, const float* tau,
+                        int chunk,
+                        int n_chunks, uint32_t* cand_key, int32_t* cand_t, int32_t* chunk_count,
+                        float* scores_opt, hipStream_t s) {
   const dim3 grid(n_chunks, B * Hkv), block(256);
-  const int G = n_q_heads / Hkv;
-#define SIKV_SCORE_CASE(UU)                                                                     \
-  case 256 * UU:                                                                                \
-    return launch_k(KID_SCORE, score_kernel<UU>, grid, block, 0, s, q, n_q_heads, Hkv, G, codes, \
-                    alpha, capacity, n_tokens, tau, n_chunks, cand_key, cand_t, chunk_count,    \
+#define SIKV_SCORE_CASE(UU)                                                                    \
+  case 256 * UU:                                                                               \
+    return launch_k(KID_SCORE, score_kernel<UU>, grid, block, 0, s, codes, alpha, capacity,    \
+                    n_tokens, sel_lut, sel_inv, tau, n_chunks, cand_key, cand_t, chunk_count,  \
                     scores_opt);
   switch (chunk) {
     SIKV_SCORE_CASE(1)
@@ -413,15 +572,15 @@ hipError_t launch_score(const uint16_t* q, int n_q_heads, int B, int Hkv, const 
 #undef SIKV_SCORE_CASE
 }
 
-hipError_t launch_select(const uint16_t* q, int n_q_heads, int B, int Hkv, const uint8_t* codes,
-                         const float* alpha, int capacity, int n_tokens, int top_k, int chunk,
-                         int n_chunks, uint32_t* cand_key, int32_t* cand_t,
-                         const int32_t* chunk_count, uint32_t* comp_key, int32_t* comp_t,
-                         int32_t* idx, hipStream_t s) {
+hipError_t launch_select(int B, int Hkv, const uint8_t* codes, const float* alpha, int capacity,
+                         int n_tokens, const int* sel_lut, const float* sel_inv, int top_k,
+                         int chunk, int n_chunks,
+                         uint32_t* cand_key, int32_t* cand_t, const int32_t* chunk_count,
+                         uint32_t* comp_key, int32_t* comp_t, int32_t* idx, hipStream_t s) {
   if (n_chunks > kMaxChunks) return hipErrorInvalidValue;
-  return launch_k(KID_SELECT, select_kernel, dim3(B * Hkv), dim3(1024), 0, s, q, n_q_heads, Hkv,
-                  n_q_heads / Hkv, codes, alpha, capacity, n_tokens, top_k, chunk, n_chunks,
-                  cand_key, cand_t, chunk_count, comp_key, comp_t, idx);
+  return launch_k(KID_SELECT, select_kernel, dim3(B * Hkv), dim3(1024), 0, s, codes, alpha,
+                  capacity, n_tokens, sel_lut, sel_inv, top_k, chunk, n_chunks, cand_key, cand_t,
+                  chunk_count, comp_key, comp_t, idx);
 }
 
 }  // namespace sikv

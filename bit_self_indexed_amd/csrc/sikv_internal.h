@@ -25,7 +25,7 @@ enum KernelId {
   KID_MU_PARTIAL = 0,
   KID_MU_FINAL,
   KID_CODES,
-  KID_SAMPLE,
+  KID_PREP,
   KID_SCORE,
   KID_SELECT,
   KID_ATTN,
@@ -48,69 +48,79 @@ __device__ __forceinline__ float key_score(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// Selection query (sum of the KV head's G query heads, fp32, g ascending) and its
-// look-up table, in LDS: lut[j*16 + p] = ((+-x0 +- x1) +- x2) +- x3 with x_i the
-// query's channel 4j+i and the sign of x_i negative iff bit i of p is set
-// (§2.1 item 2: a query piece dotted with the 16 sign vertices).  Every thread of
-// the block must call it; ends with a barrier.
-__device__ __forceinline__ void build_selection_lut(const uint16_t* __restrict__ q, int b, int h,
-                                                    int n_q_heads, int G, float* qbar,
-                                                    float* lut) {
-  const int tid = threadIdx.x;
-  if (tid < kD) {
-    const uint16_t* qp = q + ((size_t)b * n_q_heads + (size_t)h * G) * kD + tid;
-    float s = __uint_as_float((uint32_t)qp[0] << 16);
-    for (int g = 1; g < G; ++g) s += __uint_as_float((uint32_t)qp[(size_t)g * kD] << 16);
-    qbar[tid] = s;
-  }
-  __syncthreads();
-  for (int e = tid; e < kLut; e += blockDim.x) {
-    const int j = e >> 4, p = e & 15;
-    const float x0 = qbar[4 * j], x1 = qbar[4 * j + 1], x2 = qbar[4 * j + 2], x3 = qbar[4 * j + 3];
-    float v = (p & 1) ? -x0 : x0;
-    v += (p & 2) ? -x1 : x1;
-    v += (p & 4) ? -x2 : x2;
-    v += (p & 8) ? -x3 : x3;
-    lut[e] = v;
-  }
-  __syncthreads();
+// Look-up table of one query vector x (LDS, 128 floats): lut[j*16 + p] =
+// ((+-x0 +- x1) +- x2) +- x3 with x_i = x[4j+i], negative iff bit i of p is set
+// (§2.1 item 2: a query piece dotted with the 16 sign vertices).  No barrier.
+__device__ __forceinline__ float lut_entry(const float* x, int e) {
+  const int j = e >> 4, p = e & 15;
+  const float x0 = x[4 * j], x1 = x[4 * j + 1], x2 = x[4 * j + 2], x3 = x[4 * j + 3];
+  float v = (p & 1) ? -x0 : x0;
+  v += (p & 2) ? -x1 : x1;
+  v += (p & 4) ? -x2 : x2;
+  v += (p & 8) ? -x3 : x3;
+  return v;
 }
 
-// Sum over the 8 sub-vectors held in one 32-bit word of a code (sub-vectors
-// 8w..8w+7).  The nibbles are moved to byte lanes already multiplied by 4 (even
-// nibbles from d << 2, odd ones from d >> 2), so each look-up needs a single
-// byte extract for its LDS address; the table slice of sub-vector j starts at
-// byte 64*j.
+// Byte k of x, zero-extended, as one v_perm_b32 (selector byte 0x0c yields 0x00).
+__device__ __forceinline__ uint32_t byte_of(uint32_t x, uint32_t k) {
+  return __builtin_amdgcn_perm(0u, x, 0x0c0c0c00u | k);
+}
+
+// Sum over the 8 sub-vectors of one code word with a nibble table (sub-vectors
+// 8w..8w+7, table slice of sub-vector j at byte 64*j).  The nibbles are moved to
+// byte lanes already multiplied by 4 (even nibbles from d << 2, odd ones from
+// d >> 2), so each look-up needs a single byte extract for its LDS address.
 __device__ __forceinline__ float lut_word(const float* __restrict__ lutw, uint32_t d) {
   const uint32_t e = (d << 2) & 0x3c3c3c3cu;
   const uint32_t o = (d >> 2) & 0x3c3c3c3cu;
   const char* L = reinterpret_cast<const char*>(lutw);
-  float a = *reinterpret_cast<const float*>(L + 0 * 64 + (e & 0xffu));
-  float c = *reinterpret_cast<const float*>(L + 1 * 64 + (o & 0xffu));
-  a += *reinterpret_cast<const float*>(L + 2 * 64 + ((e >> 8) & 0xffu));
-  c += *reinterpret_cast<const float*>(L + 3 * 64 + ((o >> 8) & 0xffu));
-  a += *reinterpret_cast<const float*>(L + 4 * 64 + ((e >> 16) & 0xffu));
-  c += *reinterpret_cast<const float*>(L + 5 * 64 + ((o >> 16) & 0xffu));
-  a += *reinterpret_cast<const float*>(L + 6 * 64 + (e >> 24));
-  c += *reinterpret_cast<const float*>(L + 7 * 64 + (o >> 24));
+  float a = *reinterpret_cast<const float*>(L + 0 * 64 + byte_of(e, 0));
+  float c = *reinterpret_cast<const float*>(L + 1 * 64 + byte_of(o, 0));
+  a += *reinterpret_cast<const float*>(L + 2 * 64 + byte_of(e, 1));
+  c += *reinterpret_cast<const float*>(L + 3 * 64 + byte_of(o, 1));
+  a += *reinterpret_cast<const float*>(L + 4 * 64 + byte_of(e, 2));
+  c += *reinterpret_cast<const float*>(L + 5 * 64 + byte_of(o, 2));
+  a += *reinterpret_cast<const float*>(L + 6 * 64 + byte_of(e, 3));
+  c += *reinterpret_cast<const float*>(L + 7 * 64 + byte_of(o, 3));
   return a + c;
 }
 
-// Compressed-domain score of one token: sum_j LUT[j][nibble_j] (fixed order:
-// per word as in lut_word, words combined as (w0 + w1) + (w2 + w3)).  The
-// caller multiplies by the token's scale.
+// q . sigma(code) with a per-query-head nibble table: (w0 + w1) + (w2 + w3).
 __device__ __forceinline__ float lut_dot(const float* __restrict__ lut, uint4 c) {
-  const float s0 = lut_word(lut + 0 * 128, c.x);
-  const float s1 = lut_word(lut + 1 * 128, c.y);
-  const float s2 = lut_word(lut + 2 * 128, c.z);
-  const float s3 = lut_word(lut + 3 * 128, c.w);
-  return (s0 + s1) + (s2 + s3);
+  return (lut_word(lut, c.x) + lut_word(lut + 128, c.y)) +
+         (lut_word(lut + 256, c.z) + lut_word(lut + 384, c.w));
 }
 
-// Selection score as used by every kernel that ranks tokens; -0 is mapped to +0
-// so that equal scores have equal keys.
-__device__ __forceinline__ float selection_score(const float* __restrict__ lut, uint4 c, float a) {
-  return a * lut_dot(lut, c) + 0.0f;
+// Selection table in int32 fixed point: itab[j*16 + p] = rint(lut[j*16 + p] * 2^e)
+// with 2^e chosen per KV head so that sum_c |qbar_c| * 2^e < 2^30.  Integer sums
+// are exact and order-free, and v_add3 adds two terms per instruction; the
+// rounding of the 32 terms costs at most 16 * 2^-e <= 2^-26 * sum_c |qbar_c|.
+__device__ __forceinline__ int ilut_word(const int* __restrict__ lutw, uint32_t d) {
+  const uint32_t e = (d << 2) & 0x3c3c3c3cu;
+  const uint32_t o = (d >> 2) & 0x3c3c3c3cu;
+  const char* L = reinterpret_cast<const char*>(lutw);
+  const int a0 = *reinterpret_cast<const int*>(L + 0 * 64 + byte_of(e, 0));
+  const int a1 = *reinterpret_cast<const int*>(L + 1 * 64 + byte_of(o, 0));
+  const int a2 = *reinterpret_cast<const int*>(L + 2 * 64 + byte_of(e, 1));
+  const int a3 = *reinterpret_cast<const int*>(L + 3 * 64 + byte_of(o, 1));
+  const int a4 = *reinterpret_cast<const int*>(L + 4 * 64 + byte_of(e, 2));
+  const int a5 = *reinterpret_cast<const int*>(L + 5 * 64 + byte_of(o, 2));
+  const int a6 = *reinterpret_cast<const int*>(L + 6 * 64 + byte_of(e, 3));
+  const int a7 = *reinterpret_cast<const int*>(L + 7 * 64 + byte_of(o, 3));
+  return (a0 + a1 + a2) + (a3 + a4 + a5) + (a6 + a7);
+}
+
+__device__ __forceinline__ int ilut_dot(const int* __restrict__ itab, uint4 c) {
+  return ilut_word(itab, c.x) + ilut_word(itab + 128, c.y) + ilut_word(itab + 256, c.z) +
+         ilut_word(itab + 384, c.w);
+}
+
+// Selection score of one token, as used by every kernel that ranks tokens
+// (same table, exact integer sum, then alpha * (sum * 2^-e)); -0 is mapped to
+// +0 so that equal scores have equal keys.
+__device__ __forceinline__ float selection_score(const int* __restrict__ itab, float inv_scale,
+                                                 uint4 c, float a) {
+  return a * ((float)ilut_dot(itab, c) * inv_scale) + 0.0f;
 }
 
 // Number of set bits of a 64-lane ballot below this lane.
@@ -130,25 +140,29 @@ hipError_t launch_codes(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, i
                         float* alpha, uint16_t* k_sink, hipStream_t s);
 
 // score.hip
-hipError_t launch_sample(const uint16_t* q, int n_q_heads, int B, int Hkv, const uint8_t* codes,
-                         const float* alpha, int capacity, int n_tokens, int top_k, int force_exact,
-                         float* tau, hipStream_t s);
-hipError_t launch_score(const uint16_t* q, int n_q_heads, int B, int Hkv, const uint8_t* codes,
-                        const float* alpha, int capacity, int n_tokens, const float* tau,
-                        int chunk, int n_chunks, uint32_t* cand_key, int32_t* cand_t,
-                        int32_t* chunk_count, float* scores_opt, hipStream_t s);
-hipError_t launch_select(const uint16_t* q, int n_q_heads, int B, int Hkv, const uint8_t* codes,
-                         const float* alpha, int capacity, int n_tokens, int top_k, int chunk,
-                         int n_chunks, uint32_t* cand_key, int32_t* cand_t,
-                         const int32_t* chunk_count, uint32_t* comp_key, int32_t* comp_t,
-                         int32_t* idx, hipStream_t s);
+// mode 0: attention tables only; 1: all tables + sampled threshold; 2: all
+// tables + a threshold that forces the exact whole-head selection.
+hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const float* mu,
+                       const uint8_t* codes, const float* alpha, int capacity, int n_tokens,
+                       int top_k, int mode, int* sel_lut, float* sel_inv, float* att_lut,
+                       float* att_qmu, float* tau, hipStream_t s);
+hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha, int capacity,
+                        int n_tokens, const int* sel_lut, const float* sel_inv, const float* tau,
+                        int chunk,
+                        int n_chunks, uint32_t* cand_key, int32_t* cand_t, int32_t* chunk_count,
+                        float* scores_opt, hipStream_t s);
+hipError_t launch_select(int B, int Hkv, const uint8_t* codes, const float* alpha, int capacity,
+                         int n_tokens, const int* sel_lut, const float* sel_inv, int top_k,
+                         int chunk, int n_chunks,
+                         uint32_t* cand_key, int32_t* cand_t, const int32_t* chunk_count,
+                         uint32_t* comp_key, int32_t* comp_t, int32_t* idx, hipStream_t s);
 
 // attn.hip
 hipError_t launch_attn(const uint16_t* q, int n_q_heads, int B, int Hkv, const uint8_t* codes,
-                       const float* alpha, const float* mu, const uint16_t* k_sink,
-                       const uint16_t* v, int64_t vsb, int64_t vsh, int64_t vst, int capacity,
-                       int n_tokens, const int32_t* idx, int top_k, float sm_scale, int split,
-                       int n_splits, float* part_o, float* part_ml, hipStream_t s);
+                       const float* alpha, const uint16_t* k_sink, const uint16_t* v, int64_t vsb,
+                       int64_t vsh, int64_t vst, int capacity, int n_tokens, const int32_t* idx,
+                       int top_k, const float* att_lut, const float* att_qmu, float sm_scale,
+                       int split, int n_splits, float* part_o, float* part_ml, hipStream_t s);
 hipError_t launch_combine(const float* part_o, const float* part_ml, int BHq, int n_splits,
                           float* out, hipStream_t s);
 
