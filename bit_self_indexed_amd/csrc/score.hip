@@ -151,9 +151,32 @@ __device__ __forceinline__ Round block_round(const uint32_t* keys, int n, int k,
   return r;
 }
 
+// need-th largest (1 <= need <= m <= 64) of the keys sub[0..m) by wave 0 alone:
+// lane i counts the keys greater than and not smaller than its own; the lanes
+// with gt < need <= ge all hold the answer.  Result in out[0] (key), out[1]
+// (number of keys greater than it).  Caller provides the barrier.
+__device__ __forceinline__ void wave_kth(const uint32_t* sub, int m, int need, int* out) {
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  const uint32_t mine = lane < m ? sub[lane] : 0u;
+  int gt = 0, ge = 0;
+  for (int j = 0; j < m; ++j) {
+    const uint32_t o = (uint32_t)__shfl((int)mine, j);
+    gt += o > mine;
+    ge += o >= mine;
+  }
+  const bool hit = lane < m && gt < need && need <= ge;
+  const uint64_t b = __ballot(hit);
+  if (hit && (uint32_t)lane == (uint32_t)__builtin_ctzll(b)) {
+    out[0] = (int)mine;
+    out[1] = gt;
+  }
+}
+
 // Exact k-th largest of n keys in [lo, hi] (1 <= k <= n).  The first round runs
 // over all keys; the keys of its boundary digit (usually few) are then copied to
-// `sub` (LDS) and the remaining rounds run over them only.
+// `sub` (LDS) and resolved by one wave when they are at most 64, else by more
+// rounds over them only.
 __device__ Kth block_kth(const uint32_t* keys, int n, int k, uint32_t lo, uint32_t hi,
                          uint32_t* hist, int* tmp, uint32_t* sub, int* scount) {
   const uint32_t span = hi - lo;
@@ -180,6 +203,14 @@ __device__ Kth block_kth(const uint32_t* keys, int n, int k, uint32_t lo, uint32
       __syncthreads();
       src = sub;
       ns = r.count;
+      if (ns <= 64) {
+        wave_kth(sub, ns, need, tmp + 24);
+        __syncthreads();
+        const uint32_t key = (uint32_t)tmp[24];
+        const int gt = tmp[25];
+        __syncthreads();
+        return Kth{key, above + gt, need - gt};
+      }
     }
     first = false;
   }
@@ -199,9 +230,17 @@ __device__ void block_emit(const uint32_t* keys, const int32_t* pos, int n, int 
     gt += kk > r.key;
     eq += kk == r.key;
   }
-  int tg, te;
-  const int gt_before = block_excl_scan(gt, tmp, &tg);
-  int eq_before = block_excl_scan(eq, tmp, &te);
+  int gt_before, eq_before;
+  if (n < 65536) {
+    int tot;
+    const int ex = block_excl_scan((gt << 16) | eq, tmp, &tot);
+    gt_before = ex >> 16;
+    eq_before = ex & 0xffff;
+  } else {
+    int tg, te;
+    gt_before = block_excl_scan(gt, tmp, &tg);
+    eq_before = block_excl_scan(eq, tmp, &te);
+  }
   int o = gt_before + min(eq_before, r.need);
   for (int i = i0; i < i1; ++i) {
     const uint32_t kk = keys[i];
@@ -219,18 +258,56 @@ __device__ __forceinline__ void load_itab(const int* __restrict__ gtab, int* ita
   for (int i = threadIdx.x; i < kLut / 4; i += blockDim.x) dst[i] = src[i];
 }
 
+// A key at or below the k-th largest of n keys in [lo, hi], within 2^-22 of the
+// span: the lower edge of the k-th largest's digit after two radix rounds (the
+// exact key when the boundary digit holds at most 64 keys).
+__device__ uint32_t block_kth_floor(const uint32_t* keys, int n, int k, uint32_t lo, uint32_t hi,
+                                    uint32_t* hist, int* tmp, uint32_t* sub, int* scount) {
+  const uint32_t span = hi - lo;
+  const int top = span ? 32 - __clz(span) : 0;
+  if (top == 0) return lo;
+  const Round r = block_round(keys, n, k, lo, top, 0u, hist, tmp);
+  const uint32_t prefix = (uint32_t)r.digit << r.shift;
+  if (r.shift == 0) return lo + prefix;
+  const int need = k - r.above;
+  const uint32_t* src = keys;
+  int ns = n;
+  if (r.count <= kSubMax) {
+    if (threadIdx.x == 0) *scount = 0;
+    __syncthreads();
+    const uint64_t want = (uint64_t)prefix >> r.shift;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      const uint32_t key = keys[i];
+      if (((uint64_t)(key - lo) >> r.shift) == want) sub[atomicAdd(scount, 1)] = key;
+    }
+    __syncthreads();
+    src = sub;
+    ns = r.count;
+    if (ns <= 64) {
+      wave_kth(sub, ns, need, tmp + 24);
+      __syncthreads();
+      const uint32_t key = (uint32_t)tmp[24];
+      __syncthreads();
+      return key;
+    }
+  }
+  const Round r2 = block_round(src, ns, need, lo, r.shift, prefix, hist, tmp);
+  return lo + (prefix | ((uint32_t)r2.digit << r2.shift));
+}
+
 // ------------------------------------------------------------------ prep
-// mode 0: attention tables only (sel_tab and tau unused); 1: all tables +
-// sampled threshold; 2: all tables + tau = +inf (forces the exact whole-head
-// selection).
+// mode 0: attention tables only (sel_lut, sel_inv and tau unused); 1: all tables
+// + sampled threshold; 2: all tables + tau = +inf (forces the exact whole-head
+// selection).  Every global load is issued before the first barrier.
 __global__ __launch_bounds__(1024) void prep_kernel(
     const uint16_t* __restrict__ q, int n_q_heads, int Hkv, int G, const float* __restrict__ mu,
     const uint8_t* __restrict__ codes, const float* __restrict__ alpha, int capacity, int n_tokens,
     int rank, int mode, int* __restrict__ sel_lut, float* __restrict__ sel_inv,
     float* __restrict__ att_lut, float* __restrict__ att_qmu, float* __restrict__ tau) {
   __shared__ float qv[kMaxGroup + 1][kD];  // q_g, then the selection query (sum)
+  __shared__ float mus[kD];
   __shared__ int itab[kLut];
-  __shared__ float red_a[16];
+  __shared__ float red_a[2];
   __shared__ uint32_t keys[kSampleMax];
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t sub[kSubMax];
@@ -244,8 +321,8 @@ __global__ __launch_bounds__(1024) void prep_kernel(
   const int m = full ? n : kSampleMax;
   const bool sample = mode == 1 && (full || rank <= m);
   const int64_t row0 = (int64_t)bh * capacity;
+  const int64_t hq0 = (int64_t)b * n_q_heads + (int64_t)h * G;
 
-  // Sample loads first (consumed after the tables are built).
   constexpr int kPer = kSampleMax / 1024;
   uint4 c[kPer];
   float a[kPer];
@@ -267,59 +344,54 @@ __global__ __launch_bounds__(1024) void prep_kernel(
       a[u] = alpha[row0 + t];
     }
   }
-  // Queries of the group and their sum (fp32, g ascending).
-  const uint16_t* qb = q + ((int64_t)b * n_q_heads + (int64_t)h * G) * kD;
-  for (int i = tid; i < G * kD; i += blockDim.x)
-    qv[i / kD][i % kD] = __uint_as_float((uint32_t)qb[i] << 16);
+  const float qx = tid < G * kD ? __uint_as_float((uint32_t)q[hq0 * kD + tid] << 16) : 0.0f;
+  const float mx = tid < kD ? mu[(int64_t)bh * kD + tid] : 0.0f;
+  if (tid < G * kD) qv[tid / kD][tid % kD] = qx;
+  if (tid < kD) mus[tid] = mx;
   __syncthreads();
+
+  // Selection query (fp32 sum, g ascending) and sum |qbar|; q_g . mu; attention
+  // tables of the G query heads.
   if (tid < kD) {
     float s = qv[0][tid];
     for (int g = 1; g < G; ++g) s += qv[g][tid];
     qv[kMaxGroup][tid] = s;
-  }
-  // Attention tables of the G query heads and their q.mu.
-  const int64_t hq0 = (int64_t)b * n_q_heads + (int64_t)h * G;
-  for (int i = tid; i < G * kLut; i += blockDim.x)
-    att_lut[hq0 * kLut + i] = lut_entry(qv[i / kLut], i % kLut);
-  for (int g = wave; g < G; g += (int)(blockDim.x >> 6)) {
-    const float* mb = mu + (int64_t)bh * kD;
-    float d = fmaf(qv[g][lane], mb[lane], qv[g][lane + 64] * mb[lane + 64]);
+    float v = fabsf(s);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    if (lane == 0) red_a[wave] = v;
+  } else if (wave >= 2 && wave < 2 + G) {
+    const int g = wave - 2;
+    float d = fmaf(qv[g][lane], mus[lane], qv[g][lane + 64] * mus[lane + 64]);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) d += __shfl_xor(d, o);
     if (lane == 0) att_qmu[hq0 + g] = d;
   }
-  __syncthreads();
+  for (int i = tid; i < G * kLut; i += blockDim.x)
+    att_lut[hq0 * kLut + i] = lut_entry(qv[i / kLut], i % kLut);
   if (mode == 0) return;
+  __syncthreads();
+
   // Selection table in fixed point: A = sum_c |qbar_c| = m * 2^x (m in [0.5, 1)),
   // scale 2^(30 - x) so that any sum of 32 entries stays below 2^30 in magnitude.
-  if (wave == 0) {
-    float v = fabsf(qv[kMaxGroup][lane]) + fabsf(qv[kMaxGroup][lane + 64]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    if (lane == 0) red_a[0] = v;
-  }
-  __syncthreads();
+  const float A = red_a[0] + red_a[1];
   int ex = 0;
-  if (red_a[0] > 0.0f) {
-    frexpf(red_a[0], &ex);
+  if (A > 0.0f) {
+    frexpf(A, &ex);
     ex = 30 - ex;
   }
-  for (int e = tid; e < kLut; e += blockDim.x) {
-    const int v = (int)rintf(ldexpf(lut_entry(qv[kMaxGroup], e), ex));
-    itab[e] = v;
-    sel_lut[(int64_t)bh * kLut + e] = v;
-  }
   const float inv = ldexpf(1.0f, -ex);
+  if (tid < kLut) {
+    const int v = (int)rintf(ldexpf(lut_entry(qv[kMaxGroup], tid), ex));
+    itab[tid] = v;
+    sel_lut[(int64_t)bh * kLut + tid] = v;
+  }
   if (tid == 0) sel_inv[bh] = inv;
+  if (mode == 2 || !sample) {  // +inf: nothing passes; -inf: keep all
+    if (tid == 0) tau[bh] = __uint_as_float(mode == 2 ? 0x7f800000u : 0xff800000u);
+    return;
+  }
   __syncthreads();
-  if (mode == 2) {
-    if (tid == 0) tau[bh] = __uint_as_float(0x7f800000u);  // +inf: nothing passes
-    return;
-  }
-  if (!sample) {  // threshold would sit below every sample: keep all
-    if (tid == 0) tau[bh] = __uint_as_float(0xff800000u);
-    return;
-  }
   uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
@@ -332,8 +404,8 @@ __global__ __launch_bounds__(1024) void prep_kernel(
     }
   }
   block_minmax(lo, hi, mm, &lo, &hi);
-  const Kth kt = block_kth(keys, m, rank, lo, hi, hist, tmp, sub, &scount);
-  if (tid == 0) tau[bh] = key_score(kt.key);
+  const uint32_t kth = block_kth_floor(keys, m, rank, lo, hi, hist, tmp, sub, &scount);
+  if (tid == 0) tau[bh] = key_score(kth);
 }
 
 // ------------------------------------------------------------------ score
@@ -476,39 +548,52 @@ __global__ __launch_bounds__(1024) void select_kernel(
     block_emit(comp_key + cbase, comp_t + cbase, n, top_k, r, out, tmp);
     return;
   }
-  // Gather the candidates into one ordered list: element i lives in the tile
-  // ci with off[ci] <= i < off[ci + 1] (binary search), 8 loads in flight per
-  // thread.
+  // Gather the candidates into one ordered list.  Wave w copies tiles w, w+nw,
+  // ...; the first 256 candidates of 4 tiles are loaded before any is stored.
   const bool in_lds = C <= kSelectLds;
   uint32_t* dk = in_lds ? lkey : comp_key + cbase;
   int32_t* dp = in_lds ? lpos : comp_t + cbase;
-  for (int base = 0; base < C; base += 8 * (int)blockDim.x) {
-    uint32_t kk[8];
-    int32_t tt[8];
+  {
+    const int lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+    for (int c0 = wave; c0 < n_chunks; c0 += 4 * nw) {
+      uint32_t kk[4][4];
+      int32_t tt[4][4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = base + u * blockDim.x + tid;
-      kk[u] = 0u;
-      tt[u] = 0;
-      if (i < C) {
-        int l = 0, r = n_chunks;
-        while (r - l > 1) {
-          const int mid = (l + r) >> 1;
-          if (off[mid] <= i) l = mid; else r = mid;
+      for (int v = 0; v < 4; ++v) {
+        const int ci = c0 + v * nw;
+        const int o = ci < n_chunks ? off[ci] : 0;
+        const int cnt = ci < n_chunks ? off[ci + 1] - o : 0;
+        const int64_t src = cbase + (int64_t)ci * chunk;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int j = lane + 64 * u;
+          kk[v][u] = j < cnt ? cand_key[src + j] : 0u;
+          tt[v][u] = j < cnt ? cand_t[src + j] : 0;
         }
-        const int64_t src = cbase + (int64_t)l * chunk + (i - off[l]);
-        kk[u] = cand_key[src];
-        tt[u] = cand_t[src];
       }
-    }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = base + u * blockDim.x + tid;
-      if (i < C) {
-        dk[i] = kk[u];
-        dp[i] = tt[u];
-        lo = min(lo, kk[u]);
-        hi = max(hi, kk[u]);
+      for (int v = 0; v < 4; ++v) {
+        const int ci = c0 + v * nw;
+        if (ci >= n_chunks) continue;
+        const int o = off[ci], cnt = off[ci + 1] - o;
+        const int64_t src = cbase + (int64_t)ci * chunk;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int j = lane + 64 * u;
+          if (j < cnt) {
+            dk[o + j] = kk[v][u];
+            dp[o + j] = tt[v][u];
+            lo = min(lo, kk[v][u]);
+            hi = max(hi, kk[v][u]);
+          }
+        }
+        for (int j = 256 + lane; j < cnt; j += 64) {  // tiles with many candidates
+          const uint32_t key = cand_key[src + j];
+          dk[o + j] = key;
+          dp[o + j] = cand_t[src + j];
+          lo = min(lo, key);
+          hi = max(hi, key);
+        }
       }
     }
   }
