@@ -47,6 +47,12 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-dense", action="store_true", help="skip the dense bf16 comparator")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--summarize-trace", nargs=2, metavar=("RUN_DIR", "OUT_TXT"),
+                   help="write a text summary of a rocprofv3 --kernel-trace --stats run and exit")
+    p.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON"),
+                   help="turn FETCH_SIZE and WRITE_SIZE counter runs into HBM bytes per launch "
+                        "and exit")
+    p.add_argument("--profile-command", default="", help="command recorded in a summary")
     return p.parse_args()
 
 
@@ -95,6 +101,90 @@ def measured_traffic(kernel: str, workload: str):
         return None
 
 
+# ----------------------------------------------------------------------------- profiles
+# Library kernels, with the sources that decide what each one reads and writes.
+KERNEL_SOURCES = {
+    "prep": ["score.hip", "sikv_internal.h", "api.cpp"],
+    "score": ["score.hip", "sikv_internal.h", "api.cpp"],
+    "select": ["score.hip", "sikv_internal.h", "api.cpp"],
+    "attn": ["attn.hip", "sikv_internal.h", "api.cpp"],
+    "combine": ["attn.hip", "sikv_internal.h", "api.cpp"],
+    "codes": ["encode.hip", "sikv_internal.h", "api.cpp"],
+    "mu_partial": ["encode.hip", "sikv_internal.h", "api.cpp"],
+    "mu_final": ["encode.hip", "sikv_internal.h", "api.cpp"],
+    "dense": ["dense.hip", "sikv_internal.h", "api.cpp"],
+    "copy": ["util.hip", "sikv_internal.h", "api.cpp"],
+}
+COPY_BYTES = 512 << 20  # sikv_stream_copy size used below: reads and writes this many bytes
+
+
+def short_kernel_name(name: str) -> str:
+    import re
+    s = name.replace("void ", "").replace("(anonymous namespace)::", "")
+    s = re.sub(r"\(.*", "", s)
+    s = s.split("::")[-1] if "sikv::" in s else s
+    if s.startswith("at::"):
+        s = "torch " + re.sub(r"<.*", "", s.split("::")[-1])
+    return s
+
+
+def library_kernel(name: str):
+    base = short_kernel_name(name).split("<")[0]
+    return base[:-len("_kernel")] if base.endswith("_kernel") and base[:-len("_kernel")] in KERNEL_SOURCES else None
+
+
+def summarize_trace(run_dir: str, out_txt: str, command: str) -> None:
+    """rocprofv3 top_kernels table (sqlite results) -> short text summary."""
+    import glob
+    import sqlite3
+    db = sorted(glob.glob(os.path.join(run_dir, "*.db")))[0]
+    rows = sqlite3.connect(db).execute("select * from top_kernels").fetchall()
+    lines = ["# rocprofv3 kernel statistics (top_kernels table of the results database)",
+             "# command, run from the repository root:", f"#   {command}",
+             "# durations in microseconds",
+             f"{'kernel':<34}{'calls':>7}{'total_us':>12}{'avg_us':>10}{'pct':>7}"]
+    for name, calls, tot, avg, pct in rows:
+        lines.append(f"{short_kernel_name(name)[:33]:<34}{calls:>7}{tot:>12.1f}{avg:>10.2f}{pct:>7.2f}")
+    open(out_txt, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _counter_per_kernel(run_dir: str, counter: str):
+    import csv
+    import glob
+    f = sorted(glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True))[0]
+    acc = {}
+    for r in csv.DictReader(open(f)):
+        if r["Counter_Name"] != counter:
+            continue
+        k = library_kernel(r["Kernel_Name"])
+        if k is None:
+            continue
+        v = acc.setdefault(k, [0, 0.0])
+        v[0] += 1
+        v[1] += float(r["Counter_Value"]) * 1024.0   # counters read in KiB
+    return {k: (n, tot / n) for k, (n, tot) in acc.items()}
+
+
+def summarize_traffic(fetch_dir: str, write_dir: str, out_json: str, command: str) -> None:
+    """FETCH_SIZE / WRITE_SIZE per dispatch, scaled so that the copy kernel of
+    known size reads exactly COPY_BYTES and writes exactly COPY_BYTES."""
+    fetch = _counter_per_kernel(fetch_dir, "FETCH_SIZE")
+    write = _counter_per_kernel(write_dir, "WRITE_SIZE")
+    f_scale = COPY_BYTES / fetch["copy"][1]
+    w_scale = COPY_BYTES / write["copy"][1]
+    out = {"command": command, "copy_bytes": COPY_BYTES,
+           "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
+    for k in sorted(set(fetch) & set(write)):
+        fb, wb = fetch[k][1] * f_scale, write[k][1] * w_scale
+        out["kernels"][k] = {
+            "dispatches": fetch[k][0], "fetch_bytes_per_launch": fb,
+            "write_bytes_per_launch": wb, "hbm_bytes_per_launch": fb + wb,
+            "sources": KERNEL_SOURCES[k], "source_hash": source_hash(KERNEL_SOURCES[k])}
+    json.dump(out, open(out_json, "w"), indent=1)
+    print(json.dumps(out, indent=1))
+
+
 # ----------------------------------------------------------------------------- CPU
 def cpu_baseline(w, d, budget_s: float):
     """The oracle as it stands, single-threaded BLAS, timed on a bounded sample of
@@ -138,6 +228,12 @@ def cpu_baseline(w, d, budget_s: float):
 # ----------------------------------------------------------------------------- main
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, args.profile_command)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, args.profile_command)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               f"(the path shards by (batch, KV head) with no communication; see the design "

@@ -17,6 +17,7 @@ using namespace sikv;
 
 constexpr size_t kAlign = 256;
 constexpr int kMaxChunks = 2048;
+constexpr int64_t kAttnBlocks = 1024;  // attention blocks resident at once (4 per CU)
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -30,13 +31,21 @@ struct EncodePlan {
 
 struct ScorePlan {
   int chunk, n_chunks;
-  size_t off_tau, off_cnt, off_ckey, off_ct, off_pkey, off_pt, off_tab, off_inv, off_lut, off_qmu;
+  size_t off_tau, off_cnt, off_ckey, off_ct, off_pkey, off_pt, off_tab, off_inv, off_lut, off_qmu,
+      off_slog;
   size_t bytes;
 };
 
 struct AttnPlan {
-  int split, n_splits;
-  size_t off_o, off_ml, off_lut, off_qmu, bytes;
+  int cpb, n_splits;
+  size_t off_o, off_ml, off_lut, off_qmu, off_slog, bytes;
+};
+
+// Attention tables of the query heads, written by the prep kernel.
+struct AttnTables {
+  float* lut;
+  float* qmu;
+  float* slog;
 };
 
 struct DecodePlan {
@@ -81,26 +90,32 @@ bool plan_score(const sikv_cache_desc* c, int n_q_heads, ScorePlan* p) {
   p->off_inv = o;  o += align_up((size_t)BH * sizeof(float));
   p->off_lut = o;  o += align_up((size_t)c->batch * n_q_heads * kLut * sizeof(float));
   p->off_qmu = o;  o += align_up((size_t)c->batch * n_q_heads * sizeof(float));
+  p->off_slog = o; o += align_up((size_t)c->batch * n_q_heads * kSink * sizeof(float));
   p->bytes = o;
   return true;
 }
 
-// Entries of the attended list (64 sinks + k) per block: the largest of
-// 256/128/64 that still gives >= 1024 blocks.  Workspace: split partials (o,
-// max, sum) and, for a standalone call, the query heads' tables.
+// Attention grid: the attended list (64 sinks + k) of each (b, KV head) is cut
+// into chunks of kAttnChunk entries; a block of four waves takes chunks_per_block
+// consecutive chunks (a multiple of 4, so every wave gets the same count), the
+// smallest such that the grid stays within about one resident generation of
+// blocks (4 per CU).  Workspace: the block partials (o, max, sum) and, for a
+// standalone call, the query heads' tables.
 void plan_attn(const sikv_cache_desc* c, int n_q_heads, int top_k, AttnPlan* p) {
   const int64_t BH = (int64_t)c->batch * c->n_kv_heads;
-  const int64_t L = (int64_t)kSink + top_k;
-  int split = 256;
-  while (split > 64 && BH * cdiv(L, split) < 1024) split /= 2;
-  p->split = split;
-  p->n_splits = (int)cdiv(L, split);
+  const int64_t nch = cdiv((int64_t)kSink + top_k, kAttnChunk);
+  int64_t cpb = 4;
+  while (BH * cdiv(nch, cpb) > kAttnBlocks) cpb += 4;
+  p->cpb = (int)cpb;
+  p->n_splits = (int)cdiv(nch, cpb);
   const size_t rows = (size_t)c->batch * n_q_heads * p->n_splits;
+  const size_t hq = (size_t)c->batch * n_q_heads;
   p->off_o = 0;
   p->off_ml = align_up(rows * kD * sizeof(float));
   p->off_lut = p->off_ml + align_up(rows * 2 * sizeof(float));
-  p->off_qmu = p->off_lut + align_up((size_t)c->batch * n_q_heads * kLut * sizeof(float));
-  p->bytes = p->off_qmu + align_up((size_t)c->batch * n_q_heads * sizeof(float));
+  p->off_qmu = p->off_lut + align_up(hq * kLut * sizeof(float));
+  p->off_slog = p->off_qmu + align_up(hq * sizeof(float));
+  p->bytes = p->off_slog + align_up(hq * kSink * sizeof(float));
 }
 
 bool plan_decode(const sikv_cache_desc* c, int n_q_heads, int top_k, DecodePlan* p) {
@@ -179,8 +194,8 @@ sikv_status run_score_topk(const sikv_cache_desc* c, const uint16_t* q, int n_q_
   float* inv = at<float>(ws, sp.off_inv);
   const int mode = g_force_exact.load(std::memory_order_relaxed) ? 2 : 1;
   SIKV_TRY(launch_prep(q, n_q_heads, B, Hkv, c->mu, c->codes, c->alpha, c->capacity, c->n_tokens,
-                       top_k, mode, tab, inv, at<float>(ws, sp.off_lut), at<float>(ws, sp.off_qmu),
-                       tau, s));
+                       c->k_sink, top_k, mode, tab, inv, at<float>(ws, sp.off_lut),
+                       at<float>(ws, sp.off_qmu), at<float>(ws, sp.off_slog), tau, s));
   SIKV_TRY(launch_score(B, Hkv, c->codes, c->alpha, c->capacity, c->n_tokens, tab, inv, tau,
                         sp.chunk, sp.n_chunks, ckey, ct, cnt, scores_opt, s));
   SIKV_TRY(launch_select(B, Hkv, c->codes, c->alpha, c->capacity, c->n_tokens, tab, inv, top_k,
@@ -188,26 +203,24 @@ sikv_status run_score_topk(const sikv_cache_desc* c, const uint16_t* q, int n_q_
   return SIKV_OK;
 }
 
-// Attention (+ split merge).  att_lut / att_qmu: the query heads' tables, built
-// here by a prep launch when the caller has none (standalone call).
+// Attention (+ split merge).  tab: the query heads' tables; built here by a prep
+// launch when the caller has none (standalone call).
 sikv_status run_attn(const sikv_cache_desc* c, const uint16_t* q, int n_q_heads,
                      const int32_t* idx, int top_k, float sm_scale, float* out, void* ws,
-                     const AttnPlan& ap, const float* att_lut, const float* att_qmu,
-                     hipStream_t s) {
+                     const AttnPlan& ap, const AttnTables* tab, hipStream_t s) {
   float* po = at<float>(ws, ap.off_o);
   float* pml = at<float>(ws, ap.off_ml);
-  if (att_lut == nullptr) {
-    float* lut = at<float>(ws, ap.off_lut);
-    float* qmu = at<float>(ws, ap.off_qmu);
+  AttnTables own{at<float>(ws, ap.off_lut), at<float>(ws, ap.off_qmu), at<float>(ws, ap.off_slog)};
+  if (tab == nullptr) {
     SIKV_TRY(launch_prep(q, n_q_heads, c->batch, c->n_kv_heads, c->mu, c->codes, c->alpha,
-                         c->capacity, c->n_tokens, top_k, 0, nullptr, nullptr, lut, qmu, nullptr,
-                         s));
-    att_lut = lut;
-    att_qmu = qmu;
+                         c->capacity, c->n_tokens, c->k_sink, top_k, 0, nullptr, nullptr, own.lut,
+                         own.qmu, own.slog, nullptr, s));
+    tab = &own;
   }
-  SIKV_TRY(launch_attn(q, n_q_heads, c->batch, c->n_kv_heads, c->codes, c->alpha, c->k_sink, c->v,
+  SIKV_TRY(launch_attn(n_q_heads, c->batch, c->n_kv_heads, c->codes, c->alpha, c->v,
                        c->v_stride_b, c->v_stride_h, c->v_stride_t, c->capacity, c->n_tokens, idx,
-                       top_k, att_lut, att_qmu, sm_scale, ap.split, ap.n_splits, po, pml, s));
+                       top_k, tab->lut, tab->qmu, tab->slog, sm_scale, ap.cpb, ap.n_splits, po,
+                       pml, s));
   SIKV_TRY(launch_combine(po, pml, c->batch * n_q_heads, ap.n_splits, out, s));
   return SIKV_OK;
 }
@@ -334,7 +347,7 @@ sikv_status sikv_sparse_attn(const sikv_cache_desc* c, const uint16_t* q, int32_
   plan_attn(c, n_q_heads, top_k, &ap);
   st = check_ws(ws, ws_bytes, ap.bytes);
   if (st != SIKV_OK) return st;
-  return run_attn(c, q, n_q_heads, idx, top_k, sm_scale, out, ws, ap, nullptr, nullptr,
+  return run_attn(c, q, n_q_heads, idx, top_k, sm_scale, out, ws, ap, nullptr,
                   static_cast<hipStream_t>(stream));
 }
 
@@ -358,8 +371,10 @@ sikv_status sikv_decode_step(const sikv_cache_desc* c, const uint16_t* q, int32_
   char* wsc = at<char>(ws, dp.off_score);
   st = run_score_topk(c, q, n_q_heads, top_k, idx, nullptr, wsc, dp.sp, s);
   if (st != SIKV_OK) return st;
+  const AttnTables tab{at<float>(wsc, dp.sp.off_lut), at<float>(wsc, dp.sp.off_qmu),
+                       at<float>(wsc, dp.sp.off_slog)};
   return run_attn(c, q, n_q_heads, idx, top_k, sm_scale, out, at<char>(ws, dp.off_attn), dp.ap,
-                  at<float>(wsc, dp.sp.off_lut), at<float>(wsc, dp.sp.off_qmu), s);
+                  &tab, s);
 }
 
 size_t sikv_workspace_bytes(int32_t op, const sikv_cache_desc* c, int32_t n_q_heads,

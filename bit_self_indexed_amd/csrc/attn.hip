@@ -4,24 +4,26 @@
 // technical summary §2.1 item 3 (64 full-precision sink tokens always kept) and
 // item 4 (dequantisation fused with sparse attention in one pass).
 //
-// One block per (split of <= 256 attended entries, b*h); the block serves the G
-// query heads of the KV head, so every gathered code and V row is read once per
-// KV head.  Order of work inside a block:
-//   1  each 16-lane group issues the gathers of its V rows (16 bytes per lane)
-//      as soon as the indices are known; they are consumed last;
-//   2  one lane per entry loads its code and scale (sinks: the bf16 key row);
-//   3  the per-query-head tables LUT_g[j][p] = q_g(4j..4j+3) . (sign vertex p)
-//      and q_g . mu, built once per KV head by the prep kernel, are copied to LDS;
-//   4  logits: q.k^ = q.mu + alpha * sum_j LUT_g[j][nibble_j] (the key is never
-//      materialised; rounding mu + alpha*v to fp32 first is a relative 2^-24
-//      effect, far inside the fp32 accumulation error); sinks: exact dot with
-//      the bf16 row; pre-scaled by log2(e) * sm_scale;
-//   5  per head: max, exp2, sum over the split;
-//   6  P.V from the prefetched rows, fp32 FMAs, reduced over the 16 groups,
-//      written as this split's (max, sum, o) partial.
-// The combine kernel then merges the splits.  (A last-block-merges variant
-// needs device-scope fences, which on gfx950 write back and invalidate the
-// whole L2 of the XCD in every block: far slower than one more launch.)
+// The attended list of one (b, KV head) is entries 0..63 (the sinks) followed
+// by the k selected positions.  It is cut into chunks of 32 entries; every wave
+// runs its own loop over chunks with an online softmax, so waves never wait for
+// each other until the final merge of the block's four waves.  A block serves
+// the G query heads of its KV head: each gathered code and V row is read once.
+// Per chunk, in one wave:
+//   logits   lane (e, half) computes entry e for the heads g = half, half+2, ...:
+//            q_g . k^ = q_g . mu + alpha * sum_j LUT_g[j][nibble_j]  (the key is
+//            never materialised; rounding mu + alpha*v to fp32 first would be a
+//            relative 2^-24 effect, far inside the fp32 accumulation error);
+//            sink entries take the exact bf16-key logits made by the prep kernel;
+//   softmax  chunk max per head over 32 lanes, running max / sum update,
+//            probabilities through a wave-private LDS row;
+//   P.V      16-lane group r owns entries r, r+4, ..., r+28: 16 bytes (8 bf16
+//            channels) of each V row per lane, fp32 FMAs into G x 8 accumulators.
+// The next chunk's codes, scales and V rows are requested before the current
+// chunk is computed.  The combine kernel then merges the blocks' partials.
+// (A last-block-merges variant needs device-scope fences, which on gfx950 write
+// back and invalidate the whole L2 of the XCD in every block: far slower than
+// one more launch.)
 #include <hip/hip_ext.h>
 
 #include "sikv_internal.h"
@@ -30,146 +32,179 @@ namespace sikv {
 
 namespace {
 
-constexpr int kSplitMax = 256;       // attended-list entries per block
-constexpr int kPf = kSplitMax / 16;  // V rows prefetched per 16-lane group
+constexpr int kRows = kAttnChunk / 4;  // V rows per 16-lane group per chunk
+
+// Logit inputs of one chunk for one lane.
+template <int G>
+struct ChunkRegs {
+  uint4 code;                   // code of entry (lane & 31)
+  float a;                      // its scale (0 for sinks)
+  int t;                        // its token position
+  float sl[(G + 1) / 2];        // sink logits of this lane's heads (sinks only)
+};
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 template <int G>
-__global__ __launch_bounds__(256) void attn_kernel(
-    const uint16_t* __restrict__ q, int n_q_heads, int Hkv, const uint8_t* __restrict__ codes,
-    const float* __restrict__ alpha, const uint16_t* __restrict__ k_sink,
+__device__ __forceinline__ void load_chunk(ChunkRegs<G>& r, int chunk, int L, int lane,
+                                           const int32_t* __restrict__ ib,
+                                           const uint8_t* __restrict__ crow,
+                                           const float* __restrict__ arow, int n_tokens,
+                                           const float* __restrict__ slog) {
+  const int el = lane & 31, half = lane >> 5;
+  const int e = chunk * kAttnChunk + el;
+  if (chunk * kAttnChunk < kSink) {  // sink chunk (wave-uniform)
+    r.t = e;
+    r.code = make_uint4(0u, 0u, 0u, 0u);
+    r.a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < (G + 1) / 2; ++i) r.sl[i] = slog[min(2 * i + half, G - 1) * kSink + e];
+  } else {
+    // entries past the end re-read the last one; their probabilities are zero
+    const int t = min(max(ib[min(e, L - 1) - kSink], 0), n_tokens - 1);  // clamp: memory safety
+    r.t = t;
+    r.code = *reinterpret_cast<const uint4*>(crow + (int64_t)t * kCodeBytes);
+    r.a = arow[t];
+#pragma unroll
+    for (int i = 0; i < (G + 1) / 2; ++i) r.sl[i] = 0.0f;
+  }
+}
+
+// V rows of one chunk for this lane's 16-lane group (t from load_chunk; rows
+// past the end of the list are real rows whose probability is zero).
+__device__ __forceinline__ void load_rows(uint4 (&vr)[kRows], int lane, int t,
+                                          const uint16_t* __restrict__ vb, int64_t vst) {
+  const int grp = lane >> 4;
+#pragma unroll
+  for (int u = 0; u < kRows; ++u) {
+    const int tu = __shfl(t, grp + 4 * u);
+    vr[u] = *reinterpret_cast<const uint4*>(vb + (int64_t)tu * vst);
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(256, G <= 4 ? 4 : 2) void attn_kernel(
+    int n_q_heads, int Hkv, const uint8_t* __restrict__ codes, const float* __restrict__ alpha,
     const uint16_t* __restrict__ v, int64_t vsb, int64_t vsh, int64_t vst, int capacity,
     int n_tokens, const int32_t* __restrict__ idx, int top_k, const float* __restrict__ att_lut,
-    const float* __restrict__ att_qmu, float sm_log2, int split, int n_splits,
-    float* __restrict__ part_o, float* __restrict__ part_ml) {
-  __shared__ float qf[G][kD];
+    const float* __restrict__ att_qmu, const float* __restrict__ att_slog, float sm_log2,
+    int cpb, int n_splits, float* __restrict__ part_o, float* __restrict__ part_ml) {
+  constexpr int GH = (G + 1) / 2;
   __shared__ float lutq[G][kLut];
-  __shared__ float pl[G][kSplitMax];
-  __shared__ float red[4][G][kD];
-  __shared__ float wm[G], wl[G];
+  __shared__ __align__(16) float pb[4][kAttnChunk][G];
+  __shared__ float mo[4][G][kD];
+  __shared__ float mml[4][G][2];
 
   const int bh = blockIdx.y, b = bh / Hkv, h = bh - b * Hkv;
   const int s = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int rg = tid >> 4, cg = tid & 15;
+  const int el = lane & 31, half = lane >> 5, seg = lane & 15, grp = lane >> 4;
   const int L = kSink + top_k;
-  const int e0 = s * split;
-  const int ne = min(L, e0 + split) - e0;
+  const int n_chunks = (L + kAttnChunk - 1) / kAttnChunk;
+  const int c_end = min(n_chunks, (s + 1) * cpb);
   const int64_t row0 = (int64_t)bh * capacity;
-  const int32_t* ib = idx + (int64_t)bh * top_k;
   const int64_t hq0 = (int64_t)b * n_q_heads + (int64_t)h * G;
+  const int32_t* ib = idx + (int64_t)bh * top_k;
+  const uint8_t* crow = codes + row0 * kCodeBytes;
+  const float* arow = alpha + row0;
+  const uint16_t* vb = v + (int64_t)b * vsb + (int64_t)h * vsh + seg * 8;
+  const float* slog = att_slog + hq0 * kSink;
 
-  // 1. V rows of this lane group's entries.
-  const uint16_t* vb = v + (int64_t)b * vsb + (int64_t)h * vsh + cg * 8;
-  uint4 vr[kPf];
-#pragma unroll
-  for (int u = 0; u < kPf; ++u) {
-    const int el = rg + 16 * u;
-    uint4 w = make_uint4(0u, 0u, 0u, 0u);
-    if (el < ne) {
-      const int e = e0 + el;
-      int t = e < kSink ? e : ib[e - kSink];
-      t = min(max(t, 0), n_tokens - 1);  // memory safety only: indices must be valid
-      w = *reinterpret_cast<const uint4*>(vb + (int64_t)t * vst);
-    }
-    vr[u] = w;
-  }
-  // 2. Logit inputs: one lane per entry.
-  int ta = 0;
-  uint4 ch = make_uint4(0u, 0u, 0u, 0u);
-  float a = 0.0f;
-  if (tid < ne) {
-    const int e = e0 + tid;
-    ta = e < kSink ? e : ib[e - kSink];
-    ta = min(max(ta, 0), n_tokens - 1);
-    if (ta >= kSink) {
-      ch = *reinterpret_cast<const uint4*>(codes + (row0 + ta) * kCodeBytes);
-      a = alpha[row0 + ta];
-    }
-  }
-  // 3. Tables of the G query heads (and the queries themselves if this split
-  //    holds sink entries).
+  int c = s * cpb + wave;
+  ChunkRegs<G> nx;
+  if (c < c_end) load_chunk<G>(nx, c, L, lane, ib, crow, arow, n_tokens, slog);
+
   {
     const float4* src = reinterpret_cast<const float4*>(att_lut + hq0 * kLut);
     float4* dst = reinterpret_cast<float4*>(&lutq[0][0]);
     for (int i = tid; i < G * kLut / 4; i += 256) dst[i] = src[i];
   }
-  if (e0 < kSink) {
-    const uint16_t* qb = q + hq0 * kD;
-    for (int i = tid; i < G * kD; i += 256)
-      qf[i / kD][i % kD] = __uint_as_float((uint32_t)qb[i] << 16);
-  }
-  float qmu[G];
+  float qmu[GH];
 #pragma unroll
-  for (int g = 0; g < G; ++g) qmu[g] = att_qmu[hq0 + g];
+  for (int i = 0; i < GH; ++i) qmu[i] = (2 * i + half < G) ? att_qmu[hq0 + 2 * i + half] : 0.0f;
   __syncthreads();
 
-  // 4. Logits (log2 domain).
-  if (tid < ne) {
-    float lg[G];
-    if (ta < kSink) {
-      const uint16_t* kr = k_sink + ((int64_t)bh * kSink + ta) * kD;
+  float m[G], lsum[GH], acc[G][8];
 #pragma unroll
-      for (int g = 0; g < G; ++g) lg[g] = 0.0f;
-      for (int c8 = 0; c8 < kD / 8; ++c8) {
-        const uint4 w = *reinterpret_cast<const uint4*>(kr + c8 * 8);
-        const float x[8] = {bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y),
-                            bf16lo(w.z), bf16hi(w.z), bf16lo(w.w), bf16hi(w.w)};
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) lg[g] = fmaf(qf[g][c8 * 8 + i], x[i], lg[g]);
-      }
-    } else {
-#pragma unroll
-      for (int g = 0; g < G; ++g) lg[g] = fmaf(a, lut_dot(lutq[g], ch), qmu[g]);
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) pl[g][tid] = lg[g] * sm_log2;
-  }
-  __syncthreads();
-
-  // 5. Per-head max and exp2 over the split.
-  for (int g = wave; g < G; g += 4) {
-    float mx = -INFINITY;
-    for (int i = lane; i < ne; i += 64) mx = fmaxf(mx, pl[g][i]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    float sum = 0.0f;
-    for (int i = lane; i < ne; i += 64) {
-      const float p = exp2f(pl[g][i] - mx);
-      pl[g][i] = p;
-      sum += p;
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
-    if (lane == 0) {
-      wm[g] = mx;
-      wl[g] = sum;
-    }
-  }
-  __syncthreads();
-
-  // 6. P.V over the prefetched rows.
-  float acc[G][8];
-#pragma unroll
-  for (int g = 0; g < G; ++g)
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[g][i] = 0.0f;
+  }
 #pragma unroll
-  for (int u = 0; u < kPf; ++u) {
-    const int el = rg + 16 * u;
-    if (el < ne) {
+  for (int i = 0; i < GH; ++i) lsum[i] = 0.0f;
+
+  for (; c < c_end; c += 4) {
+    const ChunkRegs<G> cur = nx;
+    if (c + 4 < c_end) load_chunk<G>(nx, c + 4, L, lane, ib, crow, arow, n_tokens, slog);
+    const bool live = c * kAttnChunk + el < L;
+    // logits (log2 domain) of this lane's heads g = 2i + half
+    float lg[GH];
+#pragma unroll
+    for (int i = 0; i < GH; ++i) {
+      const int g = min(2 * i + half, G - 1);
+      float dot;
+      if (c * kAttnChunk < kSink) {
+        dot = cur.sl[i];
+      } else {
+        dot = fmaf(cur.a, lut_dot(lutq[g], cur.code), qmu[i]);
+      }
+      lg[i] = (live && 2 * i + half < G) ? dot * sm_log2 : -INFINITY;
+    }
+    uint4 vr[kRows];
+    load_rows(vr, lane, cur.t, vb, vst);
+    // chunk max per head: heads of parity `half` live in this half of the wave
+    float cm[GH], co[GH];
+#pragma unroll
+    for (int i = 0; i < GH; ++i) {
+      float x = lg[i];
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+      cm[i] = x;
+      co[i] = __shfl_xor(x, 32);
+    }
+    float sc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mx = ((g & 1) == half) ? cm[g >> 1] : co[g >> 1];
+      const float mn = fmaxf(m[g], mx);
+      sc[g] = exp2f(m[g] - mn);
+      m[g] = mn;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[g][i] *= sc[g];
+    }
+#pragma unroll
+    for (int i = 0; i < GH; ++i) {
+      const int g1 = min(2 * i + 1, G - 1);
+      const float mg = half ? m[g1] : m[2 * i];
+      const float sg = half ? sc[g1] : sc[2 * i];
+      const float p = exp2f(lg[i] - mg);
+      lsum[i] = fmaf(lsum[i], sg, p);
+      if (2 * i + half < G) pb[wave][el][2 * i + half] = p;
+    }
+    wave_sync_lds();
+    // P.V
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {
+      const int eu = grp + 4 * u;
       const uint4 w = vr[u];
       const float x[8] = {bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y),
                           bf16lo(w.z), bf16hi(w.z), bf16lo(w.w), bf16hi(w.w)};
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float p = pl[g][el];
+        const float p = pb[wave][eu][g];
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[g][i] = fmaf(p, x[i], acc[g][i]);
       }
     }
+    wave_sync_lds();
   }
+
+  // Wave partial: sums over the four 16-lane groups and over the 32 lanes.
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -179,21 +214,46 @@ __global__ __launch_bounds__(256) void attn_kernel(
       x += __shfl_xor(x, 32);
       acc[g][i] = x;
     }
+#pragma unroll
+  for (int i = 0; i < GH; ++i) {
+    float x = lsum[i];
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    lsum[i] = x;
+  }
   if (lane < 16) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) red[wave][g][cg * 8 + i] = acc[g][i];
+      for (int i = 0; i < 8; ++i) mo[wave][g][seg * 8 + i] = acc[g][i];
+  }
+  if (el == 0) {
+#pragma unroll
+    for (int i = 0; i < GH; ++i) {
+      const int g = 2 * i + half;
+      if (g < G) {
+        mml[wave][g][0] = half ? m[min(2 * i + 1, G - 1)] : m[2 * i];
+        mml[wave][g][1] = lsum[i];
+      }
+    }
   }
   __syncthreads();
+  // Block merge of the four wave partials (waves without a chunk hold -inf, 0).
   for (int i = tid; i < G * kD; i += 256) {
-    const int g = i / kD, c = i % kD;
-    part_o[((hq0 + g) * n_splits + s) * kD + c] =
-        (red[0][g][c] + red[1][g][c]) + (red[2][g][c] + red[3][g][c]);
-  }
-  if (tid < G) {
-    part_ml[((hq0 + tid) * n_splits + s) * 2 + 0] = wm[tid];
-    part_ml[((hq0 + tid) * n_splits + s) * 2 + 1] = wl[tid];
+    const int g = i / kD, ch = i % kD;
+    const float M = fmaxf(fmaxf(mml[0][g][0], mml[1][g][0]), fmaxf(mml[2][g][0], mml[3][g][0]));
+    float o = 0.0f, l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = exp2f(mml[w][g][0] - M);
+      o = fmaf(f, mo[w][g][ch], o);
+      l = fmaf(f, mml[w][g][1], l);
+    }
+    part_o[((hq0 + g) * n_splits + s) * kD + ch] = o;
+    if (ch == 0) {
+      part_ml[((hq0 + g) * n_splits + s) * 2 + 0] = M;
+      part_ml[((hq0 + g) * n_splits + s) * 2 + 1] = l;
+    }
   }
 }
 
@@ -265,19 +325,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_attn(const uint16_t* q, int n_q_heads, int B, int Hkv, const uint8_t* codes,
-                       const float* alpha, const uint16_t* k_sink, const uint16_t* v, int64_t vsb,
-                       int64_t vsh, int64_t vst, int capacity, int n_tokens, const int32_t* idx,
-                       int top_k, const float* att_lut, const float* att_qmu, float sm_scale,
-                       int split, int n_splits, float* part_o, float* part_ml, hipStream_t s) {
-  if (split > kSplitMax) return hipErrorInvalidValue;
+hipError_t launch_attn(int n_q_heads, int B, int Hkv, const uint8_t* codes, const float* alpha,
+                       const uint16_t* v, int64_t vsb, int64_t vsh, int64_t vst, int capacity,
+                       int n_tokens, const int32_t* idx, int top_k, const float* att_lut,
+                       const float* att_qmu, const float* att_slog, float sm_scale,
+                       int chunks_per_block, int n_splits, float* part_o, float* part_ml,
+                       hipStream_t s) {
+  const int n_chunks = (kSink + top_k + kAttnChunk - 1) / kAttnChunk;
+  if (chunks_per_block < 1 || (int64_t)n_splits * chunks_per_block < n_chunks ||
+      (int64_t)(n_splits - 1) * chunks_per_block >= n_chunks)
+    return hipErrorInvalidValue;
   const float sm_log2 = sm_scale * 1.4426950408889634f;
   const dim3 grid(n_splits, B * Hkv), block(256);
 #define SIKV_ATTN_CASE(GG)                                                                     \
   case GG:                                                                                     \
-    return launch_k(KID_ATTN, attn_kernel<GG>, grid, block, 0, s, q, n_q_heads, Hkv, codes,    \
-                    alpha, k_sink, v, vsb, vsh, vst, capacity, n_tokens, idx, top_k, att_lut,  \
-                    att_qmu, sm_log2, split, n_splits, part_o, part_ml);
+    return launch_k(KID_ATTN, attn_kernel<GG>, grid, block, 0, s, n_q_heads, Hkv, codes,       \
+                    alpha, v, vsb, vsh, vst, capacity, n_tokens, idx, top_k, att_lut, att_qmu, \
+                    att_slog, sm_log2, chunks_per_block, n_splits, part_o, part_ml);
   switch (n_q_heads / Hkv) {
     SIKV_ATTN_CASE(1)
     SIKV_ATTN_CASE(2)

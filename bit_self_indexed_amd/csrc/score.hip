@@ -302,8 +302,9 @@ __device__ uint32_t block_kth_floor(const uint32_t* keys, int n, int k, uint32_t
 __global__ __launch_bounds__(1024) void prep_kernel(
     const uint16_t* __restrict__ q, int n_q_heads, int Hkv, int G, const float* __restrict__ mu,
     const uint8_t* __restrict__ codes, const float* __restrict__ alpha, int capacity, int n_tokens,
-    int rank, int mode, int* __restrict__ sel_lut, float* __restrict__ sel_inv,
-    float* __restrict__ att_lut, float* __restrict__ att_qmu, float* __restrict__ tau) {
+    const uint16_t* __restrict__ k_sink, int rank, int mode, int* __restrict__ sel_lut,
+    float* __restrict__ sel_inv, float* __restrict__ att_lut, float* __restrict__ att_qmu,
+    float* __restrict__ att_slog, float* __restrict__ tau) {
   __shared__ float qv[kMaxGroup + 1][kD];  // q_g, then the selection query (sum)
   __shared__ float mus[kD];
   __shared__ int itab[kLut];
@@ -344,6 +345,9 @@ __global__ __launch_bounds__(1024) void prep_kernel(
       a[u] = alpha[row0 + t];
     }
   }
+  // Sink key rows: 16 lanes x 8 channels per row, 64 rows.
+  const uint4 ks = *reinterpret_cast<const uint4*>(k_sink + ((int64_t)bh * kSink + (tid >> 4)) * kD +
+                                                   (tid & 15) * 8);
   const float qx = tid < G * kD ? __uint_as_float((uint32_t)q[hq0 * kD + tid] << 16) : 0.0f;
   const float mx = tid < kD ? mu[(int64_t)bh * kD + tid] : 0.0f;
   if (tid < G * kD) qv[tid / kD][tid % kD] = qx;
@@ -369,6 +373,20 @@ __global__ __launch_bounds__(1024) void prep_kernel(
   }
   for (int i = tid; i < G * kLut; i += blockDim.x)
     att_lut[hq0 * kLut + i] = lut_entry(qv[i / kLut], i % kLut);
+  // Exact logits of the sinks (full-precision keys): q_g . k_sink[r], fp32.
+  {
+    const int r = tid >> 4, c0 = (tid & 15) * 8;
+    const float x[8] = {bf16lo(ks.x), bf16hi(ks.x), bf16lo(ks.y), bf16hi(ks.y),
+                        bf16lo(ks.z), bf16hi(ks.z), bf16lo(ks.w), bf16hi(ks.w)};
+    for (int g = 0; g < G; ++g) {
+      float d = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) d = fmaf(qv[g][c0 + i], x[i], d);
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) d += __shfl_xor(d, o);
+      if ((tid & 15) == 0) att_slog[(hq0 + g) * kSink + r] = d;
+    }
+  }
   if (mode == 0) return;
   __syncthreads();
 
@@ -616,8 +634,9 @@ __global__ __launch_bounds__(1024) void select_kernel(
 // with negligible probability; the select kernel handles that case exactly anyway.
 hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const float* mu,
                        const uint8_t* codes, const float* alpha, int capacity, int n_tokens,
-                       int top_k, int mode, int* sel_lut, float* sel_inv, float* att_lut,
-                       float* att_qmu, float* tau, hipStream_t s) {
+                       const uint16_t* k_sink, int top_k, int mode, int* sel_lut,
+                       float* sel_inv, float* att_lut, float* att_qmu, float* att_slog,
+                       float* tau, hipStream_t s) {
   const int n = n_tokens - kSink;
   int rank = 1;
   if (mode == 1) {
@@ -630,8 +649,8 @@ hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const f
     }
   }
   return launch_k(KID_PREP, prep_kernel, dim3(B * Hkv), dim3(1024), 0, s, q, n_q_heads, Hkv,
-                  n_q_heads / Hkv, mu, codes, alpha, capacity, n_tokens, rank, mode, sel_lut,
-                  sel_inv, att_lut, att_qmu, tau);
+                  n_q_heads / Hkv, mu, codes, alpha, capacity, n_tokens, k_sink, rank, mode,
+                  sel_lut, sel_inv, att_lut, att_qmu, att_slog, tau);
 }
 
 hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha, int capacity,

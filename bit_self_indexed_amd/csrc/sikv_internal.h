@@ -142,10 +142,14 @@ hipError_t launch_codes(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, i
 // score.hip
 // mode 0: attention tables only; 1: all tables + sampled threshold; 2: all
 // tables + a threshold that forces the exact whole-head selection.
+// Every mode also writes the attention tables of the query heads: att_lut
+// [B*Hq][512], att_qmu [B*Hq] (q_g . mu) and att_slog [B*Hq][64] (exact sink
+// logits q_g . k_sink[r]).
 hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const float* mu,
                        const uint8_t* codes, const float* alpha, int capacity, int n_tokens,
-                       int top_k, int mode, int* sel_lut, float* sel_inv, float* att_lut,
-                       float* att_qmu, float* tau, hipStream_t s);
+                       const uint16_t* k_sink, int top_k, int mode, int* sel_lut,
+                       float* sel_inv, float* att_lut, float* att_qmu, float* att_slog,
+                       float* tau, hipStream_t s);
 hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha, int capacity,
                         int n_tokens, const int* sel_lut, const float* sel_inv, const float* tau,
                         int chunk,
@@ -158,11 +162,16 @@ hipError_t launch_select(int B, int Hkv, const uint8_t* codes, const float* alph
                          uint32_t* comp_key, int32_t* comp_t, int32_t* idx, hipStream_t s);
 
 // attn.hip
-hipError_t launch_attn(const uint16_t* q, int n_q_heads, int B, int Hkv, const uint8_t* codes,
-                       const float* alpha, const uint16_t* k_sink, const uint16_t* v, int64_t vsb,
-                       int64_t vsh, int64_t vst, int capacity, int n_tokens, const int32_t* idx,
-                       int top_k, const float* att_lut, const float* att_qmu, float sm_scale,
-                       int split, int n_splits, float* part_o, float* part_ml, hipStream_t s);
+// Attended entries are processed in chunks of kAttnChunk; a block takes
+// chunks_per_block consecutive chunks of one (b, KV head) and writes one
+// (max, sum, o) partial per query head.
+constexpr int kAttnChunk = 32;
+hipError_t launch_attn(int n_q_heads, int B, int Hkv, const uint8_t* codes, const float* alpha,
+                       const uint16_t* v, int64_t vsb, int64_t vsh, int64_t vst, int capacity,
+                       int n_tokens, const int32_t* idx, int top_k, const float* att_lut,
+                       const float* att_qmu, const float* att_slog, float sm_scale,
+                       int chunks_per_block, int n_splits, float* part_o, float* part_ml,
+                       hipStream_t s);
 hipError_t launch_combine(const float* part_o, const float* part_ml, int BHq, int n_splits,
                           float* out, hipStream_t s);
 
