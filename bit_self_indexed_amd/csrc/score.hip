@@ -10,10 +10,11 @@
 //   prep    - one block per (b, h): builds the selection query's table (the
 //             16-entry table of each 4-dim sub-vector, in int32 fixed point so
 //             that a token's 32 look-ups are summed exactly with 3-input integer
-//             adds), the attention tables of the G query heads and their q.mu;
-//             then scores a fixed, evenly spaced sample of the candidates and
-//             takes a conservative threshold tau below the expected k-th score
-//             (the whole candidate set when it is small);
+//             adds), the attention tables of the G query heads, their q.mu and
+//             the exact logits of the 64 sinks; then scores a stratified sample
+//             of 4096 candidates (16 contiguous tokens from the middle of each of
+//             256 equal segments) and takes a conservative threshold tau below
+//             the expected k-th score (the whole candidate set when it is small);
 //   score   - the HBM stream: 16-byte code + 4-byte scale per token, one lane per
 //             token, 2 KB table in LDS (16-entry look-ups never conflict in the
 //             LDS banks); tokens with score >= tau are written, in token order,
@@ -32,7 +33,7 @@ namespace sikv {
 namespace {
 
 constexpr int kSampleMax = 4096;   // sampled candidates per head
-constexpr int kSampleRun = 256;    // contiguous tokens per sample stratum
+constexpr int kSampleRun = 16;     // contiguous tokens per stratum (256 strata)
 constexpr int kSelectLds = 16384;  // candidates kept in LDS by select
 constexpr int kMaxChunks = 2048;
 constexpr int kSubMax = 1024;
@@ -258,41 +259,39 @@ __device__ __forceinline__ void load_itab(const int* __restrict__ gtab, int* ita
   for (int i = threadIdx.x; i < kLut / 4; i += blockDim.x) dst[i] = src[i];
 }
 
-// A key at or below the k-th largest of n keys in [lo, hi], within 2^-22 of the
-// span: the lower edge of the k-th largest's digit after two radix rounds (the
-// exact key when the boundary digit holds at most 64 keys).
-__device__ uint32_t block_kth_floor(const uint32_t* keys, int n, int k, uint32_t lo, uint32_t hi,
-                                    uint32_t* hist, int* tmp, uint32_t* sub, int* scount) {
-  const uint32_t span = hi - lo;
-  const int top = span ? 32 - __clz(span) : 0;
-  if (top == 0) return lo;
-  const Round r = block_round(keys, n, k, lo, top, 0u, hist, tmp);
-  const uint32_t prefix = (uint32_t)r.digit << r.shift;
-  if (r.shift == 0) return lo + prefix;
-  const int need = k - r.above;
-  const uint32_t* src = keys;
-  int ns = n;
-  if (r.count <= kSubMax) {
-    if (threadIdx.x == 0) *scount = 0;
-    __syncthreads();
-    const uint64_t want = (uint64_t)prefix >> r.shift;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-      const uint32_t key = keys[i];
-      if (((uint64_t)(key - lo) >> r.shift) == want) sub[atomicAdd(scount, 1)] = key;
-    }
-    __syncthreads();
-    src = sub;
-    ns = r.count;
-    if (ns <= 64) {
-      wave_kth(sub, ns, need, tmp + 24);
-      __syncthreads();
-      const uint32_t key = (uint32_t)tmp[24];
-      __syncthreads();
-      return key;
-    }
+// A value at or below the k-th largest of the n scores sc (1 <= k <= n), all in
+// [smin, smax]: the lower edge of the bin holding it in a 2048-bin equal-width
+// histogram, lowered by one more bin so that rounding cannot lift it above.
+// hist: LDS >= 2048; tmp: LDS >= 24 ints.
+__device__ float block_score_floor(const float* sc, int n, int k, float smin, float smax,
+                                   uint32_t* hist, int* tmp) {
+  if (!(smax > smin)) return smin;
+  constexpr int kBins = 2048;
+  const float w = (smax - smin) * (1.0f / kBins);
+  const float inv = (float)kBins / (smax - smin);
+  for (int i = threadIdx.x; i < kBins; i += blockDim.x) hist[i] = 0u;
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int d = min(max((int)((sc[i] - smin) * inv), 0), kBins - 1);
+    atomicAdd(&hist[d], 1u);
   }
-  const Round r2 = block_round(src, ns, need, lo, r.shift, prefix, hist, tmp);
-  return lo + (prefix | ((uint32_t)r2.digit << r2.shift));
+  __syncthreads();
+  const int per = (kBins + blockDim.x - 1) / blockDim.x;
+  const int d0 = threadIdx.x * per;
+  int cnt = 0;
+  for (int d = d0; d < d0 + per && d < kBins; ++d) cnt += (int)hist[d];
+  int total;
+  int pre = block_excl_scan(cnt, tmp, &total);
+  const int x = total - k;  // ascending rank of the k-th largest
+  for (int d = d0; d < d0 + per && d < kBins; ++d) {
+    const int c = (int)hist[d];
+    if (pre <= x && x < pre + c) tmp[18] = d;
+    pre += c;
+  }
+  __syncthreads();
+  const int d = tmp[18];
+  __syncthreads();
+  return smin + (float)(d - 1) * w;
 }
 
 // ------------------------------------------------------------------ prep
@@ -309,12 +308,10 @@ __global__ __launch_bounds__(1024) void prep_kernel(
   __shared__ float mus[kD];
   __shared__ int itab[kLut];
   __shared__ float red_a[2];
-  __shared__ uint32_t keys[kSampleMax];
+  __shared__ float ssc[kSampleMax];
   __shared__ uint32_t hist[2048];
-  __shared__ uint32_t sub[kSubMax];
   __shared__ int tmp[32];
   __shared__ uint32_t mm[32];
-  __shared__ int scount;
   const int bh = blockIdx.x, b = bh / Hkv, h = bh - b * Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = n_tokens - kSink;
@@ -333,13 +330,12 @@ __global__ __launch_bounds__(1024) void prep_kernel(
     c[u] = make_uint4(0u, 0u, 0u, 0u);
     a[u] = 0.0f;
     if (sample && i < m) {
-      int t;
-      if (full) {
-        t = kSink + i;
-      } else {
-        const int st = i / kSampleRun;
-        const int start = (int)(((int64_t)st * (n - kSampleRun)) / (kSampleMax / kSampleRun - 1));
-        t = kSink + start + (i - st * kSampleRun);
+      // stratum st = i / 16 of 256 equal segments: 16 tokens centred in it
+      int t = kSink + i;
+      if (!full) {
+        const int st = i / kSampleRun, ns = kSampleMax / kSampleRun;
+        const int64_t seg0 = (int64_t)st * n / ns, seg1 = (int64_t)(st + 1) * n / ns;
+        t = kSink + (int)(seg0 + (seg1 - seg0 - kSampleRun) / 2) + (i - st * kSampleRun);
       }
       c[u] = *reinterpret_cast<const uint4*>(codes + (row0 + t) * kCodeBytes);
       a[u] = alpha[row0 + t];
@@ -415,15 +411,15 @@ __global__ __launch_bounds__(1024) void prep_kernel(
   for (int u = 0; u < kPer; ++u) {
     const int i = tid + u * 1024;
     if (i < m) {
-      const uint32_t key = score_key(selection_score(itab, inv, c[u], a[u]));
-      keys[i] = key;
-      lo = min(lo, key);
-      hi = max(hi, key);
+      const float sv = selection_score(itab, inv, c[u], a[u]);
+      ssc[i] = sv;
+      lo = min(lo, score_key(sv));
+      hi = max(hi, score_key(sv));
     }
   }
-  block_minmax(lo, hi, mm, &lo, &hi);
-  const uint32_t kth = block_kth_floor(keys, m, rank, lo, hi, hist, tmp, sub, &scount);
-  if (tid == 0) tau[bh] = key_score(kth);
+  block_minmax(lo, hi, mm, &lo, &hi);  // its barriers also publish ssc
+  const float th = block_score_floor(ssc, m, rank, key_score(lo), key_score(hi), hist, tmp);
+  if (tid == 0) tau[bh] = th;
 }
 
 // ------------------------------------------------------------------ score
