@@ -1,9 +1,9 @@
 """Benchmark of the self-indexing compressed-key decode path on one MI355X.
 
-A step is one decode step of one layer: append-encode of the current token
-(its key row, frozen channel mean) then sikv_decode_step (selection-query LUT,
-LUT-GEMV score of every cached token, exact top-k, fused dequant attention
-over sinks + top-k).  Steps rotate over --layers independent layer caches so
+A step is one decode step of one layer, one sikv_append_decode_step call:
+append-encode of the current token (its key row, frozen channel mean) then
+the decode step (selection-query LUT, LUT-GEMV score of every cached token,
+exact top-k, fused dequant attention over sinks + top-k).  Steps rotate over --layers independent layer caches so
 that the working set (layers x ~174 MB at 128K context) is far larger than
 the 256 MB Infinity Cache: every step reads its cache from HBM, as in a real
 multi-layer decode.  Each layer's step is captured once in a HIP graph and
@@ -281,8 +281,9 @@ def main():
 
     def step(layer):
         c = caches[layer]
-        sk.sikv_encode(c, k_new, t_begin=N - 1, recompute_mu=False)
-        sk.sikv_decode_step(c, q_all, w.top_k, sm, idx_out=idxs[layer], out=outs[layer])
+        c.n_tokens = N - 1  # the step appends token N-1 (same row every step) and decodes
+        sk.sikv_append_decode_step(c, k_new, q_all, w.top_k, sm, idx_out=idxs[layer],
+                                   out=outs[layer])
 
     for i in range(max(args.warmup, L)):
         step(i % L)

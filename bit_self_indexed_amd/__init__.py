@@ -38,7 +38,7 @@ class SikvError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m bit_self_indexed_amd.build` "
+            f"{LIB_PATH} is not built; run `python bit_self_indexed_amd/build.py` "
             "(the HIP library is required, there is no fallback)")
     lib = ctypes.CDLL(LIB_PATH)
     _abi.declare(lib)
@@ -215,6 +215,36 @@ def sikv_decode_step(cache: Cache, q: torch.Tensor, top_k: int, sm_scale: float 
     _check(lib.sikv_decode_step(ctypes.byref(d), qb.data_ptr(), n_q, top_k, ctypes.c_float(sm),
                                 _ptr(idx_out), out.data_ptr(), ws, wsn, _stream(cache.device)),
            "sikv_decode_step")
+    return out
+
+
+def sikv_append_decode_step(cache: Cache, k_new: torch.Tensor, q: torch.Tensor, top_k: int,
+                            sm_scale: float | None = None, idx_out: torch.Tensor | None = None,
+                            out: torch.Tensor | None = None):
+    """sikv_encode of token cache.n_tokens (k_new: [B, Hkv, 1, 128]) then
+    sikv_decode_step over n_tokens + 1 tokens, in one call (raises n_tokens)."""
+    kb = _bits(k_new)
+    if kb.dim() != 4 or kb.shape[2] != 1:
+        raise ValueError("k_new must be [B, Hkv, 1, 128]")
+    ksb, ksh, _ = _strides_rows(kb, "k_new")
+    qb = _bits(q).contiguous()
+    n_q = qb.shape[1]
+    sm = 1.0 / math.sqrt(HEAD_DIM) if sm_scale is None else float(sm_scale)
+    if out is None:
+        out = torch.empty((cache.batch, n_q, HEAD_DIM), dtype=torch.float32, device=cache.device)
+    cache.n_tokens += 1
+    try:
+        d = cache.desc()
+        need = int(lib.sikv_workspace_bytes(OP_DECODE_STEP, ctypes.byref(d), n_q, top_k))
+        ws, wsn = cache.ws.get(need)
+        _check(lib.sikv_append_decode_step(ctypes.byref(d), kb.data_ptr(), ksb, ksh,
+                                           qb.data_ptr(), n_q, top_k, ctypes.c_float(sm),
+                                           _ptr(idx_out), out.data_ptr(), ws, wsn,
+                                           _stream(cache.device)),
+               "sikv_append_decode_step")
+    except Exception:
+        cache.n_tokens -= 1
+        raise
     return out
 
 

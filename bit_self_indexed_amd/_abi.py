@@ -47,6 +47,8 @@ SIGNATURES = {
     "sikv_score_topk": (_I32, [_DESC, _P, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "sikv_sparse_attn": (_I32, [_DESC, _P, _I32, _P, _I32, C.c_float, _P, _P, _SZ, _P]),
     "sikv_decode_step": (_I32, [_DESC, _P, _I32, _I32, C.c_float, _P, _P, _P, _SZ, _P]),
+    "sikv_append_decode_step": (_I32, [_DESC, _P, _I64, _I64, _P, _I32, _I32, C.c_float, _P, _P,
+                                       _P, _SZ, _P]),
     "sikv_workspace_bytes": (_SZ, [_I32, _DESC, _I32, _I32]),
     "sikv_status_str": (C.c_char_p, [_I32]),
     "sikv_abi_version": (_I32, []),

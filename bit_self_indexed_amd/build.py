@@ -2,7 +2,8 @@
 
 Every call recompiles every source (no staleness check), in parallel, into
 ``_build/`` at the repository root, then links ``bit_self_indexed_amd/libsikv.so``.
-Run ``python -m bit_self_indexed_amd.build`` or call ``build()``.
+Run ``python bit_self_indexed_amd/build.py`` (as a script: importing the package
+needs a built library) or call ``build()``.
 """
 
 from __future__ import annotations

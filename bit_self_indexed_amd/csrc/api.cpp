@@ -17,7 +17,7 @@ using namespace sikv;
 
 constexpr size_t kAlign = 256;
 constexpr int kMaxChunks = 2048;
-constexpr int64_t kAttnBlocks = 1024;  // attention blocks resident at once (4 per CU)
+constexpr int64_t kAttnBlocks = 512;  // attention grid target: two blocks per CU
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -98,9 +98,10 @@ bool plan_score(const sikv_cache_desc* c, int n_q_heads, ScorePlan* p) {
 // Attention grid: the attended list (64 sinks + k) of each (b, KV head) is cut
 // into chunks of kAttnChunk entries; a block of four waves takes chunks_per_block
 // consecutive chunks (a multiple of 4, so every wave gets the same count), the
-// smallest such that the grid stays within about one resident generation of
-// blocks (4 per CU).  Workspace: the block partials (o, max, sum) and, for a
-// standalone call, the query heads' tables.
+// smallest such that the grid has at most two blocks per CU: each wave then
+// loops over several chunks with its prefetch running ahead, which measured
+// faster than more, shorter-lived blocks.  Workspace: the block partials (o,
+// max, sum) and, for a standalone call, the query heads' tables.
 void plan_attn(const sikv_cache_desc* c, int n_q_heads, int top_k, AttnPlan* p) {
   const int64_t BH = (int64_t)c->batch * c->n_kv_heads;
   const int64_t nch = cdiv((int64_t)kSink + top_k, kAttnChunk);
@@ -180,9 +181,10 @@ std::atomic<int> g_force_exact{0};
 
 // prep (tables + threshold) -> score -> select.  The prep kernel also leaves the
 // query heads' attention tables in the workspace for a following attention.
+// k_new (may be null): key of token n_tokens-1, encoded by the prep kernel first.
 sikv_status run_score_topk(const sikv_cache_desc* c, const uint16_t* q, int n_q_heads, int top_k,
                            int32_t* idx, float* scores_opt, void* ws, const ScorePlan& sp,
-                           hipStream_t s) {
+                           const uint16_t* k_new, int64_t ksb, int64_t ksh, hipStream_t s) {
   const int B = c->batch, Hkv = c->n_kv_heads;
   float* tau = at<float>(ws, sp.off_tau);
   int32_t* cnt = at<int32_t>(ws, sp.off_cnt);
@@ -194,8 +196,9 @@ sikv_status run_score_topk(const sikv_cache_desc* c, const uint16_t* q, int n_q_
   float* inv = at<float>(ws, sp.off_inv);
   const int mode = g_force_exact.load(std::memory_order_relaxed) ? 2 : 1;
   SIKV_TRY(launch_prep(q, n_q_heads, B, Hkv, c->mu, c->codes, c->alpha, c->capacity, c->n_tokens,
-                       c->k_sink, top_k, mode, tab, inv, at<float>(ws, sp.off_lut),
-                       at<float>(ws, sp.off_qmu), at<float>(ws, sp.off_slog), tau, s));
+                       c->k_sink, k_new, ksb, ksh, top_k, mode, tab, inv,
+                       at<float>(ws, sp.off_lut), at<float>(ws, sp.off_qmu),
+                       at<float>(ws, sp.off_slog), tau, s));
   SIKV_TRY(launch_score(B, Hkv, c->codes, c->alpha, c->capacity, c->n_tokens, tab, inv, tau,
                         sp.chunk, sp.n_chunks, ckey, ct, cnt, scores_opt, s));
   SIKV_TRY(launch_select(B, Hkv, c->codes, c->alpha, c->capacity, c->n_tokens, tab, inv, top_k,
@@ -213,8 +216,8 @@ sikv_status run_attn(const sikv_cache_desc* c, const uint16_t* q, int n_q_heads,
   AttnTables own{at<float>(ws, ap.off_lut), at<float>(ws, ap.off_qmu), at<float>(ws, ap.off_slog)};
   if (tab == nullptr) {
     SIKV_TRY(launch_prep(q, n_q_heads, c->batch, c->n_kv_heads, c->mu, c->codes, c->alpha,
-                         c->capacity, c->n_tokens, c->k_sink, top_k, 0, nullptr, nullptr, own.lut,
-                         own.qmu, own.slog, nullptr, s));
+                         c->capacity, c->n_tokens, c->k_sink, nullptr, 0, 0, top_k, 0, nullptr,
+                         nullptr, own.lut, own.qmu, own.slog, nullptr, s));
     tab = &own;
   }
   SIKV_TRY(launch_attn(n_q_heads, c->batch, c->n_kv_heads, c->codes, c->alpha, c->v,
@@ -327,7 +330,7 @@ sikv_status sikv_score_topk(const sikv_cache_desc* c, const uint16_t* q, int32_t
   if (!plan_score(c, n_q_heads, &sp)) return SIKV_ERR_UNSUPPORTED;
   st = check_ws(ws, ws_bytes, sp.bytes);
   if (st != SIKV_OK) return st;
-  return run_score_topk(c, q, n_q_heads, top_k, idx, scores_opt, ws, sp,
+  return run_score_topk(c, q, n_q_heads, top_k, idx, scores_opt, ws, sp, nullptr, 0, 0,
                         static_cast<hipStream_t>(stream));
 }
 
@@ -351,9 +354,11 @@ sikv_status sikv_sparse_attn(const sikv_cache_desc* c, const uint16_t* q, int32_
                   static_cast<hipStream_t>(stream));
 }
 
-sikv_status sikv_decode_step(const sikv_cache_desc* c, const uint16_t* q, int32_t n_q_heads,
-                             int32_t top_k, float sm_scale, int32_t* idx_out_opt, float* out,
-                             void* ws, size_t ws_bytes, void* stream) {
+namespace {
+sikv_status decode_step(const sikv_cache_desc* c, const uint16_t* k_new, int64_t ksb, int64_t ksh,
+                        const uint16_t* q, int32_t n_q_heads, int32_t top_k, float sm_scale,
+                        int32_t* idx_out_opt, float* out, void* ws, size_t ws_bytes,
+                        void* stream) {
   sikv_status st = check_desc(c);
   if (st != SIKV_OK) return st;
   st = check_query(c, q, n_q_heads, top_k);
@@ -369,12 +374,31 @@ sikv_status sikv_decode_step(const sikv_cache_desc* c, const uint16_t* q, int32_
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t* idx = idx_out_opt ? idx_out_opt : at<int32_t>(ws, dp.off_idx);
   char* wsc = at<char>(ws, dp.off_score);
-  st = run_score_topk(c, q, n_q_heads, top_k, idx, nullptr, wsc, dp.sp, s);
+  st = run_score_topk(c, q, n_q_heads, top_k, idx, nullptr, wsc, dp.sp, k_new, ksb, ksh, s);
   if (st != SIKV_OK) return st;
   const AttnTables tab{at<float>(wsc, dp.sp.off_lut), at<float>(wsc, dp.sp.off_qmu),
                        at<float>(wsc, dp.sp.off_slog)};
   return run_attn(c, q, n_q_heads, idx, top_k, sm_scale, out, at<char>(ws, dp.off_attn), dp.ap,
                   &tab, s);
+}
+}  // namespace
+
+sikv_status sikv_decode_step(const sikv_cache_desc* c, const uint16_t* q, int32_t n_q_heads,
+                             int32_t top_k, float sm_scale, int32_t* idx_out_opt, float* out,
+                             void* ws, size_t ws_bytes, void* stream) {
+  return decode_step(c, nullptr, 0, 0, q, n_q_heads, top_k, sm_scale, idx_out_opt, out, ws,
+                     ws_bytes, stream);
+}
+
+sikv_status sikv_append_decode_step(const sikv_cache_desc* c, const uint16_t* k_new,
+                                    int64_t k_stride_b, int64_t k_stride_h, const uint16_t* q,
+                                    int32_t n_q_heads, int32_t top_k, float sm_scale,
+                                    int32_t* idx_out_opt, float* out, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  if (k_new == nullptr || misaligned(k_new, 16) || bad_strides(k_stride_b, k_stride_h, 0))
+    return SIKV_ERR_INVALID_ARG;
+  return decode_step(c, k_new, k_stride_b, k_stride_h, q, n_q_heads, top_k, sm_scale, idx_out_opt,
+                     out, ws, ws_bytes, stream);
 }
 
 size_t sikv_workspace_bytes(int32_t op, const sikv_cache_desc* c, int32_t n_q_heads,

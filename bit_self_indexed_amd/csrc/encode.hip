@@ -19,11 +19,6 @@ namespace sikv {
 
 namespace {
 
-__device__ __forceinline__ float chan(const uint4& w, int c) {
-  const uint32_t x = (c >> 1) == 0 ? w.x : (c >> 1) == 1 ? w.y : (c >> 1) == 2 ? w.z : w.w;
-  return (c & 1) ? bf16hi(x) : bf16lo(x);
-}
-
 // Pairwise tree over 16 leaves (one aligned 16-leaf subtree).
 __device__ __forceinline__ float tree16(const float* l) {
   const float a0 = l[0] + l[1], a1 = l[2] + l[3], a2 = l[4] + l[5], a3 = l[6] + l[7];
@@ -95,10 +90,8 @@ __global__ __launch_bounds__(128) void mu_final_kernel(const float* __restrict__
 }
 
 // Codes, scales and sink copy: one block per (128-token tile, b*h); 16 lanes per
-// 256-byte key row, 8 channels (one code byte) per lane, 8 rows per thread.
-// bit c = (k_c < mu_c); scale = tree(|fl(k_c - mu_c)|) * 2^-7 where the lane's 8
-// channels form an aligned subtree and the xor butterfly over lanes 1,2,4,8 forms
-// the top levels (each lane ends with the same bits).
+// 256-byte key row (encode_row16), 8 channels (one code byte) per lane, 8 rows
+// per thread.
 __global__ __launch_bounds__(256) void codes_kernel(const uint16_t* __restrict__ k, int64_t sb,
                                                     int64_t sh, int64_t st, int Hkv, int t_begin,
                                                     int t_end, int capacity,
@@ -127,25 +120,11 @@ __global__ __launch_bounds__(256) void codes_kernel(const uint16_t* __restrict__
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int t = tb + i * 16 + rs;
-    uint32_t byte = 0;
-    float a[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const float x = chan(w[i], c);
-      byte |= (x < m[c] ? 1u : 0u) << c;
-      a[c] = fabsf(x - m[c]);
-    }
-    float s = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    s += __shfl_xor(s, 4);
-    s += __shfl_xor(s, 8);
-    const uint32_t v16 = byte | (__shfl_down(byte, 1, 16) << 8);
-    const uint32_t v32 = v16 | (__shfl_down(v16, 2, 16) << 16);
+    const RowCode rc = encode_row16(w[i], m);
     if (t < t_end) {
       const int64_t row = (int64_t)bh * capacity + t;
-      if ((cg & 3) == 0) *reinterpret_cast<uint32_t*>(codes + row * kCodeBytes + cg) = v32;
-      if (cg == 0) alpha[row] = s * 0.0078125f;
+      if ((cg & 3) == 0) *reinterpret_cast<uint32_t*>(codes + row * kCodeBytes + cg) = rc.word;
+      if (cg == 0) alpha[row] = rc.alpha;
       if (t < kSink)
         *reinterpret_cast<uint4*>(k_sink + ((int64_t)bh * kSink + t) * kD + cg * 8) = w[i];
     }

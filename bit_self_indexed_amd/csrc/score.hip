@@ -297,13 +297,16 @@ __device__ float block_score_floor(const float* sc, int n, int k, float smin, fl
 // ------------------------------------------------------------------ prep
 // mode 0: attention tables only (sel_lut, sel_inv and tau unused); 1: all tables
 // + sampled threshold; 2: all tables + tau = +inf (forces the exact whole-head
-// selection).  Every global load is issued before the first barrier.
+// selection).  k_new != null: first encode the key of token n_tokens-1 (append);
+// the sample then leaves that token out.  Every global load is issued before
+// the first barrier.
 __global__ __launch_bounds__(1024) void prep_kernel(
     const uint16_t* __restrict__ q, int n_q_heads, int Hkv, int G, const float* __restrict__ mu,
-    const uint8_t* __restrict__ codes, const float* __restrict__ alpha, int capacity, int n_tokens,
-    const uint16_t* __restrict__ k_sink, int rank, int mode, int* __restrict__ sel_lut,
-    float* __restrict__ sel_inv, float* __restrict__ att_lut, float* __restrict__ att_qmu,
-    float* __restrict__ att_slog, float* __restrict__ tau) {
+    uint8_t* __restrict__ codes, float* __restrict__ alpha, int capacity, int n_tokens,
+    const uint16_t* __restrict__ k_sink, const uint16_t* __restrict__ k_new, int64_t ksb,
+    int64_t ksh, int rank, int mode, int* __restrict__ sel_lut, float* __restrict__ sel_inv,
+    float* __restrict__ att_lut, float* __restrict__ att_qmu, float* __restrict__ att_slog,
+    float* __restrict__ tau) {
   __shared__ float qv[kMaxGroup + 1][kD];  // q_g, then the selection query (sum)
   __shared__ float mus[kD];
   __shared__ int itab[kLut];
@@ -314,12 +317,23 @@ __global__ __launch_bounds__(1024) void prep_kernel(
   __shared__ uint32_t mm[32];
   const int bh = blockIdx.x, b = bh / Hkv, h = bh - b * Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = n_tokens - kSink;
+  const int n = n_tokens - kSink - (k_new != nullptr ? 1 : 0);  // candidates the sample covers
   const bool full = n <= kSampleMax;
   const int m = full ? n : kSampleMax;
-  const bool sample = mode == 1 && (full || rank <= m);
+  const bool sample = mode == 1 && m > 0 && rank <= m;
   const int64_t row0 = (int64_t)bh * capacity;
   const int64_t hq0 = (int64_t)b * n_q_heads + (int64_t)h * G;
+
+  // Appended key row: 16 lanes x 8 channels, with the matching means.
+  uint4 kw = make_uint4(0u, 0u, 0u, 0u);
+  float km[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (k_new != nullptr && tid < 16) {
+    kw = *reinterpret_cast<const uint4*>(k_new + (int64_t)b * ksb + (int64_t)h * ksh + tid * 8);
+    const float4 m0 = *reinterpret_cast<const float4*>(mu + (int64_t)bh * kD + tid * 8);
+    const float4 m1 = *reinterpret_cast<const float4*>(mu + (int64_t)bh * kD + tid * 8 + 4);
+    km[0] = m0.x; km[1] = m0.y; km[2] = m0.z; km[3] = m0.w;
+    km[4] = m1.x; km[5] = m1.y; km[6] = m1.z; km[7] = m1.w;
+  }
 
   constexpr int kPer = kSampleMax / 1024;
   uint4 c[kPer];
@@ -348,6 +362,12 @@ __global__ __launch_bounds__(1024) void prep_kernel(
   const float mx = tid < kD ? mu[(int64_t)bh * kD + tid] : 0.0f;
   if (tid < G * kD) qv[tid / kD][tid % kD] = qx;
   if (tid < kD) mus[tid] = mx;
+  if (k_new != nullptr && wave == 0) {  // the whole wave runs the 16-lane shuffles
+    const RowCode rc = encode_row16(kw, km);
+    const int64_t row = row0 + n_tokens - 1;
+    if (tid < 16 && (tid & 3) == 0) *reinterpret_cast<uint32_t*>(codes + row * kCodeBytes + tid) = rc.word;
+    if (tid == 0) alpha[row] = rc.alpha;
+  }
   __syncthreads();
 
   // Selection query (fp32 sum, g ascending) and sum |qbar|; q_g . mu; attention
@@ -629,11 +649,11 @@ __global__ __launch_bounds__(1024) void select_kernel(
 // standard deviations and a small floor, so that fewer than k tokens pass only
 // with negligible probability; the select kernel handles that case exactly anyway.
 hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const float* mu,
-                       const uint8_t* codes, const float* alpha, int capacity, int n_tokens,
-                       const uint16_t* k_sink, int top_k, int mode, int* sel_lut,
-                       float* sel_inv, float* att_lut, float* att_qmu, float* att_slog,
-                       float* tau, hipStream_t s) {
-  const int n = n_tokens - kSink;
+                       uint8_t* codes, float* alpha, int capacity, int n_tokens,
+                       const uint16_t* k_sink, const uint16_t* k_new, int64_t ksb, int64_t ksh,
+                       int top_k, int mode, int* sel_lut, float* sel_inv, float* att_lut,
+                       float* att_qmu, float* att_slog, float* tau, hipStream_t s) {
+  const int n = n_tokens - kSink - (k_new != nullptr ? 1 : 0);
   int rank = 1;
   if (mode == 1) {
     if (n <= kSampleMax) {
@@ -645,8 +665,8 @@ hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const f
     }
   }
   return launch_k(KID_PREP, prep_kernel, dim3(B * Hkv), dim3(1024), 0, s, q, n_q_heads, Hkv,
-                  n_q_heads / Hkv, mu, codes, alpha, capacity, n_tokens, k_sink, rank, mode,
-                  sel_lut, sel_inv, att_lut, att_qmu, att_slog, tau);
+                  n_q_heads / Hkv, mu, codes, alpha, capacity, n_tokens, k_sink, k_new, ksb, ksh,
+                  rank, mode, sel_lut, sel_inv, att_lut, att_qmu, att_slog, tau);
 }
 
 hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha, int capacity,

@@ -39,6 +39,42 @@ enum KernelId {
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Channel c (0..7) of 8 bf16 values packed in a uint4.
+__device__ __forceinline__ float chan(const uint4& w, int c) {
+  const uint32_t x = (c >> 1) == 0 ? w.x : (c >> 1) == 1 ? w.y : (c >> 1) == 2 ? w.z : w.w;
+  return (c & 1) ? bf16hi(x) : bf16lo(x);
+}
+
+// Sign code and scale of one key row held by 16 consecutive lanes (lane cg of
+// the group: channels 8cg..8cg+7 in w, their means in m).  Bit c = (k_c < mu_c)
+// (§2.1 item 1, entropy-aware normalisation then sign); scale = adjacent-pair
+// fp32 tree of |fl(k_c - mu_c)| over the 128 channels, times 2^-7: each lane's 8
+// channels are an aligned subtree and the xor butterfly over lanes 1, 2, 4, 8
+// forms the top levels, so every lane ends with the same bits.  Returns, in lane
+// cg with cg % 4 == 0, the code bytes of channels 8cg..8cg+31 as one word.
+struct RowCode {
+  uint32_t word;
+  float alpha;
+};
+__device__ __forceinline__ RowCode encode_row16(const uint4& w, const float (&m)[8]) {
+  uint32_t byte = 0;
+  float a[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float x = chan(w, c);
+    byte |= (x < m[c] ? 1u : 0u) << c;
+    a[c] = fabsf(x - m[c]);
+  }
+  float s = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+  s += __shfl_xor(s, 1);
+  s += __shfl_xor(s, 2);
+  s += __shfl_xor(s, 4);
+  s += __shfl_xor(s, 8);
+  const uint32_t v16 = byte | (__shfl_down(byte, 1, 16) << 8);
+  const uint32_t v32 = v16 | (__shfl_down(v16, 2, 16) << 16);
+  return RowCode{v32, s * 0.0078125f};
+}
+
 // Order-preserving map of fp32 (no NaN) to uint32.
 __device__ __forceinline__ uint32_t score_key(float s) {
   uint32_t u = __float_as_uint(s);
@@ -145,11 +181,15 @@ hipError_t launch_codes(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, i
 // Every mode also writes the attention tables of the query heads: att_lut
 // [B*Hq][512], att_qmu [B*Hq] (q_g . mu) and att_slog [B*Hq][64] (exact sink
 // logits q_g . k_sink[r]).
+// k_new (may be null): bf16 key of token n_tokens-1, element (b,h,c) at
+// k_new[b*ksb + h*ksh + c]; the kernel first encodes it into codes / alpha
+// (append with the frozen mean, bit-identical to launch_codes) and leaves that
+// token out of its sample.
 hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const float* mu,
-                       const uint8_t* codes, const float* alpha, int capacity, int n_tokens,
-                       const uint16_t* k_sink, int top_k, int mode, int* sel_lut,
-                       float* sel_inv, float* att_lut, float* att_qmu, float* att_slog,
-                       float* tau, hipStream_t s);
+                       uint8_t* codes, float* alpha, int capacity, int n_tokens,
+                       const uint16_t* k_sink, const uint16_t* k_new, int64_t ksb, int64_t ksh,
+                       int top_k, int mode, int* sel_lut, float* sel_inv, float* att_lut,
+                       float* att_qmu, float* att_slog, float* tau, hipStream_t s);
 hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha, int capacity,
                         int n_tokens, const int* sel_lut, const float* sel_inv, const float* tau,
                         int chunk,

@@ -162,6 +162,24 @@ sikv_status sikv_decode_step(const sikv_cache_desc *cache, const uint16_t *q, in
                              int32_t top_k, float sm_scale, int32_t *idx_out_opt, float *out,
                              void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * sikv_append_decode_step - the current token's key enters the cache and the
+ * step runs, in one call: exactly sikv_encode(k_new, t_begin = n_tokens-1,
+ * t_end = n_tokens, recompute_mu = 0) followed by sikv_decode_step, with the
+ * encode folded into the step's first kernel (one launch fewer per step).
+ * Results (codes and scale of the new row, idx, out) are bit-identical to the
+ * two calls.  n_tokens already counts the new token.
+ *   k_new  bf16 key of token n_tokens-1: element (b,h,c) at
+ *          k_new[b*k_stride_b + h*k_stride_h + c] (strides in elements,
+ *          multiples of 8; 16-byte aligned).
+ * Workspace: SIKV_OP_DECODE_STEP.
+ */
+sikv_status sikv_append_decode_step(const sikv_cache_desc *cache, const uint16_t *k_new,
+                                    int64_t k_stride_b, int64_t k_stride_h, const uint16_t *q,
+                                    int32_t n_q_heads, int32_t top_k, float sm_scale,
+                                    int32_t *idx_out_opt, float *out, void *ws, size_t ws_bytes,
+                                    void *stream);
+
 /* Workspace bytes needed by `op` (SIKV_OP_*) for this cache and call shape.
  * Host only, launches nothing.  Returns 0 for an invalid combination. */
 size_t sikv_workspace_bytes(int32_t op, const sikv_cache_desc *cache, int32_t n_q_heads,

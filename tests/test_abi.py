@@ -136,6 +136,24 @@ def test_attention_and_decode_validation():
                                 None) == WORKSPACE
 
 
+def test_append_decode_validation():
+    d = desc()
+    f = C.c_float
+    need = lib.sikv_workspace_bytes(3, C.byref(d), 4, 16)
+    # missing or misaligned new key row, bad strides: rejected before any launch
+    assert lib.sikv_append_decode_step(C.byref(d), None, 1024, 128, FAKE, 4, 16, f(0.088), None,
+                                       FAKE, FAKE, need, None) == INVALID
+    assert lib.sikv_append_decode_step(C.byref(d), FAKE + 2, 1024, 128, FAKE, 4, 16, f(0.088),
+                                       None, FAKE, FAKE, need, None) == INVALID
+    assert lib.sikv_append_decode_step(C.byref(d), FAKE, 1024, 100, FAKE, 4, 16, f(0.088), None,
+                                       FAKE, FAKE, need, None) == INVALID
+    assert lib.sikv_append_decode_step(C.byref(d), FAKE, 1024, 128, FAKE, 4, 16, f(0.088), None,
+                                       FAKE, FAKE, need - 256, None) == WORKSPACE
+    nd = desc(v=None)
+    assert lib.sikv_append_decode_step(C.byref(nd), FAKE, 1024, 128, FAKE, 4, 16, f(0.088), None,
+                                       FAKE, FAKE, need, None) == INVALID
+
+
 def test_encode_validation():
     d = desc()
     e = lib.sikv_encode

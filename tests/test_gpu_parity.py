@@ -170,6 +170,42 @@ def test_append_and_strided_inputs():
             check_rows(out[b, h * G:(h + 1) * G], ref, f"append attn b={b} h={h}")
 
 
+def test_fused_append_matches_separate_calls():
+    """sikv_append_decode_step == sikv_encode (append) + sikv_decode_step, bit for bit
+    (new row's code and scale, idx, attention output), at a small and a multi-tile size."""
+    for w in (S.custom("fused_small", 1, 4, 1, 3000, 200, n_planted=8, cfg_id=120),
+              S.custom("fused_multi", 2, 8, 2, 9000, 700, n_planted=8, cfg_id=121)):
+        say(f"[parity] case={w.name} N={w.n_tokens}")
+        d = S.draw(w)
+        K, V, q = dev_bf16(d["K"]), dev_bf16(d["V"]), dev_bf16(d["q"])
+        N = w.n_tokens
+        res = []
+        for fused in (False, True):
+            cache = sk.Cache(w.batch, w.n_kv_heads, N, v=V)
+            sk.sikv_encode(cache, K[:, :, :N - 1])
+            idx = torch.empty((w.batch, w.n_kv_heads, w.top_k), dtype=torch.int32, device="cuda")
+            if fused:
+                out = sk.sikv_append_decode_step(cache, K[:, :, N - 1:N], q, w.top_k, SM,
+                                                 idx_out=idx)
+            else:
+                sk.sikv_encode(cache, K[:, :, N - 1:N], t_begin=N - 1, recompute_mu=False)
+                out = sk.sikv_decode_step(cache, q, w.top_k, SM, idx_out=idx)
+            torch.cuda.synchronize()
+            assert cache.n_tokens == N
+            res.append((cache.codes[:, :, N - 1].cpu().numpy(),
+                        cache.alpha[:, :, N - 1].cpu().numpy().view(np.uint32),
+                        idx.cpu().numpy(), out.cpu().numpy().view(np.uint32)))
+        for a, b, what in zip(res[0], res[1], ("code", "alpha", "idx", "out")):
+            assert np.array_equal(a, b), f"{w.name}: {what} differs"
+        # and the fused row matches the oracle's append encoding
+        for b in range(w.batch):
+            for h in range(w.n_kv_heads):
+                pre = oracle_head(d["K"][b, h, :N - 1], N - 1)
+                app = O.encode_rows(d["K"][b, h, N - 1:N], pre["mu"])
+                assert np.array_equal(res[1][0][b, h], app["codes"][0])
+                assert np.array_equal(res[1][1][b, h], app["alpha"].view(np.uint32)[0])
+
+
 def test_all_scores_tied():
     """Identical key rows: every candidate has the same score, so the top-k is the
     k smallest positions (ties go to the smaller position)."""
