@@ -24,7 +24,11 @@ entropy balance), scale (least-squares optimality, round trip), lookup table
 (all 16 sign vertices enumerated, exact identity with the dequantised dot
 product), top-k (brute-force sort, heapq), attention (dense softmax attention
 through torch's fp64 SDPA when every token is kept, q = 0, one dominant
-token), decode step (planted-token recall).  No function is left unpinned.
+token), decode step (planted-token recall), codebook (closed-form members,
+pure-sign data gives the vertices, least-squares optimality and sign
+consistency by perturbation, brute-force channel loop for its scores, dense
+SDPA with its reconstructed keys, lower reconstruction error than the
+vertices).  No function is left unpinned.
 """
 
 from __future__ import annotations
@@ -119,7 +123,7 @@ def token_scale(k_bits, mu) -> np.ndarray:
     return (tree_sum_f32(a, axis=-1) * np.float32(2.0 ** -7)).astype(np.float32)
 
 
-def encode(k_bits, n_tokens: int) -> dict:
+def encode(k_bits, n_tokens: int, with_codebook: bool = False) -> dict:
     """Prefill compression of one cache (§2.1 items 1 and 3).
 
     k_bits: [B, H, >=N, 128] bf16 bits.  Returns mu [B,H,128] f32, codes
@@ -129,12 +133,19 @@ def encode(k_bits, n_tokens: int) -> dict:
     k_bits = np.asarray(k_bits)
     mu = channel_mean(k_bits, n_tokens)
     rows = k_bits[..., :n_tokens, :]
-    return {
+    out = {
         "mu": mu,
         "codes": pack_codes(sign_bits(rows, mu)),
         "alpha": token_scale(rows, mu),
         "k_sink": np.array(k_bits[..., :N_SINK, :], dtype=np.uint16),
     }
+    if with_codebook:   # optional data-derived centres (``codebook``), per (b, h)
+        lead = k_bits.shape[:-2]
+        cb = np.zeros(lead + (N_SUB, N_PATTERNS, SUB_DIM), np.float32)
+        for ix in np.ndindex(*lead):
+            cb[ix] = codebook(k_bits[ix], mu[ix], out["codes"][ix], out["alpha"][ix], n_tokens)
+        out["codebook"] = cb
+    return out
 
 
 def encode_rows(k_bits, mu) -> dict:
@@ -143,14 +154,58 @@ def encode_rows(k_bits, mu) -> dict:
     return {"codes": pack_codes(sign_bits(k_bits, mu)), "alpha": token_scale(k_bits, mu)}
 
 
-def dequantize(codes, alpha, mu) -> np.ndarray:
-    """Reconstructed key k^_c = fl32(mu_c + alpha * v_c), v_c = +1 for bit 0 and -1
-    for bit 1 (§2.1 item 1: the code doubles as the quantised key).  alpha*v is
-    exact, so this is one rounding.  Returns float32 [..., T, 128]."""
-    bits = np.unpackbits(np.asarray(codes, np.uint8), axis=-1, bitorder="little")
-    v = (1.0 - 2.0 * bits).astype(np.float32)
-    return (np.asarray(mu, np.float32)[..., None, :]
-            + np.asarray(alpha, np.float32)[..., :, None] * v).astype(np.float32)
+def dequantize(codes, alpha, mu, cb=None) -> np.ndarray:
+    """Reconstructed key k^_c = fl32(mu_c + alpha * v_c) (§2.1 item 1: the code
+    doubles as the quantised key), with v the centre of the token's cluster in
+    sub-vector j = c // 4: the sign vertex (v_c = +1 for bit 0, -1 for bit 1)
+    or, given a codebook ``cb`` [32,16,4], component c % 4 of cb[j, nibble_j].
+    mu + alpha*v is formed in fp64 and rounded once (for sign vertices alpha*v
+    is exact and this is the fp32 sum).  Returns float32 [..., T, 128]."""
+    a = np.asarray(alpha, np.float64)[..., :, None]
+    if cb is None:
+        bits = np.unpackbits(np.asarray(codes, np.uint8), axis=-1, bitorder="little")
+        v = 1.0 - 2.0 * bits.astype(np.float64)
+    else:
+        nib = code_nibbles(codes).astype(np.intp)                       # [..., T, 32]
+        v = np.asarray(cb, np.float64)[np.arange(N_SUB), nib].reshape(nib.shape[:-1] + (HEAD_DIM,))
+    return (np.asarray(mu, np.float64)[..., None, :] + a * v).astype(np.float32)
+
+
+CB_FRAC_BITS = 24   # fixed-point fraction bits of the codebook accumulators
+
+
+def codebook(k_bits, mu, codes, alpha, n_tokens: int) -> np.ndarray:
+    """Data-derived cluster centres of one (batch, KV head) (§2.1 item 1: the
+    sign pattern of a 4-dim sub-vector assigns it to one of 16 clusters in a
+    single pass, with no iterations; §2.1 item 2: the query is dotted with the
+    16 centre vectors).
+
+    READING: centre C[j, p] (4 components) = mean, over the prefill non-sink
+    tokens t in [64, N) whose sub-vector j has pattern p, of the normalised
+    sub-vector divided by the token's scale, x = fl32(fl32(k_c - mu_c) / alpha_t)
+    (a token with alpha_t = 0 adds 0).  Each x is turned into fixed point,
+    rint(x * 2^24) (int64, ties to even), so that the sums are exact and
+    order-free; C = fl32((sum * 2^-24) / count) with the division in fp64.  An
+    empty cluster keeps its sign vertex.  Frozen for appended tokens, like mu.
+
+    k_bits [>=N, 128] bf16 bits; mu [128]; codes [>=N, 16]; alpha [>=N].
+    Returns float32 [32, 16, 4]."""
+    rows = slice(N_SINK, n_tokens)
+    kt = (bf16_to_f32(np.asarray(k_bits)[rows]) - np.asarray(mu, np.float32)).astype(np.float32)
+    a = np.asarray(alpha, np.float32)[rows][:, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        x = np.where(a > 0, kt / np.where(a > 0, a, np.float32(1)), np.float32(0)).astype(np.float32)
+    fx = np.rint(x.astype(np.float64) * 2.0 ** CB_FRAC_BITS).astype(np.int64)
+    fx = fx.reshape(-1, N_SUB, SUB_DIM)                                   # [T, 32, 4]
+    nib = code_nibbles(np.asarray(codes)[rows]).astype(np.intp)           # [T, 32]
+    sums = np.zeros((N_SUB, N_PATTERNS, SUB_DIM), np.int64)
+    cnt = np.zeros((N_SUB, N_PATTERNS), np.int64)
+    for j in range(N_SUB):
+        np.add.at(sums[j], nib[:, j], fx[:, j, :])
+        np.add.at(cnt[j], nib[:, j], 1)
+    mean = (sums.astype(np.float64) * 2.0 ** -CB_FRAC_BITS) / np.maximum(cnt, 1)[..., None]
+    out = np.where(cnt[..., None] > 0, mean, centres()[None, :, :])
+    return out.astype(np.float32)
 
 
 # --------------------------------------------------------------------------- #
@@ -174,11 +229,14 @@ def group_query(q_bits, n_kv_heads: int) -> np.ndarray:
     return q.reshape(b, n_kv_heads, hq // n_kv_heads, d).sum(axis=2)
 
 
-def query_lut(qbar) -> np.ndarray:
+def query_lut(qbar, cb=None) -> np.ndarray:
     """§2.1 item 2: split the query like the key and dot each 4-dim piece with the
-    16 centres.  qbar [..., 128] -> LUT [..., 32, 16] fp64."""
+    16 centres (the sign vertices, or the codebook ``cb`` [32,16,4] of the KV
+    head).  qbar [..., 128] -> LUT [..., 32, 16] fp64."""
     qs = np.asarray(qbar, np.float64).reshape(qbar.shape[:-1] + (N_SUB, SUB_DIM))
-    return qs @ centres().T
+    if cb is None:
+        return qs @ centres().T
+    return np.einsum("...ji,jpi->...jp", qs, np.asarray(cb, np.float64))
 
 
 def code_nibbles(codes) -> np.ndarray:
@@ -218,7 +276,7 @@ def select_topk(scores, k: int, first_token: int = N_SINK) -> np.ndarray:
 # Sparse attention over top-k plus sinks: §2.1 items 3 and 4
 # --------------------------------------------------------------------------- #
 def sparse_attention(q_bits_group, idx, k_sink_bits, codes, alpha, mu, v_bits,
-                     sm_scale: float) -> np.ndarray:
+                     sm_scale: float, cb=None) -> np.ndarray:
     """Attention of the G query heads of one KV head over S = {0..63} U idx
     (§2.1 item 3: sinks always kept in full precision; item 4: keys dequantised
     inside the attention).  Keys: bf16 sink rows for t < 64, else k^_t (fp32,
@@ -227,12 +285,13 @@ def sparse_attention(q_bits_group, idx, k_sink_bits, codes, alpha, mu, v_bits,
     a decoding query sees every cached token.  fp64, returned as float32 [G,128].
 
     q_bits_group [G,128]; idx [k] (token positions >= 64); k_sink_bits [64,128];
-    codes [N,16], alpha [N], mu [128], v_bits [N,128] of that KV head."""
+    codes [N,16], alpha [N], mu [128], v_bits [N,128] of that KV head; cb: its
+    codebook or None (sign vertices)."""
     idx = np.asarray(idx, np.int64)
     q = bf16_to_f32(q_bits_group).astype(np.float64)
     kap = np.concatenate([bf16_to_f32(k_sink_bits).astype(np.float64),
                           dequantize(np.asarray(codes)[idx], np.asarray(alpha)[idx],
-                                     mu).astype(np.float64)], axis=0)
+                                     mu, cb).astype(np.float64)], axis=0)
     rows = np.concatenate([np.arange(N_SINK, dtype=np.int64), idx])
     vals = bf16_to_f32(np.asarray(v_bits)[rows]).astype(np.float64)
     logits = (kap @ q.T) * float(sm_scale)                      # [|S|, G]
@@ -243,17 +302,19 @@ def sparse_attention(q_bits_group, idx, k_sink_bits, codes, alpha, mu, v_bits,
 
 
 def head_scores(q_bits, codes, alpha, b: int, h: int, n_kv_heads: int,
-                n_tokens: int) -> np.ndarray:
-    """Selection scores of the candidates t in [64, N) of one (batch, KV head)."""
+                n_tokens: int, cb=None) -> np.ndarray:
+    """Selection scores of the candidates t in [64, N) of one (batch, KV head)
+    (cb: that head's codebook, or None for the sign vertices)."""
     qbar = group_query(q_bits[b:b + 1], n_kv_heads)[0, h]
-    return lut_scores(query_lut(qbar), codes[N_SINK:n_tokens], alpha[N_SINK:n_tokens])
+    return lut_scores(query_lut(qbar, cb), codes[N_SINK:n_tokens], alpha[N_SINK:n_tokens])
 
 
 def decode_step(q_bits, cache: dict, v_bits, top_k: int, sm_scale: float,
                 n_tokens: int, heads=None) -> dict:
     """One decode step: LUT scores -> top-k -> sparse attention, per (b, KV head).
 
-    cache: ``encode`` output (codes/alpha indexed by token).  v_bits [B,H,>=N,128].
+    cache: ``encode`` output (codes/alpha indexed by token; the codebook is used
+    when present).  v_bits [B,H,>=N,128].
     heads: optional list of (b, h) pairs to compute (others left zero / -1).
     Returns idx [B,H,k] int64 and out [B,Hq,128] float32."""
     q_bits = np.asarray(q_bits)
@@ -263,11 +324,14 @@ def decode_step(q_bits, cache: dict, v_bits, top_k: int, sm_scale: float,
     idx = np.full((b_n, n_kv, top_k), -1, np.int64)
     out = np.zeros((b_n, hq, HEAD_DIM), np.float32)
     pairs = heads if heads is not None else [(b, h) for b in range(b_n) for h in range(n_kv)]
+    cbs = cache.get("codebook")
     for b, h in pairs:
-        s = head_scores(q_bits, cache["codes"][b, h], cache["alpha"][b, h], b, h, n_kv, n_tokens)
+        cb = None if cbs is None else cbs[b, h]
+        s = head_scores(q_bits, cache["codes"][b, h], cache["alpha"][b, h], b, h, n_kv, n_tokens,
+                        cb)
         sel = select_topk(s, top_k)
         idx[b, h] = sel
         out[b, h * g:(h + 1) * g] = sparse_attention(
             q_bits[b, h * g:(h + 1) * g], sel, cache["k_sink"][b, h], cache["codes"][b, h],
-            cache["alpha"][b, h], cache["mu"][b, h], v_bits[b, h], sm_scale)
+            cache["alpha"][b, h], cache["mu"][b, h], v_bits[b, h], sm_scale, cb)
     return {"idx": idx, "out": out}

@@ -320,3 +320,134 @@ def test_planted_recall_tiny():
     enc = O.encode(d["K"], w.n_tokens)
     res = O.decode_step(d["q"], enc, d["V"], w.top_k, 1 / math.sqrt(128), w.n_tokens)
     assert set(d["planted"][0, 0].tolist()) <= set(res["idx"][0, 0].tolist())
+
+
+# ----------------------------------------------------------------- codebook
+def _cb_case(rows_f32, mu_f32, alpha=None):
+    """Rows (float32 values exactly representable in bf16) -> codebook inputs."""
+    kb = _bf16(rows_f32)
+    mu = np.asarray(mu_f32, np.float32)
+    codes = O.pack_codes(O.sign_bits(kb, mu))
+    a = O.token_scale(kb, mu) if alpha is None else np.asarray(alpha, np.float32)
+    return kb, mu, codes, a
+
+
+def test_codebook_identical_members_and_pair_mean():
+    """Closed forms: members sharing x = k~/alpha give exactly that centre; two
+    members give their mean; the pattern index follows the sign bits."""
+    n = 64 + 3
+    rows = np.ones((n, 128), np.float32)
+    rows[64, :4] = [2.0, -1.0, 0.5, -0.25]           # pattern 0b1010 = 10
+    rows[65, :4] = [2.0, -1.0, 0.5, -0.25]
+    rows[66, :4] = [4.0, -3.0, 1.5, -0.75]           # same pattern
+    alpha = np.ones(n, np.float32)
+    alpha[66] = 2.0                                   # x = (2, -1.5, 0.75, -0.375)
+    kb, mu, codes, a = _cb_case(rows, np.zeros(128, np.float32), alpha)
+    cb = O.codebook(kb, mu, codes, a, n)
+    exp = (np.array([2.0, -1.0, 0.5, -0.25]) * 2 + np.array([2.0, -1.5, 0.75, -0.375])) / 3
+    assert np.array_equal(cb[0, 10], exp.astype(np.float32))
+    # sub-vector 1 of every member is (1,1,1,1) -> pattern 0, centre exactly 1 / alpha mean
+    assert np.allclose(cb[1, 0], (1.0 + 1.0 + 0.5) / 3, rtol=0, atol=2 ** -24)
+    # all other clusters are empty -> sign vertices
+    v = O.centres()
+    for p in range(16):
+        if p != 10:
+            assert np.array_equal(cb[0, p], v[p].astype(np.float32))
+
+
+def test_codebook_of_pure_sign_data_is_the_vertices():
+    """|k_c - mu_c| = alpha for every channel: every member is exactly a sign
+    vertex, so every non-empty centre is its vertex."""
+    rng = np.random.default_rng(21)
+    n = 64 + 500
+    mu = rng.integers(-4, 4, 128).astype(np.float32)
+    sgn = np.where(rng.random((n, 128)) < 0.5, -1.0, 1.0).astype(np.float32)
+    kb, mu, codes, a = _cb_case(mu + 0.5 * sgn, mu)
+    assert np.all(a == 0.5)
+    cb = O.codebook(kb, mu, codes, a, n)
+    assert np.array_equal(cb, np.broadcast_to(O.centres()[None], cb.shape).astype(np.float32))
+
+
+def test_codebook_is_least_squares_and_sign_consistent():
+    """For fixed assignments the mean minimises the squared error of x = k~/alpha
+    (perturbation), and every component has the sign its pattern bit implies."""
+    rng = np.random.default_rng(22)
+    n = 64 + 3000
+    kb = _rand_keys(rng, n)[0]
+    mu = O.channel_mean(kb, n)
+    codes = O.pack_codes(O.sign_bits(kb, mu))
+    a = O.token_scale(kb, mu)
+    cb = O.codebook(kb, mu, codes, a, n).astype(np.float64)
+    x = ((S.bf16_bits_to_f32(kb[64:]) - mu).astype(np.float32) / a[64:, None]).astype(np.float64)
+    nib = O.code_nibbles(codes[64:])
+    for j in (0, 7, 31):
+        for p in range(16):
+            m = x[nib[:, j] == p, 4 * j:4 * j + 4]
+            if len(m) == 0:
+                continue
+            f0 = ((m - cb[j, p]) ** 2).sum()
+            for i in range(4):
+                for eps in (1e-3, -1e-3):
+                    c = cb[j, p].copy()
+                    c[i] += eps
+                    assert ((m - c) ** 2).sum() > f0
+            bits = (p >> np.arange(4)) & 1
+            assert np.all(np.where(bits == 1, cb[j, p] < 0, cb[j, p] > 0))
+
+
+def test_codebook_lut_scores_match_bruteforce():
+    """LUT scores with data centres equal alpha * sum_c qbar_c * centre component,
+    accumulated channel by channel in a plain loop (tiny case)."""
+    rng = np.random.default_rng(23)
+    n = 64 + 40
+    kb = _rand_keys(rng, n)[0]
+    enc = O.encode(kb[None, None], n, with_codebook=True)
+    cb, codes, a = enc["codebook"][0, 0], enc["codes"][0, 0], enc["alpha"][0, 0]
+    qbar = rng.standard_normal(128)
+    s = O.lut_scores(O.query_lut(qbar, cb), codes[64:], a[64:])
+    for t in range(40):
+        acc = 0.0
+        for c in range(128):
+            byte = int(codes[64 + t, c // 8])
+            j = c // 4
+            p = (byte >> (4 * (j & 1))) & 0xF
+            acc += qbar[c] * float(cb[j, p, c % 4])
+        assert abs(s[t] - float(a[64 + t]) * acc) <= 1e-12 * (1 + abs(s[t]))
+    # and the dequantised keys reproduce the same dot products
+    kh = O.dequantize(codes[64:], a[64:], enc["mu"][0, 0], cb).astype(np.float64)
+    direct = (kh - enc["mu"][0, 0].astype(np.float64)) @ qbar
+    assert np.allclose(direct, s, rtol=1e-5, atol=1e-5)
+
+
+def test_codebook_attention_all_tokens_equals_dense_sdpa():
+    """With data centres and k = N - 64 the sparse path is dense attention over
+    [K_sink; K^(codebook)]."""
+    rng = np.random.default_rng(24)
+    B, Hq, Hkv, N, G, sm = 1, 2, 1, 200, 2, 1 / math.sqrt(128)
+    q = _bf16(rng.standard_normal((B, Hq, 128)))
+    k = _bf16(rng.normal(0, 1.5, (B, Hkv, 1, 128)) + rng.standard_normal((B, Hkv, N, 128)))
+    v = _bf16(rng.standard_normal((B, Hkv, N, 128)))
+    enc = O.encode(k, N, with_codebook=True)
+    res = O.decode_step(q, enc, v, N - 64, sm, N)
+    kap = np.concatenate([S.bf16_bits_to_f32(enc["k_sink"][0, 0]),
+                          O.dequantize(enc["codes"][0, 0, 64:], enc["alpha"][0, 0, 64:],
+                                       enc["mu"][0, 0], enc["codebook"][0, 0])]).astype(np.float64)
+    qq = torch.tensor(S.bf16_bits_to_f32(q[0]), dtype=torch.float64)
+    kk = torch.tensor(kap)[None].expand(G, -1, -1)
+    vv = torch.tensor(S.bf16_bits_to_f32(v[0, 0]).astype(np.float64))[None].expand(G, -1, -1)
+    ref = torch.nn.functional.scaled_dot_product_attention(qq[:, None, :], kk, vv, scale=sm)[:, 0]
+    assert np.allclose(res["out"][0], ref.numpy(), rtol=1e-6, atol=1e-7)
+
+
+def test_codebook_reconstruction_beats_vertices():
+    """The data centres reconstruct the keys with less squared error than the
+    scaled sign vertices (they are the per-cluster least-squares fit)."""
+    rng = np.random.default_rng(25)
+    n = 64 + 2000
+    kb = _rand_keys(rng, n)[0]
+    enc = O.encode(kb[None, None], n, with_codebook=True)
+    x = S.bf16_bits_to_f32(kb[64:]).astype(np.float64)
+    c, a, mu = enc["codes"][0, 0, 64:], enc["alpha"][0, 0, 64:], enc["mu"][0, 0]
+    e_cb = ((O.dequantize(c, a, mu, enc["codebook"][0, 0]) - x) ** 2).sum()
+    e_v = ((O.dequantize(c, a, mu) - x) ** 2).sum()
+    assert e_cb < e_v
