@@ -107,11 +107,12 @@ class Cache:
 
     codes uint8 [B,Hkv,cap,16], alpha fp32 [B,Hkv,cap], mu fp32 [B,Hkv,128],
     k_sink bf16 [B,Hkv,64,128] are owned here; ``v`` (bf16 [B,Hkv,>=cap,128],
-    unit channel stride) is only referenced.
+    unit channel stride) is only referenced.  codebook=True adds data-derived
+    centres, fp32 [B,Hkv,32,16,4], written at prefill and used by every call.
     """
 
     def __init__(self, batch: int, n_kv_heads: int, capacity: int, device="cuda",
-                 v: torch.Tensor | None = None):
+                 v: torch.Tensor | None = None, codebook: bool = False):
         dev = torch.device(device)
         self.batch, self.n_kv_heads, self.capacity = batch, n_kv_heads, capacity
         self.n_tokens = 0
@@ -120,6 +121,8 @@ class Cache:
         self.mu = torch.zeros((batch, n_kv_heads, HEAD_DIM), dtype=torch.float32, device=dev)
         self.k_sink = torch.zeros((batch, n_kv_heads, N_SINK, HEAD_DIM), dtype=torch.bfloat16,
                                   device=dev)
+        self.codebook = (torch.zeros((batch, n_kv_heads, 32, 16, 4), dtype=torch.float32,
+                                     device=dev) if codebook else None)
         self.v = v
         self.ws = Workspace(dev)
 
@@ -139,7 +142,7 @@ class Cache:
             sb, sh, st = _strides_rows(self.v, "v")
             d.v = self.v.data_ptr()
             d.v_stride_b, d.v_stride_h, d.v_stride_t = sb, sh, st
-        d.codebook = None
+        d.codebook = self.codebook.data_ptr() if self.codebook is not None else None
         return d
 
 

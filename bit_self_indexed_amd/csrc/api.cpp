@@ -25,8 +25,9 @@ inline bool misaligned(const void* p, size_t a) { return (reinterpret_cast<uintp
 
 // ------------------------------------------------------------------ plans
 struct EncodePlan {
-  int nblk;
-  size_t bytes;
+  int nblk;          // mean partial tiles per head
+  int cb_nblk;       // codebook statistics blocks per head (0: no codebook)
+  size_t off_cb, bytes;
 };
 
 struct ScorePlan {
@@ -56,8 +57,11 @@ struct DecodePlan {
 
 EncodePlan plan_encode(const sikv_cache_desc* c) {
   EncodePlan p;
+  const size_t BH = (size_t)c->batch * c->n_kv_heads;
   p.nblk = (int)cdiv(c->n_tokens, 256);
-  p.bytes = align_up((size_t)c->batch * c->n_kv_heads * p.nblk * kD * sizeof(float));
+  p.cb_nblk = c->codebook != nullptr ? cb_blocks(c->n_tokens) : 0;
+  p.off_cb = align_up(BH * p.nblk * kD * sizeof(float));
+  p.bytes = p.off_cb + align_up(BH * p.cb_nblk * kCbStride * sizeof(long long));
   return p;
 }
 
@@ -132,13 +136,13 @@ bool plan_decode(const sikv_cache_desc* c, int n_q_heads, int top_k, DecodePlan*
 // ------------------------------------------------------------------ validation
 sikv_status check_desc(const sikv_cache_desc* c) {
   if (c == nullptr) return SIKV_ERR_INVALID_ARG;
-  if (c->head_dim != kD || c->n_sink != kSink || c->codebook != nullptr) return SIKV_ERR_UNSUPPORTED;
+  if (c->head_dim != kD || c->n_sink != kSink) return SIKV_ERR_UNSUPPORTED;
   if (c->batch < 1 || c->n_kv_heads < 1 || (int64_t)c->batch * c->n_kv_heads > 65535)
     return SIKV_ERR_INVALID_ARG;
   if (c->n_tokens <= kSink || c->capacity < c->n_tokens) return SIKV_ERR_INVALID_ARG;
   if (!c->codes || !c->alpha || !c->mu || !c->k_sink) return SIKV_ERR_INVALID_ARG;
   if (misaligned(c->codes, 16) || misaligned(c->alpha, 4) || misaligned(c->mu, 16) ||
-      misaligned(c->k_sink, 16))
+      misaligned(c->k_sink, 16) || misaligned(c->codebook, 16))
     return SIKV_ERR_INVALID_ARG;
   return SIKV_OK;
 }
@@ -196,7 +200,7 @@ sikv_status run_score_topk(const sikv_cache_desc* c, const uint16_t* q, int n_q_
   float* inv = at<float>(ws, sp.off_inv);
   const int mode = g_force_exact.load(std::memory_order_relaxed) ? 2 : 1;
   SIKV_TRY(launch_prep(q, n_q_heads, B, Hkv, c->mu, c->codes, c->alpha, c->capacity, c->n_tokens,
-                       c->k_sink, k_new, ksb, ksh, top_k, mode, tab, inv,
+                       c->k_sink, k_new, ksb, ksh, c->codebook, top_k, mode, tab, inv,
                        at<float>(ws, sp.off_lut), at<float>(ws, sp.off_qmu),
                        at<float>(ws, sp.off_slog), tau, s));
   SIKV_TRY(launch_score(B, Hkv, c->codes, c->alpha, c->capacity, c->n_tokens, tab, inv, tau,
@@ -216,7 +220,8 @@ sikv_status run_attn(const sikv_cache_desc* c, const uint16_t* q, int n_q_heads,
   AttnTables own{at<float>(ws, ap.off_lut), at<float>(ws, ap.off_qmu), at<float>(ws, ap.off_slog)};
   if (tab == nullptr) {
     SIKV_TRY(launch_prep(q, n_q_heads, c->batch, c->n_kv_heads, c->mu, c->codes, c->alpha,
-                         c->capacity, c->n_tokens, c->k_sink, nullptr, 0, 0, top_k, 0, nullptr,
+                         c->capacity, c->n_tokens, c->k_sink, nullptr, 0, 0, c->codebook, top_k, 0,
+                         nullptr,
                          nullptr, own.lut, own.qmu, own.slog, nullptr, s));
     tab = &own;
   }
@@ -241,7 +246,7 @@ double g_ms[KID_COUNT];
 int64_t g_cnt[KID_COUNT];
 const char* const g_names[KID_COUNT] = {"mu_partial", "mu_final", "codes", "prep",
                                         "score",      "select",   "attn",  "combine",
-                                        "dense",      "copy"};
+                                        "dense",      "copy",     "cb_final"};
 
 hipEvent_t take_event() {
   if (!g_pool.empty()) {
@@ -312,6 +317,14 @@ sikv_status sikv_encode(const sikv_cache_desc* c, const uint16_t* k, int64_t k_s
     SIKV_TRY(launch_mu_partial(k, k_stride_b, k_stride_h, k_stride_t, c->batch, c->n_kv_heads,
                                c->n_tokens, partial, p.nblk, s));
     SIKV_TRY(launch_mu_final(partial, c->batch * c->n_kv_heads, p.nblk, c->n_tokens, c->mu, s));
+    if (c->codebook != nullptr) {  // codes + codebook statistics in one pass, then the centres
+      long long* part = at<long long>(ws, p.off_cb);
+      SIKV_TRY(launch_codes_cb(k, k_stride_b, k_stride_h, k_stride_t, c->batch, c->n_kv_heads,
+                               c->n_tokens, c->capacity, c->mu, c->codes, c->alpha, c->k_sink,
+                               part, s));
+      SIKV_TRY(launch_cb_final(part, c->batch * c->n_kv_heads, p.cb_nblk, c->codebook, s));
+      return SIKV_OK;
+    }
   }
   SIKV_TRY(launch_codes(k, k_stride_b, k_stride_h, k_stride_t, c->batch, c->n_kv_heads, t_begin,
                         t_end, c->capacity, c->mu, c->codes, c->alpha, c->k_sink, s));

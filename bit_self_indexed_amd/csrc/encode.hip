@@ -89,19 +89,31 @@ __global__ __launch_bounds__(128) void mu_final_kernel(const float* __restrict__
   mu[(int64_t)bh * kD + c] = __fdiv_rn(stk[levels][c], (float)(n_tokens - kSink));
 }
 
-// Codes, scales and sink copy: one block per (128-token tile, b*h); 16 lanes per
-// 256-byte key row (encode_row16), 8 channels (one code byte) per lane, 8 rows
-// per thread.
+// Codes, scales and sink copy: one block per (tpb 128-token tiles, b*h); 16
+// lanes per 256-byte key row (encode_row16), 8 channels (one code byte) per lane,
+// 8 rows per thread and tile.  CB: also accumulate the codebook statistics of
+// the block's tokens in [64, n_tokens) (§2.1 item 1, one-pass clustering: a
+// sub-vector's cluster is its sign pattern): x_c = fl32(fl32(k_c - mu_c) /
+// alpha), rint(x_c * 2^24) added as int64 (exact, order-free) to the bin of
+// (sub-vector, pattern), and the count of that bin; block totals go to cb_part.
+template <bool CB>
 __global__ __launch_bounds__(256) void codes_kernel(const uint16_t* __restrict__ k, int64_t sb,
                                                     int64_t sh, int64_t st, int Hkv, int t_begin,
-                                                    int t_end, int capacity,
+                                                    int t_end, int capacity, int tpb,
                                                     const float* __restrict__ mu,
                                                     uint8_t* __restrict__ codes,
                                                     float* __restrict__ alpha,
-                                                    uint16_t* __restrict__ k_sink) {
+                                                    uint16_t* __restrict__ k_sink,
+                                                    long long* __restrict__ cb_part) {
+  __shared__ unsigned long long cbs[CB ? kSub * 16 * 4 : 1];
+  __shared__ int cbn[CB ? kSub * 16 : 1];
   const int bh = blockIdx.y, b = bh / Hkv, h = bh - b * Hkv;
   const int tid = threadIdx.x, cg = tid & 15, rs = tid >> 4;
-  const int tb = t_begin + blockIdx.x * 128;
+  if (CB) {
+    for (int i = tid; i < kSub * 16 * 4; i += 256) cbs[i] = 0ull;
+    for (int i = tid; i < kSub * 16; i += 256) cbn[i] = 0;
+    __syncthreads();
+  }
   float m[8];
   {
     const float4 m0 = *reinterpret_cast<const float4*>(mu + (int64_t)bh * kD + cg * 8);
@@ -110,25 +122,71 @@ __global__ __launch_bounds__(256) void codes_kernel(const uint16_t* __restrict__
     m[4] = m1.x; m[5] = m1.y; m[6] = m1.z; m[7] = m1.w;
   }
   const uint16_t* base = k + (int64_t)b * sb + (int64_t)h * sh + cg * 8;
-  uint4 w[8];
+  const int n_tiles = (t_end - t_begin + 127) / 128;
+  const int tile_end = min(n_tiles, (int)(blockIdx.x + 1) * tpb);
+  for (int tile = blockIdx.x * tpb; tile < tile_end; ++tile) {
+    const int tb = t_begin + tile * 128;
+    uint4 w[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int t = tb + i * 16 + rs;
-    w[i] = (t < t_end) ? *reinterpret_cast<const uint4*>(base + (int64_t)(t - t_begin) * st)
-                       : make_uint4(0u, 0u, 0u, 0u);
-  }
+    for (int i = 0; i < 8; ++i) {
+      const int t = tb + i * 16 + rs;
+      w[i] = (t < t_end) ? *reinterpret_cast<const uint4*>(base + (int64_t)(t - t_begin) * st)
+                         : make_uint4(0u, 0u, 0u, 0u);
+    }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int t = tb + i * 16 + rs;
-    const RowCode rc = encode_row16(w[i], m);
-    if (t < t_end) {
-      const int64_t row = (int64_t)bh * capacity + t;
-      if ((cg & 3) == 0) *reinterpret_cast<uint32_t*>(codes + row * kCodeBytes + cg) = rc.word;
-      if (cg == 0) alpha[row] = rc.alpha;
-      if (t < kSink)
-        *reinterpret_cast<uint4*>(k_sink + ((int64_t)bh * kSink + t) * kD + cg * 8) = w[i];
+    for (int i = 0; i < 8; ++i) {
+      const int t = tb + i * 16 + rs;
+      const RowCode rc = encode_row16(w[i], m);
+      if (t < t_end) {
+        const int64_t row = (int64_t)bh * capacity + t;
+        if ((cg & 3) == 0) *reinterpret_cast<uint32_t*>(codes + row * kCodeBytes + cg) = rc.word;
+        if (cg == 0) alpha[row] = rc.alpha;
+        if (t < kSink)
+          *reinterpret_cast<uint4*>(k_sink + ((int64_t)bh * kSink + t) * kD + cg * 8) = w[i];
+      }
+      if (CB && t >= kSink && t < t_end) {
+        const int bin0 = (2 * cg) * 16 + (int)(rc.byte & 15u);
+        const int bin1 = (2 * cg + 1) * 16 + (int)(rc.byte >> 4);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float d = chan(w[i], c) - m[c];
+          const float x = rc.alpha > 0.0f ? __fdiv_rn(d, rc.alpha) : 0.0f;
+          const long long fx = __double2ll_rn((double)x * (double)(1 << kCbFracBits));
+          atomicAdd(&cbs[(c < 4 ? bin0 : bin1) * 4 + (c & 3)], (unsigned long long)fx);
+        }
+        atomicAdd(&cbn[bin0], 1);
+        atomicAdd(&cbn[bin1], 1);
+      }
     }
   }
+  if (CB) {
+    __syncthreads();
+    long long* out = cb_part + ((int64_t)bh * gridDim.x + blockIdx.x) * kCbStride;
+    for (int i = tid; i < kSub * 16 * 4; i += 256) out[i] = (long long)cbs[i];
+    for (int i = tid; i < kSub * 16; i += 256) out[kSub * 16 * 4 + i] = cbn[i];
+  }
+}
+
+// Codebook, stage 2: one block per b*h, thread (j, p).  Block statistics are
+// summed in block order (exact integer sums), then centre_i =
+// fl32((sum_i * 2^-24) / count) computed in fp64; empty cluster: sign vertex p.
+__global__ __launch_bounds__(512) void cb_final_kernel(const long long* __restrict__ part, int nblk,
+                                                       float* __restrict__ codebook) {
+  const int bh = blockIdx.x, jp = threadIdx.x, p = jp & 15;
+  long long s[4] = {0, 0, 0, 0}, n = 0;
+  for (int bk = 0; bk < nblk; ++bk) {
+    const long long* q = part + ((int64_t)bh * nblk + bk) * kCbStride;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] += q[jp * 4 + i];
+    n += q[kSub * 16 * 4 + jp];
+  }
+  float4 c;
+  float* cv = &c.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    cv[i] = n > 0 ? (float)(((double)s[i] * (1.0 / (double)(1 << kCbFracBits))) / (double)n)
+                  : (((p >> i) & 1) ? -1.0f : 1.0f);
+  reinterpret_cast<float4*>(codebook)[(int64_t)bh * kSub * 16 + jp] = c;
 }
 
 }  // namespace
@@ -149,8 +207,23 @@ hipError_t launch_codes(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, i
                         int t_begin, int t_end, int capacity, const float* mu, uint8_t* codes,
                         float* alpha, uint16_t* k_sink, hipStream_t s) {
   const int tiles = (t_end - t_begin + 127) / 128;
-  return launch_k(KID_CODES, codes_kernel, dim3(tiles, B * Hkv), dim3(256), 0, s, k, sb, sh, st,
-                  Hkv, t_begin, t_end, capacity, mu, codes, alpha, k_sink);
+  return launch_k(KID_CODES, codes_kernel<false>, dim3(tiles, B * Hkv), dim3(256), 0, s, k, sb,
+                  sh, st, Hkv, t_begin, t_end, capacity, 1, mu, codes, alpha, k_sink,
+                  (long long*)nullptr);
+}
+
+hipError_t launch_codes_cb(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
+                           int n_tokens, int capacity, const float* mu, uint8_t* codes,
+                           float* alpha, uint16_t* k_sink, long long* cb_part, hipStream_t s) {
+  return launch_k(KID_CODES, codes_kernel<true>, dim3(cb_blocks(n_tokens), B * Hkv), dim3(256), 0,
+                  s, k, sb, sh, st, Hkv, 0, n_tokens, capacity, kCbTiles, mu, codes, alpha, k_sink,
+                  cb_part);
+}
+
+hipError_t launch_cb_final(const long long* cb_part, int BH, int nblk, float* codebook,
+                           hipStream_t s) {
+  return launch_k(KID_CB_FINAL, cb_final_kernel, dim3(BH), dim3(kSub * 16), 0, s, cb_part, nblk,
+                  codebook);
 }
 
 }  // namespace sikv

@@ -304,13 +304,15 @@ __global__ __launch_bounds__(1024) void prep_kernel(
     const uint16_t* __restrict__ q, int n_q_heads, int Hkv, int G, const float* __restrict__ mu,
     uint8_t* __restrict__ codes, float* __restrict__ alpha, int capacity, int n_tokens,
     const uint16_t* __restrict__ k_sink, const uint16_t* __restrict__ k_new, int64_t ksb,
-    int64_t ksh, int rank, int mode, int* __restrict__ sel_lut, float* __restrict__ sel_inv,
-    float* __restrict__ att_lut, float* __restrict__ att_qmu, float* __restrict__ att_slog,
-    float* __restrict__ tau) {
+    int64_t ksh, const float* __restrict__ codebook, int rank, int mode,
+    int* __restrict__ sel_lut, float* __restrict__ sel_inv, float* __restrict__ att_lut,
+    float* __restrict__ att_qmu, float* __restrict__ att_slog, float* __restrict__ tau) {
   __shared__ float qv[kMaxGroup + 1][kD];  // q_g, then the selection query (sum)
   __shared__ float mus[kD];
   __shared__ int itab[kLut];
   __shared__ float red_a[2];
+  __shared__ float4 cbl[kLut];             // codebook centres of this KV head, if any
+  __shared__ float jmax[kSub];
   __shared__ float ssc[kSampleMax];
   __shared__ uint32_t hist[2048];
   __shared__ int tmp[32];
@@ -323,6 +325,10 @@ __global__ __launch_bounds__(1024) void prep_kernel(
   const bool sample = mode == 1 && m > 0 && rank <= m;
   const int64_t row0 = (int64_t)bh * capacity;
   const int64_t hq0 = (int64_t)b * n_q_heads + (int64_t)h * G;
+  const bool has_cb = codebook != nullptr;
+  const float4 cbv = (has_cb && tid < kLut)
+                         ? reinterpret_cast<const float4*>(codebook)[(int64_t)bh * kLut + tid]
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
 
   // Appended key row: 16 lanes x 8 channels, with the matching means.
   uint4 kw = make_uint4(0u, 0u, 0u, 0u);
@@ -362,6 +368,7 @@ __global__ __launch_bounds__(1024) void prep_kernel(
   const float mx = tid < kD ? mu[(int64_t)bh * kD + tid] : 0.0f;
   if (tid < G * kD) qv[tid / kD][tid % kD] = qx;
   if (tid < kD) mus[tid] = mx;
+  if (has_cb && tid < kLut) cbl[tid] = cbv;
   if (k_new != nullptr && wave == 0) {  // the whole wave runs the 16-lane shuffles
     const RowCode rc = encode_row16(kw, km);
     const int64_t row = row0 + n_tokens - 1;
@@ -388,7 +395,8 @@ __global__ __launch_bounds__(1024) void prep_kernel(
     if (lane == 0) att_qmu[hq0 + g] = d;
   }
   for (int i = tid; i < G * kLut; i += blockDim.x)
-    att_lut[hq0 * kLut + i] = lut_entry(qv[i / kLut], i % kLut);
+    att_lut[hq0 * kLut + i] = has_cb ? cb_lut_entry(qv[i / kLut], cbl, i % kLut)
+                                     : lut_entry(qv[i / kLut], i % kLut);
   // Exact logits of the sinks (full-precision keys): q_g . k_sink[r], fp32.
   {
     const int r = tid >> 4, c0 = (tid & 15) * 8;
@@ -406,9 +414,25 @@ __global__ __launch_bounds__(1024) void prep_kernel(
   if (mode == 0) return;
   __syncthreads();
 
-  // Selection table in fixed point: A = sum_c |qbar_c| = m * 2^x (m in [0.5, 1)),
-  // scale 2^(30 - x) so that any sum of 32 entries stays below 2^30 in magnitude.
-  const float A = red_a[0] + red_a[1];
+  // Selection table in fixed point.  A bounds |sum_j LUT[j][p_j]|: sum_c |qbar_c|
+  // for the sign vertices, sum_j max_p |LUT[j][p]| for a codebook.  With
+  // A = m * 2^x (m in [0.5, 1)) the scale is 2^(30 - x), so any sum of 32
+  // entries stays below 2^30 in magnitude.
+  const float lv = tid < kLut ? (has_cb ? cb_lut_entry(qv[kMaxGroup], cbl, tid)
+                                        : lut_entry(qv[kMaxGroup], tid))
+                              : 0.0f;
+  float A;
+  if (has_cb) {
+    float x = fabsf(lv);
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+    if (tid < kLut && (tid & 15) == 0) jmax[tid >> 4] = x;
+    __syncthreads();
+    A = 0.0f;
+    for (int j = 0; j < kSub; ++j) A += jmax[j];
+  } else {
+    A = red_a[0] + red_a[1];
+  }
   int ex = 0;
   if (A > 0.0f) {
     frexpf(A, &ex);
@@ -416,7 +440,7 @@ __global__ __launch_bounds__(1024) void prep_kernel(
   }
   const float inv = ldexpf(1.0f, -ex);
   if (tid < kLut) {
-    const int v = (int)rintf(ldexpf(lut_entry(qv[kMaxGroup], tid), ex));
+    const int v = (int)rintf(ldexpf(lv, ex));
     itab[tid] = v;
     sel_lut[(int64_t)bh * kLut + tid] = v;
   }
@@ -651,8 +675,9 @@ __global__ __launch_bounds__(1024) void select_kernel(
 hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const float* mu,
                        uint8_t* codes, float* alpha, int capacity, int n_tokens,
                        const uint16_t* k_sink, const uint16_t* k_new, int64_t ksb, int64_t ksh,
-                       int top_k, int mode, int* sel_lut, float* sel_inv, float* att_lut,
-                       float* att_qmu, float* att_slog, float* tau, hipStream_t s) {
+                       const float* codebook, int top_k, int mode, int* sel_lut, float* sel_inv,
+                       float* att_lut, float* att_qmu, float* att_slog, float* tau,
+                       hipStream_t s) {
   const int n = n_tokens - kSink - (k_new != nullptr ? 1 : 0);
   int rank = 1;
   if (mode == 1) {
@@ -666,7 +691,7 @@ hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const f
   }
   return launch_k(KID_PREP, prep_kernel, dim3(B * Hkv), dim3(1024), 0, s, q, n_q_heads, Hkv,
                   n_q_heads / Hkv, mu, codes, alpha, capacity, n_tokens, k_sink, k_new, ksb, ksh,
-                  rank, mode, sel_lut, sel_inv, att_lut, att_qmu, att_slog, tau);
+                  codebook, rank, mode, sel_lut, sel_inv, att_lut, att_qmu, att_slog, tau);
 }
 
 hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha, int capacity,

@@ -32,6 +32,7 @@ enum KernelId {
   KID_COMBINE,
   KID_DENSE,
   KID_COPY,
+  KID_CB_FINAL,
   KID_COUNT
 };
 
@@ -55,6 +56,7 @@ __device__ __forceinline__ float chan(const uint4& w, int c) {
 struct RowCode {
   uint32_t word;
   float alpha;
+  uint32_t byte;  // this lane's code byte (channels 8cg..8cg+7)
 };
 __device__ __forceinline__ RowCode encode_row16(const uint4& w, const float (&m)[8]) {
   uint32_t byte = 0;
@@ -72,7 +74,7 @@ __device__ __forceinline__ RowCode encode_row16(const uint4& w, const float (&m)
   s += __shfl_xor(s, 8);
   const uint32_t v16 = byte | (__shfl_down(byte, 1, 16) << 8);
   const uint32_t v32 = v16 | (__shfl_down(v16, 2, 16) << 16);
-  return RowCode{v32, s * 0.0078125f};
+  return RowCode{v32, s * 0.0078125f, byte};
 }
 
 // Order-preserving map of fp32 (no NaN) to uint32.
@@ -95,6 +97,14 @@ __device__ __forceinline__ float lut_entry(const float* x, int e) {
   v += (p & 4) ? -x2 : x2;
   v += (p & 8) ? -x3 : x3;
   return v;
+}
+
+// Table entry with data-derived centres: lut[j*16 + p] = x(4j..4j+3) . cb[j*16 + p]
+// (cb: the KV head's codebook, 16 centres of 4 components per sub-vector).
+__device__ __forceinline__ float cb_lut_entry(const float* x, const float4* cb, int e) {
+  const int j = e >> 4;
+  const float4 c = cb[e];
+  return ((x[4 * j] * c.x + x[4 * j + 1] * c.y) + x[4 * j + 2] * c.z) + x[4 * j + 3] * c.w;
 }
 
 // Byte k of x, zero-extended, as one v_perm_b32 (selector byte 0x0c yields 0x00).
@@ -174,6 +184,21 @@ hipError_t launch_mu_final(const float* partial, int BH, int nblk, int n_tokens,
 hipError_t launch_codes(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
                         int t_begin, int t_end, int capacity, const float* mu, uint8_t* codes,
                         float* alpha, uint16_t* k_sink, hipStream_t s);
+// Prefill codes with the codebook statistics: like launch_codes over [0, n_tokens),
+// plus, per block of kCbTiles x 128 tokens, the fixed-point sums of k~/alpha and
+// the counts of every (sub-vector, pattern) over the tokens [64, n_tokens),
+// written to cb_part [B*Hkv][nblk][kCbStride] (nblk = cb_blocks(n_tokens)).
+constexpr int kCbTiles = 32;
+constexpr int kCbStride = kSub * 16 * 4 + kSub * 16;  // sums (int64) then counts
+constexpr int kCbFracBits = 24;
+inline int cb_blocks(int n_tokens) { return (n_tokens + 128 * kCbTiles - 1) / (128 * kCbTiles); }
+hipError_t launch_codes_cb(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
+                           int n_tokens, int capacity, const float* mu, uint8_t* codes,
+                           float* alpha, uint16_t* k_sink, long long* cb_part, hipStream_t s);
+// Codebook from the block statistics: centre = fl32((sum * 2^-24) / count) in
+// fp64, the sign vertex for an empty cluster.  codebook [B*Hkv][32][16][4].
+hipError_t launch_cb_final(const long long* cb_part, int BH, int nblk, float* codebook,
+                           hipStream_t s);
 
 // score.hip
 // mode 0: attention tables only; 1: all tables + sampled threshold; 2: all
@@ -181,15 +206,17 @@ hipError_t launch_codes(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, i
 // Every mode also writes the attention tables of the query heads: att_lut
 // [B*Hq][512], att_qmu [B*Hq] (q_g . mu) and att_slog [B*Hq][64] (exact sink
 // logits q_g . k_sink[r]).
-// k_new (may be null): bf16 key of token n_tokens-1, element (b,h,c) at
+// codebook (may be null): the KV heads' centres [B*Hkv][32][16][4] (else the
+// sign vertices).  k_new (may be null): bf16 key of token n_tokens-1, element (b,h,c) at
 // k_new[b*ksb + h*ksh + c]; the kernel first encodes it into codes / alpha
 // (append with the frozen mean, bit-identical to launch_codes) and leaves that
 // token out of its sample.
 hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const float* mu,
                        uint8_t* codes, float* alpha, int capacity, int n_tokens,
                        const uint16_t* k_sink, const uint16_t* k_new, int64_t ksb, int64_t ksh,
-                       int top_k, int mode, int* sel_lut, float* sel_inv, float* att_lut,
-                       float* att_qmu, float* att_slog, float* tau, hipStream_t s);
+                       const float* codebook, int top_k, int mode, int* sel_lut, float* sel_inv,
+                       float* att_lut, float* att_qmu, float* att_slog, float* tau,
+                       hipStream_t s);
 hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha, int capacity,
                         int n_tokens, const int* sel_lut, const float* sel_inv, const float* tau,
                         int chunk,

@@ -77,7 +77,14 @@ typedef int32_t sikv_status;
  *   v      bf16 value cache, element (b,h,t,c) at v[b*v_stride_b + h*v_stride_h
  *          + t*v_stride_t + c] (strides in elements, multiples of 8; rows
  *          16-byte aligned).  Only read.
- *   codebook  reserved for data-derived cluster centres; must be NULL.
+ *   codebook  NULL: the 16 centres of every sub-vector are the sign vertices
+ *          (+1 for bit 0, -1 for bit 1 per channel) scaled by alpha.  Else
+ *          fp32 [B][Hkv][32][16][4], 16-byte aligned: data-derived centres
+ *          (§2.1 item 1, one-pass clustering by sign pattern; §2.1 item 2, the
+ *          query is dotted with the 16 centres): sikv_encode with
+ *          recompute_mu = 1 writes them, every scoring and attention call
+ *          uses them (key_t = mu + alpha_t * centre of its cluster, per
+ *          sub-vector).  Appended tokens keep the prefill centres.
  * n_tokens (N) is the number of valid tokens of every sequence (64 < N <=
  * capacity); candidates for top-k are the tokens 64..N-1.
  */
@@ -96,7 +103,7 @@ typedef struct sikv_cache_desc {
   int64_t v_stride_b;
   int64_t v_stride_h;
   int64_t v_stride_t;
-  const float *codebook;
+  float *codebook;
 } sikv_cache_desc;
 
 /*
@@ -116,6 +123,12 @@ typedef struct sikv_cache_desc {
  *                k_sink).  The caller then raises n_tokens.  Needs no workspace.
  *   alpha is the adjacent-pair fp32 tree of |fl(k_c - mu_c)| over the 128
  *   channels times 2^-7.  Results are bit-identical to that definition.
+ *   With a codebook, prefill also writes it: centre (j, p) = mean over the
+ *   tokens 64..N-1 whose sub-vector j has pattern p of x = fl(fl(k_c - mu_c) /
+ *   alpha_t) (0 if alpha_t = 0), summed exactly as rint(x * 2^24) in int64,
+ *   then fl32((sum * 2^-24) / count) in fp64; an empty cluster keeps its sign
+ *   vertex.  Bit-identical to that definition.  Prefill workspace grows by
+ *   B*Hkv*ceil(N/4096)*2560*8 bytes.
  */
 sikv_status sikv_encode(const sikv_cache_desc *cache, const uint16_t *k, int64_t k_stride_b,
                         int64_t k_stride_h, int64_t k_stride_t, int32_t t_begin, int32_t t_end,

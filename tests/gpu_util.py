@@ -73,7 +73,11 @@ def check_rows(out: np.ndarray, ref: np.ndarray, what: str = "", tol: float = AT
     return float(err.max())
 
 
-def check_scores(gpu_s: np.ndarray, s: np.ndarray, alpha: np.ndarray, qbar: np.ndarray, what=""):
-    bound = SCORE_TOL * alpha.astype(np.float64) * np.abs(qbar).sum() + 1e-30
+def check_scores(gpu_s: np.ndarray, s: np.ndarray, alpha: np.ndarray, qbar: np.ndarray, what="",
+                 lut_bound=None):
+    """lut_bound: bound on |sum_j LUT[j][p_j]| (default sum_c |qbar_c|, exact for the
+    sign vertices; with a codebook, sum_j max_p |LUT[j][p]|)."""
+    a_bound = np.abs(qbar).sum() if lut_bound is None else lut_bound
+    bound = SCORE_TOL * alpha.astype(np.float64) * a_bound + 1e-30
     err = np.abs(gpu_s.astype(np.float64) - s)
     assert np.all(err <= bound), f"{what}: worst score error ratio {(err / bound).max():.3f}"

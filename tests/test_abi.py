@@ -79,6 +79,10 @@ def test_workspace_sizes():
     assert lib.sikv_workspace_bytes(1, None, 4, 16) == 0
     big = desc(capacity=600000, n_tokens=524288, batch=1, n_kv_heads=8)
     assert lib.sikv_workspace_bytes(3, C.byref(big), 40, 4096) > 0
+    # prefill with a codebook needs room for the per-block cluster statistics
+    cbd = desc(codebook=FAKE + 0x500000)
+    assert (lib.sikv_workspace_bytes(0, C.byref(cbd), 1, 1)
+            >= lib.sikv_workspace_bytes(0, C.byref(d), 1, 1) + 2 * 2 * 1 * 2560 * 8)
     assert lib.sikv_dense_workspace_bytes(4, 8, 32, 131072) > 0
     assert lib.sikv_dense_workspace_bytes(4, 8, 30, 131072) == 0
 
@@ -86,7 +90,7 @@ def test_workspace_sizes():
 @pytest.mark.parametrize("field,value,expect", [
     ("head_dim", 64, UNSUPPORTED),
     ("n_sink", 32, UNSUPPORTED),
-    ("codebook", FAKE, UNSUPPORTED),
+    ("codebook", FAKE + 4, INVALID),                                # misaligned
     ("n_tokens", 64, INVALID),
     ("n_tokens", 1001, INVALID),
     ("batch", 0, INVALID),

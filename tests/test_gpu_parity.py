@@ -170,6 +170,80 @@ def test_append_and_strided_inputs():
             check_rows(out[b, h * G:(h + 1) * G], ref, f"append attn b={b} h={h}")
 
 
+CB_CASES = [
+    ("cb_tiny_4k", None),
+    ("cb_g5_multi_tile", S.custom("cb_g5", 2, 10, 2, 20123, 1500, n_planted=16, cfg_id=130)),
+    ("cb_mu_per_head", S.custom("cb_mu", 2, 8, 2, 9000, 600, n_planted=8, cfg_id=131,
+                                mu_per_head=True)),
+]
+
+
+@pytest.mark.parametrize("name,w", CB_CASES, ids=[c[0] for c in CB_CASES])
+def test_codebook_parity(name, w):
+    """Data-derived centres: the codebook is bit-exact, scores / top-k / attention /
+    decode step match the oracle with the same centres, appends keep them."""
+    w = S.WORKLOADS["tiny_4k"] if w is None else w
+    say(f"[parity] case={name} B={w.batch} Hq={w.n_q_heads} Hkv={w.n_kv_heads} "
+        f"N={w.n_tokens} k={w.top_k}")
+    d = S.draw(w)
+    N, G = w.n_tokens, w.group
+    n0 = N - 5                                        # prefill, then 5 appended tokens
+    K, q = dev_bf16(d["K"]), dev_bf16(d["q"])
+    V = dev_bf16(d["V"])
+    cache = sk.Cache(w.batch, w.n_kv_heads, N, v=V, codebook=True)
+    sk.sikv_encode(cache, K[:, :, :n0])
+    sk.sikv_encode(cache, K[:, :, n0:], t_begin=n0, recompute_mu=False)
+    torch.cuda.synchronize()
+    gcb = cache.codebook.cpu().numpy()
+    codes, alpha = cache.codes.cpu().numpy(), cache.alpha.cpu().numpy()
+    oc = {}
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            pre = O.encode(d["K"][b, h, :n0][None, None], n0, with_codebook=True)
+            app = O.encode_rows(d["K"][b, h, n0:N], pre["mu"][0, 0])
+            cb = pre["codebook"][0, 0]
+            assert np.array_equal(gcb[b, h].view(np.uint32), cb.view(np.uint32)), (b, h)
+            call = np.concatenate([pre["codes"][0, 0], app["codes"]])
+            aall = np.concatenate([pre["alpha"][0, 0], app["alpha"]])
+            assert np.array_equal(codes[b, h, :N], call)
+            assert np.array_equal(alpha[b, h, :N].view(np.uint32), aall.view(np.uint32))
+            oc[b, h] = dict(codes=call, alpha=aall, cb=cb, mu=pre["mu"][0, 0],
+                            k_sink=pre["k_sink"][0, 0])
+
+    scores = torch.full((w.batch, w.n_kv_heads, N), float("nan"), device="cuda")
+    idx = sk.sikv_score_topk(cache, q, w.top_k, scores=scores)
+    torch.cuda.synchronize()
+    gs, gi = scores.cpu().numpy(), idx.cpu().numpy()
+    qbar = O.group_query(d["q"], w.n_kv_heads)
+    oidx = np.zeros((w.batch, w.n_kv_heads, w.top_k), np.int32)
+    for (b, h), o in oc.items():
+        s = O.head_scores(d["q"], o["codes"], o["alpha"], b, h, w.n_kv_heads, N, o["cb"])
+        A = np.abs(O.query_lut(qbar[b, h], o["cb"])).max(axis=1).sum()
+        check_scores(gs[b, h, 64:N], s, o["alpha"][64:N], qbar[b, h], f"{name} scores b={b} h={h}",
+                     lut_bound=A)
+        check_topk(gi[b, h], s, w.top_k, N, f"{name} topk b={b} h={h}")
+        oidx[b, h] = O.select_topk(s, w.top_k)
+
+    sk.debug_force_exact_select(True)
+    try:
+        idx2 = sk.sikv_score_topk(cache, q, w.top_k)
+        torch.cuda.synchronize()
+    finally:
+        sk.debug_force_exact_select(False)
+    assert np.array_equal(idx2.cpu().numpy(), gi)
+
+    out = sk.sikv_sparse_attn(cache, q, torch.from_numpy(oidx).cuda(), SM).cpu().numpy()
+    idx_out = torch.empty_like(idx)
+    out2 = sk.sikv_decode_step(cache, q, w.top_k, SM, idx_out=idx_out).cpu().numpy()
+    di = idx_out.cpu().numpy()
+    assert np.array_equal(di, gi)
+    for (b, h), o in oc.items():
+        for sel, res, what in ((oidx[b, h], out, "attn"), (di[b, h], out2, "decode")):
+            ref = O.sparse_attention(d["q"][b, h * G:(h + 1) * G], sel, o["k_sink"], o["codes"],
+                                     o["alpha"], o["mu"], d["V"][b, h], SM, o["cb"])
+            check_rows(res[b, h * G:(h + 1) * G], ref, f"{name} {what} b={b} h={h}")
+
+
 def test_fused_append_matches_separate_calls():
     """sikv_append_decode_step == sikv_encode (append) + sikv_decode_step, bit for bit
     (new row's code and scale, idx, attention output), at a small and a multi-tile size."""
