@@ -373,6 +373,18 @@ def main():
     sk.timing_enable(False)
     enc_us = sum(1e3 * tot / 3 for name, (n, tot) in et.items() if name in ("mu_partial", "mu_final", "codes") and n)
     del enc_c
+    # the same with data-derived centres (one-pass cluster statistics + finalize)
+    sk.timing_reset()
+    sk.timing_enable(True)
+    enc_c = sk.Cache(w.batch, w.n_kv_heads, N, device=dev, v=None, codebook=True)
+    for _ in range(3):
+        sk.sikv_encode(enc_c, K)
+    torch.cuda.synchronize()
+    et = sk.timing_read()
+    sk.timing_enable(False)
+    enc_cb_us = sum(1e3 * tot / 3 for name, (n, tot) in et.items()
+                    if name in ("mu_partial", "mu_final", "codes", "cb_final") and n)
+    del enc_c
 
     # dense bf16 comparator over the same (uncompressed) cache
     dense_us = dense_torch_us = None
@@ -447,6 +459,7 @@ def main():
         / (sum(kern_us.get(n, 0.0) for n in ("prep", "score", "select")) * 1e-6) / 1e9
         / HBM_PEAK_GBS,
         "encode_prefill_us": enc_us,
+        "encode_prefill_codebook_us": enc_cb_us,
         "copy_kernel_gbs": copy_gbs,
         "decode_step_us_graph": graph_ms * 1e3 if graph_ms is not None else None,
         "dense_bf16_us": dense_us,

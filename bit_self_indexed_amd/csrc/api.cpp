@@ -58,7 +58,7 @@ struct DecodePlan {
 EncodePlan plan_encode(const sikv_cache_desc* c) {
   EncodePlan p;
   const size_t BH = (size_t)c->batch * c->n_kv_heads;
-  p.nblk = (int)cdiv(c->n_tokens, 256);
+  p.nblk = (int)cdiv(c->n_tokens, kMuTile);
   p.cb_nblk = c->codebook != nullptr ? cb_blocks(c->n_tokens) : 0;
   p.off_cb = align_up(BH * p.nblk * kD * sizeof(float));
   p.bytes = p.off_cb + align_up(BH * p.cb_nblk * kCbStride * sizeof(long long));

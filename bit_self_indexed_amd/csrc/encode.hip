@@ -27,38 +27,50 @@ __device__ __forceinline__ float tree16(const float* l) {
   return (b0 + b1) + (b2 + b3);
 }
 
-// Mean, stage 1: one block per (256-token tile, b*h).  Thread (rs, cg) owns the
-// aligned 16-row group rs of the tile and channels 8cg..8cg+7; its 16-leaf
-// subtree is summed in registers, then the 16 group sums are combined by the
-// tree's top 4 levels.  Leaves outside [64, N) are +0.0 (never loaded).
+// Mean, stage 1: one block per (4096-token tile, b*h), 16 sub-tiles of 256
+// tokens in turn.  In a sub-tile, thread (rs, cg) owns the aligned 16-row group
+// rs and channels 8cg..8cg+7; its 16-leaf subtree is summed in registers and
+// the 16 group sums are combined by the next 4 levels of the tree; the 16
+// sub-tile sums then form the 4 levels above.  Leaves outside [64, N) are +0.0
+// (never loaded).
 __global__ __launch_bounds__(256) void mu_partial_kernel(const uint16_t* __restrict__ k, int64_t sb,
                                                          int64_t sh, int64_t st, int Hkv,
                                                          int n_tokens, float* __restrict__ partial,
                                                          int nblk) {
   __shared__ float red[16][kD + 1];
+  __shared__ float subs[16][kD];
   const int bh = blockIdx.y, b = bh / Hkv, h = bh - b * Hkv;
   const int tid = threadIdx.x, cg = tid & 15, rs = tid >> 4;
-  const int t0 = blockIdx.x * 256 + rs * 16;
   const uint16_t* base = k + (int64_t)b * sb + (int64_t)h * sh + cg * 8;
-  uint4 w[16];
+  for (int sub = 0; sub < 16; ++sub) {
+    const int t0 = blockIdx.x * kMuTile + sub * 256 + rs * 16;
+    uint4 w[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int t = t0 + i;
-    w[i] = (t >= kSink && t < n_tokens) ? *reinterpret_cast<const uint4*>(base + (int64_t)t * st)
-                                        : make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < 16; ++i) {
+      const int t = t0 + i;
+      w[i] = (t >= kSink && t < n_tokens) ? *reinterpret_cast<const uint4*>(base + (int64_t)t * st)
+                                          : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float l[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) l[i] = chan(w[i], c);
+      red[rs][cg * 8 + c] = tree16(l);
+    }
+    __syncthreads();
+    if (tid < kD) {
+      float l[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) l[r] = red[r][tid];
+      subs[sub][tid] = tree16(l);
+    }
+    __syncthreads();
   }
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    float l[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) l[i] = chan(w[i], c);
-    red[rs][cg * 8 + c] = tree16(l);
-  }
-  __syncthreads();
   if (tid < kD) {
     float l[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) l[r] = red[r][tid];
+    for (int r = 0; r < 16; ++r) l[r] = subs[r][tid];
     partial[((int64_t)bh * nblk + blockIdx.x) * kD + tid] = tree16(l);
   }
 }
@@ -67,6 +79,7 @@ __global__ __launch_bounds__(256) void mu_partial_kernel(const uint16_t* __restr
 // the leaves of the remaining levels (padded with +0.0 to a power of two) and
 // are reduced by a binary counter: leaf i is merged with the pending subtree of
 // each level where i has a trailing 1 bit, which is exactly the pairwise tree.
+// Leaves are loaded 16 at a time ahead of the merges.
 __global__ __launch_bounds__(128) void mu_final_kernel(const float* __restrict__ partial, int nblk,
                                                        int n_tokens, float* __restrict__ mu) {
   __shared__ float stk[32][kD];
@@ -77,14 +90,22 @@ __global__ __launch_bounds__(128) void mu_final_kernel(const float* __restrict__
     ++levels;
   }
   const float* p = partial + (int64_t)bh * nblk * kD + c;
-  for (int i = 0; i < n2; ++i) {
-    float x = (i < nblk) ? p[(int64_t)i * kD] : 0.0f;
-    int lvl = 0;
-    for (unsigned ii = (unsigned)i; ii & 1u; ii >>= 1) {
-      x = stk[lvl][c] + x;
-      ++lvl;
+  for (int i0 = 0; i0 < n2; i0 += 16) {
+    float leaf[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) leaf[u] = (i0 + u < nblk) ? p[(int64_t)(i0 + u) * kD] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = i0 + u;
+      if (i >= n2) break;
+      float x = leaf[u];
+      int lvl = 0;
+      for (unsigned ii = (unsigned)i; ii & 1u; ii >>= 1) {
+        x = stk[lvl][c] + x;
+        ++lvl;
+      }
+      stk[lvl][c] = x;
     }
-    stk[lvl][c] = x;
   }
   mu[(int64_t)bh * kD + c] = __fdiv_rn(stk[levels][c], (float)(n_tokens - kSink));
 }

@@ -177,6 +177,7 @@ __device__ __forceinline__ int ballot_rank(uint64_t m) {
 
 // ---------------------------------------------------------------- host launchers
 // encode.hip
+constexpr int kMuTile = 4096;  // tokens per mean partial (an aligned subtree of the token tree)
 hipError_t launch_mu_partial(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
                              int n_tokens, float* partial, int nblk, hipStream_t s);
 hipError_t launch_mu_final(const float* partial, int BH, int nblk, int n_tokens, float* mu,
