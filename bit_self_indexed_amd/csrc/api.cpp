@@ -32,8 +32,8 @@ struct EncodePlan {
 
 struct ScorePlan {
   int chunk, n_chunks;
-  size_t off_tau, off_cnt, off_ckey, off_ct, off_pkey, off_pt, off_tab, off_inv, off_lut, off_qmu,
-      off_slog;
+  size_t off_tau, off_bin, off_cnt, off_ckey, off_ct, off_pkey, off_pt, off_tab, off_inv,
+      off_lut, off_qmu, off_slog;
   size_t bytes;
 };
 
@@ -85,6 +85,7 @@ bool plan_score(const sikv_cache_desc* c, int n_q_heads, ScorePlan* p) {
   const size_t cap = (size_t)BH * p->n_chunks * p->chunk;
   size_t o = 0;
   p->off_tau = o;  o += align_up((size_t)BH * sizeof(float));
+  p->off_bin = o;  o += align_up((size_t)BH * sizeof(float));
   p->off_cnt = o;  o += align_up((size_t)BH * p->n_chunks * sizeof(int32_t));
   p->off_ckey = o; o += align_up(cap * sizeof(uint32_t));
   p->off_ct = o;   o += align_up(cap * sizeof(int32_t));
@@ -202,11 +203,12 @@ sikv_status run_score_topk(const sikv_cache_desc* c, const uint16_t* q, int n_q_
   SIKV_TRY(launch_prep(q, n_q_heads, B, Hkv, c->mu, c->codes, c->alpha, c->capacity, c->n_tokens,
                        c->k_sink, k_new, ksb, ksh, c->codebook, top_k, mode, tab, inv,
                        at<float>(ws, sp.off_lut), at<float>(ws, sp.off_qmu),
-                       at<float>(ws, sp.off_slog), tau, s));
+                       at<float>(ws, sp.off_slog), tau, at<float>(ws, sp.off_bin), s));
   SIKV_TRY(launch_score(B, Hkv, c->codes, c->alpha, c->capacity, c->n_tokens, tab, inv, tau,
                         sp.chunk, sp.n_chunks, ckey, ct, cnt, scores_opt, s));
   SIKV_TRY(launch_select(B, Hkv, c->codes, c->alpha, c->capacity, c->n_tokens, tab, inv, top_k,
-                         sp.chunk, sp.n_chunks, ckey, ct, cnt, pkey, pt, idx, s));
+                         sp.chunk, sp.n_chunks, ckey, ct, cnt, tau, at<float>(ws, sp.off_bin),
+                         pkey, pt, idx, s));
   return SIKV_OK;
 }
 
@@ -222,7 +224,7 @@ sikv_status run_attn(const sikv_cache_desc* c, const uint16_t* q, int n_q_heads,
     SIKV_TRY(launch_prep(q, n_q_heads, c->batch, c->n_kv_heads, c->mu, c->codes, c->alpha,
                          c->capacity, c->n_tokens, c->k_sink, nullptr, 0, 0, c->codebook, top_k, 0,
                          nullptr,
-                         nullptr, own.lut, own.qmu, own.slog, nullptr, s));
+                         nullptr, own.lut, own.qmu, own.slog, nullptr, nullptr, s));
     tab = &own;
   }
   SIKV_TRY(launch_attn(n_q_heads, c->batch, c->n_kv_heads, c->codes, c->alpha, c->v,

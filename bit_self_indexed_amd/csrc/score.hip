@@ -117,6 +117,11 @@ struct Round {
   int digit, above, count, shift;
 };
 
+// Given a histogram of nb bins (in LDS, published) over keys in ascending bin
+// order, the bin holding the k-th largest key: (bin, keys in larger bins, keys
+// in it).  tmp: LDS >= 24 ints.  Five barriers.
+__device__ __forceinline__ Round hist_pick(const uint32_t* hist, int nb, int k, int* tmp);
+
 __device__ __forceinline__ Round block_round(const uint32_t* keys, int n, int k, uint32_t lo,
                                              int top, uint32_t prefix, uint32_t* hist, int* tmp) {
   const int width = top < 11 ? top : 11;
@@ -130,6 +135,12 @@ __device__ __forceinline__ Round block_round(const uint32_t* keys, int n, int k,
     if (((uint64_t)r >> top) == want) atomicAdd(&hist[(r >> shift) & (uint32_t)(nb - 1)], 1u);
   }
   __syncthreads();
+  Round r = hist_pick(hist, nb, k, tmp);
+  r.shift = shift;
+  return r;
+}
+
+__device__ __forceinline__ Round hist_pick(const uint32_t* hist, int nb, int k, int* tmp) {
   const int per = (nb + blockDim.x - 1) / blockDim.x;
   const int d0 = threadIdx.x * per;
   int cnt = 0;
@@ -147,29 +158,34 @@ __device__ __forceinline__ Round block_round(const uint32_t* keys, int n, int k,
     pre += c;
   }
   __syncthreads();
-  const Round r{tmp[18], tmp[19], tmp[20], shift};
+  const Round r{tmp[18], tmp[19], tmp[20], 0};
   __syncthreads();
   return r;
 }
 
 // need-th largest (1 <= need <= m <= 64) of the keys sub[0..m) by wave 0 alone:
-// lane i counts the keys greater than and not smaller than its own; the lanes
-// with gt < need <= ge all hold the answer.  Result in out[0] (key), out[1]
-// (number of keys greater than it).  Caller provides the barrier.
+// a bitonic sort of the 64 lanes into descending order (missing lanes hold 0,
+// below every key of a real score), then the key in lane need-1 and the number
+// of keys above it.  Result in out[0] (key), out[1] (number of keys greater
+// than it).  Caller provides the barrier.
 __device__ __forceinline__ void wave_kth(const uint32_t* sub, int m, int need, int* out) {
   if (threadIdx.x >= 64) return;
   const int lane = threadIdx.x;
-  const uint32_t mine = lane < m ? sub[lane] : 0u;
-  int gt = 0, ge = 0;
-  for (int j = 0; j < m; ++j) {
-    const uint32_t o = (uint32_t)__shfl((int)mine, j);
-    gt += o > mine;
-    ge += o >= mine;
+  uint32_t x = lane < m ? sub[lane] : 0u;
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint32_t y = (uint32_t)__shfl_xor((int)x, j);
+      const bool desc = (lane & k) == 0 || k == 64;
+      const bool low = (lane & j) == 0;
+      x = (low == desc) ? max(x, y) : min(x, y);
+    }
   }
-  const bool hit = lane < m && gt < need && need <= ge;
-  const uint64_t b = __ballot(hit);
-  if (hit && (uint32_t)lane == (uint32_t)__builtin_ctzll(b)) {
-    out[0] = (int)mine;
+  const uint32_t kth = (uint32_t)__shfl((int)x, need - 1);
+  const int gt = __popcll(__ballot(x > kth));
+  if (lane == 0) {
+    out[0] = (int)kth;
     out[1] = gt;
   }
 }
@@ -306,7 +322,8 @@ __global__ __launch_bounds__(1024) void prep_kernel(
     const uint16_t* __restrict__ k_sink, const uint16_t* __restrict__ k_new, int64_t ksb,
     int64_t ksh, const float* __restrict__ codebook, int rank, int mode,
     int* __restrict__ sel_lut, float* __restrict__ sel_inv, float* __restrict__ att_lut,
-    float* __restrict__ att_qmu, float* __restrict__ att_slog, float* __restrict__ tau) {
+    float* __restrict__ att_qmu, float* __restrict__ att_slog, float* __restrict__ tau,
+    float* __restrict__ bin_scale) {
   __shared__ float qv[kMaxGroup + 1][kD];  // q_g, then the selection query (sum)
   __shared__ float mus[kD];
   __shared__ int itab[kLut];
@@ -446,7 +463,10 @@ __global__ __launch_bounds__(1024) void prep_kernel(
   }
   if (tid == 0) sel_inv[bh] = inv;
   if (mode == 2 || !sample) {  // +inf: nothing passes; -inf: keep all
-    if (tid == 0) tau[bh] = __uint_as_float(mode == 2 ? 0x7f800000u : 0xff800000u);
+    if (tid == 0) {
+      tau[bh] = __uint_as_float(mode == 2 ? 0x7f800000u : 0xff800000u);
+      bin_scale[bh] = 0.0f;
+    }
     return;
   }
   __syncthreads();
@@ -463,7 +483,13 @@ __global__ __launch_bounds__(1024) void prep_kernel(
   }
   block_minmax(lo, hi, mm, &lo, &hi);  // its barriers also publish ssc
   const float th = block_score_floor(ssc, m, rank, key_score(lo), key_score(hi), hist, tmp);
-  if (tid == 0) tau[bh] = th;
+  if (tid == 0) {
+    tau[bh] = th;
+    // the select kernel bins candidate scores linearly, 2048 bins from tau up
+    // to the sample maximum (higher scores share the top bin)
+    const float span = key_score(hi) - th;
+    bin_scale[bh] = span > 0.0f ? 2048.0f / span : 0.0f;
+  }
 }
 
 // ------------------------------------------------------------------ score
@@ -544,13 +570,14 @@ __global__ __launch_bounds__(1024) void select_kernel(
     int n_tokens, const int* __restrict__ sel_lut, const float* __restrict__ sel_inv, int top_k,
     int chunk, int n_chunks,
     const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_t,
-    const int32_t* __restrict__ chunk_count, uint32_t* __restrict__ comp_key,
+    const int32_t* __restrict__ chunk_count, const float* __restrict__ tau,
+    const float* __restrict__ bin_scale, uint32_t* __restrict__ comp_key,
     int32_t* __restrict__ comp_t, int32_t* __restrict__ idx) {
   __shared__ int off[kMaxChunks + 1];
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t lkey[kSelectLds];
   __shared__ int32_t lpos[kSelectLds];
-  __shared__ uint32_t sub[kSubMax];
+  __shared__ uint32_t sub[2 * kSubMax];  // boundary-bin keys, then block_kth's own sub-list
   __shared__ int tmp[32];
   __shared__ uint32_t mm[32];
   __shared__ int scount;
@@ -562,6 +589,7 @@ __global__ __launch_bounds__(1024) void select_kernel(
     for (int j = tid; j < top_k; j += blockDim.x) out[j] = kSink + j;
     return;
   }
+  for (int i = tid; i < 2048; i += blockDim.x) hist[i] = 0u;  // published by the scan's barriers
   // Tile counts -> offsets of each tile's candidates in the ordered list.
   {
     const int per = (n_chunks + blockDim.x - 1) / blockDim.x;  // <= 2
@@ -608,7 +636,14 @@ __global__ __launch_bounds__(1024) void select_kernel(
   }
   // Gather the candidates into one ordered list.  Wave w copies tiles w, w+nw,
   // ...; the first 256 candidates of 4 tiles are loaded before any is stored.
+  // Kept in LDS, each candidate's score is also counted in a 2048-bin linear
+  // histogram from tau up (bin width set by the prep kernel from its sample).
   const bool in_lds = C <= kSelectLds;
+  const float th = tau[bh], bsc = bin_scale[bh];
+  auto bin_of = [th, bsc](uint32_t key) {
+    const float z = (key_score(key) - th) * bsc;  // NaN (no scale) -> bin 0
+    return z >= 2047.0f ? 2047 : (z > 0.0f ? (int)z : 0);
+  };
   uint32_t* dk = in_lds ? lkey : comp_key + cbase;
   int32_t* dp = in_lds ? lpos : comp_t + cbase;
   {
@@ -643,6 +678,7 @@ __global__ __launch_bounds__(1024) void select_kernel(
             dp[o + j] = tt[v][u];
             lo = min(lo, kk[v][u]);
             hi = max(hi, kk[v][u]);
+            if (in_lds) atomicAdd(&hist[bin_of(kk[v][u])], 1u);
           }
         }
         for (int j = 256 + lane; j < cnt; j += 64) {  // tiles with many candidates
@@ -651,15 +687,48 @@ __global__ __launch_bounds__(1024) void select_kernel(
           dp[o + j] = cand_t[src + j];
           lo = min(lo, key);
           hi = max(hi, key);
+          if (in_lds) atomicAdd(&hist[bin_of(key)], 1u);
         }
       }
     }
   }
-  block_minmax(lo, hi, mm, &lo, &hi);  // its barriers also publish the copies
   if (in_lds) {
-    const Kth r = block_kth(lkey, C, top_k, lo, hi, hist, tmp, sub, &scount);
+    __syncthreads();  // publishes the list and the histogram
+    // The boundary bin of the k-th largest; its keys (usually a few dozen) go to
+    // a sub-list resolved by one wave, or by radix rounds if more than 64.
+    const Round rb = hist_pick(hist, 2048, top_k, tmp);
+    Kth r;
+    if (rb.count <= kSubMax) {
+      if (tid == 0) scount = 0;
+      __syncthreads();
+      for (int i = tid; i < C; i += blockDim.x) {
+        const uint32_t key = lkey[i];
+        if (bin_of(key) == rb.digit) sub[atomicAdd(&scount, 1)] = key;
+      }
+      __syncthreads();
+      const int ns = scount, need = top_k - rb.above;
+      if (ns <= 64) {
+        wave_kth(sub, ns, need, tmp + 24);
+        __syncthreads();
+        r = Kth{(uint32_t)tmp[24], rb.above + tmp[25], need - tmp[25]};
+        __syncthreads();
+      } else {
+        uint32_t slo = 0xffffffffu, shi = 0u;
+        for (int i = tid; i < ns; i += blockDim.x) {
+          slo = min(slo, sub[i]);
+          shi = max(shi, sub[i]);
+        }
+        block_minmax(slo, shi, mm, &slo, &shi);
+        const Kth rs = block_kth(sub, ns, need, slo, shi, hist, tmp, sub + kSubMax, &scount);
+        r = Kth{rs.key, rb.above + rs.above, rs.need};
+      }
+    } else {  // degenerate spread (e.g. no usable bin scale): radix over the whole list
+      block_minmax(lo, hi, mm, &lo, &hi);
+      r = block_kth(lkey, C, top_k, lo, hi, hist, tmp, sub, &scount);
+    }
     block_emit(lkey, lpos, C, top_k, r, out, tmp);
   } else {
+    block_minmax(lo, hi, mm, &lo, &hi);  // its barriers also publish the copies
     const Kth r = block_kth(comp_key + cbase, C, top_k, lo, hi, hist, tmp, sub, &scount);
     block_emit(comp_key + cbase, comp_t + cbase, C, top_k, r, out, tmp);
   }
@@ -677,7 +746,7 @@ hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const f
                        const uint16_t* k_sink, const uint16_t* k_new, int64_t ksb, int64_t ksh,
                        const float* codebook, int top_k, int mode, int* sel_lut, float* sel_inv,
                        float* att_lut, float* att_qmu, float* att_slog, float* tau,
-                       hipStream_t s) {
+                       float* bin_scale, hipStream_t s) {
   const int n = n_tokens - kSink - (k_new != nullptr ? 1 : 0);
   int rank = 1;
   if (mode == 1) {
@@ -691,7 +760,8 @@ hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const f
   }
   return launch_k(KID_PREP, prep_kernel, dim3(B * Hkv), dim3(1024), 0, s, q, n_q_heads, Hkv,
                   n_q_heads / Hkv, mu, codes, alpha, capacity, n_tokens, k_sink, k_new, ksb, ksh,
-                  codebook, rank, mode, sel_lut, sel_inv, att_lut, att_qmu, att_slog, tau);
+                  codebook, rank, mode, sel_lut, sel_inv, att_lut, att_qmu, att_slog, tau,
+                  bin_scale);
 }
 
 hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha, int capacity,
@@ -721,11 +791,12 @@ hipError_t launch_select(int B, int Hkv, const uint8_t* codes, const float* alph
                          int n_tokens, const int* sel_lut, const float* sel_inv, int top_k,
                          int chunk, int n_chunks,
                          uint32_t* cand_key, int32_t* cand_t, const int32_t* chunk_count,
-                         uint32_t* comp_key, int32_t* comp_t, int32_t* idx, hipStream_t s) {
+                         const float* tau, const float* bin_scale, uint32_t* comp_key,
+                         int32_t* comp_t, int32_t* idx, hipStream_t s) {
   if (n_chunks > kMaxChunks) return hipErrorInvalidValue;
   return launch_k(KID_SELECT, select_kernel, dim3(B * Hkv), dim3(1024), 0, s, codes, alpha,
                   capacity, n_tokens, sel_lut, sel_inv, top_k, chunk, n_chunks, cand_key, cand_t,
-                  chunk_count, comp_key, comp_t, idx);
+                  chunk_count, tau, bin_scale, comp_key, comp_t, idx);
 }
 
 }  // namespace sikv

@@ -211,13 +211,14 @@ hipError_t launch_cb_final(const long long* cb_part, int BH, int nblk, float* co
 // sign vertices).  k_new (may be null): bf16 key of token n_tokens-1, element (b,h,c) at
 // k_new[b*ksb + h*ksh + c]; the kernel first encodes it into codes / alpha
 // (append with the frozen mean, bit-identical to launch_codes) and leaves that
-// token out of its sample.
+// token out of its sample.  bin_scale [B*Hkv]: width of the select kernel's
+// score bins (2048 bins from tau to the sample maximum; 0 when not sampled).
 hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const float* mu,
                        uint8_t* codes, float* alpha, int capacity, int n_tokens,
                        const uint16_t* k_sink, const uint16_t* k_new, int64_t ksb, int64_t ksh,
                        const float* codebook, int top_k, int mode, int* sel_lut, float* sel_inv,
                        float* att_lut, float* att_qmu, float* att_slog, float* tau,
-                       hipStream_t s);
+                       float* bin_scale, hipStream_t s);
 hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha, int capacity,
                         int n_tokens, const int* sel_lut, const float* sel_inv, const float* tau,
                         int chunk,
@@ -227,7 +228,8 @@ hipError_t launch_select(int B, int Hkv, const uint8_t* codes, const float* alph
                          int n_tokens, const int* sel_lut, const float* sel_inv, int top_k,
                          int chunk, int n_chunks,
                          uint32_t* cand_key, int32_t* cand_t, const int32_t* chunk_count,
-                         uint32_t* comp_key, int32_t* comp_t, int32_t* idx, hipStream_t s);
+                         const float* tau, const float* bin_scale, uint32_t* comp_key,
+                         int32_t* comp_t, int32_t* idx, hipStream_t s);
 
 // attn.hip
 // Attended entries are processed in chunks of kAttnChunk; a block takes
