@@ -275,13 +275,18 @@ __device__ __forceinline__ void load_itab(const int* __restrict__ gtab, int* ita
   for (int i = threadIdx.x; i < kLut / 4; i += blockDim.x) dst[i] = src[i];
 }
 
-// A value at or below the k-th largest of the n scores sc (1 <= k <= n), all in
-// [smin, smax]: the lower edge of the bin holding it in a 2048-bin equal-width
-// histogram, lowered by one more bin so that rounding cannot lift it above.
-// hist: LDS >= 2048; tmp: LDS >= 24 ints.
-__device__ float block_score_floor(const float* sc, int n, int k, float smin, float smax,
-                                   uint32_t* hist, int* tmp) {
-  if (!(smax > smin)) return smin;
+// Two bounds from one 2048-bin equal-width histogram of the n scores sc, all in
+// [smin, smax]: *lo at or below the k_lo-th largest (the lower edge of its bin,
+// lowered by one more bin so that rounding cannot lift it above), and *hi at or
+// above the k_hi-th largest (the upper edge of its bin, raised by one more bin;
+// smax if k_hi < 1).  1 <= k_lo <= n.  hist: LDS >= 2048; tmp: LDS >= 24 ints.
+__device__ void block_score_band(const float* sc, int n, int k_lo, int k_hi, float smin,
+                                 float smax, uint32_t* hist, int* tmp, float* lo, float* hi) {
+  if (!(smax > smin)) {
+    *lo = smin;
+    *hi = smax;
+    return;
+  }
   constexpr int kBins = 2048;
   const float w = (smax - smin) * (1.0f / kBins);
   const float inv = (float)kBins / (smax - smin);
@@ -298,16 +303,21 @@ __device__ float block_score_floor(const float* sc, int n, int k, float smin, fl
   for (int d = d0; d < d0 + per && d < kBins; ++d) cnt += (int)hist[d];
   int total;
   int pre = block_excl_scan(cnt, tmp, &total);
-  const int x = total - k;  // ascending rank of the k-th largest
+  const int x_lo = total - k_lo;  // ascending ranks of the k-th largest
+  const int x_hi = total - k_hi;
+  if (threadIdx.x == 0) tmp[21] = kBins - 1;
+  __syncthreads();
   for (int d = d0; d < d0 + per && d < kBins; ++d) {
     const int c = (int)hist[d];
-    if (pre <= x && x < pre + c) tmp[18] = d;
+    if (pre <= x_lo && x_lo < pre + c) tmp[18] = d;
+    if (k_hi >= 1 && pre <= x_hi && x_hi < pre + c) tmp[21] = d;
     pre += c;
   }
   __syncthreads();
-  const int d = tmp[18];
+  const int dl = tmp[18], dh = tmp[21];
   __syncthreads();
-  return smin + (float)(d - 1) * w;
+  *lo = smin + (float)(dl - 1) * w;
+  *hi = k_hi >= 1 ? fminf(smax, smin + (float)(dh + 2) * w) : smax;
 }
 
 // ------------------------------------------------------------------ prep
@@ -320,7 +330,7 @@ __global__ __launch_bounds__(1024) void prep_kernel(
     const uint16_t* __restrict__ q, int n_q_heads, int Hkv, int G, const float* __restrict__ mu,
     uint8_t* __restrict__ codes, float* __restrict__ alpha, int capacity, int n_tokens,
     const uint16_t* __restrict__ k_sink, const uint16_t* __restrict__ k_new, int64_t ksb,
-    int64_t ksh, const float* __restrict__ codebook, int rank, int mode,
+    int64_t ksh, const float* __restrict__ codebook, int rank, int rank_hi, int mode,
     int* __restrict__ sel_lut, float* __restrict__ sel_inv, float* __restrict__ att_lut,
     float* __restrict__ att_qmu, float* __restrict__ att_slog, float* __restrict__ tau,
     float* __restrict__ bin_scale) {
@@ -482,12 +492,13 @@ __global__ __launch_bounds__(1024) void prep_kernel(
     }
   }
   block_minmax(lo, hi, mm, &lo, &hi);  // its barriers also publish ssc
-  const float th = block_score_floor(ssc, m, rank, key_score(lo), key_score(hi), hist, tmp);
+  float th, th_hi;
+  block_score_band(ssc, m, rank, rank_hi, key_score(lo), key_score(hi), hist, tmp, &th, &th_hi);
   if (tid == 0) {
     tau[bh] = th;
     // the select kernel bins candidate scores linearly, 2048 bins from tau up
-    // to the sample maximum (higher scores share the top bin)
-    const float span = key_score(hi) - th;
+    // to an upper estimate of the k-th score (higher scores share the top bin)
+    const float span = th_hi - th;
     bin_scale[bh] = span > 0.0f ? 2048.0f / span : 0.0f;
   }
 }
@@ -562,6 +573,16 @@ __global__ __launch_bounds__(256) void score_kernel(
     run += (w4.x + w4.y) + (w4.z + w4.w);
   }
   if (tid == 0) chunk_count[(int64_t)bh * n_chunks + blockIdx.x] = run;
+}
+
+// Histogram count of one key per lane (valid lanes only).  Keys above the band
+// all land in the top bin: those are counted once per wave (ballot popcount)
+// instead of by one LDS atomic each, which would serialise on one address.
+__device__ __forceinline__ void count_bin(uint32_t* hist, bool valid, int bin, int lane) {
+  const bool top = valid && bin == 2047;
+  const uint64_t m = __ballot(top);
+  if (valid && !top) atomicAdd(&hist[bin], 1u);
+  if (m != 0ull && lane == __builtin_ctzll(m)) atomicAdd(&hist[2047], (uint32_t)__popcll(m));
 }
 
 // ------------------------------------------------------------------ select
@@ -678,16 +699,19 @@ __global__ __launch_bounds__(1024) void select_kernel(
             dp[o + j] = tt[v][u];
             lo = min(lo, kk[v][u]);
             hi = max(hi, kk[v][u]);
-            if (in_lds) atomicAdd(&hist[bin_of(kk[v][u])], 1u);
           }
+          if (in_lds) count_bin(hist, j < cnt, bin_of(kk[v][u]), lane);
         }
-        for (int j = 256 + lane; j < cnt; j += 64) {  // tiles with many candidates
-          const uint32_t key = cand_key[src + j];
-          dk[o + j] = key;
-          dp[o + j] = cand_t[src + j];
-          lo = min(lo, key);
-          hi = max(hi, key);
-          if (in_lds) atomicAdd(&hist[bin_of(key)], 1u);
+        for (int j0 = 256; j0 < cnt; j0 += 64) {  // tiles with many candidates
+          const int j = j0 + lane;
+          const uint32_t key = j < cnt ? cand_key[src + j] : 0u;
+          if (j < cnt) {
+            dk[o + j] = key;
+            dp[o + j] = cand_t[src + j];
+            lo = min(lo, key);
+            hi = max(hi, key);
+          }
+          if (in_lds) count_bin(hist, j < cnt, bin_of(key), lane);
         }
       }
     }
@@ -737,8 +761,9 @@ __global__ __launch_bounds__(1024) void select_kernel(
 }  // namespace
 
 // rank: how many of the sampled scores lie at or above tau.  For a small head the
-// whole candidate set is the sample and rank = k (tau is then the exact k-th
-// score).  Otherwise the expected rank of the k-th score in the sample plus five
+// whole candidate set is the sample and rank = k (tau is then at most the exact
+// k-th score).  rank_hi: the rank of the upper end of the select kernel's score
+// bins (e - 5 sqrt(e) - 8, or the top of the sample if that is below 1).  Otherwise the expected rank of the k-th score in the sample plus five
 // standard deviations and a small floor, so that fewer than k tokens pass only
 // with negligible probability; the select kernel handles that case exactly anyway.
 hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const float* mu,
@@ -748,19 +773,22 @@ hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const f
                        float* att_lut, float* att_qmu, float* att_slog, float* tau,
                        float* bin_scale, hipStream_t s) {
   const int n = n_tokens - kSink - (k_new != nullptr ? 1 : 0);
-  int rank = 1;
+  int rank = 1, rank_hi = 0;
   if (mode == 1) {
     if (n <= kSampleMax) {
       rank = top_k;
+      rank_hi = top_k;
     } else {
       const double e = (double)top_k * kSampleMax / (double)n;
       const double r = e + 5.0 * __builtin_sqrt(e) + 8.0;
       rank = r > kSampleMax ? kSampleMax + 1 : (int)r + 1;
+      const double rh = e - 5.0 * __builtin_sqrt(e) - 8.0;  // the k-th score lies below w.h.p.
+      rank_hi = rh < 1.0 ? 0 : (int)rh;
     }
   }
   return launch_k(KID_PREP, prep_kernel, dim3(B * Hkv), dim3(1024), 0, s, q, n_q_heads, Hkv,
                   n_q_heads / Hkv, mu, codes, alpha, capacity, n_tokens, k_sink, k_new, ksb, ksh,
-                  codebook, rank, mode, sel_lut, sel_inv, att_lut, att_qmu, att_slog, tau,
+                  codebook, rank, rank_hi, mode, sel_lut, sel_inv, att_lut, att_qmu, att_slog, tau,
                   bin_scale);
 }
 
