@@ -28,7 +28,9 @@ token), decode step (planted-token recall), codebook (closed-form members,
 pure-sign data gives the vertices, least-squares optimality and sign
 consistency by perturbation, brute-force channel loop for its scores, dense
 SDPA with its reconstructed keys, lower reconstruction error than the
-vertices).  No function is left unpinned.
+vertices), quantised values (hand-derived layout and codes, exact levels, constant
+groups, error bound against the scale, all-tokens attention against SDPA over the
+reconstructed values).  No function is left unpinned.
 """
 
 from __future__ import annotations
@@ -209,6 +211,51 @@ def codebook(k_bits, mu, codes, alpha, n_tokens: int) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------- #
+# Quantised values (2-bit, per token): the memory side of the method
+# --------------------------------------------------------------------------- #
+V_GROUP = 32          # channels per value group (one scale and one zero point each)
+V_LEVELS = 3          # 2 bits: codes 0..3
+
+
+def quantize_v(v_bits):
+    """READING (values): the pages report the KV cache shrinking about 5x with 2-bit
+    quantisation at the compression ratio of a 2-bit per-token value scheme, and keep the
+    64 sink tokens in full precision (§2.1 item 3).  Read here as: every non-sink value
+    row is split into 4 groups of 32 channels; per group, z = min, scale s = fl32((max -
+    z) / 3), both stored as fp16 (round to nearest even); code q_c = clamp(rint(fl32(
+    fl32(v_c - z16) / s16)), 0, 3) with z16, s16 the stored values (q = 0 when s16 = 0).
+    Layout: codes [..., T, 32] u8, channel c at byte c // 4, bits 2*(c % 4) and up;
+    scales [..., T, 4, 2] uint16 fp16 bits, (scale, zero) per group.
+
+    v_bits [..., T, 128] bf16 bits.  Returns (codes, sz)."""
+    x = bf16_to_f32(v_bits).astype(np.float32)
+    g = x.reshape(x.shape[:-1] + (HEAD_DIM // V_GROUP, V_GROUP))
+    z = g.min(axis=-1)
+    s = ((g.max(axis=-1) - z) / np.float32(V_LEVELS)).astype(np.float32)
+    z16, s16 = z.astype(np.float16), s.astype(np.float16)
+    zf, sf = z16.astype(np.float32)[..., None], s16.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = ((g - zf).astype(np.float32) / np.where(sf > 0, sf, np.float32(1))).astype(np.float32)
+    q = np.where(sf > 0, np.clip(np.rint(r), 0, V_LEVELS), 0).astype(np.uint8)
+    q = q.reshape(x.shape)                                       # [..., T, 128]
+    q4 = q.reshape(q.shape[:-1] + (HEAD_DIM // 4, 4))
+    codes = (q4[..., 0] | (q4[..., 1] << 2) | (q4[..., 2] << 4) | (q4[..., 3] << 6)).astype(np.uint8)
+    sz = np.stack([s16.view(np.uint16), z16.view(np.uint16)], axis=-1)
+    return codes, sz
+
+
+def dequantize_v(codes, sz) -> np.ndarray:
+    """v^_c = z + q_c * s with the stored fp16 scale and zero point (exact in fp64).
+    codes [..., T, 32], sz [..., T, 4, 2] -> fp64 [..., T, 128]."""
+    c = np.asarray(codes, np.uint8)
+    q = np.stack([(c >> (2 * i)) & 3 for i in range(4)], axis=-1).reshape(c.shape[:-1] + (HEAD_DIM,))
+    s = np.asarray(sz, np.uint16)[..., 0].view(np.float16).astype(np.float64)
+    z = np.asarray(sz, np.uint16)[..., 1].view(np.float16).astype(np.float64)
+    grp = np.arange(HEAD_DIM) // V_GROUP
+    return z[..., grp] + q.astype(np.float64) * s[..., grp]
+
+
+# --------------------------------------------------------------------------- #
 # Decode retrieval: §2.1 item 2 (compressed-domain top-k by LUT-GEMV)
 # --------------------------------------------------------------------------- #
 def centres() -> np.ndarray:
@@ -276,7 +323,7 @@ def select_topk(scores, k: int, first_token: int = N_SINK) -> np.ndarray:
 # Sparse attention over top-k plus sinks: §2.1 items 3 and 4
 # --------------------------------------------------------------------------- #
 def sparse_attention(q_bits_group, idx, k_sink_bits, codes, alpha, mu, v_bits,
-                     sm_scale: float, cb=None) -> np.ndarray:
+                     sm_scale: float, cb=None, vq=None) -> np.ndarray:
     """Attention of the G query heads of one KV head over S = {0..63} U idx
     (§2.1 item 3: sinks always kept in full precision; item 4: keys dequantised
     inside the attention).  Keys: bf16 sink rows for t < 64, else k^_t (fp32,
@@ -286,7 +333,9 @@ def sparse_attention(q_bits_group, idx, k_sink_bits, codes, alpha, mu, v_bits,
 
     q_bits_group [G,128]; idx [k] (token positions >= 64); k_sink_bits [64,128];
     codes [N,16], alpha [N], mu [128], v_bits [N,128] of that KV head; cb: its
-    codebook or None (sign vertices)."""
+    codebook or None (sign vertices); vq: None, or its quantised values (codes [N,32],
+    sz [N,4,2]) from ``quantize_v``, used for every attended t >= 64 (the sinks keep
+    their bf16 rows)."""
     idx = np.asarray(idx, np.int64)
     q = bf16_to_f32(q_bits_group).astype(np.float64)
     kap = np.concatenate([bf16_to_f32(k_sink_bits).astype(np.float64),
@@ -294,6 +343,8 @@ def sparse_attention(q_bits_group, idx, k_sink_bits, codes, alpha, mu, v_bits,
                                      mu, cb).astype(np.float64)], axis=0)
     rows = np.concatenate([np.arange(N_SINK, dtype=np.int64), idx])
     vals = bf16_to_f32(np.asarray(v_bits)[rows]).astype(np.float64)
+    if vq is not None:
+        vals[N_SINK:] = dequantize_v(np.asarray(vq[0])[idx], np.asarray(vq[1])[idx])
     logits = (kap @ q.T) * float(sm_scale)                      # [|S|, G]
     logits -= logits.max(axis=0, keepdims=True)
     p = np.exp(logits)
@@ -310,12 +361,13 @@ def head_scores(q_bits, codes, alpha, b: int, h: int, n_kv_heads: int,
 
 
 def decode_step(q_bits, cache: dict, v_bits, top_k: int, sm_scale: float,
-                n_tokens: int, heads=None) -> dict:
+                n_tokens: int, heads=None, vq=None) -> dict:
     """One decode step: LUT scores -> top-k -> sparse attention, per (b, KV head).
 
     cache: ``encode`` output (codes/alpha indexed by token; the codebook is used
     when present).  v_bits [B,H,>=N,128].
     heads: optional list of (b, h) pairs to compute (others left zero / -1).
+    vq: optional quantised values (codes [B,H,N,32], sz [B,H,N,4,2]).
     Returns idx [B,H,k] int64 and out [B,Hq,128] float32."""
     q_bits = np.asarray(q_bits)
     b_n, hq, _ = q_bits.shape
@@ -333,5 +385,6 @@ def decode_step(q_bits, cache: dict, v_bits, top_k: int, sm_scale: float,
         idx[b, h] = sel
         out[b, h * g:(h + 1) * g] = sparse_attention(
             q_bits[b, h * g:(h + 1) * g], sel, cache["k_sink"][b, h], cache["codes"][b, h],
-            cache["alpha"][b, h], cache["mu"][b, h], v_bits[b, h], sm_scale, cb)
+            cache["alpha"][b, h], cache["mu"][b, h], v_bits[b, h], sm_scale, cb,
+            None if vq is None else (vq[0][b, h], vq[1][b, h]))
     return {"idx": idx, "out": out}

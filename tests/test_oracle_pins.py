@@ -451,3 +451,74 @@ def test_codebook_reconstruction_beats_vertices():
     e_cb = ((O.dequantize(c, a, mu, enc["codebook"][0, 0]) - x) ** 2).sum()
     e_v = ((O.dequantize(c, a, mu) - x) ** 2).sum()
     assert e_cb < e_v
+
+
+# ----------------------------------------------------------------- quantised values
+def test_value_quantisation_hand_case():
+    """Hand-derived case: a group holding exactly z, z+s, z+2s, z+3s (fp16-exact)
+    gets codes 0..3, the layout puts channel c at byte c // 4, bits 2*(c % 4)."""
+    row = np.zeros(128, np.float32)
+    row[:32] = np.tile(np.array([1.0, 1.5, 2.0, 2.5], np.float32), 8)     # z=1, s=0.5
+    row[32:64] = -3.0                                                       # constant group
+    row[64:96] = np.linspace(-1.0, 2.0, 32).astype(np.float32)
+    row[96:] = np.tile(np.array([0.25, 0.0, 0.0, 0.0], np.float32), 8)
+    codes, sz = O.quantize_v(_bf16(row)[None])
+    assert codes.shape == (1, 32) and sz.shape == (1, 4, 2)
+    # group 0: codes 0,1,2,3 repeated -> byte 0b11100100
+    assert codes[0, :8].tolist() == [0b11100100] * 8
+    assert sz[0, 0].view(np.float16).tolist() == [0.5, 1.0]
+    # group 1: constant -> scale 0, zero -3, codes 0
+    assert codes[0, 8:16].tolist() == [0] * 8
+    assert sz[0, 1].view(np.float16).tolist() == [0.0, -3.0]
+    # group 3: one 0.25 then three zeros per 4 channels -> codes 3,0,0,0 -> byte 0b00000011
+    assert codes[0, 24:].tolist() == [3] * 8
+    rec = O.dequantize_v(codes, sz)[0]
+    assert np.array_equal(rec[:32], row[:32].astype(np.float64))
+    assert np.array_equal(rec[32:64], row[32:64].astype(np.float64))
+    # group 3: scale 0.25 / 3 is not fp16-exact, so the top level is 3 * fp16(0.25 / 3)
+    s3 = float(np.float16(np.float32(0.25) / np.float32(3)))
+    assert rec[96] == 3 * s3 and abs(rec[96] - 0.25) < 2 ** -12
+    assert np.all(rec[97:100] == 0.0)
+
+
+def test_value_quantisation_error_bound_and_extremes():
+    """Every reconstructed value lies within half a step (plus the fp16 rounding of the
+    scale and zero point) of the input; codes span 0..3 and the group minimum is
+    reconstructed exactly up to the zero point's rounding."""
+    rng = np.random.default_rng(31)
+    v = _bf16(rng.standard_normal((500, 128)) * rng.uniform(0.1, 5.0, (500, 1)))
+    codes, sz = O.quantize_v(v)
+    rec = O.dequantize_v(codes, sz)
+    x = S.bf16_bits_to_f32(v).astype(np.float64).reshape(500, 4, 32)
+    s = sz[..., 0].view(np.float16).astype(np.float64)[..., None]
+    z = sz[..., 1].view(np.float16).astype(np.float64)[..., None]
+    err = np.abs(rec.reshape(500, 4, 32) - x)
+    zerr = np.abs(z - x.min(axis=-1, keepdims=True))
+    bound = 0.5 * s + zerr + 3 * np.abs(s - (x.max(-1, keepdims=True) - x.min(-1, keepdims=True)) / 3) + 1e-6
+    assert np.all(err <= bound)
+    q = np.stack([(codes >> (2 * i)) & 3 for i in range(4)], -1).reshape(500, 4, 32)
+    assert q.min() == 0 and q.max() == 3
+    assert np.all(q.min(axis=-1) == 0)
+
+
+def test_quantised_value_attention_equals_dense_sdpa():
+    """With k = N - 64 and quantised values the sparse path is dense attention with the
+    bf16 sink values and the reconstructed values of every other token."""
+    rng = np.random.default_rng(32)
+    B, Hq, Hkv, N, G, sm = 1, 2, 1, 180, 2, 1 / math.sqrt(128)
+    q = _bf16(rng.standard_normal((B, Hq, 128)))
+    k = _bf16(rng.normal(0, 1.5, (B, Hkv, 1, 128)) + rng.standard_normal((B, Hkv, N, 128)))
+    v = _bf16(rng.standard_normal((B, Hkv, N, 128)))
+    enc = O.encode(k, N)
+    vq = O.quantize_v(v)
+    res = O.decode_step(q, enc, v, N - 64, sm, N, vq=vq)
+    kap = np.concatenate([S.bf16_bits_to_f32(enc["k_sink"][0, 0]),
+                          O.dequantize(enc["codes"][0, 0, 64:], enc["alpha"][0, 0, 64:],
+                                       enc["mu"][0, 0])]).astype(np.float64)
+    vals = np.concatenate([S.bf16_bits_to_f32(v[0, 0, :64]).astype(np.float64),
+                           O.dequantize_v(vq[0][0, 0, 64:], vq[1][0, 0, 64:])])
+    qq = torch.tensor(S.bf16_bits_to_f32(q[0]), dtype=torch.float64)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        qq[:, None, :], torch.tensor(kap)[None].expand(G, -1, -1),
+        torch.tensor(vals)[None].expand(G, -1, -1), scale=sm)[:, 0]
+    assert np.allclose(res["out"][0], ref.numpy(), rtol=1e-6, atol=1e-7)
