@@ -109,10 +109,13 @@ class Cache:
     k_sink bf16 [B,Hkv,64,128] are owned here; ``v`` (bf16 [B,Hkv,>=cap,128],
     unit channel stride) is only referenced.  codebook=True adds data-derived
     centres, fp32 [B,Hkv,32,16,4], written at prefill and used by every call.
+    quant_v=True keeps the values 2-bit instead (vq uint8 [B,Hkv,cap,32], vsz
+    uint32 [B,Hkv,cap,4], v_sink bf16 [B,Hkv,64,128], written by sikv_encode_v
+    or the fused append step); ``v`` is then not read.
     """
 
     def __init__(self, batch: int, n_kv_heads: int, capacity: int, device="cuda",
-                 v: torch.Tensor | None = None, codebook: bool = False):
+                 v: torch.Tensor | None = None, codebook: bool = False, quant_v: bool = False):
         dev = torch.device(device)
         self.batch, self.n_kv_heads, self.capacity = batch, n_kv_heads, capacity
         self.n_tokens = 0
@@ -123,6 +126,12 @@ class Cache:
                                   device=dev)
         self.codebook = (torch.zeros((batch, n_kv_heads, 32, 16, 4), dtype=torch.float32,
                                      device=dev) if codebook else None)
+        self.vq = self.vsz = self.v_sink = None
+        if quant_v:
+            self.vq = torch.zeros((batch, n_kv_heads, capacity, 32), dtype=torch.uint8, device=dev)
+            self.vsz = torch.zeros((batch, n_kv_heads, capacity, 4), dtype=torch.int32, device=dev)
+            self.v_sink = torch.zeros((batch, n_kv_heads, N_SINK, HEAD_DIM), dtype=torch.bfloat16,
+                                      device=dev)
         self.v = v
         self.ws = Workspace(dev)
 
@@ -143,6 +152,7 @@ class Cache:
             d.v = self.v.data_ptr()
             d.v_stride_b, d.v_stride_h, d.v_stride_t = sb, sh, st
         d.codebook = self.codebook.data_ptr() if self.codebook is not None else None
+        d.vq, d.vsz, d.v_sink = _ptr(self.vq), _ptr(self.vsz), _ptr(self.v_sink)
         return d
 
 
@@ -170,6 +180,16 @@ def sikv_encode(cache: Cache, k: torch.Tensor, t_begin: int = 0, t_end: int | No
            "sikv_encode")
     if not recompute_mu:
         cache.n_tokens = max(cache.n_tokens, t_end)
+
+
+def sikv_encode_v(cache: Cache, v: torch.Tensor, t_begin: int = 0) -> None:
+    """2-bit value codes of tokens [t_begin, t_begin + v.shape[2]) (v holds
+    exactly those rows); rows below 64 are also kept whole in cache.v_sink."""
+    vb = _bits(v)
+    sb, sh, st = _strides_rows(vb, "v")
+    d = cache.desc()
+    _check(lib.sikv_encode_v(ctypes.byref(d), vb.data_ptr(), sb, sh, st, t_begin,
+                             t_begin + vb.shape[2], _stream(cache.device)), "sikv_encode_v")
 
 
 def sikv_score_topk(cache: Cache, q: torch.Tensor, top_k: int, idx: torch.Tensor | None = None,
@@ -223,13 +243,20 @@ def sikv_decode_step(cache: Cache, q: torch.Tensor, top_k: int, sm_scale: float 
 
 def sikv_append_decode_step(cache: Cache, k_new: torch.Tensor, q: torch.Tensor, top_k: int,
                             sm_scale: float | None = None, idx_out: torch.Tensor | None = None,
-                            out: torch.Tensor | None = None):
+                            out: torch.Tensor | None = None, v_new: torch.Tensor | None = None):
     """sikv_encode of token cache.n_tokens (k_new: [B, Hkv, 1, 128]) then
-    sikv_decode_step over n_tokens + 1 tokens, in one call (raises n_tokens)."""
+    sikv_decode_step over n_tokens + 1 tokens, in one call (raises n_tokens).
+    v_new ([B, Hkv, 1, 128], quantised-value caches only) is encoded too."""
     kb = _bits(k_new)
     if kb.dim() != 4 or kb.shape[2] != 1:
         raise ValueError("k_new must be [B, Hkv, 1, 128]")
     ksb, ksh, _ = _strides_rows(kb, "k_new")
+    vnb, vsb, vsh = None, 0, 0
+    if v_new is not None:
+        vnb = _bits(v_new)
+        if vnb.dim() != 4 or vnb.shape[2] != 1:
+            raise ValueError("v_new must be [B, Hkv, 1, 128]")
+        vsb, vsh, _ = _strides_rows(vnb, "v_new")
     qb = _bits(q).contiguous()
     n_q = qb.shape[1]
     sm = 1.0 / math.sqrt(HEAD_DIM) if sm_scale is None else float(sm_scale)
@@ -240,8 +267,8 @@ def sikv_append_decode_step(cache: Cache, k_new: torch.Tensor, q: torch.Tensor, 
         d = cache.desc()
         need = int(lib.sikv_workspace_bytes(OP_DECODE_STEP, ctypes.byref(d), n_q, top_k))
         ws, wsn = cache.ws.get(need)
-        _check(lib.sikv_append_decode_step(ctypes.byref(d), kb.data_ptr(), ksb, ksh,
-                                           qb.data_ptr(), n_q, top_k, ctypes.c_float(sm),
+        _check(lib.sikv_append_decode_step(ctypes.byref(d), kb.data_ptr(), ksb, ksh, _ptr(vnb),
+                                           vsb, vsh, qb.data_ptr(), n_q, top_k, ctypes.c_float(sm),
                                            _ptr(idx_out), out.data_ptr(), ws, wsn,
                                            _stream(cache.device)),
                "sikv_append_decode_step")

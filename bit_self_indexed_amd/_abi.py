@@ -4,7 +4,7 @@ from __future__ import annotations
 
 import ctypes as C
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 STATUS = {
     0: "SIKV_OK",
@@ -32,6 +32,9 @@ class CacheDesc(C.Structure):
         ("v_stride_h", C.c_int64),
         ("v_stride_t", C.c_int64),
         ("codebook", C.c_void_p),
+        ("vq", C.c_void_p),
+        ("vsz", C.c_void_p),
+        ("v_sink", C.c_void_p),
     ]
 
 
@@ -47,8 +50,9 @@ SIGNATURES = {
     "sikv_score_topk": (_I32, [_DESC, _P, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "sikv_sparse_attn": (_I32, [_DESC, _P, _I32, _P, _I32, C.c_float, _P, _P, _SZ, _P]),
     "sikv_decode_step": (_I32, [_DESC, _P, _I32, _I32, C.c_float, _P, _P, _P, _SZ, _P]),
-    "sikv_append_decode_step": (_I32, [_DESC, _P, _I64, _I64, _P, _I32, _I32, C.c_float, _P, _P,
-                                       _P, _SZ, _P]),
+    "sikv_append_decode_step": (_I32, [_DESC, _P, _I64, _I64, _P, _I64, _I64, _P, _I32, _I32,
+                                       C.c_float, _P, _P, _P, _SZ, _P]),
+    "sikv_encode_v": (_I32, [_DESC, _P, _I64, _I64, _I64, _I32, _I32, _P]),
     "sikv_workspace_bytes": (_SZ, [_I32, _DESC, _I32, _I32]),
     "sikv_status_str": (C.c_char_p, [_I32]),
     "sikv_abi_version": (_I32, []),

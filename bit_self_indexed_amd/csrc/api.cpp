@@ -145,6 +145,10 @@ sikv_status check_desc(const sikv_cache_desc* c) {
   if (misaligned(c->codes, 16) || misaligned(c->alpha, 4) || misaligned(c->mu, 16) ||
       misaligned(c->k_sink, 16) || misaligned(c->codebook, 16))
     return SIKV_ERR_INVALID_ARG;
+  if ((c->vq != nullptr || c->vsz != nullptr || c->v_sink != nullptr) &&
+      (!c->vq || !c->vsz || !c->v_sink || misaligned(c->vq, 16) || misaligned(c->vsz, 16) ||
+       misaligned(c->v_sink, 16)))
+    return SIKV_ERR_INVALID_ARG;
   return SIKV_OK;
 }
 
@@ -153,6 +157,7 @@ bool bad_strides(int64_t sb, int64_t sh, int64_t st) {
 }
 
 sikv_status check_v(const sikv_cache_desc* c) {
+  if (c->vq != nullptr) return SIKV_OK;  // quantised values (checked in check_desc)
   if (c->v == nullptr || misaligned(c->v, 16) || bad_strides(c->v_stride_b, c->v_stride_h, c->v_stride_t))
     return SIKV_ERR_INVALID_ARG;
   return SIKV_OK;
@@ -189,7 +194,8 @@ std::atomic<int> g_force_exact{0};
 // k_new (may be null): key of token n_tokens-1, encoded by the prep kernel first.
 sikv_status run_score_topk(const sikv_cache_desc* c, const uint16_t* q, int n_q_heads, int top_k,
                            int32_t* idx, float* scores_opt, void* ws, const ScorePlan& sp,
-                           const uint16_t* k_new, int64_t ksb, int64_t ksh, hipStream_t s) {
+                           const uint16_t* k_new, int64_t ksb, int64_t ksh,
+                           const uint16_t* v_new, int64_t vnsb, int64_t vnsh, hipStream_t s) {
   const int B = c->batch, Hkv = c->n_kv_heads;
   float* tau = at<float>(ws, sp.off_tau);
   int32_t* cnt = at<int32_t>(ws, sp.off_cnt);
@@ -201,7 +207,8 @@ sikv_status run_score_topk(const sikv_cache_desc* c, const uint16_t* q, int n_q_
   float* inv = at<float>(ws, sp.off_inv);
   const int mode = g_force_exact.load(std::memory_order_relaxed) ? 2 : 1;
   SIKV_TRY(launch_prep(q, n_q_heads, B, Hkv, c->mu, c->codes, c->alpha, c->capacity, c->n_tokens,
-                       c->k_sink, k_new, ksb, ksh, c->codebook, top_k, mode, tab, inv,
+                       c->k_sink, k_new, ksb, ksh, v_new, vnsb, vnsh, c->vq, c->vsz, c->codebook,
+                       top_k, mode, tab, inv,
                        at<float>(ws, sp.off_lut), at<float>(ws, sp.off_qmu),
                        at<float>(ws, sp.off_slog), tau, at<float>(ws, sp.off_bin), s));
   SIKV_TRY(launch_score(B, Hkv, c->codes, c->alpha, c->capacity, c->n_tokens, tab, inv, tau,
@@ -222,13 +229,14 @@ sikv_status run_attn(const sikv_cache_desc* c, const uint16_t* q, int n_q_heads,
   AttnTables own{at<float>(ws, ap.off_lut), at<float>(ws, ap.off_qmu), at<float>(ws, ap.off_slog)};
   if (tab == nullptr) {
     SIKV_TRY(launch_prep(q, n_q_heads, c->batch, c->n_kv_heads, c->mu, c->codes, c->alpha,
-                         c->capacity, c->n_tokens, c->k_sink, nullptr, 0, 0, c->codebook, top_k, 0,
-                         nullptr,
+                         c->capacity, c->n_tokens, c->k_sink, nullptr, 0, 0, nullptr, 0, 0,
+                         nullptr, nullptr, c->codebook, top_k, 0, nullptr,
                          nullptr, own.lut, own.qmu, own.slog, nullptr, nullptr, s));
     tab = &own;
   }
   SIKV_TRY(launch_attn(n_q_heads, c->batch, c->n_kv_heads, c->codes, c->alpha, c->v,
-                       c->v_stride_b, c->v_stride_h, c->v_stride_t, c->capacity, c->n_tokens, idx,
+                       c->v_stride_b, c->v_stride_h, c->v_stride_t, c->vq, c->vsz, c->v_sink,
+                       c->capacity, c->n_tokens, idx,
                        top_k, tab->lut, tab->qmu, tab->slog, sm_scale, ap.cpb, ap.n_splits, po,
                        pml, s));
   SIKV_TRY(launch_combine(po, pml, c->batch * n_q_heads, ap.n_splits, out, s));
@@ -248,7 +256,7 @@ double g_ms[KID_COUNT];
 int64_t g_cnt[KID_COUNT];
 const char* const g_names[KID_COUNT] = {"mu_partial", "mu_final", "codes", "prep",
                                         "score",      "select",   "attn",  "combine",
-                                        "dense",      "copy",     "cb_final"};
+                                        "dense",      "copy",     "cb_final", "vcodes"};
 
 hipEvent_t take_event() {
   if (!g_pool.empty()) {
@@ -345,7 +353,8 @@ sikv_status sikv_score_topk(const sikv_cache_desc* c, const uint16_t* q, int32_t
   if (!plan_score(c, n_q_heads, &sp)) return SIKV_ERR_UNSUPPORTED;
   st = check_ws(ws, ws_bytes, sp.bytes);
   if (st != SIKV_OK) return st;
-  return run_score_topk(c, q, n_q_heads, top_k, idx, scores_opt, ws, sp, nullptr, 0, 0,
+  return run_score_topk(c, q, n_q_heads, top_k, idx, scores_opt, ws, sp, nullptr, 0, 0, nullptr,
+                        0, 0,
                         static_cast<hipStream_t>(stream));
 }
 
@@ -371,6 +380,7 @@ sikv_status sikv_sparse_attn(const sikv_cache_desc* c, const uint16_t* q, int32_
 
 namespace {
 sikv_status decode_step(const sikv_cache_desc* c, const uint16_t* k_new, int64_t ksb, int64_t ksh,
+                        const uint16_t* v_new, int64_t vnsb, int64_t vnsh,
                         const uint16_t* q, int32_t n_q_heads, int32_t top_k, float sm_scale,
                         int32_t* idx_out_opt, float* out, void* ws, size_t ws_bytes,
                         void* stream) {
@@ -389,7 +399,8 @@ sikv_status decode_step(const sikv_cache_desc* c, const uint16_t* k_new, int64_t
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t* idx = idx_out_opt ? idx_out_opt : at<int32_t>(ws, dp.off_idx);
   char* wsc = at<char>(ws, dp.off_score);
-  st = run_score_topk(c, q, n_q_heads, top_k, idx, nullptr, wsc, dp.sp, k_new, ksb, ksh, s);
+  st = run_score_topk(c, q, n_q_heads, top_k, idx, nullptr, wsc, dp.sp, k_new, ksb, ksh, v_new,
+                      vnsb, vnsh, s);
   if (st != SIKV_OK) return st;
   const AttnTables tab{at<float>(wsc, dp.sp.off_lut), at<float>(wsc, dp.sp.off_qmu),
                        at<float>(wsc, dp.sp.off_slog)};
@@ -401,19 +412,38 @@ sikv_status decode_step(const sikv_cache_desc* c, const uint16_t* k_new, int64_t
 sikv_status sikv_decode_step(const sikv_cache_desc* c, const uint16_t* q, int32_t n_q_heads,
                              int32_t top_k, float sm_scale, int32_t* idx_out_opt, float* out,
                              void* ws, size_t ws_bytes, void* stream) {
-  return decode_step(c, nullptr, 0, 0, q, n_q_heads, top_k, sm_scale, idx_out_opt, out, ws,
-                     ws_bytes, stream);
+  return decode_step(c, nullptr, 0, 0, nullptr, 0, 0, q, n_q_heads, top_k, sm_scale, idx_out_opt,
+                     out, ws, ws_bytes, stream);
 }
 
 sikv_status sikv_append_decode_step(const sikv_cache_desc* c, const uint16_t* k_new,
-                                    int64_t k_stride_b, int64_t k_stride_h, const uint16_t* q,
-                                    int32_t n_q_heads, int32_t top_k, float sm_scale,
-                                    int32_t* idx_out_opt, float* out, void* ws, size_t ws_bytes,
-                                    void* stream) {
+                                    int64_t k_stride_b, int64_t k_stride_h,
+                                    const uint16_t* v_new, int64_t v_stride_b,
+                                    int64_t v_stride_h, const uint16_t* q, int32_t n_q_heads,
+                                    int32_t top_k, float sm_scale, int32_t* idx_out_opt,
+                                    float* out, void* ws, size_t ws_bytes, void* stream) {
   if (k_new == nullptr || misaligned(k_new, 16) || bad_strides(k_stride_b, k_stride_h, 0))
     return SIKV_ERR_INVALID_ARG;
-  return decode_step(c, k_new, k_stride_b, k_stride_h, q, n_q_heads, top_k, sm_scale, idx_out_opt,
-                     out, ws, ws_bytes, stream);
+  if (v_new != nullptr && (c == nullptr || c->vq == nullptr || misaligned(v_new, 16) ||
+                           bad_strides(v_stride_b, v_stride_h, 0)))
+    return SIKV_ERR_INVALID_ARG;
+  return decode_step(c, k_new, k_stride_b, k_stride_h, v_new, v_stride_b, v_stride_h, q,
+                     n_q_heads, top_k, sm_scale, idx_out_opt, out, ws, ws_bytes, stream);
+}
+
+sikv_status sikv_encode_v(const sikv_cache_desc* c, const uint16_t* v, int64_t v_stride_b,
+                          int64_t v_stride_h, int64_t v_stride_t, int32_t t_begin, int32_t t_end,
+                          void* stream) {
+  const sikv_status st = check_desc(c);
+  if (st != SIKV_OK) return st;
+  if (c->vq == nullptr) return SIKV_ERR_INVALID_ARG;
+  if (v == nullptr || misaligned(v, 16) || bad_strides(v_stride_b, v_stride_h, v_stride_t))
+    return SIKV_ERR_INVALID_ARG;
+  if (t_begin < 0 || t_end <= t_begin || t_end > c->capacity) return SIKV_ERR_INVALID_ARG;
+  SIKV_TRY(launch_vcodes(v, v_stride_b, v_stride_h, v_stride_t, c->batch, c->n_kv_heads, t_begin,
+                         t_end, c->capacity, c->vq, c->vsz, c->v_sink,
+                         static_cast<hipStream_t>(stream)));
+  return SIKV_OK;
 }
 
 size_t sikv_workspace_bytes(int32_t op, const sikv_cache_desc* c, int32_t n_q_heads,

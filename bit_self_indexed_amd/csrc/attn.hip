@@ -74,22 +74,46 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<G>& r, int chunk, int L, in
   }
 }
 
+// Where a lane finds the values of its 8 channels: bf16 rows, or (quantised
+// values) 2-bit codes + the group's fp16 (scale, zero) for t >= 64 and the bf16
+// sink rows for t < 64.
+struct VSource {
+  const uint16_t* vb;    // bf16 V at this lane's channels, row stride vst
+  int64_t vst;
+  const uint8_t* vq;     // this head's value codes, 32 B per token
+  const uint32_t* vsz;   // this head's (scale, zero) words, 4 per token
+  const uint16_t* vsk;   // this head's bf16 sink rows at this lane's channels
+};
+
 // V rows of one chunk for this lane's 16-lane group (t from load_chunk; rows
-// past the end of the list are real rows whose probability is zero).
-__device__ __forceinline__ void load_rows(uint4 (&vr)[kRows], int lane, int t,
-                                          const uint16_t* __restrict__ vb, int64_t vst) {
-  const int grp = lane >> 4;
+// past the end of the list are real rows whose probability is zero).  QV and a
+// non-sink chunk: .x holds the lane's 16 code bits, .y its group's scale/zero.
+template <bool QV>
+__device__ __forceinline__ void load_rows(uint4 (&vr)[kRows], int lane, int t, bool sink_chunk,
+                                          const VSource& vs) {
+  const int grp = lane >> 4, seg = lane & 15;
 #pragma unroll
   for (int u = 0; u < kRows; ++u) {
     const int tu = __shfl(t, grp + 4 * u);
-    vr[u] = *reinterpret_cast<const uint4*>(vb + (int64_t)tu * vst);
+    if (!QV) {
+      vr[u] = *reinterpret_cast<const uint4*>(vs.vb + (int64_t)tu * vs.vst);
+    } else if (sink_chunk) {
+      vr[u] = *reinterpret_cast<const uint4*>(vs.vsk + (int64_t)tu * kD);
+    } else {
+      vr[u].x = *reinterpret_cast<const uint16_t*>(vs.vq + (int64_t)tu * kVCodeBytes + 2 * seg);
+      vr[u].y = vs.vsz[(int64_t)tu * 4 + (seg >> 2)];
+      vr[u].z = 0u;
+      vr[u].w = 0u;
+    }
   }
 }
 
-template <int G>
-__global__ __launch_bounds__(256, G <= 4 ? 4 : 2) void attn_kernel(
+template <int G, bool QV>
+__global__ __launch_bounds__(256, (G <= 4 && !QV) ? 4 : 2) void attn_kernel(
     int n_q_heads, int Hkv, const uint8_t* __restrict__ codes, const float* __restrict__ alpha,
-    const uint16_t* __restrict__ v, int64_t vsb, int64_t vsh, int64_t vst, int capacity,
+    const uint16_t* __restrict__ v, int64_t vsb, int64_t vsh, int64_t vst,
+    const uint8_t* __restrict__ vq, const uint32_t* __restrict__ vsz,
+    const uint16_t* __restrict__ vsink, int capacity,
     int n_tokens, const int32_t* __restrict__ idx, int top_k, const float* __restrict__ att_lut,
     const float* __restrict__ att_qmu, const float* __restrict__ att_slog, float sm_log2,
     int cpb, int n_splits, float* __restrict__ part_o, float* __restrict__ part_ml) {
@@ -111,7 +135,12 @@ __global__ __launch_bounds__(256, G <= 4 ? 4 : 2) void attn_kernel(
   const int32_t* ib = idx + (int64_t)bh * top_k;
   const uint8_t* crow = codes + row0 * kCodeBytes;
   const float* arow = alpha + row0;
-  const uint16_t* vb = v + (int64_t)b * vsb + (int64_t)h * vsh + seg * 8;
+  VSource vs;
+  vs.vb = QV ? nullptr : v + (int64_t)b * vsb + (int64_t)h * vsh + seg * 8;
+  vs.vst = vst;
+  vs.vq = QV ? vq + row0 * kVCodeBytes : nullptr;
+  vs.vsz = QV ? vsz + row0 * 4 : nullptr;
+  vs.vsk = QV ? vsink + (int64_t)bh * kSink * kD + seg * 8 : nullptr;
   const float* slog = att_slog + hq0 * kSink;
 
   int c = s * cpb + wave;
@@ -128,10 +157,11 @@ __global__ __launch_bounds__(256, G <= 4 ? 4 : 2) void attn_kernel(
   for (int i = 0; i < GH; ++i) qmu[i] = (2 * i + half < G) ? att_qmu[hq0 + 2 * i + half] : 0.0f;
   __syncthreads();
 
-  float m[G], lsum[GH], acc[G][8];
+  float m[G], lsum[GH], acc[G][8], zacc[G];  // zacc: sum of p * zero point (QV)
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m[g] = -INFINITY;
+    zacc[g] = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[g][i] = 0.0f;
   }
@@ -155,8 +185,9 @@ __global__ __launch_bounds__(256, G <= 4 ? 4 : 2) void attn_kernel(
       }
       lg[i] = (live && 2 * i + half < G) ? dot * sm_log2 : -INFINITY;
     }
+    const bool sink_chunk = c * kAttnChunk < kSink;
     uint4 vr[kRows];
-    load_rows(vr, lane, cur.t, vb, vst);
+    load_rows<QV>(vr, lane, cur.t, sink_chunk, vs);
     // chunk max per head: heads of parity `half` live in this half of the wave
     float cm[GH], co[GH];
 #pragma unroll
@@ -176,6 +207,7 @@ __global__ __launch_bounds__(256, G <= 4 ? 4 : 2) void attn_kernel(
       m[g] = mn;
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[g][i] *= sc[g];
+      if (QV) zacc[g] *= sc[g];
     }
 #pragma unroll
     for (int i = 0; i < GH; ++i) {
@@ -188,17 +220,39 @@ __global__ __launch_bounds__(256, G <= 4 ? 4 : 2) void attn_kernel(
     }
     wave_sync_lds();
     // P.V
+    if (!QV || sink_chunk) {
 #pragma unroll
-    for (int u = 0; u < kRows; ++u) {
-      const int eu = grp + 4 * u;
-      const uint4 w = vr[u];
-      const float x[8] = {bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y),
-                          bf16lo(w.z), bf16hi(w.z), bf16lo(w.w), bf16hi(w.w)};
+      for (int u = 0; u < kRows; ++u) {
+        const int eu = grp + 4 * u;
+        const uint4 w = vr[u];
+        const float x[8] = {bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y),
+                            bf16lo(w.z), bf16hi(w.z), bf16lo(w.w), bf16hi(w.w)};
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float p = pb[wave][eu][g];
+        for (int g = 0; g < G; ++g) {
+          const float p = pb[wave][eu][g];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[g][i] = fmaf(p, x[i], acc[g][i]);
+          for (int i = 0; i < 8; ++i) acc[g][i] = fmaf(p, x[i], acc[g][i]);
+        }
+      }
+    } else {
+      // v = z + q * s: acc += (p * s) * q per channel, p * z once per row
+#pragma unroll
+      for (int u = 0; u < kRows; ++u) {
+        const int eu = grp + 4 * u;
+        const uint32_t qb = vr[u].x, sz = vr[u].y;
+        const float sv = __half2float(__ushort_as_half((unsigned short)(sz & 0xffffu)));
+        const float zv = __half2float(__ushort_as_half((unsigned short)(sz >> 16)));
+        float qf[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qf[i] = (float)((qb >> (2 * i)) & 3u);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float p = pb[wave][eu][g];
+          const float ps = p * sv;
+          zacc[g] = fmaf(p, zv, zacc[g]);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[g][i] = fmaf(ps, qf[i], acc[g][i]);
+        }
       }
     }
     wave_sync_lds();
@@ -209,7 +263,7 @@ __global__ __launch_bounds__(256, G <= 4 ? 4 : 2) void attn_kernel(
   for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float x = acc[g][i];
+      float x = QV ? acc[g][i] + zacc[g] : acc[g][i];
       x += __shfl_xor(x, 16);
       x += __shfl_xor(x, 32);
       acc[g][i] = x;
@@ -326,7 +380,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }  // namespace
 
 hipError_t launch_attn(int n_q_heads, int B, int Hkv, const uint8_t* codes, const float* alpha,
-                       const uint16_t* v, int64_t vsb, int64_t vsh, int64_t vst, int capacity,
+                       const uint16_t* v, int64_t vsb, int64_t vsh, int64_t vst,
+                       const uint8_t* vq, const uint32_t* vsz, const uint16_t* vsink, int capacity,
                        int n_tokens, const int32_t* idx, int top_k, const float* att_lut,
                        const float* att_qmu, const float* att_slog, float sm_scale,
                        int chunks_per_block, int n_splits, float* part_o, float* part_ml,
@@ -339,9 +394,15 @@ hipError_t launch_attn(int n_q_heads, int B, int Hkv, const uint8_t* codes, cons
   const dim3 grid(n_splits, B * Hkv), block(256);
 #define SIKV_ATTN_CASE(GG)                                                                     \
   case GG:                                                                                     \
-    return launch_k(KID_ATTN, attn_kernel<GG>, grid, block, 0, s, n_q_heads, Hkv, codes,       \
-                    alpha, v, vsb, vsh, vst, capacity, n_tokens, idx, top_k, att_lut, att_qmu, \
-                    att_slog, sm_log2, chunks_per_block, n_splits, part_o, part_ml);
+    if (vq != nullptr)                                                                         \
+      return launch_k(KID_ATTN, attn_kernel<GG, true>, grid, block, 0, s, n_q_heads, Hkv,      \
+                      codes, alpha, v, vsb, vsh, vst, vq, vsz, vsink, capacity, n_tokens, idx, \
+                      top_k, att_lut, att_qmu, att_slog, sm_log2, chunks_per_block, n_splits,  \
+                      part_o, part_ml);                                                        \
+    return launch_k(KID_ATTN, attn_kernel<GG, false>, grid, block, 0, s, n_q_heads, Hkv,       \
+                    codes, alpha, v, vsb, vsh, vst, vq, vsz, vsink, capacity, n_tokens, idx,   \
+                    top_k, att_lut, att_qmu, att_slog, sm_log2, chunks_per_block, n_splits,    \
+                    part_o, part_ml);
   switch (n_q_heads / Hkv) {
     SIKV_ATTN_CASE(1)
     SIKV_ATTN_CASE(2)

@@ -188,6 +188,41 @@ __global__ __launch_bounds__(256) void codes_kernel(const uint16_t* __restrict__
   }
 }
 
+// Value codes: one block per (128-row tile, b*h); 16 lanes per row, 8 rows per
+// thread (quantize_vrow16); lane pairs write one code word, group leaders the
+// (scale, zero) word; rows below 64 are also kept whole in v_sink.
+__global__ __launch_bounds__(256) void vcodes_kernel(const uint16_t* __restrict__ v, int64_t sb,
+                                                     int64_t sh, int64_t st, int Hkv, int t_begin,
+                                                     int t_end, int capacity,
+                                                     uint8_t* __restrict__ vq,
+                                                     uint32_t* __restrict__ vsz,
+                                                     uint16_t* __restrict__ v_sink) {
+  const int bh = blockIdx.y, b = bh / Hkv, h = bh - b * Hkv;
+  const int tid = threadIdx.x, cg = tid & 15, rs = tid >> 4;
+  const int tb = t_begin + blockIdx.x * 128;
+  const uint16_t* base = v + (int64_t)b * sb + (int64_t)h * sh + cg * 8;
+  uint4 w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int t = tb + i * 16 + rs;
+    w[i] = (t < t_end) ? *reinterpret_cast<const uint4*>(base + (int64_t)(t - t_begin) * st)
+                       : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int t = tb + i * 16 + rs;
+    const VRowCode rc = quantize_vrow16(w[i]);
+    const uint32_t pair = rc.bits | (__shfl_down(rc.bits, 1, 16) << 16);
+    if (t < t_end) {
+      const int64_t row = (int64_t)bh * capacity + t;
+      if ((cg & 1) == 0) *reinterpret_cast<uint32_t*>(vq + row * kVCodeBytes + 2 * cg) = pair;
+      if ((cg & 3) == 0) vsz[row * 4 + (cg >> 2)] = rc.sz;
+      if (t < kSink)
+        *reinterpret_cast<uint4*>(v_sink + ((int64_t)bh * kSink + t) * kD + cg * 8) = w[i];
+    }
+  }
+}
+
 // Codebook, stage 2: one block per b*h, thread (j, p).  Block statistics are
 // summed in block order (exact integer sums), then centre_i =
 // fl32((sum_i * 2^-24) / count) computed in fp64; empty cluster: sign vertex p.
@@ -231,6 +266,14 @@ hipError_t launch_codes(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, i
   return launch_k(KID_CODES, codes_kernel<false>, dim3(tiles, B * Hkv), dim3(256), 0, s, k, sb,
                   sh, st, Hkv, t_begin, t_end, capacity, 1, mu, codes, alpha, k_sink,
                   (long long*)nullptr);
+}
+
+hipError_t launch_vcodes(const uint16_t* v, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
+                         int t_begin, int t_end, int capacity, uint8_t* vq, uint32_t* vsz,
+                         uint16_t* v_sink, hipStream_t s) {
+  const int tiles = (t_end - t_begin + 127) / 128;
+  return launch_k(KID_VCODES, vcodes_kernel, dim3(tiles, B * Hkv), dim3(256), 0, s, v, sb, sh, st,
+                  Hkv, t_begin, t_end, capacity, vq, vsz, v_sink);
 }
 
 hipError_t launch_codes_cb(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,

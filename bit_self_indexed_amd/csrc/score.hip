@@ -330,7 +330,9 @@ __global__ __launch_bounds__(1024) void prep_kernel(
     const uint16_t* __restrict__ q, int n_q_heads, int Hkv, int G, const float* __restrict__ mu,
     uint8_t* __restrict__ codes, float* __restrict__ alpha, int capacity, int n_tokens,
     const uint16_t* __restrict__ k_sink, const uint16_t* __restrict__ k_new, int64_t ksb,
-    int64_t ksh, const float* __restrict__ codebook, int rank, int rank_hi, int mode,
+    int64_t ksh, const uint16_t* __restrict__ v_new, int64_t vnsb, int64_t vnsh,
+    uint8_t* __restrict__ vq, uint32_t* __restrict__ vsz,
+    const float* __restrict__ codebook, int rank, int rank_hi, int mode,
     int* __restrict__ sel_lut, float* __restrict__ sel_inv, float* __restrict__ att_lut,
     float* __restrict__ att_qmu, float* __restrict__ att_slog, float* __restrict__ tau,
     float* __restrict__ bin_scale) {
@@ -357,6 +359,11 @@ __global__ __launch_bounds__(1024) void prep_kernel(
                          ? reinterpret_cast<const float4*>(codebook)[(int64_t)bh * kLut + tid]
                          : make_float4(0.f, 0.f, 0.f, 0.f);
 
+  // Appended value row (quantised values): 16 lanes of wave 1, 8 channels each.
+  uint4 vw = make_uint4(0u, 0u, 0u, 0u);
+  if (v_new != nullptr && tid >= 64 && tid < 80)
+    vw = *reinterpret_cast<const uint4*>(v_new + (int64_t)b * vnsb + (int64_t)h * vnsh +
+                                         (tid - 64) * 8);
   // Appended key row: 16 lanes x 8 channels, with the matching means.
   uint4 kw = make_uint4(0u, 0u, 0u, 0u);
   float km[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -401,6 +408,14 @@ __global__ __launch_bounds__(1024) void prep_kernel(
     const int64_t row = row0 + n_tokens - 1;
     if (tid < 16 && (tid & 3) == 0) *reinterpret_cast<uint32_t*>(codes + row * kCodeBytes + tid) = rc.word;
     if (tid == 0) alpha[row] = rc.alpha;
+  }
+  if (v_new != nullptr && wave == 1) {  // the whole wave runs the 4-lane shuffles
+    const VRowCode rc = quantize_vrow16(vw);
+    const uint32_t pair = rc.bits | (__shfl_down(rc.bits, 1, 16) << 16);
+    const int cg = lane, row = n_tokens - 1;
+    if (cg < 16 && (cg & 1) == 0)
+      *reinterpret_cast<uint32_t*>(vq + (row0 + row) * kVCodeBytes + 2 * cg) = pair;
+    if (cg < 16 && (cg & 3) == 0) vsz[(row0 + row) * 4 + (cg >> 2)] = rc.sz;
   }
   __syncthreads();
 
@@ -769,9 +784,10 @@ __global__ __launch_bounds__(1024) void select_kernel(
 hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const float* mu,
                        uint8_t* codes, float* alpha, int capacity, int n_tokens,
                        const uint16_t* k_sink, const uint16_t* k_new, int64_t ksb, int64_t ksh,
-                       const float* codebook, int top_k, int mode, int* sel_lut, float* sel_inv,
-                       float* att_lut, float* att_qmu, float* att_slog, float* tau,
-                       float* bin_scale, hipStream_t s) {
+                       const uint16_t* v_new, int64_t vnsb, int64_t vnsh, uint8_t* vq,
+                       uint32_t* vsz, const float* codebook, int top_k, int mode, int* sel_lut,
+                       float* sel_inv, float* att_lut, float* att_qmu, float* att_slog,
+                       float* tau, float* bin_scale, hipStream_t s) {
   const int n = n_tokens - kSink - (k_new != nullptr ? 1 : 0);
   int rank = 1, rank_hi = 0;
   if (mode == 1) {
@@ -788,7 +804,7 @@ hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const f
   }
   return launch_k(KID_PREP, prep_kernel, dim3(B * Hkv), dim3(1024), 0, s, q, n_q_heads, Hkv,
                   n_q_heads / Hkv, mu, codes, alpha, capacity, n_tokens, k_sink, k_new, ksb, ksh,
-                  codebook, rank, rank_hi, mode, sel_lut, sel_inv, att_lut, att_qmu, att_slog, tau,
+                  v_new, vnsb, vnsh, vq, vsz, codebook, rank, rank_hi, mode, sel_lut, sel_inv, att_lut, att_qmu, att_slog, tau,
                   bin_scale);
 }
 

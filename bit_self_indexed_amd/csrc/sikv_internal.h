@@ -7,6 +7,7 @@
 // streamed (encode, value gathers).
 #pragma once
 
+#include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -16,6 +17,7 @@ namespace sikv {
 constexpr int kD = 128;          // head dim
 constexpr int kSink = 64;        // full-precision sink tokens (§2.1 item 3)
 constexpr int kCodeBytes = 16;   // 1 bit per channel
+constexpr int kVCodeBytes = 32;  // 2-bit value codes per token
 constexpr int kSub = 32;         // 4-dim sub-vectors per key (§2.1 item 1)
 constexpr int kLut = kSub * 16;  // table entries per query
 constexpr int kMaxGroup = 8;
@@ -33,6 +35,7 @@ enum KernelId {
   KID_DENSE,
   KID_COPY,
   KID_CB_FINAL,
+  KID_VCODES,
   KID_COUNT
 };
 
@@ -75,6 +78,42 @@ __device__ __forceinline__ RowCode encode_row16(const uint4& w, const float (&m)
   const uint32_t v16 = byte | (__shfl_down(byte, 1, 16) << 8);
   const uint32_t v32 = v16 | (__shfl_down(v16, 2, 16) << 16);
   return RowCode{v32, s * 0.0078125f, byte};
+}
+
+// 2-bit value code of one bf16 value row held by 16 consecutive lanes (lane cg:
+// channels 8cg..8cg+7 in w; groups of 32 channels = 4 lanes).  Per group: zero
+// point z = min, scale s = fl32((max - z) / 3), both rounded to fp16; code
+// q_c = clamp(rint(fl32(fl32(v_c - z16) / s16)), 0, 3) (0 if s16 = 0).  Returns
+// the lane's 16 code bits (channel 8cg+i at bits 2i) and its group's (scale,
+// zero) fp16 bits as one word.
+struct VRowCode {
+  uint32_t bits;
+  uint32_t sz;
+};
+__device__ __forceinline__ VRowCode quantize_vrow16(const uint4& w) {
+  float x[8];
+  float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[i] = chan(w, i);
+    lo = i == 0 ? x[i] : fminf(lo, x[i]);
+    hi = i == 0 ? x[i] : fmaxf(hi, x[i]);
+  }
+  lo = fminf(lo, __shfl_xor(lo, 1));
+  hi = fmaxf(hi, __shfl_xor(hi, 1));
+  lo = fminf(lo, __shfl_xor(lo, 2));
+  hi = fmaxf(hi, __shfl_xor(hi, 2));
+  lo = lo == 0.0f ? 0.0f : lo;  // a zero minimum is stored as +0
+  const __half z16 = __float2half_rn(lo);
+  const __half s16 = __float2half_rn(__fdiv_rn(hi - lo, 3.0f));
+  const float zf = __half2float(z16), sf = __half2float(s16);
+  uint32_t bits = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float q = sf > 0.0f ? fminf(fmaxf(rintf(__fdiv_rn(x[i] - zf, sf)), 0.0f), 3.0f) : 0.0f;
+    bits |= (uint32_t)q << (2 * i);
+  }
+  return VRowCode{bits, (uint32_t)__half_as_ushort(s16) | ((uint32_t)__half_as_ushort(z16) << 16)};
 }
 
 // Order-preserving map of fp32 (no NaN) to uint32.
@@ -185,6 +224,11 @@ hipError_t launch_mu_final(const float* partial, int BH, int nblk, int n_tokens,
 hipError_t launch_codes(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
                         int t_begin, int t_end, int capacity, const float* mu, uint8_t* codes,
                         float* alpha, uint16_t* k_sink, hipStream_t s);
+// 2-bit value codes of rows t_begin..t_end-1 (quantize_vrow16): vq [B*Hkv][cap][32],
+// vsz [B*Hkv][cap][4] words; rows below 64 are also copied to v_sink.
+hipError_t launch_vcodes(const uint16_t* v, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
+                         int t_begin, int t_end, int capacity, uint8_t* vq, uint32_t* vsz,
+                         uint16_t* v_sink, hipStream_t s);
 // Prefill codes with the codebook statistics: like launch_codes over [0, n_tokens),
 // plus, per block of kCbTiles x 128 tokens, the fixed-point sums of k~/alpha and
 // the counts of every (sub-vector, pattern) over the tokens [64, n_tokens),
@@ -211,14 +255,16 @@ hipError_t launch_cb_final(const long long* cb_part, int BH, int nblk, float* co
 // sign vertices).  k_new (may be null): bf16 key of token n_tokens-1, element (b,h,c) at
 // k_new[b*ksb + h*ksh + c]; the kernel first encodes it into codes / alpha
 // (append with the frozen mean, bit-identical to launch_codes) and leaves that
-// token out of its sample.  bin_scale [B*Hkv]: width of the select kernel's
+// token out of its sample.  v_new (may be null): that token's bf16 value row,
+// quantised into vq / vsz (launch_vcodes layout).  bin_scale [B*Hkv]: width of the select kernel's
 // score bins (2048 bins from tau to the sample maximum; 0 when not sampled).
 hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const float* mu,
                        uint8_t* codes, float* alpha, int capacity, int n_tokens,
                        const uint16_t* k_sink, const uint16_t* k_new, int64_t ksb, int64_t ksh,
-                       const float* codebook, int top_k, int mode, int* sel_lut, float* sel_inv,
-                       float* att_lut, float* att_qmu, float* att_slog, float* tau,
-                       float* bin_scale, hipStream_t s);
+                       const uint16_t* v_new, int64_t vnsb, int64_t vnsh, uint8_t* vq,
+                       uint32_t* vsz, const float* codebook, int top_k, int mode, int* sel_lut,
+                       float* sel_inv, float* att_lut, float* att_qmu, float* att_slog,
+                       float* tau, float* bin_scale, hipStream_t s);
 hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha, int capacity,
                         int n_tokens, const int* sel_lut, const float* sel_inv, const float* tau,
                         int chunk,
@@ -236,8 +282,11 @@ hipError_t launch_select(int B, int Hkv, const uint8_t* codes, const float* alph
 // chunks_per_block consecutive chunks of one (b, KV head) and writes one
 // (max, sum, o) partial per query head.
 constexpr int kAttnChunk = 32;
+// vq (may be null): quantised values (vq, vsz: launch_vcodes; vsink [B*Hkv][64][128]
+// bf16) replace the bf16 V rows.
 hipError_t launch_attn(int n_q_heads, int B, int Hkv, const uint8_t* codes, const float* alpha,
-                       const uint16_t* v, int64_t vsb, int64_t vsh, int64_t vst, int capacity,
+                       const uint16_t* v, int64_t vsb, int64_t vsh, int64_t vst,
+                       const uint8_t* vq, const uint32_t* vsz, const uint16_t* vsink, int capacity,
                        int n_tokens, const int32_t* idx, int top_k, const float* att_lut,
                        const float* att_qmu, const float* att_slog, float sm_scale,
                        int chunks_per_block, int n_splits, float* part_o, float* part_ml,

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define SIKV_ABI_VERSION 1
+#define SIKV_ABI_VERSION 2
 #define SIKV_HEAD_DIM 128
 #define SIKV_N_SINK 64
 #define SIKV_MAX_GROUP 8
@@ -85,6 +85,15 @@ typedef int32_t sikv_status;
  *          recompute_mu = 1 writes them, every scoring and attention call
  *          uses them (key_t = mu + alpha_t * centre of its cluster, per
  *          sub-vector).  Appended tokens keep the prefill centres.
+ *   vq, vsz, v_sink  NULL: attention reads the bf16 V cache `v`.  Else (all three
+ *          set, 16-byte aligned) the values are kept 2-bit (the pages' 2-bit
+ *          setting, read as a per-token value scheme; the 64 sinks stay full
+ *          precision, §2.1 item 3): vq uint8 [B][Hkv][capacity][32] (channel c at
+ *          byte c/4, bits 2*(c%4)), vsz uint32 [B][Hkv][capacity][4] (per group of
+ *          32 channels: fp16 scale in the low half, fp16 zero point in the high
+ *          half), v_sink bf16 [B][Hkv][64][128]; written by sikv_encode_v (or the
+ *          fused step); `v` is then not read and may be NULL.  Value of channel c:
+ *          zero + code * scale of its group.
  * n_tokens (N) is the number of valid tokens of every sequence (64 < N <=
  * capacity); candidates for top-k are the tokens 64..N-1.
  */
@@ -104,6 +113,9 @@ typedef struct sikv_cache_desc {
   int64_t v_stride_h;
   int64_t v_stride_t;
   float *codebook;
+  uint8_t *vq;
+  uint32_t *vsz;
+  uint16_t *v_sink;
 } sikv_cache_desc;
 
 /*
@@ -133,6 +145,21 @@ typedef struct sikv_cache_desc {
 sikv_status sikv_encode(const sikv_cache_desc *cache, const uint16_t *k, int64_t k_stride_b,
                         int64_t k_stride_h, int64_t k_stride_t, int32_t t_begin, int32_t t_end,
                         int32_t recompute_mu, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * sikv_encode_v - 2-bit value codes of tokens t_begin..t_end-1 (requires vq, vsz
+ * and v_sink in the descriptor).  Per token and group of 32 channels: z = min
+ * (+0 when zero), s = fl32((max - z) / 3), both rounded to fp16 (nearest even);
+ * code = clamp(rint(fl32(fl32(v - z16) / s16)), 0, 3), 0 when s16 = 0.  Rows
+ * below 64 are also copied whole to v_sink.  Stateless per token: the same call
+ * serves prefill and append.  Bit-identical to that definition.
+ *   v  bf16 values of those tokens: element (b,h,t,c) at v[b*v_stride_b +
+ *      h*v_stride_h + (t - t_begin)*v_stride_t + c] (strides multiples of 8,
+ *      16-byte aligned).  No workspace.
+ */
+sikv_status sikv_encode_v(const sikv_cache_desc *cache, const uint16_t *v, int64_t v_stride_b,
+                          int64_t v_stride_h, int64_t v_stride_t, int32_t t_begin, int32_t t_end,
+                          void *stream);
 
 /*
  * sikv_score_topk - compressed-domain retrieval (§2.1 item 2).  For every KV
@@ -185,13 +212,16 @@ sikv_status sikv_decode_step(const sikv_cache_desc *cache, const uint16_t *q, in
  *   k_new  bf16 key of token n_tokens-1: element (b,h,c) at
  *          k_new[b*k_stride_b + h*k_stride_h + c] (strides in elements,
  *          multiples of 8; 16-byte aligned).
+ *   v_new  NULL, or (quantised values) that token's bf16 value row, same
+ *          stride scheme, encoded as sikv_encode_v would before the step.
  * Workspace: SIKV_OP_DECODE_STEP.
  */
 sikv_status sikv_append_decode_step(const sikv_cache_desc *cache, const uint16_t *k_new,
-                                    int64_t k_stride_b, int64_t k_stride_h, const uint16_t *q,
-                                    int32_t n_q_heads, int32_t top_k, float sm_scale,
-                                    int32_t *idx_out_opt, float *out, void *ws, size_t ws_bytes,
-                                    void *stream);
+                                    int64_t k_stride_b, int64_t k_stride_h,
+                                    const uint16_t *v_new, int64_t v_stride_b,
+                                    int64_t v_stride_h, const uint16_t *q, int32_t n_q_heads,
+                                    int32_t top_k, float sm_scale, int32_t *idx_out_opt,
+                                    float *out, void *ws, size_t ws_bytes, void *stream);
 
 /* Workspace bytes needed by `op` (SIKV_OP_*) for this cache and call shape.
  * Host only, launches nothing.  Returns 0 for an invalid combination. */

@@ -221,8 +221,8 @@ def quantize_v(v_bits):
     """READING (values): the pages report the KV cache shrinking about 5x with 2-bit
     quantisation at the compression ratio of a 2-bit per-token value scheme, and keep the
     64 sink tokens in full precision (§2.1 item 3).  Read here as: every non-sink value
-    row is split into 4 groups of 32 channels; per group, z = min, scale s = fl32((max -
-    z) / 3), both stored as fp16 (round to nearest even); code q_c = clamp(rint(fl32(
+    row is split into 4 groups of 32 channels; per group, z = min (+0 when it is zero),
+    scale s = fl32((max - z) / 3), both stored as fp16 (round to nearest even); code q_c = clamp(rint(fl32(
     fl32(v_c - z16) / s16)), 0, 3) with z16, s16 the stored values (q = 0 when s16 = 0).
     Layout: codes [..., T, 32] u8, channel c at byte c // 4, bits 2*(c % 4) and up;
     scales [..., T, 4, 2] uint16 fp16 bits, (scale, zero) per group.
@@ -231,6 +231,7 @@ def quantize_v(v_bits):
     x = bf16_to_f32(v_bits).astype(np.float32)
     g = x.reshape(x.shape[:-1] + (HEAD_DIM // V_GROUP, V_GROUP))
     z = g.min(axis=-1)
+    z = np.where(z == 0, np.float32(0), z).astype(np.float32)   # a zero minimum is +0
     s = ((g.max(axis=-1) - z) / np.float32(V_LEVELS)).astype(np.float32)
     z16, s16 = z.astype(np.float16), s.astype(np.float16)
     zf, sf = z16.astype(np.float32)[..., None], s16.astype(np.float32)[..., None]

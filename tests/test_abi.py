@@ -38,10 +38,10 @@ def test_header_functions_are_exported_and_declared():
 
 def test_abi_version_and_desc_layout():
     assert lib.sikv_abi_version() == _abi.ABI_VERSION
-    assert lib.sikv_desc_size() == C.sizeof(_abi.CacheDesc) == 96
+    assert lib.sikv_desc_size() == C.sizeof(_abi.CacheDesc) == 120
     offs = {f[0]: getattr(_abi.CacheDesc, f[0]).offset for f in _abi.CacheDesc._fields_}
     assert offs["codes"] == 24 and offs["v"] == 56 and offs["v_stride_t"] == 80
-    assert offs["codebook"] == 88
+    assert offs["codebook"] == 88 and offs["vq"] == 96 and offs["v_sink"] == 112
 
 
 def test_status_strings():
@@ -56,7 +56,7 @@ def desc(**kw):
     d.batch, d.n_kv_heads, d.head_dim, d.capacity, d.n_tokens, d.n_sink = 2, 2, 128, 1000, 900, 64
     d.codes, d.alpha, d.mu, d.k_sink = FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000
     d.v, d.v_stride_b, d.v_stride_h, d.v_stride_t = FAKE + 0x400000, 2 * 1000 * 128, 1000 * 128, 128
-    d.codebook = None
+    d.codebook = d.vq = d.vsz = d.v_sink = None
     for k, v in kw.items():
         setattr(d, k, v)
     return d
@@ -98,6 +98,8 @@ def test_workspace_sizes():
     ("codes", FAKE + 8, INVALID),
     ("mu", FAKE + 4, INVALID),
     ("alpha", FAKE + 2, INVALID),
+    ("vq", FAKE + 0x600000, INVALID),                               # vsz, v_sink missing
+    ("v_sink", FAKE + 0x600000, INVALID),
 ])
 def test_descriptor_validation(field, value, expect):
     d = desc(**{field: value})
@@ -145,17 +147,45 @@ def test_append_decode_validation():
     f = C.c_float
     need = lib.sikv_workspace_bytes(3, C.byref(d), 4, 16)
     # missing or misaligned new key row, bad strides: rejected before any launch
-    assert lib.sikv_append_decode_step(C.byref(d), None, 1024, 128, FAKE, 4, 16, f(0.088), None,
+    assert lib.sikv_append_decode_step(C.byref(d), None, 1024, 128, None, 0, 0, FAKE, 4, 16, f(0.088), None,
                                        FAKE, FAKE, need, None) == INVALID
-    assert lib.sikv_append_decode_step(C.byref(d), FAKE + 2, 1024, 128, FAKE, 4, 16, f(0.088),
+    assert lib.sikv_append_decode_step(C.byref(d), FAKE + 2, 1024, 128, None, 0, 0, FAKE, 4, 16, f(0.088),
                                        None, FAKE, FAKE, need, None) == INVALID
-    assert lib.sikv_append_decode_step(C.byref(d), FAKE, 1024, 100, FAKE, 4, 16, f(0.088), None,
+    assert lib.sikv_append_decode_step(C.byref(d), FAKE, 1024, 100, None, 0, 0, FAKE, 4, 16, f(0.088), None,
                                        FAKE, FAKE, need, None) == INVALID
-    assert lib.sikv_append_decode_step(C.byref(d), FAKE, 1024, 128, FAKE, 4, 16, f(0.088), None,
+    assert lib.sikv_append_decode_step(C.byref(d), FAKE, 1024, 128, None, 0, 0, FAKE, 4, 16, f(0.088), None,
                                        FAKE, FAKE, need - 256, None) == WORKSPACE
     nd = desc(v=None)
-    assert lib.sikv_append_decode_step(C.byref(nd), FAKE, 1024, 128, FAKE, 4, 16, f(0.088), None,
+    assert lib.sikv_append_decode_step(C.byref(nd), FAKE, 1024, 128, None, 0, 0, FAKE, 4, 16, f(0.088), None,
                                        FAKE, FAKE, need, None) == INVALID
+
+
+def test_quantised_value_validation():
+    f = C.c_float
+    qd = desc(v=None, vq=FAKE + 0x600000, vsz=FAKE + 0x700000, v_sink=FAKE + 0x800000)
+    d = desc()
+    need = lib.sikv_workspace_bytes(3, C.byref(qd), 4, 16)
+    assert need > 0
+    # v_new only with quantised values; aligned, strides multiples of 8
+    assert lib.sikv_append_decode_step(C.byref(d), FAKE, 1024, 128, FAKE, 1024, 128, FAKE, 4, 16,
+                                       f(0.088), None, FAKE, FAKE, need, None) == INVALID
+    assert lib.sikv_append_decode_step(C.byref(qd), FAKE, 1024, 128, FAKE + 2, 1024, 128, FAKE,
+                                       4, 16, f(0.088), None, FAKE, FAKE, need, None) == INVALID
+    assert lib.sikv_append_decode_step(C.byref(qd), FAKE, 1024, 128, FAKE, 1024, 12, FAKE, 4, 16,
+                                       f(0.088), None, FAKE, FAKE, need, None) == INVALID
+    assert lib.sikv_append_decode_step(C.byref(qd), FAKE, 1024, 128, FAKE, 1024, 128, FAKE, 4, 16,
+                                       f(0.088), None, FAKE, FAKE, need - 256, None) == WORKSPACE
+    ev = lib.sikv_encode_v
+    assert ev(C.byref(d), FAKE, 0, 0, 128, 0, 10, None) == INVALID          # no vq
+    assert ev(C.byref(qd), None, 0, 0, 128, 0, 10, None) == INVALID
+    assert ev(C.byref(qd), FAKE + 2, 0, 0, 128, 0, 10, None) == INVALID
+    assert ev(C.byref(qd), FAKE, 0, 0, 100, 0, 10, None) == INVALID         # stride
+    assert ev(C.byref(qd), FAKE, 0, 0, 128, 10, 10, None) == INVALID        # empty
+    assert ev(C.byref(qd), FAKE, 0, 0, 128, -1, 10, None) == INVALID
+    assert ev(C.byref(qd), FAKE, 0, 0, 128, 0, 1001, None) == INVALID       # > capacity
+    assert lib.sikv_encode_v(None, FAKE, 0, 0, 128, 0, 10, None) == INVALID
+    misal = desc(v=None, vq=FAKE + 0x600004, vsz=FAKE + 0x700000, v_sink=FAKE + 0x800000)
+    assert score(misal) == INVALID
 
 
 def test_encode_validation():
