@@ -46,6 +46,7 @@ def parse():
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-dense", action="store_true", help="skip the dense bf16 comparator")
+    p.add_argument("--no-qv", action="store_true", help="skip the 2-bit value variant")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--summarize-trace", nargs=2, metavar=("RUN_DIR", "OUT_TXT"),
                    help="write a text summary of a rocprofv3 --kernel-trace --stats run and exit")
@@ -67,6 +68,9 @@ def algorithmic_bytes(w, kernel: str) -> float:
     if kernel == "attn":            # idx + code + scale + V row per selected token,
         per_head = k * (4 + 16 + 4 + 256) + 64 * 512 + 512     # sinks K+V, mean
         return BH * per_head + w.batch * w.n_q_heads * 256       # queries
+    if kernel == "attn_qv":         # the same with 2-bit values: 32-byte codes + 4 fp16 pairs
+        per_head = k * (4 + 16 + 4 + 32 + 16) + 64 * 512 + 512
+        return BH * per_head + w.batch * w.n_q_heads * 256
     if kernel == "select":          # selection written
         return 4.0 * BH * k
     if kernel == "codes":           # append: one key row in, code + scale out
@@ -386,6 +390,48 @@ def main():
                     if name in ("mu_partial", "mu_final", "codes", "cb_final") and n)
     del enc_c
 
+    # the same step with 2-bit values (per-token groups of 32 channels, bf16 sinks):
+    # the appended value row is quantised inside the step
+    qv_us = qv_kern_us = None
+    if not args.no_qv:
+        V0 = up(d["V"])
+        qcaches = []
+        for layer in range(L):
+            c = sk.Cache(w.batch, w.n_kv_heads, N, device=dev, quant_v=True)
+            sk.sikv_encode(c, K[:, :, :N - 1])
+            sk.sikv_encode_v(c, V0[:, :, :N - 1])
+            qcaches.append(c)
+        v_new = V0[:, :, N - 1:N]
+        torch.cuda.synchronize()
+        del V0
+
+        def qstep(layer):
+            c = qcaches[layer]
+            c.n_tokens = N - 1
+            sk.sikv_append_decode_step(c, k_new, q_all, w.top_k, sm, idx_out=idxs[layer],
+                                       out=outs[layer], v_new=v_new)
+
+        for i in range(max(args.warmup, L)):
+            qstep(i % L)
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(args.steps):
+            qstep(i % L)
+        ev1.record()
+        torch.cuda.synchronize()
+        qv_us = ev0.elapsed_time(ev1) * 1e3 / args.steps
+        sk.timing_reset()
+        sk.timing_enable(True)
+        for i in range(args.steps):
+            qstep(i % L)
+        torch.cuda.synchronize()
+        qt = sk.timing_read()
+        sk.timing_enable(False)
+        qv_kern_us = {name: 1e3 * tot / n for name, (n, tot) in qt.items() if n}
+        log(f"2-bit values: {qv_us:.1f} us/step, kernel avg us:",
+            {k: round(v, 2) for k, v in qv_kern_us.items()})
+        del qcaches
+
     # dense bf16 comparator over the same (uncompressed) cache
     dense_us = dense_torch_us = None
     if not args.no_dense:
@@ -476,6 +522,15 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if qv_us is not None:
+        a_qv = algorithmic_bytes(w, "attn_qv")
+        report["quantised_values"] = {
+            "decode_step_us": qv_us,
+            "kernel_avg_us": qv_kern_us,
+            "speedup_vs_dense": (min(dense_us, dense_torch_us) / qv_us) if dense_us else None,
+            "attn_algorithmic_bytes": a_qv,
+            "attn_achieved_gbs": a_qv / (qv_kern_us["attn"] * 1e-6) / 1e9,
+        }
     print(json.dumps(report), flush=True)
 
 
