@@ -103,15 +103,16 @@ bool plan_score(const sikv_cache_desc* c, int n_q_heads, ScorePlan* p) {
 // Attention grid: the attended list (64 sinks + k) of each (b, KV head) is cut
 // into chunks of kAttnChunk entries; a block of four waves takes chunks_per_block
 // consecutive chunks (a multiple of 4, so every wave gets the same count), the
-// smallest such that the grid has at most two blocks per CU: each wave then
-// loops over several chunks with its prefetch running ahead, which measured
-// faster than more, shorter-lived blocks.  Workspace: the block partials (o,
+// smallest such that the grid has at most two blocks per CU (and at most
+// kAttnMaxCpb, the block's LDS slice of positions): each wave then loops over
+// several chunks with its prefetch running ahead, which measured faster than
+// more, shorter-lived blocks.  Workspace: the block partials (o,
 // max, sum) and, for a standalone call, the query heads' tables.
 void plan_attn(const sikv_cache_desc* c, int n_q_heads, int top_k, AttnPlan* p) {
   const int64_t BH = (int64_t)c->batch * c->n_kv_heads;
   const int64_t nch = cdiv((int64_t)kSink + top_k, kAttnChunk);
   int64_t cpb = 4;
-  while (BH * cdiv(nch, cpb) > kAttnBlocks) cpb += 4;
+  while (BH * cdiv(nch, cpb) > kAttnBlocks && cpb < kAttnMaxCpb) cpb += 4;
   p->cpb = (int)cpb;
   p->n_splits = (int)cdiv(nch, cpb);
   const size_t rows = (size_t)c->batch * n_q_heads * p->n_splits;

@@ -19,8 +19,15 @@
 //            probabilities through a wave-private LDS row;
 //   P.V      16-lane group r owns entries r, r+4, ..., r+28: 16 bytes (8 bf16
 //            channels) of each V row per lane, fp32 FMAs into G x 8 accumulators.
-// The next chunk's codes, scales and V rows are requested before the current
-// chunk is computed.  The combine kernel then merges the blocks' partials.
+// The block first copies its slice of the position list into LDS (one round
+// trip), so a wave can issue all loads of its next chunk (codes, scales and V
+// rows) right after the current chunk's have arrived, before computing it.
+// Measured on the 128K shape (random positions, 8 rotating layers): ~25 us per
+// block of 5 chunks per wave; contiguous positions take ~8 us less and a
+// single resident layer another ~5 us less, so the time is set by the random
+// gathers themselves (DRAM pages, translation), with the VALU work (~750
+// instructions per chunk, two waves per SIMD) as the floor underneath.  The
+// combine kernel then merges the blocks' partials.
 // (A last-block-merges variant needs device-scope fences, which on gfx950 write
 // back and invalidate the whole L2 of the XCD in every block: far slower than
 // one more launch.)
@@ -34,82 +41,167 @@ namespace {
 
 constexpr int kRows = kAttnChunk / 4;  // V rows per 16-lane group per chunk
 
-// Logit inputs of one chunk for one lane.
-template <int G>
-struct ChunkRegs {
-  uint4 code;                   // code of entry (lane & 31)
-  float a;                      // its scale (0 for sinks)
-  int t;                        // its token position
-  float sl[(G + 1) / 2];        // sink logits of this lane's heads (sinks only)
-};
-
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int G>
-__device__ __forceinline__ void load_chunk(ChunkRegs<G>& r, int chunk, int L, int lane,
-                                           const int32_t* __restrict__ ib,
-                                           const uint8_t* __restrict__ crow,
-                                           const float* __restrict__ arow, int n_tokens,
-                                           const float* __restrict__ slog) {
-  const int el = lane & 31, half = lane >> 5;
-  const int e = chunk * kAttnChunk + el;
-  if (chunk * kAttnChunk < kSink) {  // sink chunk (wave-uniform)
-    r.t = e;
-    r.code = make_uint4(0u, 0u, 0u, 0u);
-    r.a = 0.0f;
-#pragma unroll
-    for (int i = 0; i < (G + 1) / 2; ++i) r.sl[i] = slog[min(2 * i + half, G - 1) * kSink + e];
-  } else {
-    // entries past the end re-read the last one; their probabilities are zero
-    const int t = min(max(ib[min(e, L - 1) - kSink], 0), n_tokens - 1);  // clamp: memory safety
-    r.t = t;
-    r.code = *reinterpret_cast<const uint4*>(crow + (int64_t)t * kCodeBytes);
-    r.a = arow[t];
-#pragma unroll
-    for (int i = 0; i < (G + 1) / 2; ++i) r.sl[i] = 0.0f;
-  }
-}
-
-// Where a lane finds the values of its 8 channels: bf16 rows, or (quantised
-// values) 2-bit codes + the group's fp16 (scale, zero) for t >= 64 and the bf16
-// sink rows for t < 64.
-struct VSource {
-  const uint16_t* vb;    // bf16 V at this lane's channels, row stride vst
+// Where a lane finds its inputs: codes / scales of the head, bf16 V at this
+// lane's channels (row stride vst), or (quantised values) the head's 2-bit
+// codes (32 B per token), (scale, zero) words (4 per token) and bf16 sink rows.
+struct Src {
+  const uint8_t* codes;
+  const float* alpha;
+  const float* slog;     // sink logits of the block's G query heads [G][64]
+  const uint16_t* vb;
   int64_t vst;
-  const uint8_t* vq;     // this head's value codes, 32 B per token
-  const uint32_t* vsz;   // this head's (scale, zero) words, 4 per token
-  const uint16_t* vsk;   // this head's bf16 sink rows at this lane's channels
+  const uint8_t* vq;
+  const uint32_t* vsz;
+  const uint16_t* vsk;
 };
 
-// V rows of one chunk for this lane's 16-lane group (t from load_chunk; rows
-// past the end of the list are real rows whose probability is zero).  QV and a
-// non-sink chunk: .x holds the lane's 16 code bits, .y its group's scale/zero.
-template <bool QV>
-__device__ __forceinline__ void load_rows(uint4 (&vr)[kRows], int lane, int t, bool sink_chunk,
-                                          const VSource& vs) {
-  const int grp = lane >> 4, seg = lane & 15;
+// Registers of one chunk for one lane: the logit inputs of entry (lane & 31)
+// and the V data of the 16-lane group's 8 rows (entries grp, grp+4, ...).
+// Quantised values of a non-sink chunk: v[u].x holds the lane's 16 code bits,
+// v[u].y its group's scale/zero word.
+template <int G>
+struct Chunk {
+  uint4 code;
+  float a;
+  float sl[(G + 1) / 2];  // sink logits (sink chunks)
+  uint4 v[kRows];
+};
+
+// Issues every load of block-local chunk lc.  sidx holds the block's positions
+// (the sinks' own, entries past the list end repeat its last), so every
+// address is a real row.  A sink chunk reads the sink logits instead of codes.
+template <int G, bool QV>
+__device__ __forceinline__ void load_chunk(Chunk<G>& x, int lc, bool sink, const int* sidx,
+                                           int lane, const Src& src) {
+  const int el = lane & 31, half = lane >> 5, grp = lane >> 4, seg = lane & 15;
+  const int t = sidx[lc * kAttnChunk + el];
+  if (sink) {
+    x.code = make_uint4(0u, 0u, 0u, 0u);
+    x.a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < (G + 1) / 2; ++i) x.sl[i] = src.slog[min(2 * i + half, G - 1) * kSink + t];
+  } else {
+    x.code = *reinterpret_cast<const uint4*>(src.codes + (int64_t)t * kCodeBytes);
+    x.a = src.alpha[t];
+#pragma unroll
+    for (int i = 0; i < (G + 1) / 2; ++i) x.sl[i] = 0.0f;
+  }
 #pragma unroll
   for (int u = 0; u < kRows; ++u) {
-    const int tu = __shfl(t, grp + 4 * u);
+    const int tu = sidx[lc * kAttnChunk + grp + 4 * u];
     if (!QV) {
-      vr[u] = *reinterpret_cast<const uint4*>(vs.vb + (int64_t)tu * vs.vst);
-    } else if (sink_chunk) {
-      vr[u] = *reinterpret_cast<const uint4*>(vs.vsk + (int64_t)tu * kD);
+      x.v[u] = *reinterpret_cast<const uint4*>(src.vb + (int64_t)tu * src.vst);
+    } else if (sink) {
+      x.v[u] = *reinterpret_cast<const uint4*>(src.vsk + (int64_t)tu * kD);
     } else {
-      vr[u].x = *reinterpret_cast<const uint16_t*>(vs.vq + (int64_t)tu * kVCodeBytes + 2 * seg);
-      vr[u].y = vs.vsz[(int64_t)tu * 4 + (seg >> 2)];
-      vr[u].z = 0u;
-      vr[u].w = 0u;
+      x.v[u].x = *reinterpret_cast<const uint16_t*>(src.vq + (int64_t)tu * kVCodeBytes + 2 * seg);
+      x.v[u].y = src.vsz[(int64_t)tu * 4 + (seg >> 2)];
+      x.v[u].z = 0u;
+      x.v[u].w = 0u;
     }
   }
 }
 
+// Online-softmax state of one wave (heads of parity `half` in this half).
+template <int G>
+struct Acc {
+  float m[G], lsum[(G + 1) / 2], acc[G][8], zacc[G];  // zacc: sum of p * zero point (QV)
+};
+
 template <int G, bool QV>
-__global__ __launch_bounds__(256, (G <= 4 && !QV) ? 4 : 2) void attn_kernel(
+__device__ __forceinline__ void process_chunk(Acc<G>& st, const Chunk<G>& x, bool sink, bool live,
+                                              const float (*lutq)[kLut], const float* qmu,
+                                              float sm_log2, float (*pbw)[G], int lane) {
+  constexpr int GH = (G + 1) / 2;
+  const int el = lane & 31, half = lane >> 5, grp = lane >> 4;
+  // logits (log2 domain) of this lane's heads g = 2i + half
+  float lg[GH];
+#pragma unroll
+  for (int i = 0; i < GH; ++i) {
+    const int g = min(2 * i + half, G - 1);
+    const float dot = sink ? x.sl[i] : fmaf(x.a, lut_dot(lutq[g], x.code), qmu[i]);
+    lg[i] = (live && 2 * i + half < G) ? dot * sm_log2 : -INFINITY;
+  }
+  // chunk max per head: heads of parity `half` live in this half of the wave
+  float cm[GH], co[GH];
+#pragma unroll
+  for (int i = 0; i < GH; ++i) {
+    float v = lg[i];
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    cm[i] = v;
+    co[i] = __shfl_xor(v, 32);
+  }
+  float sc[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float mx = ((g & 1) == half) ? cm[g >> 1] : co[g >> 1];
+    const float mn = fmaxf(st.m[g], mx);
+    sc[g] = exp2f(st.m[g] - mn);
+    st.m[g] = mn;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.acc[g][i] *= sc[g];
+    if (QV) st.zacc[g] *= sc[g];
+  }
+#pragma unroll
+  for (int i = 0; i < GH; ++i) {
+    const int g1 = min(2 * i + 1, G - 1);
+    const float m_odd = st.m[g1], m_even = st.m[2 * i];  // values, not addresses, are selected
+    const float s_odd = sc[g1], s_even = sc[2 * i];
+    const float mg = half ? m_odd : m_even;
+    const float sg = half ? s_odd : s_even;
+    const float p = exp2f(lg[i] - mg);
+    st.lsum[i] = fmaf(st.lsum[i], sg, p);
+    if (2 * i + half < G) pbw[el][2 * i + half] = p;
+  }
+  wave_sync_lds();
+  // P.V
+  if (!QV || sink) {
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {
+      const int eu = grp + 4 * u;
+      const uint4 w = x.v[u];
+      const float v[8] = {bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y),
+                          bf16lo(w.z), bf16hi(w.z), bf16lo(w.w), bf16hi(w.w)};
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float p = pbw[eu][g];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) st.acc[g][i] = fmaf(p, v[i], st.acc[g][i]);
+      }
+    }
+  } else {
+    // v = z + q * s: acc += (p * s) * q per channel, p * z once per row
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {
+      const int eu = grp + 4 * u;
+      const uint32_t qb = x.v[u].x, sz = x.v[u].y;
+      const float sv = __half2float(__ushort_as_half((unsigned short)(sz & 0xffffu)));
+      const float zv = __half2float(__ushort_as_half((unsigned short)(sz >> 16)));
+      float qf[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qf[i] = (float)((qb >> (2 * i)) & 3u);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float p = pbw[eu][g];
+        const float ps = p * sv;
+        st.zacc[g] = fmaf(p, zv, st.zacc[g]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) st.acc[g][i] = fmaf(ps, qf[i], st.acc[g][i]);
+      }
+    }
+  }
+  wave_sync_lds();
+}
+
+template <int G, bool QV>
+__global__ __launch_bounds__(256, 2) void attn_kernel(
     int n_q_heads, int Hkv, const uint8_t* __restrict__ codes, const float* __restrict__ alpha,
     const uint16_t* __restrict__ v, int64_t vsb, int64_t vsh, int64_t vst,
     const uint8_t* __restrict__ vq, const uint32_t* __restrict__ vsz,
@@ -119,143 +211,85 @@ __global__ __launch_bounds__(256, (G <= 4 && !QV) ? 4 : 2) void attn_kernel(
     int cpb, int n_splits, float* __restrict__ part_o, float* __restrict__ part_ml) {
   constexpr int GH = (G + 1) / 2;
   __shared__ float lutq[G][kLut];
+  __shared__ int sidx[kAttnMaxCpb * kAttnChunk];
   __shared__ __align__(16) float pb[4][kAttnChunk][G];
   __shared__ float mo[4][G][kD];
   __shared__ float mml[4][G][2];
 
   const int bh = blockIdx.y, b = bh / Hkv, h = bh - b * Hkv;
   const int s = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int el = lane & 31, half = lane >> 5, seg = lane & 15, grp = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
+  const int el = lane & 31, half = lane >> 5, seg = lane & 15;
   const int L = kSink + top_k;
   const int n_chunks = (L + kAttnChunk - 1) / kAttnChunk;
-  const int c_end = min(n_chunks, (s + 1) * cpb);
+  const int c0 = s * cpb, c_end = min(n_chunks, c0 + cpb);
   const int64_t row0 = (int64_t)bh * capacity;
   const int64_t hq0 = (int64_t)b * n_q_heads + (int64_t)h * G;
   const int32_t* ib = idx + (int64_t)bh * top_k;
-  const uint8_t* crow = codes + row0 * kCodeBytes;
-  const float* arow = alpha + row0;
-  VSource vs;
-  vs.vb = QV ? nullptr : v + (int64_t)b * vsb + (int64_t)h * vsh + seg * 8;
-  vs.vst = vst;
-  vs.vq = QV ? vq + row0 * kVCodeBytes : nullptr;
-  vs.vsz = QV ? vsz + row0 * 4 : nullptr;
-  vs.vsk = QV ? vsink + (int64_t)bh * kSink * kD + seg * 8 : nullptr;
-  const float* slog = att_slog + hq0 * kSink;
+  Src src;
+  src.codes = codes + row0 * kCodeBytes;
+  src.alpha = alpha + row0;
+  src.slog = att_slog + hq0 * kSink;
+  src.vb = QV ? nullptr : v + (int64_t)b * vsb + (int64_t)h * vsh + seg * 8;
+  src.vst = vst;
+  src.vq = QV ? vq + row0 * kVCodeBytes : nullptr;
+  src.vsz = QV ? vsz + row0 * 4 : nullptr;
+  src.vsk = QV ? vsink + (int64_t)bh * kSink * kD + seg * 8 : nullptr;
 
-  int c = s * cpb + wave;
-  ChunkRegs<G> nx;
-  if (c < c_end) load_chunk<G>(nx, c, L, lane, ib, crow, arow, n_tokens, slog);
-
+  // The block's positions (clamped into [0, n_tokens): memory safety only) and
+  // the G attention tables into LDS.
   {
-    const float4* src = reinterpret_cast<const float4*>(att_lut + hq0 * kLut);
+    const int e0 = c0 * kAttnChunk, ne = (c_end - c0) * kAttnChunk;
+    for (int i = tid; i < ne; i += 256) {
+      const int e = min(e0 + i, L - 1);
+      sidx[i] = e < kSink ? e : min(max(ib[e - kSink], 0), n_tokens - 1);
+    }
+    const float4* lsrc = reinterpret_cast<const float4*>(att_lut + hq0 * kLut);
     float4* dst = reinterpret_cast<float4*>(&lutq[0][0]);
-    for (int i = tid; i < G * kLut / 4; i += 256) dst[i] = src[i];
+    for (int i = tid; i < G * kLut / 4; i += 256) dst[i] = lsrc[i];
   }
   float qmu[GH];
 #pragma unroll
   for (int i = 0; i < GH; ++i) qmu[i] = (2 * i + half < G) ? att_qmu[hq0 + 2 * i + half] : 0.0f;
   __syncthreads();
 
-  float m[G], lsum[GH], acc[G][8], zacc[G];  // zacc: sum of p * zero point (QV)
+  Acc<G> st;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    m[g] = -INFINITY;
-    zacc[g] = 0.0f;
+    st.m[g] = -INFINITY;
+    st.zacc[g] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[g][i] = 0.0f;
+    for (int i = 0; i < 8; ++i) st.acc[g][i] = 0.0f;
   }
 #pragma unroll
-  for (int i = 0; i < GH; ++i) lsum[i] = 0.0f;
+  for (int i = 0; i < GH; ++i) st.lsum[i] = 0.0f;
 
-  for (; c < c_end; c += 4) {
-    const ChunkRegs<G> cur = nx;
-    if (c + 4 < c_end) load_chunk<G>(nx, c + 4, L, lane, ib, crow, arow, n_tokens, slog);
-    const bool live = c * kAttnChunk + el < L;
-    // logits (log2 domain) of this lane's heads g = 2i + half
-    float lg[GH];
-#pragma unroll
-    for (int i = 0; i < GH; ++i) {
-      const int g = min(2 * i + half, G - 1);
-      float dot;
-      if (c * kAttnChunk < kSink) {
-        dot = cur.sl[i];
-      } else {
-        dot = fmaf(cur.a, lut_dot(lutq[g], cur.code), qmu[i]);
-      }
-      lg[i] = (live && 2 * i + half < G) ? dot * sm_log2 : -INFINITY;
+  // Wave w takes the block's chunks w, w+4, ...  A sink chunk (only the first
+  // chunk of waves 0 and 1 of split 0) is done on its own; then every chunk's
+  // loads are issued one chunk ahead, right after the previous chunk's have
+  // been consumed, so the only loads a chunk waits for were issued a whole
+  // chunk earlier (the last chunk is peeled: no branch around the prefetch).
+  int c = c0 + wave;
+  if (c < c_end && c * kAttnChunk < kSink) {
+    Chunk<G> sk;
+    load_chunk<G, QV>(sk, c - c0, true, sidx, lane, src);
+    process_chunk<G, QV>(st, sk, true, true, lutq, qmu, sm_log2, pb[wave], lane);
+    c += 4;
+  }
+  if (c < c_end) {
+    const int c_last = c + ((c_end - 1 - c) & ~3);
+    Chunk<G> nx;
+    load_chunk<G, QV>(nx, c - c0, false, sidx, lane, src);
+    for (; c < c_last; c += 4) {
+      const Chunk<G> cur = nx;
+      load_chunk<G, QV>(nx, c + 4 - c0, false, sidx, lane, src);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the chunk's work
+      process_chunk<G, QV>(st, cur, false, c * kAttnChunk + el < L, lutq, qmu, sm_log2, pb[wave],
+                           lane);
     }
-    const bool sink_chunk = c * kAttnChunk < kSink;
-    uint4 vr[kRows];
-    load_rows<QV>(vr, lane, cur.t, sink_chunk, vs);
-    // chunk max per head: heads of parity `half` live in this half of the wave
-    float cm[GH], co[GH];
-#pragma unroll
-    for (int i = 0; i < GH; ++i) {
-      float x = lg[i];
-#pragma unroll
-      for (int o = 16; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-      cm[i] = x;
-      co[i] = __shfl_xor(x, 32);
-    }
-    float sc[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float mx = ((g & 1) == half) ? cm[g >> 1] : co[g >> 1];
-      const float mn = fmaxf(m[g], mx);
-      sc[g] = exp2f(m[g] - mn);
-      m[g] = mn;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[g][i] *= sc[g];
-      if (QV) zacc[g] *= sc[g];
-    }
-#pragma unroll
-    for (int i = 0; i < GH; ++i) {
-      const int g1 = min(2 * i + 1, G - 1);
-      const float mg = half ? m[g1] : m[2 * i];
-      const float sg = half ? sc[g1] : sc[2 * i];
-      const float p = exp2f(lg[i] - mg);
-      lsum[i] = fmaf(lsum[i], sg, p);
-      if (2 * i + half < G) pb[wave][el][2 * i + half] = p;
-    }
-    wave_sync_lds();
-    // P.V
-    if (!QV || sink_chunk) {
-#pragma unroll
-      for (int u = 0; u < kRows; ++u) {
-        const int eu = grp + 4 * u;
-        const uint4 w = vr[u];
-        const float x[8] = {bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y),
-                            bf16lo(w.z), bf16hi(w.z), bf16lo(w.w), bf16hi(w.w)};
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float p = pb[wave][eu][g];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc[g][i] = fmaf(p, x[i], acc[g][i]);
-        }
-      }
-    } else {
-      // v = z + q * s: acc += (p * s) * q per channel, p * z once per row
-#pragma unroll
-      for (int u = 0; u < kRows; ++u) {
-        const int eu = grp + 4 * u;
-        const uint32_t qb = vr[u].x, sz = vr[u].y;
-        const float sv = __half2float(__ushort_as_half((unsigned short)(sz & 0xffffu)));
-        const float zv = __half2float(__ushort_as_half((unsigned short)(sz >> 16)));
-        float qf[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qf[i] = (float)((qb >> (2 * i)) & 3u);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float p = pb[wave][eu][g];
-          const float ps = p * sv;
-          zacc[g] = fmaf(p, zv, zacc[g]);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc[g][i] = fmaf(ps, qf[i], acc[g][i]);
-        }
-      }
-    }
-    wave_sync_lds();
+    process_chunk<G, QV>(st, nx, false, c * kAttnChunk + el < L, lutq, qmu, sm_log2, pb[wave],
+                         lane);
   }
 
   // Wave partial: sums over the four 16-lane groups and over the 32 lanes.
@@ -263,31 +297,32 @@ __global__ __launch_bounds__(256, (G <= 4 && !QV) ? 4 : 2) void attn_kernel(
   for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float x = QV ? acc[g][i] + zacc[g] : acc[g][i];
+      float x = QV ? st.acc[g][i] + st.zacc[g] : st.acc[g][i];
       x += __shfl_xor(x, 16);
       x += __shfl_xor(x, 32);
-      acc[g][i] = x;
+      st.acc[g][i] = x;
     }
 #pragma unroll
   for (int i = 0; i < GH; ++i) {
-    float x = lsum[i];
+    float x = st.lsum[i];
 #pragma unroll
     for (int o = 16; o > 0; o >>= 1) x += __shfl_xor(x, o);
-    lsum[i] = x;
+    st.lsum[i] = x;
   }
   if (lane < 16) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) mo[wave][g][seg * 8 + i] = acc[g][i];
+      for (int i = 0; i < 8; ++i) mo[wave][g][seg * 8 + i] = st.acc[g][i];
   }
   if (el == 0) {
 #pragma unroll
     for (int i = 0; i < GH; ++i) {
       const int g = 2 * i + half;
       if (g < G) {
-        mml[wave][g][0] = half ? m[min(2 * i + 1, G - 1)] : m[2 * i];
-        mml[wave][g][1] = lsum[i];
+        const float m_odd = st.m[min(2 * i + 1, G - 1)], m_even = st.m[2 * i];
+        mml[wave][g][0] = half ? m_odd : m_even;
+        mml[wave][g][1] = st.lsum[i];
       }
     }
   }
@@ -387,7 +422,8 @@ hipError_t launch_attn(int n_q_heads, int B, int Hkv, const uint8_t* codes, cons
                        int chunks_per_block, int n_splits, float* part_o, float* part_ml,
                        hipStream_t s) {
   const int n_chunks = (kSink + top_k + kAttnChunk - 1) / kAttnChunk;
-  if (chunks_per_block < 1 || (int64_t)n_splits * chunks_per_block < n_chunks ||
+  if (chunks_per_block < 1 || chunks_per_block > kAttnMaxCpb ||
+      (int64_t)n_splits * chunks_per_block < n_chunks ||
       (int64_t)(n_splits - 1) * chunks_per_block >= n_chunks)
     return hipErrorInvalidValue;
   const float sm_log2 = sm_scale * 1.4426950408889634f;

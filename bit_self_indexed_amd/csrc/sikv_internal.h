@@ -282,6 +282,7 @@ hipError_t launch_select(int B, int Hkv, const uint8_t* codes, const float* alph
 // chunks_per_block consecutive chunks of one (b, KV head) and writes one
 // (max, sum, o) partial per query head.
 constexpr int kAttnChunk = 32;
+constexpr int kAttnMaxCpb = 64;  // chunks per block at most (the block's positions sit in LDS)
 // vq (may be null): quantised values (vq, vsz: launch_vcodes; vsink [B*Hkv][64][128]
 // bf16) replace the bf16 V rows.
 hipError_t launch_attn(int n_q_heads, int B, int Hkv, const uint8_t* codes, const float* alpha,
