@@ -30,7 +30,10 @@ consistency by perturbation, brute-force channel loop for its scores, dense
 SDPA with its reconstructed keys, lower reconstruction error than the
 vertices), quantised values (hand-derived layout and codes, exact levels, constant
 groups, error bound against the scale, all-tokens attention against SDPA over the
-reconstructed values).  No function is left unpinned.
+reconstructed values), K-means baseline (one iteration equals the one-pass codebook,
+scikit-learn's Lloyd K-means on separated clusters, non-increasing objective), dense
+retrieval scores (equal to the LUT scores plus q.mu on keys that are exactly their
+own reconstruction).  No function is left unpinned.
 """
 
 from __future__ import annotations
@@ -208,6 +211,71 @@ def codebook(k_bits, mu, codes, alpha, n_tokens: int) -> np.ndarray:
     mean = (sums.astype(np.float64) * 2.0 ** -CB_FRAC_BITS) / np.maximum(cnt, 1)[..., None]
     out = np.where(cnt[..., None] > 0, mean, centres()[None, :, :])
     return out.astype(np.float32)
+
+
+def normalised_subvectors(k_bits, mu, alpha, n_tokens: int) -> np.ndarray:
+    """The points the clustering works on: x = fl32(fl32(k_c - mu_c) / alpha_t) for the
+    prefill non-sink tokens t in [64, N) (0 where alpha_t = 0), grouped into the 32
+    4-dim sub-vectors.  Returns float32 [N - 64, 32, 4]."""
+    rows = slice(N_SINK, n_tokens)
+    kt = (bf16_to_f32(np.asarray(k_bits)[rows]) - np.asarray(mu, np.float32)).astype(np.float32)
+    a = np.asarray(alpha, np.float32)[rows][:, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        x = np.where(a > 0, kt / np.where(a > 0, a, np.float32(1)), np.float32(0)).astype(np.float32)
+    return x.reshape(-1, N_SUB, SUB_DIM)
+
+
+def kmeans_codebook(k_bits, mu, alpha, n_tokens: int, n_iter: int = 20) -> np.ndarray:
+    """The iterative clustering the one-pass sign clustering replaces (§2.1 item 1)
+    and is timed against (§4, module speed-ups: K-means with 20 iterations).
+
+    READING (the pages name only "K-means, 20 iterations"): Lloyd iterations on the
+    same points as ``codebook`` (``normalised_subvectors``), 16 clusters per
+    sub-vector position j, started from the 16 sign vertices.  Each iteration assigns
+    every point to its nearest centre, the squared Euclidean distance taken in fp32 in
+    a fixed order, ((d0^2 + d1^2) + d2^2) + d3^2 with d_i = fl32(x_i - c_i) (each
+    product and sum rounded to fp32), the lowest index winning ties; then a centre is
+    the mean of its points, with the fixed-point sums and fp64 division of
+    ``codebook``; an empty cluster keeps its previous centre.  Starting from the
+    vertices, the nearest vertex of a point is its sign pattern, so one iteration
+    gives exactly ``codebook``.
+
+    k_bits [>=N, 128] bf16 bits; mu [128]; alpha [>=N].  Returns float32 [32, 16, 4]."""
+    x = normalised_subvectors(k_bits, mu, alpha, n_tokens)               # [T, 32, 4]
+    fx = np.rint(x.astype(np.float64) * 2.0 ** CB_FRAC_BITS)             # exact integers
+    c = np.broadcast_to(centres().astype(np.float32), (N_SUB, N_PATTERNS, SUB_DIM)).copy()
+    for _ in range(n_iter):
+        d = (x[:, :, None, :] - c[None, :, :, :]).astype(np.float32)     # [T, 32, 16, 4]
+        sq = (d * d).astype(np.float32)
+        dist = (((sq[..., 0] + sq[..., 1]).astype(np.float32) + sq[..., 2]).astype(np.float32)
+                + sq[..., 3]).astype(np.float32)                         # [T, 32, 16]
+        lab = np.argmin(dist, axis=-1)                                   # first minimum
+        new = c.copy()
+        for j in range(N_SUB):
+            cnt = np.bincount(lab[:, j], minlength=N_PATTERNS)
+            for i in range(SUB_DIM):
+                sm = np.bincount(lab[:, j], weights=fx[:, j, i], minlength=N_PATTERNS)
+                mean = (sm * 2.0 ** -CB_FRAC_BITS) / np.maximum(cnt, 1)
+                new[j, :, i] = np.where(cnt > 0, mean, c[j, :, i]).astype(np.float32)
+        c = new
+    return c
+
+
+def kmeans_objective(k_bits, mu, alpha, n_tokens: int, cb) -> float:
+    """Sum over points of the squared distance to the nearest centre (fp64)."""
+    x = normalised_subvectors(k_bits, mu, alpha, n_tokens).astype(np.float64)
+    d = ((x[:, :, None, :] - np.asarray(cb, np.float64)[None]) ** 2).sum(-1)
+    return float(d.min(axis=-1).sum())
+
+
+def dense_scores(q_bits, k_bits, n_kv_heads: int, n_tokens: int) -> np.ndarray:
+    """Full dot-product retrieval, the comparator of the LUT-GEMV score (§4, module
+    speed-ups: retrieval against the full dot product): the selection query of each
+    KV head (``group_query``) dotted with every cached bf16 key, t < N, in fp64.
+    q_bits [B,Hq,128]; k_bits [B,Hkv,>=N,128] -> fp64 [B,Hkv,N]."""
+    qbar = group_query(q_bits, n_kv_heads)                               # [B, Hkv, 128]
+    k = bf16_to_f32(np.asarray(k_bits)[..., :n_tokens, :]).astype(np.float64)
+    return np.einsum("bhc,bhtc->bht", qbar, k)
 
 
 # --------------------------------------------------------------------------- #

@@ -522,3 +522,105 @@ def test_quantised_value_attention_equals_dense_sdpa():
         qq[:, None, :], torch.tensor(kap)[None].expand(G, -1, -1),
         torch.tensor(vals)[None].expand(G, -1, -1), scale=sm)[:, 0]
     assert np.allclose(res["out"][0], ref.numpy(), rtol=1e-6, atol=1e-7)
+
+
+# ----------------------------------------------------------------- K-means baseline
+def _head_case(seed, n):
+    w = S.custom("km", 1, 4, 1, n, 100, n_planted=4, cfg_id=seed)
+    K = S.draw(w)["K"][0, 0]
+    e = O.encode(K[None, None], n)
+    return K, e["mu"][0, 0], e["codes"][0, 0], e["alpha"][0, 0]
+
+
+@pytest.mark.parametrize("seed,n", [(160, 3000), (161, 5003)])
+def test_kmeans_one_iteration_is_the_codebook(seed, n):
+    """From the sign vertices, a point's nearest vertex is its sign pattern, so the
+    first Lloyd step is exactly the one-pass sign clustering (empty clusters keep
+    the vertex in both)."""
+    K, mu, codes, alpha = _head_case(seed, n)
+    cb = O.codebook(K, mu, codes, alpha, n)
+    km = O.kmeans_codebook(K, mu, alpha, n, 1)
+    assert np.array_equal(cb.view(np.uint32), km.view(np.uint32))
+
+
+def test_kmeans_objective_never_increases():
+    K, mu, _, alpha = _head_case(162, 4000)
+    objs = [O.kmeans_objective(K, mu, alpha, 4000, O.kmeans_codebook(K, mu, alpha, 4000, it))
+            for it in (1, 2, 3, 5, 8, 20)]
+    assert all(b <= a * (1 + 1e-9) for a, b in zip(objs, objs[1:])), objs
+    assert objs[-1] < 0.9 * objs[0]                     # the iterations do move the centres
+
+
+def test_kmeans_matches_scikit_learn_lloyd():
+    """scikit-learn's Lloyd K-means from the same 16 vertices, on points whose
+    clusters straddle the orthant borders (so the assignment changes after the
+    first step) and are exactly representable (mu = 0, alpha = 1: x = k)."""
+    from sklearn.cluster import KMeans
+    rng = np.random.default_rng(163)
+    v = O.centres()
+    n_per, n = 40, 64 + 16 * 40
+    rows = np.zeros((n, 128), np.float32)
+    for j in range(32):
+        true = v * rng.uniform(0.3, 1.6, (16, 4))
+        pts = np.repeat(true, n_per, axis=0) + rng.normal(0, 0.45, (16 * n_per, 4))
+        rows[64:, 4 * j:4 * j + 4] = pts[rng.permutation(16 * n_per)]
+    kb = _bf16(rows)
+    x = S.bf16_bits_to_f32(kb).astype(np.float64)
+    mu, alpha = np.zeros(128, np.float32), np.ones(n, np.float32)
+    ours = O.kmeans_codebook(kb, mu, alpha, n, 20)
+    moved = 0
+    for j in range(32):
+        pts = x[64:, 4 * j:4 * j + 4]
+        km = KMeans(n_clusters=16, init=v.copy(), n_init=1, max_iter=20, tol=0.0,
+                    algorithm="lloyd").fit(pts)
+        assert np.bincount(km.labels_, minlength=16).min() > 0
+        np.testing.assert_allclose(ours[j], km.cluster_centers_, rtol=0, atol=1e-5)
+        sign_pattern = ((pts < 0) * (1 << np.arange(4))).sum(axis=1)
+        moved += int(np.any(km.labels_ != sign_pattern))
+    assert moved > 0                                     # the assignment did change
+
+
+# ----------------------------------------------------------------- dense retrieval scores
+def test_dense_scores_closed_form():
+    """Keys that are scaled unit vectors: score = s_t * qbar[c_t], with qbar the sum
+    of the group's query rows (small integers: every value exact)."""
+    rng = np.random.default_rng(164)
+    B, Hkv, G, N = 2, 3, 2, 70
+    q = rng.integers(-4, 5, (B, Hkv * G, 128)).astype(np.float32)
+    K = np.zeros((B, Hkv, N, 128), np.float32)
+    c = rng.integers(0, 128, (B, Hkv, N))
+    sc = rng.integers(-3, 4, (B, Hkv, N)).astype(np.float32)
+    for b in range(B):
+        for h in range(Hkv):
+            for t in range(N):
+                K[b, h, t, c[b, h, t]] = sc[b, h, t]
+    got = O.dense_scores(_bf16(q), _bf16(K), Hkv, N)
+    for b in range(B):
+        for h in range(Hkv):
+            qbar = q[b, h * G] + q[b, h * G + 1]
+            for t in range(N):
+                assert got[b, h, t] == sc[b, h, t] * qbar[c[b, h, t]]
+
+
+def test_dense_scores_equal_lut_scores_on_exact_reconstructions():
+    """Keys k = alpha * v with v a sign vector, in +/- pairs so that the channel
+    mean is exactly 0 and every token's scale is alpha: the key is its own
+    reconstruction, so the full dot product equals the LUT-GEMV score."""
+    rng = np.random.default_rng(165)
+    n_pairs = 200
+    signs = rng.choice([-1.0, 1.0], (n_pairs, 128))
+    scale = 2.0 ** rng.integers(-3, 3, n_pairs)
+    half = signs * scale[:, None]
+    rows = np.empty((64 + 2 * n_pairs, 128), np.float32)
+    rows[:64] = rng.standard_normal((64, 128))
+    rows[64::2] = half
+    rows[65::2] = -half
+    n = rows.shape[0]
+    kb = _bf16(rows)
+    e = O.encode(kb[None, None], n)
+    assert not np.any(e["mu"])
+    q = _bf16(rng.standard_normal((1, 3, 128)))
+    lut = O.query_lut(O.group_query(q, 1)[0, 0])
+    s_lut = O.lut_scores(lut, e["codes"][0, 0, 64:], e["alpha"][0, 0, 64:])
+    s_dense = O.dense_scores(q, kb[None, None], 1, n)[0, 0, 64:]
+    np.testing.assert_allclose(s_dense, s_lut, rtol=1e-15, atol=1e-12)
