@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-dense", action="store_true", help="skip the dense bf16 comparator")
     p.add_argument("--no-qv", action="store_true", help="skip the 2-bit value variant")
+    p.add_argument("--no-baselines", action="store_true",
+                   help="skip the K-means and dense-retrieval comparators")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--summarize-trace", nargs=2, metavar=("RUN_DIR", "OUT_TXT"),
                    help="write a text summary of a rocprofv3 --kernel-trace --stats run and exit")
@@ -390,6 +392,41 @@ def main():
                     if name in ("mu_partial", "mu_final", "codes", "cb_final") and n)
     del enc_c
 
+    # The pages' module speed-ups (technical summary §4): one-pass sign clustering
+    # against K-means with 20 iterations (both over this prefill), and the LUT-GEMV
+    # retrieval pass against a full bf16 dot-product scan writing every score.
+    km20_us = km_assign_us = dense_scores_us = None
+    if not args.no_baselines:
+        km_c = sk.Cache(w.batch, w.n_kv_heads, N, device=dev, v=None, codebook=True)
+        sk.sikv_encode(km_c, K)
+        sk.sikv_kmeans_codebook(km_c, K, 1)
+        torch.cuda.synchronize()
+        sk.timing_reset()
+        sk.timing_enable(True)
+        sk.sikv_kmeans_codebook(km_c, K, 20)
+        torch.cuda.synchronize()
+        kt2 = sk.timing_read()
+        sk.timing_enable(False)
+        km20_us = sum(1e3 * tot for name, (n, tot) in kt2.items()
+                      if name in ("kmeans_assign", "cb_final") and n)
+        km_assign_us = 1e3 * kt2["kmeans_assign"][1] / kt2["kmeans_assign"][0]
+        del km_c
+        dscores = torch.empty((w.batch, w.n_kv_heads, N), dtype=torch.float32, device=dev)
+        sk.sikv_dense_scores(q_all, K, scores=dscores)
+        torch.cuda.synchronize()
+        sk.timing_reset()
+        sk.timing_enable(True)
+        for _ in range(10):
+            sk.sikv_dense_scores(q_all, K, scores=dscores)
+        torch.cuda.synchronize()
+        kt3 = sk.timing_read()
+        sk.timing_enable(False)
+        dense_scores_us = 1e3 * kt3["dense_scores"][1] / kt3["dense_scores"][0]
+        del dscores
+        log(f"K-means 20 iterations {km20_us:.1f} us (assign {km_assign_us:.1f} us each); "
+            f"one-pass clustering adds {enc_cb_us - enc_us:.1f} us to the prefill encode; "
+            f"dense q.K scan {dense_scores_us:.1f} us")
+
     # the same step with 2-bit values (per-token groups of 32 channels, bf16 sinks):
     # the appended value row is quantised inside the step
     qv_us = qv_kern_us = None
@@ -522,6 +559,27 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if km20_us is not None:
+        score_us = kern_us.get("score", 0.0)
+        report["module_speedups"] = {
+            "clustering": {
+                "one_pass_us": enc_cb_us - enc_us,
+                "kmeans20_us": km20_us,
+                "kmeans_assign_us": km_assign_us,
+                "ratio": km20_us / max(enc_cb_us - enc_us, 1e-9),
+                "note": "one-pass = the encode's extra cost for the cluster statistics and "
+                        "centres; K-means = 20 Lloyd iterations over the same prefill keys",
+            },
+            "retrieval": {
+                "lut_score_us": score_us,
+                "lut_prep_score_select_us": sum(kern_us.get(n, 0.0)
+                                                for n in ("prep", "score", "select")),
+                "dense_scan_us": dense_scores_us,
+                "ratio_score_kernel": dense_scores_us / max(score_us, 1e-9),
+                "ratio_with_prep_and_topk": dense_scores_us / max(
+                    sum(kern_us.get(n, 0.0) for n in ("prep", "score", "select")), 1e-9),
+            },
+        }
     if qv_us is not None:
         a_qv = algorithmic_bytes(w, "attn_qv")
         report["quantised_values"] = {

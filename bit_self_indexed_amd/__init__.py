@@ -24,7 +24,7 @@ HEAD_DIM = 128
 N_SINK = 64
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsikv.so")
 
-OP_ENCODE, OP_SCORE_TOPK, OP_SPARSE_ATTN, OP_DECODE_STEP = 0, 1, 2, 3
+OP_ENCODE, OP_SCORE_TOPK, OP_SPARSE_ATTN, OP_DECODE_STEP, OP_KMEANS = 0, 1, 2, 3, 4
 
 
 class SikvError(RuntimeError):
@@ -296,6 +296,38 @@ def sikv_dense_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                vb.data_ptr(), vsb, vsh, vst, ctypes.c_float(sm), out.data_ptr(),
                                w, wn, _stream(q.device)), "sikv_dense_attn")
     return out
+
+
+def sikv_kmeans_codebook(cache: Cache, k: torch.Tensor, n_iter: int = 20) -> None:
+    """K-means baseline of the sign clustering: n_iter Lloyd iterations from the sign
+    vertices over the prefill keys k ([B, Hkv, n_tokens, 128], the ones sikv_encode
+    compressed), written to cache.codebook (one iteration = the one-pass codebook)."""
+    if cache.codebook is None:
+        raise ValueError("the cache has no codebook")
+    kb = _bits(k)
+    sb, sh, st = _strides_rows(kb, "k")
+    d = cache.desc()
+    need = int(lib.sikv_workspace_bytes(OP_KMEANS, ctypes.byref(d), 1, 1))
+    ws, wsn = cache.ws.get(need)
+    _check(lib.sikv_kmeans_codebook(ctypes.byref(d), kb.data_ptr(), sb, sh, st, int(n_iter), ws,
+                                    wsn, _stream(cache.device)), "sikv_kmeans_codebook")
+
+
+def sikv_dense_scores(q: torch.Tensor, k: torch.Tensor, n_tokens: int | None = None,
+                      scores: torch.Tensor | None = None) -> torch.Tensor:
+    """Full dot-product retrieval scores (the comparator of the LUT-GEMV score):
+    fp32 [B, Hkv, n_tokens], selection query (sum of each KV head's query group)
+    dotted with every bf16 key."""
+    qb, kb = _bits(q).contiguous(), _bits(k)
+    B, n_q = qb.shape[0], qb.shape[1]
+    Hkv = kb.shape[1]
+    N = kb.shape[2] if n_tokens is None else int(n_tokens)
+    ksb, ksh, kst = _strides_rows(kb, "k")
+    if scores is None:
+        scores = torch.empty((B, Hkv, N), dtype=torch.float32, device=q.device)
+    _check(lib.sikv_dense_scores(B, Hkv, n_q, N, qb.data_ptr(), kb.data_ptr(), ksb, ksh, kst,
+                                 scores.data_ptr(), _stream(q.device)), "sikv_dense_scores")
+    return scores
 
 
 def sikv_stream_copy(dst: torch.Tensor, src: torch.Tensor) -> None:

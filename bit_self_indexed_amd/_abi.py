@@ -4,7 +4,7 @@ from __future__ import annotations
 
 import ctypes as C
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 STATUS = {
     0: "SIKV_OK",
@@ -60,6 +60,8 @@ SIGNATURES = {
     "sikv_dense_attn": (_I32, [_I32, _I32, _I32, _I32, _P, _P, _I64, _I64, _I64, _P, _I64, _I64,
                                _I64, C.c_float, _P, _P, _SZ, _P]),
     "sikv_dense_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "sikv_kmeans_codebook": (_I32, [_DESC, _P, _I64, _I64, _I64, _I32, _P, _SZ, _P]),
+    "sikv_dense_scores": (_I32, [_I32, _I32, _I32, _I32, _P, _P, _I64, _I64, _I64, _P, _P]),
     "sikv_stream_copy": (_I32, [_P, _P, _SZ, _P]),
     "sikv_timing_enable": (_I32, [_I32]),
     "sikv_timing_reset": (_I32, []),

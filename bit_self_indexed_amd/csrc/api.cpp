@@ -257,7 +257,8 @@ double g_ms[KID_COUNT];
 int64_t g_cnt[KID_COUNT];
 const char* const g_names[KID_COUNT] = {"mu_partial", "mu_final", "codes", "prep",
                                         "score",      "select",   "attn",  "combine",
-                                        "dense",      "copy",     "cb_final", "vcodes"};
+                                        "dense",      "copy",     "cb_final", "vcodes",
+                                        "kmeans_assign", "dense_scores"};
 
 hipEvent_t take_event() {
   if (!g_pool.empty()) {
@@ -472,6 +473,10 @@ size_t sikv_workspace_bytes(int32_t op, const sikv_cache_desc* c, int32_t n_q_he
       DecodePlan dp;
       return plan_decode(c, n_q_heads, top_k, &dp) ? dp.bytes : 0;
     }
+    case SIKV_OP_KMEANS:
+      if (c->codebook == nullptr) return 0;
+      return align_up((size_t)c->batch * c->n_kv_heads * cb_blocks(c->n_tokens) * kCbStride *
+                      sizeof(long long));
     default:
       return 0;
   }
@@ -508,6 +513,44 @@ size_t sikv_dense_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t n_q
   const int64_t n_splits = cdiv(n_tokens, split);
   const size_t rows = (size_t)batch * n_q_heads * n_splits;
   return align_up(rows * kD * sizeof(float)) + align_up(rows * 2 * sizeof(float));
+}
+
+sikv_status sikv_kmeans_codebook(const sikv_cache_desc* c, const uint16_t* k, int64_t k_stride_b,
+                                 int64_t k_stride_h, int64_t k_stride_t, int32_t n_iter, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  sikv_status st = check_desc(c);
+  if (st != SIKV_OK) return st;
+  if (c->codebook == nullptr || k == nullptr || misaligned(k, 16) ||
+      bad_strides(k_stride_b, k_stride_h, k_stride_t) || n_iter < 1 || n_iter > 1000)
+    return SIKV_ERR_INVALID_ARG;
+  st = check_ws(ws, ws_bytes, sikv_workspace_bytes(SIKV_OP_KMEANS, c, 1, 1));
+  if (st != SIKV_OK) return st;
+  long long* part = static_cast<long long*>(ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int BH = c->batch * c->n_kv_heads, nblk = cb_blocks(c->n_tokens);
+  for (int it = 0; it < n_iter; ++it) {
+    SIKV_TRY(launch_kmeans_assign(k, k_stride_b, k_stride_h, k_stride_t, c->batch, c->n_kv_heads,
+                                  c->n_tokens, c->capacity, c->mu, c->alpha,
+                                  it == 0 ? nullptr : c->codebook, part, s));
+    SIKV_TRY(launch_cb_final(part, BH, nblk, c->codebook, s, it == 0 ? 0 : 1));
+  }
+  return SIKV_OK;
+}
+
+sikv_status sikv_dense_scores(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads,
+                              int32_t n_tokens, const uint16_t* q, const uint16_t* k,
+                              int64_t k_stride_b, int64_t k_stride_h, int64_t k_stride_t,
+                              float* scores, void* stream) {
+  if (batch < 1 || n_kv_heads < 1 || n_q_heads < 1 || n_tokens < 1 || n_q_heads % n_kv_heads ||
+      (int64_t)batch * n_kv_heads > 65535)
+    return SIKV_ERR_INVALID_ARG;
+  if (n_q_heads / n_kv_heads > kMaxGroup) return SIKV_ERR_UNSUPPORTED;
+  if (!q || !k || !scores || misaligned(q, 16) || misaligned(k, 16) || misaligned(scores, 4) ||
+      bad_strides(k_stride_b, k_stride_h, k_stride_t))
+    return SIKV_ERR_INVALID_ARG;
+  SIKV_TRY(launch_dense_scores(q, n_q_heads, batch, n_kv_heads, n_tokens, k, k_stride_b,
+                               k_stride_h, k_stride_t, scores, static_cast<hipStream_t>(stream)));
+  return SIKV_OK;
 }
 
 sikv_status sikv_dense_attn(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads, int32_t n_tokens,

@@ -177,7 +177,64 @@ __global__ __launch_bounds__(256) void dense_kernel(
   }
 }
 
+// Full dot-product retrieval (the comparator of the LUT-GEMV score): one block
+// per (256 tokens, b*h); 16 lanes x 16 bytes per bf16 key row, all 16 rows of
+// a thread issued before any is used, partial dots reduced over the 16 lanes.
+// The selection query qbar = sum of the G query rows (fp32, g ascending), each
+// lane holding its 8 channels.
+constexpr int kScoreRows = 16;  // rows per 16-lane group per block
+__global__ __launch_bounds__(256) void dense_scores_kernel(
+    const uint16_t* __restrict__ q, int n_q_heads, int Hkv, int G, int n_tokens,
+    const uint16_t* __restrict__ k, int64_t ksb, int64_t ksh, int64_t kst,
+    float* __restrict__ scores) {
+  const int bh = blockIdx.y, b = bh / Hkv, h = bh - b * Hkv;
+  const int tid = threadIdx.x, rg = tid >> 4, cg = tid & 15;
+  float qs[8];
+  {
+    const uint16_t* qb = q + ((int64_t)b * n_q_heads + (int64_t)h * G) * kD + cg * 8;
+    const uint4 w0 = *reinterpret_cast<const uint4*>(qb);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qs[i] = chan(w0, i);
+    for (int g = 1; g < G; ++g) {
+      const uint4 w = *reinterpret_cast<const uint4*>(qb + (int64_t)g * kD);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qs[i] += chan(w, i);
+    }
+  }
+  const int t0 = blockIdx.x * 16 * kScoreRows;
+  const uint16_t* kb = k + (int64_t)b * ksb + (int64_t)h * ksh + cg * 8;
+  uint4 w[kScoreRows];
+#pragma unroll
+  for (int u = 0; u < kScoreRows; ++u) {
+    const int t = t0 + u * 16 + rg;
+    w[u] = t < n_tokens ? *reinterpret_cast<const uint4*>(kb + (int64_t)t * kst)
+                        : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int u = 0; u < kScoreRows; ++u) {
+    float d = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) d = fmaf(qs[i], chan(w[u], i), d);
+    d += __shfl_xor(d, 8);
+    d += __shfl_xor(d, 4);
+    d += __shfl_xor(d, 2);
+    d += __shfl_xor(d, 1);
+    const int t = t0 + u * 16 + rg;
+    if (cg == 0 && t < n_tokens) scores[(int64_t)bh * n_tokens + t] = d;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_dense_scores(const uint16_t* q, int n_q_heads, int B, int Hkv, int n_tokens,
+                               const uint16_t* k, int64_t ksb, int64_t ksh, int64_t kst,
+                               float* scores, hipStream_t s) {
+  const int G = n_q_heads / Hkv;
+  if (G < 1 || G * Hkv != n_q_heads || n_tokens < 1) return hipErrorInvalidValue;
+  const dim3 grid((n_tokens + 16 * kScoreRows - 1) / (16 * kScoreRows), B * Hkv), block(256);
+  return launch_k(KID_DSCORES, dense_scores_kernel, grid, block, 0, s, q, n_q_heads, Hkv, G,
+                  n_tokens, k, ksb, ksh, kst, scores);
+}
 
 hipError_t launch_dense(const uint16_t* q, int n_q_heads, int B, int Hkv, int n_tokens,
                         const uint16_t* k, int64_t ksb, int64_t ksh, int64_t kst,

@@ -227,7 +227,7 @@ __global__ __launch_bounds__(256) void vcodes_kernel(const uint16_t* __restrict_
 // summed in block order (exact integer sums), then centre_i =
 // fl32((sum_i * 2^-24) / count) computed in fp64; empty cluster: sign vertex p.
 __global__ __launch_bounds__(512) void cb_final_kernel(const long long* __restrict__ part, int nblk,
-                                                       float* __restrict__ codebook) {
+                                                       float* __restrict__ codebook, int keep) {
   const int bh = blockIdx.x, jp = threadIdx.x, p = jp & 15;
   long long s[4] = {0, 0, 0, 0}, n = 0;
   for (int bk = 0; bk < nblk; ++bk) {
@@ -236,13 +236,105 @@ __global__ __launch_bounds__(512) void cb_final_kernel(const long long* __restri
     for (int i = 0; i < 4; ++i) s[i] += q[jp * 4 + i];
     n += q[kSub * 16 * 4 + jp];
   }
+  float4* dst = reinterpret_cast<float4*>(codebook) + (int64_t)bh * kSub * 16 + jp;
+  const float4 prev = keep ? *dst : make_float4(0.f, 0.f, 0.f, 0.f);
+  const float* pv = &prev.x;
   float4 c;
   float* cv = &c.x;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     cv[i] = n > 0 ? (float)(((double)s[i] * (1.0 / (double)(1 << kCbFracBits))) / (double)n)
-                  : (((p >> i) & 1) ? -1.0f : 1.0f);
-  reinterpret_cast<float4*>(codebook)[(int64_t)bh * kSub * 16 + jp] = c;
+                  : (keep ? pv[i] : (((p >> i) & 1) ? -1.0f : 1.0f));
+  *dst = c;
+}
+
+// K-means baseline, assignment step: the points and block statistics of
+// codes_kernel<true>, with the cluster of a sub-vector chosen as its nearest
+// centre instead of its sign pattern.  Thread (row group rs, channel group cg)
+// holds sub-vectors 2cg and 2cg+1 of its tokens, so it keeps their 2 x 16
+// centres in registers.
+__global__ __launch_bounds__(256, 2) void kmeans_assign_kernel(
+    const uint16_t* __restrict__ k, int64_t sb, int64_t sh, int64_t st, int Hkv, int n_tokens,
+    int capacity, int tpb, const float* __restrict__ mu, const float* __restrict__ alpha,
+    const float* __restrict__ centres, long long* __restrict__ cb_part) {
+  __shared__ unsigned long long cbs[kSub * 16 * 4];
+  __shared__ int cbn[kSub * 16];
+  const int bh = blockIdx.y, b = bh / Hkv, h = bh - b * Hkv;
+  const int tid = threadIdx.x, cg = tid & 15, rs = tid >> 4;
+  float4 cen[2][16];
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int p = 0; p < 16; ++p)
+      cen[half][p] = centres != nullptr
+                         ? reinterpret_cast<const float4*>(centres)[((int64_t)bh * kSub + 2 * cg +
+                                                                     half) * 16 + p]
+                         : make_float4((p & 1) ? -1.f : 1.f, (p & 2) ? -1.f : 1.f,
+                                       (p & 4) ? -1.f : 1.f, (p & 8) ? -1.f : 1.f);
+  for (int i = tid; i < kSub * 16; i += 256) cbn[i] = 0;
+  for (int i = tid; i < kSub * 16 * 4; i += 256) cbs[i] = 0ull;
+  __syncthreads();
+  float m[8];
+  {
+    const float4 m0 = *reinterpret_cast<const float4*>(mu + (int64_t)bh * kD + cg * 8);
+    const float4 m1 = *reinterpret_cast<const float4*>(mu + (int64_t)bh * kD + cg * 8 + 4);
+    m[0] = m0.x; m[1] = m0.y; m[2] = m0.z; m[3] = m0.w;
+    m[4] = m1.x; m[5] = m1.y; m[6] = m1.z; m[7] = m1.w;
+  }
+  const uint16_t* base = k + (int64_t)b * sb + (int64_t)h * sh + cg * 8;
+  const int n_tiles = (n_tokens + 127) / 128;
+  const int tile_end = min(n_tiles, (int)(blockIdx.x + 1) * tpb);
+  for (int tile = blockIdx.x * tpb; tile < tile_end; ++tile) {
+    const int tb = tile * 128;
+    uint4 w[8];
+    float a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = tb + i * 16 + rs;
+      const bool ok = t >= kSink && t < n_tokens;
+      w[i] = ok ? *reinterpret_cast<const uint4*>(base + (int64_t)t * st) : make_uint4(0u, 0u, 0u, 0u);
+      a[i] = ok ? alpha[(int64_t)bh * capacity + t] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = tb + i * 16 + rs;
+      if (t < kSink || t >= n_tokens) continue;
+      float x[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float d = chan(w[i], c) - m[c];
+        x[c] = a[i] > 0.0f ? __fdiv_rn(d, a[i]) : 0.0f;
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int j = 2 * cg + half;
+        const float* xs = x + 4 * half;
+        int best = 0;
+        float bd = 0.0f;
+#pragma unroll
+        for (int p = 0; p < 16; ++p) {
+          const float4 c = cen[half][p];
+          const float d0 = xs[0] - c.x, d1 = xs[1] - c.y, d2 = xs[2] - c.z, d3 = xs[3] - c.w;
+          const float dist = ((d0 * d0 + d1 * d1) + d2 * d2) + d3 * d3;
+          if (p == 0 || dist < bd) {
+            bd = dist;
+            best = p;
+          }
+        }
+        const int bin = j * 16 + best;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const long long fx = __double2ll_rn((double)xs[c] * (double)(1 << kCbFracBits));
+          atomicAdd(&cbs[bin * 4 + c], (unsigned long long)fx);
+        }
+        atomicAdd(&cbn[bin], 1);
+      }
+    }
+  }
+  __syncthreads();
+  long long* out = cb_part + ((int64_t)bh * gridDim.x + blockIdx.x) * kCbStride;
+  for (int i = tid; i < kSub * 16 * 4; i += 256) out[i] = (long long)cbs[i];
+  for (int i = tid; i < kSub * 16; i += 256) out[kSub * 16 * 4 + i] = cbn[i];
 }
 
 }  // namespace
@@ -285,9 +377,18 @@ hipError_t launch_codes_cb(const uint16_t* k, int64_t sb, int64_t sh, int64_t st
 }
 
 hipError_t launch_cb_final(const long long* cb_part, int BH, int nblk, float* codebook,
-                           hipStream_t s) {
+                           hipStream_t s, int keep) {
   return launch_k(KID_CB_FINAL, cb_final_kernel, dim3(BH), dim3(kSub * 16), 0, s, cb_part, nblk,
-                  codebook);
+                  codebook, keep);
+}
+
+hipError_t launch_kmeans_assign(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B,
+                                int Hkv, int n_tokens, int capacity, const float* mu,
+                                const float* alpha, const float* centres, long long* cb_part,
+                                hipStream_t s) {
+  return launch_k(KID_KM_ASSIGN, kmeans_assign_kernel, dim3(cb_blocks(n_tokens), B * Hkv),
+                  dim3(256), 0, s, k, sb, sh, st, Hkv, n_tokens, capacity, kCbTiles, mu, alpha,
+                  centres, cb_part);
 }
 
 }  // namespace sikv

@@ -36,6 +36,8 @@ enum KernelId {
   KID_COPY,
   KID_CB_FINAL,
   KID_VCODES,
+  KID_KM_ASSIGN,
+  KID_DSCORES,
   KID_COUNT
 };
 
@@ -241,9 +243,19 @@ hipError_t launch_codes_cb(const uint16_t* k, int64_t sb, int64_t sh, int64_t st
                            int n_tokens, int capacity, const float* mu, uint8_t* codes,
                            float* alpha, uint16_t* k_sink, long long* cb_part, hipStream_t s);
 // Codebook from the block statistics: centre = fl32((sum * 2^-24) / count) in
-// fp64, the sign vertex for an empty cluster.  codebook [B*Hkv][32][16][4].
+// fp64; an empty cluster gets the sign vertex (keep = 0) or keeps the centre
+// already in codebook (keep = 1).  codebook [B*Hkv][32][16][4].
 hipError_t launch_cb_final(const long long* cb_part, int BH, int nblk, float* codebook,
-                           hipStream_t s);
+                           hipStream_t s, int keep = 0);
+// One Lloyd step of the K-means baseline, stage 1: every prefill point x
+// (tokens [64, n_tokens), x = fl32(fl32(k - mu) / alpha)) goes to its nearest
+// centre of `centres` [B*Hkv][32][16][4] (null: the sign vertices), squared
+// distance in fp32 ((d0^2 + d1^2) + d2^2) + d3^2, lowest index on ties; block
+// statistics as launch_codes_cb (then launch_cb_final with keep = 1).
+hipError_t launch_kmeans_assign(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B,
+                                int Hkv, int n_tokens, int capacity, const float* mu,
+                                const float* alpha, const float* centres, long long* cb_part,
+                                hipStream_t s);
 
 // score.hip
 // mode 0: attention tables only; 1: all tables + sampled threshold; 2: all
@@ -296,6 +308,11 @@ hipError_t launch_combine(const float* part_o, const float* part_ml, int BHq, in
                           float* out, hipStream_t s);
 
 // dense.hip
+// Full dot-product retrieval scores: scores[bh * n_tokens + t] = qbar . k_t for
+// t < n_tokens, qbar = sum of the G query rows of the KV head (fp32, g order).
+hipError_t launch_dense_scores(const uint16_t* q, int n_q_heads, int B, int Hkv, int n_tokens,
+                               const uint16_t* k, int64_t ksb, int64_t ksh, int64_t kst,
+                               float* scores, hipStream_t s);
 hipError_t launch_dense(const uint16_t* q, int n_q_heads, int B, int Hkv, int n_tokens,
                         const uint16_t* k, int64_t ksb, int64_t ksh, int64_t kst,
                         const uint16_t* v, int64_t vsb, int64_t vsh, int64_t vst, float sm_scale,

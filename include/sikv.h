@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define SIKV_ABI_VERSION 2
+#define SIKV_ABI_VERSION 3
 #define SIKV_HEAD_DIM 128
 #define SIKV_N_SINK 64
 #define SIKV_MAX_GROUP 8
@@ -60,6 +60,7 @@ typedef int32_t sikv_status;
 #define SIKV_OP_SCORE_TOPK 1
 #define SIKV_OP_SPARSE_ATTN 2
 #define SIKV_OP_DECODE_STEP 3
+#define SIKV_OP_KMEANS 4
 
 /*
  * The compressed cache of one layer (caller-owned device arrays), described in
@@ -252,6 +253,39 @@ sikv_status sikv_dense_attn(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads
                             size_t ws_bytes, void *stream);
 size_t sikv_dense_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads,
                                   int32_t n_tokens);
+
+/*
+ * Comparators of the pages' module speed-ups (technical summary §4, efficiency:
+ * the sign clustering against K-means with 20 iterations; LUT retrieval against
+ * the full dot product).  Not part of the decode path.
+ *
+ * sikv_kmeans_codebook - the iterative clustering that the one-pass sign
+ * clustering replaces (§2.1 item 1): n_iter (1..1000) Lloyd iterations over the
+ * points x = fl32(fl32(k - mu) / alpha_t) of the prefill tokens [64, n_tokens),
+ * 16 clusters per sub-vector position, started from the 16 sign vertices; a
+ * point goes to its nearest centre, the squared distance in fp32 as
+ * ((d0^2 + d1^2) + d2^2) + d3^2 with d_i = fl32(x_i - c_i), the lowest index
+ * on ties; a centre is the mean of its points (sums of rint(x * 2^24) in int64,
+ * exact; fl32((sum * 2^-24) / count) in fp64); an empty cluster keeps its
+ * centre.  One iteration gives exactly the one-pass codebook.  Needs the
+ * cache's codebook (written), mu and alpha (from sikv_encode's prefill over the
+ * same keys k, laid out as in sikv_encode).  Workspace: SIKV_OP_KMEANS.
+ */
+sikv_status sikv_kmeans_codebook(const sikv_cache_desc *cache, const uint16_t *k,
+                                 int64_t k_stride_b, int64_t k_stride_h, int64_t k_stride_t,
+                                 int32_t n_iter, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * sikv_dense_scores - full dot-product retrieval scores: scores[(b*n_kv_heads +
+ * h) * n_tokens + t] = qbar_h . K[b,h,t] for every t < n_tokens, with qbar_h the
+ * fp32 sum (g ascending) of the G query rows h*G..h*G+G-1 (the selection query
+ * of the LUT-GEMV score), K bf16 with the stride scheme of sikv_cache_desc,
+ * q bf16 [B][n_q_heads][128].  No workspace.
+ */
+sikv_status sikv_dense_scores(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads,
+                              int32_t n_tokens, const uint16_t *q, const uint16_t *k,
+                              int64_t k_stride_b, int64_t k_stride_h, int64_t k_stride_t,
+                              float *scores, void *stream);
 
 /* Plain device copy of `bytes` (multiple of 16, both pointers 16-byte
  * aligned): the reference kernel for bandwidth and traffic-counter scaling. */

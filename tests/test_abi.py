@@ -222,3 +222,27 @@ def test_timing_facility_without_launches():
     n, ms = C.c_int64(), C.c_double()
     assert lib.sikv_timing_read(0, C.byref(n), C.byref(ms)) == OK and n.value == 0
     assert lib.sikv_timing_read(99, C.byref(n), C.byref(ms)) == INVALID
+
+
+def test_baseline_comparator_validation():
+    """K-means and dense-score comparators reject bad arguments before any launch."""
+    d = desc()
+    cbd = desc(codebook=FAKE + 0x500000)
+    km = lib.sikv_kmeans_codebook
+    need = lib.sikv_workspace_bytes(4, C.byref(cbd), 1, 1)
+    assert need > 0 and lib.sikv_workspace_bytes(4, C.byref(d), 1, 1) == 0   # no codebook
+    assert km(C.byref(d), FAKE, 0, 0, 128, 20, FAKE, need, None) == INVALID   # no codebook
+    assert km(C.byref(cbd), None, 0, 0, 128, 20, FAKE, need, None) == INVALID
+    assert km(C.byref(cbd), FAKE + 2, 0, 0, 128, 20, FAKE, need, None) == INVALID
+    assert km(C.byref(cbd), FAKE, 0, 0, 100, 20, FAKE, need, None) == INVALID   # stride
+    assert km(C.byref(cbd), FAKE, 0, 0, 128, 0, FAKE, need, None) == INVALID    # n_iter
+    assert km(C.byref(cbd), FAKE, 0, 0, 128, 1001, FAKE, need, None) == INVALID
+    assert km(C.byref(cbd), FAKE, 0, 0, 128, 20, FAKE, need - 8, None) == WORKSPACE
+    assert km(C.byref(cbd), FAKE, 0, 0, 128, 20, None, 0, None) == WORKSPACE
+    ds = lib.sikv_dense_scores
+    assert ds(2, 2, 4, 1000, FAKE, FAKE, 0, 0, 128, None, None) == INVALID      # no output
+    assert ds(2, 2, 3, 1000, FAKE, FAKE, 0, 0, 128, FAKE, None) == INVALID      # Hq % Hkv
+    assert ds(2, 2, 18, 1000, FAKE, FAKE, 0, 0, 128, FAKE, None) == UNSUPPORTED  # G = 9
+    assert ds(2, 2, 4, 0, FAKE, FAKE, 0, 0, 128, FAKE, None) == INVALID
+    assert ds(2, 2, 4, 1000, FAKE + 2, FAKE, 0, 0, 128, FAKE, None) == INVALID
+    assert ds(2, 2, 4, 1000, FAKE, FAKE, 0, 0, 100, FAKE, None) == INVALID     # stride
