@@ -120,6 +120,10 @@ KERNEL_SOURCES = {
     "mu_final": ["encode.hip", "sikv_internal.h", "api.cpp"],
     "dense": ["dense.hip", "sikv_internal.h", "api.cpp"],
     "copy": ["util.hip", "sikv_internal.h", "api.cpp"],
+    "cb_final": ["encode.hip", "sikv_internal.h", "api.cpp"],
+    "vcodes": ["encode.hip", "sikv_internal.h", "api.cpp"],
+    "kmeans_assign": ["encode.hip", "sikv_internal.h", "api.cpp"],
+    "dense_scores": ["dense.hip", "sikv_internal.h", "api.cpp"],
 }
 COPY_BYTES = 512 << 20  # sikv_stream_copy size used below: reads and writes this many bytes
 
