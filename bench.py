@@ -47,6 +47,9 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-dense", action="store_true", help="skip the dense bf16 comparator")
     p.add_argument("--no-qv", action="store_true", help="skip the 2-bit value variant")
+    p.add_argument("--no-prefill", action="store_true",
+                   help="skip timing the prefill compression against torch's fused prefill "
+                        "attention of the same shape")
     p.add_argument("--no-baselines", action="store_true",
                    help="skip the K-means and dense-retrieval comparators")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -198,6 +201,74 @@ def summarize_traffic(fetch_dir: str, write_dir: str, out_json: str, command: st
             "sources": KERNEL_SOURCES[k], "source_hash": source_hash(KERNEL_SOURCES[k])}
     json.dump(out, open(out_json, "w"), indent=1)
     print(json.dumps(out, indent=1))
+
+
+# ----------------------------------------------------------------------------- prefill
+def prefill_overhead(sk, torch, dev, K, V, n: int = 32768, reps: int = 5):
+    """The compression's cost at prefill against the prefill attention it rides on
+    (the pages report +5 % time to the second token): one layer of B=1, 32/8 heads,
+    n tokens.  Compression = sikv_encode (mean, codes, scales, sinks), with the
+    one-pass codebook, plus sikv_encode_v (2-bit values).  Dense prefill attention =
+    torch's fused causal SDPA (flash or memory-efficient kernels only) over the same
+    K and V.  Also both at once, the compression on a second stream (default
+    priority) while the attention runs: the overhead a prefill sees if the encode
+    of layer l overlaps later work."""
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    Hkv = K.shape[1]
+    Kp = K[:1, :, :n].contiguous()
+    Vp = V[:1, :, :n].contiguous()
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    Qp = torch.randn((1, 4 * Hkv, n, 128), generator=g, device=dev, dtype=torch.float32).to(
+        torch.bfloat16)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def attn():
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+            return F.scaled_dot_product_attention(Qp, Kp, Vp, is_causal=True, enable_gqa=True)
+
+    cache = sk.Cache(1, Hkv, n, device=dev, codebook=True, quant_v=True)
+
+    def encode():
+        sk.sikv_encode(cache, Kp)
+        sk.sikv_encode_v(cache, Vp)
+
+    def timed(f):
+        f()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(reps):
+            f()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) * 1e3 / reps
+
+    try:
+        attn_us = timed(attn)
+    except RuntimeError as e:  # no fused kernel for this device: report none
+        log(f"prefill attention unavailable: {e}")
+        return {"n_tokens": n, "attention_us": None}
+    enc_us = timed(encode)
+    side = torch.cuda.Stream(dev)
+    main = torch.cuda.current_stream(dev)
+
+    def both():
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            encode()
+        attn()
+        main.wait_stream(side)
+
+    both_us = timed(both)
+    out = {"n_tokens": n, "batch": 1, "n_q_heads": 4 * Hkv, "n_kv_heads": Hkv,
+           "attention_us": attn_us, "encode_us": enc_us, "encode_frac": enc_us / attn_us,
+           "overlapped_us": both_us, "overlapped_frac": both_us / attn_us - 1.0,
+           "encode": "keys with one-pass codebook + 2-bit values",
+           "attention": "torch causal SDPA (fused kernels only), bf16"}
+    log(f"prefill n={n}: attention {attn_us:.0f} us, encode {enc_us:.0f} us "
+        f"({100 * enc_us / attn_us:.2f} %), both overlapped {both_us:.0f} us")
+    return out
 
 
 # ----------------------------------------------------------------------------- CPU
@@ -510,6 +581,10 @@ def main():
         dense_torch_us = ev0.elapsed_time(ev1) * 1e3 / reps
         log(f"dense torch {dense_torch_us:.1f} us (max rel diff to the dense kernel {rel:.1e})")
 
+    prefill = None
+    if not args.no_prefill:
+        prefill = prefill_overhead(sk, torch, dev, K, caches[0].v)
+
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle")
@@ -563,6 +638,8 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if prefill is not None:
+        report["prefill_overhead"] = prefill
     if km20_us is not None:
         score_us = kern_us.get("score", 0.0)
         report["module_speedups"] = {
