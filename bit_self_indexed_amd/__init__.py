@@ -133,6 +133,7 @@ class Cache:
             self.v_sink = torch.zeros((batch, n_kv_heads, N_SINK, HEAD_DIM), dtype=torch.bfloat16,
                                       device=dev)
         self.v = v
+        self.seq_lens = None  # ragged batch: int32 [B] on the device (see view())
         self.ws = Workspace(dev)
 
     @property
@@ -153,7 +154,21 @@ class Cache:
             d.v_stride_b, d.v_stride_h, d.v_stride_t = sb, sh, st
         d.codebook = self.codebook.data_ptr() if self.codebook is not None else None
         d.vq, d.vsz, d.v_sink = _ptr(self.vq), _ptr(self.vsz), _ptr(self.v_sink)
+        d.seq_lens = _ptr(self.seq_lens)
         return d
+
+    def view(self, b: int) -> "Cache":
+        """Sequence b as a batch-1 cache sharing this cache's memory (for ragged
+        prefill: encode each sequence with its own length, then set seq_lens)."""
+        c = Cache.__new__(Cache)
+        c.batch, c.n_kv_heads, c.capacity = 1, self.n_kv_heads, self.capacity
+        c.n_tokens = self.n_tokens
+        for name in ("codes", "alpha", "mu", "k_sink", "codebook", "vq", "vsz", "v_sink", "v"):
+            t = getattr(self, name)
+            setattr(c, name, None if t is None else t[b:b + 1])
+        c.seq_lens = None
+        c.ws = self.ws
+        return c
 
 
 def workspace_bytes(op: int, cache: Cache, n_q_heads: int = 1, top_k: int = 1) -> int:
@@ -263,6 +278,8 @@ def sikv_append_decode_step(cache: Cache, k_new: torch.Tensor, q: torch.Tensor, 
     if out is None:
         out = torch.empty((cache.batch, n_q, HEAD_DIM), dtype=torch.float32, device=cache.device)
     cache.n_tokens += 1
+    if cache.seq_lens is not None:
+        cache.seq_lens += 1   # every sequence appends one token (stream-ordered on the device)
     try:
         d = cache.desc()
         need = int(lib.sikv_workspace_bytes(OP_DECODE_STEP, ctypes.byref(d), n_q, top_k))
@@ -274,6 +291,8 @@ def sikv_append_decode_step(cache: Cache, k_new: torch.Tensor, q: torch.Tensor, 
                "sikv_append_decode_step")
     except Exception:
         cache.n_tokens -= 1
+        if cache.seq_lens is not None:
+            cache.seq_lens -= 1
         raise
     return out
 

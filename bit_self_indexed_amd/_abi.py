@@ -4,7 +4,7 @@ from __future__ import annotations
 
 import ctypes as C
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 STATUS = {
     0: "SIKV_OK",
@@ -35,6 +35,7 @@ class CacheDesc(C.Structure):
         ("vq", C.c_void_p),
         ("vsz", C.c_void_p),
         ("v_sink", C.c_void_p),
+        ("seq_lens", C.c_void_p),
     ]
 
 

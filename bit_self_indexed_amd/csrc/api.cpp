@@ -144,7 +144,7 @@ sikv_status check_desc(const sikv_cache_desc* c) {
   if (c->n_tokens <= kSink || c->capacity < c->n_tokens) return SIKV_ERR_INVALID_ARG;
   if (!c->codes || !c->alpha || !c->mu || !c->k_sink) return SIKV_ERR_INVALID_ARG;
   if (misaligned(c->codes, 16) || misaligned(c->alpha, 4) || misaligned(c->mu, 16) ||
-      misaligned(c->k_sink, 16) || misaligned(c->codebook, 16))
+      misaligned(c->k_sink, 16) || misaligned(c->codebook, 16) || misaligned(c->seq_lens, 4))
     return SIKV_ERR_INVALID_ARG;
   if ((c->vq != nullptr || c->vsz != nullptr || c->v_sink != nullptr) &&
       (!c->vq || !c->vsz || !c->v_sink || misaligned(c->vq, 16) || misaligned(c->vsz, 16) ||
@@ -211,12 +211,13 @@ sikv_status run_score_topk(const sikv_cache_desc* c, const uint16_t* q, int n_q_
                        c->k_sink, k_new, ksb, ksh, v_new, vnsb, vnsh, c->vq, c->vsz, c->codebook,
                        top_k, mode, tab, inv,
                        at<float>(ws, sp.off_lut), at<float>(ws, sp.off_qmu),
-                       at<float>(ws, sp.off_slog), tau, at<float>(ws, sp.off_bin), s));
-  SIKV_TRY(launch_score(B, Hkv, c->codes, c->alpha, c->capacity, c->n_tokens, tab, inv, tau,
-                        sp.chunk, sp.n_chunks, ckey, ct, cnt, scores_opt, s));
-  SIKV_TRY(launch_select(B, Hkv, c->codes, c->alpha, c->capacity, c->n_tokens, tab, inv, top_k,
-                         sp.chunk, sp.n_chunks, ckey, ct, cnt, tau, at<float>(ws, sp.off_bin),
-                         pkey, pt, idx, s));
+                       at<float>(ws, sp.off_slog), tau, at<float>(ws, sp.off_bin), c->seq_lens,
+                       s));
+  SIKV_TRY(launch_score(B, Hkv, c->codes, c->alpha, c->capacity, c->n_tokens, c->seq_lens, tab,
+                        inv, tau, sp.chunk, sp.n_chunks, ckey, ct, cnt, scores_opt, s));
+  SIKV_TRY(launch_select(B, Hkv, c->codes, c->alpha, c->capacity, c->n_tokens, c->seq_lens, tab,
+                         inv, top_k, sp.chunk, sp.n_chunks, ckey, ct, cnt, tau,
+                         at<float>(ws, sp.off_bin), pkey, pt, idx, s));
   return SIKV_OK;
 }
 
@@ -232,13 +233,12 @@ sikv_status run_attn(const sikv_cache_desc* c, const uint16_t* q, int n_q_heads,
     SIKV_TRY(launch_prep(q, n_q_heads, c->batch, c->n_kv_heads, c->mu, c->codes, c->alpha,
                          c->capacity, c->n_tokens, c->k_sink, nullptr, 0, 0, nullptr, 0, 0,
                          nullptr, nullptr, c->codebook, top_k, 0, nullptr,
-                         nullptr, own.lut, own.qmu, own.slog, nullptr, nullptr, s));
+                         nullptr, own.lut, own.qmu, own.slog, nullptr, nullptr, c->seq_lens, s));
     tab = &own;
   }
   SIKV_TRY(launch_attn(n_q_heads, c->batch, c->n_kv_heads, c->codes, c->alpha, c->v,
                        c->v_stride_b, c->v_stride_h, c->v_stride_t, c->vq, c->vsz, c->v_sink,
-                       c->capacity, c->n_tokens, idx,
-                       top_k, tab->lut, tab->qmu, tab->slog, sm_scale, ap.cpb, ap.n_splits, po,
+                       c->capacity, c->n_tokens, c->seq_lens, idx, top_k, tab->lut, tab->qmu, tab->slog, sm_scale, ap.cpb, ap.n_splits, po,
                        pml, s));
   SIKV_TRY(launch_combine(po, pml, c->batch * n_q_heads, ap.n_splits, out, s));
   return SIKV_OK;

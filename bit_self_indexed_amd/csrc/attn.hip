@@ -205,8 +205,9 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(
     int n_q_heads, int Hkv, const uint8_t* __restrict__ codes, const float* __restrict__ alpha,
     const uint16_t* __restrict__ v, int64_t vsb, int64_t vsh, int64_t vst,
     const uint8_t* __restrict__ vq, const uint32_t* __restrict__ vsz,
-    const uint16_t* __restrict__ vsink, int capacity,
-    int n_tokens, const int32_t* __restrict__ idx, int top_k, const float* __restrict__ att_lut,
+    const uint16_t* __restrict__ vsink, int capacity, int n_tokens,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ idx, int top_k,
+    const float* __restrict__ att_lut,
     const float* __restrict__ att_qmu, const float* __restrict__ att_slog, float sm_log2,
     int cpb, int n_splits, float* __restrict__ part_o, float* __restrict__ part_ml) {
   constexpr int GH = (G + 1) / 2;
@@ -221,9 +222,10 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
   const int el = lane & 31, half = lane >> 5, seg = lane & 15;
-  const int L = kSink + top_k;
+  const int nt = seq_len(seq_lens, b, n_tokens);          // this sequence's length
+  const int L = kSink + seq_topk(top_k, nt);               // its attended entries
   const int n_chunks = (L + kAttnChunk - 1) / kAttnChunk;
-  const int c0 = s * cpb, c_end = min(n_chunks, c0 + cpb);
+  const int c0 = s * cpb, c_end = min(n_chunks, c0 + cpb);  // may be empty (ragged batch)
   const int64_t row0 = (int64_t)bh * capacity;
   const int64_t hq0 = (int64_t)b * n_q_heads + (int64_t)h * G;
   const int32_t* ib = idx + (int64_t)bh * top_k;
@@ -243,7 +245,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(
     const int e0 = c0 * kAttnChunk, ne = (c_end - c0) * kAttnChunk;
     for (int i = tid; i < ne; i += 256) {
       const int e = min(e0 + i, L - 1);
-      sidx[i] = e < kSink ? e : min(max(ib[e - kSink], 0), n_tokens - 1);
+      sidx[i] = e < kSink ? e : min(max(ib[e - kSink], 0), nt - 1);
     }
     const float4* lsrc = reinterpret_cast<const float4*>(att_lut + hq0 * kLut);
     float4* dst = reinterpret_cast<float4*>(&lutq[0][0]);
@@ -327,14 +329,15 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(
     }
   }
   __syncthreads();
-  // Block merge of the four wave partials (waves without a chunk hold -inf, 0).
+  // Block merge of the four wave partials (waves without a chunk hold -inf, 0;
+  // a block without any, possible in a ragged batch, writes (-inf, 0, 0)).
   for (int i = tid; i < G * kD; i += 256) {
     const int g = i / kD, ch = i % kD;
     const float M = fmaxf(fmaxf(mml[0][g][0], mml[1][g][0]), fmaxf(mml[2][g][0], mml[3][g][0]));
     float o = 0.0f, l = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float f = exp2f(mml[w][g][0] - M);
+      const float f = M == -INFINITY ? 0.0f : exp2f(mml[w][g][0] - M);
       o = fmaf(f, mo[w][g][ch], o);
       l = fmaf(f, mml[w][g][1], l);
     }
@@ -417,7 +420,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 hipError_t launch_attn(int n_q_heads, int B, int Hkv, const uint8_t* codes, const float* alpha,
                        const uint16_t* v, int64_t vsb, int64_t vsh, int64_t vst,
                        const uint8_t* vq, const uint32_t* vsz, const uint16_t* vsink, int capacity,
-                       int n_tokens, const int32_t* idx, int top_k, const float* att_lut,
+                       int n_tokens, const int32_t* seq_lens, const int32_t* idx, int top_k,
+                       const float* att_lut,
                        const float* att_qmu, const float* att_slog, float sm_scale,
                        int chunks_per_block, int n_splits, float* part_o, float* part_ml,
                        hipStream_t s) {
@@ -432,11 +436,13 @@ hipError_t launch_attn(int n_q_heads, int B, int Hkv, const uint8_t* codes, cons
   case GG:                                                                                     \
     if (vq != nullptr)                                                                         \
       return launch_k(KID_ATTN, attn_kernel<GG, true>, grid, block, 0, s, n_q_heads, Hkv,      \
-                      codes, alpha, v, vsb, vsh, vst, vq, vsz, vsink, capacity, n_tokens, idx, \
+                      codes, alpha, v, vsb, vsh, vst, vq, vsz, vsink, capacity, n_tokens,       \
+                      seq_lens, idx,                                                           \
                       top_k, att_lut, att_qmu, att_slog, sm_log2, chunks_per_block, n_splits,  \
                       part_o, part_ml);                                                        \
     return launch_k(KID_ATTN, attn_kernel<GG, false>, grid, block, 0, s, n_q_heads, Hkv,       \
-                    codes, alpha, v, vsb, vsh, vst, vq, vsz, vsink, capacity, n_tokens, idx,   \
+                    codes, alpha, v, vsb, vsh, vst, vq, vsz, vsink, capacity, n_tokens,       \
+                    seq_lens, idx,                                                             \
                     top_k, att_lut, att_qmu, att_slog, sm_log2, chunks_per_block, n_splits,    \
                     part_o, part_ml);
   switch (n_q_heads / Hkv) {

@@ -320,6 +320,27 @@ __device__ void block_score_band(const float* sc, int n, int k_lo, int k_hi, flo
   *hi = k_hi >= 1 ? fminf(smax, smin + (float)(dh + 2) * w) : smax;
 }
 
+// rank: how many of the sampled scores lie at or above tau.  For a small head the
+// whole candidate set (n <= 4096) is the sample and rank = k (tau is then at most
+// the exact k-th score).  Otherwise the expected rank e = k * 4096 / n of the k-th
+// score in the sample plus five standard deviations and a small floor, so that
+// fewer than k tokens pass only with negligible probability (the select kernel
+// handles that case exactly anyway).  rank_hi: the rank of the upper end of the
+// select kernel's score bins, e - 5 sqrt(e) - 8 (the k-th score lies below it
+// with high probability), or the top of the sample if that is below 1.
+__device__ __forceinline__ void sample_ranks(int k, int n, int* rank, int* rank_hi) {
+  if (n <= kSampleMax) {
+    *rank = k;
+    *rank_hi = k;
+    return;
+  }
+  const double e = (double)k * kSampleMax / (double)n;
+  const double r = e + 5.0 * sqrt(e) + 8.0;
+  *rank = r > kSampleMax ? kSampleMax + 1 : (int)r + 1;
+  const double rh = e - 5.0 * sqrt(e) - 8.0;
+  *rank_hi = rh < 1.0 ? 0 : (int)rh;
+}
+
 // ------------------------------------------------------------------ prep
 // mode 0: attention tables only (sel_lut, sel_inv and tau unused); 1: all tables
 // + sampled threshold; 2: all tables + tau = +inf (forces the exact whole-head
@@ -332,7 +353,7 @@ __global__ __launch_bounds__(1024) void prep_kernel(
     const uint16_t* __restrict__ k_sink, const uint16_t* __restrict__ k_new, int64_t ksb,
     int64_t ksh, const uint16_t* __restrict__ v_new, int64_t vnsb, int64_t vnsh,
     uint8_t* __restrict__ vq, uint32_t* __restrict__ vsz,
-    const float* __restrict__ codebook, int rank, int rank_hi, int mode,
+    const float* __restrict__ codebook, int top_k, int mode, const int32_t* __restrict__ seq_lens,
     int* __restrict__ sel_lut, float* __restrict__ sel_inv, float* __restrict__ att_lut,
     float* __restrict__ att_qmu, float* __restrict__ att_slog, float* __restrict__ tau,
     float* __restrict__ bin_scale) {
@@ -348,7 +369,10 @@ __global__ __launch_bounds__(1024) void prep_kernel(
   __shared__ uint32_t mm[32];
   const int bh = blockIdx.x, b = bh / Hkv, h = bh - b * Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = n_tokens - kSink - (k_new != nullptr ? 1 : 0);  // candidates the sample covers
+  const int nt = seq_len(seq_lens, b, n_tokens);                   // this sequence's length
+  const int n = nt - kSink - (k_new != nullptr ? 1 : 0);  // candidates the sample covers
+  int rank = 1, rank_hi = 0;
+  if (mode == 1) sample_ranks(seq_topk(top_k, nt), n, &rank, &rank_hi);
   const bool full = n <= kSampleMax;
   const int m = full ? n : kSampleMax;
   const bool sample = mode == 1 && m > 0 && rank <= m;
@@ -405,14 +429,14 @@ __global__ __launch_bounds__(1024) void prep_kernel(
   if (has_cb && tid < kLut) cbl[tid] = cbv;
   if (k_new != nullptr && wave == 0) {  // the whole wave runs the 16-lane shuffles
     const RowCode rc = encode_row16(kw, km);
-    const int64_t row = row0 + n_tokens - 1;
+    const int64_t row = row0 + nt - 1;
     if (tid < 16 && (tid & 3) == 0) *reinterpret_cast<uint32_t*>(codes + row * kCodeBytes + tid) = rc.word;
     if (tid == 0) alpha[row] = rc.alpha;
   }
   if (v_new != nullptr && wave == 1) {  // the whole wave runs the 4-lane shuffles
     const VRowCode rc = quantize_vrow16(vw);
     const uint32_t pair = rc.bits | (__shfl_down(rc.bits, 1, 16) << 16);
-    const int cg = lane, row = n_tokens - 1;
+    const int cg = lane, row = nt - 1;
     if (cg < 16 && (cg & 1) == 0)
       *reinterpret_cast<uint32_t*>(vq + (row0 + row) * kVCodeBytes + 2 * cg) = pair;
     if (cg < 16 && (cg & 3) == 0) vsz[(row0 + row) * 4 + (cg >> 2)] = rc.sz;
@@ -525,7 +549,8 @@ __global__ __launch_bounds__(1024) void prep_kernel(
 template <int U>
 __global__ __launch_bounds__(256) void score_kernel(
     const uint8_t* __restrict__ codes, const float* __restrict__ alpha, int capacity,
-    int n_tokens, const int* __restrict__ sel_lut, const float* __restrict__ sel_inv,
+    int n_tokens, int Hkv, const int32_t* __restrict__ seq_lens,
+    const int* __restrict__ sel_lut, const float* __restrict__ sel_inv,
     const float* __restrict__ tau, int n_chunks, uint32_t* __restrict__ cand_key,
     int32_t* __restrict__ cand_t, int32_t* __restrict__ chunk_count,
     float* __restrict__ scores_opt) {
@@ -539,7 +564,7 @@ __global__ __launch_bounds__(256) void score_kernel(
   const uint4* __restrict__ cb = reinterpret_cast<const uint4*>(codes) + row0;
   const float* __restrict__ ab = alpha + row0;
   const int2 tv = reinterpret_cast<const int2*>(sel_lut + (int64_t)bh * kLut)[tid];
-  const int lim = n_tokens - t0;  // tokens of this tile that exist
+  const int lim = seq_len(seq_lens, bh / Hkv, n_tokens) - t0;  // tokens of this tile that exist
   uint4 c[U];
   float a[U];
   if (lim >= kChunk) {
@@ -603,7 +628,8 @@ __device__ __forceinline__ void count_bin(uint32_t* hist, bool valid, int bin, i
 // ------------------------------------------------------------------ select
 __global__ __launch_bounds__(1024) void select_kernel(
     const uint8_t* __restrict__ codes, const float* __restrict__ alpha, int capacity,
-    int n_tokens, const int* __restrict__ sel_lut, const float* __restrict__ sel_inv, int top_k,
+    int n_tokens, int Hkv, const int32_t* __restrict__ seq_lens,
+    const int* __restrict__ sel_lut, const float* __restrict__ sel_inv, int top_k_max,
     int chunk, int n_chunks,
     const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_t,
     const int32_t* __restrict__ chunk_count, const float* __restrict__ tau,
@@ -619,8 +645,11 @@ __global__ __launch_bounds__(1024) void select_kernel(
   __shared__ int scount;
   const int bh = blockIdx.x;
   const int tid = threadIdx.x;
-  const int n = n_tokens - kSink;
-  int32_t* out = idx + (int64_t)bh * top_k;
+  const int nt = seq_len(seq_lens, bh / Hkv, n_tokens);
+  const int n = nt - kSink;
+  const int top_k = seq_topk(top_k_max, nt);  // this sequence's k; the rest of its row is -1
+  int32_t* out = idx + (int64_t)bh * top_k_max;
+  for (int j = top_k + tid; j < top_k_max; j += blockDim.x) out[j] = -1;
   if (top_k >= n) {  // every candidate is kept
     for (int j = tid; j < top_k; j += blockDim.x) out[j] = kSink + j;
     return;
@@ -775,50 +804,30 @@ __global__ __launch_bounds__(1024) void select_kernel(
 
 }  // namespace
 
-// rank: how many of the sampled scores lie at or above tau.  For a small head the
-// whole candidate set is the sample and rank = k (tau is then at most the exact
-// k-th score).  rank_hi: the rank of the upper end of the select kernel's score
-// bins (e - 5 sqrt(e) - 8, or the top of the sample if that is below 1).  Otherwise the expected rank of the k-th score in the sample plus five
-// standard deviations and a small floor, so that fewer than k tokens pass only
-// with negligible probability; the select kernel handles that case exactly anyway.
 hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const float* mu,
                        uint8_t* codes, float* alpha, int capacity, int n_tokens,
                        const uint16_t* k_sink, const uint16_t* k_new, int64_t ksb, int64_t ksh,
                        const uint16_t* v_new, int64_t vnsb, int64_t vnsh, uint8_t* vq,
                        uint32_t* vsz, const float* codebook, int top_k, int mode, int* sel_lut,
                        float* sel_inv, float* att_lut, float* att_qmu, float* att_slog,
-                       float* tau, float* bin_scale, hipStream_t s) {
-  const int n = n_tokens - kSink - (k_new != nullptr ? 1 : 0);
-  int rank = 1, rank_hi = 0;
-  if (mode == 1) {
-    if (n <= kSampleMax) {
-      rank = top_k;
-      rank_hi = top_k;
-    } else {
-      const double e = (double)top_k * kSampleMax / (double)n;
-      const double r = e + 5.0 * __builtin_sqrt(e) + 8.0;
-      rank = r > kSampleMax ? kSampleMax + 1 : (int)r + 1;
-      const double rh = e - 5.0 * __builtin_sqrt(e) - 8.0;  // the k-th score lies below w.h.p.
-      rank_hi = rh < 1.0 ? 0 : (int)rh;
-    }
-  }
+                       float* tau, float* bin_scale, const int32_t* seq_lens, hipStream_t s) {
   return launch_k(KID_PREP, prep_kernel, dim3(B * Hkv), dim3(1024), 0, s, q, n_q_heads, Hkv,
                   n_q_heads / Hkv, mu, codes, alpha, capacity, n_tokens, k_sink, k_new, ksb, ksh,
-                  v_new, vnsb, vnsh, vq, vsz, codebook, rank, rank_hi, mode, sel_lut, sel_inv, att_lut, att_qmu, att_slog, tau,
-                  bin_scale);
+                  v_new, vnsb, vnsh, vq, vsz, codebook, top_k, mode, seq_lens, sel_lut, sel_inv,
+                  att_lut, att_qmu, att_slog, tau, bin_scale);
 }
 
 hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha, int capacity,
-                        int n_tokens, const int* sel_lut, const float* sel_inv, const float* tau,
-                        int chunk,
+                        int n_tokens, const int32_t* seq_lens, const int* sel_lut,
+                        const float* sel_inv, const float* tau, int chunk,
                         int n_chunks, uint32_t* cand_key, int32_t* cand_t, int32_t* chunk_count,
                         float* scores_opt, hipStream_t s) {
   const dim3 grid(n_chunks, B * Hkv), block(256);
 #define SIKV_SCORE_CASE(UU)                                                                    \
   case 256 * UU:                                                                               \
     return launch_k(KID_SCORE, score_kernel<UU>, grid, block, 0, s, codes, alpha, capacity,    \
-                    n_tokens, sel_lut, sel_inv, tau, n_chunks, cand_key, cand_t, chunk_count,  \
-                    scores_opt);
+                    n_tokens, Hkv, seq_lens, sel_lut, sel_inv, tau, n_chunks, cand_key,        \
+                    cand_t, chunk_count, scores_opt);
   switch (chunk) {
     SIKV_SCORE_CASE(1)
     SIKV_SCORE_CASE(2)
@@ -832,14 +841,15 @@ hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha
 }
 
 hipError_t launch_select(int B, int Hkv, const uint8_t* codes, const float* alpha, int capacity,
-                         int n_tokens, const int* sel_lut, const float* sel_inv, int top_k,
-                         int chunk, int n_chunks,
+                         int n_tokens, const int32_t* seq_lens, const int* sel_lut,
+                         const float* sel_inv, int top_k, int chunk, int n_chunks,
                          uint32_t* cand_key, int32_t* cand_t, const int32_t* chunk_count,
                          const float* tau, const float* bin_scale, uint32_t* comp_key,
                          int32_t* comp_t, int32_t* idx, hipStream_t s) {
   if (n_chunks > kMaxChunks) return hipErrorInvalidValue;
   return launch_k(KID_SELECT, select_kernel, dim3(B * Hkv), dim3(1024), 0, s, codes, alpha,
-                  capacity, n_tokens, sel_lut, sel_inv, top_k, chunk, n_chunks, cand_key, cand_t,
+                  capacity, n_tokens, Hkv, seq_lens, sel_lut, sel_inv, top_k, chunk, n_chunks,
+                  cand_key, cand_t,
                   chunk_count, tau, bin_scale, comp_key, comp_t, idx);
 }
 

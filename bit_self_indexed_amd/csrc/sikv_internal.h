@@ -118,6 +118,16 @@ __device__ __forceinline__ VRowCode quantize_vrow16(const uint4& w) {
   return VRowCode{bits, (uint32_t)__half_as_ushort(s16) | ((uint32_t)__half_as_ushort(z16) << 16)};
 }
 
+// Ragged batches: the length of sequence b is seq_lens[b] clamped into
+// [65, n_max] (n_max, the descriptor's n_tokens, when seq_lens is null), and it
+// selects min(k, length - 64) tokens.
+__device__ __forceinline__ int seq_len(const int32_t* seq_lens, int b, int n_max) {
+  return seq_lens != nullptr ? min(max(seq_lens[b], kSink + 1), n_max) : n_max;
+}
+__host__ __device__ __forceinline__ int seq_topk(int k, int n) {
+  return k < n - kSink ? k : n - kSink;
+}
+
 // Order-preserving map of fp32 (no NaN) to uint32.
 __device__ __forceinline__ uint32_t score_key(float s) {
   uint32_t u = __float_as_uint(s);
@@ -257,7 +267,8 @@ hipError_t launch_kmeans_assign(const uint16_t* k, int64_t sb, int64_t sh, int64
                                 const float* alpha, const float* centres, long long* cb_part,
                                 hipStream_t s);
 
-// score.hip
+// score.hip.  seq_lens (may be null): per-sequence lengths of a ragged batch
+// (seq_len / seq_topk above); n_tokens is then the longest, which sizes grids.
 // mode 0: attention tables only; 1: all tables + sampled threshold; 2: all
 // tables + a threshold that forces the exact whole-head selection.
 // Every mode also writes the attention tables of the query heads: att_lut
@@ -276,15 +287,15 @@ hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const f
                        const uint16_t* v_new, int64_t vnsb, int64_t vnsh, uint8_t* vq,
                        uint32_t* vsz, const float* codebook, int top_k, int mode, int* sel_lut,
                        float* sel_inv, float* att_lut, float* att_qmu, float* att_slog,
-                       float* tau, float* bin_scale, hipStream_t s);
+                       float* tau, float* bin_scale, const int32_t* seq_lens, hipStream_t s);
 hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha, int capacity,
-                        int n_tokens, const int* sel_lut, const float* sel_inv, const float* tau,
-                        int chunk,
+                        int n_tokens, const int32_t* seq_lens, const int* sel_lut,
+                        const float* sel_inv, const float* tau, int chunk,
                         int n_chunks, uint32_t* cand_key, int32_t* cand_t, int32_t* chunk_count,
                         float* scores_opt, hipStream_t s);
 hipError_t launch_select(int B, int Hkv, const uint8_t* codes, const float* alpha, int capacity,
-                         int n_tokens, const int* sel_lut, const float* sel_inv, int top_k,
-                         int chunk, int n_chunks,
+                         int n_tokens, const int32_t* seq_lens, const int* sel_lut,
+                         const float* sel_inv, int top_k, int chunk, int n_chunks,
                          uint32_t* cand_key, int32_t* cand_t, const int32_t* chunk_count,
                          const float* tau, const float* bin_scale, uint32_t* comp_key,
                          int32_t* comp_t, int32_t* idx, hipStream_t s);
@@ -300,7 +311,8 @@ constexpr int kAttnMaxCpb = 64;  // chunks per block at most (the block's positi
 hipError_t launch_attn(int n_q_heads, int B, int Hkv, const uint8_t* codes, const float* alpha,
                        const uint16_t* v, int64_t vsb, int64_t vsh, int64_t vst,
                        const uint8_t* vq, const uint32_t* vsz, const uint16_t* vsink, int capacity,
-                       int n_tokens, const int32_t* idx, int top_k, const float* att_lut,
+                       int n_tokens, const int32_t* seq_lens, const int32_t* idx, int top_k,
+                       const float* att_lut,
                        const float* att_qmu, const float* att_slog, float sm_scale,
                        int chunks_per_block, int n_splits, float* part_o, float* part_ml,
                        hipStream_t s);

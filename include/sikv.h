@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define SIKV_ABI_VERSION 3
+#define SIKV_ABI_VERSION 4
 #define SIKV_HEAD_DIM 128
 #define SIKV_N_SINK 64
 #define SIKV_MAX_GROUP 8
@@ -95,8 +95,20 @@ typedef int32_t sikv_status;
  *          half), v_sink bf16 [B][Hkv][64][128]; written by sikv_encode_v (or the
  *          fused step); `v` is then not read and may be NULL.  Value of channel c:
  *          zero + code * scale of its group.
+ *   seq_lens  NULL: every sequence has n_tokens tokens.  Else (ragged batch, a
+ *          device array int32 [B], 4-byte aligned, read by the kernels) sequence
+ *          b has seq_lens[b] tokens and n_tokens is the longest (it sizes grids
+ *          and workspaces); a length outside (64, n_tokens] is clamped into it.
+ *          Scoring, top-k and attention of sequence b use its own tokens
+ *          64..seq_lens[b]-1, its top-k is k_b = min(k, seq_lens[b] - 64) and row
+ *          b of idx holds k_b positions followed by -1; the fused append step
+ *          writes the new token of sequence b at row seq_lens[b]-1 (seq_lens
+ *          already counts it).  sikv_encode / sikv_encode_v ignore it: ragged
+ *          prefill is one call per sequence on a batch-1 view (pointers offset
+ *          to that sequence's rows).
  * n_tokens (N) is the number of valid tokens of every sequence (64 < N <=
- * capacity); candidates for top-k are the tokens 64..N-1.
+ * capacity; the longest one with seq_lens); candidates for top-k are the tokens
+ * 64..N-1.
  */
 typedef struct sikv_cache_desc {
   int32_t batch;
@@ -117,6 +129,7 @@ typedef struct sikv_cache_desc {
   uint8_t *vq;
   uint32_t *vsz;
   uint16_t *v_sink;
+  const int32_t *seq_lens;
 } sikv_cache_desc;
 
 /*
