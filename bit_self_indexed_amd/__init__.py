@@ -109,9 +109,12 @@ class Cache:
     k_sink bf16 [B,Hkv,64,128] are owned here; ``v`` (bf16 [B,Hkv,>=cap,128],
     unit channel stride) is only referenced.  codebook=True adds data-derived
     centres, fp32 [B,Hkv,32,16,4], written at prefill and used by every call.
-    quant_v=True keeps the values 2-bit instead (vq uint8 [B,Hkv,cap,32], vsz
-    uint32 [B,Hkv,cap,4], v_sink bf16 [B,Hkv,64,128], written by sikv_encode_v
-    or the fused append step); ``v`` is then not read.
+    quant_v=True keeps the values 2-bit instead: vrec uint8 [B,Hkv,cap,64], one
+    record per token (value codes, bytes 0..31; fp16 scale/zero words of the 4
+    channel groups, 32..47; a copy of the key code, 48..63), and v_sink bf16
+    [B,Hkv,64,128], written by sikv_encode_v / sikv_encode or the fused append
+    step; ``v`` is then not read.  ``vq`` and ``vsz`` are views of the record
+    fields (codes [B,Hkv,cap,32] uint8, words [B,Hkv,cap,4] int32).
     """
 
     def __init__(self, batch: int, n_kv_heads: int, capacity: int, device="cuda",
@@ -126,10 +129,10 @@ class Cache:
                                   device=dev)
         self.codebook = (torch.zeros((batch, n_kv_heads, 32, 16, 4), dtype=torch.float32,
                                      device=dev) if codebook else None)
-        self.vq = self.vsz = self.v_sink = None
+        self.vrec = self.v_sink = None
         if quant_v:
-            self.vq = torch.zeros((batch, n_kv_heads, capacity, 32), dtype=torch.uint8, device=dev)
-            self.vsz = torch.zeros((batch, n_kv_heads, capacity, 4), dtype=torch.int32, device=dev)
+            self.vrec = torch.zeros((batch, n_kv_heads, capacity, 64), dtype=torch.uint8,
+                                    device=dev)
             self.v_sink = torch.zeros((batch, n_kv_heads, N_SINK, HEAD_DIM), dtype=torch.bfloat16,
                                       device=dev)
         self.v = v
@@ -153,9 +156,17 @@ class Cache:
             d.v = self.v.data_ptr()
             d.v_stride_b, d.v_stride_h, d.v_stride_t = sb, sh, st
         d.codebook = self.codebook.data_ptr() if self.codebook is not None else None
-        d.vq, d.vsz, d.v_sink = _ptr(self.vq), _ptr(self.vsz), _ptr(self.v_sink)
+        d.vrec, d.v_sink = _ptr(self.vrec), _ptr(self.v_sink)
         d.seq_lens = _ptr(self.seq_lens)
         return d
+
+    @property
+    def vq(self):
+        return None if self.vrec is None else self.vrec[..., :32]
+
+    @property
+    def vsz(self):
+        return None if self.vrec is None else self.vrec[..., 32:48].view(torch.int32)
 
     def view(self, b: int) -> "Cache":
         """Sequence b as a batch-1 cache sharing this cache's memory (for ragged
@@ -163,7 +174,7 @@ class Cache:
         c = Cache.__new__(Cache)
         c.batch, c.n_kv_heads, c.capacity = 1, self.n_kv_heads, self.capacity
         c.n_tokens = self.n_tokens
-        for name in ("codes", "alpha", "mu", "k_sink", "codebook", "vq", "vsz", "v_sink", "v"):
+        for name in ("codes", "alpha", "mu", "k_sink", "codebook", "vrec", "v_sink", "v"):
             t = getattr(self, name)
             setattr(c, name, None if t is None else t[b:b + 1])
         c.seq_lens = None

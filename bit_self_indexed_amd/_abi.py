@@ -4,7 +4,7 @@ from __future__ import annotations
 
 import ctypes as C
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 STATUS = {
     0: "SIKV_OK",
@@ -32,8 +32,7 @@ class CacheDesc(C.Structure):
         ("v_stride_h", C.c_int64),
         ("v_stride_t", C.c_int64),
         ("codebook", C.c_void_p),
-        ("vq", C.c_void_p),
-        ("vsz", C.c_void_p),
+        ("vrec", C.c_void_p),
         ("v_sink", C.c_void_p),
         ("seq_lens", C.c_void_p),
     ]

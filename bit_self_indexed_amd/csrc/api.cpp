@@ -146,9 +146,8 @@ sikv_status check_desc(const sikv_cache_desc* c) {
   if (misaligned(c->codes, 16) || misaligned(c->alpha, 4) || misaligned(c->mu, 16) ||
       misaligned(c->k_sink, 16) || misaligned(c->codebook, 16) || misaligned(c->seq_lens, 4))
     return SIKV_ERR_INVALID_ARG;
-  if ((c->vq != nullptr || c->vsz != nullptr || c->v_sink != nullptr) &&
-      (!c->vq || !c->vsz || !c->v_sink || misaligned(c->vq, 16) || misaligned(c->vsz, 16) ||
-       misaligned(c->v_sink, 16)))
+  if ((c->vrec != nullptr || c->v_sink != nullptr) &&
+      (!c->vrec || !c->v_sink || misaligned(c->vrec, 64) || misaligned(c->v_sink, 16)))
     return SIKV_ERR_INVALID_ARG;
   return SIKV_OK;
 }
@@ -158,7 +157,7 @@ bool bad_strides(int64_t sb, int64_t sh, int64_t st) {
 }
 
 sikv_status check_v(const sikv_cache_desc* c) {
-  if (c->vq != nullptr) return SIKV_OK;  // quantised values (checked in check_desc)
+  if (c->vrec != nullptr) return SIKV_OK;  // quantised values (checked in check_desc)
   if (c->v == nullptr || misaligned(c->v, 16) || bad_strides(c->v_stride_b, c->v_stride_h, c->v_stride_t))
     return SIKV_ERR_INVALID_ARG;
   return SIKV_OK;
@@ -208,7 +207,7 @@ sikv_status run_score_topk(const sikv_cache_desc* c, const uint16_t* q, int n_q_
   float* inv = at<float>(ws, sp.off_inv);
   const int mode = g_force_exact.load(std::memory_order_relaxed) ? 2 : 1;
   SIKV_TRY(launch_prep(q, n_q_heads, B, Hkv, c->mu, c->codes, c->alpha, c->capacity, c->n_tokens,
-                       c->k_sink, k_new, ksb, ksh, v_new, vnsb, vnsh, c->vq, c->vsz, c->codebook,
+                       c->k_sink, k_new, ksb, ksh, v_new, vnsb, vnsh, c->vrec, c->codebook,
                        top_k, mode, tab, inv,
                        at<float>(ws, sp.off_lut), at<float>(ws, sp.off_qmu),
                        at<float>(ws, sp.off_slog), tau, at<float>(ws, sp.off_bin), c->seq_lens,
@@ -232,12 +231,12 @@ sikv_status run_attn(const sikv_cache_desc* c, const uint16_t* q, int n_q_heads,
   if (tab == nullptr) {
     SIKV_TRY(launch_prep(q, n_q_heads, c->batch, c->n_kv_heads, c->mu, c->codes, c->alpha,
                          c->capacity, c->n_tokens, c->k_sink, nullptr, 0, 0, nullptr, 0, 0,
-                         nullptr, nullptr, c->codebook, top_k, 0, nullptr,
+                         nullptr, c->codebook, top_k, 0, nullptr,
                          nullptr, own.lut, own.qmu, own.slog, nullptr, nullptr, c->seq_lens, s));
     tab = &own;
   }
   SIKV_TRY(launch_attn(n_q_heads, c->batch, c->n_kv_heads, c->codes, c->alpha, c->v,
-                       c->v_stride_b, c->v_stride_h, c->v_stride_t, c->vq, c->vsz, c->v_sink,
+                       c->v_stride_b, c->v_stride_h, c->v_stride_t, c->vrec, c->v_sink,
                        c->capacity, c->n_tokens, c->seq_lens, idx, top_k, tab->lut, tab->qmu, tab->slog, sm_scale, ap.cpb, ap.n_splits, po,
                        pml, s));
   SIKV_TRY(launch_combine(po, pml, c->batch * n_q_heads, ap.n_splits, out, s));
@@ -333,13 +332,13 @@ sikv_status sikv_encode(const sikv_cache_desc* c, const uint16_t* k, int64_t k_s
       long long* part = at<long long>(ws, p.off_cb);
       SIKV_TRY(launch_codes_cb(k, k_stride_b, k_stride_h, k_stride_t, c->batch, c->n_kv_heads,
                                c->n_tokens, c->capacity, c->mu, c->codes, c->alpha, c->k_sink,
-                               part, s));
+                               c->vrec, part, s));
       SIKV_TRY(launch_cb_final(part, c->batch * c->n_kv_heads, p.cb_nblk, c->codebook, s));
       return SIKV_OK;
     }
   }
   SIKV_TRY(launch_codes(k, k_stride_b, k_stride_h, k_stride_t, c->batch, c->n_kv_heads, t_begin,
-                        t_end, c->capacity, c->mu, c->codes, c->alpha, c->k_sink, s));
+                        t_end, c->capacity, c->mu, c->codes, c->alpha, c->k_sink, c->vrec, s));
   return SIKV_OK;
 }
 
@@ -426,7 +425,7 @@ sikv_status sikv_append_decode_step(const sikv_cache_desc* c, const uint16_t* k_
                                     float* out, void* ws, size_t ws_bytes, void* stream) {
   if (k_new == nullptr || misaligned(k_new, 16) || bad_strides(k_stride_b, k_stride_h, 0))
     return SIKV_ERR_INVALID_ARG;
-  if (v_new != nullptr && (c == nullptr || c->vq == nullptr || misaligned(v_new, 16) ||
+  if (v_new != nullptr && (c == nullptr || c->vrec == nullptr || misaligned(v_new, 16) ||
                            bad_strides(v_stride_b, v_stride_h, 0)))
     return SIKV_ERR_INVALID_ARG;
   return decode_step(c, k_new, k_stride_b, k_stride_h, v_new, v_stride_b, v_stride_h, q,
@@ -438,12 +437,12 @@ sikv_status sikv_encode_v(const sikv_cache_desc* c, const uint16_t* v, int64_t v
                           void* stream) {
   const sikv_status st = check_desc(c);
   if (st != SIKV_OK) return st;
-  if (c->vq == nullptr) return SIKV_ERR_INVALID_ARG;
+  if (c->vrec == nullptr) return SIKV_ERR_INVALID_ARG;
   if (v == nullptr || misaligned(v, 16) || bad_strides(v_stride_b, v_stride_h, v_stride_t))
     return SIKV_ERR_INVALID_ARG;
   if (t_begin < 0 || t_end <= t_begin || t_end > c->capacity) return SIKV_ERR_INVALID_ARG;
   SIKV_TRY(launch_vcodes(v, v_stride_b, v_stride_h, v_stride_t, c->batch, c->n_kv_heads, t_begin,
-                         t_end, c->capacity, c->vq, c->vsz, c->v_sink,
+                         t_end, c->capacity, c->vrec, c->v_sink,
                          static_cast<hipStream_t>(stream)));
   return SIKV_OK;
 }

@@ -56,8 +56,7 @@ struct Src {
   const float* slog;     // sink logits of the block's G query heads [G][64]
   const uint16_t* vb;
   int64_t vst;
-  const uint8_t* vq;
-  const uint32_t* vsz;
+  const uint8_t* vrec;    // quantised values: the head's 64-byte value records
   const uint16_t* vsk;
 };
 
@@ -87,7 +86,10 @@ __device__ __forceinline__ void load_chunk(Chunk<G>& x, int lc, bool sink, const
 #pragma unroll
     for (int i = 0; i < (G + 1) / 2; ++i) x.sl[i] = src.slog[min(2 * i + half, G - 1) * kSink + t];
   } else {
-    x.code = *reinterpret_cast<const uint4*>(src.codes + (int64_t)t * kCodeBytes);
+    // quantised values: the key code copy in the token's value record, which the
+    // V loads below fetch anyway
+    x.code = QV ? *reinterpret_cast<const uint4*>(src.vrec + (int64_t)t * kVRecBytes + kVRecCode)
+                : *reinterpret_cast<const uint4*>(src.codes + (int64_t)t * kCodeBytes);
     x.a = src.alpha[t];
 #pragma unroll
     for (int i = 0; i < (G + 1) / 2; ++i) x.sl[i] = 0.0f;
@@ -100,8 +102,9 @@ __device__ __forceinline__ void load_chunk(Chunk<G>& x, int lc, bool sink, const
     } else if (sink) {
       x.v[u] = *reinterpret_cast<const uint4*>(src.vsk + (int64_t)tu * kD);
     } else {
-      x.v[u].x = *reinterpret_cast<const uint16_t*>(src.vq + (int64_t)tu * kVCodeBytes + 2 * seg);
-      x.v[u].y = src.vsz[(int64_t)tu * 4 + (seg >> 2)];
+      const uint8_t* rec = src.vrec + (int64_t)tu * kVRecBytes;
+      x.v[u].x = *reinterpret_cast<const uint16_t*>(rec + 2 * seg);
+      x.v[u].y = *reinterpret_cast<const uint32_t*>(rec + kVRecSz + 4 * (seg >> 2));
       x.v[u].z = 0u;
       x.v[u].w = 0u;
     }
@@ -204,7 +207,7 @@ template <int G, bool QV>
 __global__ __launch_bounds__(256, 2) void attn_kernel(
     int n_q_heads, int Hkv, const uint8_t* __restrict__ codes, const float* __restrict__ alpha,
     const uint16_t* __restrict__ v, int64_t vsb, int64_t vsh, int64_t vst,
-    const uint8_t* __restrict__ vq, const uint32_t* __restrict__ vsz,
+    const uint8_t* __restrict__ vrec,
     const uint16_t* __restrict__ vsink, int capacity, int n_tokens,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ idx, int top_k,
     const float* __restrict__ att_lut,
@@ -235,8 +238,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(
   src.slog = att_slog + hq0 * kSink;
   src.vb = QV ? nullptr : v + (int64_t)b * vsb + (int64_t)h * vsh + seg * 8;
   src.vst = vst;
-  src.vq = QV ? vq + row0 * kVCodeBytes : nullptr;
-  src.vsz = QV ? vsz + row0 * 4 : nullptr;
+  src.vrec = QV ? vrec + row0 * kVRecBytes : nullptr;
   src.vsk = QV ? vsink + (int64_t)bh * kSink * kD + seg * 8 : nullptr;
 
   // The block's positions (clamped into [0, n_tokens): memory safety only) and
@@ -419,7 +421,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 hipError_t launch_attn(int n_q_heads, int B, int Hkv, const uint8_t* codes, const float* alpha,
                        const uint16_t* v, int64_t vsb, int64_t vsh, int64_t vst,
-                       const uint8_t* vq, const uint32_t* vsz, const uint16_t* vsink, int capacity,
+                       const uint8_t* vrec, const uint16_t* vsink, int capacity,
                        int n_tokens, const int32_t* seq_lens, const int32_t* idx, int top_k,
                        const float* att_lut,
                        const float* att_qmu, const float* att_slog, float sm_scale,
@@ -434,14 +436,14 @@ hipError_t launch_attn(int n_q_heads, int B, int Hkv, const uint8_t* codes, cons
   const dim3 grid(n_splits, B * Hkv), block(256);
 #define SIKV_ATTN_CASE(GG)                                                                     \
   case GG:                                                                                     \
-    if (vq != nullptr)                                                                         \
+    if (vrec != nullptr)                                                                       \
       return launch_k(KID_ATTN, attn_kernel<GG, true>, grid, block, 0, s, n_q_heads, Hkv,      \
-                      codes, alpha, v, vsb, vsh, vst, vq, vsz, vsink, capacity, n_tokens,       \
+                      codes, alpha, v, vsb, vsh, vst, vrec, vsink, capacity, n_tokens,          \
                       seq_lens, idx,                                                           \
                       top_k, att_lut, att_qmu, att_slog, sm_log2, chunks_per_block, n_splits,  \
                       part_o, part_ml);                                                        \
     return launch_k(KID_ATTN, attn_kernel<GG, false>, grid, block, 0, s, n_q_heads, Hkv,       \
-                    codes, alpha, v, vsb, vsh, vst, vq, vsz, vsink, capacity, n_tokens,       \
+                    codes, alpha, v, vsb, vsh, vst, vrec, vsink, capacity, n_tokens,          \
                     seq_lens, idx,                                                             \
                     top_k, att_lut, att_qmu, att_slog, sm_log2, chunks_per_block, n_splits,    \
                     part_o, part_ml);

@@ -125,6 +125,7 @@ __global__ __launch_bounds__(256) void codes_kernel(const uint16_t* __restrict__
                                                     uint8_t* __restrict__ codes,
                                                     float* __restrict__ alpha,
                                                     uint16_t* __restrict__ k_sink,
+                                                    uint8_t* __restrict__ vrec,
                                                     long long* __restrict__ cb_part) {
   __shared__ unsigned long long cbs[CB ? kSub * 16 * 4 : 1];
   __shared__ int cbn[CB ? kSub * 16 : 1];
@@ -160,7 +161,11 @@ __global__ __launch_bounds__(256) void codes_kernel(const uint16_t* __restrict__
       const RowCode rc = encode_row16(w[i], m);
       if (t < t_end) {
         const int64_t row = (int64_t)bh * capacity + t;
-        if ((cg & 3) == 0) *reinterpret_cast<uint32_t*>(codes + row * kCodeBytes + cg) = rc.word;
+        if ((cg & 3) == 0) {
+          *reinterpret_cast<uint32_t*>(codes + row * kCodeBytes + cg) = rc.word;
+          if (vrec != nullptr)
+            *reinterpret_cast<uint32_t*>(vrec + row * kVRecBytes + kVRecCode + cg) = rc.word;
+        }
         if (cg == 0) alpha[row] = rc.alpha;
         if (t < kSink)
           *reinterpret_cast<uint4*>(k_sink + ((int64_t)bh * kSink + t) * kD + cg * 8) = w[i];
@@ -194,8 +199,7 @@ __global__ __launch_bounds__(256) void codes_kernel(const uint16_t* __restrict__
 __global__ __launch_bounds__(256) void vcodes_kernel(const uint16_t* __restrict__ v, int64_t sb,
                                                      int64_t sh, int64_t st, int Hkv, int t_begin,
                                                      int t_end, int capacity,
-                                                     uint8_t* __restrict__ vq,
-                                                     uint32_t* __restrict__ vsz,
+                                                     uint8_t* __restrict__ vrec,
                                                      uint16_t* __restrict__ v_sink) {
   const int bh = blockIdx.y, b = bh / Hkv, h = bh - b * Hkv;
   const int tid = threadIdx.x, cg = tid & 15, rs = tid >> 4;
@@ -215,8 +219,9 @@ __global__ __launch_bounds__(256) void vcodes_kernel(const uint16_t* __restrict_
     const uint32_t pair = rc.bits | (__shfl_down(rc.bits, 1, 16) << 16);
     if (t < t_end) {
       const int64_t row = (int64_t)bh * capacity + t;
-      if ((cg & 1) == 0) *reinterpret_cast<uint32_t*>(vq + row * kVCodeBytes + 2 * cg) = pair;
-      if ((cg & 3) == 0) vsz[row * 4 + (cg >> 2)] = rc.sz;
+      uint8_t* rec = vrec + row * kVRecBytes;
+      if ((cg & 1) == 0) *reinterpret_cast<uint32_t*>(rec + 2 * cg) = pair;
+      if ((cg & 3) == 0) *reinterpret_cast<uint32_t*>(rec + kVRecSz + cg) = rc.sz;
       if (t < kSink)
         *reinterpret_cast<uint4*>(v_sink + ((int64_t)bh * kSink + t) * kD + cg * 8) = w[i];
     }
@@ -353,27 +358,28 @@ hipError_t launch_mu_final(const float* partial, int BH, int nblk, int n_tokens,
 
 hipError_t launch_codes(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
                         int t_begin, int t_end, int capacity, const float* mu, uint8_t* codes,
-                        float* alpha, uint16_t* k_sink, hipStream_t s) {
+                        float* alpha, uint16_t* k_sink, uint8_t* vrec, hipStream_t s) {
   const int tiles = (t_end - t_begin + 127) / 128;
   return launch_k(KID_CODES, codes_kernel<false>, dim3(tiles, B * Hkv), dim3(256), 0, s, k, sb,
-                  sh, st, Hkv, t_begin, t_end, capacity, 1, mu, codes, alpha, k_sink,
+                  sh, st, Hkv, t_begin, t_end, capacity, 1, mu, codes, alpha, k_sink, vrec,
                   (long long*)nullptr);
 }
 
 hipError_t launch_vcodes(const uint16_t* v, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
-                         int t_begin, int t_end, int capacity, uint8_t* vq, uint32_t* vsz,
+                         int t_begin, int t_end, int capacity, uint8_t* vrec,
                          uint16_t* v_sink, hipStream_t s) {
   const int tiles = (t_end - t_begin + 127) / 128;
   return launch_k(KID_VCODES, vcodes_kernel, dim3(tiles, B * Hkv), dim3(256), 0, s, v, sb, sh, st,
-                  Hkv, t_begin, t_end, capacity, vq, vsz, v_sink);
+                  Hkv, t_begin, t_end, capacity, vrec, v_sink);
 }
 
 hipError_t launch_codes_cb(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
                            int n_tokens, int capacity, const float* mu, uint8_t* codes,
-                           float* alpha, uint16_t* k_sink, long long* cb_part, hipStream_t s) {
+                           float* alpha, uint16_t* k_sink, uint8_t* vrec, long long* cb_part,
+                           hipStream_t s) {
   return launch_k(KID_CODES, codes_kernel<true>, dim3(cb_blocks(n_tokens), B * Hkv), dim3(256), 0,
                   s, k, sb, sh, st, Hkv, 0, n_tokens, capacity, kCbTiles, mu, codes, alpha, k_sink,
-                  cb_part);
+                  vrec, cb_part);
 }
 
 hipError_t launch_cb_final(const long long* cb_part, int BH, int nblk, float* codebook,

@@ -352,7 +352,7 @@ __global__ __launch_bounds__(1024) void prep_kernel(
     uint8_t* __restrict__ codes, float* __restrict__ alpha, int capacity, int n_tokens,
     const uint16_t* __restrict__ k_sink, const uint16_t* __restrict__ k_new, int64_t ksb,
     int64_t ksh, const uint16_t* __restrict__ v_new, int64_t vnsb, int64_t vnsh,
-    uint8_t* __restrict__ vq, uint32_t* __restrict__ vsz,
+    uint8_t* __restrict__ vrec,
     const float* __restrict__ codebook, int top_k, int mode, const int32_t* __restrict__ seq_lens,
     int* __restrict__ sel_lut, float* __restrict__ sel_inv, float* __restrict__ att_lut,
     float* __restrict__ att_qmu, float* __restrict__ att_slog, float* __restrict__ tau,
@@ -430,16 +430,20 @@ __global__ __launch_bounds__(1024) void prep_kernel(
   if (k_new != nullptr && wave == 0) {  // the whole wave runs the 16-lane shuffles
     const RowCode rc = encode_row16(kw, km);
     const int64_t row = row0 + nt - 1;
-    if (tid < 16 && (tid & 3) == 0) *reinterpret_cast<uint32_t*>(codes + row * kCodeBytes + tid) = rc.word;
+    if (tid < 16 && (tid & 3) == 0) {
+      *reinterpret_cast<uint32_t*>(codes + row * kCodeBytes + tid) = rc.word;
+      if (vrec != nullptr)
+        *reinterpret_cast<uint32_t*>(vrec + row * kVRecBytes + kVRecCode + tid) = rc.word;
+    }
     if (tid == 0) alpha[row] = rc.alpha;
   }
   if (v_new != nullptr && wave == 1) {  // the whole wave runs the 4-lane shuffles
     const VRowCode rc = quantize_vrow16(vw);
     const uint32_t pair = rc.bits | (__shfl_down(rc.bits, 1, 16) << 16);
-    const int cg = lane, row = nt - 1;
-    if (cg < 16 && (cg & 1) == 0)
-      *reinterpret_cast<uint32_t*>(vq + (row0 + row) * kVCodeBytes + 2 * cg) = pair;
-    if (cg < 16 && (cg & 3) == 0) vsz[(row0 + row) * 4 + (cg >> 2)] = rc.sz;
+    const int cg = lane;
+    uint8_t* rec = vrec + (row0 + nt - 1) * kVRecBytes;
+    if (cg < 16 && (cg & 1) == 0) *reinterpret_cast<uint32_t*>(rec + 2 * cg) = pair;
+    if (cg < 16 && (cg & 3) == 0) *reinterpret_cast<uint32_t*>(rec + kVRecSz + cg) = rc.sz;
   }
   __syncthreads();
 
@@ -807,13 +811,13 @@ __global__ __launch_bounds__(1024) void select_kernel(
 hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const float* mu,
                        uint8_t* codes, float* alpha, int capacity, int n_tokens,
                        const uint16_t* k_sink, const uint16_t* k_new, int64_t ksb, int64_t ksh,
-                       const uint16_t* v_new, int64_t vnsb, int64_t vnsh, uint8_t* vq,
-                       uint32_t* vsz, const float* codebook, int top_k, int mode, int* sel_lut,
+                       const uint16_t* v_new, int64_t vnsb, int64_t vnsh, uint8_t* vrec,
+                       const float* codebook, int top_k, int mode, int* sel_lut,
                        float* sel_inv, float* att_lut, float* att_qmu, float* att_slog,
                        float* tau, float* bin_scale, const int32_t* seq_lens, hipStream_t s) {
   return launch_k(KID_PREP, prep_kernel, dim3(B * Hkv), dim3(1024), 0, s, q, n_q_heads, Hkv,
                   n_q_heads / Hkv, mu, codes, alpha, capacity, n_tokens, k_sink, k_new, ksb, ksh,
-                  v_new, vnsb, vnsh, vq, vsz, codebook, top_k, mode, seq_lens, sel_lut, sel_inv,
+                  v_new, vnsb, vnsh, vrec, codebook, top_k, mode, seq_lens, sel_lut, sel_inv,
                   att_lut, att_qmu, att_slog, tau, bin_scale);
 }
 

@@ -17,7 +17,13 @@ namespace sikv {
 constexpr int kD = 128;          // head dim
 constexpr int kSink = 64;        // full-precision sink tokens (§2.1 item 3)
 constexpr int kCodeBytes = 16;   // 1 bit per channel
-constexpr int kVCodeBytes = 32;  // 2-bit value codes per token
+// Quantised values: one 64-byte record per token row: its 2-bit value codes
+// (32 B), the (scale, zero) fp16 words of its 4 channel groups (16 B) and a
+// copy of its 16-byte key code, so that the attention fetches one record (plus
+// the scale) per attended token instead of four scattered pieces.
+constexpr int kVRecBytes = 64;
+constexpr int kVRecSz = 32;    // offset of the 4 (scale, zero) words
+constexpr int kVRecCode = 48;  // offset of the key code copy
 constexpr int kSub = 32;         // 4-dim sub-vectors per key (§2.1 item 1)
 constexpr int kLut = kSub * 16;  // table entries per query
 constexpr int kMaxGroup = 8;
@@ -233,13 +239,14 @@ hipError_t launch_mu_partial(const uint16_t* k, int64_t sb, int64_t sh, int64_t 
                              int n_tokens, float* partial, int nblk, hipStream_t s);
 hipError_t launch_mu_final(const float* partial, int BH, int nblk, int n_tokens, float* mu,
                            hipStream_t s);
+// vrec (may be null): value records, whose key code copy is written too.
 hipError_t launch_codes(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
                         int t_begin, int t_end, int capacity, const float* mu, uint8_t* codes,
-                        float* alpha, uint16_t* k_sink, hipStream_t s);
-// 2-bit value codes of rows t_begin..t_end-1 (quantize_vrow16): vq [B*Hkv][cap][32],
-// vsz [B*Hkv][cap][4] words; rows below 64 are also copied to v_sink.
+                        float* alpha, uint16_t* k_sink, uint8_t* vrec, hipStream_t s);
+// 2-bit value codes of rows t_begin..t_end-1 (quantize_vrow16) into bytes 0..47 of
+// their records vrec [B*Hkv][cap][64]; rows below 64 are also copied to v_sink.
 hipError_t launch_vcodes(const uint16_t* v, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
-                         int t_begin, int t_end, int capacity, uint8_t* vq, uint32_t* vsz,
+                         int t_begin, int t_end, int capacity, uint8_t* vrec,
                          uint16_t* v_sink, hipStream_t s);
 // Prefill codes with the codebook statistics: like launch_codes over [0, n_tokens),
 // plus, per block of kCbTiles x 128 tokens, the fixed-point sums of k~/alpha and
@@ -251,7 +258,8 @@ constexpr int kCbFracBits = 24;
 inline int cb_blocks(int n_tokens) { return (n_tokens + 128 * kCbTiles - 1) / (128 * kCbTiles); }
 hipError_t launch_codes_cb(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
                            int n_tokens, int capacity, const float* mu, uint8_t* codes,
-                           float* alpha, uint16_t* k_sink, long long* cb_part, hipStream_t s);
+                           float* alpha, uint16_t* k_sink, uint8_t* vrec, long long* cb_part,
+                           hipStream_t s);
 // Codebook from the block statistics: centre = fl32((sum * 2^-24) / count) in
 // fp64; an empty cluster gets the sign vertex (keep = 0) or keeps the centre
 // already in codebook (keep = 1).  codebook [B*Hkv][32][16][4].
@@ -279,13 +287,13 @@ hipError_t launch_kmeans_assign(const uint16_t* k, int64_t sb, int64_t sh, int64
 // k_new[b*ksb + h*ksh + c]; the kernel first encodes it into codes / alpha
 // (append with the frozen mean, bit-identical to launch_codes) and leaves that
 // token out of its sample.  v_new (may be null): that token's bf16 value row,
-// quantised into vq / vsz (launch_vcodes layout).  bin_scale [B*Hkv]: width of the select kernel's
+// quantised into its value record (launch_vcodes layout; the key code copy too).  bin_scale [B*Hkv]: width of the select kernel's
 // score bins (2048 bins from tau to the sample maximum; 0 when not sampled).
 hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const float* mu,
                        uint8_t* codes, float* alpha, int capacity, int n_tokens,
                        const uint16_t* k_sink, const uint16_t* k_new, int64_t ksb, int64_t ksh,
-                       const uint16_t* v_new, int64_t vnsb, int64_t vnsh, uint8_t* vq,
-                       uint32_t* vsz, const float* codebook, int top_k, int mode, int* sel_lut,
+                       const uint16_t* v_new, int64_t vnsb, int64_t vnsh, uint8_t* vrec,
+                       const float* codebook, int top_k, int mode, int* sel_lut,
                        float* sel_inv, float* att_lut, float* att_qmu, float* att_slog,
                        float* tau, float* bin_scale, const int32_t* seq_lens, hipStream_t s);
 hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha, int capacity,
@@ -306,11 +314,11 @@ hipError_t launch_select(int B, int Hkv, const uint8_t* codes, const float* alph
 // (max, sum, o) partial per query head.
 constexpr int kAttnChunk = 32;
 constexpr int kAttnMaxCpb = 64;  // chunks per block at most (the block's positions sit in LDS)
-// vq (may be null): quantised values (vq, vsz: launch_vcodes; vsink [B*Hkv][64][128]
-// bf16) replace the bf16 V rows.
+// vrec (may be null): quantised values (records as launch_vcodes, key code copy
+// included; vsink [B*Hkv][64][128] bf16) replace the bf16 V rows and the codes.
 hipError_t launch_attn(int n_q_heads, int B, int Hkv, const uint8_t* codes, const float* alpha,
                        const uint16_t* v, int64_t vsb, int64_t vsh, int64_t vst,
-                       const uint8_t* vq, const uint32_t* vsz, const uint16_t* vsink, int capacity,
+                       const uint8_t* vrec, const uint16_t* vsink, int capacity,
                        int n_tokens, const int32_t* seq_lens, const int32_t* idx, int top_k,
                        const float* att_lut,
                        const float* att_qmu, const float* att_slog, float sm_scale,

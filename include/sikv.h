@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define SIKV_ABI_VERSION 4
+#define SIKV_ABI_VERSION 5
 #define SIKV_HEAD_DIM 128
 #define SIKV_N_SINK 64
 #define SIKV_MAX_GROUP 8
@@ -86,15 +86,19 @@ typedef int32_t sikv_status;
  *          recompute_mu = 1 writes them, every scoring and attention call
  *          uses them (key_t = mu + alpha_t * centre of its cluster, per
  *          sub-vector).  Appended tokens keep the prefill centres.
- *   vq, vsz, v_sink  NULL: attention reads the bf16 V cache `v`.  Else (all three
- *          set, 16-byte aligned) the values are kept 2-bit (the pages' 2-bit
- *          setting, read as a per-token value scheme; the 64 sinks stay full
- *          precision, §2.1 item 3): vq uint8 [B][Hkv][capacity][32] (channel c at
- *          byte c/4, bits 2*(c%4)), vsz uint32 [B][Hkv][capacity][4] (per group of
- *          32 channels: fp16 scale in the low half, fp16 zero point in the high
- *          half), v_sink bf16 [B][Hkv][64][128]; written by sikv_encode_v (or the
- *          fused step); `v` is then not read and may be NULL.  Value of channel c:
- *          zero + code * scale of its group.
+ *   vrec, v_sink  NULL: attention reads the bf16 V cache `v`.  Else (both set;
+ *          vrec 64-byte, v_sink 16-byte aligned) the values are kept 2-bit (the
+ *          pages' 2-bit setting, read as a per-token value scheme; the 64 sinks
+ *          stay full precision, §2.1 item 3) in one 64-byte record per token,
+ *          vrec uint8 [B][Hkv][capacity][64]: bytes 0..31 the value codes
+ *          (channel c at byte c/4, bits 2*(c%4)), bytes 32..47 four uint32
+ *          words, one per group of 32 channels (fp16 scale in the low half, fp16
+ *          zero point in the high half), bytes 48..63 a copy of the token's
+ *          16-byte key code; v_sink bf16 [B][Hkv][64][128].  sikv_encode_v (or
+ *          the fused step) writes bytes 0..47 and v_sink, sikv_encode (or the
+ *          fused step) also writes the key code copy; `v` is then not read and
+ *          may be NULL.  Value of channel c: zero + code * scale of its group.
+ *          One record holds all an attended token needs but its scale alpha.
  *   seq_lens  NULL: every sequence has n_tokens tokens.  Else (ragged batch, a
  *          device array int32 [B], 4-byte aligned, read by the kernels) sequence
  *          b has seq_lens[b] tokens and n_tokens is the longest (it sizes grids
@@ -126,8 +130,7 @@ typedef struct sikv_cache_desc {
   int64_t v_stride_h;
   int64_t v_stride_t;
   float *codebook;
-  uint8_t *vq;
-  uint32_t *vsz;
+  uint8_t *vrec;
   uint16_t *v_sink;
   const int32_t *seq_lens;
 } sikv_cache_desc;
@@ -161,8 +164,8 @@ sikv_status sikv_encode(const sikv_cache_desc *cache, const uint16_t *k, int64_t
                         int32_t recompute_mu, void *ws, size_t ws_bytes, void *stream);
 
 /*
- * sikv_encode_v - 2-bit value codes of tokens t_begin..t_end-1 (requires vq, vsz
- * and v_sink in the descriptor).  Per token and group of 32 channels: z = min
+ * sikv_encode_v - 2-bit value codes of tokens t_begin..t_end-1 (requires vrec
+ * and v_sink in the descriptor), bytes 0..47 of their records.  Per token and group of 32 channels: z = min
  * (+0 when zero), s = fl32((max - z) / 3), both rounded to fp16 (nearest even);
  * code = clamp(rint(fl32(fl32(v - z16) / s16)), 0, 3), 0 when s16 = 0.  Rows
  * below 64 are also copied whole to v_sink.  Stateless per token: the same call

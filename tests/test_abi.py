@@ -38,11 +38,11 @@ def test_header_functions_are_exported_and_declared():
 
 def test_abi_version_and_desc_layout():
     assert lib.sikv_abi_version() == _abi.ABI_VERSION
-    assert lib.sikv_desc_size() == C.sizeof(_abi.CacheDesc) == 128
+    assert lib.sikv_desc_size() == C.sizeof(_abi.CacheDesc) == 120
     offs = {f[0]: getattr(_abi.CacheDesc, f[0]).offset for f in _abi.CacheDesc._fields_}
     assert offs["codes"] == 24 and offs["v"] == 56 and offs["v_stride_t"] == 80
-    assert offs["codebook"] == 88 and offs["vq"] == 96 and offs["v_sink"] == 112
-    assert offs["seq_lens"] == 120
+    assert offs["codebook"] == 88 and offs["vrec"] == 96 and offs["v_sink"] == 104
+    assert offs["seq_lens"] == 112
 
 
 def test_status_strings():
@@ -57,7 +57,7 @@ def desc(**kw):
     d.batch, d.n_kv_heads, d.head_dim, d.capacity, d.n_tokens, d.n_sink = 2, 2, 128, 1000, 900, 64
     d.codes, d.alpha, d.mu, d.k_sink = FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000
     d.v, d.v_stride_b, d.v_stride_h, d.v_stride_t = FAKE + 0x400000, 2 * 1000 * 128, 1000 * 128, 128
-    d.codebook = d.vq = d.vsz = d.v_sink = d.seq_lens = None
+    d.codebook = d.vrec = d.v_sink = d.seq_lens = None
     for k, v in kw.items():
         setattr(d, k, v)
     return d
@@ -99,7 +99,7 @@ def test_workspace_sizes():
     ("codes", FAKE + 8, INVALID),
     ("mu", FAKE + 4, INVALID),
     ("alpha", FAKE + 2, INVALID),
-    ("vq", FAKE + 0x600000, INVALID),                               # vsz, v_sink missing
+    ("vrec", FAKE + 0x600000, INVALID),                             # v_sink missing
     ("v_sink", FAKE + 0x600000, INVALID),
     ("seq_lens", FAKE + 2, INVALID),                                # misaligned
 ])
@@ -164,7 +164,7 @@ def test_append_decode_validation():
 
 def test_quantised_value_validation():
     f = C.c_float
-    qd = desc(v=None, vq=FAKE + 0x600000, vsz=FAKE + 0x700000, v_sink=FAKE + 0x800000)
+    qd = desc(v=None, vrec=FAKE + 0x600000, v_sink=FAKE + 0x800000)
     d = desc()
     need = lib.sikv_workspace_bytes(3, C.byref(qd), 4, 16)
     assert need > 0
@@ -186,7 +186,7 @@ def test_quantised_value_validation():
     assert ev(C.byref(qd), FAKE, 0, 0, 128, -1, 10, None) == INVALID
     assert ev(C.byref(qd), FAKE, 0, 0, 128, 0, 1001, None) == INVALID       # > capacity
     assert lib.sikv_encode_v(None, FAKE, 0, 0, 128, 0, 10, None) == INVALID
-    misal = desc(v=None, vq=FAKE + 0x600004, vsz=FAKE + 0x700000, v_sink=FAKE + 0x800000)
+    misal = desc(v=None, vrec=FAKE + 0x600010, v_sink=FAKE + 0x800000)         # not 64-aligned
     assert score(misal) == INVALID
 
 

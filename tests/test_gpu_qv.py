@@ -72,6 +72,9 @@ def test_quantised_value_parity(name, w):
     assert np.array_equal(gq, oq), f"{name}: value codes differ"
     assert np.array_equal(gsz, osz), f"{name}: scale/zero words differ"
     assert np.array_equal(host_u16(cache.v_sink), Vh[:, :, :64])
+    # each value record also carries its token's key code
+    rec = cache.vrec[:, :, :N].cpu().numpy()
+    assert np.array_equal(rec[..., 48:64], cache.codes[:, :, :N].cpu().numpy())
 
     oc = [[oracle_head(d["K"][b, h], N) for h in range(w.n_kv_heads)] for b in range(w.batch)]
     oidx = np.zeros((w.batch, w.n_kv_heads, w.top_k), np.int32)
@@ -120,9 +123,11 @@ def test_quantised_value_fused_append():
                 out = sk.sikv_decode_step(cache, q, w.top_k, SM, idx_out=idx)
             torch.cuda.synchronize()
             vq, vsz = _vq_host(cache, N)
+            rec = cache.vrec[:, :, N - 1].cpu().numpy()
             res.append((vq[:, :, N - 1], vsz[:, :, N - 1], idx.cpu().numpy(),
-                        out.cpu().numpy().view(np.uint32)))
-        for a, b, what in zip(res[0], res[1], ("vq", "vsz", "idx", "out")):
+                        out.cpu().numpy().view(np.uint32), rec))
+        assert np.array_equal(res[1][4][..., 48:64], cache.codes[:, :, N - 1].cpu().numpy())
+        for a, b, what in zip(res[0], res[1], ("vq", "vsz", "idx", "out", "record")):
             assert np.array_equal(a, b), f"{w.name}: {what} differs"
         oq, osz = O.quantize_v(d["V"][:, :, N - 1:N])
         assert np.array_equal(res[1][0], oq[:, :, 0])
