@@ -47,6 +47,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-dense", action="store_true", help="skip the dense bf16 comparator")
     p.add_argument("--no-qv", action="store_true", help="skip the 2-bit value variant")
+    p.add_argument("--no-paged", action="store_true", help="skip the paged-cache variant")
     p.add_argument("--no-prefill", action="store_true",
                    help="skip timing the prefill compression against torch's fused prefill "
                         "attention of the same shape")
@@ -544,6 +545,55 @@ def main():
             {k: round(v, 2) for k, v in qv_kern_us.items()})
         del qcaches
 
+    # the same step on paged caches: 256-token pool pages in a shuffled order
+    paged_us = paged_kern_us = None
+    if not args.no_paged:
+        P = 256
+        pps = (N + P - 1) // P
+        n_pages = w.batch * pps
+        gperm = torch.Generator(device="cpu")
+        gperm.manual_seed(7)
+        pcaches = []
+        for layer in range(L):
+            perm = torch.randperm(n_pages, generator=gperm).to(torch.int32)
+            table = perm.view(w.batch, pps).to(dev)
+            Vl = caches[layer].v
+            pool = torch.empty((n_pages, w.n_kv_heads, P, 128), dtype=torch.bfloat16, device=dev)
+            pool[perm.to(dev).long()] = Vl.view(w.batch, w.n_kv_heads, pps, P, 128).permute(
+                0, 2, 1, 3, 4).reshape(n_pages, w.n_kv_heads, P, 128)
+            c = sk.Cache.paged(w.batch, w.n_kv_heads, P, n_pages, table, device=dev, v=pool)
+            c.n_tokens = N - 1
+            sk.sikv_encode(c, K[:, :, :N - 1])
+            pcaches.append(c)
+        torch.cuda.synchronize()
+
+        def pstep(layer):
+            c = pcaches[layer]
+            c.n_tokens = N - 1
+            sk.sikv_append_decode_step(c, k_new, q_all, w.top_k, sm, idx_out=idxs[layer],
+                                       out=outs[layer])
+
+        for i in range(max(args.warmup, L)):
+            pstep(i % L)
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(args.steps):
+            pstep(i % L)
+        ev1.record()
+        torch.cuda.synchronize()
+        paged_us = ev0.elapsed_time(ev1) * 1e3 / args.steps
+        sk.timing_reset()
+        sk.timing_enable(True)
+        for i in range(args.steps):
+            pstep(i % L)
+        torch.cuda.synchronize()
+        pt = sk.timing_read()
+        sk.timing_enable(False)
+        paged_kern_us = {name: 1e3 * tot / n for name, (n, tot) in pt.items() if n}
+        log(f"paged (256-token pages): {paged_us:.1f} us/step, kernel avg us:",
+            {k: round(v, 2) for k, v in paged_kern_us.items()})
+        del pcaches
+
     # dense bf16 comparator over the same (uncompressed) cache
     dense_us = dense_torch_us = None
     if not args.no_dense:
@@ -640,6 +690,9 @@ def main():
     }
     if prefill is not None:
         report["prefill_overhead"] = prefill
+    if paged_us is not None:
+        report["paged"] = {"page_size": 256, "page_order": "shuffled", "decode_step_us": paged_us,
+                           "kernel_avg_us": paged_kern_us}
     if km20_us is not None:
         score_us = kern_us.get("score", 0.0)
         report["module_speedups"] = {

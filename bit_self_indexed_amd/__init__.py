@@ -137,7 +137,34 @@ class Cache:
                                       device=dev)
         self.v = v
         self.seq_lens = None  # ragged batch: int32 [B] on the device (see view())
+        self.page_table = None  # paged pool (see paged())
+        self.page_size = self.pages_per_seq = self.n_pages = 0
         self.ws = Workspace(dev)
+
+    @classmethod
+    def paged(cls, batch: int, n_kv_heads: int, page_size: int, n_pages: int,
+              page_table: torch.Tensor, device="cuda", v: torch.Tensor | None = None,
+              codebook: bool = False, quant_v: bool = False) -> "Cache":
+        """A cache whose per-token arrays live in a pool of n_pages pages of page_size
+        tokens (all KV heads per page): codes [n_pages,Hkv,P,16], alpha [n_pages,Hkv,P],
+        vrec [n_pages,Hkv,P,64]; page_table int32 [batch, pages_per_seq] on the device
+        maps each sequence's logical pages to pool pages; ``v`` (bf16 values) is a pool
+        [n_pages,Hkv,P,128] addressed the same way.  Means, sinks and codebooks stay per
+        sequence."""
+        dev = torch.device(device)
+        pps = int(page_table.shape[1])
+        c = cls(batch, n_kv_heads, 1, device=dev, v=v, codebook=codebook, quant_v=False)
+        c.capacity = pps * page_size
+        P = page_size
+        c.codes = torch.zeros((n_pages, n_kv_heads, P, 16), dtype=torch.uint8, device=dev)
+        c.alpha = torch.zeros((n_pages, n_kv_heads, P), dtype=torch.float32, device=dev)
+        if quant_v:
+            c.vrec = torch.zeros((n_pages, n_kv_heads, P, 64), dtype=torch.uint8, device=dev)
+            c.v_sink = torch.zeros((batch, n_kv_heads, N_SINK, HEAD_DIM), dtype=torch.bfloat16,
+                                   device=dev)
+        c.page_table = page_table
+        c.page_size, c.pages_per_seq, c.n_pages = P, pps, n_pages
+        return c
 
     @property
     def device(self):
@@ -158,6 +185,10 @@ class Cache:
         d.codebook = self.codebook.data_ptr() if self.codebook is not None else None
         d.vrec, d.v_sink = _ptr(self.vrec), _ptr(self.v_sink)
         d.seq_lens = _ptr(self.seq_lens)
+        if self.page_table is not None:
+            d.page_table = self.page_table.data_ptr()
+            d.page_size, d.pages_per_seq, d.n_pages = (self.page_size, self.pages_per_seq,
+                                                       self.n_pages)
         return d
 
     @property
@@ -174,10 +205,14 @@ class Cache:
         c = Cache.__new__(Cache)
         c.batch, c.n_kv_heads, c.capacity = 1, self.n_kv_heads, self.capacity
         c.n_tokens = self.n_tokens
+        paged = self.page_table is not None
+        pooled = ("codes", "alpha", "vrec", "v") if paged else ()
         for name in ("codes", "alpha", "mu", "k_sink", "codebook", "vrec", "v_sink", "v"):
             t = getattr(self, name)
-            setattr(c, name, None if t is None else t[b:b + 1])
+            setattr(c, name, None if t is None else (t if name in pooled else t[b:b + 1]))
         c.seq_lens = None
+        c.page_table = self.page_table[b:b + 1] if paged else None
+        c.page_size, c.pages_per_seq, c.n_pages = self.page_size, self.pages_per_seq, self.n_pages
         c.ws = self.ws
         return c
 

@@ -4,7 +4,7 @@ from __future__ import annotations
 
 import ctypes as C
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 STATUS = {
     0: "SIKV_OK",
@@ -35,6 +35,11 @@ class CacheDesc(C.Structure):
         ("vrec", C.c_void_p),
         ("v_sink", C.c_void_p),
         ("seq_lens", C.c_void_p),
+        ("page_table", C.c_void_p),
+        ("page_size", C.c_int32),
+        ("pages_per_seq", C.c_int32),
+        ("n_pages", C.c_int32),
+        ("reserved", C.c_int32),
     ]
 
 

@@ -136,6 +136,17 @@ bool plan_decode(const sikv_cache_desc* c, int n_q_heads, int top_k, DecodePlan*
 }
 
 // ------------------------------------------------------------------ validation
+// Token-row addressing of the cache's per-token arrays (contiguous or paged).
+RowMap rows_of(const sikv_cache_desc* c) {
+  RowMap m;
+  m.capacity = c->capacity;
+  m.table = c->page_table;
+  m.lg_page = c->page_table != nullptr ? __builtin_ctz((unsigned)c->page_size) : 0;
+  m.pps = c->pages_per_seq;
+  m.Hkv = c->n_kv_heads;
+  return m;
+}
+
 sikv_status check_desc(const sikv_cache_desc* c) {
   if (c == nullptr) return SIKV_ERR_INVALID_ARG;
   if (c->head_dim != kD || c->n_sink != kSink) return SIKV_ERR_UNSUPPORTED;
@@ -146,6 +157,15 @@ sikv_status check_desc(const sikv_cache_desc* c) {
   if (misaligned(c->codes, 16) || misaligned(c->alpha, 4) || misaligned(c->mu, 16) ||
       misaligned(c->k_sink, 16) || misaligned(c->codebook, 16) || misaligned(c->seq_lens, 4))
     return SIKV_ERR_INVALID_ARG;
+  if (c->page_table != nullptr) {
+    // pages of a power-of-two size >= 256 tokens holding all KV heads; the pool
+    // row index fits in int32 (the attention stages rows in LDS as int32)
+    const int64_t P = c->page_size;
+    if (P < 256 || (P & (P - 1)) != 0 || c->pages_per_seq < 1 || c->n_pages < 1 ||
+        misaligned(c->page_table, 4) || (int64_t)c->pages_per_seq * P != c->capacity ||
+        (int64_t)c->n_pages * c->n_kv_heads * P > 0x7fffffffLL)
+      return SIKV_ERR_INVALID_ARG;
+  }
   if ((c->vrec != nullptr || c->v_sink != nullptr) &&
       (!c->vrec || !c->v_sink || misaligned(c->vrec, 64) || misaligned(c->v_sink, 16)))
     return SIKV_ERR_INVALID_ARG;
@@ -159,6 +179,10 @@ bool bad_strides(int64_t sb, int64_t sh, int64_t st) {
 sikv_status check_v(const sikv_cache_desc* c) {
   if (c->vrec != nullptr) return SIKV_OK;  // quantised values (checked in check_desc)
   if (c->v == nullptr || misaligned(c->v, 16) || bad_strides(c->v_stride_b, c->v_stride_h, c->v_stride_t))
+    return SIKV_ERR_INVALID_ARG;
+  if (c->page_table != nullptr &&  // paged: the V pool [n_pages][Hkv][page_size][128], dense
+      (c->v_stride_t != kD || c->v_stride_h != (int64_t)c->page_size * kD ||
+       c->v_stride_b != (int64_t)c->n_kv_heads * c->page_size * kD))
     return SIKV_ERR_INVALID_ARG;
   return SIKV_OK;
 }
@@ -206,15 +230,15 @@ sikv_status run_score_topk(const sikv_cache_desc* c, const uint16_t* q, int n_q_
   int32_t* tab = at<int32_t>(ws, sp.off_tab);
   float* inv = at<float>(ws, sp.off_inv);
   const int mode = g_force_exact.load(std::memory_order_relaxed) ? 2 : 1;
-  SIKV_TRY(launch_prep(q, n_q_heads, B, Hkv, c->mu, c->codes, c->alpha, c->capacity, c->n_tokens,
+  SIKV_TRY(launch_prep(q, n_q_heads, B, Hkv, c->mu, c->codes, c->alpha, rows_of(c), c->n_tokens,
                        c->k_sink, k_new, ksb, ksh, v_new, vnsb, vnsh, c->vrec, c->codebook,
                        top_k, mode, tab, inv,
                        at<float>(ws, sp.off_lut), at<float>(ws, sp.off_qmu),
                        at<float>(ws, sp.off_slog), tau, at<float>(ws, sp.off_bin), c->seq_lens,
                        s));
-  SIKV_TRY(launch_score(B, Hkv, c->codes, c->alpha, c->capacity, c->n_tokens, c->seq_lens, tab,
+  SIKV_TRY(launch_score(B, Hkv, c->codes, c->alpha, rows_of(c), c->n_tokens, c->seq_lens, tab,
                         inv, tau, sp.chunk, sp.n_chunks, ckey, ct, cnt, scores_opt, s));
-  SIKV_TRY(launch_select(B, Hkv, c->codes, c->alpha, c->capacity, c->n_tokens, c->seq_lens, tab,
+  SIKV_TRY(launch_select(B, Hkv, c->codes, c->alpha, rows_of(c), c->n_tokens, c->seq_lens, tab,
                          inv, top_k, sp.chunk, sp.n_chunks, ckey, ct, cnt, tau,
                          at<float>(ws, sp.off_bin), pkey, pt, idx, s));
   return SIKV_OK;
@@ -230,14 +254,14 @@ sikv_status run_attn(const sikv_cache_desc* c, const uint16_t* q, int n_q_heads,
   AttnTables own{at<float>(ws, ap.off_lut), at<float>(ws, ap.off_qmu), at<float>(ws, ap.off_slog)};
   if (tab == nullptr) {
     SIKV_TRY(launch_prep(q, n_q_heads, c->batch, c->n_kv_heads, c->mu, c->codes, c->alpha,
-                         c->capacity, c->n_tokens, c->k_sink, nullptr, 0, 0, nullptr, 0, 0,
+                         rows_of(c), c->n_tokens, c->k_sink, nullptr, 0, 0, nullptr, 0, 0,
                          nullptr, c->codebook, top_k, 0, nullptr,
                          nullptr, own.lut, own.qmu, own.slog, nullptr, nullptr, c->seq_lens, s));
     tab = &own;
   }
   SIKV_TRY(launch_attn(n_q_heads, c->batch, c->n_kv_heads, c->codes, c->alpha, c->v,
                        c->v_stride_b, c->v_stride_h, c->v_stride_t, c->vrec, c->v_sink,
-                       c->capacity, c->n_tokens, c->seq_lens, idx, top_k, tab->lut, tab->qmu, tab->slog, sm_scale, ap.cpb, ap.n_splits, po,
+                       rows_of(c), c->n_tokens, c->seq_lens, idx, top_k, tab->lut, tab->qmu, tab->slog, sm_scale, ap.cpb, ap.n_splits, po,
                        pml, s));
   SIKV_TRY(launch_combine(po, pml, c->batch * n_q_heads, ap.n_splits, out, s));
   return SIKV_OK;
@@ -331,14 +355,14 @@ sikv_status sikv_encode(const sikv_cache_desc* c, const uint16_t* k, int64_t k_s
     if (c->codebook != nullptr) {  // codes + codebook statistics in one pass, then the centres
       long long* part = at<long long>(ws, p.off_cb);
       SIKV_TRY(launch_codes_cb(k, k_stride_b, k_stride_h, k_stride_t, c->batch, c->n_kv_heads,
-                               c->n_tokens, c->capacity, c->mu, c->codes, c->alpha, c->k_sink,
+                               c->n_tokens, rows_of(c), c->mu, c->codes, c->alpha, c->k_sink,
                                c->vrec, part, s));
       SIKV_TRY(launch_cb_final(part, c->batch * c->n_kv_heads, p.cb_nblk, c->codebook, s));
       return SIKV_OK;
     }
   }
   SIKV_TRY(launch_codes(k, k_stride_b, k_stride_h, k_stride_t, c->batch, c->n_kv_heads, t_begin,
-                        t_end, c->capacity, c->mu, c->codes, c->alpha, c->k_sink, c->vrec, s));
+                        t_end, rows_of(c), c->mu, c->codes, c->alpha, c->k_sink, c->vrec, s));
   return SIKV_OK;
 }
 
@@ -442,7 +466,7 @@ sikv_status sikv_encode_v(const sikv_cache_desc* c, const uint16_t* v, int64_t v
     return SIKV_ERR_INVALID_ARG;
   if (t_begin < 0 || t_end <= t_begin || t_end > c->capacity) return SIKV_ERR_INVALID_ARG;
   SIKV_TRY(launch_vcodes(v, v_stride_b, v_stride_h, v_stride_t, c->batch, c->n_kv_heads, t_begin,
-                         t_end, c->capacity, c->vrec, c->v_sink,
+                         t_end, rows_of(c), c->vrec, c->v_sink,
                          static_cast<hipStream_t>(stream)));
   return SIKV_OK;
 }
@@ -529,7 +553,7 @@ sikv_status sikv_kmeans_codebook(const sikv_cache_desc* c, const uint16_t* k, in
   const int BH = c->batch * c->n_kv_heads, nblk = cb_blocks(c->n_tokens);
   for (int it = 0; it < n_iter; ++it) {
     SIKV_TRY(launch_kmeans_assign(k, k_stride_b, k_stride_h, k_stride_t, c->batch, c->n_kv_heads,
-                                  c->n_tokens, c->capacity, c->mu, c->alpha,
+                                  c->n_tokens, rows_of(c), c->mu, c->alpha,
                                   it == 0 ? nullptr : c->codebook, part, s));
     SIKV_TRY(launch_cb_final(part, BH, nblk, c->codebook, s, it == 0 ? 0 : 1));
   }

@@ -72,19 +72,21 @@ struct Chunk {
   uint4 v[kRows];
 };
 
-// Issues every load of block-local chunk lc.  sidx holds the block's positions
-// (the sinks' own, entries past the list end repeat its last), so every
-// address is a real row.  A sink chunk reads the sink logits instead of codes.
+// Issues every load of chunk c (block-local lc).  sidx holds the rows of the
+// block's entries, relative to the Src bases (entries past the list end repeat
+// its last), so every address is a real row.  A sink chunk reads the sink
+// logits (and, quantised, the bf16 sink rows) by entry index instead.
 template <int G, bool QV>
-__device__ __forceinline__ void load_chunk(Chunk<G>& x, int lc, bool sink, const int* sidx,
-                                           int lane, const Src& src) {
+__device__ __forceinline__ void load_chunk(Chunk<G>& x, int c, int lc, bool sink,
+                                           const int* sidx, int lane, const Src& src) {
   const int el = lane & 31, half = lane >> 5, grp = lane >> 4, seg = lane & 15;
   const int t = sidx[lc * kAttnChunk + el];
   if (sink) {
     x.code = make_uint4(0u, 0u, 0u, 0u);
     x.a = 0.0f;
 #pragma unroll
-    for (int i = 0; i < (G + 1) / 2; ++i) x.sl[i] = src.slog[min(2 * i + half, G - 1) * kSink + t];
+    for (int i = 0; i < (G + 1) / 2; ++i)
+      x.sl[i] = src.slog[min(2 * i + half, G - 1) * kSink + c * kAttnChunk + el];
   } else {
     // quantised values: the key code copy in the token's value record, which the
     // V loads below fetch anyway
@@ -100,7 +102,7 @@ __device__ __forceinline__ void load_chunk(Chunk<G>& x, int lc, bool sink, const
     if (!QV) {
       x.v[u] = *reinterpret_cast<const uint4*>(src.vb + (int64_t)tu * src.vst);
     } else if (sink) {
-      x.v[u] = *reinterpret_cast<const uint4*>(src.vsk + (int64_t)tu * kD);
+      x.v[u] = *reinterpret_cast<const uint4*>(src.vsk + (int64_t)(c * kAttnChunk + grp + 4 * u) * kD);
     } else {
       const uint8_t* rec = src.vrec + (int64_t)tu * kVRecBytes;
       x.v[u].x = *reinterpret_cast<const uint16_t*>(rec + 2 * seg);
@@ -208,7 +210,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(
     int n_q_heads, int Hkv, const uint8_t* __restrict__ codes, const float* __restrict__ alpha,
     const uint16_t* __restrict__ v, int64_t vsb, int64_t vsh, int64_t vst,
     const uint8_t* __restrict__ vrec,
-    const uint16_t* __restrict__ vsink, int capacity, int n_tokens,
+    const uint16_t* __restrict__ vsink, RowMap rm, int n_tokens,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ idx, int top_k,
     const float* __restrict__ att_lut,
     const float* __restrict__ att_qmu, const float* __restrict__ att_slog, float sm_log2,
@@ -229,14 +231,17 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(
   const int L = kSink + seq_topk(top_k, nt);               // its attended entries
   const int n_chunks = (L + kAttnChunk - 1) / kAttnChunk;
   const int c0 = s * cpb, c_end = min(n_chunks, c0 + cpb);  // may be empty (ragged batch)
-  const int64_t row0 = (int64_t)bh * capacity;
+  // Rows: contiguous, relative to this head's first row (positions); paged,
+  // absolute pool rows (the bf16 V pool then has the rows' layout, vst apart).
+  const bool paged = rm.table != nullptr;
+  const int64_t row0 = paged ? 0 : (int64_t)bh * rm.capacity;
   const int64_t hq0 = (int64_t)b * n_q_heads + (int64_t)h * G;
   const int32_t* ib = idx + (int64_t)bh * top_k;
   Src src;
   src.codes = codes + row0 * kCodeBytes;
   src.alpha = alpha + row0;
   src.slog = att_slog + hq0 * kSink;
-  src.vb = QV ? nullptr : v + (int64_t)b * vsb + (int64_t)h * vsh + seg * 8;
+  src.vb = QV ? nullptr : (paged ? v : v + (int64_t)b * vsb + (int64_t)h * vsh) + seg * 8;
   src.vst = vst;
   src.vrec = QV ? vrec + row0 * kVRecBytes : nullptr;
   src.vsk = QV ? vsink + (int64_t)bh * kSink * kD + seg * 8 : nullptr;
@@ -247,7 +252,8 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(
     const int e0 = c0 * kAttnChunk, ne = (c_end - c0) * kAttnChunk;
     for (int i = tid; i < ne; i += 256) {
       const int e = min(e0 + i, L - 1);
-      sidx[i] = e < kSink ? e : min(max(ib[e - kSink], 0), nt - 1);
+      const int t = e < kSink ? e : min(max(ib[e - kSink], 0), nt - 1);
+      sidx[i] = paged ? (int)rm.row(b, h, t) : t;
     }
     const float4* lsrc = reinterpret_cast<const float4*>(att_lut + hq0 * kLut);
     float4* dst = reinterpret_cast<float4*>(&lutq[0][0]);
@@ -277,17 +283,17 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(
   int c = c0 + wave;
   if (c < c_end && c * kAttnChunk < kSink) {
     Chunk<G> sk;
-    load_chunk<G, QV>(sk, c - c0, true, sidx, lane, src);
+    load_chunk<G, QV>(sk, c, c - c0, true, sidx, lane, src);
     process_chunk<G, QV>(st, sk, true, true, lutq, qmu, sm_log2, pb[wave], lane);
     c += 4;
   }
   if (c < c_end) {
     const int c_last = c + ((c_end - 1 - c) & ~3);
     Chunk<G> nx;
-    load_chunk<G, QV>(nx, c - c0, false, sidx, lane, src);
+    load_chunk<G, QV>(nx, c, c - c0, false, sidx, lane, src);
     for (; c < c_last; c += 4) {
       const Chunk<G> cur = nx;
-      load_chunk<G, QV>(nx, c + 4 - c0, false, sidx, lane, src);
+      load_chunk<G, QV>(nx, c + 4, c + 4 - c0, false, sidx, lane, src);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the chunk's work
       process_chunk<G, QV>(st, cur, false, c * kAttnChunk + el < L, lutq, qmu, sm_log2, pb[wave],
                            lane);
@@ -421,7 +427,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 hipError_t launch_attn(int n_q_heads, int B, int Hkv, const uint8_t* codes, const float* alpha,
                        const uint16_t* v, int64_t vsb, int64_t vsh, int64_t vst,
-                       const uint8_t* vrec, const uint16_t* vsink, int capacity,
+                       const uint8_t* vrec, const uint16_t* vsink, const RowMap& rm,
                        int n_tokens, const int32_t* seq_lens, const int32_t* idx, int top_k,
                        const float* att_lut,
                        const float* att_qmu, const float* att_slog, float sm_scale,
@@ -438,12 +444,12 @@ hipError_t launch_attn(int n_q_heads, int B, int Hkv, const uint8_t* codes, cons
   case GG:                                                                                     \
     if (vrec != nullptr)                                                                       \
       return launch_k(KID_ATTN, attn_kernel<GG, true>, grid, block, 0, s, n_q_heads, Hkv,      \
-                      codes, alpha, v, vsb, vsh, vst, vrec, vsink, capacity, n_tokens,          \
+                      codes, alpha, v, vsb, vsh, vst, vrec, vsink, rm, n_tokens,                \
                       seq_lens, idx,                                                           \
                       top_k, att_lut, att_qmu, att_slog, sm_log2, chunks_per_block, n_splits,  \
                       part_o, part_ml);                                                        \
     return launch_k(KID_ATTN, attn_kernel<GG, false>, grid, block, 0, s, n_q_heads, Hkv,       \
-                    codes, alpha, v, vsb, vsh, vst, vrec, vsink, capacity, n_tokens,          \
+                    codes, alpha, v, vsb, vsh, vst, vrec, vsink, rm, n_tokens,                \
                     seq_lens, idx,                                                             \
                     top_k, att_lut, att_qmu, att_slog, sm_log2, chunks_per_block, n_splits,    \
                     part_o, part_ml);

@@ -120,7 +120,7 @@ __global__ __launch_bounds__(128) void mu_final_kernel(const float* __restrict__
 template <bool CB>
 __global__ __launch_bounds__(256) void codes_kernel(const uint16_t* __restrict__ k, int64_t sb,
                                                     int64_t sh, int64_t st, int Hkv, int t_begin,
-                                                    int t_end, int capacity, int tpb,
+                                                    int t_end, RowMap rm, int tpb,
                                                     const float* __restrict__ mu,
                                                     uint8_t* __restrict__ codes,
                                                     float* __restrict__ alpha,
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void codes_kernel(const uint16_t* __restrict__
       const int t = tb + i * 16 + rs;
       const RowCode rc = encode_row16(w[i], m);
       if (t < t_end) {
-        const int64_t row = (int64_t)bh * capacity + t;
+        const int64_t row = rm.row(b, h, t);
         if ((cg & 3) == 0) {
           *reinterpret_cast<uint32_t*>(codes + row * kCodeBytes + cg) = rc.word;
           if (vrec != nullptr)
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(256) void codes_kernel(const uint16_t* __restrict__
 // (scale, zero) word; rows below 64 are also kept whole in v_sink.
 __global__ __launch_bounds__(256) void vcodes_kernel(const uint16_t* __restrict__ v, int64_t sb,
                                                      int64_t sh, int64_t st, int Hkv, int t_begin,
-                                                     int t_end, int capacity,
+                                                     int t_end, RowMap rm,
                                                      uint8_t* __restrict__ vrec,
                                                      uint16_t* __restrict__ v_sink) {
   const int bh = blockIdx.y, b = bh / Hkv, h = bh - b * Hkv;
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(256) void vcodes_kernel(const uint16_t* __restrict_
     const VRowCode rc = quantize_vrow16(w[i]);
     const uint32_t pair = rc.bits | (__shfl_down(rc.bits, 1, 16) << 16);
     if (t < t_end) {
-      const int64_t row = (int64_t)bh * capacity + t;
+      const int64_t row = rm.row(b, h, t);
       uint8_t* rec = vrec + row * kVRecBytes;
       if ((cg & 1) == 0) *reinterpret_cast<uint32_t*>(rec + 2 * cg) = pair;
       if ((cg & 3) == 0) *reinterpret_cast<uint32_t*>(rec + kVRecSz + cg) = rc.sz;
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(512) void cb_final_kernel(const long long* __restri
 // centres in registers.
 __global__ __launch_bounds__(256, 2) void kmeans_assign_kernel(
     const uint16_t* __restrict__ k, int64_t sb, int64_t sh, int64_t st, int Hkv, int n_tokens,
-    int capacity, int tpb, const float* __restrict__ mu, const float* __restrict__ alpha,
+    RowMap rm, int tpb, const float* __restrict__ mu, const float* __restrict__ alpha,
     const float* __restrict__ centres, long long* __restrict__ cb_part) {
   __shared__ unsigned long long cbs[kSub * 16 * 4];
   __shared__ int cbn[kSub * 16];
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(256, 2) void kmeans_assign_kernel(
       const int t = tb + i * 16 + rs;
       const bool ok = t >= kSink && t < n_tokens;
       w[i] = ok ? *reinterpret_cast<const uint4*>(base + (int64_t)t * st) : make_uint4(0u, 0u, 0u, 0u);
-      a[i] = ok ? alpha[(int64_t)bh * capacity + t] : 0.0f;
+      a[i] = ok ? alpha[rm.row(b, h, t)] : 0.0f;
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -357,28 +357,28 @@ hipError_t launch_mu_final(const float* partial, int BH, int nblk, int n_tokens,
 }
 
 hipError_t launch_codes(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
-                        int t_begin, int t_end, int capacity, const float* mu, uint8_t* codes,
+                        int t_begin, int t_end, const RowMap& rm, const float* mu, uint8_t* codes,
                         float* alpha, uint16_t* k_sink, uint8_t* vrec, hipStream_t s) {
   const int tiles = (t_end - t_begin + 127) / 128;
   return launch_k(KID_CODES, codes_kernel<false>, dim3(tiles, B * Hkv), dim3(256), 0, s, k, sb,
-                  sh, st, Hkv, t_begin, t_end, capacity, 1, mu, codes, alpha, k_sink, vrec,
+                  sh, st, Hkv, t_begin, t_end, rm, 1, mu, codes, alpha, k_sink, vrec,
                   (long long*)nullptr);
 }
 
 hipError_t launch_vcodes(const uint16_t* v, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
-                         int t_begin, int t_end, int capacity, uint8_t* vrec,
+                         int t_begin, int t_end, const RowMap& rm, uint8_t* vrec,
                          uint16_t* v_sink, hipStream_t s) {
   const int tiles = (t_end - t_begin + 127) / 128;
   return launch_k(KID_VCODES, vcodes_kernel, dim3(tiles, B * Hkv), dim3(256), 0, s, v, sb, sh, st,
-                  Hkv, t_begin, t_end, capacity, vrec, v_sink);
+                  Hkv, t_begin, t_end, rm, vrec, v_sink);
 }
 
 hipError_t launch_codes_cb(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
-                           int n_tokens, int capacity, const float* mu, uint8_t* codes,
+                           int n_tokens, const RowMap& rm, const float* mu, uint8_t* codes,
                            float* alpha, uint16_t* k_sink, uint8_t* vrec, long long* cb_part,
                            hipStream_t s) {
   return launch_k(KID_CODES, codes_kernel<true>, dim3(cb_blocks(n_tokens), B * Hkv), dim3(256), 0,
-                  s, k, sb, sh, st, Hkv, 0, n_tokens, capacity, kCbTiles, mu, codes, alpha, k_sink,
+                  s, k, sb, sh, st, Hkv, 0, n_tokens, rm, kCbTiles, mu, codes, alpha, k_sink,
                   vrec, cb_part);
 }
 
@@ -389,11 +389,11 @@ hipError_t launch_cb_final(const long long* cb_part, int BH, int nblk, float* co
 }
 
 hipError_t launch_kmeans_assign(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B,
-                                int Hkv, int n_tokens, int capacity, const float* mu,
+                                int Hkv, int n_tokens, const RowMap& rm, const float* mu,
                                 const float* alpha, const float* centres, long long* cb_part,
                                 hipStream_t s) {
   return launch_k(KID_KM_ASSIGN, kmeans_assign_kernel, dim3(cb_blocks(n_tokens), B * Hkv),
-                  dim3(256), 0, s, k, sb, sh, st, Hkv, n_tokens, capacity, kCbTiles, mu, alpha,
+                  dim3(256), 0, s, k, sb, sh, st, Hkv, n_tokens, rm, kCbTiles, mu, alpha,
                   centres, cb_part);
 }
 

@@ -349,7 +349,7 @@ __device__ __forceinline__ void sample_ranks(int k, int n, int* rank, int* rank_
 // the first barrier.
 __global__ __launch_bounds__(1024) void prep_kernel(
     const uint16_t* __restrict__ q, int n_q_heads, int Hkv, int G, const float* __restrict__ mu,
-    uint8_t* __restrict__ codes, float* __restrict__ alpha, int capacity, int n_tokens,
+    uint8_t* __restrict__ codes, float* __restrict__ alpha, RowMap rm, int n_tokens,
     const uint16_t* __restrict__ k_sink, const uint16_t* __restrict__ k_new, int64_t ksb,
     int64_t ksh, const uint16_t* __restrict__ v_new, int64_t vnsb, int64_t vnsh,
     uint8_t* __restrict__ vrec,
@@ -376,7 +376,6 @@ __global__ __launch_bounds__(1024) void prep_kernel(
   const bool full = n <= kSampleMax;
   const int m = full ? n : kSampleMax;
   const bool sample = mode == 1 && m > 0 && rank <= m;
-  const int64_t row0 = (int64_t)bh * capacity;
   const int64_t hq0 = (int64_t)b * n_q_heads + (int64_t)h * G;
   const bool has_cb = codebook != nullptr;
   const float4 cbv = (has_cb && tid < kLut)
@@ -415,8 +414,9 @@ __global__ __launch_bounds__(1024) void prep_kernel(
         const int64_t seg0 = (int64_t)st * n / ns, seg1 = (int64_t)(st + 1) * n / ns;
         t = kSink + (int)(seg0 + (seg1 - seg0 - kSampleRun) / 2) + (i - st * kSampleRun);
       }
-      c[u] = *reinterpret_cast<const uint4*>(codes + (row0 + t) * kCodeBytes);
-      a[u] = alpha[row0 + t];
+      const int64_t r = rm.row(b, h, t);
+      c[u] = *reinterpret_cast<const uint4*>(codes + r * kCodeBytes);
+      a[u] = alpha[r];
     }
   }
   // Sink key rows: 16 lanes x 8 channels per row, 64 rows.
@@ -429,7 +429,7 @@ __global__ __launch_bounds__(1024) void prep_kernel(
   if (has_cb && tid < kLut) cbl[tid] = cbv;
   if (k_new != nullptr && wave == 0) {  // the whole wave runs the 16-lane shuffles
     const RowCode rc = encode_row16(kw, km);
-    const int64_t row = row0 + nt - 1;
+    const int64_t row = rm.row(b, h, nt - 1);
     if (tid < 16 && (tid & 3) == 0) {
       *reinterpret_cast<uint32_t*>(codes + row * kCodeBytes + tid) = rc.word;
       if (vrec != nullptr)
@@ -441,7 +441,7 @@ __global__ __launch_bounds__(1024) void prep_kernel(
     const VRowCode rc = quantize_vrow16(vw);
     const uint32_t pair = rc.bits | (__shfl_down(rc.bits, 1, 16) << 16);
     const int cg = lane;
-    uint8_t* rec = vrec + (row0 + nt - 1) * kVRecBytes;
+    uint8_t* rec = vrec + rm.row(b, h, nt - 1) * kVRecBytes;
     if (cg < 16 && (cg & 1) == 0) *reinterpret_cast<uint32_t*>(rec + 2 * cg) = pair;
     if (cg < 16 && (cg & 3) == 0) *reinterpret_cast<uint32_t*>(rec + kVRecSz + cg) = rc.sz;
   }
@@ -552,7 +552,7 @@ __global__ __launch_bounds__(1024) void prep_kernel(
 // scalar base; full tiles load without bounds checks.
 template <int U>
 __global__ __launch_bounds__(256) void score_kernel(
-    const uint8_t* __restrict__ codes, const float* __restrict__ alpha, int capacity,
+    const uint8_t* __restrict__ codes, const float* __restrict__ alpha, RowMap rm,
     int n_tokens, int Hkv, const int32_t* __restrict__ seq_lens,
     const int* __restrict__ sel_lut, const float* __restrict__ sel_inv,
     const float* __restrict__ tau, int n_chunks, uint32_t* __restrict__ cand_key,
@@ -564,14 +564,34 @@ __global__ __launch_bounds__(256) void score_kernel(
   const int bh = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = kSink + blockIdx.x * kChunk;
-  const int64_t row0 = (int64_t)bh * capacity + t0;
+  const int64_t row0 = (int64_t)bh * rm.capacity + t0;  // contiguous rows; also the scores' index
   const uint4* __restrict__ cb = reinterpret_cast<const uint4*>(codes) + row0;
   const float* __restrict__ ab = alpha + row0;
   const int2 tv = reinterpret_cast<const int2*>(sel_lut + (int64_t)bh * kLut)[tid];
   const int lim = seq_len(seq_lens, bh / Hkv, n_tokens) - t0;  // tokens of this tile that exist
   uint4 c[U];
   float a[U];
-  if (lim >= kChunk) {
+  if (rm.table != nullptr) {
+    // Paged: the tile's 256 * U tokens span at most U + 1 pages (a page holds at
+    // least 256 tokens); their ids are block-uniform loads (scalar), and each
+    // lane picks its token's page from them.
+    const int b = bh / Hkv, h = bh - b * Hkv, lg = rm.lg_page;
+    const int32_t* __restrict__ tb = rm.table + (int64_t)b * rm.pps;
+    const int first = t0 >> lg, last = min((t0 + kChunk - 1) >> lg, rm.pps - 1);
+    int pgs[U + 1];
+#pragma unroll
+    for (int j = 0; j <= U; ++j) pgs[j] = tb[min(first + j, last)];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = u * 256 + tid, t = t0 + i, j = (t >> lg) - first;
+      int pg = pgs[0];
+#pragma unroll
+      for (int jj = 1; jj <= U; ++jj) pg = j == jj ? pgs[jj] : pg;
+      const int64_t r = (((int64_t)pg * Hkv + h) << lg) | (int64_t)(t & ((1 << lg) - 1));
+      c[u] = i < lim ? reinterpret_cast<const uint4*>(codes)[r] : make_uint4(0u, 0u, 0u, 0u);
+      a[u] = i < lim ? alpha[r] : 0.0f;
+    }
+  } else if (lim >= kChunk) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       c[u] = cb[u * 256 + tid];
@@ -631,7 +651,7 @@ __device__ __forceinline__ void count_bin(uint32_t* hist, bool valid, int bin, i
 
 // ------------------------------------------------------------------ select
 __global__ __launch_bounds__(1024) void select_kernel(
-    const uint8_t* __restrict__ codes, const float* __restrict__ alpha, int capacity,
+    const uint8_t* __restrict__ codes, const float* __restrict__ alpha, RowMap rm,
     int n_tokens, int Hkv, const int32_t* __restrict__ seq_lens,
     const int* __restrict__ sel_lut, const float* __restrict__ sel_inv, int top_k_max,
     int chunk, int n_chunks,
@@ -688,11 +708,12 @@ __global__ __launch_bounds__(1024) void select_kernel(
     load_itab(sel_lut + (int64_t)bh * kLut, itab);
     const float inv = sel_inv[bh];
     __syncthreads();
-    const int64_t row0 = (int64_t)bh * capacity;
+    const int b = bh / Hkv, h = bh - b * Hkv;
     for (int i = tid; i < n; i += blockDim.x) {
       const int t = kSink + i;
-      const uint4 c = *reinterpret_cast<const uint4*>(codes + (row0 + t) * kCodeBytes);
-      const uint32_t key = score_key(selection_score(itab, inv, c, alpha[row0 + t]));
+      const int64_t r = rm.row(b, h, t);
+      const uint4 c = *reinterpret_cast<const uint4*>(codes + r * kCodeBytes);
+      const uint32_t key = score_key(selection_score(itab, inv, c, alpha[r]));
       comp_key[cbase + i] = key;
       comp_t[cbase + i] = t;
       lo = min(lo, key);
@@ -809,19 +830,19 @@ __global__ __launch_bounds__(1024) void select_kernel(
 }  // namespace
 
 hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const float* mu,
-                       uint8_t* codes, float* alpha, int capacity, int n_tokens,
+                       uint8_t* codes, float* alpha, const RowMap& rm, int n_tokens,
                        const uint16_t* k_sink, const uint16_t* k_new, int64_t ksb, int64_t ksh,
                        const uint16_t* v_new, int64_t vnsb, int64_t vnsh, uint8_t* vrec,
                        const float* codebook, int top_k, int mode, int* sel_lut,
                        float* sel_inv, float* att_lut, float* att_qmu, float* att_slog,
                        float* tau, float* bin_scale, const int32_t* seq_lens, hipStream_t s) {
   return launch_k(KID_PREP, prep_kernel, dim3(B * Hkv), dim3(1024), 0, s, q, n_q_heads, Hkv,
-                  n_q_heads / Hkv, mu, codes, alpha, capacity, n_tokens, k_sink, k_new, ksb, ksh,
+                  n_q_heads / Hkv, mu, codes, alpha, rm, n_tokens, k_sink, k_new, ksb, ksh,
                   v_new, vnsb, vnsh, vrec, codebook, top_k, mode, seq_lens, sel_lut, sel_inv,
                   att_lut, att_qmu, att_slog, tau, bin_scale);
 }
 
-hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha, int capacity,
+hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha, const RowMap& rm,
                         int n_tokens, const int32_t* seq_lens, const int* sel_lut,
                         const float* sel_inv, const float* tau, int chunk,
                         int n_chunks, uint32_t* cand_key, int32_t* cand_t, int32_t* chunk_count,
@@ -829,7 +850,7 @@ hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha
   const dim3 grid(n_chunks, B * Hkv), block(256);
 #define SIKV_SCORE_CASE(UU)                                                                    \
   case 256 * UU:                                                                               \
-    return launch_k(KID_SCORE, score_kernel<UU>, grid, block, 0, s, codes, alpha, capacity,    \
+    return launch_k(KID_SCORE, score_kernel<UU>, grid, block, 0, s, codes, alpha, rm,          \
                     n_tokens, Hkv, seq_lens, sel_lut, sel_inv, tau, n_chunks, cand_key,        \
                     cand_t, chunk_count, scores_opt);
   switch (chunk) {
@@ -844,7 +865,7 @@ hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha
 #undef SIKV_SCORE_CASE
 }
 
-hipError_t launch_select(int B, int Hkv, const uint8_t* codes, const float* alpha, int capacity,
+hipError_t launch_select(int B, int Hkv, const uint8_t* codes, const float* alpha, const RowMap& rm,
                          int n_tokens, const int32_t* seq_lens, const int* sel_lut,
                          const float* sel_inv, int top_k, int chunk, int n_chunks,
                          uint32_t* cand_key, int32_t* cand_t, const int32_t* chunk_count,
@@ -852,7 +873,7 @@ hipError_t launch_select(int B, int Hkv, const uint8_t* codes, const float* alph
                          int32_t* comp_t, int32_t* idx, hipStream_t s) {
   if (n_chunks > kMaxChunks) return hipErrorInvalidValue;
   return launch_k(KID_SELECT, select_kernel, dim3(B * Hkv), dim3(1024), 0, s, codes, alpha,
-                  capacity, n_tokens, Hkv, seq_lens, sel_lut, sel_inv, top_k, chunk, n_chunks,
+                  rm, n_tokens, Hkv, seq_lens, sel_lut, sel_inv, top_k, chunk, n_chunks,
                   cand_key, cand_t,
                   chunk_count, tau, bin_scale, comp_key, comp_t, idx);
 }

@@ -124,6 +124,24 @@ __device__ __forceinline__ VRowCode quantize_vrow16(const uint4& w) {
   return VRowCode{bits, (uint32_t)__half_as_ushort(s16) | ((uint32_t)__half_as_ushort(z16) << 16)};
 }
 
+// Where token t of (batch b, KV head h) lives in the per-token arrays (codes,
+// alpha, value records and, paged, the bf16 V pool).  Contiguous: row
+// (b * Hkv + h) * capacity + t.  Paged: the sequence's page table entry for t
+// names a pool page of 2^lg_page tokens holding all KV heads: row
+// (page * Hkv + h) * 2^lg_page + t mod 2^lg_page.
+struct RowMap {
+  int64_t capacity;
+  const int32_t* table;  // null: contiguous; else [B][pps] page ids
+  int lg_page;
+  int pps;
+  int Hkv;
+  __device__ __forceinline__ int64_t row(int b, int h, int t) const {
+    if (table == nullptr) return ((int64_t)b * Hkv + h) * capacity + t;
+    const int64_t pg = table[(int64_t)b * pps + (t >> lg_page)];
+    return ((pg * Hkv + h) << lg_page) | (int64_t)(t & ((1 << lg_page) - 1));
+  }
+};
+
 // Ragged batches: the length of sequence b is seq_lens[b] clamped into
 // [65, n_max] (n_max, the descriptor's n_tokens, when seq_lens is null), and it
 // selects min(k, length - 64) tokens.
@@ -241,12 +259,12 @@ hipError_t launch_mu_final(const float* partial, int BH, int nblk, int n_tokens,
                            hipStream_t s);
 // vrec (may be null): value records, whose key code copy is written too.
 hipError_t launch_codes(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
-                        int t_begin, int t_end, int capacity, const float* mu, uint8_t* codes,
+                        int t_begin, int t_end, const RowMap& rm, const float* mu, uint8_t* codes,
                         float* alpha, uint16_t* k_sink, uint8_t* vrec, hipStream_t s);
 // 2-bit value codes of rows t_begin..t_end-1 (quantize_vrow16) into bytes 0..47 of
 // their records vrec [B*Hkv][cap][64]; rows below 64 are also copied to v_sink.
 hipError_t launch_vcodes(const uint16_t* v, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
-                         int t_begin, int t_end, int capacity, uint8_t* vrec,
+                         int t_begin, int t_end, const RowMap& rm, uint8_t* vrec,
                          uint16_t* v_sink, hipStream_t s);
 // Prefill codes with the codebook statistics: like launch_codes over [0, n_tokens),
 // plus, per block of kCbTiles x 128 tokens, the fixed-point sums of k~/alpha and
@@ -257,7 +275,7 @@ constexpr int kCbStride = kSub * 16 * 4 + kSub * 16;  // sums (int64) then count
 constexpr int kCbFracBits = 24;
 inline int cb_blocks(int n_tokens) { return (n_tokens + 128 * kCbTiles - 1) / (128 * kCbTiles); }
 hipError_t launch_codes_cb(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
-                           int n_tokens, int capacity, const float* mu, uint8_t* codes,
+                           int n_tokens, const RowMap& rm, const float* mu, uint8_t* codes,
                            float* alpha, uint16_t* k_sink, uint8_t* vrec, long long* cb_part,
                            hipStream_t s);
 // Codebook from the block statistics: centre = fl32((sum * 2^-24) / count) in
@@ -271,7 +289,7 @@ hipError_t launch_cb_final(const long long* cb_part, int BH, int nblk, float* co
 // distance in fp32 ((d0^2 + d1^2) + d2^2) + d3^2, lowest index on ties; block
 // statistics as launch_codes_cb (then launch_cb_final with keep = 1).
 hipError_t launch_kmeans_assign(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B,
-                                int Hkv, int n_tokens, int capacity, const float* mu,
+                                int Hkv, int n_tokens, const RowMap& rm, const float* mu,
                                 const float* alpha, const float* centres, long long* cb_part,
                                 hipStream_t s);
 
@@ -290,18 +308,18 @@ hipError_t launch_kmeans_assign(const uint16_t* k, int64_t sb, int64_t sh, int64
 // quantised into its value record (launch_vcodes layout; the key code copy too).  bin_scale [B*Hkv]: width of the select kernel's
 // score bins (2048 bins from tau to the sample maximum; 0 when not sampled).
 hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const float* mu,
-                       uint8_t* codes, float* alpha, int capacity, int n_tokens,
+                       uint8_t* codes, float* alpha, const RowMap& rm, int n_tokens,
                        const uint16_t* k_sink, const uint16_t* k_new, int64_t ksb, int64_t ksh,
                        const uint16_t* v_new, int64_t vnsb, int64_t vnsh, uint8_t* vrec,
                        const float* codebook, int top_k, int mode, int* sel_lut,
                        float* sel_inv, float* att_lut, float* att_qmu, float* att_slog,
                        float* tau, float* bin_scale, const int32_t* seq_lens, hipStream_t s);
-hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha, int capacity,
+hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha, const RowMap& rm,
                         int n_tokens, const int32_t* seq_lens, const int* sel_lut,
                         const float* sel_inv, const float* tau, int chunk,
                         int n_chunks, uint32_t* cand_key, int32_t* cand_t, int32_t* chunk_count,
                         float* scores_opt, hipStream_t s);
-hipError_t launch_select(int B, int Hkv, const uint8_t* codes, const float* alpha, int capacity,
+hipError_t launch_select(int B, int Hkv, const uint8_t* codes, const float* alpha, const RowMap& rm,
                          int n_tokens, const int32_t* seq_lens, const int* sel_lut,
                          const float* sel_inv, int top_k, int chunk, int n_chunks,
                          uint32_t* cand_key, int32_t* cand_t, const int32_t* chunk_count,
@@ -318,7 +336,7 @@ constexpr int kAttnMaxCpb = 64;  // chunks per block at most (the block's positi
 // included; vsink [B*Hkv][64][128] bf16) replace the bf16 V rows and the codes.
 hipError_t launch_attn(int n_q_heads, int B, int Hkv, const uint8_t* codes, const float* alpha,
                        const uint16_t* v, int64_t vsb, int64_t vsh, int64_t vst,
-                       const uint8_t* vrec, const uint16_t* vsink, int capacity,
+                       const uint8_t* vrec, const uint16_t* vsink, const RowMap& rm,
                        int n_tokens, const int32_t* seq_lens, const int32_t* idx, int top_k,
                        const float* att_lut,
                        const float* att_qmu, const float* att_slog, float sm_scale,

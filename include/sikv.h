@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define SIKV_ABI_VERSION 5
+#define SIKV_ABI_VERSION 6
 #define SIKV_HEAD_DIM 128
 #define SIKV_N_SINK 64
 #define SIKV_MAX_GROUP 8
@@ -110,6 +110,18 @@ typedef int32_t sikv_status;
  *          already counts it).  sikv_encode / sikv_encode_v ignore it: ragged
  *          prefill is one call per sequence on a batch-1 view (pointers offset
  *          to that sequence's rows).
+ *   page_table, page_size, pages_per_seq, n_pages  page_table NULL: each (b, h)
+ *          owns capacity contiguous rows of the per-token arrays.  Else (paged,
+ *          a device array int32 [B][pages_per_seq], 4-byte aligned) token t of
+ *          sequence b lives in pool page p = page_table[b][t / page_size], which
+ *          holds page_size tokens of every KV head: codes uint8
+ *          [n_pages][Hkv][page_size][16], alpha fp32 [n_pages][Hkv][page_size],
+ *          vrec uint8 [n_pages][Hkv][page_size][64], and a bf16 V pool `v` laid out
+ *          [n_pages][Hkv][page_size][128] (v_stride_b = Hkv*page_size*128,
+ *          v_stride_h = page_size*128, v_stride_t = 128).  page_size is a power of
+ *          two >= 256, capacity = pages_per_seq * page_size, and n_pages * Hkv *
+ *          page_size < 2^31.  mu, k_sink, codebook, v_sink stay per sequence.  Page
+ *          ids are trusted (the caller keeps them in [0, n_pages)).
  * n_tokens (N) is the number of valid tokens of every sequence (64 < N <=
  * capacity; the longest one with seq_lens); candidates for top-k are the tokens
  * 64..N-1.
@@ -133,6 +145,11 @@ typedef struct sikv_cache_desc {
   uint8_t *vrec;
   uint16_t *v_sink;
   const int32_t *seq_lens;
+  const int32_t *page_table;
+  int32_t page_size;
+  int32_t pages_per_seq;
+  int32_t n_pages;
+  int32_t reserved;
 } sikv_cache_desc;
 
 /*

@@ -38,11 +38,11 @@ def test_header_functions_are_exported_and_declared():
 
 def test_abi_version_and_desc_layout():
     assert lib.sikv_abi_version() == _abi.ABI_VERSION
-    assert lib.sikv_desc_size() == C.sizeof(_abi.CacheDesc) == 120
+    assert lib.sikv_desc_size() == C.sizeof(_abi.CacheDesc) == 144
     offs = {f[0]: getattr(_abi.CacheDesc, f[0]).offset for f in _abi.CacheDesc._fields_}
     assert offs["codes"] == 24 and offs["v"] == 56 and offs["v_stride_t"] == 80
     assert offs["codebook"] == 88 and offs["vrec"] == 96 and offs["v_sink"] == 104
-    assert offs["seq_lens"] == 112
+    assert offs["seq_lens"] == 112 and offs["page_table"] == 120 and offs["n_pages"] == 136
 
 
 def test_status_strings():
@@ -57,7 +57,8 @@ def desc(**kw):
     d.batch, d.n_kv_heads, d.head_dim, d.capacity, d.n_tokens, d.n_sink = 2, 2, 128, 1000, 900, 64
     d.codes, d.alpha, d.mu, d.k_sink = FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000
     d.v, d.v_stride_b, d.v_stride_h, d.v_stride_t = FAKE + 0x400000, 2 * 1000 * 128, 1000 * 128, 128
-    d.codebook = d.vrec = d.v_sink = d.seq_lens = None
+    d.codebook = d.vrec = d.v_sink = d.seq_lens = d.page_table = None
+    d.page_size = d.pages_per_seq = d.n_pages = 0
     for k, v in kw.items():
         setattr(d, k, v)
     return d
@@ -224,6 +225,25 @@ def test_timing_facility_without_launches():
     n, ms = C.c_int64(), C.c_double()
     assert lib.sikv_timing_read(0, C.byref(n), C.byref(ms)) == OK and n.value == 0
     assert lib.sikv_timing_read(99, C.byref(n), C.byref(ms)) == INVALID
+
+
+def test_paged_descriptor_validation():
+    """Page size a power of two >= 256, capacity = pages_per_seq * page_size,
+    a row count that fits int32, the bf16 V pool dense in the page layout."""
+    ok = dict(page_table=FAKE + 0x900000, page_size=256, pages_per_seq=4, n_pages=16,
+              capacity=1024, n_tokens=900, v_stride_b=2 * 256 * 128, v_stride_h=256 * 128,
+              v_stride_t=128)
+    assert score(desc(**ok)) == WORKSPACE                    # valid: fails only for workspace
+    f = C.c_float
+    attn = lambda d: lib.sikv_sparse_attn(C.byref(d), FAKE, 4, FAKE, 16, f(0.088), FAKE, None, 0,
+                                          None)
+    assert attn(desc(**ok)) == WORKSPACE
+    for bad in (dict(page_size=128), dict(page_size=384), dict(pages_per_seq=0),
+                dict(n_pages=0), dict(capacity=1000), dict(page_table=FAKE + 0x900002),
+                dict(n_pages=1 << 22, page_size=512, pages_per_seq=2)):
+        assert score(desc(**{**ok, **bad})) == INVALID, bad
+    assert attn(desc(**{**ok, "v_stride_t": 256})) == INVALID    # V pool not in page layout
+    assert attn(desc(**{**ok, "v_stride_h": 1000 * 128})) == INVALID
 
 
 def test_baseline_comparator_validation():
