@@ -205,7 +205,8 @@ sikv_status sikv_encode_v(const sikv_cache_desc *cache, const uint16_t *v, int64
  *   q          bf16 [B][n_q_heads][128], contiguous.
  *   top_k      1..N-64.
  *   idx        int32 [B][Hkv][top_k], ascending token positions.
- *   scores_opt NULL, or fp32 [B][Hkv][capacity]: receives every candidate's
+ *   scores_opt NULL, or fp32 [B][Hkv][capacity] (logical positions, also for a
+ *          paged cache): receives every candidate's
  *              score (test hook; entries t < 64 and t >= N untouched).
  */
 sikv_status sikv_score_topk(const sikv_cache_desc *cache, const uint16_t *q, int32_t n_q_heads,
