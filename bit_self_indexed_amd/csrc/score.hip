@@ -26,6 +26,8 @@
 //             every token, so the result never depends on the sample.
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "sikv_internal.h"
 
 namespace sikv {
@@ -734,9 +736,13 @@ __global__ __launch_bounds__(1024) void select_kernel(
     const float z = (key_score(key) - th) * bsc;  // NaN (no scale) -> bin 0
     return z >= 2047.0f ? 2047 : (z > 0.0f ? (int)z : 0);
   };
-  uint32_t* dk = in_lds ? lkey : comp_key + cbase;
-  int32_t* dp = in_lds ? lpos : comp_t + cbase;
-  {
+  // Two instances, so that the LDS list is written with LDS stores (a pointer
+  // that may address either memory would make every store a flat one, which
+  // waits on both memory counters).
+  auto gather = [&](auto lds_tag) {
+    constexpr bool kLds = decltype(lds_tag)::value;
+    uint32_t* __restrict__ dk = kLds ? lkey : comp_key + cbase;
+    int32_t* __restrict__ dp = kLds ? lpos : comp_t + cbase;
     const int lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
     for (int c0 = wave; c0 < n_chunks; c0 += 4 * nw) {
       uint32_t kk[4][4];
@@ -769,7 +775,7 @@ __global__ __launch_bounds__(1024) void select_kernel(
             lo = min(lo, kk[v][u]);
             hi = max(hi, kk[v][u]);
           }
-          if (in_lds) count_bin(hist, j < cnt, bin_of(kk[v][u]), lane);
+          if constexpr (kLds) count_bin(hist, j < cnt, bin_of(kk[v][u]), lane);
         }
         for (int j0 = 256; j0 < cnt; j0 += 64) {  // tiles with many candidates
           const int j = j0 + lane;
@@ -780,11 +786,15 @@ __global__ __launch_bounds__(1024) void select_kernel(
             lo = min(lo, key);
             hi = max(hi, key);
           }
-          if (in_lds) count_bin(hist, j < cnt, bin_of(key), lane);
+          if constexpr (kLds) count_bin(hist, j < cnt, bin_of(key), lane);
         }
       }
     }
-  }
+  };
+  if (in_lds)
+    gather(std::true_type{});
+  else
+    gather(std::false_type{});
   if (in_lds) {
     __syncthreads();  // publishes the list and the histogram
     // The boundary bin of the k-th largest; its keys (usually a few dozen) go to
