@@ -297,6 +297,46 @@ def test_all_scores_tied():
         assert np.array_equal(idx[0, h], expect)
 
 
+
+def test_select_list_in_workspace():
+    """More candidates than the select kernel keeps in LDS (16384): the candidate
+    list goes to the workspace.  (a) every score tied at N = 20000 (no usable
+    score spread: radix rounds over the whole list); (b) random keys with
+    k = 15500 of 65472 candidates (about 18K pass the sampled threshold)."""
+    w = S.custom("ties_big", 1, 4, 1, 20000, 777, n_planted=0, cfg_id=112)
+    say("[parity] case=ties_big")
+    d = S.draw(w)
+    K = d["K"].copy()
+    K[:, :, 64:] = K[:, :, 64:65]
+    cache = sk.Cache(w.batch, w.n_kv_heads, w.n_tokens, v=dev_bf16(d["V"]))
+    sk.sikv_encode(cache, dev_bf16(K))
+    idx = sk.sikv_score_topk(cache, dev_bf16(d["q"]), w.top_k).cpu().numpy()
+    assert np.array_equal(idx[0, 0], np.arange(64, 64 + w.top_k))
+
+    w = S.custom("big_k", 1, 4, 1, 65536, 15500, n_planted=16, cfg_id=113)
+    say("[parity] case=big_k")
+    d = S.draw(w)
+    N, G = w.n_tokens, w.group
+    q = dev_bf16(d["q"])
+    cache = sk.Cache(w.batch, w.n_kv_heads, N, v=dev_bf16(d["V"]))
+    sk.sikv_encode(cache, dev_bf16(d["K"]))
+    idx_out = torch.empty((1, 1, w.top_k), dtype=torch.int32, device="cuda")
+    out = sk.sikv_decode_step(cache, q, w.top_k, SM, idx_out=idx_out).cpu().numpy()
+    di = idx_out.cpu().numpy()
+    o = oracle_head(d["K"][0, 0], N)
+    s = oracle_scores(d["q"], o["codes"], o["alpha"], 0, 0, 1, N)
+    check_topk(di[0, 0], s, w.top_k, N, "big_k topk")
+    sk.debug_force_exact_select(True)
+    try:
+        idx2 = sk.sikv_score_topk(cache, q, w.top_k).cpu().numpy()
+    finally:
+        sk.debug_force_exact_select(False)
+    assert np.array_equal(idx2, di)
+    ref = O.sparse_attention(d["q"][0, :G], di[0, 0], o["k_sink"], o["codes"], o["alpha"],
+                             o["mu"], d["V"][0, 0], SM)
+    check_rows(out[0, :G], ref, "big_k decode")
+
+
 def test_dense_comparator():
     w = S.custom("dense", 2, 8, 2, 3000, 100, n_planted=4, cfg_id=112)
     say("[parity] case=dense_comparator")
