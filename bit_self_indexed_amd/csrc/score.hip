@@ -400,34 +400,57 @@ __global__ __launch_bounds__(1024) void prep_kernel(
     km[4] = m1.x; km[5] = m1.y; km[6] = m1.z; km[7] = m1.w;
   }
 
+  // The query, mean and sink rows are loaded first: the tables need only them
+  // and are built while the sample's loads are still in flight (loads complete
+  // in order, so a wait for q never waits for the sample).
+  const uint4 ks = *reinterpret_cast<const uint4*>(k_sink + ((int64_t)bh * kSink + (tid >> 4)) * kD +
+                                                   (tid & 15) * 8);
+  // (unconditional loads at clamped indices: a load in a branch whose value is
+  // used inside it would wait there for every load issued before it)
+  const uint16_t qraw = q[hq0 * kD + min(tid, G * kD - 1)];
+  const float mraw = mu[(int64_t)bh * kD + min(tid, kD - 1)];
+
+  // Sample rows: stratum st = i / 16 of 256 equal segments, 16 tokens centred in
+  // it (the whole candidate set when small).  Every lane loads a real row (token
+  // 64 for unused slots, never scored), so the wait counts do not depend on
+  // which lanes sample; page ids, if paged, are all loaded before any code.
   constexpr int kPer = kSampleMax / 1024;
+  int st_t[kPer];
+  bool use[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = tid + u * 1024;
+    use[u] = sample && i < m;
+    int t = kSink + i;
+    if (!full) {
+      const int st = i / kSampleRun, ns = kSampleMax / kSampleRun;
+      const int64_t seg0 = (int64_t)st * n / ns, seg1 = (int64_t)(st + 1) * n / ns;
+      t = kSink + (int)(seg0 + (seg1 - seg0 - kSampleRun) / 2) + (i - st * kSampleRun);
+    }
+    st_t[u] = use[u] ? t : kSink;
+  }
+  int64_t rows[kPer];
+  if (rm.table != nullptr) {
+    int32_t pg[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) pg[u] = rm.table[(int64_t)b * rm.pps + (st_t[u] >> rm.lg_page)];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      rows[u] = (((int64_t)pg[u] * Hkv + h) << rm.lg_page) |
+                (int64_t)(st_t[u] & ((1 << rm.lg_page) - 1));
+  } else {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) rows[u] = ((int64_t)b * Hkv + h) * rm.capacity + st_t[u];
+  }
   uint4 c[kPer];
   float a[kPer];
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
-    const int i = tid + u * 1024;
-    c[u] = make_uint4(0u, 0u, 0u, 0u);
-    a[u] = 0.0f;
-    if (sample && i < m) {
-      // stratum st = i / 16 of 256 equal segments: 16 tokens centred in it
-      int t = kSink + i;
-      if (!full) {
-        const int st = i / kSampleRun, ns = kSampleMax / kSampleRun;
-        const int64_t seg0 = (int64_t)st * n / ns, seg1 = (int64_t)(st + 1) * n / ns;
-        t = kSink + (int)(seg0 + (seg1 - seg0 - kSampleRun) / 2) + (i - st * kSampleRun);
-      }
-      const int64_t r = rm.row(b, h, t);
-      c[u] = *reinterpret_cast<const uint4*>(codes + r * kCodeBytes);
-      a[u] = alpha[r];
-    }
+    c[u] = *reinterpret_cast<const uint4*>(codes + rows[u] * kCodeBytes);
+    a[u] = alpha[rows[u]];
   }
-  // Sink key rows: 16 lanes x 8 channels per row, 64 rows.
-  const uint4 ks = *reinterpret_cast<const uint4*>(k_sink + ((int64_t)bh * kSink + (tid >> 4)) * kD +
-                                                   (tid & 15) * 8);
-  const float qx = tid < G * kD ? __uint_as_float((uint32_t)q[hq0 * kD + tid] << 16) : 0.0f;
-  const float mx = tid < kD ? mu[(int64_t)bh * kD + tid] : 0.0f;
-  if (tid < G * kD) qv[tid / kD][tid % kD] = qx;
-  if (tid < kD) mus[tid] = mx;
+  if (tid < G * kD) qv[tid / kD][tid % kD] = __uint_as_float((uint32_t)qraw << 16);
+  if (tid < kD) mus[tid] = mraw;
   if (has_cb && tid < kLut) cbl[tid] = cbv;
   if (k_new != nullptr && wave == 0) {  // the whole wave runs the 16-lane shuffles
     const RowCode rc = encode_row16(kw, km);
