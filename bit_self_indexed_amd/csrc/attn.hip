@@ -368,48 +368,57 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   __shared__ float wred[2][4];
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int sg = tid >> 5, cq = tid & 31;
-  const float* ml = part_ml + r * n_splits * 2;
+  const int sg = tid >> 5, cq = tid & 31;  // split group, 16-byte column slice
+  const float2* __restrict__ ml = reinterpret_cast<const float2*>(part_ml + r * n_splits * 2);
+  const float4* __restrict__ po = reinterpret_cast<const float4*>(part_o + r * n_splits * kD) + cq;
+  // Splits sg, sg + 8, sg + 16, sg + 24 are loaded before the maximum is known
+  // (unconditionally, at clamped indices, and masked after), so the partials
+  // are fetched in the same round trip as the maxima.
+  constexpr int kPre = 4;
+  float2 mv[kPre];
+  float4 ov[kPre];
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) {
+    const int sc = min(sg + 8 * u, n_splits - 1);
+    mv[u] = ml[sc];
+    ov[u] = po[(int64_t)sc * (kD / 4)];
+  }
   float m = -INFINITY;
-  for (int s = tid; s < n_splits; s += 256) m = fmaxf(m, ml[2 * s]);
+#pragma unroll
+  for (int u = 0; u < kPre; ++u)
+    if (sg + 8 * u < n_splits) m = fmaxf(m, mv[u].x);
+  for (int sc = sg + 8 * kPre; sc < n_splits; sc += 8) m = fmaxf(m, ml[sc].x);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   if (lane == 0) wred[0][wave] = m;
   __syncthreads();
   m = fmaxf(fmaxf(wred[0][0], wred[0][1]), fmaxf(wred[0][2], wred[0][3]));
-  float l = 0.0f;
-  for (int s = tid; s < n_splits; s += 256) l = fmaf(exp2f(ml[2 * s] - m), ml[2 * s + 1], l);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
-  if (lane == 0) wred[1][wave] = l;
-  const float4* po = reinterpret_cast<const float4*>(part_o + r * n_splits * kD) + cq;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  int s = sg;
-  for (; s + 24 < n_splits; s += 32) {
-    float wv[4];
-    float4 ov[4];
+  float l = 0.0f;  // summed by the cq == 0 lane of each split group only
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      wv[u] = ml[2 * (s + 8 * u)];
-      ov[u] = po[(int64_t)(s + 8 * u) * (kD / 4)];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float w = exp2f(wv[u] - m);
+  for (int u = 0; u < kPre; ++u) {
+    if (sg + 8 * u < n_splits) {
+      const float w = exp2f(mv[u].x - m);
+      if (cq == 0) l = fmaf(w, mv[u].y, l);
       acc.x = fmaf(w, ov[u].x, acc.x);
       acc.y = fmaf(w, ov[u].y, acc.y);
       acc.z = fmaf(w, ov[u].z, acc.z);
       acc.w = fmaf(w, ov[u].w, acc.w);
     }
   }
-  for (; s < n_splits; s += 8) {
-    const float w = exp2f(ml[2 * s] - m);
-    const float4 ov = po[(int64_t)s * (kD / 4)];
-    acc.x = fmaf(w, ov.x, acc.x);
-    acc.y = fmaf(w, ov.y, acc.y);
-    acc.z = fmaf(w, ov.z, acc.z);
-    acc.w = fmaf(w, ov.w, acc.w);
+  for (int sc = sg + 8 * kPre; sc < n_splits; sc += 8) {
+    const float2 x = ml[sc];
+    const float4 o4 = po[(int64_t)sc * (kD / 4)];
+    const float w = exp2f(x.x - m);
+    if (cq == 0) l = fmaf(w, x.y, l);
+    acc.x = fmaf(w, o4.x, acc.x);
+    acc.y = fmaf(w, o4.y, acc.y);
+    acc.z = fmaf(w, o4.z, acc.z);
+    acc.w = fmaf(w, o4.w, acc.w);
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
+  if (lane == 0) wred[1][wave] = l;
   red[sg][cq * 4 + 0] = acc.x;
   red[sg][cq * 4 + 1] = acc.y;
   red[sg][cq * 4 + 2] = acc.z;
