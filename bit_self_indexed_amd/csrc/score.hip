@@ -269,6 +269,46 @@ __device__ void block_emit(const uint32_t* keys, const int32_t* pos, int n, int 
   }
 }
 
+// block_emit for a list held in LDS (n <= kSelectLds), with coalesced output:
+// each thread reads its run (an odd length, so the runs' strided LDS reads
+// never share a bank) into registers once, the (gt, eq) counts are scanned,
+// every thread then writes its taken positions into the key list (free once
+// all runs are read), and the block copies them out in order, consecutive
+// threads storing consecutive entries.  Two barriers beyond the scan.
+constexpr int kEmitRun = 17;  // longest run: odd and >= kSelectLds / 1024
+static_assert(kEmitRun >= ((kSelectLds / 1024) | 1), "runs of a 1024-thread block");
+__device__ void block_emit_lds(uint32_t* keys, const int32_t* pos, int n, int k, Kth r,
+                               int32_t* __restrict__ out, int* tmp) {
+  int per = (n + blockDim.x - 1) / blockDim.x;
+  per |= 1;
+  const int i0 = threadIdx.x * per;
+  uint32_t kr[kEmitRun];
+  int32_t pr[kEmitRun];
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < kEmitRun; ++j) {
+    const bool v = j < per && i0 + j < n;
+    kr[j] = v ? keys[i0 + j] : 0u;
+    pr[j] = v ? pos[i0 + j] : 0;
+    gt += (v && kr[j] > r.key) ? 1 : 0;
+    eq += (v && kr[j] == r.key) ? 1 : 0;
+  }
+  int tot;
+  const int ex = block_excl_scan((gt << 16) | eq, tmp, &tot);  // n <= kSelectLds < 2^16
+  int eq_before = ex & 0xffff;
+  int o = (ex >> 16) + min(eq_before, r.need);
+  __syncthreads();  // every run is read: the key list becomes the staging area
+#pragma unroll
+  for (int j = 0; j < kEmitRun; ++j) {
+    const bool v = j < per && i0 + j < n;
+    bool take = v && kr[j] > r.key;
+    if (v && kr[j] == r.key) take = eq_before++ < r.need;
+    if (take && o < k) keys[o++] = (uint32_t)pr[j];
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < k; j += blockDim.x) out[j] = (int32_t)keys[j];
+}
+
 // Copies the selection table of one head from global memory into LDS (2 KB).
 // No barrier.
 __device__ __forceinline__ void load_itab(const int* __restrict__ gtab, int* itab) {
@@ -852,7 +892,7 @@ __global__ __launch_bounds__(1024) void select_kernel(
       block_minmax(lo, hi, mm, &lo, &hi);
       r = block_kth(lkey, C, top_k, lo, hi, hist, tmp, sub, &scount);
     }
-    block_emit(lkey, lpos, C, top_k, r, out, tmp);
+    block_emit_lds(lkey, lpos, C, top_k, r, out, tmp);
   } else {
     block_minmax(lo, hi, mm, &lo, &hi);  // its barriers also publish the copies
     const Kth r = block_kth(comp_key + cbase, C, top_k, lo, hi, hist, tmp, sub, &scount);
