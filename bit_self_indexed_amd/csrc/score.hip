@@ -744,14 +744,37 @@ __global__ __launch_bounds__(1024) void select_kernel(
     return;
   }
   for (int i = tid; i < 2048; i += blockDim.x) hist[i] = 0u;  // published by the scan's barriers
-  // Tile counts -> offsets of each tile's candidates in the ordered list.
+  // Tile counts -> offsets of each tile's candidates in the ordered list.  The
+  // counts are loaded first, then the first 256 slots of each wave's first four
+  // tiles, which stay in flight while the counts are scanned (loads complete in
+  // order; all of them unconditional at clamped indices, so that no wait sits
+  // inside a branch).  A tile's slot region holds chunk >= 256 entries, so every
+  // slot load is in bounds; slots past a tile's count are discarded.
+  const int64_t cbase = (int64_t)bh * n_chunks * chunk;
+  uint32_t pk[4][4];
+  int32_t pt[4][4];
   {
     const int per = (n_chunks + blockDim.x - 1) / blockDim.x;  // <= 2
     const int c0 = tid * per;
-    int cs[2] = {0, 0};
+    int cs[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      if (j < per && c0 + j < n_chunks) cs[j] = chunk_count[(int64_t)bh * n_chunks + c0 + j];
+      cs[j] = chunk_count[(int64_t)bh * n_chunks + min(c0 + j, n_chunks - 1)];
+    {
+      const int lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t src = cbase + (int64_t)min(wave + v * nw, n_chunks - 1) * chunk;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          pk[v][u] = cand_key[src + lane + 64 * u];
+          pt[v][u] = cand_t[src + lane + 64 * u];
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (!(j < per && c0 + j < n_chunks)) cs[j] = 0;
     int total;
     int pre = block_excl_scan(cs[0] + cs[1], tmp, &total);
 #pragma unroll
@@ -764,7 +787,6 @@ __global__ __launch_bounds__(1024) void select_kernel(
     __syncthreads();
   }
   const int C = off[n_chunks];
-  const int64_t cbase = (int64_t)bh * n_chunks * chunk;
   uint32_t lo = 0xffffffffu, hi = 0u;
   if (C < top_k) {
     // Exact path over the whole head: rescore every candidate with the same
@@ -810,17 +832,27 @@ __global__ __launch_bounds__(1024) void select_kernel(
     for (int c0 = wave; c0 < n_chunks; c0 += 4 * nw) {
       uint32_t kk[4][4];
       int32_t tt[4][4];
+      if (c0 == wave) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int ci = c0 + v * nw;
-        const int o = ci < n_chunks ? off[ci] : 0;
-        const int cnt = ci < n_chunks ? off[ci + 1] - o : 0;
-        const int64_t src = cbase + (int64_t)ci * chunk;
+        for (int v = 0; v < 4; ++v)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int j = lane + 64 * u;
-          kk[v][u] = j < cnt ? cand_key[src + j] : 0u;
-          tt[v][u] = j < cnt ? cand_t[src + j] : 0;
+          for (int u = 0; u < 4; ++u) {
+            kk[v][u] = pk[v][u];
+            tt[v][u] = pt[v][u];
+          }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int ci = c0 + v * nw;
+          const int o = ci < n_chunks ? off[ci] : 0;
+          const int cnt = ci < n_chunks ? off[ci + 1] - o : 0;
+          const int64_t src = cbase + (int64_t)ci * chunk;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int j = lane + 64 * u;
+            kk[v][u] = j < cnt ? cand_key[src + j] : 0u;
+            tt[v][u] = j < cnt ? cand_t[src + j] : 0;
+          }
         }
       }
 #pragma unroll
