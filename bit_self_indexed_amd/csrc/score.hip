@@ -269,44 +269,56 @@ __device__ void block_emit(const uint32_t* keys, const int32_t* pos, int n, int 
   }
 }
 
-// block_emit for a list held in LDS (n <= kSelectLds), with coalesced output:
-// each thread reads its run (an odd length, so the runs' strided LDS reads
-// never share a bank) into registers once, the (gt, eq) counts are scanned,
-// every thread then writes its taken positions into the key list (free once
-// all runs are read), and the block copies them out in order, consecutive
-// threads storing consecutive entries.  Two barriers beyond the scan.
+// The select kernel's LDS list (n <= kSelectLds entries) cut into one run per
+// thread, held in registers: an odd run length, so that the runs' strided LDS
+// reads never share a bank.
 constexpr int kEmitRun = 17;  // longest run: odd and >= kSelectLds / 1024
 static_assert(kEmitRun >= ((kSelectLds / 1024) | 1), "runs of a 1024-thread block");
-__device__ void block_emit_lds(uint32_t* keys, const int32_t* pos, int n, int k, Kth r,
-                               int32_t* __restrict__ out, int* tmp) {
-  int per = (n + blockDim.x - 1) / blockDim.x;
-  per |= 1;
-  const int i0 = threadIdx.x * per;
-  uint32_t kr[kEmitRun];
-  int32_t pr[kEmitRun];
+struct Run {
+  uint32_t key[kEmitRun];
+  int32_t pos[kEmitRun];
+  int per, i0, n;
+  __device__ __forceinline__ bool valid(int j) const { return j < per && i0 + j < n; }
+};
+
+// Loads the runs (blockDim.x = 1024).  No barrier.
+__device__ __forceinline__ void run_load(Run& rn, const uint32_t* keys, const int32_t* pos, int n) {
+  rn.per = ((n + blockDim.x - 1) / blockDim.x) | 1;
+  rn.i0 = threadIdx.x * rn.per;
+  rn.n = n;
+#pragma unroll
+  for (int j = 0; j < kEmitRun; ++j) {
+    rn.key[j] = rn.valid(j) ? keys[rn.i0 + j] : 0u;
+    rn.pos[j] = rn.valid(j) ? pos[rn.i0 + j] : 0;
+  }
+}
+
+// block_emit over the runs, with coalesced output: the (gt, eq) counts are
+// scanned, every thread writes its taken positions into the key list (stage;
+// the caller no longer needs it), and the block copies them out in order,
+// consecutive threads storing consecutive entries.  Two barriers beyond the
+// scan.
+__device__ void run_emit(const Run& rn, int k, Kth r, uint32_t* stage, int32_t* __restrict__ out,
+                         int* tmp) {
   int gt = 0, eq = 0;
 #pragma unroll
   for (int j = 0; j < kEmitRun; ++j) {
-    const bool v = j < per && i0 + j < n;
-    kr[j] = v ? keys[i0 + j] : 0u;
-    pr[j] = v ? pos[i0 + j] : 0;
-    gt += (v && kr[j] > r.key) ? 1 : 0;
-    eq += (v && kr[j] == r.key) ? 1 : 0;
+    gt += (rn.valid(j) && rn.key[j] > r.key) ? 1 : 0;
+    eq += (rn.valid(j) && rn.key[j] == r.key) ? 1 : 0;
   }
   int tot;
   const int ex = block_excl_scan((gt << 16) | eq, tmp, &tot);  // n <= kSelectLds < 2^16
   int eq_before = ex & 0xffff;
   int o = (ex >> 16) + min(eq_before, r.need);
-  __syncthreads();  // every run is read: the key list becomes the staging area
+  __syncthreads();  // no thread reads the list any more
 #pragma unroll
   for (int j = 0; j < kEmitRun; ++j) {
-    const bool v = j < per && i0 + j < n;
-    bool take = v && kr[j] > r.key;
-    if (v && kr[j] == r.key) take = eq_before++ < r.need;
-    if (take && o < k) keys[o++] = (uint32_t)pr[j];
+    bool take = rn.valid(j) && rn.key[j] > r.key;
+    if (rn.valid(j) && rn.key[j] == r.key) take = eq_before++ < r.need;
+    if (take && o < k) stage[o++] = (uint32_t)rn.pos[j];
   }
   __syncthreads();
-  for (int j = threadIdx.x; j < k; j += blockDim.x) out[j] = (int32_t)keys[j];
+  for (int j = threadIdx.x; j < k; j += blockDim.x) out[j] = (int32_t)stage[j];
 }
 
 // Copies the selection table of one head from global memory into LDS (2 KB).
@@ -892,17 +904,20 @@ __global__ __launch_bounds__(1024) void select_kernel(
     gather(std::false_type{});
   if (in_lds) {
     __syncthreads();  // publishes the list and the histogram
-    // The boundary bin of the k-th largest; its keys (usually a few dozen) go to
-    // a sub-list resolved by one wave, or by radix rounds if more than 64.
+    // Each thread's run of the list goes to registers while the histogram is
+    // scanned for the boundary bin of the k-th largest; the bin's keys (usually
+    // a few dozen) go to a sub-list resolved by one wave, or by radix rounds if
+    // more than 64.
+    Run rn;
+    run_load(rn, lkey, lpos, C);
     const Round rb = hist_pick(hist, 2048, top_k, tmp);
     Kth r;
     if (rb.count <= kSubMax) {
       if (tid == 0) scount = 0;
       __syncthreads();
-      for (int i = tid; i < C; i += blockDim.x) {
-        const uint32_t key = lkey[i];
-        if (bin_of(key) == rb.digit) sub[atomicAdd(&scount, 1)] = key;
-      }
+#pragma unroll
+      for (int j = 0; j < kEmitRun; ++j)
+        if (rn.valid(j) && bin_of(rn.key[j]) == rb.digit) sub[atomicAdd(&scount, 1)] = rn.key[j];
       __syncthreads();
       const int ns = scount, need = top_k - rb.above;
       if (ns <= 64) {
@@ -924,7 +939,7 @@ __global__ __launch_bounds__(1024) void select_kernel(
       block_minmax(lo, hi, mm, &lo, &hi);
       r = block_kth(lkey, C, top_k, lo, hi, hist, tmp, sub, &scount);
     }
-    block_emit_lds(lkey, lpos, C, top_k, r, out, tmp);
+    run_emit(rn, top_k, r, lkey, out, tmp);
   } else {
     block_minmax(lo, hi, mm, &lo, &hi);  // its barriers also publish the copies
     const Kth r = block_kth(comp_key + cbase, C, top_k, lo, hi, hist, tmp, sub, &scount);
