@@ -122,7 +122,8 @@ struct Round {
 // Given a histogram of nb bins (in LDS, published) over keys in ascending bin
 // order, the bin holding the k-th largest key: (bin, keys in larger bins, keys
 // in it).  tmp: LDS >= 24 ints.  Five barriers.
-__device__ __forceinline__ Round hist_pick(const uint32_t* hist, int nb, int k, int* tmp);
+__device__ __forceinline__ Round hist_pick(const uint32_t* hist, int nb, int k, int* tmp,
+                                           int top_fill = -1);
 
 __device__ __forceinline__ Round block_round(const uint32_t* keys, int n, int k, uint32_t lo,
                                              int top, uint32_t prefix, uint32_t* hist, int* tmp) {
@@ -142,16 +143,23 @@ __device__ __forceinline__ Round block_round(const uint32_t* keys, int n, int k,
   return r;
 }
 
-__device__ __forceinline__ Round hist_pick(const uint32_t* hist, int nb, int k, int* tmp) {
+// top_fill >= 0: the top bin (nb - 1) was not counted; its count is top_fill
+// minus the other bins' total.
+__device__ __forceinline__ Round hist_pick(const uint32_t* hist, int nb, int k, int* tmp,
+                                           int top_fill) {
   const int per = (nb + blockDim.x - 1) / blockDim.x;
   const int d0 = threadIdx.x * per;
+  const bool implicit_top = top_fill >= 0;
   int cnt = 0;
-  for (int d = d0; d < d0 + per && d < nb; ++d) cnt += (int)hist[d];
+  for (int d = d0; d < d0 + per && d < nb; ++d)
+    cnt += (implicit_top && d == nb - 1) ? 0 : (int)hist[d];
   int total;
   int pre = block_excl_scan(cnt, tmp, &total);
+  const int top_count = implicit_top ? top_fill - total : 0;
+  if (implicit_top) total = top_fill;
   const int x = total - k;  // ascending rank of the k-th largest among the matched
   for (int d = d0; d < d0 + per && d < nb; ++d) {
-    const int c = (int)hist[d];
+    const int c = (implicit_top && d == nb - 1) ? top_count : (int)hist[d];
     if (pre <= x && x < pre + c) {
       tmp[18] = d;
       tmp[19] = total - (pre + c);
@@ -717,13 +725,11 @@ __global__ __launch_bounds__(256) void score_kernel(
 }
 
 // Histogram count of one key per lane (valid lanes only).  Keys above the band
-// all land in the top bin: those are counted once per wave (ballot popcount)
-// instead of by one LDS atomic each, which would serialise on one address.
-__device__ __forceinline__ void count_bin(uint32_t* hist, bool valid, int bin, int lane) {
-  const bool top = valid && bin == 2047;
-  const uint64_t m = __ballot(top);
-  if (valid && !top) atomicAdd(&hist[bin], 1u);
-  if (m != 0ull && lane == __builtin_ctzll(m)) atomicAdd(&hist[2047], (uint32_t)__popcll(m));
+// all land in the top bin, which is not counted here (its count is the list
+// length minus the other bins', taken by hist_pick): one LDS atomic each on one
+// address would serialise.
+__device__ __forceinline__ void count_bin(uint32_t* hist, bool valid, int bin) {
+  if (valid && bin != 2047) atomicAdd(&hist[bin], 1u);
 }
 
 // ------------------------------------------------------------------ select
@@ -879,10 +885,12 @@ __global__ __launch_bounds__(1024) void select_kernel(
           if (j < cnt) {
             dk[o + j] = kk[v][u];
             dp[o + j] = tt[v][u];
-            lo = min(lo, kk[v][u]);
-            hi = max(hi, kk[v][u]);
+            if constexpr (!kLds) {  // the LDS list takes its range only when needed
+              lo = min(lo, kk[v][u]);
+              hi = max(hi, kk[v][u]);
+            }
           }
-          if constexpr (kLds) count_bin(hist, j < cnt, bin_of(kk[v][u]), lane);
+          if constexpr (kLds) count_bin(hist, j < cnt, bin_of(kk[v][u]));
         }
         for (int j0 = 256; j0 < cnt; j0 += 64) {  // tiles with many candidates
           const int j = j0 + lane;
@@ -890,10 +898,12 @@ __global__ __launch_bounds__(1024) void select_kernel(
           if (j < cnt) {
             dk[o + j] = key;
             dp[o + j] = cand_t[src + j];
-            lo = min(lo, key);
-            hi = max(hi, key);
+            if constexpr (!kLds) {
+              lo = min(lo, key);
+              hi = max(hi, key);
+            }
           }
-          if constexpr (kLds) count_bin(hist, j < cnt, bin_of(key), lane);
+          if constexpr (kLds) count_bin(hist, j < cnt, bin_of(key));
         }
       }
     }
@@ -910,7 +920,7 @@ __global__ __launch_bounds__(1024) void select_kernel(
     // more than 64.
     Run rn;
     run_load(rn, lkey, lpos, C);
-    const Round rb = hist_pick(hist, 2048, top_k, tmp);
+    const Round rb = hist_pick(hist, 2048, top_k, tmp, C);
     Kth r;
     if (rb.count <= kSubMax) {
       if (tid == 0) scount = 0;
@@ -936,6 +946,12 @@ __global__ __launch_bounds__(1024) void select_kernel(
         r = Kth{rs.key, rb.above + rs.above, rs.need};
       }
     } else {  // degenerate spread (e.g. no usable bin scale): radix over the whole list
+#pragma unroll
+      for (int j = 0; j < kEmitRun; ++j)
+        if (rn.valid(j)) {
+          lo = min(lo, rn.key[j]);
+          hi = max(hi, rn.key[j]);
+        }
       block_minmax(lo, hi, mm, &lo, &hi);
       r = block_kth(lkey, C, top_k, lo, hi, hist, tmp, sub, &scount);
     }
