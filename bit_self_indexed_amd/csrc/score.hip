@@ -174,29 +174,26 @@ __device__ __forceinline__ Round hist_pick(const uint32_t* hist, int nb, int k, 
 }
 
 // need-th largest (1 <= need <= m <= 64) of the keys sub[0..m) by wave 0 alone:
-// a bitonic sort of the 64 lanes into descending order (missing lanes hold 0,
-// below every key of a real score), then the key in lane need-1 and the number
-// of keys above it.  Result in out[0] (key), out[1] (number of keys greater
-// than it).  Caller provides the barrier.
+// lane l holds key l and counts the keys above and equal to it, reading the
+// others one by one from lane registers (v_readlane, no LDS round trips); the
+// lanes with gt < need <= gt + eq hold the answer.  Result in out[0] (key),
+// out[1] (number of keys greater than it).  Caller provides the barrier.
 __device__ __forceinline__ void wave_kth(const uint32_t* sub, int m, int need, int* out) {
   if (threadIdx.x >= 64) return;
   const int lane = threadIdx.x;
-  uint32_t x = lane < m ? sub[lane] : 0u;
-#pragma unroll
-  for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const uint32_t y = (uint32_t)__shfl_xor((int)x, j);
-      const bool desc = (lane & k) == 0 || k == 64;
-      const bool low = (lane & j) == 0;
-      x = (low == desc) ? max(x, y) : min(x, y);
-    }
+  const uint32_t x = lane < m ? sub[lane] : 0u;
+  int gt = 0, eq = 0;
+  for (int i = 0; i < m; ++i) {
+    const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, i);
+    gt += y > x ? 1 : 0;
+    eq += y == x ? 1 : 0;
   }
-  const uint32_t kth = (uint32_t)__shfl((int)x, need - 1);
-  const int gt = __popcll(__ballot(x > kth));
+  const uint64_t hit = __ballot(lane < m && gt < need && need <= gt + eq);
+  const int l = (int)__builtin_ctzll(hit);  // hit != 0: the need-th largest exists
+  const int key = __builtin_amdgcn_readlane((int)x, l), above = __builtin_amdgcn_readlane(gt, l);
   if (lane == 0) {
-    out[0] = (int)kth;
-    out[1] = gt;
+    out[0] = key;
+    out[1] = above;
   }
 }
 
