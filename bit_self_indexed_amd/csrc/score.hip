@@ -42,46 +42,33 @@ constexpr int kSubMax = 1024;
 
 // ------------------------------------------------------------------ block helpers
 // Exclusive prefix sum of one int per thread over the block (blockDim a multiple
-// of 64, at most 1024).  tmp: LDS, >= 17 ints.  Returns the exclusive sum and the
-// block total.  Three barriers.
+// of 64, at most 1024).  tmp: LDS, >= 16 ints.  Returns the exclusive sum and the
+// block total.  Two barriers.
 __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_incl_scan(v);
   if (lane == 63) tmp[wave] = x;
   __syncthreads();
-  if (wave == 0) {
-    const int t = lane < nw ? tmp[lane] : 0;
-    int y = t;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const int z = __shfl_up(y, o);
-      if (lane >= o) y += z;
-    }
-    if (lane < nw) tmp[lane] = y - t;
-    if (lane == nw - 1) tmp[16] = y;
-  }
-  __syncthreads();
-  const int r = tmp[wave] + x - v;
-  *total = tmp[16];
-  __syncthreads();
-  return r;
+  const int t = lane < nw ? tmp[lane] : 0;  // wave totals in lanes 0..nw-1 (row 0)
+  const int ts = wave_incl_scan(t);
+  const int wbase = __builtin_amdgcn_readlane(ts, wave) - __builtin_amdgcn_readlane(t, wave);
+  *total = __builtin_amdgcn_readlane(ts, nw - 1);
+  __syncthreads();  // tmp may be reused as soon as this returns
+  return wbase + x - v;
 }
 
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, o));
-  return x;
+  const int r = row_allreduce((int)x, [](int a, int b) { return (int)min((uint32_t)a, (uint32_t)b); });
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane(r, 0), b = (uint32_t)__builtin_amdgcn_readlane(r, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane(r, 32), d = (uint32_t)__builtin_amdgcn_readlane(r, 48);
+  return min(min(a, b), min(c, d));
 }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o));
-  return x;
+  const int r = row_allreduce((int)x, [](int a, int b) { return (int)max((uint32_t)a, (uint32_t)b); });
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane(r, 0), b = (uint32_t)__builtin_amdgcn_readlane(r, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane(r, 32), d = (uint32_t)__builtin_amdgcn_readlane(r, 48);
+  return max(max(a, b), max(c, d));
 }
 
 // Block-wide min and max of per-thread values; tmp: LDS >= 32 uint32.
@@ -535,15 +522,11 @@ __global__ __launch_bounds__(1024) void prep_kernel(
     float s = qv[0][tid];
     for (int g = 1; g < G; ++g) s += qv[g][tid];
     qv[kMaxGroup][tid] = s;
-    float v = fabsf(s);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    const float v = wave_sum(fabsf(s));
     if (lane == 0) red_a[wave] = v;
   } else if (wave >= 2 && wave < 2 + G) {
     const int g = wave - 2;
-    float d = fmaf(qv[g][lane], mus[lane], qv[g][lane + 64] * mus[lane + 64]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) d += __shfl_xor(d, o);
+    const float d = wave_sum(fmaf(qv[g][lane], mus[lane], qv[g][lane + 64] * mus[lane + 64]));
     if (lane == 0) att_qmu[hq0 + g] = d;
   }
   for (int i = tid; i < G * kLut; i += blockDim.x)
@@ -558,8 +541,7 @@ __global__ __launch_bounds__(1024) void prep_kernel(
       float d = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) d = fmaf(qv[g][c0 + i], x[i], d);
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) d += __shfl_xor(d, o);
+      d = row_allreduce(d, [](float a, float b) { return a + b; });  // the row's 16 lanes
       if ((tid & 15) == 0) att_slog[(hq0 + g) * kSink + r] = d;
     }
   }
@@ -575,9 +557,7 @@ __global__ __launch_bounds__(1024) void prep_kernel(
                               : 0.0f;
   float A;
   if (has_cb) {
-    float x = fabsf(lv);
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+    const float x = row_allreduce(fabsf(lv), [](float a, float b) { return fmaxf(a, b); });
     if (tid < kLut && (tid & 15) == 0) jmax[tid >> 4] = x;
     __syncthreads();
     A = 0.0f;

@@ -244,6 +244,60 @@ __device__ __forceinline__ float selection_score(const int* __restrict__ itab, f
   return a * ((float)ilut_dot(itab, c) * inv_scale) + 0.0f;
 }
 
+// ---------------------------------------------------------------- cross-lane (DPP)
+// Moves within 16-lane rows (data-parallel primitives) and lane reads: plain
+// VALU work, where __shfl_* goes through the LDS crossbar (ds_bpermute) with
+// its latency on every step of a reduction or scan.
+enum : int {
+  kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118,
+  kDppRowRor1 = 0x121, kDppRowRor2 = 0x122, kDppRowRor4 = 0x124, kDppRowRor8 = 0x128,
+  kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143,
+};
+// x moved by kCtrl; lanes whose source is outside the row, or whose row is not
+// in kRowMask, read 0.
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ int dpp(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, kCtrl, kRowMask, 0xf, true);
+}
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(dpp<kCtrl>(__float_as_int(x)));
+}
+__device__ __forceinline__ float readlane(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+// Inclusive prefix sum over the 64 lanes (row scans, then rows 0-1 carried
+// into rows 1 and 3, then rows 0-1 into rows 2-3).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += dpp<kDppRowShr1>(x);
+  x += dpp<kDppRowShr2>(x);
+  x += dpp<kDppRowShr4>(x);
+  x += dpp<kDppRowShr8>(x);
+  x += dpp<kDppRowBcast15, 0xa>(x);
+  x += dpp<kDppRowBcast31, 0xc>(x);
+  return x;
+}
+
+// op over each 16-lane row, the result in every lane of the row.
+template <class T, class Op>
+__device__ __forceinline__ T row_allreduce(T x, Op op) {
+  x = op(x, dpp<kDppRowRor8>(x));
+  x = op(x, dpp<kDppRowRor4>(x));
+  x = op(x, dpp<kDppRowRor2>(x));
+  x = op(x, dpp<kDppRowRor1>(x));
+  return x;
+}
+
+// Sum over the 64 lanes, the same value in every lane.  Call it in wave-uniform
+// control flow and branch only on its result: lane reads inside a branch would
+// let the compiler move the reduction's last step into the branch, where the
+// lanes read no longer execute it.
+__device__ __forceinline__ float wave_sum(float x) {
+  const float v = row_allreduce(x, [](float a, float b) { return a + b; });
+  return (readlane(v, 0) + readlane(v, 16)) + (readlane(v, 32) + readlane(v, 48));
+}
+
 // Number of set bits of a 64-lane ballot below this lane.
 __device__ __forceinline__ int ballot_rank(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
