@@ -134,14 +134,15 @@ __device__ __forceinline__ void process_chunk(Acc<G>& st, const Chunk<G>& x, boo
     lg[i] = (live && 2 * i + half < G) ? dot * sm_log2 : -INFINITY;
   }
   // chunk max per head: heads of parity `half` live in this half of the wave
+  // (row maxima by DPP, then the four rows' values read as scalars)
   float cm[GH], co[GH];
 #pragma unroll
   for (int i = 0; i < GH; ++i) {
-    float v = lg[i];
-#pragma unroll
-    for (int o = 16; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    cm[i] = v;
-    co[i] = __shfl_xor(v, 32);
+    const float v = row_allreduce(lg[i], [](float a, float b) { return fmaxf(a, b); });
+    const float h0 = fmaxf(readlane(v, 0), readlane(v, 16));
+    const float h1 = fmaxf(readlane(v, 32), readlane(v, 48));
+    cm[i] = half ? h1 : h0;
+    co[i] = half ? h0 : h1;
   }
   float sc[G];
 #pragma unroll
@@ -314,10 +315,9 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(
     }
 #pragma unroll
   for (int i = 0; i < GH; ++i) {
-    float x = st.lsum[i];
-#pragma unroll
-    for (int o = 16; o > 0; o >>= 1) x += __shfl_xor(x, o);
-    st.lsum[i] = x;
+    const float x = row_allreduce(st.lsum[i], [](float a, float b) { return a + b; });
+    const float h0 = readlane(x, 0) + readlane(x, 16), h1 = readlane(x, 32) + readlane(x, 48);
+    st.lsum[i] = half ? h1 : h0;
   }
   if (lane < 16) {
 #pragma unroll
@@ -388,8 +388,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   for (int u = 0; u < kPre; ++u)
     if (sg + 8 * u < n_splits) m = fmaxf(m, mv[u].x);
   for (int sc = sg + 8 * kPre; sc < n_splits; sc += 8) m = fmaxf(m, ml[sc].x);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  {
+    const float v = row_allreduce(m, [](float a, float b) { return fmaxf(a, b); });
+    m = fmaxf(fmaxf(readlane(v, 0), readlane(v, 16)), fmaxf(readlane(v, 32), readlane(v, 48)));
+  }
   if (lane == 0) wred[0][wave] = m;
   __syncthreads();
   m = fmaxf(fmaxf(wred[0][0], wred[0][1]), fmaxf(wred[0][2], wred[0][3]));
@@ -416,8 +418,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     acc.z = fmaf(w, o4.z, acc.z);
     acc.w = fmaf(w, o4.w, acc.w);
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
+  l = wave_sum(l);
   if (lane == 0) wred[1][wave] = l;
   red[sg][cq * 4 + 0] = acc.x;
   red[sg][cq * 4 + 1] = acc.y;
