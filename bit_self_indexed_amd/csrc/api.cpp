@@ -17,7 +17,11 @@ using namespace sikv;
 
 constexpr size_t kAlign = 256;
 constexpr int kMaxChunks = 2048;
-constexpr int64_t kAttnBlocks = 512;  // attention grid target: two blocks per CU
+// Attention grid targets: one block per CU for bf16 values (256-byte rows; fewer
+// concurrent gather streams measured faster), two for 2-bit value records
+// (64 bytes; more waves to cover the gathers' latency).
+constexpr int64_t kAttnBlocksBf16 = 256;
+constexpr int64_t kAttnBlocksQv = 512;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -103,16 +107,17 @@ bool plan_score(const sikv_cache_desc* c, int n_q_heads, ScorePlan* p) {
 // Attention grid: the attended list (64 sinks + k) of each (b, KV head) is cut
 // into chunks of kAttnChunk entries; a block of four waves takes chunks_per_block
 // consecutive chunks (a multiple of 4, so every wave gets the same count), the
-// smallest such that the grid has at most two blocks per CU (and at most
+// smallest such that the grid stays within the value format's target (at most
 // kAttnMaxCpb, the block's LDS slice of positions): each wave then loops over
 // several chunks with its prefetch running ahead, which measured faster than
-// more, shorter-lived blocks.  Workspace: the block partials (o,
-// max, sum) and, for a standalone call, the query heads' tables.
+// more, shorter-lived blocks.  Workspace: the block partials (o, max, sum) and,
+// for a standalone call, the query heads' tables.
 void plan_attn(const sikv_cache_desc* c, int n_q_heads, int top_k, AttnPlan* p) {
   const int64_t BH = (int64_t)c->batch * c->n_kv_heads;
   const int64_t nch = cdiv((int64_t)kSink + top_k, kAttnChunk);
+  const int64_t target = c->vrec != nullptr ? kAttnBlocksQv : kAttnBlocksBf16;
   int64_t cpb = 4;
-  while (BH * cdiv(nch, cpb) > kAttnBlocks && cpb < kAttnMaxCpb) cpb += 4;
+  while (BH * cdiv(nch, cpb) > target && cpb < kAttnMaxCpb) cpb += 4;
   p->cpb = (int)cpb;
   p->n_splits = (int)cdiv(nch, cpb);
   const size_t rows = (size_t)c->batch * n_q_heads * p->n_splits;
