@@ -323,8 +323,8 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(the path shards by (batch, KV head) with no communication; see the design "
-              f"notes)", file=sys.stderr)
+              f"(the path shards by (batch, KV head) with no communication between GPUs, so "
+              f"N GPUs each holding 1/N of the heads step in the one-GPU time)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -7,8 +7,8 @@ Source of the method: the web summary of "Self-Indexing KVCache: Predicting
 Sparse Attention from Compressed Keys" (arXiv 2603.14224), technical summary.
 Citations below name its sections: §1 (problem), §2 (methodology),
 §2.1 items 1-4 (core components), §3 (contributions).  The summary prints no
-equations, so every formula here is the plainest reading of that prose; the
-readings are marked READING and listed in the design notes.
+equations, so every formula here is the plainest reading of that prose; each
+such reading is marked READING where it is made.
 
 Precision: every score, logit, softmax and weighted sum is fp64.  Two
 reductions are fp32 on purpose, because their exact bits decide the sign
