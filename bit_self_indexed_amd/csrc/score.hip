@@ -16,9 +16,10 @@
 //             256 equal segments) and takes a conservative threshold tau below
 //             the expected k-th score (the whole candidate set when it is small);
 //   score   - the HBM stream: 16-byte code + 4-byte scale per token, one lane per
-//             token, 2 KB table in LDS (16-entry look-ups never conflict in the
-//             LDS banks); tokens with score >= tau are written, in token order,
-//             to a per-tile slot (no atomics);
+//             token, one wave per tile with its loads a step ahead of its
+//             look-ups, 2 KB table in LDS (16-entry look-ups never conflict in
+//             the LDS banks); tokens with score >= tau are written, in token
+//             order, to a per-tile slot (no atomics);
 //   select  - one block per (b, h): radix select of the exact k-th largest over
 //             the candidates, then an ordered compaction (ascending positions,
 //             ties to the smaller position).  If fewer than k candidates passed
@@ -609,10 +610,19 @@ __global__ __launch_bounds__(1024) void prep_kernel(
 }
 
 // ------------------------------------------------------------------ score
-// One block per (tile of 256*U candidates, b*h); lane <-> token.  Tile base
-// pointers are block-uniform, so every load is a 32-bit lane offset from a
-// scalar base; full tiles load without bounds checks.
-template <int U>
+// One block per tile of 256*U candidates (lane <-> token); wave w scores the
+// tile's w-th quarter, U groups of 64 tokens, on its own, and the four waves
+// meet once more only to place their candidates.  Small enough (<= 64 VGPRs
+// at U = 8) for eight waves per SIMD, so that a 2048-tile grid is resident at
+// once.  Each wave issues all its loads before the table barrier; they are
+// unconditional, at token indices clamped to the sequence's last token
+// (always a valid row), so the compiler counts the loads in flight exactly
+// and each group waits only for its own data.  Rows are 32-bit lane offsets
+// from a wave-uniform base row: a 64-token group lies within one page of a
+// paged cache (groups start at multiples of 64, pages at multiples of
+// >= 256), so one page id serves the group.  Candidates (score >= tau) are
+// written in token order after the last load.
+template <int U, bool kPaged, int S = (U < 8 ? U : 8)>
 __global__ __launch_bounds__(256) void score_kernel(
     const uint8_t* __restrict__ codes, const float* __restrict__ alpha, RowMap rm,
     int n_tokens, int Hkv, const int32_t* __restrict__ seq_lens,
@@ -620,85 +630,120 @@ __global__ __launch_bounds__(256) void score_kernel(
     const float* __restrict__ tau, int n_chunks, uint32_t* __restrict__ cand_key,
     int32_t* __restrict__ cand_t, int32_t* __restrict__ chunk_count,
     float* __restrict__ scores_opt) {
-  __shared__ int itab[kLut];
-  __shared__ int wcnt[U * 4];
   constexpr int kChunk = 256 * U;
-  const int bh = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = kSink + blockIdx.x * kChunk;
-  const int64_t row0 = (int64_t)bh * rm.capacity + t0;  // contiguous rows; also the scores' index
-  const uint4* __restrict__ cb = reinterpret_cast<const uint4*>(codes) + row0;
-  const float* __restrict__ ab = alpha + row0;
+  constexpr int NS = U / S;  // steps of S groups; step s+2 is loaded once step s is scored
+  static_assert(U % S == 0, "tile shape");
+  __shared__ int itab[kLut];
+  __shared__ int wcnt[4];
+  const int bh = blockIdx.y, b = bh / Hkv, h = bh - b * Hkv;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: rows from scalar bases
+  const int nt = seq_len(seq_lens, b, n_tokens);
+  const int t0 = kSink + blockIdx.x * kChunk;  // the tile's first token
+  const int tw = t0 + wave * (64 * U);         // this wave's first token
+  const int lim = nt - tw;  // tokens of this wave's quarter in the sequence (<= 0: none)
   const int2 tv = reinterpret_cast<const int2*>(sel_lut + (int64_t)bh * kLut)[tid];
-  const int lim = seq_len(seq_lens, bh / Hkv, n_tokens) - t0;  // tokens of this tile that exist
-  uint4 c[U];
-  float a[U];
-  if (rm.table != nullptr) {
-    // Paged: the tile's 256 * U tokens span at most U + 1 pages (a page holds at
-    // least 256 tokens); their ids are block-uniform loads (scalar), and each
-    // lane picks its token's page from them.
-    const int b = bh / Hkv, h = bh - b * Hkv, lg = rm.lg_page;
-    const int32_t* __restrict__ tb = rm.table + (int64_t)b * rm.pps;
-    const int first = t0 >> lg, last = min((t0 + kChunk - 1) >> lg, rm.pps - 1);
-    int pgs[U + 1];
+  const int64_t hrow = (int64_t)bh * rm.capacity;  // contiguous: the head's first row
+  // Paged: the quarter's tokens (clamped to the sequence) span at most U + 1
+  // pages; lane j holds the id of the j-th, read out per group with a lane read
+  // (a per-group load would wait behind every code load in flight).
+  const int lg = rm.lg_page;
+  const int pfirst = min(tw, nt - 1) >> lg;
+  int pv = 0;
+  if constexpr (kPaged)
+    pv = rm.table[(int64_t)b * rm.pps + min(pfirst + lane, (nt - 1) >> lg)];
+  // Loads of step st; dep is a zero the compiler cannot see through, which ties
+  // a prefetch to the scoring it must follow.
+  uint4 c[NS][S];
+  float a[NS][S];
+  auto load_step = [&](int st, int dep) {
 #pragma unroll
-    for (int j = 0; j <= U; ++j) pgs[j] = tb[min(first + j, last)];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = u * 256 + tid, t = t0 + i, j = (t >> lg) - first;
-      int pg = pgs[0];
-#pragma unroll
-      for (int jj = 1; jj <= U; ++jj) pg = j == jj ? pgs[jj] : pg;
-      const int64_t r = (((int64_t)pg * Hkv + h) << lg) | (int64_t)(t & ((1 << lg) - 1));
-      c[u] = i < lim ? reinterpret_cast<const uint4*>(codes)[r] : make_uint4(0u, 0u, 0u, 0u);
-      a[u] = i < lim ? alpha[r] : 0.0f;
+    for (int u = 0; u < S; ++u) {
+      const int g0 = tw + (st * S + u) * 64;  // first token of the group
+      const int gb = min(g0, nt - 1);         // base row's token (uniform)
+      const uint32_t o = (uint32_t)(min(g0 + lane, nt - 1) - gb + dep);
+      int64_t r0;
+      if constexpr (kPaged) {
+        const int64_t pg = __builtin_amdgcn_readlane(pv, (gb >> lg) - pfirst);
+        r0 = ((pg * Hkv + h) << lg) | (int64_t)(gb & ((1 << lg) - 1));
+      } else {
+        r0 = hrow + gb;
+      }
+      c[st][u] = *reinterpret_cast<const uint4*>(
+          reinterpret_cast<const char*>(codes + r0 * kCodeBytes) + (o << 4));
+      a[st][u] = *reinterpret_cast<const float*>(
+          reinterpret_cast<const char*>(alpha + r0) + (o << 2));
     }
-  } else if (lim >= kChunk) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      c[u] = cb[u * 256 + tid];
-      a[u] = ab[u * 256 + tid];
-    }
-  } else {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = u * 256 + tid;
-      c[u] = i < lim ? cb[i] : make_uint4(0u, 0u, 0u, 0u);
-      a[u] = i < lim ? ab[i] : 0.0f;
-    }
-  }
-  reinterpret_cast<int2*>(itab)[tid] = tv;
+  };
+  load_step(0, 0);
+  if constexpr (NS > 1) load_step(1, 0);
+  int tz;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(tz));  // the table is stored after the loads go out
+  reinterpret_cast<int2*>(itab)[tid] = make_int2(tv.x ^ tz, tv.y ^ tz);
   const float inv = sel_inv[bh];
   const float th = tau[bh];
   __syncthreads();
-  uint64_t mask[U];
   uint32_t key[U];
+  uint32_t bits = 0;  // bit g: token g*64 + lane of the quarter passed
+  // gate: a zero from an asm placed after the previous step's prefetch; the
+  // step's codes and scales are read through it, so their use (and the wait
+  // for them) cannot move ahead of that prefetch.
+  auto score_step = [&](int st, int gate) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int i = u * 256 + tid;
-    const float s = selection_score(itab, inv, c[u], a[u]);
-    if (scores_opt != nullptr && i < lim) scores_opt[row0 + i] = s;
-    key[u] = score_key(s);
-    mask[u] = __ballot(i < lim && s >= th);
-    if (lane == 0) wcnt[u * 4 + wave] = __popcll(mask[u]);
+    for (int u = 0; u < S; ++u) {
+      const int g = st * S + u;
+      uint4 cg = c[st][u];
+      cg.x ^= gate, cg.y ^= gate, cg.z ^= gate, cg.w ^= gate;
+      const float ag = __int_as_float(__float_as_int(a[st][u]) ^ gate);
+      const float sv = selection_score(itab, inv, cg, ag);
+      key[g] = score_key(sv);
+      if (g * 64 + lane < lim && sv >= th) bits |= 1u << g;
+    }
+  };
+  int gate;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(gate));
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    score_step(st, gate);
+    if (st + 2 < NS) {
+      int dep;  // the prefetch follows this step's look-ups
+      asm volatile("v_mov_b32 %0, 0" : "=v"(dep) : "v"(bits));
+      load_step(st + 2, dep);
+      __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued here, not sunk
+    }
+    // after the prefetch and after this step's sums (so that a step's look-ups
+    // are not all issued before its first sum)
+    asm volatile("v_mov_b32 %0, 0" : "=v"(gate) : "v"(bits));
   }
+  int cnt = 0;
+#pragma unroll
+  for (int g = 0; g < U; ++g) cnt += __popcll(__ballot((bits >> g) & 1u));
+  if (lane == 0) wcnt[wave] = cnt;
   __syncthreads();
-  int run = 0;
+  int run = 0;  // candidates of the waves before this one
+#pragma unroll
+  for (int w = 0; w < 3; ++w) run += w < wave ? wcnt[w] : 0;
   const int64_t slot = ((int64_t)bh * n_chunks + blockIdx.x) * kChunk;
   uint32_t* __restrict__ kout = cand_key + slot;
   int32_t* __restrict__ tout = cand_t + slot;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int4 w4 = reinterpret_cast<const int4*>(wcnt)[u];
-    const int before = (wave > 0 ? w4.x : 0) + (wave > 1 ? w4.y : 0) + (wave > 2 ? w4.z : 0);
-    if ((mask[u] >> lane) & 1ull) {
-      const int p = run + before + ballot_rank(mask[u]);
-      kout[p] = key[u];
-      tout[p] = t0 + u * 256 + tid;
+  for (int g = 0; g < U; ++g) {
+    const bool pass = (bits >> g) & 1u;
+    const uint64_t m = __ballot(pass);
+    if (pass) {
+      const int p = run + ballot_rank(m);
+      kout[p] = key[g];
+      tout[p] = tw + g * 64 + lane;
     }
-    run += (w4.x + w4.y) + (w4.z + w4.w);
+    run += __popcll(m);
   }
-  if (tid == 0) chunk_count[(int64_t)bh * n_chunks + blockIdx.x] = run;
+  if (scores_opt != nullptr) {  // key_score inverts score_key exactly
+    float* __restrict__ so = scores_opt + hrow + tw;
+#pragma unroll
+    for (int g = 0; g < U; ++g)
+      if (g * 64 + lane < lim) so[g * 64 + lane] = key_score(key[g]);
+  }
+  if (tid == 255) chunk_count[(int64_t)bh * n_chunks + blockIdx.x] = run;  // the last wave's run ends the tile
 }
 
 // Histogram count of one key per lane (valid lanes only).  Keys above the band
@@ -963,9 +1008,13 @@ hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha
   const dim3 grid(n_chunks, B * Hkv), block(256);
 #define SIKV_SCORE_CASE(UU)                                                                    \
   case 256 * UU:                                                                               \
-    return launch_k(KID_SCORE, score_kernel<UU>, grid, block, 0, s, codes, alpha, rm,          \
-                    n_tokens, Hkv, seq_lens, sel_lut, sel_inv, tau, n_chunks, cand_key,        \
-                    cand_t, chunk_count, scores_opt);
+    return rm.table != nullptr                                                                 \
+               ? launch_k(KID_SCORE, score_kernel<UU, true>, grid, block, 0, s, codes, alpha,  \
+                          rm, n_tokens, Hkv, seq_lens, sel_lut, sel_inv, tau, n_chunks,        \
+                          cand_key, cand_t, chunk_count, scores_opt)                           \
+               : launch_k(KID_SCORE, score_kernel<UU, false>, grid, block, 0, s, codes, alpha, \
+                          rm, n_tokens, Hkv, seq_lens, sel_lut, sel_inv, tau, n_chunks,        \
+                          cand_key, cand_t, chunk_count, scores_opt);
   switch (chunk) {
     SIKV_SCORE_CASE(1)
     SIKV_SCORE_CASE(2)
