@@ -945,11 +945,47 @@ __global__ __launch_bounds__(1024) void select_kernel(
     const Round rb = hist_pick(hist, 2048, top_k, tmp, C);
     Kth r;
     if (rb.count <= kSubMax) {
+      // The keys of the k-th's bin d form one interval [klo, khi] (bin_of never
+      // decreases as the key grows; patterns above +inf are taken as the top
+      // bin), so that the pass below compares keys instead of recomputing every
+      // bin.  Wave 0 finds the first key of a bin >= d, wave 1 of a bin >= d+1:
+      // 64 keys around the key of tau + e / bin_scale, or, if the boundary is
+      // not among them, 6 bits a round from the top.
+      if (tid < 128) {
+        const int lane = tid & 63, d = rb.digit;
+        const int e = tid < 64 ? d : d + 1;
+        auto below = [&](uint32_t k) {  // bin of k < e
+          return (k > 0xff800000u ? 2047 : bin_of(k)) < e;
+        };
+        uint32_t first = 0u;  // e == 0: every key
+        if (e > 2047) {
+          first = 0xffffffffu;  // none: khi ends at the last key
+        } else if (e > 0) {
+          const uint32_t x0 = score_key(th + (float)e / bsc);
+          const uint32_t base = min(max(x0, 32u), 0xffffffffu - 63u) - 32u;
+          const int t = __popcll(__ballot(below(base + (uint32_t)lane)));
+          if (t > 0 && t < 64) {
+            first = base + (uint32_t)t;
+          } else {
+            uint32_t a = 0u;  // the last key below e (key 0 is: bin 0 < e)
+#pragma unroll
+            for (int r = 0; r < 6; ++r) {
+              const int sh = r < 5 ? 26 - 6 * r : 0;  // bits 31..26, ..., 7..2, then 1..0
+              const bool ok = (r < 5 || lane < 4) && below(a | ((uint32_t)lane << sh));
+              a |= (uint32_t)(__popcll(__ballot(ok)) - 1) << sh;
+            }
+            first = a + 1u;
+          }
+        }
+        if (lane == 0) mm[tid >> 6] = tid < 64 ? first : (e > 2047 ? first : first - 1u);
+      }
       if (tid == 0) scount = 0;
       __syncthreads();
+      const uint32_t klo = mm[0], khi = mm[1];
 #pragma unroll
       for (int j = 0; j < kEmitRun; ++j)
-        if (rn.valid(j) && bin_of(rn.key[j]) == rb.digit) sub[atomicAdd(&scount, 1)] = rn.key[j];
+        if (rn.valid(j) && rn.key[j] >= klo && rn.key[j] <= khi)
+          sub[atomicAdd(&scount, 1)] = rn.key[j];
       __syncthreads();
       const int ns = scount, need = top_k - rb.above;
       if (ns <= 64) {
