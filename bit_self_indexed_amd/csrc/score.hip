@@ -74,7 +74,8 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
 
 // Block-wide min and max of per-thread values; tmp: LDS >= 32 uint32.
 __device__ __forceinline__ void block_minmax(uint32_t lo, uint32_t hi, uint32_t* tmp,
-                                             uint32_t* out_lo, uint32_t* out_hi) {
+                                             uint32_t* out_lo, uint32_t* out_hi,
+                                             bool reuse = true) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   lo = wave_min_u32(lo);
   hi = wave_max_u32(hi);
@@ -90,7 +91,7 @@ __device__ __forceinline__ void block_minmax(uint32_t lo, uint32_t hi, uint32_t*
   }
   *out_lo = a;
   *out_hi = c;
-  __syncthreads();
+  if (reuse) __syncthreads();  // before tmp is written again
 }
 
 struct Kth {
@@ -326,7 +327,9 @@ __device__ __forceinline__ void load_itab(const int* __restrict__ gtab, int* ita
 // [smin, smax]: *lo at or below the k_lo-th largest (the lower edge of its bin,
 // lowered by one more bin so that rounding cannot lift it above), and *hi at or
 // above the k_hi-th largest (the upper edge of its bin, raised by one more bin;
-// smax if k_hi < 1).  1 <= k_lo <= n.  hist: LDS >= 2048; tmp: LDS >= 24 ints.
+// smax if k_hi < 1).  1 <= k_lo <= n.  hist: LDS, 2048 counters already zero
+// (and published); tmp: LDS >= 24 ints, which hold the two bins on return (no
+// barrier after their last read: the caller does not reuse tmp or hist).
 __device__ void block_score_band(const float* sc, int n, int k_lo, int k_hi, float smin,
                                  float smax, uint32_t* hist, int* tmp, float* lo, float* hi) {
   if (!(smax > smin)) {
@@ -337,8 +340,6 @@ __device__ void block_score_band(const float* sc, int n, int k_lo, int k_hi, flo
   constexpr int kBins = 2048;
   const float w = (smax - smin) * (1.0f / kBins);
   const float inv = (float)kBins / (smax - smin);
-  for (int i = threadIdx.x; i < kBins; i += blockDim.x) hist[i] = 0u;
-  __syncthreads();
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
     const int d = min(max((int)((sc[i] - smin) * inv), 0), kBins - 1);
     atomicAdd(&hist[d], 1u);
@@ -348,12 +349,11 @@ __device__ void block_score_band(const float* sc, int n, int k_lo, int k_hi, flo
   const int d0 = threadIdx.x * per;
   int cnt = 0;
   for (int d = d0; d < d0 + per && d < kBins; ++d) cnt += (int)hist[d];
+  if (threadIdx.x == 0) tmp[21] = kBins - 1;  // published by the scan's barriers
   int total;
-  int pre = block_excl_scan(cnt, tmp, &total);
+  int pre = block_excl_scan(cnt, tmp, &total);  // uses tmp[0..15]
   const int x_lo = total - k_lo;  // ascending ranks of the k-th largest
   const int x_hi = total - k_hi;
-  if (threadIdx.x == 0) tmp[21] = kBins - 1;
-  __syncthreads();
   for (int d = d0; d < d0 + per && d < kBins; ++d) {
     const int c = (int)hist[d];
     if (pre <= x_lo && x_lo < pre + c) tmp[18] = d;
@@ -362,7 +362,6 @@ __device__ void block_score_band(const float* sc, int n, int k_lo, int k_hi, flo
   }
   __syncthreads();
   const int dl = tmp[18], dh = tmp[21];
-  __syncthreads();
   *lo = smin + (float)(dl - 1) * w;
   *hi = k_hi >= 1 ? fminf(smax, smin + (float)(dh + 2) * w) : smax;
 }
@@ -428,6 +427,8 @@ __global__ __launch_bounds__(1024) void prep_kernel(
   const float4 cbv = (has_cb && tid < kLut)
                          ? reinterpret_cast<const float4*>(codebook)[(int64_t)bh * kLut + tid]
                          : make_float4(0.f, 0.f, 0.f, 0.f);
+
+  for (int i = tid; i < 2048; i += blockDim.x) hist[i] = 0u;  // the band's counters
 
   // Appended value row (quantised values): 16 lanes of wave 1, 8 channels each.
   uint4 vw = make_uint4(0u, 0u, 0u, 0u);
@@ -597,7 +598,7 @@ __global__ __launch_bounds__(1024) void prep_kernel(
       hi = max(hi, score_key(sv));
     }
   }
-  block_minmax(lo, hi, mm, &lo, &hi);  // its barriers also publish ssc
+  block_minmax(lo, hi, mm, &lo, &hi, false);  // its barrier also publishes ssc; mm is not reused
   float th, th_hi;
   block_score_band(ssc, m, rank, rank_hi, key_score(lo), key_score(hi), hist, tmp, &th, &th_hi);
   if (tid == 0) {
