@@ -688,7 +688,9 @@ __global__ __launch_bounds__(256) void score_kernel(
   uint32_t bits = 0;  // bit g: token g*64 + lane of the quarter passed
   // gate: a zero from an asm placed after the previous step's prefetch; the
   // step's codes and scales are read through it, so their use (and the wait
-  // for them) cannot move ahead of that prefetch.
+  // for them) cannot move ahead of that prefetch.  With one step it still
+  // keeps the decode after the table barrier: without it the compiler hoists
+  // most look-ups into one batch (85 VGPRs, fewer waves per SIMD).
   auto score_step = [&](int st, int gate) {
 #pragma unroll
     for (int u = 0; u < S; ++u) {
