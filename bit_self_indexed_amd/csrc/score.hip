@@ -632,8 +632,8 @@ __global__ __launch_bounds__(256) void score_kernel(
     int32_t* __restrict__ cand_t, int32_t* __restrict__ chunk_count,
     float* __restrict__ scores_opt) {
   constexpr int kChunk = 256 * U;
-  constexpr int NS = U / S;  // steps of S groups; step s+2 is loaded once step s is scored
-  static_assert(U % S == 0, "tile shape");
+  constexpr int NS = U / S;  // steps of S groups, all loaded before the table barrier
+  static_assert(U % S == 0 && NS <= 2, "tile shape");
   __shared__ int itab[kLut];
   __shared__ int wcnt[4];
   const int bh = blockIdx.y, b = bh / Hkv, h = bh - b * Hkv;
@@ -653,16 +653,15 @@ __global__ __launch_bounds__(256) void score_kernel(
   int pv = 0;
   if constexpr (kPaged)
     pv = rm.table[(int64_t)b * rm.pps + min(pfirst + lane, (nt - 1) >> lg)];
-  // Loads of step st; dep is a zero the compiler cannot see through, which ties
-  // a prefetch to the scoring it must follow.
+  // Loads of step st.
   uint4 c[NS][S];
   float a[NS][S];
-  auto load_step = [&](int st, int dep) {
+  auto load_step = [&](int st) {
 #pragma unroll
     for (int u = 0; u < S; ++u) {
       const int g0 = tw + (st * S + u) * 64;  // first token of the group
       const int gb = min(g0, nt - 1);         // base row's token (uniform)
-      const uint32_t o = (uint32_t)(min(g0 + lane, nt - 1) - gb + dep);
+      const uint32_t o = (uint32_t)(min(g0 + lane, nt - 1) - gb);
       int64_t r0;
       if constexpr (kPaged) {
         const int64_t pg = __builtin_amdgcn_readlane(pv, (gb >> lg) - pfirst);
@@ -676,8 +675,8 @@ __global__ __launch_bounds__(256) void score_kernel(
           reinterpret_cast<const char*>(alpha + r0) + (o << 2));
     }
   };
-  load_step(0, 0);
-  if constexpr (NS > 1) load_step(1, 0);
+  load_step(0);
+  if constexpr (NS > 1) load_step(1);
   int tz;
   asm volatile("v_mov_b32 %0, 0" : "=v"(tz));  // the table is stored after the loads go out
   reinterpret_cast<int2*>(itab)[tid] = make_int2(tv.x ^ tz, tv.y ^ tz);
@@ -686,10 +685,9 @@ __global__ __launch_bounds__(256) void score_kernel(
   __syncthreads();
   uint32_t key[U];
   uint32_t bits = 0;  // bit g: token g*64 + lane of the quarter passed
-  // gate: a zero from an asm placed after the previous step's prefetch; the
-  // step's codes and scales are read through it, so their use (and the wait
-  // for them) cannot move ahead of that prefetch.  With one step it still
-  // keeps the decode after the table barrier: without it the compiler hoists
+  // gate: a zero from an asm placed after the table barrier (then after the
+  // previous step's sums); the step's codes and scales are read through it, so
+  // their decode stays behind it, in order: without it the compiler hoists
   // most look-ups into one batch (85 VGPRs, fewer waves per SIMD).
   auto score_step = [&](int st, int gate) {
 #pragma unroll
@@ -708,14 +706,8 @@ __global__ __launch_bounds__(256) void score_kernel(
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
     score_step(st, gate);
-    if (st + 2 < NS) {
-      int dep;  // the prefetch follows this step's look-ups
-      asm volatile("v_mov_b32 %0, 0" : "=v"(dep) : "v"(bits));
-      load_step(st + 2, dep);
-      __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued here, not sunk
-    }
-    // after the prefetch and after this step's sums (so that a step's look-ups
-    // are not all issued before its first sum)
+    // after this step's sums (so that the next step's look-ups are not issued
+    // before them, nor this step's sums moved past the count exchange)
     asm volatile("v_mov_b32 %0, 0" : "=v"(gate) : "v"(bits));
   }
   int cnt = 0;
