@@ -116,3 +116,32 @@ def test_paged_pool_matches_contiguous(name, N, lengths, k, page):
     a, b = _step(cont, q, k), _step(paged, q, k)
     assert torch.equal(a[0], b[0]), f"{name} page={page}: top-k"
     assert torch.equal(a[1], b[1]), f"{name} page={page}: attention"
+
+
+def test_sixteen_groups_per_wave():
+    """Past 2048 tiles of 2048 tokens the plan doubles the tile (U = 16, two
+    load steps per wave): one head of 4.2M tokens, the candidate path against
+    the select kernel's exact rescan of the whole head."""
+    n = 2049 * 2048 + 100            # candidates: 2050 tiles of 2048 would exceed 2048
+    N, k = 64 + n, 5000
+    say(f"[tiles] U16 N={N} k={k}")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(16)
+    K = torch.randn((1, 1, N, 128), generator=g, device="cuda").to(torch.bfloat16)
+    V = torch.randn((1, 1, N, 128), generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn((1, 4, 128), generator=g, device="cuda").to(torch.bfloat16)
+    cache = sk.Cache(1, 1, N, v=V)
+    sk.sikv_encode(cache, K)
+    del K
+    i1 = torch.empty((1, 1, k), dtype=torch.int32, device="cuda")
+    o1 = sk.sikv_decode_step(cache, q, k, SM, idx_out=i1).cpu()
+    sk.debug_force_exact_select(True)
+    try:
+        i2 = torch.empty_like(i1)
+        o2 = sk.sikv_decode_step(cache, q, k, SM, idx_out=i2).cpu()
+    finally:
+        sk.debug_force_exact_select(False)
+    torch.cuda.synchronize()
+    assert torch.equal(i1.cpu(), i2.cpu()), "U16 top-k against the exact rescan"
+    assert torch.equal(o1, o2), "U16 attention"
+    assert int(i1.min()) >= 64 and int(i1.max()) < N
