@@ -12,8 +12,8 @@
 //             that a token's 32 look-ups are summed exactly with 3-input integer
 //             adds), the attention tables of the G query heads, their q.mu and
 //             the exact logits of the 64 sinks; then scores a stratified sample
-//             of 4096 candidates (16 contiguous tokens from the middle of each of
-//             256 equal segments) and takes a conservative threshold tau below
+//             of 3072 candidates (16 contiguous tokens from the middle of each of
+//             192 equal segments) and takes a conservative threshold tau below
 //             the expected k-th score (the whole candidate set when it is small);
 //   score   - the HBM stream: 16-byte code + 4-byte scale per token, one lane per
 //             token, one wave per tile with its loads a step ahead of its
@@ -35,8 +35,8 @@ namespace sikv {
 
 namespace {
 
-constexpr int kSampleMax = 4096;   // sampled candidates per head
-constexpr int kSampleRun = 16;     // contiguous tokens per stratum (256 strata)
+constexpr int kSampleMax = 3072;   // sampled candidates per head
+constexpr int kSampleRun = 16;     // contiguous tokens per stratum (192 strata)
 constexpr int kSelectLds = 16384;  // candidates kept in LDS by select
 constexpr int kMaxChunks = 2048;
 constexpr int kSubMax = 1024;
@@ -367,8 +367,8 @@ __device__ void block_score_band(const float* sc, int n, int k_lo, int k_hi, flo
 }
 
 // rank: how many of the sampled scores lie at or above tau.  For a small head the
-// whole candidate set (n <= 4096) is the sample and rank = k (tau is then at most
-// the exact k-th score).  Otherwise the expected rank e = k * 4096 / n of the k-th
+// whole candidate set (n <= 3072) is the sample and rank = k (tau is then at most
+// the exact k-th score).  Otherwise the expected rank e = k * 3072 / n of the k-th
 // score in the sample plus five standard deviations and a small floor, so that
 // fewer than k tokens pass only with negligible probability (the select kernel
 // handles that case exactly anyway).  rank_hi: the rank of the upper end of the
@@ -456,7 +456,7 @@ __global__ __launch_bounds__(1024) void prep_kernel(
   const uint16_t qraw = q[hq0 * kD + min(tid, G * kD - 1)];
   const float mraw = mu[(int64_t)bh * kD + min(tid, kD - 1)];
 
-  // Sample rows: stratum st = i / 16 of 256 equal segments, 16 tokens centred in
+  // Sample rows: stratum st = i / 16 of 192 equal segments, 16 tokens centred in
   // it (the whole candidate set when small).  Every lane loads a real row (token
   // 64 for unused slots, never scored), so the wait counts do not depend on
   // which lanes sample; page ids, if paged, are all loaded before any code.
