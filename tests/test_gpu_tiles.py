@@ -145,3 +145,30 @@ def test_sixteen_groups_per_wave():
     assert torch.equal(i1.cpu(), i2.cpu()), "U16 top-k against the exact rescan"
     assert torch.equal(o1, o2), "U16 attention"
     assert int(i1.min()) >= 64 and int(i1.max()) < N
+
+
+@pytest.mark.parametrize("page", [256])
+def test_paged_quantised_values_match_contiguous(page):
+    """2-bit value records at the U = 8 shape: a paged pool against a contiguous
+    cache, both with ragged lengths (bit-identical positions and outputs)."""
+    name, N, lengths, k = SHAPES[0]
+    say(f"[tiles] paged 2-bit {name} page={page} N={N} lengths={lengths} k={k}")
+    K, V, q = _draw(N, 700 + page)
+    pps = -(-N // page)
+    cap = pps * page
+    n_pages = B * pps + 3
+    perm = np.random.default_rng(page + N + 1).permutation(n_pages)[:B * pps].reshape(B, pps)
+    table = torch.tensor(perm, dtype=torch.int32, device="cuda")
+    cont = sk.Cache(B, HKV, cap, quant_v=True)
+    paged = sk.Cache.paged(B, HKV, page, n_pages, table, quant_v=True)
+    for c in (cont, paged):
+        for b, n in enumerate(lengths):
+            vb = c.view(b)
+            vb.n_tokens = n
+            sk.sikv_encode(vb, K[b:b + 1, :, :n])
+            sk.sikv_encode_v(vb, V[b:b + 1, :, :n])
+        c.n_tokens = max(lengths)
+        c.seq_lens = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    a, b = _step(cont, q, k), _step(paged, q, k)
+    assert torch.equal(a[0], b[0]), f"2-bit page={page}: top-k"
+    assert torch.equal(a[1], b[1]), f"2-bit page={page}: attention"
