@@ -750,6 +750,79 @@ __device__ __forceinline__ void count_bin(uint32_t* hist, bool valid, int bin) {
 }
 
 // ------------------------------------------------------------------ select
+// The select kernel's rare paths, kept out of line: inlined, their live values
+// pushed the common path past the SGPR budget (54 spilled SGPRs, reloaded by
+// lane reads; out of line, 42 around the calls, and the select kernel went from
+// 14.26 to 13.63 us at long_128k).
+
+// Fewer than k candidates passed: rescore the whole head with the score
+// kernel's table and arithmetic, in order, and select over all of it.
+__device__ __noinline__ void select_exact_head(
+    const uint8_t* __restrict__ codes, const float* __restrict__ alpha, RowMap rm, int Hkv,
+    int bh, int n, int top_k, const int* __restrict__ sel_lut, const float* __restrict__ sel_inv,
+    uint32_t* __restrict__ comp_key, int32_t* __restrict__ comp_t, int* itab, uint32_t* hist,
+    int* tmp, uint32_t* sub, int* scount, uint32_t* mm, int32_t* __restrict__ out) {
+  const int tid = threadIdx.x;
+  load_itab(sel_lut + (int64_t)bh * kLut, itab);
+  const float inv = sel_inv[bh];
+  __syncthreads();
+  const int b = bh / Hkv, h = bh - b * Hkv;
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  for (int i = tid; i < n; i += blockDim.x) {
+    const int t = kSink + i;
+    const int64_t r = rm.row(b, h, t);
+    const uint4 c = *reinterpret_cast<const uint4*>(codes + r * kCodeBytes);
+    const uint32_t key = score_key(selection_score(itab, inv, c, alpha[r]));
+    comp_key[i] = key;
+    comp_t[i] = t;
+    lo = min(lo, key);
+    hi = max(hi, key);
+  }
+  block_minmax(lo, hi, mm, &lo, &hi);
+  const Kth r = block_kth(comp_key, n, top_k, lo, hi, hist, tmp, sub, scount);
+  block_emit(comp_key, comp_t, n, top_k, r, out, tmp);
+}
+
+// More candidates than the LDS list holds: the ordered list goes to the
+// workspace (tile by tile, wave w taking tiles w, w + 16, ...) and radix rounds
+// select over it.
+__device__ __noinline__ void select_workspace(
+    const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_t, int chunk,
+    int n_chunks, const int* off, int C, int top_k, uint32_t* __restrict__ comp_key,
+    int32_t* __restrict__ comp_t, uint32_t* hist, int* tmp, uint32_t* sub, int* scount,
+    uint32_t* mm, int32_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  for (int ci = wave; ci < n_chunks; ci += nw) {
+    const int o = off[ci], cnt = off[ci + 1] - o;
+    const int64_t src = (int64_t)ci * chunk;
+    for (int j = lane; j < cnt; j += 64) {
+      const uint32_t key = cand_key[src + j];
+      comp_key[o + j] = key;
+      comp_t[o + j] = cand_t[src + j];
+      lo = min(lo, key);
+      hi = max(hi, key);
+    }
+  }
+  block_minmax(lo, hi, mm, &lo, &hi);  // its barriers also publish the copies
+  const Kth r = block_kth(comp_key, C, top_k, lo, hi, hist, tmp, sub, scount);
+  block_emit(comp_key, comp_t, C, top_k, r, out, tmp);
+}
+
+// The k-th's bin holds too many keys (e.g. no usable bin scale): radix rounds
+// over the whole LDS list.
+__device__ __noinline__ Kth select_degenerate(const uint32_t* lkey, int C, int top_k,
+                                              uint32_t* hist, int* tmp, uint32_t* sub,
+                                              int* scount, uint32_t* mm) {
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  for (int i = threadIdx.x; i < C; i += blockDim.x) {
+    lo = min(lo, lkey[i]);
+    hi = max(hi, lkey[i]);
+  }
+  block_minmax(lo, hi, mm, &lo, &hi);
+  return block_kth(lkey, C, top_k, lo, hi, hist, tmp, sub, scount);
+}
+
 __global__ __launch_bounds__(1024) void select_kernel(
     const uint8_t* __restrict__ codes, const float* __restrict__ alpha, RowMap rm,
     int n_tokens, int Hkv, const int32_t* __restrict__ seq_lens,
@@ -823,27 +896,10 @@ __global__ __launch_bounds__(1024) void select_kernel(
   }
   const int C = off[n_chunks];
   uint32_t lo = 0xffffffffu, hi = 0u;
-  if (C < top_k) {
-    // Exact path over the whole head: rescore every candidate with the same
-    // table and arithmetic as the score kernel, in order.
-    int* itab = reinterpret_cast<int*>(lkey);  // the LDS list is unused here
-    load_itab(sel_lut + (int64_t)bh * kLut, itab);
-    const float inv = sel_inv[bh];
-    __syncthreads();
-    const int b = bh / Hkv, h = bh - b * Hkv;
-    for (int i = tid; i < n; i += blockDim.x) {
-      const int t = kSink + i;
-      const int64_t r = rm.row(b, h, t);
-      const uint4 c = *reinterpret_cast<const uint4*>(codes + r * kCodeBytes);
-      const uint32_t key = score_key(selection_score(itab, inv, c, alpha[r]));
-      comp_key[cbase + i] = key;
-      comp_t[cbase + i] = t;
-      lo = min(lo, key);
-      hi = max(hi, key);
-    }
-    block_minmax(lo, hi, mm, &lo, &hi);
-    const Kth r = block_kth(comp_key + cbase, n, top_k, lo, hi, hist, tmp, sub, &scount);
-    block_emit(comp_key + cbase, comp_t + cbase, n, top_k, r, out, tmp);
+  if (C < top_k) {  // the LDS list is unused: it holds the table
+    select_exact_head(codes, alpha, rm, Hkv, bh, n, top_k, sel_lut, sel_inv, comp_key + cbase,
+                      comp_t + cbase, reinterpret_cast<int*>(lkey), hist, tmp, sub, &scount, mm,
+                      out);
     return;
   }
   // Gather the candidates into one ordered list.  Wave w copies tiles w, w+nw,
@@ -925,10 +981,12 @@ __global__ __launch_bounds__(1024) void select_kernel(
       }
     }
   };
-  if (in_lds)
-    gather(std::true_type{});
-  else
-    gather(std::false_type{});
+  if (!in_lds) {
+    select_workspace(cand_key + cbase, cand_t + cbase, chunk, n_chunks, off, C, top_k,
+                     comp_key + cbase, comp_t + cbase, hist, tmp, sub, &scount, mm, out);
+    return;
+  }
+  gather(std::true_type{});
   if (in_lds) {
     __syncthreads();  // publishes the list and the histogram
     // Each thread's run of the list goes to registers while the histogram is
@@ -999,20 +1057,9 @@ __global__ __launch_bounds__(1024) void select_kernel(
         r = Kth{rs.key, rb.above + rs.above, rs.need};
       }
     } else {  // degenerate spread (e.g. no usable bin scale): radix over the whole list
-#pragma unroll
-      for (int j = 0; j < kEmitRun; ++j)
-        if (rn.valid(j)) {
-          lo = min(lo, rn.key[j]);
-          hi = max(hi, rn.key[j]);
-        }
-      block_minmax(lo, hi, mm, &lo, &hi);
-      r = block_kth(lkey, C, top_k, lo, hi, hist, tmp, sub, &scount);
+      r = select_degenerate(lkey, C, top_k, hist, tmp, sub, &scount, mm);
     }
     run_emit(rn, top_k, r, lkey, out, tmp);
-  } else {
-    block_minmax(lo, hi, mm, &lo, &hi);  // its barriers also publish the copies
-    const Kth r = block_kth(comp_key + cbase, C, top_k, lo, hi, hist, tmp, sub, &scount);
-    block_emit(comp_key + cbase, comp_t + cbase, C, top_k, r, out, tmp);
   }
 }
 
