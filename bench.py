@@ -36,6 +36,23 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def kernel_times(sk, caches, run):
+    """Per-kernel (launches, total ms) of run(), timed by a caller-owned timer
+    attached to the given caches for the duration of the call."""
+    import torch
+    timer = sk.Timer()
+    for c in caches:
+        c.timer = timer
+    try:
+        run()
+        torch.cuda.synchronize()
+        return timer.read()
+    finally:
+        for c in caches:
+            c.timer = None
+        timer.close()
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -429,13 +446,11 @@ def main():
     del src, dst
 
     # per-kernel durations (event-bracketed launches, eager, same rotation)
-    sk.timing_reset()
-    sk.timing_enable(True)
-    for i in range(args.steps):
-        step(i % L)
-    torch.cuda.synchronize()
-    kt = sk.timing_read()
-    sk.timing_enable(False)
+    def run_steps():
+        for i in range(args.steps):
+            step(i % L)
+
+    kt = kernel_times(sk, caches, run_steps)
     kern_us = {name: 1e3 * tot / n for name, (n, tot) in kt.items() if n}
     per_step_us = {name: 1e3 * tot / args.steps for name, (n, tot) in kt.items() if n}
     dominant = max(("score", "attn"), key=lambda n: per_step_us.get(n, 0.0))
@@ -445,25 +460,18 @@ def main():
     log("kernel avg us:", {k: round(v, 2) for k, v in kern_us.items()})
 
     # prefill encode (1 layer, full K), for context
-    sk.timing_reset()
-    sk.timing_enable(True)
     enc_c = sk.Cache(w.batch, w.n_kv_heads, N, device=dev, v=None)
-    for _ in range(3):
-        sk.sikv_encode(enc_c, K)
-    torch.cuda.synchronize()
-    et = sk.timing_read()
-    sk.timing_enable(False)
+
+    def encode3():
+        for _ in range(3):
+            sk.sikv_encode(enc_c, K)
+
+    et = kernel_times(sk, [enc_c], encode3)
     enc_us = sum(1e3 * tot / 3 for name, (n, tot) in et.items() if name in ("mu_partial", "mu_final", "codes") and n)
     del enc_c
     # the same with data-derived centres (one-pass cluster statistics + finalize)
-    sk.timing_reset()
-    sk.timing_enable(True)
     enc_c = sk.Cache(w.batch, w.n_kv_heads, N, device=dev, v=None, codebook=True)
-    for _ in range(3):
-        sk.sikv_encode(enc_c, K)
-    torch.cuda.synchronize()
-    et = sk.timing_read()
-    sk.timing_enable(False)
+    et = kernel_times(sk, [enc_c], encode3)
     enc_cb_us = sum(1e3 * tot / 3 for name, (n, tot) in et.items()
                     if name in ("mu_partial", "mu_final", "codes", "cb_final") and n)
     del enc_c
@@ -477,12 +485,7 @@ def main():
         sk.sikv_encode(km_c, K)
         sk.sikv_kmeans_codebook(km_c, K, 1)
         torch.cuda.synchronize()
-        sk.timing_reset()
-        sk.timing_enable(True)
-        sk.sikv_kmeans_codebook(km_c, K, 20)
-        torch.cuda.synchronize()
-        kt2 = sk.timing_read()
-        sk.timing_enable(False)
+        kt2 = kernel_times(sk, [km_c], lambda: sk.sikv_kmeans_codebook(km_c, K, 20))
         km20_us = sum(1e3 * tot for name, (n, tot) in kt2.items()
                       if name in ("kmeans_assign", "cb_final") and n)
         km_assign_us = 1e3 * kt2["kmeans_assign"][1] / kt2["kmeans_assign"][0]
@@ -490,13 +493,12 @@ def main():
         dscores = torch.empty((w.batch, w.n_kv_heads, N), dtype=torch.float32, device=dev)
         sk.sikv_dense_scores(q_all, K, scores=dscores)
         torch.cuda.synchronize()
-        sk.timing_reset()
-        sk.timing_enable(True)
+        dtimer = sk.Timer()
         for _ in range(10):
-            sk.sikv_dense_scores(q_all, K, scores=dscores)
+            sk.sikv_dense_scores(q_all, K, scores=dscores, timer=dtimer)
         torch.cuda.synchronize()
-        kt3 = sk.timing_read()
-        sk.timing_enable(False)
+        kt3 = dtimer.read()
+        dtimer.close()
         dense_scores_us = 1e3 * kt3["dense_scores"][1] / kt3["dense_scores"][0]
         del dscores
         log(f"K-means 20 iterations {km20_us:.1f} us (assign {km_assign_us:.1f} us each); "
@@ -533,13 +535,11 @@ def main():
         ev1.record()
         torch.cuda.synchronize()
         qv_us = ev0.elapsed_time(ev1) * 1e3 / args.steps
-        sk.timing_reset()
-        sk.timing_enable(True)
-        for i in range(args.steps):
-            qstep(i % L)
-        torch.cuda.synchronize()
-        qt = sk.timing_read()
-        sk.timing_enable(False)
+        def run_q():
+            for i in range(args.steps):
+                qstep(i % L)
+
+        qt = kernel_times(sk, qcaches, run_q)
         qv_kern_us = {name: 1e3 * tot / n for name, (n, tot) in qt.items() if n}
         log(f"2-bit values: {qv_us:.1f} us/step, kernel avg us:",
             {k: round(v, 2) for k, v in qv_kern_us.items()})
@@ -582,13 +582,11 @@ def main():
         ev1.record()
         torch.cuda.synchronize()
         paged_us = ev0.elapsed_time(ev1) * 1e3 / args.steps
-        sk.timing_reset()
-        sk.timing_enable(True)
-        for i in range(args.steps):
-            pstep(i % L)
-        torch.cuda.synchronize()
-        pt = sk.timing_read()
-        sk.timing_enable(False)
+        def run_p():
+            for i in range(args.steps):
+                pstep(i % L)
+
+        pt = kernel_times(sk, pcaches, run_p)
         paged_kern_us = {name: 1e3 * tot / n for name, (n, tot) in pt.items() if n}
         log(f"paged (256-token pages): {paged_us:.1f} us/step, kernel avg us:",
             {k: round(v, 2) for k, v in paged_kern_us.items()})

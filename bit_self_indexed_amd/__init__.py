@@ -25,6 +25,7 @@ N_SINK = 64
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsikv.so")
 
 OP_ENCODE, OP_SCORE_TOPK, OP_SPARSE_ATTN, OP_DECODE_STEP, OP_KMEANS = 0, 1, 2, 3, 4
+FLAG_EXACT_SELECT = _abi.FLAG_EXACT_SELECT
 
 
 class SikvError(RuntimeError):
@@ -85,6 +86,46 @@ def _strides_rows(t: torch.Tensor, name: str):
     return t.stride(0), t.stride(1), t.stride(2)
 
 
+class Timer:
+    """A caller-owned kernel timer (sikv_timer): calls on a cache whose ``timer``
+    is set, and comparator calls given ``timer=``, bracket each kernel they
+    launch with HIP events on their stream.  ``read()`` synchronises on them."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        _check(lib.sikv_timer_create(ctypes.byref(h)), "sikv_timer_create")
+        self.handle = h
+
+    def reset(self) -> None:
+        _check(lib.sikv_timer_reset(self.handle), "sikv_timer_reset")
+
+    def read(self) -> dict:
+        """{kernel name: (launches, total ms)} since the last reset."""
+        res = {}
+        for i in range(lib.sikv_timer_count()):
+            n = ctypes.c_int64()
+            ms = ctypes.c_double()
+            _check(lib.sikv_timer_read(self.handle, i, ctypes.byref(n), ctypes.byref(ms)),
+                   "sikv_timer_read")
+            res[lib.sikv_timer_name(i).decode()] = (int(n.value), float(ms.value))
+        return res
+
+    def close(self) -> None:
+        if self.handle:
+            _check(lib.sikv_timer_destroy(self.handle), "sikv_timer_destroy")
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _timer(t) -> ctypes.c_void_p | None:
+    return None if t is None else t.handle
+
+
 class Workspace:
     """Caller-owned device scratch, grown on demand (256-byte aligned)."""
 
@@ -139,6 +180,7 @@ class Cache:
         self.seq_lens = None  # ragged batch: int32 [B] on the device (see view())
         self.page_table = None  # paged pool (see paged())
         self.page_size = self.pages_per_seq = self.n_pages = 0
+        self.timer = None  # a Timer: every call on this cache times its kernels
         self.ws = Workspace(dev)
 
     @classmethod
@@ -189,6 +231,8 @@ class Cache:
             d.page_table = self.page_table.data_ptr()
             d.page_size, d.pages_per_seq, d.n_pages = (self.page_size, self.pages_per_seq,
                                                        self.n_pages)
+        d.flags = 0
+        d.timer = _timer(self.timer)
         return d
 
     @property
@@ -213,6 +257,7 @@ class Cache:
         c.seq_lens = None
         c.page_table = self.page_table[b:b + 1] if paged else None
         c.page_size, c.pages_per_seq, c.n_pages = self.page_size, self.pages_per_seq, self.n_pages
+        c.timer = self.timer
         c.ws = self.ws
         return c
 
@@ -254,10 +299,14 @@ def sikv_encode_v(cache: Cache, v: torch.Tensor, t_begin: int = 0) -> None:
 
 
 def sikv_score_topk(cache: Cache, q: torch.Tensor, top_k: int, idx: torch.Tensor | None = None,
-                    scores: torch.Tensor | None = None) -> torch.Tensor:
+                    scores: torch.Tensor | None = None, exact_select: bool = False) -> torch.Tensor:
+    """exact_select: skip the sampled threshold and take the exact whole-head
+    selection path (SIKV_FLAG_EXACT_SELECT for this call only; same result)."""
     qb = _bits(q).contiguous()
     n_q = qb.shape[1]
     d = cache.desc()
+    if exact_select:
+        d.flags |= FLAG_EXACT_SELECT
     if idx is None:
         idx = torch.empty((cache.batch, cache.n_kv_heads, top_k), dtype=torch.int32,
                           device=cache.device)
@@ -287,13 +336,16 @@ def sikv_sparse_attn(cache: Cache, q: torch.Tensor, idx: torch.Tensor,
 
 
 def sikv_decode_step(cache: Cache, q: torch.Tensor, top_k: int, sm_scale: float | None = None,
-                     idx_out: torch.Tensor | None = None, out: torch.Tensor | None = None):
+                     idx_out: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                     exact_select: bool = False):
     qb = _bits(q).contiguous()
     n_q = qb.shape[1]
     sm = 1.0 / math.sqrt(HEAD_DIM) if sm_scale is None else float(sm_scale)
     if out is None:
         out = torch.empty((cache.batch, n_q, HEAD_DIM), dtype=torch.float32, device=cache.device)
     d = cache.desc()
+    if exact_select:
+        d.flags |= FLAG_EXACT_SELECT
     need = int(lib.sikv_workspace_bytes(OP_DECODE_STEP, ctypes.byref(d), n_q, top_k))
     ws, wsn = cache.ws.get(need)
     _check(lib.sikv_decode_step(ctypes.byref(d), qb.data_ptr(), n_q, top_k, ctypes.c_float(sm),
@@ -345,7 +397,7 @@ def sikv_append_decode_step(cache: Cache, k_new: torch.Tensor, q: torch.Tensor, 
 
 def sikv_dense_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                     sm_scale: float | None = None, out: torch.Tensor | None = None,
-                    ws: Workspace | None = None) -> torch.Tensor:
+                    ws: Workspace | None = None, timer: Timer | None = None) -> torch.Tensor:
     """Dense bf16 decode attention over every token (the comparator)."""
     qb, kb, vb = _bits(q).contiguous(), _bits(k), _bits(v)
     B, n_q = qb.shape[0], qb.shape[1]
@@ -359,7 +411,7 @@ def sikv_dense_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     w, wn = ws.get(int(lib.sikv_dense_workspace_bytes(B, Hkv, n_q, N)))
     _check(lib.sikv_dense_attn(B, Hkv, n_q, N, qb.data_ptr(), kb.data_ptr(), ksb, ksh, kst,
                                vb.data_ptr(), vsb, vsh, vst, ctypes.c_float(sm), out.data_ptr(),
-                               w, wn, _stream(q.device)), "sikv_dense_attn")
+                               w, wn, _stream(q.device), _timer(timer)), "sikv_dense_attn")
     return out
 
 
@@ -379,7 +431,7 @@ def sikv_kmeans_codebook(cache: Cache, k: torch.Tensor, n_iter: int = 20) -> Non
 
 
 def sikv_dense_scores(q: torch.Tensor, k: torch.Tensor, n_tokens: int | None = None,
-                      scores: torch.Tensor | None = None) -> torch.Tensor:
+                      scores: torch.Tensor | None = None, timer: Timer | None = None) -> torch.Tensor:
     """Full dot-product retrieval scores (the comparator of the LUT-GEMV score):
     fp32 [B, Hkv, n_tokens], selection query (sum of each KV head's query group)
     dotted with every bf16 key."""
@@ -391,35 +443,12 @@ def sikv_dense_scores(q: torch.Tensor, k: torch.Tensor, n_tokens: int | None = N
     if scores is None:
         scores = torch.empty((B, Hkv, N), dtype=torch.float32, device=q.device)
     _check(lib.sikv_dense_scores(B, Hkv, n_q, N, qb.data_ptr(), kb.data_ptr(), ksb, ksh, kst,
-                                 scores.data_ptr(), _stream(q.device)), "sikv_dense_scores")
+                                 scores.data_ptr(), _stream(q.device), _timer(timer)),
+           "sikv_dense_scores")
     return scores
 
 
-def sikv_stream_copy(dst: torch.Tensor, src: torch.Tensor) -> None:
+def sikv_stream_copy(dst: torch.Tensor, src: torch.Tensor, timer: Timer | None = None) -> None:
     n = src.numel() * src.element_size()
-    _check(lib.sikv_stream_copy(dst.data_ptr(), src.data_ptr(), n, _stream(src.device)),
-           "sikv_stream_copy")
-
-
-# ----------------------------------------------------------------- kernel timing
-def timing_enable(on: bool = True) -> None:
-    _check(lib.sikv_timing_enable(1 if on else 0), "sikv_timing_enable")
-
-
-def timing_reset() -> None:
-    _check(lib.sikv_timing_reset(), "sikv_timing_reset")
-
-
-def timing_read() -> dict:
-    """{kernel name: (launches, total ms)} since the last reset."""
-    res = {}
-    for i in range(lib.sikv_timing_count()):
-        n = ctypes.c_int64()
-        ms = ctypes.c_double()
-        _check(lib.sikv_timing_read(i, ctypes.byref(n), ctypes.byref(ms)), "sikv_timing_read")
-        res[lib.sikv_timing_name(i).decode()] = (int(n.value), float(ms.value))
-    return res
-
-
-def debug_force_exact_select(on: bool) -> None:
-    _check(lib.sikv_debug_force_exact_select(1 if on else 0), "sikv_debug_force_exact_select")
+    _check(lib.sikv_stream_copy(dst.data_ptr(), src.data_ptr(), n, _stream(src.device),
+                                _timer(timer)), "sikv_stream_copy")

@@ -4,7 +4,8 @@ from __future__ import annotations
 
 import ctypes as C
 
-ABI_VERSION = 6
+ABI_VERSION = 7
+FLAG_EXACT_SELECT = 1
 
 STATUS = {
     0: "SIKV_OK",
@@ -39,7 +40,8 @@ class CacheDesc(C.Structure):
         ("page_size", C.c_int32),
         ("pages_per_seq", C.c_int32),
         ("n_pages", C.c_int32),
-        ("reserved", C.c_int32),
+        ("flags", C.c_int32),
+        ("timer", C.c_void_p),
     ]
 
 
@@ -63,17 +65,17 @@ SIGNATURES = {
     "sikv_abi_version": (_I32, []),
     "sikv_desc_size": (_SZ, []),
     "sikv_dense_attn": (_I32, [_I32, _I32, _I32, _I32, _P, _P, _I64, _I64, _I64, _P, _I64, _I64,
-                               _I64, C.c_float, _P, _P, _SZ, _P]),
+                               _I64, C.c_float, _P, _P, _SZ, _P, _P]),
     "sikv_dense_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "sikv_kmeans_codebook": (_I32, [_DESC, _P, _I64, _I64, _I64, _I32, _P, _SZ, _P]),
-    "sikv_dense_scores": (_I32, [_I32, _I32, _I32, _I32, _P, _P, _I64, _I64, _I64, _P, _P]),
-    "sikv_stream_copy": (_I32, [_P, _P, _SZ, _P]),
-    "sikv_timing_enable": (_I32, [_I32]),
-    "sikv_timing_reset": (_I32, []),
-    "sikv_timing_count": (_I32, []),
-    "sikv_timing_name": (C.c_char_p, [_I32]),
-    "sikv_timing_read": (_I32, [_I32, C.POINTER(_I64), C.POINTER(C.c_double)]),
-    "sikv_debug_force_exact_select": (_I32, [_I32]),
+    "sikv_dense_scores": (_I32, [_I32, _I32, _I32, _I32, _P, _P, _I64, _I64, _I64, _P, _P, _P]),
+    "sikv_stream_copy": (_I32, [_P, _P, _SZ, _P, _P]),
+    "sikv_timer_create": (_I32, [C.POINTER(_P)]),
+    "sikv_timer_destroy": (_I32, [_P]),
+    "sikv_timer_reset": (_I32, [_P]),
+    "sikv_timer_read": (_I32, [_P, _I32, C.POINTER(_I64), C.POINTER(C.c_double)]),
+    "sikv_timer_count": (_I32, []),
+    "sikv_timer_name": (C.c_char_p, [_I32]),
 }
 
 

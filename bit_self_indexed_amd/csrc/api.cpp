@@ -1,11 +1,12 @@
 // Host side of the C ABI declared in include/sikv.h: argument validation,
 // workspace planning and the launch sequences of each call.  Nothing here
-// allocates device memory or synchronises a stream.
+// allocates device memory, synchronises a stream or keeps state between calls:
+// each call builds its launch context (stream, optional caller-owned timer)
+// from its own arguments.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cmath>
-#include <mutex>
+#include <new>
 #include <vector>
 
 #include "../../include/sikv.h"
@@ -174,7 +175,14 @@ sikv_status check_desc(const sikv_cache_desc* c) {
   if ((c->vrec != nullptr || c->v_sink != nullptr) &&
       (!c->vrec || !c->v_sink || misaligned(c->vrec, 64) || misaligned(c->v_sink, 16)))
     return SIKV_ERR_INVALID_ARG;
+  if ((c->flags & ~SIKV_FLAG_EXACT_SELECT) != 0) return SIKV_ERR_INVALID_ARG;
   return SIKV_OK;
+}
+
+// The launch context of a call on this cache: its stream and the descriptor's
+// timer.
+Launch ctx(const sikv_cache_desc* c, void* stream) {
+  return Launch{static_cast<hipStream_t>(stream), c->timer};
 }
 
 bool bad_strides(int64_t sb, int64_t sh, int64_t st) {
@@ -216,15 +224,13 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
-std::atomic<int> g_force_exact{0};
-
 // prep (tables + threshold) -> score -> select.  The prep kernel also leaves the
 // query heads' attention tables in the workspace for a following attention.
 // k_new (may be null): key of token n_tokens-1, encoded by the prep kernel first.
 sikv_status run_score_topk(const sikv_cache_desc* c, const uint16_t* q, int n_q_heads, int top_k,
                            int32_t* idx, float* scores_opt, void* ws, const ScorePlan& sp,
                            const uint16_t* k_new, int64_t ksb, int64_t ksh,
-                           const uint16_t* v_new, int64_t vnsb, int64_t vnsh, hipStream_t s) {
+                           const uint16_t* v_new, int64_t vnsb, int64_t vnsh, const Launch& s) {
   const int B = c->batch, Hkv = c->n_kv_heads;
   float* tau = at<float>(ws, sp.off_tau);
   int32_t* cnt = at<int32_t>(ws, sp.off_cnt);
@@ -234,7 +240,7 @@ sikv_status run_score_topk(const sikv_cache_desc* c, const uint16_t* q, int n_q_
   int32_t* pt = at<int32_t>(ws, sp.off_pt);
   int32_t* tab = at<int32_t>(ws, sp.off_tab);
   float* inv = at<float>(ws, sp.off_inv);
-  const int mode = g_force_exact.load(std::memory_order_relaxed) ? 2 : 1;
+  const int mode = (c->flags & SIKV_FLAG_EXACT_SELECT) ? 2 : 1;
   SIKV_TRY(launch_prep(q, n_q_heads, B, Hkv, c->mu, c->codes, c->alpha, rows_of(c), c->n_tokens,
                        c->k_sink, k_new, ksb, ksh, v_new, vnsb, vnsh, c->vrec, c->codebook,
                        top_k, mode, tab, inv,
@@ -253,7 +259,7 @@ sikv_status run_score_topk(const sikv_cache_desc* c, const uint16_t* q, int n_q_
 // launch when the caller has none (standalone call).
 sikv_status run_attn(const sikv_cache_desc* c, const uint16_t* q, int n_q_heads,
                      const int32_t* idx, int top_k, float sm_scale, float* out, void* ws,
-                     const AttnPlan& ap, const AttnTables* tab, hipStream_t s) {
+                     const AttnPlan& ap, const AttnTables* tab, const Launch& s) {
   float* po = at<float>(ws, ap.off_o);
   float* pml = at<float>(ws, ap.off_ml);
   AttnTables own{at<float>(ws, ap.off_lut), at<float>(ws, ap.off_qmu), at<float>(ws, ap.off_slog)};
@@ -272,64 +278,65 @@ sikv_status run_attn(const sikv_cache_desc* c, const uint16_t* q, int n_q_heads,
   return SIKV_OK;
 }
 
-// ------------------------------------------------------------------ timing
-std::mutex g_tmu;
-std::atomic<int> g_timing{0};
-struct Pending {
-  int kid;
-  hipEvent_t e0, e1;
-};
-std::vector<Pending> g_pending;
-std::vector<hipEvent_t> g_pool;
-double g_ms[KID_COUNT];
-int64_t g_cnt[KID_COUNT];
 const char* const g_names[KID_COUNT] = {"mu_partial", "mu_final", "codes", "prep",
                                         "score",      "select",   "attn",  "combine",
                                         "dense",      "copy",     "cb_final", "vcodes",
                                         "kmeans_assign", "dense_scores"};
 
-hipEvent_t take_event() {
-  if (!g_pool.empty()) {
-    hipEvent_t e = g_pool.back();
-    g_pool.pop_back();
-    return e;
-  }
-  hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
-  return e;
-}
-
-sikv_status drain_pending() {
-  sikv_status st = SIKV_OK;
-  for (auto& p : g_pending) {
-    float ms = 0.0f;
-    if (hipEventSynchronize(p.e1) != hipSuccess || hipEventElapsedTime(&ms, p.e0, p.e1) != hipSuccess)
-      st = SIKV_ERR_HIP;
-    else {
-      g_ms[p.kid] += ms;
-      g_cnt[p.kid] += 1;
-    }
-    g_pool.push_back(p.e0);
-    g_pool.push_back(p.e1);
-  }
-  g_pending.clear();
-  return st;
-}
-
 }  // namespace
 
+// ------------------------------------------------------------------ timer
+// The caller-owned kernel timer: event pairs of the launches not yet read, a
+// pool of reusable events, and the per-kernel totals.
+struct sikv_timer {
+  struct Pending {
+    int kid;
+    hipEvent_t e0, e1;
+  };
+  std::vector<Pending> pending;
+  std::vector<hipEvent_t> pool;
+  double ms[KID_COUNT] = {};
+  int64_t cnt[KID_COUNT] = {};
+
+  hipEvent_t take() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  sikv_status drain() {
+    sikv_status st = SIKV_OK;
+    for (auto& p : pending) {
+      float ms_ = 0.0f;
+      if (hipEventSynchronize(p.e1) != hipSuccess ||
+          hipEventElapsedTime(&ms_, p.e0, p.e1) != hipSuccess)
+        st = SIKV_ERR_HIP;
+      else {
+        ms[p.kid] += ms_;
+        cnt[p.kid] += 1;
+      }
+      pool.push_back(p.e0);
+      pool.push_back(p.e1);
+    }
+    pending.clear();
+    return st;
+  }
+};
+
 namespace sikv {
-void timing_events(int kernel_id, hipEvent_t* start, hipEvent_t* stop) {
+void timing_events(::sikv_timer* t, int kernel_id, hipEvent_t* start, hipEvent_t* stop) {
   *start = *stop = nullptr;
-  if (!g_timing.load(std::memory_order_relaxed)) return;
-  std::lock_guard<std::mutex> lk(g_tmu);
-  hipEvent_t a = take_event(), b = take_event();
-  if (!a || !b) {
-    if (a) g_pool.push_back(a);
-    if (b) g_pool.push_back(b);
+  hipEvent_t a = t->take(), b = t->take();
+  if (!a || !b) {  // no events: the launch goes untimed
+    if (a) t->pool.push_back(a);
+    if (b) t->pool.push_back(b);
     return;
   }
-  g_pending.push_back({kernel_id, a, b});
+  t->pending.push_back({kernel_id, a, b});
   *start = a;
   *stop = b;
 }
@@ -347,7 +354,7 @@ sikv_status sikv_encode(const sikv_cache_desc* c, const uint16_t* k, int64_t k_s
     return SIKV_ERR_INVALID_ARG;
   if (recompute_mu != 0 && recompute_mu != 1) return SIKV_ERR_INVALID_ARG;
   if (t_begin < 0 || t_end <= t_begin || t_end > c->capacity) return SIKV_ERR_INVALID_ARG;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Launch s = ctx(c, stream);
   if (recompute_mu) {
     if (t_begin != 0 || t_end != c->n_tokens) return SIKV_ERR_INVALID_ARG;
     const EncodePlan p = plan_encode(c);
@@ -384,8 +391,7 @@ sikv_status sikv_score_topk(const sikv_cache_desc* c, const uint16_t* q, int32_t
   st = check_ws(ws, ws_bytes, sp.bytes);
   if (st != SIKV_OK) return st;
   return run_score_topk(c, q, n_q_heads, top_k, idx, scores_opt, ws, sp, nullptr, 0, 0, nullptr,
-                        0, 0,
-                        static_cast<hipStream_t>(stream));
+                        0, 0, ctx(c, stream));
 }
 
 sikv_status sikv_sparse_attn(const sikv_cache_desc* c, const uint16_t* q, int32_t n_q_heads,
@@ -404,8 +410,7 @@ sikv_status sikv_sparse_attn(const sikv_cache_desc* c, const uint16_t* q, int32_
   plan_attn(c, n_q_heads, top_k, &ap);
   st = check_ws(ws, ws_bytes, ap.bytes);
   if (st != SIKV_OK) return st;
-  return run_attn(c, q, n_q_heads, idx, top_k, sm_scale, out, ws, ap, nullptr,
-                  static_cast<hipStream_t>(stream));
+  return run_attn(c, q, n_q_heads, idx, top_k, sm_scale, out, ws, ap, nullptr, ctx(c, stream));
 }
 
 namespace {
@@ -426,7 +431,7 @@ sikv_status decode_step(const sikv_cache_desc* c, const uint16_t* k_new, int64_t
   if (!plan_decode(c, n_q_heads, top_k, &dp)) return SIKV_ERR_UNSUPPORTED;
   st = check_ws(ws, ws_bytes, dp.bytes);
   if (st != SIKV_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Launch s = ctx(c, stream);
   int32_t* idx = idx_out_opt ? idx_out_opt : at<int32_t>(ws, dp.off_idx);
   char* wsc = at<char>(ws, dp.off_score);
   st = run_score_topk(c, q, n_q_heads, top_k, idx, nullptr, wsc, dp.sp, k_new, ksb, ksh, v_new,
@@ -471,8 +476,7 @@ sikv_status sikv_encode_v(const sikv_cache_desc* c, const uint16_t* v, int64_t v
     return SIKV_ERR_INVALID_ARG;
   if (t_begin < 0 || t_end <= t_begin || t_end > c->capacity) return SIKV_ERR_INVALID_ARG;
   SIKV_TRY(launch_vcodes(v, v_stride_b, v_stride_h, v_stride_t, c->batch, c->n_kv_heads, t_begin,
-                         t_end, rows_of(c), c->vrec, c->v_sink,
-                         static_cast<hipStream_t>(stream)));
+                         t_end, rows_of(c), c->vrec, c->v_sink, ctx(c, stream)));
   return SIKV_OK;
 }
 
@@ -517,7 +521,8 @@ const char* sikv_status_str(sikv_status s) {
     case SIKV_ERR_INVALID_ARG:
       return "invalid argument (null or misaligned pointer, bad size or range)";
     case SIKV_ERR_UNSUPPORTED:
-      return "unsupported (head_dim must be 128, 64 sinks, 1..8 query heads per KV head, no codebook)";
+      return "unsupported (head_dim must be 128, 64 sinks, 1..8 query heads per KV head, "
+             "a score tile plan for the context length)";
     case SIKV_ERR_WORKSPACE:
       return "workspace missing, not 256-byte aligned, or smaller than sikv_workspace_bytes";
     case SIKV_ERR_HIP:
@@ -554,7 +559,7 @@ sikv_status sikv_kmeans_codebook(const sikv_cache_desc* c, const uint16_t* k, in
   st = check_ws(ws, ws_bytes, sikv_workspace_bytes(SIKV_OP_KMEANS, c, 1, 1));
   if (st != SIKV_OK) return st;
   long long* part = static_cast<long long*>(ws);
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Launch s = ctx(c, stream);
   const int BH = c->batch * c->n_kv_heads, nblk = cb_blocks(c->n_tokens);
   for (int it = 0; it < n_iter; ++it) {
     SIKV_TRY(launch_kmeans_assign(k, k_stride_b, k_stride_h, k_stride_t, c->batch, c->n_kv_heads,
@@ -568,7 +573,7 @@ sikv_status sikv_kmeans_codebook(const sikv_cache_desc* c, const uint16_t* k, in
 sikv_status sikv_dense_scores(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads,
                               int32_t n_tokens, const uint16_t* q, const uint16_t* k,
                               int64_t k_stride_b, int64_t k_stride_h, int64_t k_stride_t,
-                              float* scores, void* stream) {
+                              float* scores, void* stream, sikv_timer* timer) {
   if (batch < 1 || n_kv_heads < 1 || n_q_heads < 1 || n_tokens < 1 || n_q_heads % n_kv_heads ||
       (int64_t)batch * n_kv_heads > 65535)
     return SIKV_ERR_INVALID_ARG;
@@ -577,7 +582,8 @@ sikv_status sikv_dense_scores(int32_t batch, int32_t n_kv_heads, int32_t n_q_hea
       bad_strides(k_stride_b, k_stride_h, k_stride_t))
     return SIKV_ERR_INVALID_ARG;
   SIKV_TRY(launch_dense_scores(q, n_q_heads, batch, n_kv_heads, n_tokens, k, k_stride_b,
-                               k_stride_h, k_stride_t, scores, static_cast<hipStream_t>(stream)));
+                               k_stride_h, k_stride_t, scores,
+                               Launch{static_cast<hipStream_t>(stream), timer}));
   return SIKV_OK;
 }
 
@@ -585,7 +591,8 @@ sikv_status sikv_dense_attn(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads
                             const uint16_t* q, const uint16_t* k, int64_t k_stride_b,
                             int64_t k_stride_h, int64_t k_stride_t, const uint16_t* v,
                             int64_t v_stride_b, int64_t v_stride_h, int64_t v_stride_t,
-                            float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream) {
+                            float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream,
+                            sikv_timer* timer) {
   if (batch < 1 || n_kv_heads < 1 || n_q_heads < 1 || n_tokens < 1 || n_q_heads % n_kv_heads ||
       (int64_t)batch * n_kv_heads > 65535)
     return SIKV_ERR_INVALID_ARG;
@@ -605,7 +612,7 @@ sikv_status sikv_dense_attn(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads
   const size_t rows = (size_t)batch * n_q_heads * n_splits;
   float* po = static_cast<float*>(ws);
   float* pml = at<float>(ws, align_up(rows * kD * sizeof(float)));
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Launch s{static_cast<hipStream_t>(stream), timer};
   SIKV_TRY(launch_dense(q, n_q_heads, batch, n_kv_heads, n_tokens, k, k_stride_b, k_stride_h,
                         k_stride_t, v, v_stride_b, v_stride_h, v_stride_t, sm_scale, (int)split,
                         n_splits, po, pml, s));
@@ -613,46 +620,52 @@ sikv_status sikv_dense_attn(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads
   return SIKV_OK;
 }
 
-sikv_status sikv_stream_copy(void* dst, const void* src, size_t bytes, void* stream) {
+sikv_status sikv_stream_copy(void* dst, const void* src, size_t bytes, void* stream,
+                             sikv_timer* timer) {
   if (!dst || !src || bytes == 0 || bytes % 16 || misaligned(dst, 16) || misaligned(src, 16))
     return SIKV_ERR_INVALID_ARG;
-  SIKV_TRY(launch_copy(dst, src, bytes, static_cast<hipStream_t>(stream)));
+  SIKV_TRY(launch_copy(dst, src, bytes, Launch{static_cast<hipStream_t>(stream), timer}));
   return SIKV_OK;
 }
 
-sikv_status sikv_timing_enable(int32_t on) {
-  g_timing.store(on ? 1 : 0);
-  return SIKV_OK;
+sikv_status sikv_timer_create(sikv_timer** out) {
+  if (out == nullptr) return SIKV_ERR_INVALID_ARG;
+  *out = new (std::nothrow) sikv_timer();
+  return *out != nullptr ? SIKV_OK : SIKV_ERR_HIP;
 }
 
-sikv_status sikv_timing_reset(void) {
-  std::lock_guard<std::mutex> lk(g_tmu);
-  sikv_status st = drain_pending();
+sikv_status sikv_timer_destroy(sikv_timer* t) {
+  if (t == nullptr) return SIKV_OK;
+  sikv_status st = t->drain();
+  for (hipEvent_t e : t->pool)
+    if (hipEventDestroy(e) != hipSuccess) st = SIKV_ERR_HIP;
+  delete t;
+  return st;
+}
+
+sikv_status sikv_timer_reset(sikv_timer* t) {
+  if (t == nullptr) return SIKV_ERR_INVALID_ARG;
+  const sikv_status st = t->drain();
   for (int i = 0; i < KID_COUNT; ++i) {
-    g_ms[i] = 0.0;
-    g_cnt[i] = 0;
+    t->ms[i] = 0.0;
+    t->cnt[i] = 0;
   }
   return st;
 }
 
-int32_t sikv_timing_count(void) { return KID_COUNT; }
+int32_t sikv_timer_count(void) { return KID_COUNT; }
 
-const char* sikv_timing_name(int32_t id) {
+const char* sikv_timer_name(int32_t id) {
   return (id >= 0 && id < KID_COUNT) ? g_names[id] : "unknown";
 }
 
-sikv_status sikv_timing_read(int32_t id, int64_t* launches, double* total_ms) {
-  if (id < 0 || id >= KID_COUNT || !launches || !total_ms) return SIKV_ERR_INVALID_ARG;
-  std::lock_guard<std::mutex> lk(g_tmu);
-  sikv_status st = drain_pending();
-  *launches = g_cnt[id];
-  *total_ms = g_ms[id];
+sikv_status sikv_timer_read(sikv_timer* t, int32_t id, int64_t* launches, double* total_ms) {
+  if (t == nullptr || id < 0 || id >= KID_COUNT || !launches || !total_ms)
+    return SIKV_ERR_INVALID_ARG;
+  const sikv_status st = t->drain();
+  *launches = t->cnt[id];
+  *total_ms = t->ms[id];
   return st;
-}
-
-sikv_status sikv_debug_force_exact_select(int32_t on) {
-  g_force_exact.store(on ? 1 : 0);
-  return SIKV_OK;
 }
 
 }  // extern "C"

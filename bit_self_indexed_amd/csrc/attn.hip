@@ -442,7 +442,7 @@ hipError_t launch_attn(int n_q_heads, int B, int Hkv, const uint8_t* codes, cons
                        const float* att_lut,
                        const float* att_qmu, const float* att_slog, float sm_scale,
                        int chunks_per_block, int n_splits, float* part_o, float* part_ml,
-                       hipStream_t s) {
+                       const Launch& s) {
   const int n_chunks = (kSink + top_k + kAttnChunk - 1) / kAttnChunk;
   if (chunks_per_block < 1 || chunks_per_block > kAttnMaxCpb ||
       (int64_t)n_splits * chunks_per_block < n_chunks ||
@@ -479,7 +479,7 @@ hipError_t launch_attn(int n_q_heads, int B, int Hkv, const uint8_t* codes, cons
 }
 
 hipError_t launch_combine(const float* part_o, const float* part_ml, int BHq, int n_splits,
-                          float* out, hipStream_t s) {
+                          float* out, const Launch& s) {
   return launch_k(KID_COMBINE, combine_kernel, dim3(BHq), dim3(256), 0, s, part_o, part_ml,
                   n_splits, out);
 }

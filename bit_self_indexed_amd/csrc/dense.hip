@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void dense_scores_kernel(
 
 hipError_t launch_dense_scores(const uint16_t* q, int n_q_heads, int B, int Hkv, int n_tokens,
                                const uint16_t* k, int64_t ksb, int64_t ksh, int64_t kst,
-                               float* scores, hipStream_t s) {
+                               float* scores, const Launch& s) {
   const int G = n_q_heads / Hkv;
   if (G < 1 || G * Hkv != n_q_heads || n_tokens < 1) return hipErrorInvalidValue;
   const dim3 grid((n_tokens + 16 * kScoreRows - 1) / (16 * kScoreRows), B * Hkv), block(256);
@@ -239,7 +239,7 @@ hipError_t launch_dense_scores(const uint16_t* q, int n_q_heads, int B, int Hkv,
 hipError_t launch_dense(const uint16_t* q, int n_q_heads, int B, int Hkv, int n_tokens,
                         const uint16_t* k, int64_t ksb, int64_t ksh, int64_t kst,
                         const uint16_t* v, int64_t vsb, int64_t vsh, int64_t vst, float sm_scale,
-                        int split, int n_splits, float* part_o, float* part_ml, hipStream_t s) {
+                        int split, int n_splits, float* part_o, float* part_ml, const Launch& s) {
   const float sm_log2 = sm_scale * 1.4426950408889634f;
   const dim3 grid(n_splits, B * Hkv), block(256);
 #define SIKV_DENSE_CASE(GG)                                                                     \

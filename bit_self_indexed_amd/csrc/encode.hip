@@ -345,20 +345,20 @@ __global__ __launch_bounds__(256, 2) void kmeans_assign_kernel(
 }  // namespace
 
 hipError_t launch_mu_partial(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
-                             int n_tokens, float* partial, int nblk, hipStream_t s) {
+                             int n_tokens, float* partial, int nblk, const Launch& s) {
   return launch_k(KID_MU_PARTIAL, mu_partial_kernel, dim3(nblk, B * Hkv), dim3(256), 0, s, k, sb,
                   sh, st, Hkv, n_tokens, partial, nblk);
 }
 
 hipError_t launch_mu_final(const float* partial, int BH, int nblk, int n_tokens, float* mu,
-                           hipStream_t s) {
+                           const Launch& s) {
   return launch_k(KID_MU_FINAL, mu_final_kernel, dim3(BH), dim3(kD), 0, s, partial, nblk,
                   n_tokens, mu);
 }
 
 hipError_t launch_codes(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
                         int t_begin, int t_end, const RowMap& rm, const float* mu, uint8_t* codes,
-                        float* alpha, uint16_t* k_sink, uint8_t* vrec, hipStream_t s) {
+                        float* alpha, uint16_t* k_sink, uint8_t* vrec, const Launch& s) {
   const int tiles = (t_end - t_begin + 127) / 128;
   return launch_k(KID_CODES, codes_kernel<false>, dim3(tiles, B * Hkv), dim3(256), 0, s, k, sb,
                   sh, st, Hkv, t_begin, t_end, rm, 1, mu, codes, alpha, k_sink, vrec,
@@ -367,7 +367,7 @@ hipError_t launch_codes(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, i
 
 hipError_t launch_vcodes(const uint16_t* v, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
                          int t_begin, int t_end, const RowMap& rm, uint8_t* vrec,
-                         uint16_t* v_sink, hipStream_t s) {
+                         uint16_t* v_sink, const Launch& s) {
   const int tiles = (t_end - t_begin + 127) / 128;
   return launch_k(KID_VCODES, vcodes_kernel, dim3(tiles, B * Hkv), dim3(256), 0, s, v, sb, sh, st,
                   Hkv, t_begin, t_end, rm, vrec, v_sink);
@@ -376,14 +376,14 @@ hipError_t launch_vcodes(const uint16_t* v, int64_t sb, int64_t sh, int64_t st, 
 hipError_t launch_codes_cb(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
                            int n_tokens, const RowMap& rm, const float* mu, uint8_t* codes,
                            float* alpha, uint16_t* k_sink, uint8_t* vrec, long long* cb_part,
-                           hipStream_t s) {
+                           const Launch& s) {
   return launch_k(KID_CODES, codes_kernel<true>, dim3(cb_blocks(n_tokens), B * Hkv), dim3(256), 0,
                   s, k, sb, sh, st, Hkv, 0, n_tokens, rm, kCbTiles, mu, codes, alpha, k_sink,
                   vrec, cb_part);
 }
 
 hipError_t launch_cb_final(const long long* cb_part, int BH, int nblk, float* codebook,
-                           hipStream_t s, int keep) {
+                           const Launch& s, int keep) {
   return launch_k(KID_CB_FINAL, cb_final_kernel, dim3(BH), dim3(kSub * 16), 0, s, cb_part, nblk,
                   codebook, keep);
 }
@@ -391,7 +391,7 @@ hipError_t launch_cb_final(const long long* cb_part, int BH, int nblk, float* co
 hipError_t launch_kmeans_assign(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B,
                                 int Hkv, int n_tokens, const RowMap& rm, const float* mu,
                                 const float* alpha, const float* centres, long long* cb_part,
-                                hipStream_t s) {
+                                const Launch& s) {
   return launch_k(KID_KM_ASSIGN, kmeans_assign_kernel, dim3(cb_blocks(n_tokens), B * Hkv),
                   dim3(256), 0, s, k, sb, sh, st, Hkv, n_tokens, rm, kCbTiles, mu, alpha,
                   centres, cb_part);

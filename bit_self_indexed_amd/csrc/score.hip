@@ -1071,7 +1071,7 @@ hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const f
                        const uint16_t* v_new, int64_t vnsb, int64_t vnsh, uint8_t* vrec,
                        const float* codebook, int top_k, int mode, int* sel_lut,
                        float* sel_inv, float* att_lut, float* att_qmu, float* att_slog,
-                       float* tau, float* bin_scale, const int32_t* seq_lens, hipStream_t s) {
+                       float* tau, float* bin_scale, const int32_t* seq_lens, const Launch& s) {
   return launch_k(KID_PREP, prep_kernel, dim3(B * Hkv), dim3(1024), 0, s, q, n_q_heads, Hkv,
                   n_q_heads / Hkv, mu, codes, alpha, rm, n_tokens, k_sink, k_new, ksb, ksh,
                   v_new, vnsb, vnsh, vrec, codebook, top_k, mode, seq_lens, sel_lut, sel_inv,
@@ -1082,7 +1082,7 @@ hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha
                         int n_tokens, const int32_t* seq_lens, const int* sel_lut,
                         const float* sel_inv, const float* tau, int chunk,
                         int n_chunks, uint32_t* cand_key, int32_t* cand_t, int32_t* chunk_count,
-                        float* scores_opt, hipStream_t s) {
+                        float* scores_opt, const Launch& s) {
   const dim3 grid(n_chunks, B * Hkv), block(256);
 #define SIKV_SCORE_CASE(UU)                                                                    \
   case 256 * UU:                                                                               \
@@ -1110,7 +1110,7 @@ hipError_t launch_select(int B, int Hkv, const uint8_t* codes, const float* alph
                          const float* sel_inv, int top_k, int chunk, int n_chunks,
                          uint32_t* cand_key, int32_t* cand_t, const int32_t* chunk_count,
                          const float* tau, const float* bin_scale, uint32_t* comp_key,
-                         int32_t* comp_t, int32_t* idx, hipStream_t s) {
+                         int32_t* comp_t, int32_t* idx, const Launch& s) {
   if (n_chunks > kMaxChunks) return hipErrorInvalidValue;
   return launch_k(KID_SELECT, select_kernel, dim3(B * Hkv), dim3(1024), 0, s, codes, alpha,
                   rm, n_tokens, Hkv, seq_lens, sel_lut, sel_inv, top_k, chunk, n_chunks,

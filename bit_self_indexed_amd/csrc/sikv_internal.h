@@ -12,7 +12,17 @@
 #include <stddef.h>
 #include <stdint.h>
 
+struct sikv_timer;  // the C ABI's opaque, caller-owned kernel timer
+
 namespace sikv {
+
+// Where the kernels of one library call go: the caller's stream, and the
+// caller's timer (null: the call is not timed).  Nothing else is shared
+// between calls.
+struct Launch {
+  hipStream_t stream;
+  ::sikv_timer* timer;
+};
 
 constexpr int kD = 128;          // head dim
 constexpr int kSink = 64;        // full-precision sink tokens (§2.1 item 3)
@@ -28,7 +38,7 @@ constexpr int kSub = 32;         // 4-dim sub-vectors per key (§2.1 item 1)
 constexpr int kLut = kSub * 16;  // table entries per query
 constexpr int kMaxGroup = 8;
 
-// Kernel ids for the optional timing facility.
+// Kernel ids of the optional caller-owned timer.
 enum KernelId {
   KID_MU_PARTIAL = 0,
   KID_MU_FINAL,
@@ -308,18 +318,18 @@ __device__ __forceinline__ int ballot_rank(uint64_t m) {
 // encode.hip
 constexpr int kMuTile = 4096;  // tokens per mean partial (an aligned subtree of the token tree)
 hipError_t launch_mu_partial(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
-                             int n_tokens, float* partial, int nblk, hipStream_t s);
+                             int n_tokens, float* partial, int nblk, const Launch& s);
 hipError_t launch_mu_final(const float* partial, int BH, int nblk, int n_tokens, float* mu,
-                           hipStream_t s);
+                           const Launch& s);
 // vrec (may be null): value records, whose key code copy is written too.
 hipError_t launch_codes(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
                         int t_begin, int t_end, const RowMap& rm, const float* mu, uint8_t* codes,
-                        float* alpha, uint16_t* k_sink, uint8_t* vrec, hipStream_t s);
+                        float* alpha, uint16_t* k_sink, uint8_t* vrec, const Launch& s);
 // 2-bit value codes of rows t_begin..t_end-1 (quantize_vrow16) into bytes 0..47 of
 // their records vrec [B*Hkv][cap][64]; rows below 64 are also copied to v_sink.
 hipError_t launch_vcodes(const uint16_t* v, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
                          int t_begin, int t_end, const RowMap& rm, uint8_t* vrec,
-                         uint16_t* v_sink, hipStream_t s);
+                         uint16_t* v_sink, const Launch& s);
 // Prefill codes with the codebook statistics: like launch_codes over [0, n_tokens),
 // plus, per block of kCbTiles x 128 tokens, the fixed-point sums of k~/alpha and
 // the counts of every (sub-vector, pattern) over the tokens [64, n_tokens),
@@ -331,12 +341,12 @@ inline int cb_blocks(int n_tokens) { return (n_tokens + 128 * kCbTiles - 1) / (1
 hipError_t launch_codes_cb(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
                            int n_tokens, const RowMap& rm, const float* mu, uint8_t* codes,
                            float* alpha, uint16_t* k_sink, uint8_t* vrec, long long* cb_part,
-                           hipStream_t s);
+                           const Launch& s);
 // Codebook from the block statistics: centre = fl32((sum * 2^-24) / count) in
 // fp64; an empty cluster gets the sign vertex (keep = 0) or keeps the centre
 // already in codebook (keep = 1).  codebook [B*Hkv][32][16][4].
 hipError_t launch_cb_final(const long long* cb_part, int BH, int nblk, float* codebook,
-                           hipStream_t s, int keep = 0);
+                           const Launch& s, int keep = 0);
 // One Lloyd step of the K-means baseline, stage 1: every prefill point x
 // (tokens [64, n_tokens), x = fl32(fl32(k - mu) / alpha)) goes to its nearest
 // centre of `centres` [B*Hkv][32][16][4] (null: the sign vertices), squared
@@ -345,7 +355,7 @@ hipError_t launch_cb_final(const long long* cb_part, int BH, int nblk, float* co
 hipError_t launch_kmeans_assign(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B,
                                 int Hkv, int n_tokens, const RowMap& rm, const float* mu,
                                 const float* alpha, const float* centres, long long* cb_part,
-                                hipStream_t s);
+                                const Launch& s);
 
 // score.hip.  seq_lens (may be null): per-sequence lengths of a ragged batch
 // (seq_len / seq_topk above); n_tokens is then the longest, which sizes grids.
@@ -367,18 +377,18 @@ hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const f
                        const uint16_t* v_new, int64_t vnsb, int64_t vnsh, uint8_t* vrec,
                        const float* codebook, int top_k, int mode, int* sel_lut,
                        float* sel_inv, float* att_lut, float* att_qmu, float* att_slog,
-                       float* tau, float* bin_scale, const int32_t* seq_lens, hipStream_t s);
+                       float* tau, float* bin_scale, const int32_t* seq_lens, const Launch& s);
 hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha, const RowMap& rm,
                         int n_tokens, const int32_t* seq_lens, const int* sel_lut,
                         const float* sel_inv, const float* tau, int chunk,
                         int n_chunks, uint32_t* cand_key, int32_t* cand_t, int32_t* chunk_count,
-                        float* scores_opt, hipStream_t s);
+                        float* scores_opt, const Launch& s);
 hipError_t launch_select(int B, int Hkv, const uint8_t* codes, const float* alpha, const RowMap& rm,
                          int n_tokens, const int32_t* seq_lens, const int* sel_lut,
                          const float* sel_inv, int top_k, int chunk, int n_chunks,
                          uint32_t* cand_key, int32_t* cand_t, const int32_t* chunk_count,
                          const float* tau, const float* bin_scale, uint32_t* comp_key,
-                         int32_t* comp_t, int32_t* idx, hipStream_t s);
+                         int32_t* comp_t, int32_t* idx, const Launch& s);
 
 // attn.hip
 // Attended entries are processed in chunks of kAttnChunk; a block takes
@@ -395,38 +405,40 @@ hipError_t launch_attn(int n_q_heads, int B, int Hkv, const uint8_t* codes, cons
                        const float* att_lut,
                        const float* att_qmu, const float* att_slog, float sm_scale,
                        int chunks_per_block, int n_splits, float* part_o, float* part_ml,
-                       hipStream_t s);
+                       const Launch& s);
 hipError_t launch_combine(const float* part_o, const float* part_ml, int BHq, int n_splits,
-                          float* out, hipStream_t s);
+                          float* out, const Launch& s);
 
 // dense.hip
 // Full dot-product retrieval scores: scores[bh * n_tokens + t] = qbar . k_t for
 // t < n_tokens, qbar = sum of the G query rows of the KV head (fp32, g order).
 hipError_t launch_dense_scores(const uint16_t* q, int n_q_heads, int B, int Hkv, int n_tokens,
                                const uint16_t* k, int64_t ksb, int64_t ksh, int64_t kst,
-                               float* scores, hipStream_t s);
+                               float* scores, const Launch& s);
 hipError_t launch_dense(const uint16_t* q, int n_q_heads, int B, int Hkv, int n_tokens,
                         const uint16_t* k, int64_t ksb, int64_t ksh, int64_t kst,
                         const uint16_t* v, int64_t vsb, int64_t vsh, int64_t vst, float sm_scale,
-                        int split, int n_splits, float* part_o, float* part_ml, hipStream_t s);
+                        int split, int n_splits, float* part_o, float* part_ml, const Launch& s);
 
 // util.hip
-hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, const Launch& s);
 
-// Timing facility (api.cpp): launch through these so a timed run can bracket
-// every kernel with events.  Returns the events to use (or null ones).
-void timing_events(int kernel_id, hipEvent_t* start, hipEvent_t* stop);
+// Caller-owned kernel timer (api.cpp; the C ABI's sikv_timer): launch_k asks it
+// for a pair of events to bracket a launch with.  Returns null events when the
+// timer is null (an untimed call).
+void timing_events(::sikv_timer* timer, int kernel_id, hipEvent_t* start, hipEvent_t* stop);
 
-// Helper used by the launchers: launch with optional start/stop events.
+// Helper used by the launchers: launch on the context's stream, bracketed by the
+// timer's events when the call is timed.
 template <typename... KArgs, typename... Args>
 inline hipError_t launch_k(int kid, void (*kern)(KArgs...), dim3 grid, dim3 block, size_t shmem,
-                           hipStream_t s, Args... args) {
+                           const Launch& s, Args... args) {
   hipEvent_t e0 = nullptr, e1 = nullptr;
-  timing_events(kid, &e0, &e1);
+  if (s.timer != nullptr) timing_events(s.timer, kid, &e0, &e1);
   if (e0) {
-    hipExtLaunchKernelGGL(kern, grid, block, shmem, s, e0, e1, 0, args...);
+    hipExtLaunchKernelGGL(kern, grid, block, shmem, s.stream, e0, e1, 0, args...);
   } else {
-    hipLaunchKernelGGL(kern, grid, block, shmem, s, args...);
+    hipLaunchKernelGGL(kern, grid, block, shmem, s.stream, args...);
   }
   return hipGetLastError();
 }

@@ -17,7 +17,7 @@ __global__ __launch_bounds__(256) void copy_kernel(uint4* __restrict__ dst,
 
 }  // namespace
 
-hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s) {
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, const Launch& s) {
   const int64_t n16 = (int64_t)(bytes / 16);
   int64_t blocks = (n16 + 255) / 256;
   if (blocks > 8192) blocks = 8192;

@@ -29,9 +29,10 @@
  *   - Shapes: head_dim 128 and 64 sinks only (SIKV_ERR_UNSUPPORTED otherwise);
  *     query heads per KV head (G = n_q_heads / n_kv_heads) from 1 to 8, query
  *     head h*G+g belongs to KV head h.
- *   - Thread safety: calls keep no state between them (except the optional
- *     kernel-timing facility at the end of this file) and may run concurrently
- *     on different streams with disjoint buffers.
+ *   - State: the library keeps none.  Everything a call reads is in its
+ *     arguments and the descriptor (including the optional caller-owned timer
+ *     and the flags word), so calls may run concurrently from several threads
+ *     on different streams with disjoint buffers and workspaces.
  */
 #ifndef SIKV_H
 #define SIKV_H
@@ -43,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SIKV_ABI_VERSION 6
+#define SIKV_ABI_VERSION 7
 #define SIKV_HEAD_DIM 128
 #define SIKV_N_SINK 64
 #define SIKV_MAX_GROUP 8
@@ -54,6 +55,14 @@ typedef int32_t sikv_status;
 #define SIKV_ERR_UNSUPPORTED (-2) /* valid but outside v1 (head_dim, sinks, G)     */
 #define SIKV_ERR_WORKSPACE (-3)   /* workspace missing, misaligned or too small    */
 #define SIKV_ERR_HIP (-4)         /* a kernel launch or HIP runtime call failed    */
+
+/* bits of sikv_cache_desc.flags (every other bit must be 0) */
+#define SIKV_FLAG_EXACT_SELECT 1 /* score_topk skips its sampled threshold and
+                                    always takes its exact whole-head selection
+                                    path (same result, slower; for tests) */
+
+/* Caller-owned kernel timer (sikv_timer_create); opaque. */
+typedef struct sikv_timer sikv_timer;
 
 /* op codes of sikv_workspace_bytes */
 #define SIKV_OP_ENCODE 0
@@ -122,6 +131,10 @@ typedef int32_t sikv_status;
  *          two >= 256, capacity = pages_per_seq * page_size, and n_pages * Hkv *
  *          page_size < 2^31.  mu, k_sink, codebook, v_sink stay per sequence.  Page
  *          ids are trusted (the caller keeps them in [0, n_pages)).
+ *   flags  0, or SIKV_FLAG_EXACT_SELECT (above); any other bit is invalid.
+ *   timer  NULL, or a timer from sikv_timer_create: every kernel the call
+ *          launches is bracketed by events recorded with it (measurement
+ *          only; see the timer functions at the end of this file).
  * n_tokens (N) is the number of valid tokens of every sequence (64 < N <=
  * capacity; the longest one with seq_lens); candidates for top-k are the tokens
  * 64..N-1.
@@ -149,7 +162,8 @@ typedef struct sikv_cache_desc {
   int32_t page_size;
   int32_t pages_per_seq;
   int32_t n_pages;
-  int32_t reserved;
+  int32_t flags;
+  sikv_timer *timer;
 } sikv_cache_desc;
 
 /*
@@ -277,14 +291,15 @@ size_t sikv_desc_size(void);
  * head g of KV head h, softmax(sm_scale * q_g . K_t) over t < N, times V.
  * K and V bf16 with the stride scheme of sikv_cache_desc; q bf16
  * [B][n_q_heads][128]; out fp32 [B][n_q_heads][128].  Workspace from
- * sikv_dense_workspace_bytes.
+ * sikv_dense_workspace_bytes.  timer: NULL or a caller-owned timer (as in the
+ * descriptor).
  */
 sikv_status sikv_dense_attn(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads,
                             int32_t n_tokens, const uint16_t *q, const uint16_t *k,
                             int64_t k_stride_b, int64_t k_stride_h, int64_t k_stride_t,
                             const uint16_t *v, int64_t v_stride_b, int64_t v_stride_h,
                             int64_t v_stride_t, float sm_scale, float *out, void *ws,
-                            size_t ws_bytes, void *stream);
+                            size_t ws_bytes, void *stream, sikv_timer *timer);
 size_t sikv_dense_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads,
                                   int32_t n_tokens);
 
@@ -314,34 +329,38 @@ sikv_status sikv_kmeans_codebook(const sikv_cache_desc *cache, const uint16_t *k
  * h) * n_tokens + t] = qbar_h . K[b,h,t] for every t < n_tokens, with qbar_h the
  * fp32 sum (g ascending) of the G query rows h*G..h*G+G-1 (the selection query
  * of the LUT-GEMV score), K bf16 with the stride scheme of sikv_cache_desc,
- * q bf16 [B][n_q_heads][128].  No workspace.
+ * q bf16 [B][n_q_heads][128].  No workspace.  timer: NULL or a caller-owned
+ * timer.
  */
 sikv_status sikv_dense_scores(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads,
                               int32_t n_tokens, const uint16_t *q, const uint16_t *k,
                               int64_t k_stride_b, int64_t k_stride_h, int64_t k_stride_t,
-                              float *scores, void *stream);
+                              float *scores, void *stream, sikv_timer *timer);
 
 /* Plain device copy of `bytes` (multiple of 16, both pointers 16-byte
- * aligned): the reference kernel for bandwidth and traffic-counter scaling. */
-sikv_status sikv_stream_copy(void *dst, const void *src, size_t bytes, void *stream);
+ * aligned): the reference kernel for bandwidth and traffic-counter scaling.
+ * timer: NULL or a caller-owned timer. */
+sikv_status sikv_stream_copy(void *dst, const void *src, size_t bytes, void *stream,
+                             sikv_timer *timer);
 
 /*
- * Kernel timing (process-wide, for benchmarks).  While enabled, every kernel
- * the library launches is bracketed by HIP events recorded with the launch
- * itself; sikv_timing_read synchronises on them and returns, per kernel id
- * (0 <= id < sikv_timing_count()), the number of launches and their summed
- * duration in milliseconds since the last reset.  Not meant for concurrent use
- * from several threads.
+ * Kernel timer (measurement only, not part of the method).  A timer is a host
+ * object owned by the caller: sikv_timer_create makes one, sikv_timer_destroy
+ * frees it and its events.  A call whose descriptor (or timer argument) names
+ * a timer brackets each kernel it launches with two HIP events recorded with
+ * the launch itself, on the call's stream, created on the current device the
+ * first time they are needed and reused afterwards.  sikv_timer_read
+ * synchronises on the pending events and returns, per kernel id
+ * (0 <= id < sikv_timer_count()), the number of launches and their summed
+ * duration in milliseconds since the last reset.  A timer must be used by one
+ * thread at a time and on one device; separate timers are independent.
  */
-sikv_status sikv_timing_enable(int32_t on);
-sikv_status sikv_timing_reset(void);
-int32_t sikv_timing_count(void);
-const char *sikv_timing_name(int32_t id);
-sikv_status sikv_timing_read(int32_t id, int64_t *launches, double *total_ms);
-
-/* Test hook: when on, score_topk ignores its sampled threshold and always
- * takes its exact whole-head selection path (same result, slower). */
-sikv_status sikv_debug_force_exact_select(int32_t on);
+sikv_status sikv_timer_create(sikv_timer **out);
+sikv_status sikv_timer_destroy(sikv_timer *timer);
+sikv_status sikv_timer_reset(sikv_timer *timer);
+sikv_status sikv_timer_read(sikv_timer *timer, int32_t id, int64_t *launches, double *total_ms);
+int32_t sikv_timer_count(void);          /* number of kernel ids (a constant)        */
+const char *sikv_timer_name(int32_t id); /* static name of kernel id; never NULL     */
 
 #ifdef __cplusplus
 }

@@ -38,11 +38,12 @@ def test_header_functions_are_exported_and_declared():
 
 def test_abi_version_and_desc_layout():
     assert lib.sikv_abi_version() == _abi.ABI_VERSION
-    assert lib.sikv_desc_size() == C.sizeof(_abi.CacheDesc) == 144
+    assert lib.sikv_desc_size() == C.sizeof(_abi.CacheDesc) == 152
     offs = {f[0]: getattr(_abi.CacheDesc, f[0]).offset for f in _abi.CacheDesc._fields_}
     assert offs["codes"] == 24 and offs["v"] == 56 and offs["v_stride_t"] == 80
     assert offs["codebook"] == 88 and offs["vrec"] == 96 and offs["v_sink"] == 104
     assert offs["seq_lens"] == 112 and offs["page_table"] == 120 and offs["n_pages"] == 136
+    assert offs["flags"] == 140 and offs["timer"] == 144
 
 
 def test_status_strings():
@@ -58,7 +59,8 @@ def desc(**kw):
     d.codes, d.alpha, d.mu, d.k_sink = FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000
     d.v, d.v_stride_b, d.v_stride_h, d.v_stride_t = FAKE + 0x400000, 2 * 1000 * 128, 1000 * 128, 128
     d.codebook = d.vrec = d.v_sink = d.seq_lens = d.page_table = None
-    d.page_size = d.pages_per_seq = d.n_pages = 0
+    d.page_size = d.pages_per_seq = d.n_pages = d.flags = 0
+    d.timer = None
     for k, v in kw.items():
         setattr(d, k, v)
     return d
@@ -103,6 +105,8 @@ def test_workspace_sizes():
     ("vrec", FAKE + 0x600000, INVALID),                             # v_sink missing
     ("v_sink", FAKE + 0x600000, INVALID),
     ("seq_lens", FAKE + 2, INVALID),                                # misaligned
+    ("flags", 2, INVALID),                                          # unknown flag bit
+    ("flags", -1, INVALID),
 ])
 def test_descriptor_validation(field, value, expect):
     d = desc(**{field: value})
@@ -208,23 +212,59 @@ def test_encode_validation():
 def test_dense_and_copy_validation():
     f = C.c_float
     assert lib.sikv_dense_attn(1, 2, 3, 100, FAKE, FAKE, 0, 0, 128, FAKE, 0, 0, 128, f(0.1), FAKE,
-                               FAKE, 1 << 30, None) == INVALID
+                               FAKE, 1 << 30, None, None) == INVALID
     assert lib.sikv_dense_attn(1, 1, 9, 100, FAKE, FAKE, 0, 0, 128, FAKE, 0, 0, 128, f(0.1), FAKE,
-                               FAKE, 1 << 30, None) == UNSUPPORTED
+                               FAKE, 1 << 30, None, None) == UNSUPPORTED
     assert lib.sikv_dense_attn(1, 1, 4, 100, FAKE, FAKE, 0, 0, 128, FAKE, 0, 0, 128, f(0.1), FAKE,
-                               None, 0, None) == WORKSPACE
-    assert lib.sikv_stream_copy(FAKE, FAKE, 17, None) == INVALID
-    assert lib.sikv_stream_copy(None, FAKE, 16, None) == INVALID
+                               None, 0, None, None) == WORKSPACE
+    assert lib.sikv_stream_copy(FAKE, FAKE, 17, None, None) == INVALID
+    assert lib.sikv_stream_copy(None, FAKE, 16, None, None) == INVALID
 
 
-def test_timing_facility_without_launches():
-    assert lib.sikv_timing_count() >= 10
-    names = [lib.sikv_timing_name(i).decode() for i in range(lib.sikv_timing_count())]
+def test_timer_without_launches():
+    """A caller-owned timer: created, read (nothing launched), reset, destroyed;
+    two timers are independent objects."""
+    assert lib.sikv_timer_count() >= 10
+    names = [lib.sikv_timer_name(i).decode() for i in range(lib.sikv_timer_count())]
     assert "score" in names and "attn" in names
-    assert lib.sikv_timing_reset() == OK
+    assert lib.sikv_timer_name(99).decode() == "unknown"
+    t1, t2 = C.c_void_p(), C.c_void_p()
+    assert lib.sikv_timer_create(C.byref(t1)) == OK and t1.value
+    assert lib.sikv_timer_create(C.byref(t2)) == OK and t2.value and t2.value != t1.value
     n, ms = C.c_int64(), C.c_double()
-    assert lib.sikv_timing_read(0, C.byref(n), C.byref(ms)) == OK and n.value == 0
-    assert lib.sikv_timing_read(99, C.byref(n), C.byref(ms)) == INVALID
+    assert lib.sikv_timer_read(t1, 0, C.byref(n), C.byref(ms)) == OK and n.value == 0
+    assert lib.sikv_timer_read(t1, 99, C.byref(n), C.byref(ms)) == INVALID
+    assert lib.sikv_timer_read(None, 0, C.byref(n), C.byref(ms)) == INVALID
+    assert lib.sikv_timer_reset(t1) == OK and lib.sikv_timer_reset(None) == INVALID
+    assert lib.sikv_timer_create(None) == INVALID
+    assert lib.sikv_timer_destroy(t1) == OK and lib.sikv_timer_destroy(t2) == OK
+    assert lib.sikv_timer_destroy(None) == OK
+
+
+# Writable symbols that the toolchain and the HIP runtime put into every
+# shared library: ELF/C++ runtime bookkeeping, HIP's code-object registration
+# (fat binary wrappers, module handles, compilation-unit ids) and one host-side
+# handle per kernel, named after the kernel.
+_TOOLCHAIN_SYMBOLS = re.compile(
+    r"^(_DYNAMIC|_GLOBAL_OFFSET_TABLE_|__dso_handle|__init|__fini|__do_(init|fini)\.\w+"
+    r"|DW\.ref\.\w+|__hip_(fatbin_wrapper|gpubin_handle_\w+|cuid_\w+))$"
+    r"|::\w+_kernel(<[^>]*>)?\(")
+
+
+def test_library_has_no_mutable_globals():
+    """The C ABI keeps no state between calls: apart from what the toolchain and
+    HIP put into every library, its writable data segments hold nothing (the
+    timer and the exact-selection switch are caller-owned)."""
+    import subprocess
+    nm = subprocess.run(["nm", "-C", "--defined-only", sk.LIB_PATH], capture_output=True,
+                        text=True)
+    if nm.returncode != 0:
+        pytest.skip("nm unavailable")
+    writable = [l.split(" ", 2)[2] for l in nm.stdout.splitlines()
+                if re.match(r"^[0-9a-f]+ [bBdD] ", l)]
+    assert writable, "no writable symbols listed at all: the nm output format changed"
+    own = [n for n in writable if not _TOOLCHAIN_SYMBOLS.search(n)]
+    assert not own, own
 
 
 def test_paged_descriptor_validation():
@@ -262,9 +302,9 @@ def test_baseline_comparator_validation():
     assert km(C.byref(cbd), FAKE, 0, 0, 128, 20, FAKE, need - 8, None) == WORKSPACE
     assert km(C.byref(cbd), FAKE, 0, 0, 128, 20, None, 0, None) == WORKSPACE
     ds = lib.sikv_dense_scores
-    assert ds(2, 2, 4, 1000, FAKE, FAKE, 0, 0, 128, None, None) == INVALID      # no output
-    assert ds(2, 2, 3, 1000, FAKE, FAKE, 0, 0, 128, FAKE, None) == INVALID      # Hq % Hkv
-    assert ds(2, 2, 18, 1000, FAKE, FAKE, 0, 0, 128, FAKE, None) == UNSUPPORTED  # G = 9
-    assert ds(2, 2, 4, 0, FAKE, FAKE, 0, 0, 128, FAKE, None) == INVALID
-    assert ds(2, 2, 4, 1000, FAKE + 2, FAKE, 0, 0, 128, FAKE, None) == INVALID
-    assert ds(2, 2, 4, 1000, FAKE, FAKE, 0, 0, 100, FAKE, None) == INVALID     # stride
+    assert ds(2, 2, 4, 1000, FAKE, FAKE, 0, 0, 128, None, None, None) == INVALID      # no output
+    assert ds(2, 2, 3, 1000, FAKE, FAKE, 0, 0, 128, FAKE, None, None) == INVALID      # Hq % Hkv
+    assert ds(2, 2, 18, 1000, FAKE, FAKE, 0, 0, 128, FAKE, None, None) == UNSUPPORTED  # G = 9
+    assert ds(2, 2, 4, 0, FAKE, FAKE, 0, 0, 128, FAKE, None, None) == INVALID
+    assert ds(2, 2, 4, 1000, FAKE + 2, FAKE, 0, 0, 128, FAKE, None, None) == INVALID
+    assert ds(2, 2, 4, 1000, FAKE, FAKE, 0, 0, 100, FAKE, None, None) == INVALID     # stride

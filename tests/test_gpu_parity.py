@@ -90,12 +90,8 @@ def test_parity_case(name, w):
             oidx[b, h] = O.select_topk(s, w.top_k)
 
     # exact whole-head selection path gives the identical selection
-    sk.debug_force_exact_select(True)
-    try:
-        idx2 = sk.sikv_score_topk(cache, q, w.top_k)
-        torch.cuda.synchronize()
-    finally:
-        sk.debug_force_exact_select(False)
+    idx2 = sk.sikv_score_topk(cache, q, w.top_k, exact_select=True)
+    torch.cuda.synchronize()
     assert np.array_equal(idx2.cpu().numpy(), gi)
 
     # attention on the oracle's selection
@@ -224,12 +220,8 @@ def test_codebook_parity(name, w):
         check_topk(gi[b, h], s, w.top_k, N, f"{name} topk b={b} h={h}")
         oidx[b, h] = O.select_topk(s, w.top_k)
 
-    sk.debug_force_exact_select(True)
-    try:
-        idx2 = sk.sikv_score_topk(cache, q, w.top_k)
-        torch.cuda.synchronize()
-    finally:
-        sk.debug_force_exact_select(False)
+    idx2 = sk.sikv_score_topk(cache, q, w.top_k, exact_select=True)
+    torch.cuda.synchronize()
     assert np.array_equal(idx2.cpu().numpy(), gi)
 
     out = sk.sikv_sparse_attn(cache, q, torch.from_numpy(oidx).cuda(), SM).cpu().numpy()
@@ -326,11 +318,7 @@ def test_select_list_in_workspace():
     o = oracle_head(d["K"][0, 0], N)
     s = oracle_scores(d["q"], o["codes"], o["alpha"], 0, 0, 1, N)
     check_topk(di[0, 0], s, w.top_k, N, "big_k topk")
-    sk.debug_force_exact_select(True)
-    try:
-        idx2 = sk.sikv_score_topk(cache, q, w.top_k).cpu().numpy()
-    finally:
-        sk.debug_force_exact_select(False)
+    idx2 = sk.sikv_score_topk(cache, q, w.top_k, exact_select=True).cpu().numpy()
     assert np.array_equal(idx2, di)
     ref = O.sparse_attention(d["q"][0, :G], di[0, 0], o["k_sink"], o["codes"], o["alpha"],
                              o["mu"], d["V"][0, 0], SM)
@@ -361,3 +349,32 @@ def test_stream_copy():
     sk.sikv_stream_copy(dst, src)
     torch.cuda.synchronize()
     assert torch.equal(dst, src)
+
+
+def test_caller_owned_timer():
+    """A Timer attached to one cache times that cache's calls only: one launch of
+    each decode kernel per step, positive durations; an untimed cache's calls
+    and a second timer see nothing of it."""
+    w = S.WORKLOADS["tiny_4k"]
+    say("[timer] tiny_4k, two caches, one timed")
+    d = S.draw(w)
+    K, V, q = dev_bf16(d["K"]), dev_bf16(d["V"]), dev_bf16(d["q"])
+    timed, plain = sk.Cache(1, 1, w.n_tokens, v=V), sk.Cache(1, 1, w.n_tokens, v=V)
+    for c in (timed, plain):
+        sk.sikv_encode(c, K)
+    t1, t2 = sk.Timer(), sk.Timer()
+    timed.timer = t1
+    for _ in range(3):
+        o1 = sk.sikv_decode_step(timed, q, w.top_k, SM)
+        o2 = sk.sikv_decode_step(plain, q, w.top_k, SM)
+    torch.cuda.synchronize()
+    r1, r2 = t1.read(), t2.read()
+    for name in ("prep", "score", "select", "attn", "combine"):
+        assert r1[name][0] == 3 and r1[name][1] > 0.0, (name, r1[name])
+    assert all(n == 0 for n, _ in r2.values())
+    assert r1["codes"][0] == 0          # the prefill ran before the timer was attached
+    assert torch.equal(o1, o2)
+    t1.reset()
+    assert all(n == 0 for n, _ in t1.read().values())
+    t1.close()
+    t2.close()

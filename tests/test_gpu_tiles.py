@@ -135,12 +135,8 @@ def test_sixteen_groups_per_wave():
     del K
     i1 = torch.empty((1, 1, k), dtype=torch.int32, device="cuda")
     o1 = sk.sikv_decode_step(cache, q, k, SM, idx_out=i1).cpu()
-    sk.debug_force_exact_select(True)
-    try:
-        i2 = torch.empty_like(i1)
-        o2 = sk.sikv_decode_step(cache, q, k, SM, idx_out=i2).cpu()
-    finally:
-        sk.debug_force_exact_select(False)
+    i2 = torch.empty_like(i1)
+    o2 = sk.sikv_decode_step(cache, q, k, SM, idx_out=i2, exact_select=True).cpu()
     torch.cuda.synchronize()
     assert torch.equal(i1.cpu(), i2.cpu()), "U16 top-k against the exact rescan"
     assert torch.equal(o1, o2), "U16 attention"
