@@ -354,12 +354,8 @@ def sikv_decode_step(cache: Cache, q: torch.Tensor, top_k: int, sm_scale: float 
     return out
 
 
-def sikv_append_decode_step(cache: Cache, k_new: torch.Tensor, q: torch.Tensor, top_k: int,
-                            sm_scale: float | None = None, idx_out: torch.Tensor | None = None,
-                            out: torch.Tensor | None = None, v_new: torch.Tensor | None = None):
-    """sikv_encode of token cache.n_tokens (k_new: [B, Hkv, 1, 128]) then
-    sikv_decode_step over n_tokens + 1 tokens, in one call (raises n_tokens).
-    v_new ([B, Hkv, 1, 128], quantised-value caches only) is encoded too."""
+def _append_decode_step(cache: Cache, k_new, q, top_k, sm_scale, idx_out, out, v_new,
+                        static: bool):
     kb = _bits(k_new)
     if kb.dim() != 4 or kb.shape[2] != 1:
         raise ValueError("k_new must be [B, Hkv, 1, 128]")
@@ -380,19 +376,43 @@ def sikv_append_decode_step(cache: Cache, k_new: torch.Tensor, q: torch.Tensor, 
         cache.seq_lens += 1   # every sequence appends one token (stream-ordered on the device)
     try:
         d = cache.desc()
-        need = int(lib.sikv_workspace_bytes(OP_DECODE_STEP, ctypes.byref(d), n_q, top_k))
-        ws, wsn = cache.ws.get(need)
-        _check(lib.sikv_append_decode_step(ctypes.byref(d), kb.data_ptr(), ksb, ksh, _ptr(vnb),
-                                           vsb, vsh, qb.data_ptr(), n_q, top_k, ctypes.c_float(sm),
-                                           _ptr(idx_out), out.data_ptr(), ws, wsn,
-                                           _stream(cache.device)),
-               "sikv_append_decode_step")
+        args = (ctypes.byref(d), kb.data_ptr(), ksb, ksh, _ptr(vnb), vsb, vsh, qb.data_ptr(), n_q,
+                top_k, ctypes.c_float(sm), _ptr(idx_out), out.data_ptr())
+        if static:
+            _check(lib.sikv_append_decode_step_static(*args, _stream(cache.device)),
+                   "sikv_append_decode_step_static")
+        else:
+            need = int(lib.sikv_workspace_bytes(OP_DECODE_STEP, ctypes.byref(d), n_q, top_k))
+            ws, wsn = cache.ws.get(need)
+            _check(lib.sikv_append_decode_step(*args, ws, wsn, _stream(cache.device)),
+                   "sikv_append_decode_step")
     except Exception:
         cache.n_tokens -= 1
         if cache.seq_lens is not None:
             cache.seq_lens -= 1
         raise
     return out
+
+
+def sikv_append_decode_step(cache: Cache, k_new: torch.Tensor, q: torch.Tensor, top_k: int,
+                            sm_scale: float | None = None, idx_out: torch.Tensor | None = None,
+                            out: torch.Tensor | None = None, v_new: torch.Tensor | None = None):
+    """sikv_encode of token cache.n_tokens (k_new: [B, Hkv, 1, 128]) then
+    sikv_decode_step over n_tokens + 1 tokens, in one call (raises n_tokens).
+    v_new ([B, Hkv, 1, 128], quantised-value caches only) is encoded too."""
+    return _append_decode_step(cache, k_new, q, top_k, sm_scale, idx_out, out, v_new, False)
+
+
+def sikv_append_decode_step_static(cache: Cache, k_new: torch.Tensor, q: torch.Tensor,
+                                   top_k: int, sm_scale: float | None = None,
+                                   idx_out: torch.Tensor | None = None,
+                                   out: torch.Tensor | None = None,
+                                   v_new: torch.Tensor | None = None):
+    """sikv_append_decode_step with the library's static device scratch instead of
+    a workspace: allocates nothing on the device (``out`` and ``idx_out`` given),
+    for callers that cannot allocate; the call serialises with every other call of
+    it on the same GPU (they share the scratch)."""
+    return _append_decode_step(cache, k_new, q, top_k, sm_scale, idx_out, out, v_new, True)
 
 
 def sikv_dense_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

@@ -59,6 +59,8 @@ SIGNATURES = {
     "sikv_decode_step": (_I32, [_DESC, _P, _I32, _I32, C.c_float, _P, _P, _P, _SZ, _P]),
     "sikv_append_decode_step": (_I32, [_DESC, _P, _I64, _I64, _P, _I64, _I64, _P, _I32, _I32,
                                        C.c_float, _P, _P, _P, _SZ, _P]),
+    "sikv_append_decode_step_static": (_I32, [_DESC, _P, _I64, _I64, _P, _I64, _I64, _P, _I32,
+                                              _I32, C.c_float, _P, _P, _P]),
     "sikv_encode_v": (_I32, [_DESC, _P, _I64, _I64, _I64, _I32, _I32, _P]),
     "sikv_workspace_bytes": (_SZ, [_I32, _DESC, _I32, _I32]),
     "sikv_status_str": (C.c_char_p, [_I32]),

@@ -5,6 +5,7 @@
 // from its own arguments.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <new>
 #include <vector>
@@ -342,6 +343,43 @@ void timing_events(::sikv_timer* t, int kernel_id, hipEvent_t* start, hipEvent_t
 }
 }  // namespace sikv
 
+namespace {
+
+// ------------------------------------------------------------------ static scratch
+// The workspace of the allocation-free entry point: a static array in this
+// file's device code, one per GPU (the runtime gives every device its own copy
+// when it loads the code object there).  In host code `scratch` names a host
+// stand-in, not device memory, so it is never passed to a kernel: its device
+// address, per device, comes from hipGetSymbolAddress with that device
+// current, once, and is kept in g_scratch.  That per-device address is the
+// only state the library keeps; it never changes once set.
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[SIKV_STATIC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// Device address of the scratch of the device `stream` belongs to (the current
+// device for the null stream).
+sikv_status static_scratch(void* stream, void** out) {
+  int dev = 0, cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return SIKV_ERR_HIP;
+  dev = cur;
+  if (stream != nullptr && hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) != hipSuccess)
+    return SIKV_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SIKV_ERR_UNSUPPORTED;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return SIKV_ERR_HIP;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return SIKV_ERR_HIP;
+    if (e != hipSuccess || p == nullptr || misaligned(p, kAlign)) return SIKV_ERR_HIP;
+    g_scratch[dev].store(p, std::memory_order_release);  // the same value on any race
+  }
+  *out = p;
+  return SIKV_OK;
+}
+
+}  // namespace
+
 // ================================================================== C ABI
 extern "C" {
 
@@ -414,11 +452,14 @@ sikv_status sikv_sparse_attn(const sikv_cache_desc* c, const uint16_t* q, int32_
 }
 
 namespace {
+
+// ws == nullptr with use_static: the stream's device's static scratch (after
+// every check, so an invalid call touches nothing).
 sikv_status decode_step(const sikv_cache_desc* c, const uint16_t* k_new, int64_t ksb, int64_t ksh,
                         const uint16_t* v_new, int64_t vnsb, int64_t vnsh,
                         const uint16_t* q, int32_t n_q_heads, int32_t top_k, float sm_scale,
                         int32_t* idx_out_opt, float* out, void* ws, size_t ws_bytes,
-                        void* stream) {
+                        void* stream, bool use_static = false) {
   sikv_status st = check_desc(c);
   if (st != SIKV_OK) return st;
   st = check_query(c, q, n_q_heads, top_k);
@@ -429,6 +470,12 @@ sikv_status decode_step(const sikv_cache_desc* c, const uint16_t* k_new, int64_t
   if (!std::isfinite(sm_scale)) return SIKV_ERR_INVALID_ARG;
   DecodePlan dp;
   if (!plan_decode(c, n_q_heads, top_k, &dp)) return SIKV_ERR_UNSUPPORTED;
+  if (use_static) {
+    if (dp.bytes > SIKV_STATIC_SCRATCH_BYTES) return SIKV_ERR_WORKSPACE;
+    st = static_scratch(stream, &ws);
+    if (st != SIKV_OK) return st;
+    ws_bytes = SIKV_STATIC_SCRATCH_BYTES;
+  }
   st = check_ws(ws, ws_bytes, dp.bytes);
   if (st != SIKV_OK) return st;
   const Launch s = ctx(c, stream);
@@ -464,6 +511,21 @@ sikv_status sikv_append_decode_step(const sikv_cache_desc* c, const uint16_t* k_
     return SIKV_ERR_INVALID_ARG;
   return decode_step(c, k_new, k_stride_b, k_stride_h, v_new, v_stride_b, v_stride_h, q,
                      n_q_heads, top_k, sm_scale, idx_out_opt, out, ws, ws_bytes, stream);
+}
+
+sikv_status sikv_append_decode_step_static(const sikv_cache_desc* c, const uint16_t* k_new,
+                                           int64_t k_stride_b, int64_t k_stride_h,
+                                           const uint16_t* v_new, int64_t v_stride_b,
+                                           int64_t v_stride_h, const uint16_t* q,
+                                           int32_t n_q_heads, int32_t top_k, float sm_scale,
+                                           int32_t* idx_out_opt, float* out, void* stream) {
+  if (k_new == nullptr || misaligned(k_new, 16) || bad_strides(k_stride_b, k_stride_h, 0))
+    return SIKV_ERR_INVALID_ARG;
+  if (v_new != nullptr && (c == nullptr || c->vrec == nullptr || misaligned(v_new, 16) ||
+                           bad_strides(v_stride_b, v_stride_h, 0)))
+    return SIKV_ERR_INVALID_ARG;
+  return decode_step(c, k_new, k_stride_b, k_stride_h, v_new, v_stride_b, v_stride_h, q,
+                     n_q_heads, top_k, sm_scale, idx_out_opt, out, nullptr, 0, stream, true);
 }
 
 sikv_status sikv_encode_v(const sikv_cache_desc* c, const uint16_t* v, int64_t v_stride_b,

@@ -29,10 +29,12 @@
  *   - Shapes: head_dim 128 and 64 sinks only (SIKV_ERR_UNSUPPORTED otherwise);
  *     query heads per KV head (G = n_q_heads / n_kv_heads) from 1 to 8, query
  *     head h*G+g belongs to KV head h.
- *   - State: the library keeps none.  Everything a call reads is in its
- *     arguments and the descriptor (including the optional caller-owned timer
- *     and the flags word), so calls may run concurrently from several threads
- *     on different streams with disjoint buffers and workspaces.
+ *   - State: the library keeps none, apart from the one allocation-free entry
+ *     point's static device scratch (sikv_append_decode_step_static).
+ *     Everything any other call reads is in its arguments and the descriptor
+ *     (including the optional caller-owned timer and the flags word), so those
+ *     calls may run concurrently from several threads on different streams with
+ *     disjoint buffers and workspaces.
  */
 #ifndef SIKV_H
 #define SIKV_H
@@ -271,6 +273,32 @@ sikv_status sikv_append_decode_step(const sikv_cache_desc *cache, const uint16_t
                                     int64_t v_stride_h, const uint16_t *q, int32_t n_q_heads,
                                     int32_t top_k, float sm_scale, int32_t *idx_out_opt,
                                     float *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Bytes of the library's static device scratch (sikv_append_decode_step_static). */
+#define SIKV_STATIC_SCRATCH_BYTES ((size_t)80 << 20)
+
+/*
+ * sikv_append_decode_step_static - sikv_append_decode_step for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same arguments without the
+ * workspace, the same kernels and results.  Its scratch is a static array of
+ * SIKV_STATIC_SCRATCH_BYTES in the library's device code, one per GPU, held
+ * until the process ends; the call allocates and frees nothing.
+ *   - Calls whose workspace need, sikv_workspace_bytes(SIKV_OP_DECODE_STEP,
+ *     ...), exceeds SIKV_STATIC_SCRATCH_BYTES return SIKV_ERR_WORKSPACE and
+ *     launch nothing (80 MiB covers 4 x 8 KV heads at 128K tokens).
+ *   - The scratch of the stream's device is used (the current device for the
+ *     null stream).  Every call on one GPU shares it and it keeps the last
+ *     call's contents (no kernel reads scratch it did not write in the same
+ *     call): calls that overlap on one GPU, on different streams or threads,
+ *     race and give undefined results.  Serialise them.
+ */
+sikv_status sikv_append_decode_step_static(const sikv_cache_desc *cache, const uint16_t *k_new,
+                                           int64_t k_stride_b, int64_t k_stride_h,
+                                           const uint16_t *v_new, int64_t v_stride_b,
+                                           int64_t v_stride_h, const uint16_t *q,
+                                           int32_t n_q_heads, int32_t top_k, float sm_scale,
+                                           int32_t *idx_out_opt, float *out, void *stream);
 
 /* Workspace bytes needed by `op` (SIKV_OP_*) for this cache and call shape.
  * Host only, launches nothing.  Returns 0 for an invalid combination. */

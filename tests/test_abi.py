@@ -195,6 +195,34 @@ def test_quantised_value_validation():
     assert score(misal) == INVALID
 
 
+def test_static_scratch_entry_point_validation():
+    """sikv_append_decode_step_static checks everything before it touches the
+    GPU: bad arguments and a workspace need above the static scratch size are
+    rejected with nothing launched (the size comes from the header)."""
+    f = C.c_float
+    st = lib.sikv_append_decode_step_static
+    d = desc()
+    assert st(C.byref(d), None, 1024, 128, None, 0, 0, FAKE, 4, 16, f(0.088), None, FAKE,
+              None) == INVALID
+    assert st(C.byref(d), FAKE, 1024, 100, None, 0, 0, FAKE, 4, 16, f(0.088), None, FAKE,
+              None) == INVALID
+    assert st(C.byref(d), FAKE, 1024, 128, None, 0, 0, FAKE, 4, 16, f(0.088), None, None,
+              None) == INVALID
+    assert st(None, FAKE, 1024, 128, None, 0, 0, FAKE, 4, 16, f(0.088), None, FAKE,
+              None) == INVALID
+    limit = int(re.search(r"#define SIKV_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)",
+                          open(HEADER).read()).expand(r"\1 \2").split()[0]) << 20
+    # 4 x 8 KV heads at 128K tokens fit; 8 x 8 heads at 512K do not
+    fits = desc(batch=4, n_kv_heads=8, capacity=131072, n_tokens=131072, v_stride_b=8 * 131072 * 128,
+                v_stride_h=131072 * 128)
+    big = desc(batch=8, n_kv_heads=8, capacity=524288, n_tokens=524288, v_stride_b=8 * 524288 * 128,
+               v_stride_h=524288 * 128)
+    assert 0 < lib.sikv_workspace_bytes(3, C.byref(fits), 32, 9830) <= limit
+    assert lib.sikv_workspace_bytes(3, C.byref(big), 32, 4096) > limit
+    assert st(C.byref(big), FAKE, 1024, 128, None, 0, 0, FAKE, 32, 4096, f(0.088), None, FAKE,
+              None) == WORKSPACE
+
+
 def test_encode_validation():
     d = desc()
     e = lib.sikv_encode
@@ -249,12 +277,16 @@ _TOOLCHAIN_SYMBOLS = re.compile(
     r"^(_DYNAMIC|_GLOBAL_OFFSET_TABLE_|__dso_handle|__init|__fini|__do_(init|fini)\.\w+"
     r"|DW\.ref\.\w+|__hip_(fatbin_wrapper|gpubin_handle_\w+|cuid_\w+))$"
     r"|::\w+_kernel(<[^>]*>)?\(")
+# The one exception, by design: the allocation-free entry point's static device
+# scratch (its host stand-in) and the per-device address of it, set once.
+_STATIC_SCRATCH = re.compile(r"^\(anonymous namespace\)::(scratch|g_scratch)$")
 
 
 def test_library_has_no_mutable_globals():
     """The C ABI keeps no state between calls: apart from what the toolchain and
-    HIP put into every library, its writable data segments hold nothing (the
-    timer and the exact-selection switch are caller-owned)."""
+    HIP put into every library and the allocation-free entry point's static
+    scratch, its writable data segments hold nothing (the timer and the
+    exact-selection switch are caller-owned)."""
     import subprocess
     nm = subprocess.run(["nm", "-C", "--defined-only", sk.LIB_PATH], capture_output=True,
                         text=True)
@@ -263,7 +295,8 @@ def test_library_has_no_mutable_globals():
     writable = [l.split(" ", 2)[2] for l in nm.stdout.splitlines()
                 if re.match(r"^[0-9a-f]+ [bBdD] ", l)]
     assert writable, "no writable symbols listed at all: the nm output format changed"
-    own = [n for n in writable if not _TOOLCHAIN_SYMBOLS.search(n)]
+    own = [n for n in writable
+           if not _TOOLCHAIN_SYMBOLS.search(n) and not _STATIC_SCRATCH.search(n)]
     assert not own, own
 
 
