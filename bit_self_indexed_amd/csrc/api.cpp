@@ -39,7 +39,7 @@ struct EncodePlan {
 struct ScorePlan {
   int chunk, n_chunks;
   size_t off_tau, off_bin, off_cnt, off_ckey, off_ct, off_pkey, off_pt, off_tab, off_inv,
-      off_lut, off_qmu, off_slog;
+      off_lut, off_qmu, off_slog, off_app;
   size_t bytes;
 };
 
@@ -48,7 +48,8 @@ struct AttnPlan {
   size_t off_o, off_ml, off_lut, off_qmu, off_slog, bytes;
 };
 
-// Attention tables of the query heads, written by the prep kernel.
+// Attention tables of the query heads, written by the score kernel's leaders
+// (or, for a standalone attention call, the tables kernel).
 struct AttnTables {
   float* lut;
   float* qmu;
@@ -90,9 +91,9 @@ bool plan_score(const sikv_cache_desc* c, int n_q_heads, ScorePlan* p) {
   p->n_chunks = (int)cdiv(n, p->chunk);
   const size_t cap = (size_t)BH * p->n_chunks * p->chunk;
   size_t o = 0;
-  p->off_tau = o;  o += align_up((size_t)BH * sizeof(float));
+  p->off_tau = o;  o += align_up((size_t)BH * sizeof(unsigned long long));
   p->off_bin = o;  o += align_up((size_t)BH * sizeof(float));
-  p->off_cnt = o;  o += align_up((size_t)BH * p->n_chunks * sizeof(int32_t));
+  p->off_cnt = o;  o += align_up((size_t)BH * p->n_chunks * sizeof(int2));
   p->off_ckey = o; o += align_up(cap * sizeof(uint32_t));
   p->off_ct = o;   o += align_up(cap * sizeof(int32_t));
   p->off_pkey = o; o += align_up(cap * sizeof(uint32_t));
@@ -102,6 +103,7 @@ bool plan_score(const sikv_cache_desc* c, int n_q_heads, ScorePlan* p) {
   p->off_lut = o;  o += align_up((size_t)c->batch * n_q_heads * kLut * sizeof(float));
   p->off_qmu = o;  o += align_up((size_t)c->batch * n_q_heads * sizeof(float));
   p->off_slog = o; o += align_up((size_t)c->batch * n_q_heads * kSink * sizeof(float));
+  p->off_app = o;  o += align_up((size_t)BH * sizeof(uint32_t));
   p->bytes = o;
   return true;
 }
@@ -225,39 +227,68 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
-// prep (tables + threshold) -> score -> select.  The prep kernel also leaves the
-// query heads' attention tables in the workspace for a following attention.
-// k_new (may be null): key of token n_tokens-1, encoded by the prep kernel first.
+// The score kernel's arguments for this cache and query (workspace pointers
+// left null).
+ScoreArgs score_args(const sikv_cache_desc* c, const uint16_t* q, int n_q_heads, int top_k) {
+  ScoreArgs a{};
+  a.n_heads = c->batch * c->n_kv_heads;
+  a.codes = c->codes;
+  a.alpha = c->alpha;
+  a.rm = rows_of(c);
+  a.n_tokens = c->n_tokens;
+  a.Hkv = c->n_kv_heads;
+  a.seq_lens = c->seq_lens;
+  a.mu = c->mu;
+  a.k_sink = c->k_sink;
+  a.codebook = c->codebook;
+  a.vrec = c->vrec;
+  a.q = q;
+  a.n_q_heads = n_q_heads;
+  a.G = n_q_heads / c->n_kv_heads;
+  a.top_k = top_k;
+  a.mode = (c->flags & SIKV_FLAG_EXACT_SELECT) ? 2 : 1;
+  return a;
+}
+
+// score (leaders: selection table + threshold; tiles: candidates) -> select
+// (+ the query heads' attention tables, left in the workspace for a following
+// attention).  k_new (may be null): key of each sequence's last token,
+// encoded by the score kernel first.
 sikv_status run_score_topk(const sikv_cache_desc* c, const uint16_t* q, int n_q_heads, int top_k,
                            int32_t* idx, float* scores_opt, void* ws, const ScorePlan& sp,
                            const uint16_t* k_new, int64_t ksb, int64_t ksh,
                            const uint16_t* v_new, int64_t vnsb, int64_t vnsh, const Launch& s) {
-  const int B = c->batch, Hkv = c->n_kv_heads;
-  float* tau = at<float>(ws, sp.off_tau);
-  int32_t* cnt = at<int32_t>(ws, sp.off_cnt);
-  uint32_t* ckey = at<uint32_t>(ws, sp.off_ckey);
-  int32_t* ct = at<int32_t>(ws, sp.off_ct);
-  uint32_t* pkey = at<uint32_t>(ws, sp.off_pkey);
-  int32_t* pt = at<int32_t>(ws, sp.off_pt);
-  int32_t* tab = at<int32_t>(ws, sp.off_tab);
-  float* inv = at<float>(ws, sp.off_inv);
-  const int mode = (c->flags & SIKV_FLAG_EXACT_SELECT) ? 2 : 1;
-  SIKV_TRY(launch_prep(q, n_q_heads, B, Hkv, c->mu, c->codes, c->alpha, rows_of(c), c->n_tokens,
-                       c->k_sink, k_new, ksb, ksh, v_new, vnsb, vnsh, c->vrec, c->codebook,
-                       top_k, mode, tab, inv,
-                       at<float>(ws, sp.off_lut), at<float>(ws, sp.off_qmu),
-                       at<float>(ws, sp.off_slog), tau, at<float>(ws, sp.off_bin), c->seq_lens,
-                       s));
-  SIKV_TRY(launch_score(B, Hkv, c->codes, c->alpha, rows_of(c), c->n_tokens, c->seq_lens, tab,
-                        inv, tau, sp.chunk, sp.n_chunks, ckey, ct, cnt, scores_opt, s));
-  SIKV_TRY(launch_select(B, Hkv, c->codes, c->alpha, rows_of(c), c->n_tokens, c->seq_lens, tab,
-                         inv, top_k, sp.chunk, sp.n_chunks, ckey, ct, cnt, tau,
-                         at<float>(ws, sp.off_bin), pkey, pt, idx, s));
+  ScoreArgs a = score_args(c, q, n_q_heads, top_k);
+  a.k_new = k_new;
+  a.ksb = ksb;
+  a.ksh = ksh;
+  a.v_new = v_new;
+  a.vnsb = vnsb;
+  a.vnsh = vnsh;
+  a.tau_word = at<unsigned long long>(ws, sp.off_tau);
+  a.bin_scale = at<float>(ws, sp.off_bin);
+  a.sel_lut = at<int32_t>(ws, sp.off_tab);
+  a.sel_inv = at<float>(ws, sp.off_inv);
+  a.att_lut = at<float>(ws, sp.off_lut);
+  a.att_qmu = at<float>(ws, sp.off_qmu);
+  a.att_slog = at<float>(ws, sp.off_slog);
+  a.app_key = at<uint32_t>(ws, sp.off_app);
+  a.n_chunks = sp.n_chunks;
+  a.cand_key = at<uint32_t>(ws, sp.off_ckey);
+  a.cand_t = at<int32_t>(ws, sp.off_ct);
+  a.chunk_count = at<int2>(ws, sp.off_cnt);
+  a.scores_opt = scores_opt;
+  SIKV_TRY(launch_score(a, sp.chunk, s));
+  SIKV_TRY(launch_select(c->batch, c->n_kv_heads, c->codes, c->alpha, rows_of(c), c->n_tokens,
+                         c->seq_lens, a.sel_lut, a.sel_inv, top_k, sp.chunk, sp.n_chunks,
+                         a.cand_key, a.cand_t, a.chunk_count, a.tau_word, a.bin_scale,
+                         k_new != nullptr ? a.app_key : nullptr, at<uint32_t>(ws, sp.off_pkey),
+                         at<int32_t>(ws, sp.off_pt), idx, a, s));
   return SIKV_OK;
 }
 
-// Attention (+ split merge).  tab: the query heads' tables; built here by a prep
-// launch when the caller has none (standalone call).
+// Attention (+ split merge).  tab: the query heads' tables; built here by a
+// tables launch when the caller has none (standalone call).
 sikv_status run_attn(const sikv_cache_desc* c, const uint16_t* q, int n_q_heads,
                      const int32_t* idx, int top_k, float sm_scale, float* out, void* ws,
                      const AttnPlan& ap, const AttnTables* tab, const Launch& s) {
@@ -265,10 +296,11 @@ sikv_status run_attn(const sikv_cache_desc* c, const uint16_t* q, int n_q_heads,
   float* pml = at<float>(ws, ap.off_ml);
   AttnTables own{at<float>(ws, ap.off_lut), at<float>(ws, ap.off_qmu), at<float>(ws, ap.off_slog)};
   if (tab == nullptr) {
-    SIKV_TRY(launch_prep(q, n_q_heads, c->batch, c->n_kv_heads, c->mu, c->codes, c->alpha,
-                         rows_of(c), c->n_tokens, c->k_sink, nullptr, 0, 0, nullptr, 0, 0,
-                         nullptr, c->codebook, top_k, 0, nullptr,
-                         nullptr, own.lut, own.qmu, own.slog, nullptr, nullptr, c->seq_lens, s));
+    ScoreArgs a = score_args(c, q, n_q_heads, top_k);
+    a.att_lut = own.lut;
+    a.att_qmu = own.qmu;
+    a.att_slog = own.slog;
+    SIKV_TRY(launch_tables(a, s));
     tab = &own;
   }
   SIKV_TRY(launch_attn(n_q_heads, c->batch, c->n_kv_heads, c->codes, c->alpha, c->v,
@@ -279,7 +311,7 @@ sikv_status run_attn(const sikv_cache_desc* c, const uint16_t* q, int n_q_heads,
   return SIKV_OK;
 }
 
-const char* const g_names[KID_COUNT] = {"mu_partial", "mu_final", "codes", "prep",
+const char* const g_names[KID_COUNT] = {"mu_partial", "mu_final", "codes", "tables",
                                         "score",      "select",   "attn",  "combine",
                                         "dense",      "copy",     "cb_final", "vcodes",
                                         "kmeans_assign", "dense_scores"};

@@ -27,7 +27,6 @@
 //             every token, so the result never depends on the sample.
 #include <hip/hip_ext.h>
 
-#include <type_traits>
 
 #include "sikv_internal.h"
 
@@ -35,9 +34,10 @@ namespace sikv {
 
 namespace {
 
-constexpr int kSampleMax = 3072;   // sampled candidates per head
-constexpr int kSampleRun = 16;     // contiguous tokens per stratum (192 strata)
-constexpr int kSelectLds = 16384;  // candidates kept in LDS by select
+constexpr int kSampleMax = 2048;   // sampled candidates per head
+constexpr int kSampleRun = 16;     // contiguous tokens per stratum (128 strata)
+constexpr int kBandBins = 1024;    // equal-width bins of the sample's band
+constexpr int kSelectLds = 20480;  // candidates kept in LDS by select (keys + 16-bit offsets)
 constexpr int kMaxChunks = 2048;
 constexpr int kSubMax = 1024;
 
@@ -263,27 +263,47 @@ __device__ void block_emit(const uint32_t* keys, const int32_t* pos, int n, int 
   }
 }
 
-// The select kernel's LDS list (n <= kSelectLds entries) cut into one run per
-// thread, held in registers: an odd run length, so that the runs' strided LDS
-// reads never share a bank.
-constexpr int kEmitRun = 17;  // longest run: odd and >= kSelectLds / 1024
+// The select kernel's LDS list (n <= kSelectLds entries: keys, and positions
+// as 16-bit offsets within their tile) cut into one run per thread, held in
+// registers: an odd run length, so that the runs' strided LDS reads of the keys
+// never share a bank.
+constexpr int kEmitRun = 21;  // longest run: odd and >= kSelectLds / 1024
 static_assert(kEmitRun >= ((kSelectLds / 1024) | 1), "runs of a 1024-thread block");
 struct Run {
   uint32_t key[kEmitRun];
-  int32_t pos[kEmitRun];
+  uint32_t pos[kEmitRun];
   int per, i0, n;
   __device__ __forceinline__ bool valid(int j) const { return j < per && i0 + j < n; }
 };
 
-// Loads the runs (blockDim.x = 1024).  No barrier.
-__device__ __forceinline__ void run_load(Run& rn, const uint32_t* keys, const int32_t* pos, int n) {
+// Loads the runs (blockDim.x = 1024) and turns each entry's offset into its
+// position: its tile's first token (64 + tile * chunk; the tile of list entry i
+// is the last one whose list offset off[tile] <= i) plus the offset; entries
+// past the tiles' (an appended token) get last_pos.  The tile of the run's
+// first entry comes from a binary search of off[], then only crossings read
+// it again.  No barrier.
+__device__ __forceinline__ void run_load(Run& rn, const uint32_t* keys, const uint16_t* ofs, int n,
+                                         const int* off, int n_chunks, int chunk, int last_pos) {
   rn.per = ((n + blockDim.x - 1) / blockDim.x) | 1;
   rn.i0 = threadIdx.x * rn.per;
   rn.n = n;
 #pragma unroll
   for (int j = 0; j < kEmitRun; ++j) {
     rn.key[j] = rn.valid(j) ? keys[rn.i0 + j] : 0u;
-    rn.pos[j] = rn.valid(j) ? pos[rn.i0 + j] : 0;
+    rn.pos[j] = rn.valid(j) ? ofs[rn.i0 + j] : 0u;
+  }
+  int ci = 0;
+  for (int step = 1 << 11; step > 0; step >>= 1)
+    if (ci + step <= n_chunks && off[ci + step] <= rn.i0) ci += step;
+  int next = ci < n_chunks ? off[ci + 1] : 0x7fffffff;  // first entry of the following tile
+#pragma unroll
+  for (int j = 0; j < kEmitRun; ++j) {
+    const int i = rn.i0 + j;
+    while (i >= next) {  // crossing into a later tile (rare)
+      ++ci;
+      next = ci < n_chunks ? off[ci + 1] : 0x7fffffff;
+    }
+    rn.pos[j] = ci < n_chunks ? (uint32_t)(kSink + ci * chunk) + rn.pos[j] : (uint32_t)last_pos;
   }
 }
 
@@ -309,7 +329,7 @@ __device__ void run_emit(const Run& rn, int k, Kth r, uint32_t* stage, int32_t* 
   for (int j = 0; j < kEmitRun; ++j) {
     bool take = rn.valid(j) && rn.key[j] > r.key;
     if (rn.valid(j) && rn.key[j] == r.key) take = eq_before++ < r.need;
-    if (take && o < k) stage[o++] = (uint32_t)rn.pos[j];
+    if (take && o < k) stage[o++] = rn.pos[j];
   }
   __syncthreads();
   for (int j = threadIdx.x; j < k; j += blockDim.x) out[j] = (int32_t)stage[j];
@@ -323,56 +343,78 @@ __device__ __forceinline__ void load_itab(const int* __restrict__ gtab, int* ita
   for (int i = threadIdx.x; i < kLut / 4; i += blockDim.x) dst[i] = src[i];
 }
 
-// Two bounds from one 2048-bin equal-width histogram of the n scores sc, all in
-// [smin, smax]: *lo at or below the k_lo-th largest (the lower edge of its bin,
-// lowered by one more bin so that rounding cannot lift it above), and *hi at or
-// above the k_hi-th largest (the upper edge of its bin, raised by one more bin;
-// smax if k_hi < 1).  1 <= k_lo <= n.  hist: LDS, 2048 counters already zero
-// (and published); tmp: LDS >= 24 ints, which hold the two bins on return (no
-// barrier after their last read: the caller does not reuse tmp or hist).
-__device__ void block_score_band(const float* sc, int n, int k_lo, int k_hi, float smin,
-                                 float smax, uint32_t* hist, int* tmp, float* lo, float* hi) {
+// Two bounds from one kBandBins-bin equal-width histogram of the m sample
+// scores sc[0..m) (LDS; thread tid wrote sc[tid + 256u] and passes the minimum
+// and maximum of its valid ones): *lo at or below the k_lo-th largest (the
+// lower edge of its bin, lowered by one more bin so that rounding cannot lift
+// it above), *hi at or above the k_hi-th largest (the upper edge of its bin,
+// raised by one more bin; the maximum if k_hi < 1).  1 <= k_lo <= m.  Two
+// barriers; then wave 0 alone scans the bins, and its results are the ones to
+// use.  hist: LDS, kBandBins counters already zero (and published); red: LDS
+// >= 8 floats.
+template <int P>
+__device__ void block_score_band(const float* sc, float smin, float smax, int m, int k_lo, int k_hi,
+                                 uint32_t* hist, float* red, float* lo, float* hi) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  smin = row_allreduce(smin, [](float x, float y) { return fminf(x, y); });
+  smax = row_allreduce(smax, [](float x, float y) { return fmaxf(x, y); });
+  smin = fminf(fminf(readlane(smin, 0), readlane(smin, 16)), fminf(readlane(smin, 32), readlane(smin, 48)));
+  smax = fmaxf(fmaxf(readlane(smax, 0), readlane(smax, 16)), fmaxf(readlane(smax, 32), readlane(smax, 48)));
+  if (lane == 0) {
+    red[wave] = smin;
+    red[4 + wave] = smax;
+  }
+  __syncthreads();
+  smin = fminf(fminf(red[0], red[1]), fminf(red[2], red[3]));
+  smax = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
   if (!(smax > smin)) {
     *lo = smin;
     *hi = smax;
     return;
   }
-  constexpr int kBins = 2048;
-  const float w = (smax - smin) * (1.0f / kBins);
-  const float inv = (float)kBins / (smax - smin);
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const int d = min(max((int)((sc[i] - smin) * inv), 0), kBins - 1);
-    atomicAdd(&hist[d], 1u);
+  const float w = (smax - smin) * (1.0f / kBandBins);
+  const float inv = (float)kBandBins / (smax - smin);
+#pragma unroll
+  for (int u = 0; u < P; ++u) {
+    const int i = tid + 256 * u;
+    if (i < m) atomicAdd(&hist[min(max((int)((sc[i] - smin) * inv), 0), kBandBins - 1)], 1u);
   }
   __syncthreads();
-  const int per = (kBins + blockDim.x - 1) / blockDim.x;
-  const int d0 = threadIdx.x * per;
-  int cnt = 0;
-  for (int d = d0; d < d0 + per && d < kBins; ++d) cnt += (int)hist[d];
-  if (threadIdx.x == 0) tmp[21] = kBins - 1;  // published by the scan's barriers
-  int total;
-  int pre = block_excl_scan(cnt, tmp, &total);  // uses tmp[0..15]
-  const int x_lo = total - k_lo;  // ascending ranks of the k-th largest
-  const int x_hi = total - k_hi;
-  for (int d = d0; d < d0 + per && d < kBins; ++d) {
-    const int c = (int)hist[d];
-    if (pre <= x_lo && x_lo < pre + c) tmp[18] = d;
-    if (k_hi >= 1 && pre <= x_hi && x_hi < pre + c) tmp[21] = d;
+  if (wave != 0) return;
+  // lane l owns bins kB*l .. kB*l + kB - 1 (ascending scores)
+  constexpr int kB = kBandBins / 64;
+  uint32_t cnt[kB];
+  int tot = 0;
+#pragma unroll
+  for (int u = 0; u < kB; ++u) {
+    cnt[u] = hist[lane * kB + u];
+    tot += (int)cnt[u];
+  }
+  int pre = wave_incl_scan(tot) - tot;
+  const int x_lo = m - k_lo, x_hi = m - k_hi;  // ascending ranks of the k-th largest
+  int dl = -1, dh = -1;
+#pragma unroll
+  for (int u = 0; u < kB; ++u) {
+    const int c = (int)cnt[u];
+    if (pre <= x_lo && x_lo < pre + c) dl = lane * kB + u;
+    if (k_hi >= 1 && pre <= x_hi && x_hi < pre + c) dh = lane * kB + u;
     pre += c;
   }
-  __syncthreads();
-  const int dl = tmp[18], dh = tmp[21];
-  *lo = smin + (float)(dl - 1) * w;
-  *hi = k_hi >= 1 ? fminf(smax, smin + (float)(dh + 2) * w) : smax;
+  const uint64_t ml = __ballot(dl >= 0), mh = __ballot(dh >= 0);  // one lane each
+  const int bl = __builtin_amdgcn_readlane(dl, (int)__builtin_ctzll(ml));
+  const int bhi = mh ? __builtin_amdgcn_readlane(dh, (int)__builtin_ctzll(mh)) : kBandBins - 1;
+  *lo = smin + (float)(bl - 1) * w;
+  *hi = k_hi >= 1 ? fminf(smax, smin + (float)(bhi + 2) * w) : smax;
 }
 
 // rank: how many of the sampled scores lie at or above tau.  For a small head the
-// whole candidate set (n <= 3072) is the sample and rank = k (tau is then at most
-// the exact k-th score).  Otherwise the expected rank e = k * 3072 / n of the k-th
-// score in the sample plus five standard deviations and a small floor, so that
-// fewer than k tokens pass only with negligible probability (the select kernel
+// whole candidate set (n <= 2048) is the sample and rank = k (tau is then at most
+// the exact k-th score).  Otherwise the expected rank e = k * 2048 / n of the k-th
+// score in the sample plus four standard deviations (of a binomial count; the
+// stratified sample varies less) and a small floor, so that fewer than k tokens
+// pass only with negligible probability (about 3e-5 per head; the select kernel
 // handles that case exactly anyway).  rank_hi: the rank of the upper end of the
-// select kernel's score bins, e - 5 sqrt(e) - 8 (the k-th score lies below it
+// select kernel's score bins, e - 4 sqrt(e) - 8 (the k-th score lies below it
 // with high probability), or the top of the sample if that is below 1.
 __device__ __forceinline__ void sample_ranks(int k, int n, int* rank, int* rank_hi) {
   if (n <= kSampleMax) {
@@ -381,364 +423,535 @@ __device__ __forceinline__ void sample_ranks(int k, int n, int* rank, int* rank_
     return;
   }
   const double e = (double)k * kSampleMax / (double)n;
-  const double r = e + 5.0 * sqrt(e) + 8.0;
+  const double r = e + 4.0 * sqrt(e) + 8.0;
   *rank = r > kSampleMax ? kSampleMax + 1 : (int)r + 1;
-  const double rh = e - 5.0 * sqrt(e) - 8.0;
+  const double rh = e - 4.0 * sqrt(e) - 8.0;
   *rank_hi = rh < 1.0 ? 0 : (int)rh;
 }
 
-// ------------------------------------------------------------------ prep
-// mode 0: attention tables only (sel_lut, sel_inv and tau unused); 1: all tables
-// + sampled threshold; 2: all tables + tau = +inf (forces the exact whole-head
-// selection).  k_new != null: first encode the key of token n_tokens-1 (append);
-// the sample then leaves that token out.  Every global load is issued before
-// the first barrier.
-__global__ __launch_bounds__(1024) void prep_kernel(
-    const uint16_t* __restrict__ q, int n_q_heads, int Hkv, int G, const float* __restrict__ mu,
-    uint8_t* __restrict__ codes, float* __restrict__ alpha, RowMap rm, int n_tokens,
-    const uint16_t* __restrict__ k_sink, const uint16_t* __restrict__ k_new, int64_t ksb,
-    int64_t ksh, const uint16_t* __restrict__ v_new, int64_t vnsb, int64_t vnsh,
-    uint8_t* __restrict__ vrec,
-    const float* __restrict__ codebook, int top_k, int mode, const int32_t* __restrict__ seq_lens,
-    int* __restrict__ sel_lut, float* __restrict__ sel_inv, float* __restrict__ att_lut,
-    float* __restrict__ att_qmu, float* __restrict__ att_slog, float* __restrict__ tau,
-    float* __restrict__ bin_scale) {
-  __shared__ float qv[kMaxGroup + 1][kD];  // q_g, then the selection query (sum)
-  __shared__ float mus[kD];
-  __shared__ int itab[kLut];
-  __shared__ float red_a[2];
-  __shared__ float4 cbl[kLut];             // codebook centres of this KV head, if any
-  __shared__ float jmax[kSub];
-  __shared__ float ssc[kSampleMax];
-  __shared__ uint32_t hist[2048];
-  __shared__ int tmp[32];
-  __shared__ uint32_t mm[32];
-  const int bh = blockIdx.x, b = bh / Hkv, h = bh - b * Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nt = seq_len(seq_lens, b, n_tokens);                   // this sequence's length
-  const int n = nt - kSink - (k_new != nullptr ? 1 : 0);  // candidates the sample covers
-  int rank = 1, rank_hi = 0;
-  if (mode == 1) sample_ranks(seq_topk(top_k, nt), n, &rank, &rank_hi);
-  const bool full = n <= kSampleMax;
-  const int m = full ? n : kSampleMax;
-  const bool sample = mode == 1 && m > 0 && rank <= m;
-  const int64_t hq0 = (int64_t)b * n_q_heads + (int64_t)h * G;
-  const bool has_cb = codebook != nullptr;
-  const float4 cbv = (has_cb && tid < kLut)
-                         ? reinterpret_cast<const float4*>(codebook)[(int64_t)bh * kLut + tid]
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
+// The threshold word: a head's leader block publishes (kTauTag << 32 | tau bits)
+// with one device-scope store; the select kernel clears it after reading it, so
+// a word left from an earlier call never carries the tag.
+constexpr uint32_t kTauTag = 0x53494b56u;
+constexpr int kTauPolls = 4096;  // bounded wait: then the tile keeps every token
 
-  for (int i = tid; i < 2048; i += blockDim.x) hist[i] = 0u;  // the band's counters
-
-  // Appended value row (quantised values): 16 lanes of wave 1, 8 channels each.
-  uint4 vw = make_uint4(0u, 0u, 0u, 0u);
-  if (v_new != nullptr && tid >= 64 && tid < 80)
-    vw = *reinterpret_cast<const uint4*>(v_new + (int64_t)b * vnsb + (int64_t)h * vnsh +
-                                         (tid - 64) * 8);
-  // Appended key row: 16 lanes x 8 channels, with the matching means.
-  uint4 kw = make_uint4(0u, 0u, 0u, 0u);
-  float km[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (k_new != nullptr && tid < 16) {
-    kw = *reinterpret_cast<const uint4*>(k_new + (int64_t)b * ksb + (int64_t)h * ksh + tid * 8);
-    const float4 m0 = *reinterpret_cast<const float4*>(mu + (int64_t)bh * kD + tid * 8);
-    const float4 m1 = *reinterpret_cast<const float4*>(mu + (int64_t)bh * kD + tid * 8 + 4);
-    km[0] = m0.x; km[1] = m0.y; km[2] = m0.z; km[3] = m0.w;
-    km[4] = m1.x; km[5] = m1.y; km[6] = m1.z; km[7] = m1.w;
+// ------------------------------------------------------------------ selection table
+// The selection query's int32 table (§2.1 item 2), built by any block of 256
+// threads of the head: thread tid makes entries 2tid and 2tid+1 (sub-vector
+// j = tid >> 3).  Every block that builds it performs the same operations in the
+// same order and gets the same bits, so a token's score is one value in every
+// kernel.  qbar_c = sum over g ascending of q_g,c (fp32); A bounds the 32-term
+// sums (sum_c |qbar_c| for the sign vertices, as a wave sum of |qbar_2l| +
+// |qbar_2l+1| over lanes l; sum_j max_p |LUT[j][p]| in j order for a
+// codebook); with A = m * 2^x, m in [0.5, 1), entries are rint(LUT * 2^(30 - x)).
+// Per lane: G 4-byte loads of q (channels 2l, 2l+1) and, with a codebook, the
+// two centres.  jmax: LDS [32] (codebook only; one extra barrier).
+struct SelQ {
+  uint32_t qw[kMaxGroup];  // packed bf16 pairs: channels 2l, 2l+1 of q_g
+  float4 c0, c1;           // codebook centres of entries 2tid, 2tid+1
+};
+template <bool kCb>
+__device__ __forceinline__ void sel_issue(SelQ& s, const uint16_t* __restrict__ q, int64_t hq0,
+                                          int G, const float* __restrict__ cb, int tid) {
+  const int lane = tid & 63;
+#pragma unroll
+  for (int g = 0; g < kMaxGroup; ++g)
+    s.qw[g] = g < G ? *reinterpret_cast<const uint32_t*>(q + (hq0 + g) * kD + 2 * lane) : 0u;
+  if constexpr (kCb) {
+    s.c0 = reinterpret_cast<const float4*>(cb)[2 * tid];
+    s.c1 = reinterpret_cast<const float4*>(cb)[2 * tid + 1];
   }
-
-  // The query, mean and sink rows are loaded first: the tables need only them
-  // and are built while the sample's loads are still in flight (loads complete
-  // in order, so a wait for q never waits for the sample).
-  const uint4 ks = *reinterpret_cast<const uint4*>(k_sink + ((int64_t)bh * kSink + (tid >> 4)) * kD +
-                                                   (tid & 15) * 8);
-  // (unconditional loads at clamped indices: a load in a branch whose value is
-  // used inside it would wait there for every load issued before it)
-  const uint16_t qraw = q[hq0 * kD + min(tid, G * kD - 1)];
-  const float mraw = mu[(int64_t)bh * kD + min(tid, kD - 1)];
-
-  // Sample rows: stratum st = i / 16 of 192 equal segments, 16 tokens centred in
-  // it (the whole candidate set when small).  Every lane loads a real row (token
-  // 64 for unused slots, never scored), so the wait counts do not depend on
-  // which lanes sample; page ids, if paged, are all loaded before any code.
-  constexpr int kPer = kSampleMax / 1024;
-  int st_t[kPer];
-  bool use[kPer];
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int i = tid + u * 1024;
-    use[u] = sample && i < m;
-    int t = kSink + i;
-    if (!full) {
-      const int st = i / kSampleRun, ns = kSampleMax / kSampleRun;
-      const int64_t seg0 = (int64_t)st * n / ns, seg1 = (int64_t)(st + 1) * n / ns;
-      t = kSink + (int)(seg0 + (seg1 - seg0 - kSampleRun) / 2) + (i - st * kSampleRun);
-    }
-    st_t[u] = use[u] ? t : kSink;
-  }
-  int64_t rows[kPer];
-  if (rm.table != nullptr) {
-    int32_t pg[kPer];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) pg[u] = rm.table[(int64_t)b * rm.pps + (st_t[u] >> rm.lg_page)];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u)
-      rows[u] = (((int64_t)pg[u] * Hkv + h) << rm.lg_page) |
-                (int64_t)(st_t[u] & ((1 << rm.lg_page) - 1));
+}
+// The rest of the table from this lane's two channels of the summed query
+// (q0 = qbar_2l, q1 = qbar_2l+1; every wave holds all 128 channels).
+template <bool kCb>
+__device__ __forceinline__ int2 sel_finish(float q0, float q1, const float4& c0, const float4& c1,
+                                           float* jmax, int tid, float* inv_out) {
+  const int lane = tid & 63;
+  // channels 4j..4j+3 of this thread's sub-vector (j = tid >> 3 <= 31) sit in
+  // lanes 2j and 2j+1 of every wave
+  const int j = tid >> 3;
+  const int src = 2 * j;
+  const float x0 = __shfl(q0, src), x1 = __shfl(q1, src);
+  const float x2 = __shfl(q0, src + 1), x3 = __shfl(q1, src + 1);
+  float v0, v1;
+  if constexpr (kCb) {
+    v0 = ((x0 * c0.x + x1 * c0.y) + x2 * c0.z) + x3 * c0.w;
+    v1 = ((x0 * c1.x + x1 * c1.y) + x2 * c1.z) + x3 * c1.w;
   } else {
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) rows[u] = ((int64_t)b * Hkv + h) * rm.capacity + st_t[u];
+    v0 = sign_entry(x0, x1, x2, x3, (2 * tid) & 15);
+    v1 = sign_entry(x0, x1, x2, x3, (2 * tid + 1) & 15);
   }
-  uint4 c[kPer];
-  float a[kPer];
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    c[u] = *reinterpret_cast<const uint4*>(codes + rows[u] * kCodeBytes);
-    a[u] = alpha[rows[u]];
-  }
-  if (tid < G * kD) qv[tid / kD][tid % kD] = __uint_as_float((uint32_t)qraw << 16);
-  if (tid < kD) mus[tid] = mraw;
-  if (has_cb && tid < kLut) cbl[tid] = cbv;
-  if (k_new != nullptr && wave == 0) {  // the whole wave runs the 16-lane shuffles
-    const RowCode rc = encode_row16(kw, km);
-    const int64_t row = rm.row(b, h, nt - 1);
-    if (tid < 16 && (tid & 3) == 0) {
-      *reinterpret_cast<uint32_t*>(codes + row * kCodeBytes + tid) = rc.word;
-      if (vrec != nullptr)
-        *reinterpret_cast<uint32_t*>(vrec + row * kVRecBytes + kVRecCode + tid) = rc.word;
-    }
-    if (tid == 0) alpha[row] = rc.alpha;
-  }
-  if (v_new != nullptr && wave == 1) {  // the whole wave runs the 4-lane shuffles
-    const VRowCode rc = quantize_vrow16(vw);
-    const uint32_t pair = rc.bits | (__shfl_down(rc.bits, 1, 16) << 16);
-    const int cg = lane;
-    uint8_t* rec = vrec + rm.row(b, h, nt - 1) * kVRecBytes;
-    if (cg < 16 && (cg & 1) == 0) *reinterpret_cast<uint32_t*>(rec + 2 * cg) = pair;
-    if (cg < 16 && (cg & 3) == 0) *reinterpret_cast<uint32_t*>(rec + kVRecSz + cg) = rc.sz;
-  }
-  __syncthreads();
-
-  // Selection query (fp32 sum, g ascending) and sum |qbar|; q_g . mu; attention
-  // tables of the G query heads.
-  if (tid < kD) {
-    float s = qv[0][tid];
-    for (int g = 1; g < G; ++g) s += qv[g][tid];
-    qv[kMaxGroup][tid] = s;
-    const float v = wave_sum(fabsf(s));
-    if (lane == 0) red_a[wave] = v;
-  } else if (wave >= 2 && wave < 2 + G) {
-    const int g = wave - 2;
-    const float d = wave_sum(fmaf(qv[g][lane], mus[lane], qv[g][lane + 64] * mus[lane + 64]));
-    if (lane == 0) att_qmu[hq0 + g] = d;
-  }
-  for (int i = tid; i < G * kLut; i += blockDim.x)
-    att_lut[hq0 * kLut + i] = has_cb ? cb_lut_entry(qv[i / kLut], cbl, i % kLut)
-                                     : lut_entry(qv[i / kLut], i % kLut);
-  // Exact logits of the sinks (full-precision keys): q_g . k_sink[r], fp32.
-  {
-    const int r = tid >> 4, c0 = (tid & 15) * 8;
-    const float x[8] = {bf16lo(ks.x), bf16hi(ks.x), bf16lo(ks.y), bf16hi(ks.y),
-                        bf16lo(ks.z), bf16hi(ks.z), bf16lo(ks.w), bf16hi(ks.w)};
-    for (int g = 0; g < G; ++g) {
-      float d = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) d = fmaf(qv[g][c0 + i], x[i], d);
-      d = row_allreduce(d, [](float a, float b) { return a + b; });  // the row's 16 lanes
-      if ((tid & 15) == 0) att_slog[(hq0 + g) * kSink + r] = d;
-    }
-  }
-  if (mode == 0) return;
-  __syncthreads();
-
-  // Selection table in fixed point.  A bounds |sum_j LUT[j][p_j]|: sum_c |qbar_c|
-  // for the sign vertices, sum_j max_p |LUT[j][p]| for a codebook.  With
-  // A = m * 2^x (m in [0.5, 1)) the scale is 2^(30 - x), so any sum of 32
-  // entries stays below 2^30 in magnitude.
-  const float lv = tid < kLut ? (has_cb ? cb_lut_entry(qv[kMaxGroup], cbl, tid)
-                                        : lut_entry(qv[kMaxGroup], tid))
-                              : 0.0f;
   float A;
-  if (has_cb) {
-    const float x = row_allreduce(fabsf(lv), [](float a, float b) { return fmaxf(a, b); });
-    if (tid < kLut && (tid & 15) == 0) jmax[tid >> 4] = x;
+  if constexpr (kCb) {
+    float mx = fmaxf(fabsf(v0), fabsf(v1));
+    mx = fmaxf(mx, __shfl_xor(mx, 1));
+    mx = fmaxf(mx, __shfl_xor(mx, 2));
+    mx = fmaxf(mx, __shfl_xor(mx, 4));
+    if ((lane & 7) == 0) jmax[j] = mx;
     __syncthreads();
     A = 0.0f;
-    for (int j = 0; j < kSub; ++j) A += jmax[j];
+    for (int jj = 0; jj < kSub; ++jj) A += jmax[jj];
   } else {
-    A = red_a[0] + red_a[1];
+    A = wave_sum(fabsf(q0) + fabsf(q1));
   }
   int ex = 0;
   if (A > 0.0f) {
     frexpf(A, &ex);
     ex = 30 - ex;
   }
-  const float inv = ldexpf(1.0f, -ex);
-  if (tid < kLut) {
-    const int v = (int)rintf(ldexpf(lv, ex));
-    itab[tid] = v;
-    sel_lut[(int64_t)bh * kLut + tid] = v;
-  }
-  if (tid == 0) sel_inv[bh] = inv;
-  if (mode == 2 || !sample) {  // +inf: nothing passes; -inf: keep all
-    if (tid == 0) {
-      tau[bh] = __uint_as_float(mode == 2 ? 0x7f800000u : 0xff800000u);
-      bin_scale[bh] = 0.0f;
-    }
-    return;
-  }
-  __syncthreads();
-  uint32_t lo = 0xffffffffu, hi = 0u;
+  *inv_out = ldexpf(1.0f, -ex);
+  return make_int2((int)rintf(ldexpf(v0, ex)), (int)rintf(ldexpf(v1, ex)));
+}
+
+// From the query words in registers (sel_issue).
+template <bool kCb>
+__device__ __forceinline__ int2 sel_build(const SelQ& s, int G, float* jmax, int tid,
+                                          float* inv_out) {
+  float q0 = bf16lo(s.qw[0]), q1 = bf16hi(s.qw[0]);
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int i = tid + u * 1024;
-    if (i < m) {
-      const float sv = selection_score(itab, inv, c[u], a[u]);
-      ssc[i] = sv;
-      lo = min(lo, score_key(sv));
-      hi = max(hi, score_key(sv));
+  for (int g = 1; g < kMaxGroup; ++g)
+    if (g < G) {
+      q0 += bf16lo(s.qw[g]);
+      q1 += bf16hi(s.qw[g]);
+    }
+  return sel_finish<kCb>(q0, q1, s.c0, s.c1, jmax, tid, inv_out);
+}
+
+// From the G query rows staged in LDS (qs: [G][64] words, channels 2l, 2l+1 in
+// word l); the same sums in the same order as sel_build.
+template <bool kCb>
+__device__ __forceinline__ int2 sel_build_lds(const uint32_t* qs, int G, const float4& c0,
+                                              const float4& c1, float* jmax, int tid,
+                                              float* inv_out) {
+  const int lane = tid & 63;
+  float q0 = bf16lo(qs[lane]), q1 = bf16hi(qs[lane]);
+  for (int g = 1; g < G; ++g) {
+    const uint32_t w = qs[g * 64 + lane];
+    q0 += bf16lo(w);
+    q1 += bf16hi(w);
+  }
+  return sel_finish<kCb>(q0, q1, c0, c1, jmax, tid, inv_out);
+}
+
+// ------------------------------------------------------------------ attention tables
+// Tables of the G query heads for the attention kernel, by one block of 256
+// threads: att_lut[g][e] = q_g(4j..4j+3) . c_e (the sign vertex or the centre e,
+// j = e >> 4), att_qmu[g] = q_g . mu, and the exact logits of the 64 sinks,
+// att_slog[g][r] = q_g . k_sink[r] (full-precision keys, §2.1 item 3), fp32.
+__device__ void attention_tables(const ScoreArgs& a, int bh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = bh / a.Hkv, h = bh - b * a.Hkv, G = a.G;
+  const int64_t hq0 = (int64_t)b * a.n_q_heads + (int64_t)h * G;
+  const float* cb = a.codebook != nullptr ? a.codebook + (int64_t)bh * kLut * 4 : nullptr;
+  // table entries 2tid, 2tid+1 (sub-vector j) of every query head
+  {
+    const int j = tid >> 3;
+    float4 c0 = make_float4(0.f, 0.f, 0.f, 0.f), c1 = c0;
+    if (cb != nullptr) {
+      c0 = reinterpret_cast<const float4*>(cb)[2 * tid];
+      c1 = reinterpret_cast<const float4*>(cb)[2 * tid + 1];
+    }
+    for (int g = 0; g < G; ++g) {
+      const uint2 w = *reinterpret_cast<const uint2*>(a.q + (hq0 + g) * kD + 4 * j);
+      const float xs[4] = {bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y)};
+      float2 v;
+      if (cb != nullptr) {
+        v.x = ((xs[0] * c0.x + xs[1] * c0.y) + xs[2] * c0.z) + xs[3] * c0.w;
+        v.y = ((xs[0] * c1.x + xs[1] * c1.y) + xs[2] * c1.z) + xs[3] * c1.w;
+      } else {
+        v.x = sign_entry(xs[0], xs[1], xs[2], xs[3], (2 * tid) & 15);
+        v.y = sign_entry(xs[0], xs[1], xs[2], xs[3], (2 * tid + 1) & 15);
+      }
+      reinterpret_cast<float2*>(a.att_lut + (hq0 + g) * kLut)[tid] = v;
     }
   }
-  block_minmax(lo, hi, mm, &lo, &hi, false);  // its barrier also publishes ssc; mm is not reused
-  float th, th_hi;
-  block_score_band(ssc, m, rank, rank_hi, key_score(lo), key_score(hi), hist, tmp, &th, &th_hi);
-  if (tid == 0) {
-    tau[bh] = th;
-    // the select kernel bins candidate scores linearly, 2048 bins from tau up
-    // to an upper estimate of the k-th score (higher scores share the top bin)
-    const float span = th_hi - th;
-    bin_scale[bh] = span > 0.0f ? 2048.0f / span : 0.0f;
+  // q_g . mu: wave w takes heads w, w + 4
+  for (int g = wave; g < G; g += 4) {
+    const float* m = a.mu + (int64_t)bh * kD;
+    const uint16_t* qg = a.q + (hq0 + g) * kD;
+    const float d = wave_sum(fmaf(__uint_as_float((uint32_t)qg[lane] << 16), m[lane],
+                                  __uint_as_float((uint32_t)qg[lane + 64] << 16) * m[lane + 64]));
+    if (lane == 0) a.att_qmu[hq0 + g] = d;
+  }
+  // sink logits: 16 lanes per sink row (8 channels each), 16 rows per pass
+  const int c0 = (tid & 15) * 8;
+  for (int r0 = 0; r0 < kSink; r0 += 16) {
+    const int r = r0 + (tid >> 4);
+    const uint4 ks = *reinterpret_cast<const uint4*>(a.k_sink + ((int64_t)bh * kSink + r) * kD + c0);
+    const float x[8] = {bf16lo(ks.x), bf16hi(ks.x), bf16lo(ks.y), bf16hi(ks.y),
+                        bf16lo(ks.z), bf16hi(ks.z), bf16lo(ks.w), bf16hi(ks.w)};
+    for (int g = 0; g < G; ++g) {
+      const uint4 qq = *reinterpret_cast<const uint4*>(a.q + (hq0 + g) * kD + c0);
+      const float y[8] = {bf16lo(qq.x), bf16hi(qq.x), bf16lo(qq.y), bf16hi(qq.y),
+                          bf16lo(qq.z), bf16hi(qq.z), bf16lo(qq.w), bf16hi(qq.w)};
+      float d = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) d = fmaf(y[i], x[i], d);
+      d = row_allreduce(d, [](float u, float v) { return u + v; });  // the row's 16 lanes
+      if ((tid & 15) == 0) a.att_slog[(hq0 + g) * kSink + r] = d;
+    }
   }
 }
 
+// Attention tables alone (a standalone sparse attention call): one block of
+// 256 threads per (b, KV head).
+__global__ __launch_bounds__(256) void tables_kernel(ScoreArgs a) {
+  attention_tables(a, blockIdx.x);
+}
+
+// The appended token (k_new, the sequence's last): code and scale with the
+// frozen mean (bit-identical to the encode kernel), value record, and its
+// selection key for the select kernel (one wave; not on the threshold's path).
+__device__ __forceinline__ void leader_append(const ScoreArgs& a, int bh, int b, int h, int nt,
+                                              const int* itab, float inv) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  // key row: lanes 0..15, 8 channels each, with their means; value row: lanes
+  // 16..31
+  uint4 kw = make_uint4(0u, 0u, 0u, 0u), vw = kw;
+  float km[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  {
+    if (lane < 16) {
+      kw = *reinterpret_cast<const uint4*>(a.k_new + (int64_t)b * a.ksb + (int64_t)h * a.ksh +
+                                           lane * 8);
+      const float4 m0 = *reinterpret_cast<const float4*>(a.mu + (int64_t)bh * kD + lane * 8);
+      const float4 m1 = *reinterpret_cast<const float4*>(a.mu + (int64_t)bh * kD + lane * 8 + 4);
+      km[0] = m0.x; km[1] = m0.y; km[2] = m0.z; km[3] = m0.w;
+      km[4] = m1.x; km[5] = m1.y; km[6] = m1.z; km[7] = m1.w;
+    } else if (lane < 32 && a.v_new != nullptr) {
+      vw = *reinterpret_cast<const uint4*>(a.v_new + (int64_t)b * a.vnsb + (int64_t)h * a.vnsh +
+                                           (lane - 16) * 8);
+    }
+  }
+  uint4 cn = make_uint4(0u, 0u, 0u, 0u);
+  float an = 0.0f;
+  {  // the whole wave runs the 16-lane shuffles
+    const RowCode rc = encode_row16(kw, km);
+    const int64_t row = a.rm.row(b, h, nt - 1);
+    if (lane < 16 && (lane & 3) == 0) {
+      *reinterpret_cast<uint32_t*>(a.codes + row * kCodeBytes + lane) = rc.word;
+      if (a.vrec != nullptr)
+        *reinterpret_cast<uint32_t*>(a.vrec + row * kVRecBytes + kVRecCode + lane) = rc.word;
+    }
+    if (lane == 0) a.alpha[row] = rc.alpha;
+    if (a.v_new != nullptr) {
+      const VRowCode vc = quantize_vrow16(vw);  // lanes 16..31 hold the value row
+      const uint32_t pair = vc.bits | (__shfl_down(vc.bits, 1, 16) << 16);
+      const int cg = lane - 16;
+      uint8_t* rec = a.vrec + row * kVRecBytes;
+      if (cg >= 0 && cg < 16 && (cg & 1) == 0) *reinterpret_cast<uint32_t*>(rec + 2 * cg) = pair;
+      if (cg >= 0 && cg < 16 && (cg & 3) == 0)
+        *reinterpret_cast<uint32_t*>(rec + kVRecSz + cg) = vc.sz;
+    }
+    cn = make_uint4((uint32_t)__builtin_amdgcn_readlane((int)rc.word, 0),
+                    (uint32_t)__builtin_amdgcn_readlane((int)rc.word, 4),
+                    (uint32_t)__builtin_amdgcn_readlane((int)rc.word, 8),
+                    (uint32_t)__builtin_amdgcn_readlane((int)rc.word, 12));
+    an = readlane(rc.alpha, 0);
+  }
+  if (lane == 0) {
+    const float sv = selection_score(itab, inv, cn, an);
+    a.app_key[bh] = score_key(sv);
+    if (a.scores_opt != nullptr) a.scores_opt[(int64_t)bh * a.rm.capacity + nt - 1] = sv;
+  }
+}
+
+// ------------------------------------------------------------------ leader
+// One block per (b, KV head), dispatched before every tile block of the score
+// kernel (lowest block indices): the selection table (kept in the workspace
+// for the select kernel's exact path) and the sampled threshold tau, published
+// to the head's tiles through the threshold word (the attention tables are made
+// by extra blocks of the select kernel, off this path).
+// Sample: stratum st = i / 16 of 128 equal segments of the head's candidates,
+// 16 contiguous tokens centred in it (the whole candidate set when it is small;
+// an appended token, the last one, is left out).  The leader also encodes an appended token (k_new) into
+// the cache and leaves its selection key for the select kernel.  Three rounds
+// of 3 sample rows per thread (4 rounds: more rows in flight would take the
+// kernel past 64 VGPRs, below eight waves per SIMD).  mode 1: sampled tau;
+// mode 2: tau = +inf (nothing passes: the select kernel takes its exact
+// whole-head path).  No sample (it would not bound the k-th): tau = -inf.
+template <bool kCb>
+__device__ void leader(const ScoreArgs& a, int bh, int* itab, uint32_t* hist, uint32_t* qs,
+                       float* ssc, float* red, float* jmax) {
+  constexpr int kRows = kSampleMax / 256;  // sample rows per thread, all in flight at once
+  static_assert(kRows * 256 == kSampleMax, "sample split");
+  __builtin_amdgcn_s_setprio(3);  // issue ahead of the tile waves sharing the CU
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int b = bh / a.Hkv, h = bh - b * a.Hkv;
+  const int nt = seq_len(a.seq_lens, b, a.n_tokens);
+  const bool append = a.k_new != nullptr;
+  const int n = nt - kSink - (append ? 1 : 0);  // candidates the sample covers
+  int rank = 1, rank_hi = 0;
+  if (a.mode == 1) sample_ranks(seq_topk(a.top_k, nt), n, &rank, &rank_hi);
+  const bool full = n <= kSampleMax;
+  const int m = full ? n : kSampleMax;
+  const bool sample = a.mode == 1 && m > 0 && rank <= m;
+  const int64_t hq0 = (int64_t)b * a.n_q_heads + (int64_t)h * a.G;
+  const float* cb = a.codebook != nullptr ? a.codebook + (int64_t)bh * kLut * 4 : nullptr;
+  for (int i = tid; i < kBandBins; i += 256) hist[i] = 0u;  // the band's counters
+  // The G query rows (8 bytes per thread) and the centres, then the sample: the
+  // table's wait does not include the sample rows, and the rows go to LDS first
+  // so that only two registers per thread hold them while the sample is in
+  // flight.
+  const uint2 qv = tid < a.G * 32
+                       ? *reinterpret_cast<const uint2*>(a.q + (hq0 + (tid >> 5)) * kD + 4 * (tid & 31))
+                       : make_uint2(0u, 0u);
+  float4 c0 = make_float4(0.f, 0.f, 0.f, 0.f), c1 = c0;
+  if constexpr (kCb) {
+    c0 = reinterpret_cast<const float4*>(cb)[2 * tid];
+    c1 = reinterpret_cast<const float4*>(cb)[2 * tid + 1];
+  }
+  // Every lane loads a real sample row (token 64 for unused slots, never
+  // scored).
+  uint4 c[kRows];
+  float al[kRows];
+  if (sample) {
+    // rows as 32-bit offsets from a uniform base: the head's first row
+    // (contiguous) or the pool's (paged: pool rows fit in 32 bits)
+    const bool paged = a.rm.table != nullptr;
+    const int64_t base = paged ? 0 : (int64_t)bh * a.rm.capacity;
+    const char* cbase = reinterpret_cast<const char*>(a.codes + base * kCodeBytes);
+    const char* abase = reinterpret_cast<const char*>(a.alpha + base);
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {
+      const int i = tid + u * 256;
+      int t = kSink + i;
+      if (!full) {
+        const int st = i / kSampleRun, ns = kSampleMax / kSampleRun;
+        const int64_t seg0 = (int64_t)st * n / ns, seg1 = (int64_t)(st + 1) * n / ns;
+        t = kSink + (int)(seg0 + (seg1 - seg0 - kSampleRun) / 2) + (i - st * kSampleRun);
+      }
+      t = i < m ? t : kSink;
+      const uint32_t r = paged ? (uint32_t)a.rm.row(b, h, t) : (uint32_t)t;
+      c[u] = *reinterpret_cast<const uint4*>(cbase + (size_t)r * kCodeBytes);
+      al[u] = *reinterpret_cast<const float*>(abase + (size_t)r * 4);
+    }
+  }
+  if (tid < a.G * 32) reinterpret_cast<uint2*>(qs)[tid] = qv;
+  __syncthreads();  // qs
+  float inv;
+  const int2 tv = sel_build_lds<kCb>(qs, a.G, c0, c1, jmax, tid, &inv);
+  reinterpret_cast<int2*>(itab)[tid] = tv;
+  reinterpret_cast<int2*>(a.sel_lut + (int64_t)bh * kLut)[tid] = tv;
+  if (tid == 0) a.sel_inv[bh] = inv;
+  __syncthreads();  // itab; every read of qs is done
+  // no sample: +inf (mode 2: nothing passes) or -inf (keep all)
+  float th = a.mode == 2 ? INFINITY : -INFINITY, th_hi = 0.0f;
+  if (sample) {
+    float smin = INFINITY, smax = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {  // each row's registers free as soon as it is scored
+      const float sv = selection_score(itab, inv, c[u], al[u]);
+      ssc[tid + u * 256] = sv;
+      if (tid + u * 256 < m) {
+        smin = fminf(smin, sv);
+        smax = fmaxf(smax, sv);
+      }
+    }
+    block_score_band<kRows>(ssc, smin, smax, m, rank, rank_hi, hist, red, &th, &th_hi);
+  }
+  if (wave == 1 && append) leader_append(a, bh, b, h, nt, itab, inv);  // beside the publication
+  if (tid == 0) {
+    // the select kernel bins candidate scores linearly, 2048 bins from tau up
+    // to an upper estimate of the k-th score (higher scores share the top bin)
+    const float span = th_hi - th;
+    a.bin_scale[bh] = sample && span > 0.0f ? 2048.0f / span : 0.0f;
+    __hip_atomic_store(a.tau_word + bh, ((unsigned long long)kTauTag << 32) | __float_as_uint(th),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// The published threshold of a head: w, lane 0's earlier load of the word,
+// if it already carries the tag, else lane 0 polls (device-scope loads, a
+// short sleep between them); after kTauPolls polls the wave gives up and
+// returns -inf (the tile then keeps every token: a correct, slower
+// selection).  Wave-uniform result.
+__device__ __forceinline__ float wait_tau(unsigned long long* word, unsigned long long w) {
+  if ((threadIdx.x & 63) == 0) {
+    for (int i = 0; i < kTauPolls && (uint32_t)(w >> 32) != kTauTag; ++i) {
+      __builtin_amdgcn_s_sleep(4);
+      w = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  const uint32_t tag = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(w >> 32));
+  const uint32_t tb = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)w);
+  return tag == kTauTag ? __uint_as_float(tb) : -INFINITY;
+}
+
 // ------------------------------------------------------------------ score
-// One block per tile of 256*U candidates (lane <-> token); wave w scores the
-// tile's w-th quarter, U groups of 64 tokens, on its own, and the four waves
-// meet once more only to place their candidates.  Small enough (<= 64 VGPRs
-// at U = 8) for eight waves per SIMD, so that a 2048-tile grid is resident at
-// once.  Each wave issues all its loads before the table barrier; they are
-// unconditional, at token indices clamped to the sequence's last token
-// (always a valid row), so the compiler counts the loads in flight exactly
-// and each group waits only for its own data.  Rows are 32-bit lane offsets
-// from a wave-uniform base row: a 64-token group lies within one page of a
-// paged cache (groups start at multiples of 64, pages at multiples of
-// >= 256), so one page id serves the group.  Candidates (score >= tau) are
-// written in token order after the last load.
-template <int U, bool kPaged, int S = (U < 8 ? U : 8)>
-__global__ __launch_bounds__(256) void score_kernel(
-    const uint8_t* __restrict__ codes, const float* __restrict__ alpha, RowMap rm,
-    int n_tokens, int Hkv, const int32_t* __restrict__ seq_lens,
-    const int* __restrict__ sel_lut, const float* __restrict__ sel_inv,
-    const float* __restrict__ tau, int n_chunks, uint32_t* __restrict__ cand_key,
-    int32_t* __restrict__ cand_t, int32_t* __restrict__ chunk_count,
-    float* __restrict__ scores_opt) {
+// Grid: B*Hkv leader blocks (above), then one block per tile of 256*U
+// candidates of a head, 1-D, head-major.  In a tile, lane <-> token; wave w
+// scores the tile's w-th quarter, U groups of 64 tokens, on its own.  Each wave
+// issues all its loads first; they are unconditional, at token indices clamped
+// to the sequence's last token (always a valid row), so the compiler counts the
+// loads in flight exactly and each group waits only for its own data.  Rows are
+// 32-bit lane offsets from a wave-uniform base row: a 64-token group lies
+// within one page of a paged cache (groups start at multiples of 64, pages at
+// multiples of >= 256), so one page id serves the group.  The block builds the
+// selection table itself (the same bits as its leader's) while the loads are
+// in flight; once its tokens are scored, each wave waits for the leader's tau
+// and the candidates (score >= tau) are written in token order, with the tau
+// the tile used.  An appended token (the sequence's last) is left to the
+// leader, which encodes and scores it; the select kernel adds it at the end of
+// the head's candidates.
+// Eight waves per SIMD (64 VGPRs) for tiles of up to 8 groups, so that the
+// 2048-tile grid at 128K tokens is resident at once; the leader path and the
+// tile path each fit, but the allocator would give the merged kernel a few more
+// without the bound (the codebook variant spills 8 bytes per lane).
+template <int U, bool kPaged, bool kCb, int S = (U < 8 ? U : 8)>
+__global__ __launch_bounds__(256, (U <= 8 ? 8 : 1)) void score_kernel(ScoreArgs a) {
   constexpr int kChunk = 256 * U;
   constexpr int NS = U / S;  // steps of S groups, all loaded before the table barrier
   static_assert(U % S == 0 && NS <= 2, "tile shape");
   __shared__ int itab[kLut];
+  __shared__ uint32_t hist[kBandBins];    // leader only
+  __shared__ uint32_t qs[kMaxGroup * 64];  // leader only: the query rows
+  __shared__ float ssc[kSampleMax];       // leader only: the sample scores
+  __shared__ float red[8];                // leader only
+  __shared__ float jmax[kSub];
   __shared__ int wcnt[4];
-  const int bh = blockIdx.y, b = bh / Hkv, h = bh - b * Hkv;
+  __shared__ uint32_t wtau[4];
+  if ((int)blockIdx.x < a.n_heads) {
+    leader<kCb>(a, blockIdx.x, itab, hist, qs, ssc, red, jmax);
+    return;
+  }
+  const int tile = blockIdx.x - a.n_heads;
+  const int bh = tile / a.n_chunks, cx = tile - bh * a.n_chunks;
+  const int b = bh / a.Hkv, h = bh - b * a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: rows from scalar bases
-  const int nt = seq_len(seq_lens, b, n_tokens);
-  const int t0 = kSink + blockIdx.x * kChunk;  // the tile's first token
-  const int tw = t0 + wave * (64 * U);         // this wave's first token
+  // tokens the tiles score: an appended token (the sequence's last) is the
+  // leader's, which writes its row in this same kernel
+  const int nt = seq_len(a.seq_lens, b, a.n_tokens) - (a.k_new != nullptr ? 1 : 0);
+  const int t0 = kSink + cx * kChunk;  // the tile's first token
+  const int tw = t0 + wave * (64 * U);  // this wave's first token
   const int lim = nt - tw;  // tokens of this wave's quarter in the sequence (<= 0: none)
-  const int2 tv = reinterpret_cast<const int2*>(sel_lut + (int64_t)bh * kLut)[tid];
-  const int64_t hrow = (int64_t)bh * rm.capacity;  // contiguous: the head's first row
+  const int64_t hq0 = (int64_t)b * a.n_q_heads + (int64_t)h * a.G;
+  const float* cb = a.codebook != nullptr ? a.codebook + (int64_t)bh * kLut * 4 : nullptr;
+  SelQ sq;
+  sel_issue<kCb>(sq, a.q, hq0, a.G, cb, tid);
+  const int64_t hrow = (int64_t)bh * a.rm.capacity;  // contiguous: the head's first row
   // Paged: the quarter's tokens (clamped to the sequence) span at most U + 1
   // pages; lane j holds the id of the j-th, read out per group with a lane read
   // (a per-group load would wait behind every code load in flight).
-  const int lg = rm.lg_page;
+  const int lg = a.rm.lg_page;
   const int pfirst = min(tw, nt - 1) >> lg;
   int pv = 0;
   if constexpr (kPaged)
-    pv = rm.table[(int64_t)b * rm.pps + min(pfirst + lane, (nt - 1) >> lg)];
+    pv = a.rm.table[(int64_t)b * a.rm.pps + min(pfirst + lane, (nt - 1) >> lg)];
   // Loads of step st.
   uint4 c[NS][S];
-  float a[NS][S];
+  float al[NS][S];
+  auto row_base = [&](int gb) {
+    if constexpr (kPaged) {
+      const int64_t pg = __builtin_amdgcn_readlane(pv, (gb >> lg) - pfirst);
+      return ((pg * a.Hkv + h) << lg) | (int64_t)(gb & ((1 << lg) - 1));
+    } else {
+      return hrow + gb;
+    }
+  };
   auto load_step = [&](int st) {
 #pragma unroll
     for (int u = 0; u < S; ++u) {
       const int g0 = tw + (st * S + u) * 64;  // first token of the group
       const int gb = min(g0, nt - 1);         // base row's token (uniform)
       const uint32_t o = (uint32_t)(min(g0 + lane, nt - 1) - gb);
-      int64_t r0;
-      if constexpr (kPaged) {
-        const int64_t pg = __builtin_amdgcn_readlane(pv, (gb >> lg) - pfirst);
-        r0 = ((pg * Hkv + h) << lg) | (int64_t)(gb & ((1 << lg) - 1));
-      } else {
-        r0 = hrow + gb;
-      }
+      const int64_t r0 = row_base(gb);
       c[st][u] = *reinterpret_cast<const uint4*>(
-          reinterpret_cast<const char*>(codes + r0 * kCodeBytes) + (o << 4));
-      a[st][u] = *reinterpret_cast<const float*>(
-          reinterpret_cast<const char*>(alpha + r0) + (o << 2));
+          reinterpret_cast<const char*>(a.codes + r0 * kCodeBytes) + (o << 4));
+      al[st][u] = *reinterpret_cast<const float*>(
+          reinterpret_cast<const char*>(a.alpha + r0) + (o << 2));
     }
   };
   load_step(0);
   if constexpr (NS > 1) load_step(1);
+  float inv;
+  const int2 tv = sel_build<kCb>(sq, a.G, jmax, tid, &inv);
   int tz;
   asm volatile("v_mov_b32 %0, 0" : "=v"(tz));  // the table is stored after the loads go out
   reinterpret_cast<int2*>(itab)[tid] = make_int2(tv.x ^ tz, tv.y ^ tz);
-  const float inv = sel_inv[bh];
-  const float th = tau[bh];
   __syncthreads();
   uint32_t key[U];
-  uint32_t bits = 0;  // bit g: token g*64 + lane of the quarter passed
   // gate: a zero from an asm placed after the table barrier (then after the
   // previous step's sums); the step's codes and scales are read through it, so
   // their decode stays behind it, in order: without it the compiler hoists
-  // most look-ups into one batch (85 VGPRs, fewer waves per SIMD).
+  // most look-ups into one batch (more VGPRs, fewer waves per SIMD).
   auto score_step = [&](int st, int gate) {
 #pragma unroll
     for (int u = 0; u < S; ++u) {
       const int g = st * S + u;
       uint4 cg = c[st][u];
       cg.x ^= gate, cg.y ^= gate, cg.z ^= gate, cg.w ^= gate;
-      const float ag = __int_as_float(__float_as_int(a[st][u]) ^ gate);
-      const float sv = selection_score(itab, inv, cg, ag);
-      key[g] = score_key(sv);
-      if (g * 64 + lane < lim && sv >= th) bits |= 1u << g;
+      const float ag = __int_as_float(__float_as_int(al[st][u]) ^ gate);
+      key[g] = score_key(selection_score(itab, inv, cg, ag));
     }
   };
+  // One device-scope load of the threshold word, issued behind the code loads
+  // (it completes after them, so no group waits for it): a tile that finishes
+  // after the leader published finds tau without a further round trip.
+  unsigned long long tw0 = 0ull;
+  if (lane == 0 && lim > 0)
+    tw0 = __hip_atomic_load(a.tau_word + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   int gate;
   asm volatile("v_mov_b32 %0, 0" : "=v"(gate));
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
     score_step(st, gate);
-    // after this step's sums (so that the next step's look-ups are not issued
-    // before them, nor this step's sums moved past the count exchange)
-    asm volatile("v_mov_b32 %0, 0" : "=v"(gate) : "v"(bits));
+    uint32_t dep = key[st * S];
+#pragma unroll
+    for (int u = 1; u < S; ++u) dep ^= key[st * S + u];
+    asm volatile("v_mov_b32 %0, 0" : "=v"(gate) : "v"(dep));
   }
+  const float th = lim > 0 ? wait_tau(a.tau_word + bh, tw0) : -INFINITY;  // nothing to keep: no wait
+  const uint32_t thk = score_key(th + 0.0f);
+  uint32_t bits = 0;  // bit g: token g*64 + lane of the quarter passed
+#pragma unroll
+  for (int g = 0; g < U; ++g)
+    if (g * 64 + lane < lim && key[g] >= thk) bits |= 1u << g;
   int cnt = 0;
 #pragma unroll
   for (int g = 0; g < U; ++g) cnt += __popcll(__ballot((bits >> g) & 1u));
-  if (lane == 0) wcnt[wave] = cnt;
+  if (lane == 0) {
+    wcnt[wave] = cnt;
+    wtau[wave] = __float_as_uint(th);
+  }
   __syncthreads();
   int run = 0;  // candidates of the waves before this one
 #pragma unroll
   for (int w = 0; w < 3; ++w) run += w < wave ? wcnt[w] : 0;
-  const int64_t slot = ((int64_t)bh * n_chunks + blockIdx.x) * kChunk;
-  uint32_t* __restrict__ kout = cand_key + slot;
-  int32_t* __restrict__ tout = cand_t + slot;
+  const int64_t slot = ((int64_t)bh * a.n_chunks + cx) * kChunk;
+  uint32_t* __restrict__ kout = a.cand_key + slot;
+  int32_t* __restrict__ tout = a.cand_t + slot;
 #pragma unroll
   for (int g = 0; g < U; ++g) {
     const bool pass = (bits >> g) & 1u;
-    const uint64_t m = __ballot(pass);
+    const uint64_t mk = __ballot(pass);
     if (pass) {
-      const int p = run + ballot_rank(m);
+      const int p = run + ballot_rank(mk);
       kout[p] = key[g];
       tout[p] = tw + g * 64 + lane;
     }
-    run += __popcll(m);
+    run += __popcll(mk);
   }
-  if (scores_opt != nullptr) {  // key_score inverts score_key exactly
-    float* __restrict__ so = scores_opt + hrow + tw;
+  if (a.scores_opt != nullptr) {  // key_score inverts score_key exactly
+    float* __restrict__ so = a.scores_opt + hrow + tw;
 #pragma unroll
     for (int g = 0; g < U; ++g)
       if (g * 64 + lane < lim) so[g * 64 + lane] = key_score(key[g]);
   }
-  if (tid == 255) chunk_count[(int64_t)bh * n_chunks + blockIdx.x] = run;  // the last wave's run ends the tile
+  if (tid == 255) {  // the last wave's run ends the tile
+    // The threshold the tile kept its tokens with: the published one if any
+    // wave saw it (-inf, a wave that gave up waiting, keeps a superset); two
+    // different real values (a stale word, then the published one) are
+    // recorded as a NaN, which sends the head to the exact path.
+    uint32_t rec = 0xff800000u;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t x = wtau[w];
+      if (x != 0xff800000u) rec = (rec == 0xff800000u || rec == x) ? x : 0x7fc00001u;
+    }
+    a.chunk_count[(int64_t)bh * a.n_chunks + cx] = make_int2(run, (int)rec);
+  }
 }
 
 // Histogram count of one key per lane (valid lanes only).  Keys above the band
@@ -784,11 +997,12 @@ __device__ __noinline__ void select_exact_head(
 }
 
 // More candidates than the LDS list holds: the ordered list goes to the
-// workspace (tile by tile, wave w taking tiles w, w + 16, ...) and radix rounds
-// select over it.
-__device__ __noinline__ void select_workspace(
+// workspace (tile by tile, wave w taking tiles w, w + 16, ...; an appended
+// token last) and radix rounds select over it.
+__device__ __noinline__ bool select_workspace(
     const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_t, int chunk,
-    int n_chunks, const int* off, int C, int top_k, uint32_t* __restrict__ comp_key,
+    int n_chunks, const int* off, int C, int top_k, bool extra, uint32_t extra_key,
+    int32_t extra_pos, uint32_t thk, uint32_t* __restrict__ comp_key,
     int32_t* __restrict__ comp_t, uint32_t* hist, int* tmp, uint32_t* sub, int* scount,
     uint32_t* mm, int32_t* __restrict__ out) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
@@ -804,9 +1018,17 @@ __device__ __noinline__ void select_workspace(
       hi = max(hi, key);
     }
   }
+  if (extra && threadIdx.x == 0) {  // the appended token, last in the list
+    comp_key[C - 1] = extra_key;
+    comp_t[C - 1] = extra_pos;
+    lo = min(lo, extra_key);
+    hi = max(hi, extra_key);
+  }
   block_minmax(lo, hi, mm, &lo, &hi);  // its barriers also publish the copies
   const Kth r = block_kth(comp_key, C, top_k, lo, hi, hist, tmp, sub, scount);
+  if (r.key < thk) return false;  // below the threshold: not provably the k-th
   block_emit(comp_key, comp_t, C, top_k, r, out, tmp);
+  return true;
 }
 
 // The k-th's bin holds too many keys (e.g. no usable bin scale): radix rounds
@@ -829,25 +1051,34 @@ __global__ __launch_bounds__(1024) void select_kernel(
     const int* __restrict__ sel_lut, const float* __restrict__ sel_inv, int top_k_max,
     int chunk, int n_chunks,
     const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_t,
-    const int32_t* __restrict__ chunk_count, const float* __restrict__ tau,
-    const float* __restrict__ bin_scale, uint32_t* __restrict__ comp_key,
-    int32_t* __restrict__ comp_t, int32_t* __restrict__ idx) {
+    const int2* __restrict__ chunk_count, unsigned long long* __restrict__ tau_word,
+    const float* __restrict__ bin_scale, const uint32_t* __restrict__ app_key,
+    uint32_t* __restrict__ comp_key, int32_t* __restrict__ comp_t, int32_t* __restrict__ idx,
+    ScoreArgs ta) {
   __shared__ int off[kMaxChunks + 1];
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t lkey[kSelectLds];
-  __shared__ int32_t lpos[kSelectLds];
+  __shared__ uint16_t lofs[kSelectLds];
   __shared__ uint32_t sub[2 * kSubMax];  // boundary-bin keys, then block_kth's own sub-list
   __shared__ int tmp[32];
   __shared__ uint32_t mm[32];
   __shared__ int scount;
+  if ((int)blockIdx.x >= ta.n_heads) {  // the second half of the grid: attention tables
+    if (threadIdx.x < 256) attention_tables(ta, blockIdx.x - ta.n_heads);
+    return;
+  }
   const int bh = blockIdx.x;
   const int tid = threadIdx.x;
   const int nt = seq_len(seq_lens, bh / Hkv, n_tokens);
   const int n = nt - kSink;
   const int top_k = seq_topk(top_k_max, nt);  // this sequence's k; the rest of its row is -1
+  // The threshold the head's leader published (read here by every thread, then
+  // cleared below for the next call).
+  const uint32_t thb = (uint32_t)tau_word[bh];
   int32_t* out = idx + (int64_t)bh * top_k_max;
   for (int j = top_k + tid; j < top_k_max; j += blockDim.x) out[j] = -1;
   if (top_k >= n) {  // every candidate is kept
+    if (tid == 0) tau_word[bh] = 0ull;  // no thread of this branch reads it
     for (int j = tid; j < top_k; j += blockDim.x) out[j] = kSink + j;
     return;
   }
@@ -861,13 +1092,14 @@ __global__ __launch_bounds__(1024) void select_kernel(
   const int64_t cbase = (int64_t)bh * n_chunks * chunk;
   uint32_t pk[4][4];
   int32_t pt[4][4];
+  int any_bad;
   {
     const int per = (n_chunks + blockDim.x - 1) / blockDim.x;  // <= 2
     const int c0 = tid * per;
-    int cs[2];
+    int2 cu[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      cs[j] = chunk_count[(int64_t)bh * n_chunks + min(c0 + j, n_chunks - 1)];
+      cu[j] = chunk_count[(int64_t)bh * n_chunks + min(c0 + j, n_chunks - 1)];
     {
       const int lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
 #pragma unroll
@@ -880,9 +1112,17 @@ __global__ __launch_bounds__(1024) void select_kernel(
         }
       }
     }
+    // A tile that kept its tokens with another threshold than the published one
+    // (not -inf, the tile's own fallback, which keeps every token) may have
+    // dropped some of the top k: the head then takes the exact path.
+    int cs[2];
+    bool bad = false;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      if (!(j < per && c0 + j < n_chunks)) cs[j] = 0;
+    for (int j = 0; j < 2; ++j) {
+      const bool real = j < per && c0 + j < n_chunks;
+      cs[j] = real ? cu[j].x : 0;
+      bad |= real && (uint32_t)cu[j].y != thb && (uint32_t)cu[j].y != 0xff800000u;
+    }
     int total;
     int pre = block_excl_scan(cs[0] + cs[1], tmp, &total);
 #pragma unroll
@@ -892,11 +1132,17 @@ __global__ __launch_bounds__(1024) void select_kernel(
         pre += cs[j];
       }
     if (tid == 0) off[n_chunks] = total;
-    __syncthreads();
+    any_bad = __syncthreads_or(bad);
   }
-  const int C = off[n_chunks];
-  uint32_t lo = 0xffffffffu, hi = 0u;
-  if (C < top_k) {  // the LDS list is unused: it holds the table
+  if (tid == 0) tau_word[bh] = 0ull;  // every thread read it before the barrier
+  // An appended token (scored by the leader; the tiles stop before it) is the
+  // head's last position: it follows every tile's candidates in the list.
+  const int Ct = off[n_chunks];
+  const uint32_t thk = score_key(__uint_as_float(thb) + 0.0f);
+  const uint32_t akey = app_key != nullptr ? app_key[bh] : 0u;
+  const bool ap = app_key != nullptr && akey >= thk;
+  const int C = Ct + (ap ? 1 : 0);
+  if (C < top_k || any_bad) {  // the LDS list is unused: it holds the table
     select_exact_head(codes, alpha, rm, Hkv, bh, n, top_k, sel_lut, sel_inv, comp_key + cbase,
                       comp_t + cbase, reinterpret_cast<int*>(lkey), hist, tmp, sub, &scount, mm,
                       out);
@@ -905,20 +1151,16 @@ __global__ __launch_bounds__(1024) void select_kernel(
   // Gather the candidates into one ordered list.  Wave w copies tiles w, w+nw,
   // ...; the first 256 candidates of 4 tiles are loaded before any is stored.
   // Kept in LDS, each candidate's score is also counted in a 2048-bin linear
-  // histogram from tau up (bin width set by the prep kernel from its sample).
+  // histogram from tau up (bin width set by the leader from its sample).
   const bool in_lds = C <= kSelectLds;
-  const float th = tau[bh], bsc = bin_scale[bh];
+  const float th = __uint_as_float(thb), bsc = bin_scale[bh];
   auto bin_of = [th, bsc](uint32_t key) {
     const float z = (key_score(key) - th) * bsc;  // NaN (no scale) -> bin 0
     return z >= 2047.0f ? 2047 : (z > 0.0f ? (int)z : 0);
   };
-  // Two instances, so that the LDS list is written with LDS stores (a pointer
-  // that may address either memory would make every store a flat one, which
-  // waits on both memory counters).
-  auto gather = [&](auto lds_tag) {
-    constexpr bool kLds = decltype(lds_tag)::value;
-    uint32_t* __restrict__ dk = kLds ? lkey : comp_key + cbase;
-    int32_t* __restrict__ dp = kLds ? lpos : comp_t + cbase;
+  // The list in LDS: each tile's candidates at its offset, positions as offsets
+  // within the tile.
+  auto gather = [&]() {
     const int lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
     for (int c0 = wave; c0 < n_chunks; c0 += 4 * nw) {
       uint32_t kk[4][4];
@@ -952,41 +1194,45 @@ __global__ __launch_bounds__(1024) void select_kernel(
         if (ci >= n_chunks) continue;
         const int o = off[ci], cnt = off[ci + 1] - o;
         const int64_t src = cbase + (int64_t)ci * chunk;
+        const int tb = kSink + ci * chunk;  // the tile's first token
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int j = lane + 64 * u;
           if (j < cnt) {
-            dk[o + j] = kk[v][u];
-            dp[o + j] = tt[v][u];
-            if constexpr (!kLds) {  // the LDS list takes its range only when needed
-              lo = min(lo, kk[v][u]);
-              hi = max(hi, kk[v][u]);
-            }
+            lkey[o + j] = kk[v][u];
+            lofs[o + j] = (uint16_t)(tt[v][u] - tb);
           }
-          if constexpr (kLds) count_bin(hist, j < cnt, bin_of(kk[v][u]));
+          count_bin(hist, j < cnt, bin_of(kk[v][u]));
         }
         for (int j0 = 256; j0 < cnt; j0 += 64) {  // tiles with many candidates
           const int j = j0 + lane;
           const uint32_t key = j < cnt ? cand_key[src + j] : 0u;
           if (j < cnt) {
-            dk[o + j] = key;
-            dp[o + j] = cand_t[src + j];
-            if constexpr (!kLds) {
-              lo = min(lo, key);
-              hi = max(hi, key);
-            }
+            lkey[o + j] = key;
+            lofs[o + j] = (uint16_t)(cand_t[src + j] - tb);
           }
-          if constexpr (kLds) count_bin(hist, j < cnt, bin_of(key));
+          count_bin(hist, j < cnt, bin_of(key));
         }
       }
     }
   };
   if (!in_lds) {
-    select_workspace(cand_key + cbase, cand_t + cbase, chunk, n_chunks, off, C, top_k,
-                     comp_key + cbase, comp_t + cbase, hist, tmp, sub, &scount, mm, out);
+    if (!select_workspace(cand_key + cbase, cand_t + cbase, chunk, n_chunks, off, C, top_k, ap,
+                          akey, nt - 1, thk, comp_key + cbase, comp_t + cbase, hist, tmp, sub,
+                          &scount, mm, out)) {
+      __syncthreads();
+      select_exact_head(codes, alpha, rm, Hkv, bh, n, top_k, sel_lut, sel_inv, comp_key + cbase,
+                        comp_t + cbase, reinterpret_cast<int*>(lkey), hist, tmp, sub, &scount,
+                        mm, out);
+    }
     return;
   }
-  gather(std::true_type{});
+  gather();
+  if (ap && tid == 0) {  // its position comes from the emit (past the tiles)
+    lkey[Ct] = akey;
+    lofs[Ct] = 0;
+    count_bin(hist, true, bin_of(akey));
+  }
   if (in_lds) {
     __syncthreads();  // publishes the list and the histogram
     // Each thread's run of the list goes to registers while the histogram is
@@ -994,7 +1240,7 @@ __global__ __launch_bounds__(1024) void select_kernel(
     // a few dozen) go to a sub-list resolved by one wave, or by radix rounds if
     // more than 64.
     Run rn;
-    run_load(rn, lkey, lpos, C);
+    run_load(rn, lkey, lofs, C, off, n_chunks, chunk, nt - 1);
     const Round rb = hist_pick(hist, 2048, top_k, tmp, C);
     Kth r;
     if (rb.count <= kSubMax) {
@@ -1059,40 +1305,37 @@ __global__ __launch_bounds__(1024) void select_kernel(
     } else {  // degenerate spread (e.g. no usable bin scale): radix over the whole list
       r = select_degenerate(lkey, C, top_k, hist, tmp, sub, &scount, mm);
     }
+    // The list holds every token at or above the published threshold (tiles
+    // that gave up waiting kept more); its k-th is the head's k-th only if it
+    // is not below that threshold (else some of the top k may be missing).
+    if (r.key < thk) {
+      __syncthreads();  // the LDS list is reused by the exact path
+      select_exact_head(codes, alpha, rm, Hkv, bh, n, top_k, sel_lut, sel_inv, comp_key + cbase,
+                        comp_t + cbase, reinterpret_cast<int*>(lkey), hist, tmp, sub, &scount,
+                        mm, out);
+      return;
+    }
     run_emit(rn, top_k, r, lkey, out, tmp);
   }
 }
 
 }  // namespace
 
-hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const float* mu,
-                       uint8_t* codes, float* alpha, const RowMap& rm, int n_tokens,
-                       const uint16_t* k_sink, const uint16_t* k_new, int64_t ksb, int64_t ksh,
-                       const uint16_t* v_new, int64_t vnsb, int64_t vnsh, uint8_t* vrec,
-                       const float* codebook, int top_k, int mode, int* sel_lut,
-                       float* sel_inv, float* att_lut, float* att_qmu, float* att_slog,
-                       float* tau, float* bin_scale, const int32_t* seq_lens, const Launch& s) {
-  return launch_k(KID_PREP, prep_kernel, dim3(B * Hkv), dim3(1024), 0, s, q, n_q_heads, Hkv,
-                  n_q_heads / Hkv, mu, codes, alpha, rm, n_tokens, k_sink, k_new, ksb, ksh,
-                  v_new, vnsb, vnsh, vrec, codebook, top_k, mode, seq_lens, sel_lut, sel_inv,
-                  att_lut, att_qmu, att_slog, tau, bin_scale);
+hipError_t launch_tables(const ScoreArgs& a, const Launch& s) {
+  return launch_k(KID_TABLES, tables_kernel, dim3(a.n_heads), dim3(256), 0, s, a);
 }
 
-hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha, const RowMap& rm,
-                        int n_tokens, const int32_t* seq_lens, const int* sel_lut,
-                        const float* sel_inv, const float* tau, int chunk,
-                        int n_chunks, uint32_t* cand_key, int32_t* cand_t, int32_t* chunk_count,
-                        float* scores_opt, const Launch& s) {
-  const dim3 grid(n_chunks, B * Hkv), block(256);
-#define SIKV_SCORE_CASE(UU)                                                                    \
-  case 256 * UU:                                                                               \
-    return rm.table != nullptr                                                                 \
-               ? launch_k(KID_SCORE, score_kernel<UU, true>, grid, block, 0, s, codes, alpha,  \
-                          rm, n_tokens, Hkv, seq_lens, sel_lut, sel_inv, tau, n_chunks,        \
-                          cand_key, cand_t, chunk_count, scores_opt)                           \
-               : launch_k(KID_SCORE, score_kernel<UU, false>, grid, block, 0, s, codes, alpha, \
-                          rm, n_tokens, Hkv, seq_lens, sel_lut, sel_inv, tau, n_chunks,        \
-                          cand_key, cand_t, chunk_count, scores_opt);
+hipError_t launch_score(const ScoreArgs& a, int chunk, const Launch& s) {
+  const dim3 grid((unsigned)a.n_heads * (unsigned)(a.n_chunks + 1)), block(256);
+#define SIKV_SCORE_CASE(UU)                                                                 \
+  case 256 * UU:                                                                            \
+    if (a.codebook != nullptr)                                                              \
+      return a.rm.table != nullptr                                                          \
+                 ? launch_k(KID_SCORE, score_kernel<UU, true, true>, grid, block, 0, s, a)  \
+                 : launch_k(KID_SCORE, score_kernel<UU, false, true>, grid, block, 0, s, a); \
+    return a.rm.table != nullptr                                                            \
+               ? launch_k(KID_SCORE, score_kernel<UU, true, false>, grid, block, 0, s, a)   \
+               : launch_k(KID_SCORE, score_kernel<UU, false, false>, grid, block, 0, s, a);
   switch (chunk) {
     SIKV_SCORE_CASE(1)
     SIKV_SCORE_CASE(2)
@@ -1108,14 +1351,15 @@ hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha
 hipError_t launch_select(int B, int Hkv, const uint8_t* codes, const float* alpha, const RowMap& rm,
                          int n_tokens, const int32_t* seq_lens, const int* sel_lut,
                          const float* sel_inv, int top_k, int chunk, int n_chunks,
-                         uint32_t* cand_key, int32_t* cand_t, const int32_t* chunk_count,
-                         const float* tau, const float* bin_scale, uint32_t* comp_key,
-                         int32_t* comp_t, int32_t* idx, const Launch& s) {
+                         uint32_t* cand_key, int32_t* cand_t, const int2* chunk_count,
+                         unsigned long long* tau_word, const float* bin_scale,
+                         const uint32_t* app_key, uint32_t* comp_key, int32_t* comp_t,
+                         int32_t* idx, const ScoreArgs& ta, const Launch& s) {
   if (n_chunks > kMaxChunks) return hipErrorInvalidValue;
-  return launch_k(KID_SELECT, select_kernel, dim3(B * Hkv), dim3(1024), 0, s, codes, alpha,
+  return launch_k(KID_SELECT, select_kernel, dim3(2 * B * Hkv), dim3(1024), 0, s, codes, alpha,
                   rm, n_tokens, Hkv, seq_lens, sel_lut, sel_inv, top_k, chunk, n_chunks,
                   cand_key, cand_t,
-                  chunk_count, tau, bin_scale, comp_key, comp_t, idx);
+                  chunk_count, tau_word, bin_scale, app_key, comp_key, comp_t, idx, ta);
 }
 
 }  // namespace sikv

@@ -43,7 +43,7 @@ enum KernelId {
   KID_MU_PARTIAL = 0,
   KID_MU_FINAL,
   KID_CODES,
-  KID_PREP,
+  KID_TABLES,
   KID_SCORE,
   KID_SELECT,
   KID_ATTN,
@@ -174,14 +174,16 @@ __device__ __forceinline__ float key_score(uint32_t k) {
 // Look-up table of one query vector x (LDS, 128 floats): lut[j*16 + p] =
 // ((+-x0 +- x1) +- x2) +- x3 with x_i = x[4j+i], negative iff bit i of p is set
 // (§2.1 item 2: a query piece dotted with the 16 sign vertices).  No barrier.
-__device__ __forceinline__ float lut_entry(const float* x, int e) {
-  const int j = e >> 4, p = e & 15;
-  const float x0 = x[4 * j], x1 = x[4 * j + 1], x2 = x[4 * j + 2], x3 = x[4 * j + 3];
+__device__ __forceinline__ float sign_entry(float x0, float x1, float x2, float x3, int p) {
   float v = (p & 1) ? -x0 : x0;
   v += (p & 2) ? -x1 : x1;
   v += (p & 4) ? -x2 : x2;
   v += (p & 8) ? -x3 : x3;
   return v;
+}
+__device__ __forceinline__ float lut_entry(const float* x, int e) {
+  const int j = e >> 4;
+  return sign_entry(x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3], e & 15);
 }
 
 // Table entry with data-derived centres: lut[j*16 + p] = x(4j..4j+3) . cb[j*16 + p]
@@ -357,38 +359,73 @@ hipError_t launch_kmeans_assign(const uint16_t* k, int64_t sb, int64_t sh, int64
                                 const float* alpha, const float* centres, long long* cb_part,
                                 const Launch& s);
 
-// score.hip.  seq_lens (may be null): per-sequence lengths of a ragged batch
-// (seq_len / seq_topk above); n_tokens is then the longest, which sizes grids.
-// mode 0: attention tables only; 1: all tables + sampled threshold; 2: all
-// tables + a threshold that forces the exact whole-head selection.
-// Every mode also writes the attention tables of the query heads: att_lut
-// [B*Hq][512], att_qmu [B*Hq] (q_g . mu) and att_slog [B*Hq][64] (exact sink
-// logits q_g . k_sink[r]).
-// codebook (may be null): the KV heads' centres [B*Hkv][32][16][4] (else the
-// sign vertices).  k_new (may be null): bf16 key of token n_tokens-1, element (b,h,c) at
-// k_new[b*ksb + h*ksh + c]; the kernel first encodes it into codes / alpha
-// (append with the frozen mean, bit-identical to launch_codes) and leaves that
-// token out of its sample.  v_new (may be null): that token's bf16 value row,
-// quantised into its value record (launch_vcodes layout; the key code copy too).  bin_scale [B*Hkv]: width of the select kernel's
-// score bins (2048 bins from tau to the sample maximum; 0 when not sampled).
-hipError_t launch_prep(const uint16_t* q, int n_q_heads, int B, int Hkv, const float* mu,
-                       uint8_t* codes, float* alpha, const RowMap& rm, int n_tokens,
-                       const uint16_t* k_sink, const uint16_t* k_new, int64_t ksb, int64_t ksh,
-                       const uint16_t* v_new, int64_t vnsb, int64_t vnsh, uint8_t* vrec,
-                       const float* codebook, int top_k, int mode, int* sel_lut,
-                       float* sel_inv, float* att_lut, float* att_qmu, float* att_slog,
-                       float* tau, float* bin_scale, const int32_t* seq_lens, const Launch& s);
-hipError_t launch_score(int B, int Hkv, const uint8_t* codes, const float* alpha, const RowMap& rm,
-                        int n_tokens, const int32_t* seq_lens, const int* sel_lut,
-                        const float* sel_inv, const float* tau, int chunk,
-                        int n_chunks, uint32_t* cand_key, int32_t* cand_t, int32_t* chunk_count,
-                        float* scores_opt, const Launch& s);
+// score.hip
+// The retrieval of one decode step (§2.1 item 2), per (b, KV head): one score
+// kernel launch whose first n_heads blocks are the heads' leaders (selection
+// table, sampled threshold) and whose other blocks score 256*U-token tiles
+// (U = chunk / 256) and keep the tokens at or above the threshold; then the
+// select kernel (exact top-k, ascending positions), whose second n_heads
+// blocks make the attention tables (ta: q, mu, k_sink, codebook, att_*).
+// seq_lens (may be null): per-sequence lengths of a ragged batch (seq_len /
+// seq_topk above); n_tokens is then the longest, which sizes grids.  mode 1:
+// sampled threshold; 2: a threshold that forces the select kernel's exact
+// whole-head path.  codebook (may be null): the KV heads' centres
+// [B*Hkv][32][16][4] (else the sign vertices).  k_new (may be null): bf16 key of
+// each sequence's last token (element (b,h,c) at k_new[b*ksb + h*ksh + c]),
+// encoded into codes / alpha by the score kernel with the frozen mean
+// (bit-identical to launch_codes) and left out of the sample; v_new (may be
+// null): that token's bf16 value row, quantised into its value record.  The
+// attention tables: att_lut [B*Hq][512], att_qmu [B*Hq] (q_g . mu), att_slog
+// [B*Hq][64] (exact sink logits q_g . k_sink[r]).
+// Everything the score kernel's two kinds of blocks read and write (the
+// kernel takes it by value).
+struct ScoreArgs {
+  int n_heads;  // B * Hkv: the score kernel's first n_heads blocks are the leaders
+  // cache
+  uint8_t* codes;
+  float* alpha;
+  RowMap rm;
+  int n_tokens, Hkv;
+  const int32_t* seq_lens;
+  const float* mu;
+  const uint16_t* k_sink;
+  const float* codebook;  // [B*Hkv][32][16][4] or null (sign vertices)
+  uint8_t* vrec;          // value records or null
+  // query and selection
+  const uint16_t* q;
+  int n_q_heads, G, top_k, mode;
+  // appended token (k_new null: none)
+  const uint16_t* k_new;
+  int64_t ksb, ksh;
+  const uint16_t* v_new;
+  int64_t vnsb, vnsh;
+  // workspace
+  unsigned long long* tau_word;  // [B*Hkv]: published threshold (tag << 32 | tau bits)
+  float* bin_scale;              // [B*Hkv]
+  int* sel_lut;                  // [B*Hkv][512]
+  float* sel_inv;                // [B*Hkv]
+  float* att_lut;                // [B*Hq][512]
+  float* att_qmu;                // [B*Hq]
+  float* att_slog;               // [B*Hq][64]
+  uint32_t* app_key;             // [B*Hkv]: an appended token's selection key
+  int n_chunks;
+  uint32_t* cand_key;
+  int32_t* cand_t;
+  int2* chunk_count;             // [B*Hkv][n_chunks]: (candidates, tau bits the tile used)
+  float* scores_opt;
+};
+
+hipError_t launch_score(const ScoreArgs& a, int chunk, const Launch& s);
+// The attention tables alone, one block per head (mode, k_new and the
+// selection outputs unused).
+hipError_t launch_tables(const ScoreArgs& a, const Launch& s);
 hipError_t launch_select(int B, int Hkv, const uint8_t* codes, const float* alpha, const RowMap& rm,
                          int n_tokens, const int32_t* seq_lens, const int* sel_lut,
                          const float* sel_inv, int top_k, int chunk, int n_chunks,
-                         uint32_t* cand_key, int32_t* cand_t, const int32_t* chunk_count,
-                         const float* tau, const float* bin_scale, uint32_t* comp_key,
-                         int32_t* comp_t, int32_t* idx, const Launch& s);
+                         uint32_t* cand_key, int32_t* cand_t, const int2* chunk_count,
+                         unsigned long long* tau_word, const float* bin_scale,
+                         const uint32_t* app_key, uint32_t* comp_key, int32_t* comp_t,
+                         int32_t* idx, const ScoreArgs& ta, const Launch& s);
 
 // attn.hip
 // Attended entries are processed in chunks of kAttnChunk; a block takes

@@ -369,10 +369,11 @@ def test_caller_owned_timer():
         o2 = sk.sikv_decode_step(plain, q, w.top_k, SM)
     torch.cuda.synchronize()
     r1, r2 = t1.read(), t2.read()
-    for name in ("prep", "score", "select", "attn", "combine"):
+    for name in ("score", "select", "attn", "combine"):
         assert r1[name][0] == 3 and r1[name][1] > 0.0, (name, r1[name])
     assert all(n == 0 for n, _ in r2.values())
     assert r1["codes"][0] == 0          # the prefill ran before the timer was attached
+    assert r1["tables"][0] == 0         # the decode step's score kernel builds the tables
     assert torch.equal(o1, o2)
     t1.reset()
     assert all(n == 0 for n, _ in t1.read().values())
