@@ -75,6 +75,10 @@ def parse():
     p.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON"),
                    help="turn FETCH_SIZE and WRITE_SIZE counter runs into HBM bytes per launch "
                         "and exit")
+    p.add_argument("--summarize-counters", nargs="+", metavar="PATH",
+                   help="OUT_JSON, then the directories of rocprofv3 --pmc runs of one command: "
+                        "every counter per dispatch of each library kernel, with derived "
+                        "ratios; then exit")
     p.add_argument("--profile-command", default="", help="command recorded in a summary")
     return p.parse_args()
 
@@ -177,6 +181,84 @@ def summarize_trace(run_dir: str, out_txt: str, command: str) -> None:
         lines.append(f"{short_kernel_name(name)[:33]:<34}{calls:>7}{tot:>12.1f}{avg:>10.2f}{pct:>7.2f}")
     open(out_txt, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def _counters_per_kernel(run_dir: str):
+    """Every counter of a --pmc run: {kernel: {counter: (dispatches, mean per
+    dispatch)}}, over the dispatches with the kernel's most frequent grid size."""
+    import collections
+    import csv
+    import glob
+    f = sorted(glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True))[0]
+    acc = collections.defaultdict(lambda: collections.defaultdict(lambda: collections.defaultdict(list)))
+    for r in csv.DictReader(open(f)):
+        k = library_kernel(r["Kernel_Name"])
+        if k is not None:
+            acc[k][r["Counter_Name"]][int(r["Grid_Size"])].append(float(r["Counter_Value"]))
+    out = collections.defaultdict(dict)
+    for k, by_counter in acc.items():
+        for c, by_grid in by_counter.items():
+            vals = max(by_grid.values(), key=len)
+            out[k][c] = (len(vals), sum(vals) / len(vals))
+    return out
+
+
+# Derived ratios (counters are summed over the chip's 8 XCDs and their shader
+# engines; 1024 SIMDs in 256 CUs).
+COUNTER_RATIOS = {
+    "gpu_cycles": ("GRBM_GUI_ACTIVE / 8", lambda c: c["GRBM_GUI_ACTIVE"] / 8),
+    "valu_insts_per_wave": ("SQ_INSTS_VALU / SQ_WAVES", lambda c: c["SQ_INSTS_VALU"] / c["SQ_WAVES"]),
+    "lds_insts_per_wave": ("SQ_INSTS_LDS / SQ_WAVES", lambda c: c["SQ_INSTS_LDS"] / c["SQ_WAVES"]),
+    "valu_issue_util": ("4 * SQ_INSTS_VALU / (1024 * GRBM_GUI_ACTIVE / 8): share of the SIMDs' "
+                        "cycles issuing VALU (4 cycles per wave64 instruction)",
+                        lambda c: 4 * c["SQ_INSTS_VALU"] / (1024 * c["GRBM_GUI_ACTIVE"] / 8)),
+    "lds_busy_frac": ("SQ_LDS_IDX_ACTIVE / (256 * GRBM_GUI_ACTIVE / 8): share of the CUs' "
+                      "cycles with the LDS busy on indexed access",
+                      lambda c: c["SQ_LDS_IDX_ACTIVE"] / (256 * c["GRBM_GUI_ACTIVE"] / 8)),
+    "lds_bank_conflict_frac": ("SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE: share of the LDS's "
+                               "indexed-access cycles stalled by bank conflicts",
+                               lambda c: c["SQ_LDS_BANK_CONFLICT"] / c["SQ_LDS_IDX_ACTIVE"]),
+    "wait_issue_frac": ("SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES: share of wave time waiting for an "
+                        "instruction's inputs",
+                        lambda c: c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"]),
+    "valu_active_frac": ("SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES",
+                         lambda c: c["SQ_ACTIVE_INST_VALU"] / c["SQ_WAVE_CYCLES"]),
+    "lds_active_frac": ("SQ_ACTIVE_INST_LDS / SQ_WAVE_CYCLES",
+                        lambda c: c["SQ_ACTIVE_INST_LDS"] / c["SQ_WAVE_CYCLES"]),
+    "tcc_hit_rate": ("TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum)",
+                     lambda c: c["TCC_HIT_sum"] / (c["TCC_HIT_sum"] + c["TCC_MISS_sum"])),
+    "l2_read_req_bytes": ("32 * TCC_EA0_RDREQ_32B_sum + 64 * TCC_EA0_RDREQ_64B_sum + 128 * "
+                          "TCC_EA0_RDREQ_128B_sum: bytes the L2 requested from memory, by size",
+                          lambda c: 32 * c["TCC_EA0_RDREQ_32B_sum"] + 64 * c["TCC_EA0_RDREQ_64B_sum"]
+                          + 128 * c["TCC_EA0_RDREQ_128B_sum"]),
+}
+
+
+def summarize_counters(out_json: str, run_dirs, command: str) -> None:
+    """Counters of several --pmc runs of the same command, merged per kernel
+    (a counter taken in more than one run keeps its first run's value), with
+    the ratios above wherever their inputs were taken."""
+    merged = {}
+    for d in run_dirs:
+        for k, cs in _counters_per_kernel(d).items():
+            ent = merged.setdefault(k, {})
+            for c, (n, v) in cs.items():
+                ent.setdefault(c, {"dispatches": n, "per_dispatch": v, "run": os.path.basename(d)})
+    out = {"command": command, "runs": [os.path.basename(d) for d in run_dirs],
+           "ratios": {r: f for r, (f, _) in COUNTER_RATIOS.items()}, "kernels": {}}
+    for k in sorted(merged):
+        vals = {c: e["per_dispatch"] for c, e in merged[k].items()}
+        ratios = {}
+        for r, (_, fn) in COUNTER_RATIOS.items():
+            try:
+                ratios[r] = fn(vals)
+            except (KeyError, ZeroDivisionError):
+                pass
+        out["kernels"][k] = {"counters": merged[k], "derived": ratios,
+                             "sources": KERNEL_SOURCES[k],
+                             "source_hash": source_hash(KERNEL_SOURCES[k])}
+    json.dump(out, open(out_json, "w"), indent=1)
+    print(json.dumps({k: v["derived"] for k, v in out["kernels"].items()}, indent=1))
 
 
 def _counter_per_kernel(run_dir: str, counter: str):
@@ -397,6 +479,10 @@ def main():
         return
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, args.profile_command)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1:],
+                           args.profile_command)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

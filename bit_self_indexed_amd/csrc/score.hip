@@ -263,76 +263,64 @@ __device__ void block_emit(const uint32_t* keys, const int32_t* pos, int n, int 
   }
 }
 
-// The select kernel's LDS list (n <= kSelectLds entries: keys, and positions
-// as 16-bit offsets within their tile) cut into one run per thread, held in
-// registers: an odd run length, so that the runs' strided LDS reads of the keys
-// never share a bank.
+// Emit from the select kernel's LDS list (n <= kSelectLds entries: keys, and
+// positions as 16-bit offsets within their tile): the positions of the
+// selected keys (all keys > kth, then the first `need` keys == kth in list
+// order) in list order (= ascending position).  Each thread owns a contiguous
+// run of the list, of odd length so that the runs' strided LDS reads never
+// share a bank; it reads its run's keys and offsets into registers in one
+// batch and counts them; the counts are scanned (after which no thread reads
+// the list), every thread writes its taken positions into the list's storage
+// (stage), and the block copies them out in order, consecutive threads storing
+// consecutive words (scattered per-thread stores would cost one memory request
+// per lane).  A position is its tile's first token (64 + tile * chunk; the
+// tile of list entry i is the last one whose list offset off[tile] <= i) plus
+// the offset; entries past the tiles (an appended token) take last_pos.  The
+// tile of the run's first entry comes from a binary search of off[], then only
+// crossings read it again.
 constexpr int kEmitRun = 21;  // longest run: odd and >= kSelectLds / 1024
 static_assert(kEmitRun >= ((kSelectLds / 1024) | 1), "runs of a 1024-thread block");
-struct Run {
-  uint32_t key[kEmitRun];
-  uint32_t pos[kEmitRun];
-  int per, i0, n;
-  __device__ __forceinline__ bool valid(int j) const { return j < per && i0 + j < n; }
-};
-
-// Loads the runs (blockDim.x = 1024) and turns each entry's offset into its
-// position: its tile's first token (64 + tile * chunk; the tile of list entry i
-// is the last one whose list offset off[tile] <= i) plus the offset; entries
-// past the tiles' (an appended token) get last_pos.  The tile of the run's
-// first entry comes from a binary search of off[], then only crossings read
-// it again.  No barrier.
-__device__ __forceinline__ void run_load(Run& rn, const uint32_t* keys, const uint16_t* ofs, int n,
-                                         const int* off, int n_chunks, int chunk, int last_pos) {
-  rn.per = ((n + blockDim.x - 1) / blockDim.x) | 1;
-  rn.i0 = threadIdx.x * rn.per;
-  rn.n = n;
+__device__ void list_emit(const uint32_t* keys, const uint16_t* ofs, int n, const int* off,
+                          int n_chunks, int chunk, int last_pos, int k, Kth r, int32_t* stage,
+                          int32_t* __restrict__ out, int* tmp) {
+  const int per = ((n + blockDim.x - 1) / blockDim.x) | 1;
+  const int i0 = min(n, (int)threadIdx.x * per), m = min(n - i0, per);  // m <= kEmitRun
+  uint32_t kk[kEmitRun];
+  uint16_t oo[kEmitRun];
 #pragma unroll
   for (int j = 0; j < kEmitRun; ++j) {
-    rn.key[j] = rn.valid(j) ? keys[rn.i0 + j] : 0u;
-    rn.pos[j] = rn.valid(j) ? ofs[rn.i0 + j] : 0u;
+    kk[j] = j < m ? keys[i0 + j] : 0u;
+    oo[j] = j < m ? ofs[i0 + j] : (uint16_t)0;
   }
   int ci = 0;
   for (int step = 1 << 11; step > 0; step >>= 1)
-    if (ci + step <= n_chunks && off[ci + step] <= rn.i0) ci += step;
+    if (ci + step <= n_chunks && off[ci + step] <= i0) ci += step;
   int next = ci < n_chunks ? off[ci + 1] : 0x7fffffff;  // first entry of the following tile
-#pragma unroll
-  for (int j = 0; j < kEmitRun; ++j) {
-    const int i = rn.i0 + j;
-    while (i >= next) {  // crossing into a later tile (rare)
-      ++ci;
-      next = ci < n_chunks ? off[ci + 1] : 0x7fffffff;
-    }
-    rn.pos[j] = ci < n_chunks ? (uint32_t)(kSink + ci * chunk) + rn.pos[j] : (uint32_t)last_pos;
-  }
-}
-
-// block_emit over the runs, with coalesced output: the (gt, eq) counts are
-// scanned, every thread writes its taken positions into the key list (stage;
-// the caller no longer needs it), and the block copies them out in order,
-// consecutive threads storing consecutive entries.  Two barriers beyond the
-// scan.
-__device__ void run_emit(const Run& rn, int k, Kth r, uint32_t* stage, int32_t* __restrict__ out,
-                         int* tmp) {
   int gt = 0, eq = 0;
 #pragma unroll
   for (int j = 0; j < kEmitRun; ++j) {
-    gt += (rn.valid(j) && rn.key[j] > r.key) ? 1 : 0;
-    eq += (rn.valid(j) && rn.key[j] == r.key) ? 1 : 0;
+    gt += (j < m && kk[j] > r.key) ? 1 : 0;
+    eq += (j < m && kk[j] == r.key) ? 1 : 0;
   }
   int tot;
   const int ex = block_excl_scan((gt << 16) | eq, tmp, &tot);  // n <= kSelectLds < 2^16
   int eq_before = ex & 0xffff;
   int o = (ex >> 16) + min(eq_before, r.need);
-  __syncthreads();  // no thread reads the list any more
 #pragma unroll
   for (int j = 0; j < kEmitRun; ++j) {
-    bool take = rn.valid(j) && rn.key[j] > r.key;
-    if (rn.valid(j) && rn.key[j] == r.key) take = eq_before++ < r.need;
-    if (take && o < k) stage[o++] = rn.pos[j];
+    bool take = j < m && kk[j] > r.key;
+    if (j < m && kk[j] == r.key) take = eq_before++ < r.need;
+    if (take && o < k) {
+      const int i = i0 + j;
+      while (i >= next) {  // crossing into a later tile (rare)
+        ++ci;
+        next = ci < n_chunks ? off[ci + 1] : 0x7fffffff;
+      }
+      stage[o++] = ci < n_chunks ? kSink + ci * chunk + (int)oo[j] : last_pos;
+    }
   }
   __syncthreads();
-  for (int j = threadIdx.x; j < k; j += blockDim.x) out[j] = (int32_t)stage[j];
+  for (int j = threadIdx.x; j < k; j += blockDim.x) out[j] = stage[j];
 }
 
 // Copies the selection table of one head from global memory into LDS (2 KB).
@@ -660,7 +648,8 @@ __device__ __forceinline__ void leader_append(const ScoreArgs& a, int bh, int b,
 // One block per (b, KV head), dispatched before every tile block of the score
 // kernel (lowest block indices): the selection table (kept in the workspace
 // for the select kernel's exact path) and the sampled threshold tau, published
-// to the head's tiles through the threshold word (the attention tables are made
+// to the head's tiles through the threshold word; the block then scores the
+// head's last tile itself (so the grid has one block per tile) (the attention tables are made
 // by extra blocks of the select kernel, off this path).
 // Sample: stratum st = i / 16 of 128 equal segments of the head's candidates,
 // 16 contiguous tokens centred in it (the whole candidate set when it is small;
@@ -671,8 +660,8 @@ __device__ __forceinline__ void leader_append(const ScoreArgs& a, int bh, int b,
 // mode 2: tau = +inf (nothing passes: the select kernel takes its exact
 // whole-head path).  No sample (it would not bound the k-th): tau = -inf.
 template <bool kCb>
-__device__ void leader(const ScoreArgs& a, int bh, int* itab, uint32_t* hist, uint32_t* qs,
-                       float* ssc, float* red, float* jmax) {
+__device__ float leader(const ScoreArgs& a, int bh, int* itab, uint32_t* hist, uint32_t* qs,
+                        float* ssc, float* red, float* jmax) {
   constexpr int kRows = kSampleMax / 256;  // sample rows per thread, all in flight at once
   static_assert(kRows * 256 == kSampleMax, "sample split");
   __builtin_amdgcn_s_setprio(3);  // issue ahead of the tile waves sharing the CU
@@ -759,6 +748,8 @@ __device__ void leader(const ScoreArgs& a, int bh, int* itab, uint32_t* hist, ui
     __hip_atomic_store(a.tau_word + bh, ((unsigned long long)kTauTag << 32) | __float_as_uint(th),
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  __builtin_amdgcn_s_setprio(0);  // the block's own tile follows at normal priority
+  return inv;
 }
 
 // The published threshold of a head: w, lane 0's earlier load of the word,
@@ -779,8 +770,10 @@ __device__ __forceinline__ float wait_tau(unsigned long long* word, unsigned lon
 }
 
 // ------------------------------------------------------------------ score
-// Grid: B*Hkv leader blocks (above), then one block per tile of 256*U
-// candidates of a head, 1-D, head-major.  In a tile, lane <-> token; wave w
+// Grid: B*Hkv leader blocks (above; each also scores its head's last tile),
+// then one block per other tile of 256*U candidates of a head, 1-D, head-major:
+// one block per tile in all, so that a grid of 2048 tiles is resident at once
+// (eight blocks per CU).  In a tile, lane <-> token; wave w
 // scores the tile's w-th quarter, U groups of 64 tokens, on its own.  Each wave
 // issues all its loads first; they are unconditional, at token indices clamped
 // to the sequence's last token (always a valid row), so the compiler counts the
@@ -797,7 +790,7 @@ __device__ __forceinline__ float wait_tau(unsigned long long* word, unsigned lon
 // Eight waves per SIMD (64 VGPRs) for tiles of up to 8 groups, so that the
 // 2048-tile grid at 128K tokens is resident at once; the leader path and the
 // tile path each fit, but the allocator would give the merged kernel a few more
-// without the bound (the codebook variant spills 8 bytes per lane).
+// without the bound (the codebook variant spills 32 bytes per lane).
 template <int U, bool kPaged, bool kCb, int S = (U < 8 ? U : 8)>
 __global__ __launch_bounds__(256, (U <= 8 ? 8 : 1)) void score_kernel(ScoreArgs a) {
   constexpr int kChunk = 256 * U;
@@ -811,12 +804,21 @@ __global__ __launch_bounds__(256, (U <= 8 ? 8 : 1)) void score_kernel(ScoreArgs 
   __shared__ float jmax[kSub];
   __shared__ int wcnt[4];
   __shared__ uint32_t wtau[4];
-  if ((int)blockIdx.x < a.n_heads) {
-    leader<kCb>(a, blockIdx.x, itab, hist, qs, ssc, red, jmax);
-    return;
+  // Block bh < n_heads: the leader of head bh, which then scores the head's
+  // last tile with the table it built; the other blocks score tiles
+  // 0 .. n_chunks - 2 of their head.
+  const bool lead = (int)blockIdx.x < a.n_heads;
+  int bh, cx;
+  if (lead) {
+    bh = blockIdx.x;
+    cx = a.n_chunks - 1;
+  } else {
+    const int tile = blockIdx.x - a.n_heads, per = a.n_chunks - 1;
+    bh = tile / per;
+    cx = tile - bh * per;
   }
-  const int tile = blockIdx.x - a.n_heads;
-  const int bh = tile / a.n_chunks, cx = tile - bh * a.n_chunks;
+  float inv = 0.0f;
+  if (lead) inv = leader<kCb>(a, bh, itab, hist, qs, ssc, red, jmax);
   const int b = bh / a.Hkv, h = bh - b * a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: rows from scalar bases
@@ -829,7 +831,7 @@ __global__ __launch_bounds__(256, (U <= 8 ? 8 : 1)) void score_kernel(ScoreArgs 
   const int64_t hq0 = (int64_t)b * a.n_q_heads + (int64_t)h * a.G;
   const float* cb = a.codebook != nullptr ? a.codebook + (int64_t)bh * kLut * 4 : nullptr;
   SelQ sq;
-  sel_issue<kCb>(sq, a.q, hq0, a.G, cb, tid);
+  if (!lead) sel_issue<kCb>(sq, a.q, hq0, a.G, cb, tid);
   const int64_t hrow = (int64_t)bh * a.rm.capacity;  // contiguous: the head's first row
   // Paged: the quarter's tokens (clamped to the sequence) span at most U + 1
   // pages; lane j holds the id of the j-th, read out per group with a lane read
@@ -865,11 +867,12 @@ __global__ __launch_bounds__(256, (U <= 8 ? 8 : 1)) void score_kernel(ScoreArgs 
   };
   load_step(0);
   if constexpr (NS > 1) load_step(1);
-  float inv;
-  const int2 tv = sel_build<kCb>(sq, a.G, jmax, tid, &inv);
-  int tz;
-  asm volatile("v_mov_b32 %0, 0" : "=v"(tz));  // the table is stored after the loads go out
-  reinterpret_cast<int2*>(itab)[tid] = make_int2(tv.x ^ tz, tv.y ^ tz);
+  if (!lead) {  // (the leader's table is in itab already)
+    const int2 tv = sel_build<kCb>(sq, a.G, jmax, tid, &inv);
+    int tz;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(tz));  // the table is stored after the loads go out
+    reinterpret_cast<int2*>(itab)[tid] = make_int2(tv.x ^ tz, tv.y ^ tz);
+  }
   __syncthreads();
   uint32_t key[U];
   // gate: a zero from an asm placed after the table barrier (then after the
@@ -1084,14 +1087,15 @@ __global__ __launch_bounds__(1024) void select_kernel(
   }
   for (int i = tid; i < 2048; i += blockDim.x) hist[i] = 0u;  // published by the scan's barriers
   // Tile counts -> offsets of each tile's candidates in the ordered list.  The
-  // counts are loaded first, then the first 256 slots of each wave's first four
-  // tiles, which stay in flight while the counts are scanned (loads complete in
-  // order; all of them unconditional at clamped indices, so that no wait sits
-  // inside a branch).  A tile's slot region holds chunk >= 256 entries, so every
-  // slot load is in bounds; slots past a tile's count are discarded.
+  // counts are loaded first, then the first kPreG * 64 slots of each wave's
+  // first four tiles, which stay in flight while the counts are scanned (loads
+  // complete in order; all of them unconditional at indices clamped into the
+  // tile's slot region, so that no wait sits inside a branch); slots past a
+  // tile's count are discarded.
+  constexpr int kPreG = 4;  // 256 slots
   const int64_t cbase = (int64_t)bh * n_chunks * chunk;
-  uint32_t pk[4][4];
-  int32_t pt[4][4];
+  uint32_t pk[4][kPreG];
+  int32_t pt[4][kPreG];
   int any_bad;
   {
     const int per = (n_chunks + blockDim.x - 1) / blockDim.x;  // <= 2
@@ -1106,9 +1110,10 @@ __global__ __launch_bounds__(1024) void select_kernel(
       for (int v = 0; v < 4; ++v) {
         const int64_t src = cbase + (int64_t)min(wave + v * nw, n_chunks - 1) * chunk;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          pk[v][u] = cand_key[src + lane + 64 * u];
-          pt[v][u] = cand_t[src + lane + 64 * u];
+        for (int u = 0; u < kPreG; ++u) {
+          const int j = min(lane + 64 * u, chunk - 1);
+          pk[v][u] = cand_key[src + j];
+          pt[v][u] = cand_t[src + j];
         }
       }
     }
@@ -1163,13 +1168,13 @@ __global__ __launch_bounds__(1024) void select_kernel(
   auto gather = [&]() {
     const int lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
     for (int c0 = wave; c0 < n_chunks; c0 += 4 * nw) {
-      uint32_t kk[4][4];
-      int32_t tt[4][4];
+      uint32_t kk[4][kPreG];
+      int32_t tt[4][kPreG];
       if (c0 == wave) {
 #pragma unroll
         for (int v = 0; v < 4; ++v)
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
+          for (int u = 0; u < kPreG; ++u) {
             kk[v][u] = pk[v][u];
             tt[v][u] = pt[v][u];
           }
@@ -1181,7 +1186,7 @@ __global__ __launch_bounds__(1024) void select_kernel(
           const int cnt = ci < n_chunks ? off[ci + 1] - o : 0;
           const int64_t src = cbase + (int64_t)ci * chunk;
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
+          for (int u = 0; u < kPreG; ++u) {
             const int j = lane + 64 * u;
             kk[v][u] = j < cnt ? cand_key[src + j] : 0u;
             tt[v][u] = j < cnt ? cand_t[src + j] : 0;
@@ -1196,7 +1201,7 @@ __global__ __launch_bounds__(1024) void select_kernel(
         const int64_t src = cbase + (int64_t)ci * chunk;
         const int tb = kSink + ci * chunk;  // the tile's first token
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < kPreG; ++u) {
           const int j = lane + 64 * u;
           if (j < cnt) {
             lkey[o + j] = kk[v][u];
@@ -1204,7 +1209,7 @@ __global__ __launch_bounds__(1024) void select_kernel(
           }
           count_bin(hist, j < cnt, bin_of(kk[v][u]));
         }
-        for (int j0 = 256; j0 < cnt; j0 += 64) {  // tiles with many candidates
+        for (int j0 = 64 * kPreG; j0 < cnt; j0 += 64) {  // tiles with many candidates
           const int j = j0 + lane;
           const uint32_t key = j < cnt ? cand_key[src + j] : 0u;
           if (j < cnt) {
@@ -1235,12 +1240,9 @@ __global__ __launch_bounds__(1024) void select_kernel(
   }
   if (in_lds) {
     __syncthreads();  // publishes the list and the histogram
-    // Each thread's run of the list goes to registers while the histogram is
-    // scanned for the boundary bin of the k-th largest; the bin's keys (usually
-    // a few dozen) go to a sub-list resolved by one wave, or by radix rounds if
-    // more than 64.
-    Run rn;
-    run_load(rn, lkey, lofs, C, off, n_chunks, chunk, nt - 1);
+    // The histogram is scanned for the boundary bin of the k-th largest; the
+    // bin's keys (usually a few dozen) go to a sub-list resolved by one wave,
+    // or by radix rounds if more than 64.
     const Round rb = hist_pick(hist, 2048, top_k, tmp, C);
     Kth r;
     if (rb.count <= kSubMax) {
@@ -1281,10 +1283,10 @@ __global__ __launch_bounds__(1024) void select_kernel(
       if (tid == 0) scount = 0;
       __syncthreads();
       const uint32_t klo = mm[0], khi = mm[1];
-#pragma unroll
-      for (int j = 0; j < kEmitRun; ++j)
-        if (rn.valid(j) && rn.key[j] >= klo && rn.key[j] <= khi)
-          sub[atomicAdd(&scount, 1)] = rn.key[j];
+      for (int i = tid; i < C; i += blockDim.x) {
+        const uint32_t key = lkey[i];
+        if (key >= klo && key <= khi) sub[atomicAdd(&scount, 1)] = key;
+      }
       __syncthreads();
       const int ns = scount, need = top_k - rb.above;
       if (ns <= 64) {
@@ -1315,7 +1317,8 @@ __global__ __launch_bounds__(1024) void select_kernel(
                         mm, out);
       return;
     }
-    run_emit(rn, top_k, r, lkey, out, tmp);
+    list_emit(lkey, lofs, C, off, n_chunks, chunk, nt - 1, top_k, r,
+              reinterpret_cast<int32_t*>(lkey), out, tmp);
   }
 }
 
@@ -1326,7 +1329,7 @@ hipError_t launch_tables(const ScoreArgs& a, const Launch& s) {
 }
 
 hipError_t launch_score(const ScoreArgs& a, int chunk, const Launch& s) {
-  const dim3 grid((unsigned)a.n_heads * (unsigned)(a.n_chunks + 1)), block(256);
+  const dim3 grid((unsigned)a.n_heads * (unsigned)a.n_chunks), block(256);
 #define SIKV_SCORE_CASE(UU)                                                                 \
   case 256 * UU:                                                                            \
     if (a.codebook != nullptr)                                                              \
