@@ -138,6 +138,7 @@ KERNEL_SOURCES = {
     "score": ["score.hip", "sikv_internal.h", "api.cpp"],
     "select": ["score.hip", "sikv_internal.h", "api.cpp"],
     "attn": ["attn.hip", "sikv_internal.h", "api.cpp"],
+    "attn_qv": ["attn.hip", "sikv_internal.h", "api.cpp"],
     "combine": ["attn.hip", "sikv_internal.h", "api.cpp"],
     "codes": ["encode.hip", "sikv_internal.h", "api.cpp"],
     "mu_partial": ["encode.hip", "sikv_internal.h", "api.cpp"],
@@ -163,7 +164,10 @@ def short_kernel_name(name: str) -> str:
 
 
 def library_kernel(name: str):
-    base = short_kernel_name(name).split("<")[0]
+    short = short_kernel_name(name)
+    base = short.split("<")[0]
+    if base == "attn_kernel" and ", true>" in short:  # the 2-bit-value variant
+        return "attn_qv"
     return base[:-len("_kernel")] if base.endswith("_kernel") and base[:-len("_kernel")] in KERNEL_SOURCES else None
 
 
@@ -236,26 +240,33 @@ COUNTER_RATIOS = {
 
 def summarize_counters(out_json: str, run_dirs, command: str) -> None:
     """Counters of several --pmc runs of the same command, merged per kernel
-    (a counter taken in more than one run keeps its first run's value), with
-    the ratios above wherever their inputs were taken."""
-    merged = {}
+    (a counter taken in more than one run keeps its first run's value; values
+    are means per dispatch, 4 significant digits), with the ratios above
+    wherever their inputs were taken."""
+    merged, passes, ndisp = {}, {}, {}
     for d in run_dirs:
+        run = os.path.basename(d.rstrip("/"))
         for k, cs in _counters_per_kernel(d).items():
             ent = merged.setdefault(k, {})
             for c, (n, v) in cs.items():
-                ent.setdefault(c, {"dispatches": n, "per_dispatch": v, "run": os.path.basename(d)})
-    out = {"command": command, "runs": [os.path.basename(d) for d in run_dirs],
+                if c not in ent:
+                    ent[c] = v
+                    ndisp.setdefault(k, n)
+                    if c not in passes.setdefault(run, []):
+                        passes[run].append(c)
+    sig = lambda x: float(f"{x:.4g}")
+    out = {"command": command, "passes": passes,
            "ratios": {r: f for r, (f, _) in COUNTER_RATIOS.items()}, "kernels": {}}
     for k in sorted(merged):
-        vals = {c: e["per_dispatch"] for c, e in merged[k].items()}
         ratios = {}
         for r, (_, fn) in COUNTER_RATIOS.items():
             try:
-                ratios[r] = fn(vals)
+                ratios[r] = sig(fn(merged[k]))
             except (KeyError, ZeroDivisionError):
                 pass
-        out["kernels"][k] = {"counters": merged[k], "derived": ratios,
-                             "sources": KERNEL_SOURCES[k],
+        out["kernels"][k] = {"dispatches": ndisp.get(k, 0),
+                             "counters": {c: sig(v) for c, v in sorted(merged[k].items())},
+                             "derived": ratios, "sources": KERNEL_SOURCES[k],
                              "source_hash": source_hash(KERNEL_SOURCES[k])}
     json.dump(out, open(out_json, "w"), indent=1)
     print(json.dumps({k: v["derived"] for k, v in out["kernels"].items()}, indent=1))
