@@ -40,6 +40,7 @@ constexpr int kBandBins = 1024;    // equal-width bins of the sample's band
 constexpr int kSelectLds = 20480;  // candidates kept in LDS by select (keys + 16-bit offsets)
 constexpr int kMaxChunks = 2048;
 constexpr int kSubMax = 1024;
+constexpr int kGatherRun = 10;  // select: candidates a thread loads together past the first tiles
 
 // ------------------------------------------------------------------ block helpers
 // Exclusive prefix sum of one int per thread over the block (blockDim a multiple
@@ -1167,60 +1168,81 @@ __global__ __launch_bounds__(1024) void select_kernel(
   // within the tile.
   auto gather = [&]() {
     const int lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
-    for (int c0 = wave; c0 < n_chunks; c0 += 4 * nw) {
-      uint32_t kk[4][kPreG];
-      int32_t tt[4][kPreG];
-      if (c0 == wave) {
+    // Tiles wave + v*nw (v < 4): from the slots loaded before the scan.
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
+    for (int v = 0; v < 4; ++v) {
+      const int ci = wave + v * nw;
+      if (ci >= n_chunks) continue;
+      const int o = off[ci], cnt = off[ci + 1] - o;
+      const int64_t src = cbase + (int64_t)ci * chunk;
+      const int tb = kSink + ci * chunk;  // the tile's first token
 #pragma unroll
-          for (int u = 0; u < kPreG; ++u) {
-            kk[v][u] = pk[v][u];
-            tt[v][u] = pt[v][u];
-          }
-      } else {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int ci = c0 + v * nw;
-          const int o = ci < n_chunks ? off[ci] : 0;
-          const int cnt = ci < n_chunks ? off[ci + 1] - o : 0;
-          const int64_t src = cbase + (int64_t)ci * chunk;
-#pragma unroll
-          for (int u = 0; u < kPreG; ++u) {
-            const int j = lane + 64 * u;
-            kk[v][u] = j < cnt ? cand_key[src + j] : 0u;
-            tt[v][u] = j < cnt ? cand_t[src + j] : 0;
-          }
+      for (int u = 0; u < kPreG; ++u) {
+        const int j = lane + 64 * u;
+        if (j < cnt) {
+          lkey[o + j] = pk[v][u];
+          lofs[o + j] = (uint16_t)(pt[v][u] - tb);
         }
+        count_bin(hist, j < cnt, bin_of(pk[v][u]));
       }
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int ci = c0 + v * nw;
-        if (ci >= n_chunks) continue;
-        const int o = off[ci], cnt = off[ci + 1] - o;
-        const int64_t src = cbase + (int64_t)ci * chunk;
-        const int tb = kSink + ci * chunk;  // the tile's first token
-#pragma unroll
-        for (int u = 0; u < kPreG; ++u) {
-          const int j = lane + 64 * u;
-          if (j < cnt) {
-            lkey[o + j] = kk[v][u];
-            lofs[o + j] = (uint16_t)(tt[v][u] - tb);
-          }
-          count_bin(hist, j < cnt, bin_of(kk[v][u]));
+      for (int j0 = 64 * kPreG; j0 < cnt; j0 += 64) {  // tiles with many candidates
+        const int j = j0 + lane;
+        const uint32_t key = j < cnt ? cand_key[src + j] : 0u;
+        if (j < cnt) {
+          lkey[o + j] = key;
+          lofs[o + j] = (uint16_t)(cand_t[src + j] - tb);
         }
-        for (int j0 = 64 * kPreG; j0 < cnt; j0 += 64) {  // tiles with many candidates
-          const int j = j0 + lane;
-          const uint32_t key = j < cnt ? cand_key[src + j] : 0u;
-          if (j < cnt) {
-            lkey[o + j] = key;
-            lofs[o + j] = (uint16_t)(cand_t[src + j] - tb);
+        count_bin(hist, j < cnt, bin_of(key));
+      }
+    }
+    // Any further tiles (long contexts): their candidates, list entries
+    // off[4 nw] .. Ct, as one contiguous run per thread, kGatherRun entries a
+    // batch with all of a batch's loads in flight together; a run's tile comes
+    // from a binary search of off[], then only crossings read it again.
+    const int t4 = 4 * nw;
+    if (n_chunks > t4) {
+      const int L0 = off[t4], n_rest = Ct - L0;
+      const int per = (n_rest + (int)blockDim.x - 1) / (int)blockDim.x;
+      const int i0 = L0 + min(n_rest, tid * per), m = min(L0 + n_rest - i0, per);
+      int ci = t4;
+      for (int step = 1 << 11; step > 0; step >>= 1)
+        if (ci + step < n_chunks && off[ci + step] <= i0) ci += step;
+      int base = off[ci], next = off[ci + 1];
+      for (int b0 = 0; b0 < m; b0 += kGatherRun) {
+        uint32_t kk[kGatherRun];
+        int32_t tt[kGatherRun];
+        int cc[kGatherRun];
+#pragma unroll
+        for (int j = 0; j < kGatherRun; ++j) {
+          const int i = i0 + b0 + j;
+          kk[j] = 0u;
+          tt[j] = 0;
+          cc[j] = ci;
+          if (b0 + j < m) {
+            while (i >= next) {  // crossing into a later tile
+              ++ci;
+              base = next;
+              next = off[ci + 1];
+            }
+            const int64_t sl = cbase + (int64_t)ci * chunk + (i - base);
+            kk[j] = cand_key[sl];
+            tt[j] = cand_t[sl];
+            cc[j] = ci;
           }
-          count_bin(hist, j < cnt, bin_of(key));
+        }
+#pragma unroll
+        for (int j = 0; j < kGatherRun; ++j) {
+          const int i = i0 + b0 + j;
+          if (b0 + j < m) {
+            lkey[i] = kk[j];
+            lofs[i] = (uint16_t)(tt[j] - (kSink + cc[j] * chunk));
+          }
+          count_bin(hist, b0 + j < m, bin_of(kk[j]));
         }
       }
     }
   };
+
   if (!in_lds) {
     if (!select_workspace(cand_key + cbase, cand_t + cbase, chunk, n_chunks, off, C, top_k, ap,
                           akey, nt - 1, thk, comp_key + cbase, comp_t + cbase, hist, tmp, sub,
