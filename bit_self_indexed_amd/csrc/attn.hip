@@ -14,11 +14,13 @@
 //            q_g . k^ = q_g . mu + alpha * sum_j LUT_g[j][nibble_j]  (the key is
 //            never materialised; rounding mu + alpha*v to fp32 first would be a
 //            relative 2^-24 effect, far inside the fp32 accumulation error);
-//            sink entries take the exact bf16-key logits made by the prep kernel;
+//            sink entries take the exact bf16-key logits made beside the
+//            selection (the select launch's table blocks);
 //   softmax  chunk max per head over 32 lanes, running max / sum update,
 //            probabilities through a wave-private LDS row;
 //   P.V      16-lane group r owns entries r, r+4, ..., r+28: 16 bytes (8 bf16
-//            channels) of each V row per lane, fp32 FMAs into G x 8 accumulators.
+//            channels) of each V row per lane, fp32 FMAs into G x 8 accumulators;
+//            2-bit values with G <= 4: matrix-core products (below).
 // The block first copies its slice of the position list into LDS (one round
 // trip), so a wave can issue all loads of its next chunk (codes, scales and V
 // rows) right after the current chunk's have arrived, before computing it.
@@ -40,6 +42,37 @@ namespace sikv {
 namespace {
 
 constexpr int kRows = kAttnChunk / 4;  // V rows per 16-lane group per chunk
+
+// P.V of the 2-bit-value path on the matrix cores (G <= 4), per chunk of 32
+// entries, as v_mfma_f32_16x16x32_f16 products with K = the chunk's entries
+// (K index = entry index e):
+//   out[g][c] = sum_e p[g][e] (z[e][c/32] + s[e][c/32] q[e][c])
+//             = sum_e A[4 (c/32) + g][e] B[e][c] + sum_e p[g][e] (z - 4 s)[e][c/32],
+//   A[4 gc + g][e] = p[g][e] s[e][gc] * 2^10 (fp16, as a high and a low part),
+//   B[e][c] = 4 + q[e][c] (exact in fp16: bits 0x4400 | q << 8).
+// Row 4 gc + g of A pairs head g with channel group gc, so the 16 rows carry
+// all four groups; of each product's output only the rows of the block's own
+// channel group are kept.  The offset 4 keeps B away from fp16 subnormals
+// (which the matrix cores do not multiply exactly) and 2^10 keeps A's small
+// terms normal; a chunk whose value scale exceeds kMfScaleMax (A's high part
+// would overflow fp16) takes the FMA path instead.
+constexpr bool mf_path(int G, bool QV) { return QV && G <= 4; }
+constexpr float kMfScale = 1024.0f;
+constexpr float kMfScaleMax = 63.0f;
+constexpr int kBtStride = kD + 8;  // halves per staged B row (padded: rows 16 banks apart)
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef float float8v __attribute__((ext_vector_type(8)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
+
+// Per-wave LDS of the matrix-core path: the chunk's probabilities by head, the
+// value scales by channel group, and B (entry rows of 128 halves).
+struct MfLds {
+  float pT[4][kAttnChunk];
+  float sg[4][kAttnChunk];
+  __attribute__((aligned(16))) _Float16 bt[kAttnChunk][kBtStride];
+};
 
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -117,14 +150,48 @@ __device__ __forceinline__ void load_chunk(Chunk<G>& x, int c, int lc, bool sink
 template <int G>
 struct Acc {
   float m[G], lsum[(G + 1) / 2], acc[G][8], zacc[G];  // zacc: sum of p * zero point (QV)
+  float4v d[8];  // matrix-core path: one 16x16 output block per 16 channels
 };
 
 template <int G, bool QV>
 __device__ __forceinline__ void process_chunk(Acc<G>& st, const Chunk<G>& x, bool sink, bool live,
                                               const float (*lutq)[kLut], const float* qmu,
-                                              float sm_log2, float (*pbw)[G], int lane) {
+                                              float sm_log2, float (*pbw)[G], MfLds* mf,
+                                              int lane) {
   constexpr int GH = (G + 1) / 2;
-  const int el = lane & 31, half = lane >> 5, grp = lane >> 4;
+  constexpr bool kMf = mf_path(G, QV);
+  const int el = lane & 31, half = lane >> 5, grp = lane >> 4, seg = lane & 15;
+  // matrix-core path for this chunk: stage B and the group scales first (they
+  // do not depend on the probabilities); a scale above kMfScaleMax anywhere in
+  // the chunk sends it to the FMA path
+  bool use_mf = false;
+  if constexpr (kMf) {
+    if (!sink) {
+      bool big = false;
+#pragma unroll
+      for (int u = 0; u < kRows; ++u) {
+        const uint32_t sz = x.v[u].y;
+        big |= !(fabsf(__half2float(__ushort_as_half((unsigned short)(sz & 0xffffu)))) <= kMfScaleMax);
+      }
+      use_mf = __ballot(big) == 0ull;
+      if (use_mf) {
+#pragma unroll
+        for (int u = 0; u < kRows; ++u) {
+          const int eu = grp + 4 * u;
+          const uint32_t y = x.v[u].x & 0xffffu, t = y | (y << 14);
+          // dword k: channels 2k, 2k+1 of the lane's eight, each 4 + q as fp16
+          uint4 w;
+          w.x = ((t << 8) & 0x03000300u) | 0x44004400u;
+          w.y = ((t << 4) & 0x03000300u) | 0x44004400u;
+          w.z = (t & 0x03000300u) | 0x44004400u;
+          w.w = ((t >> 4) & 0x03000300u) | 0x44004400u;
+          *reinterpret_cast<uint4*>(&mf->bt[eu][8 * seg]) = w;
+          if ((seg & 3) == 0)
+            mf->sg[seg >> 2][eu] = __half2float(__ushort_as_half((unsigned short)(x.v[u].y & 0xffffu)));
+        }
+      }
+    }
+  }
   // logits (log2 domain) of this lane's heads g = 2i + half
   float lg[GH];
 #pragma unroll
@@ -155,6 +222,12 @@ __device__ __forceinline__ void process_chunk(Acc<G>& st, const Chunk<G>& x, boo
     for (int i = 0; i < 8; ++i) st.acc[g][i] *= sc[g];
     if (QV) st.zacc[g] *= sc[g];
   }
+  if constexpr (kMf) {  // output rows 4 * (lane / 16) + j are head j of a channel group
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) st.d[nb][j] *= j < G ? sc[j] : 0.0f;
+  }
 #pragma unroll
   for (int i = 0; i < GH; ++i) {
     const int g1 = min(2 * i + 1, G - 1);
@@ -164,10 +237,59 @@ __device__ __forceinline__ void process_chunk(Acc<G>& st, const Chunk<G>& x, boo
     const float sg = half ? s_odd : s_even;
     const float p = exp2f(lg[i] - mg);
     st.lsum[i] = fmaf(st.lsum[i], sg, p);
-    if (2 * i + half < G) pbw[el][2 * i + half] = p;
+    if (2 * i + half < G) {
+      pbw[el][2 * i + half] = p;
+      if constexpr (kMf) mf->pT[2 * i + half][el] = p;
+    }
   }
   wave_sync_lds();
   // P.V
+  if constexpr (kMf) {
+    if (use_mf) {
+      // A (lane: row m = lane % 16 = 4 gc + g, entries 8 (lane / 16) .. + 7)
+      const int am = lane & 15, agc = am >> 2, ag = am & 3, k0 = 8 * (lane >> 4);
+      float8v af;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        af[j] = ag < G ? mf->pT[ag < G ? ag : 0][k0 + j] * mf->sg[agc][k0 + j] * kMfScale : 0.0f;
+      const half8 ahi = __builtin_convertvector(af, half8);
+      const half8 alo = __builtin_convertvector(af - __builtin_convertvector(ahi, float8v), half8);
+      // B by transposed LDS reads: lane (k4 = lane / 16, r = lane % 16) points at
+      // entry k0 + 4 h + r / 4, channels 16 nb + 4 (r % 4) .. + 3, and receives
+      // entries k0 + 4 h .. + 3 of channel 16 nb + r
+      const int r = lane & 15;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        short4v t4[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const _Float16* src = &mf->bt[k0 + 4 * hh + (r >> 2)][16 * nb + 4 * (r & 3)];
+          t4[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) short4v*)(
+                  (__attribute__((address_space(3))) void*)src));
+        }
+        // whole-vector bit casts: building the fragment element by element from the
+        // transposed reads compiles to wrong register moves
+        const half8 bv = __builtin_bit_cast(
+            half8, __builtin_shufflevector(t4[0], t4[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        st.d[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bv, st.d[nb], 0, 0, 0);
+        st.d[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bv, st.d[nb], 0, 0, 0);
+      }
+      // zero points: sum_e p (z - 4 s), per lane for its channel group
+#pragma unroll
+      for (int u = 0; u < kRows; ++u) {
+        const int eu = grp + 4 * u;
+        const uint32_t sz = x.v[u].y;
+        const float sv = __half2float(__ushort_as_half((unsigned short)(sz & 0xffffu)));
+        const float zv = __half2float(__ushort_as_half((unsigned short)(sz >> 16)));
+        const float z4 = fmaf(-4.0f, sv, zv);
+#pragma unroll
+        for (int g = 0; g < G; ++g) st.zacc[g] = fmaf(pbw[eu][g], z4, st.zacc[g]);
+      }
+      wave_sync_lds();
+      return;
+    }
+  }
   if (!QV || sink) {
 #pragma unroll
     for (int u = 0; u < kRows; ++u) {
@@ -222,6 +344,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(
   __shared__ __align__(16) float pb[4][kAttnChunk][G];
   __shared__ float mo[4][G][kD];
   __shared__ float mml[4][G][2];
+  __shared__ MfLds mfl[mf_path(G, QV) ? 4 : 1];
 
   const int bh = blockIdx.y, b = bh / Hkv, h = bh - b * Hkv;
   const int s = blockIdx.x;
@@ -265,7 +388,10 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(
   for (int i = 0; i < GH; ++i) qmu[i] = (2 * i + half < G) ? att_qmu[hq0 + 2 * i + half] : 0.0f;
   __syncthreads();
 
+  MfLds* mfw = &mfl[mf_path(G, QV) ? wave : 0];
   Acc<G> st;
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) st.d[nb] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     st.m[g] = -INFINITY;
@@ -285,7 +411,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(
   if (c < c_end && c * kAttnChunk < kSink) {
     Chunk<G> sk;
     load_chunk<G, QV>(sk, c, c - c0, true, sidx, lane, src);
-    process_chunk<G, QV>(st, sk, true, true, lutq, qmu, sm_log2, pb[wave], lane);
+    process_chunk<G, QV>(st, sk, true, true, lutq, qmu, sm_log2, pb[wave], mfw, lane);
     c += 4;
   }
   if (c < c_end) {
@@ -297,10 +423,10 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(
       load_chunk<G, QV>(nx, c + 4, c + 4 - c0, false, sidx, lane, src);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the chunk's work
       process_chunk<G, QV>(st, cur, false, c * kAttnChunk + el < L, lutq, qmu, sm_log2, pb[wave],
-                           lane);
+                           mfw, lane);
     }
     process_chunk<G, QV>(st, nx, false, c * kAttnChunk + el < L, lutq, qmu, sm_log2, pb[wave],
-                         lane);
+                         mfw, lane);
   }
 
   // Wave partial: sums over the four 16-lane groups and over the 32 lanes.
@@ -324,6 +450,19 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(
     for (int g = 0; g < G; ++g)
 #pragma unroll
       for (int i = 0; i < 8; ++i) mo[wave][g][seg * 8 + i] = st.acc[g][i];
+  }
+  if constexpr (mf_path(G, QV)) {
+    // matrix-core products: lane (r4 = lane / 16, n = lane % 16) holds, for the
+    // channel blocks nb = 2 r4 and 2 r4 + 1 (channel group r4), head j's output
+    // at channel 16 nb + n
+    wave_sync_lds();
+    const int r4 = lane >> 4, n = lane & 15;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      if ((nb >> 1) != r4) continue;
+#pragma unroll
+      for (int j = 0; j < G; ++j) mo[wave][j][16 * nb + n] += st.d[nb][j] * (1.0f / kMfScale);
+    }
   }
   if (el == 0) {
 #pragma unroll

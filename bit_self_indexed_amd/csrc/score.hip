@@ -6,25 +6,29 @@
 // token is scored by looking up its sub-vector codes and accumulating, without
 // decoding the keys; the top-k tokens are then selected.
 //
-// Three kernels per decode step, all exact:
-//   prep    - one block per (b, h): builds the selection query's table (the
-//             16-entry table of each 4-dim sub-vector, in int32 fixed point so
-//             that a token's 32 look-ups are summed exactly with 3-input integer
-//             adds), the attention tables of the G query heads, their q.mu and
-//             the exact logits of the 64 sinks; then scores a stratified sample
-//             of 3072 candidates (16 contiguous tokens from the middle of each of
-//             192 equal segments) and takes a conservative threshold tau below
-//             the expected k-th score (the whole candidate set when it is small);
-//   score   - the HBM stream: 16-byte code + 4-byte scale per token, one lane per
-//             token, one wave per tile with its loads a step ahead of its
-//             look-ups, 2 KB table in LDS (16-entry look-ups never conflict in
+// Two kernels per decode step, all exact:
+//   score   - leader blocks, one per (b, h), first in the grid: build the
+//             selection query's table (the 16-entry table of each 4-dim
+//             sub-vector, in int32 fixed point so that a token's 32 look-ups
+//             are summed exactly with 3-input integer adds), score a stratified
+//             sample of 2048 candidates (16 contiguous tokens from the middle of
+//             each of 128 equal segments) and publish a conservative threshold
+//             tau below the expected k-th score through a tagged word (the
+//             whole candidate set when it is small); then each scores its head's
+//             last tile.  Tile blocks: the HBM stream, 16-byte code + 4-byte
+//             scale per token, one lane per token, the same table built in LDS
+//             while the loads are in flight (16-entry look-ups never conflict in
 //             the LDS banks); tokens with score >= tau are written, in token
-//             order, to a per-tile slot (no atomics);
-//   select  - one block per (b, h): radix select of the exact k-th largest over
-//             the candidates, then an ordered compaction (ascending positions,
-//             ties to the smaller position).  If fewer than k candidates passed
-//             (tau too high), the block rescans the whole head and selects over
-//             every token, so the result never depends on the sample.
+//             order, to a per-tile slot (no atomics) with the tau used;
+//   select  - one block per (b, h): checks the tiles' thresholds, radix select
+//             of the exact k-th largest over the candidates, then an ordered
+//             compaction (ascending positions, ties to the smaller position).
+//             If fewer than k candidates passed (tau too high), a tile kept its
+//             tokens with another threshold, or the k-th is below tau, the block
+//             rescans the whole head and selects over every token, so the result
+//             never depends on the sample or on timing.  Extra blocks of the
+//             same launch build the attention tables (the G query heads'
+//             look-up tables, q.mu, the exact logits of the 64 sinks).
 #include <hip/hip_ext.h>
 
 
