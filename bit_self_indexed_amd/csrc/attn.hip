@@ -371,21 +371,52 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(
   src.vsk = QV ? vsink + (int64_t)bh * kSink * kD + seg * 8 : nullptr;
 
   // The block's positions (clamped into [0, n_tokens): memory safety only) and
-  // the G attention tables into LDS.
-  {
-    const int e0 = c0 * kAttnChunk, ne = (c_end - c0) * kAttnChunk;
-    for (int i = tid; i < ne; i += 256) {
-      const int e = min(e0 + i, L - 1);
-      const int t = e < kSink ? e : min(max(ib[e - kSink], 0), nt - 1);
-      sidx[i] = paged ? (int)rm.row(b, h, t) : t;
-    }
-    const float4* lsrc = reinterpret_cast<const float4*>(att_lut + hq0 * kLut);
-    float4* dst = reinterpret_cast<float4*>(&lutq[0][0]);
-    for (int i = tid; i < G * kLut / 4; i += 256) dst[i] = lsrc[i];
-  }
+  // the G attention tables into LDS.  Every load of a round is issued before
+  // the first is used (as a load-store loop, each iteration waited for its
+  // load: up to eight round trips before the first chunk): the positions and
+  // the tables, then, for a paged cache, the page ids.
   float qmu[GH];
+  {
+    constexpr int kPer = kAttnMaxCpb * kAttnChunk / 256;  // positions per thread at most
+    constexpr int kLutPer = (G * kLut / 4 + 255) / 256;   // table float4s per thread
+    const int e0 = c0 * kAttnChunk, ne = (c_end - c0) * kAttnChunk;
+    const float4* lsrc = reinterpret_cast<const float4*>(att_lut + hq0 * kLut);
+    float4 lv[kLutPer];  // (unconditional loads at clamped indices: no branch, no scratch)
 #pragma unroll
-  for (int i = 0; i < GH; ++i) qmu[i] = (2 * i + half < G) ? att_qmu[hq0 + 2 * i + half] : 0.0f;
+    for (int u = 0; u < kLutPer; ++u) lv[u] = lsrc[min(tid + 256 * u, G * kLut / 4 - 1)];
+    int tv[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = tid + 256 * u;
+      const int e = min(e0 + i, L - 1);
+      tv[u] = (i < ne && e >= kSink) ? ib[e - kSink] : e;
+    }
+#pragma unroll
+    for (int i = 0; i < GH; ++i) qmu[i] = (2 * i + half < G) ? att_qmu[hq0 + 2 * i + half] : 0.0f;
+    __builtin_amdgcn_sched_barrier(0);  // all of the round's loads are out
+    float4* dst = reinterpret_cast<float4*>(&lutq[0][0]);
+#pragma unroll
+    for (int u = 0; u < kLutPer; ++u)  // (threads past the end rewrite the last entry's value)
+      dst[min(tid + 256 * u, G * kLut / 4 - 1)] = lv[u];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = min(e0 + tid + 256 * u, L - 1);
+      tv[u] = e < kSink ? e : min(max(tv[u], 0), nt - 1);
+    }
+    if (paged) {  // the page ids of all positions, then the rows
+      int pg[kPer];
+#pragma unroll
+      for (int u = 0; u < kPer; ++u)
+        pg[u] = tid + 256 * u < ne ? rm.table[(int64_t)b * rm.pps + (tv[u] >> rm.lg_page)] : 0;
+#pragma unroll
+      for (int u = 0; u < kPer; ++u)
+        tv[u] = (int)((((int64_t)pg[u] * Hkv + h) << rm.lg_page) |
+                      (int64_t)(tv[u] & ((1 << rm.lg_page) - 1)));
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      if (tid + 256 * u < ne) sidx[tid + 256 * u] = tv[u];
+  }
   __syncthreads();
 
   MfLds* mfw = &mfl[mf_path(G, QV) ? wave : 0];

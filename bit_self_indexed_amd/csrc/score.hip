@@ -1106,9 +1106,17 @@ __global__ __launch_bounds__(1024) void select_kernel(
     const int per = (n_chunks + blockDim.x - 1) / blockDim.x;  // <= 2
     const int c0 = tid * per;
     int2 cu[2];
+    // the counts go out first (as ordinary loads the compiler issued them after
+    // the slot loads, and the scan then waited for every one of those)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      cu[j] = chunk_count[(int64_t)bh * n_chunks + min(c0 + j, n_chunks - 1)];
+    for (int j = 0; j < 2; ++j) {
+      const unsigned long long w = __hip_atomic_load(
+          reinterpret_cast<const unsigned long long*>(chunk_count) + (int64_t)bh * n_chunks +
+              min(c0 + j, n_chunks - 1),
+          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      cu[j] = make_int2((int)(uint32_t)w, (int)(uint32_t)(w >> 32));
+    }
+    __builtin_amdgcn_sched_barrier(0);
     {
       const int lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
 #pragma unroll
@@ -1129,7 +1137,7 @@ __global__ __launch_bounds__(1024) void select_kernel(
     bool bad = false;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const bool real = j < per && c0 + j < n_chunks;
+      const bool real = (j < per) & (c0 + j < n_chunks);  // no branch: the load stays first
       cs[j] = real ? cu[j].x : 0;
       bad |= real && (uint32_t)cu[j].y != thb && (uint32_t)cu[j].y != 0xff800000u;
     }
