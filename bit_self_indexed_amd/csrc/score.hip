@@ -706,6 +706,7 @@ __device__ float leader(const ScoreArgs& a, int bh, int* itab, uint32_t* hist, u
     const int64_t base = paged ? 0 : (int64_t)bh * a.rm.capacity;
     const char* cbase = reinterpret_cast<const char*>(a.codes + base * kCodeBytes);
     const char* abase = reinterpret_cast<const char*>(a.alpha + base);
+    uint32_t r[kRows];
 #pragma unroll
     for (int u = 0; u < kRows; ++u) {
       const int i = tid + u * 256;
@@ -715,10 +716,21 @@ __device__ float leader(const ScoreArgs& a, int bh, int* itab, uint32_t* hist, u
         const int64_t seg0 = (int64_t)st * n / ns, seg1 = (int64_t)(st + 1) * n / ns;
         t = kSink + (int)(seg0 + (seg1 - seg0 - kSampleRun) / 2) + (i - st * kSampleRun);
       }
-      t = i < m ? t : kSink;
-      const uint32_t r = paged ? (uint32_t)a.rm.row(b, h, t) : (uint32_t)t;
-      c[u] = *reinterpret_cast<const uint4*>(cbase + (size_t)r * kCodeBytes);
-      al[u] = *reinterpret_cast<const float*>(abase + (size_t)r * 4);
+      r[u] = (uint32_t)(i < m ? t : kSink);
+    }
+    if (paged) {  // every row's page id first (one round trip), then the rows
+      const int lg = a.rm.lg_page;
+      int pg[kRows];
+#pragma unroll
+      for (int u = 0; u < kRows; ++u) pg[u] = a.rm.table[(int64_t)b * a.rm.pps + (r[u] >> lg)];
+#pragma unroll
+      for (int u = 0; u < kRows; ++u)
+        r[u] = (uint32_t)((((int64_t)pg[u] * a.Hkv + h) << lg) | (int64_t)(r[u] & ((1u << lg) - 1)));
+    }
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {
+      c[u] = *reinterpret_cast<const uint4*>(cbase + (size_t)r[u] * kCodeBytes);
+      al[u] = *reinterpret_cast<const float*>(abase + (size_t)r[u] * 4);
     }
   }
   if (tid < a.G * 32) reinterpret_cast<uint2*>(qs)[tid] = qv;
