@@ -64,6 +64,28 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
   return wbase + x - v;
 }
 
+// block_excl_scan and the block-wide OR of one flag per thread, in the same two
+// barriers.  tmp: LDS, >= 32 ints.  (__syncthreads_or reads the block's y and z
+// sizes with a vector load and waits for every load in flight before it.)
+__device__ __forceinline__ int block_excl_scan_or(int v, bool f, int* tmp, int* total, bool* any) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int x = wave_incl_scan(v);
+  const bool wf = __ballot(f) != 0ull;
+  if (lane == 63) {
+    tmp[wave] = x;
+    tmp[16 + wave] = wf ? 1 : 0;
+  }
+  __syncthreads();
+  const int t = lane < nw ? tmp[lane] : 0;
+  *any = __ballot(lane < nw && tmp[16 + lane] != 0) != 0ull;
+  const int ts = wave_incl_scan(t);
+  const int wbase = __builtin_amdgcn_readlane(ts, wave) - __builtin_amdgcn_readlane(t, wave);
+  *total = __builtin_amdgcn_readlane(ts, nw - 1);
+  __syncthreads();  // tmp may be reused as soon as this returns
+  return wbase + x - v;
+}
+
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
   const int r = row_allreduce((int)x, [](int a, int b) { return (int)min((uint32_t)a, (uint32_t)b); });
   const uint32_t a = (uint32_t)__builtin_amdgcn_readlane(r, 0), b = (uint32_t)__builtin_amdgcn_readlane(r, 16);
@@ -1154,7 +1176,8 @@ __global__ __launch_bounds__(1024) void select_kernel(
       bad |= real && (uint32_t)cu[j].y != thb && (uint32_t)cu[j].y != 0xff800000u;
     }
     int total;
-    int pre = block_excl_scan(cs[0] + cs[1], tmp, &total);
+    bool bad_any;
+    int pre = block_excl_scan_or(cs[0] + cs[1], bad, tmp, &total, &bad_any);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       if (j < per && c0 + j < n_chunks) {
@@ -1162,7 +1185,8 @@ __global__ __launch_bounds__(1024) void select_kernel(
         pre += cs[j];
       }
     if (tid == 0) off[n_chunks] = total;
-    any_bad = __syncthreads_or(bad);
+    any_bad = bad_any ? 1 : 0;
+    __syncthreads();  // off
   }
   if (tid == 0) tau_word[bh] = 0ull;  // every thread read it before the barrier
   // An appended token (scored by the leader; the tiles stop before it) is the
