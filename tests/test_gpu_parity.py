@@ -325,6 +325,43 @@ def test_select_list_in_workspace():
     check_rows(out[0, :G], ref, "big_k decode")
 
 
+@pytest.mark.parametrize("stale", ["high", "neg_inf", "zero"])
+def test_stale_threshold_word(stale):
+    """A tagged threshold word left in the caller's workspace (a fresh buffer may
+    hold anything) must not change the selection.  The words lead the workspace,
+    8 bytes per (b, KV head): the tag 0x53494b56 in the upper half, the fp32
+    threshold in the lower; the select kernel clears each one after reading it.
+    Tiles that take the planted word: high, keep nothing (fewer than k
+    candidates: whole-head rescan); neg_inf, keep every token, which the select
+    kernel accepts (a list of all 39936 candidates, past the LDS list: the
+    workspace path); zero, record a threshold other than the one the leader
+    publishes (whole-head rescan).  156 tiles per head, so the select kernel's
+    long-context gather runs too."""
+    w = S.custom("stale", 2, 8, 2, 40000, 3000, n_planted=8, cfg_id=177)
+    say(f"[parity] case=stale_threshold_word {stale}")
+    d = S.draw(w)
+    q = dev_bf16(d["q"])
+    cache = sk.Cache(w.batch, w.n_kv_heads, w.n_tokens, v=dev_bf16(d["V"]))
+    sk.sikv_encode(cache, dev_bf16(d["K"]))
+    first = sk.sikv_score_topk(cache, q, w.top_k).cpu().numpy()  # (sizes the workspace)
+    buf = cache.ws.buf
+    off = (-buf.data_ptr()) % 256
+    words = buf[off:off + 8 * w.batch * w.n_kv_heads].view(torch.int64)
+    assert bool(torch.all(words == 0)), "the previous call left its threshold words set"
+    tau = {"high": 3.0e38, "neg_inf": float("-inf"), "zero": 0.0}[stale]
+    tau_bits = int(np.array([tau], np.float32).view(np.uint32)[0])
+    words.fill_((0x53494B56 << 32) | tau_bits)
+    torch.cuda.synchronize()
+    gi = sk.sikv_score_topk(cache, q, w.top_k).cpu().numpy()
+    assert bool(torch.all(words == 0)), "planted threshold words were not read and cleared"
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            o = oracle_head(d["K"][b, h], w.n_tokens)
+            s = oracle_scores(d["q"], o["codes"], o["alpha"], b, h, w.n_kv_heads, w.n_tokens)
+            check_topk(gi[b, h], s, w.top_k, w.n_tokens, f"stale {stale} topk b={b} h={h}")
+    assert np.array_equal(gi, first)
+
+
 def test_dense_comparator():
     w = S.custom("dense", 2, 8, 2, 3000, 100, n_planted=4, cfg_id=112)
     say("[parity] case=dense_comparator")
