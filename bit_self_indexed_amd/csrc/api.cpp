@@ -92,7 +92,7 @@ bool plan_score(const sikv_cache_desc* c, int n_q_heads, ScorePlan* p) {
   const size_t cap = (size_t)BH * p->n_chunks * p->chunk;
   size_t o = 0;
   p->off_tau = o;  o += align_up((size_t)BH * sizeof(unsigned long long));
-  p->off_bin = o;  o += align_up((size_t)BH * sizeof(float));
+  p->off_bin = o;  o += align_up((size_t)2 * BH * sizeof(float));  // bin scales, then tau
   p->off_cnt = o;  o += align_up((size_t)BH * p->n_chunks * sizeof(int2));
   p->off_ckey = o; o += align_up(cap * sizeof(uint32_t));
   p->off_ct = o;   o += align_up(cap * sizeof(int32_t));

@@ -20,9 +20,10 @@
 //             while the loads are in flight (16-entry look-ups never conflict in
 //             the LDS banks); tokens with score >= tau are written, in token
 //             order, to a per-tile slot (no atomics) with the tau used;
-//   select  - one block per (b, h): checks the tiles' thresholds, radix select
-//             of the exact k-th largest over the candidates, then an ordered
-//             compaction (ascending positions, ties to the smaller position).
+//   select  - two blocks per (b, h), which both check the tiles' thresholds
+//             and find the exact k-th largest over the candidates; each then
+//             writes half of the ordered compaction (ascending positions, ties
+//             to the smaller position).
 //             If fewer than k candidates passed (tau too high), a tile kept its
 //             tokens with another threshold, or the k-th is below tau, the block
 //             rescans the whole head and selects over every token, so the result
@@ -304,14 +305,33 @@ __device__ void block_emit(const uint32_t* keys, const int32_t* pos, int n, int 
 // tile of list entry i is the last one whose list offset off[tile] <= i) plus
 // the offset; entries past the tiles (an appended token) take last_pos.  The
 // tile of the run's first entry comes from a binary search of off[], then only
-// crossings read it again.
-constexpr int kEmitRun = 21;  // longest run: odd and >= kSelectLds / 1024
-static_assert(kEmitRun >= ((kSelectLds / 1024) | 1), "runs of a 1024-thread block");
-__device__ void list_emit(const uint32_t* keys, const uint16_t* ofs, int n, const int* off,
-                          int n_chunks, int chunk, int last_pos, int k, Kth r, int32_t* stage,
-                          int32_t* __restrict__ out, int* tmp) {
-  const int per = ((n + blockDim.x - 1) / blockDim.x) | 1;
-  const int i0 = min(n, (int)threadIdx.x * per), m = min(n - i0, per);  // m <= kEmitRun
+// crossings read it again.  Two blocks share a head's list: block `half`
+// emits entries [lo, hi) of it (the first or the second half), the second
+// block first counting the entries taken before its half.
+constexpr int kEmitRun = 11;  // longest run: odd and >= (kSelectLds / 2) / 1024
+static_assert(kEmitRun >= ((kSelectLds / 2 / 1024) | 1), "runs of a 1024-thread block");
+__device__ void list_emit(const uint32_t* keys, const uint16_t* ofs, int n, int half,
+                          const int* off, int n_chunks, int chunk, int last_pos, int k, Kth r,
+                          int32_t* stage, int32_t* __restrict__ out, int* tmp) {
+  const int mid = n / 2, lo = half ? mid : 0, hi = half ? n : mid;
+  // the entries taken before this half: keys above the k-th, and the first
+  // r.need of the keys equal to it
+  int gt0 = 0, eq0 = 0;
+  if (half) {
+    int g = 0, e = 0;
+    for (int i = threadIdx.x; i < mid; i += blockDim.x) {
+      const uint32_t key = keys[i];
+      g += key > r.key ? 1 : 0;
+      e += key == r.key ? 1 : 0;
+    }
+    int t0;
+    block_excl_scan((g << 16) | e, tmp, &t0);  // n <= kSelectLds < 2^16
+    gt0 = t0 >> 16;
+    eq0 = t0 & 0xffff;
+  }
+  const int nn = hi - lo;
+  const int per = ((nn + blockDim.x - 1) / blockDim.x) | 1;
+  const int i0 = lo + min(nn, (int)threadIdx.x * per), m = min(hi - i0, per);  // m <= kEmitRun
   uint32_t kk[kEmitRun];
   uint16_t oo[kEmitRun];
 #pragma unroll
@@ -331,8 +351,8 @@ __device__ void list_emit(const uint32_t* keys, const uint16_t* ofs, int n, cons
   }
   int tot;
   const int ex = block_excl_scan((gt << 16) | eq, tmp, &tot);  // n <= kSelectLds < 2^16
-  int eq_before = ex & 0xffff;
-  int o = (ex >> 16) + min(eq_before, r.need);
+  int eq_before = eq0 + (ex & 0xffff);
+  int o = gt0 + (ex >> 16) + min(eq_before, r.need);
 #pragma unroll
   for (int j = 0; j < kEmitRun; ++j) {
     bool take = j < m && kk[j] > r.key;
@@ -347,7 +367,10 @@ __device__ void list_emit(const uint32_t* keys, const uint16_t* ofs, int n, cons
     }
   }
   __syncthreads();
-  for (int j = threadIdx.x; j < k; j += blockDim.x) out[j] = stage[j];
+  // this half's outputs: [taken before it, taken up to its end)
+  const int o0 = min(gt0 + min(eq0, r.need), k);
+  const int o1 = min(gt0 + (tot >> 16) + min(eq0 + (tot & 0xffff), r.need), k);
+  for (int j = o0 + (int)threadIdx.x; j < o1; j += blockDim.x) out[j] = stage[j];
 }
 
 // Copies the selection table of one head from global memory into LDS (2 KB).
@@ -784,6 +807,7 @@ __device__ float leader(const ScoreArgs& a, int bh, int* itab, uint32_t* hist, u
     // to an upper estimate of the k-th score (higher scores share the top bin)
     const float span = th_hi - th;
     a.bin_scale[bh] = sample && span > 0.0f ? 2048.0f / span : 0.0f;
+    a.bin_scale[a.n_heads + bh] = th;  // the select kernel's copy, never cleared
     __hip_atomic_store(a.tau_word + bh, ((unsigned long long)kTauTag << 32) | __float_as_uint(th),
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -1105,25 +1129,32 @@ __global__ __launch_bounds__(1024) void select_kernel(
   __shared__ int tmp[32];
   __shared__ uint32_t mm[32];
   __shared__ int scount;
-  if ((int)blockIdx.x >= ta.n_heads) {  // the second half of the grid: attention tables
-    if (threadIdx.x < 256) attention_tables(ta, blockIdx.x - ta.n_heads);
+  if ((int)blockIdx.x >= 2 * ta.n_heads) {  // the last third of the grid: attention tables
+    if (threadIdx.x < 256) attention_tables(ta, blockIdx.x - 2 * ta.n_heads);
     return;
   }
-  const int bh = blockIdx.x;
+  // Two blocks per head, which build the same list and find the same k-th;
+  // each then emits half of the ordered selection.  The rare paths (the
+  // whole-head rescan, the list in the workspace) are the first block's alone.
+  const int bh = blockIdx.x >> 1, half = blockIdx.x & 1;
   const int tid = threadIdx.x;
   const int nt = seq_len(seq_lens, bh / Hkv, n_tokens);
   const int n = nt - kSink;
   const int top_k = seq_topk(top_k_max, nt);  // this sequence's k; the rest of its row is -1
-  // The threshold the head's leader published (read here by every thread, then
-  // cleared below for the next call).
-  const uint32_t thb = (uint32_t)tau_word[bh];
+  // The threshold the head's leader published, from its untagged copy (never
+  // cleared, so both blocks read the same value); the first block clears the
+  // tagged word for the next call's tiles.
+  const uint32_t thb = __float_as_uint(bin_scale[ta.n_heads + bh]);
   int32_t* out = idx + (int64_t)bh * top_k_max;
-  for (int j = top_k + tid; j < top_k_max; j += blockDim.x) out[j] = -1;
   if (top_k >= n) {  // every candidate is kept
-    if (tid == 0) tau_word[bh] = 0ull;  // no thread of this branch reads it
-    for (int j = tid; j < top_k; j += blockDim.x) out[j] = kSink + j;
+    if (half == 0) {
+      if (tid == 0) tau_word[bh] = 0ull;
+      for (int j = tid; j < top_k_max; j += blockDim.x) out[j] = j < top_k ? kSink + j : -1;
+    }
     return;
   }
+  if (half == 0)
+    for (int j = top_k + tid; j < top_k_max; j += blockDim.x) out[j] = -1;
   for (int i = tid; i < 2048; i += blockDim.x) hist[i] = 0u;  // published by the scan's barriers
   // Tile counts -> offsets of each tile's candidates in the ordered list.  The
   // counts are loaded first, then the first kPreG * 64 slots of each wave's
@@ -1188,7 +1219,7 @@ __global__ __launch_bounds__(1024) void select_kernel(
     any_bad = bad_any ? 1 : 0;
     __syncthreads();  // off
   }
-  if (tid == 0) tau_word[bh] = 0ull;  // every thread read it before the barrier
+  if (half == 0 && tid == 0) tau_word[bh] = 0ull;  // every tile read it in the score kernel
   // An appended token (scored by the leader; the tiles stop before it) is the
   // head's last position: it follows every tile's candidates in the list.
   const int Ct = off[n_chunks];
@@ -1197,6 +1228,7 @@ __global__ __launch_bounds__(1024) void select_kernel(
   const bool ap = app_key != nullptr && akey >= thk;
   const int C = Ct + (ap ? 1 : 0);
   if (C < top_k || any_bad) {  // the LDS list is unused: it holds the table
+    if (half) return;
     select_exact_head(codes, alpha, rm, Hkv, bh, n, top_k, sel_lut, sel_inv, comp_key + cbase,
                       comp_t + cbase, reinterpret_cast<int*>(lkey), hist, tmp, sub, &scount, mm,
                       out);
@@ -1292,6 +1324,7 @@ __global__ __launch_bounds__(1024) void select_kernel(
   };
 
   if (!in_lds) {
+    if (half) return;
     if (!select_workspace(cand_key + cbase, cand_t + cbase, chunk, n_chunks, off, C, top_k, ap,
                           akey, nt - 1, thk, comp_key + cbase, comp_t + cbase, hist, tmp, sub,
                           &scount, mm, out)) {
@@ -1381,13 +1414,14 @@ __global__ __launch_bounds__(1024) void select_kernel(
     // that gave up waiting kept more); its k-th is the head's k-th only if it
     // is not below that threshold (else some of the top k may be missing).
     if (r.key < thk) {
+      if (half) return;
       __syncthreads();  // the LDS list is reused by the exact path
       select_exact_head(codes, alpha, rm, Hkv, bh, n, top_k, sel_lut, sel_inv, comp_key + cbase,
                         comp_t + cbase, reinterpret_cast<int*>(lkey), hist, tmp, sub, &scount,
                         mm, out);
       return;
     }
-    list_emit(lkey, lofs, C, off, n_chunks, chunk, nt - 1, top_k, r,
+    list_emit(lkey, lofs, C, half, off, n_chunks, chunk, nt - 1, top_k, r,
               reinterpret_cast<int32_t*>(lkey), out, tmp);
   }
 }
@@ -1429,7 +1463,7 @@ hipError_t launch_select(int B, int Hkv, const uint8_t* codes, const float* alph
                          const uint32_t* app_key, uint32_t* comp_key, int32_t* comp_t,
                          int32_t* idx, const ScoreArgs& ta, const Launch& s) {
   if (n_chunks > kMaxChunks) return hipErrorInvalidValue;
-  return launch_k(KID_SELECT, select_kernel, dim3(2 * B * Hkv), dim3(1024), 0, s, codes, alpha,
+  return launch_k(KID_SELECT, select_kernel, dim3(3 * B * Hkv), dim3(1024), 0, s, codes, alpha,
                   rm, n_tokens, Hkv, seq_lens, sel_lut, sel_inv, top_k, chunk, n_chunks,
                   cand_key, cand_t,
                   chunk_count, tau_word, bin_scale, app_key, comp_key, comp_t, idx, ta);

@@ -401,7 +401,7 @@ struct ScoreArgs {
   int64_t vnsb, vnsh;
   // workspace
   unsigned long long* tau_word;  // [B*Hkv]: published threshold (tag << 32 | tau bits)
-  float* bin_scale;              // [B*Hkv]
+  float* bin_scale;              // [2][B*Hkv]: the select kernel's bin scale, then tau (untagged)
   int* sel_lut;                  // [B*Hkv][512]
   float* sel_inv;                // [B*Hkv]
   float* att_lut;                // [B*Hq][512]
