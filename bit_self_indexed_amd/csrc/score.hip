@@ -20,10 +20,11 @@
 //             while the loads are in flight (16-entry look-ups never conflict in
 //             the LDS banks); tokens with score >= tau are written, in token
 //             order, to a per-tile slot (no atomics) with the tau used;
-//   select  - two blocks per (b, h), which both check the tiles' thresholds
-//             and find the exact k-th largest over the candidates; each then
-//             writes half of the ordered compaction (ascending positions, ties
-//             to the smaller position).
+//   select  - up to four blocks per (b, h) (as many as one block per CU
+//             allows), which all check the tiles' thresholds and find the
+//             exact k-th largest over the candidates; each then writes its
+//             part of the ordered compaction (ascending positions, ties to
+//             the smaller position).
 //             If fewer than k candidates passed (tau too high), a tile kept its
 //             tokens with another threshold, or the k-th is below tau, the block
 //             rescans the whole head and selects over every token, so the result
@@ -45,6 +46,7 @@ constexpr int kBandBins = 1024;    // equal-width bins of the sample's band
 constexpr int kSelectLds = 20480;  // candidates kept in LDS by select (keys + 16-bit offsets)
 constexpr int kMaxChunks = 2048;
 constexpr int kSubMax = 1024;
+constexpr int kSelectBlocks = 256;  // select grid target: one 1024-thread block per CU
 constexpr int kGatherRun = 10;  // select: candidates a thread loads together past the first tiles
 
 // ------------------------------------------------------------------ block helpers
@@ -305,21 +307,21 @@ __device__ void block_emit(const uint32_t* keys, const int32_t* pos, int n, int 
 // tile of list entry i is the last one whose list offset off[tile] <= i) plus
 // the offset; entries past the tiles (an appended token) take last_pos.  The
 // tile of the run's first entry comes from a binary search of off[], then only
-// crossings read it again.  Two blocks share a head's list: block `half`
-// emits entries [lo, hi) of it (the first or the second half), the second
-// block first counting the entries taken before its half.
-constexpr int kEmitRun = 11;  // longest run: odd and >= (kSelectLds / 2) / 1024
-static_assert(kEmitRun >= ((kSelectLds / 2 / 1024) | 1), "runs of a 1024-thread block");
-__device__ void list_emit(const uint32_t* keys, const uint16_t* ofs, int n, int half,
-                          const int* off, int n_chunks, int chunk, int last_pos, int k, Kth r,
-                          int32_t* stage, int32_t* __restrict__ out, int* tmp) {
-  const int mid = n / 2, lo = half ? mid : 0, hi = half ? n : mid;
-  // the entries taken before this half: keys above the k-th, and the first
+// crossings read it again.  n_parts blocks share a head's list: block `part`
+// emits entries [lo, hi) of it, first counting the entries taken before them.
+// kEmitRun: the longest run, odd and >= (kSelectLds / n_parts) / 1024.
+template <int kEmitRun>
+__device__ void list_emit(const uint32_t* keys, const uint16_t* ofs, int n, int part,
+                          int n_parts, const int* off, int n_chunks, int chunk, int last_pos,
+                          int k, Kth r, int32_t* stage, int32_t* __restrict__ out, int* tmp) {
+  const int lo = (int)((int64_t)n * part / n_parts);
+  const int hi = (int)((int64_t)n * (part + 1) / n_parts);
+  // the entries taken before this part: keys above the k-th, and the first
   // r.need of the keys equal to it
   int gt0 = 0, eq0 = 0;
-  if (half) {
+  if (part > 0) {
     int g = 0, e = 0;
-    for (int i = threadIdx.x; i < mid; i += blockDim.x) {
+    for (int i = threadIdx.x; i < lo; i += blockDim.x) {
       const uint32_t key = keys[i];
       g += key > r.key ? 1 : 0;
       e += key == r.key ? 1 : 0;
@@ -367,7 +369,7 @@ __device__ void list_emit(const uint32_t* keys, const uint16_t* ofs, int n, int 
     }
   }
   __syncthreads();
-  // this half's outputs: [taken before it, taken up to its end)
+  // this part's outputs: [taken before it, taken up to its end)
   const int o0 = min(gt0 + min(eq0, r.need), k);
   const int o1 = min(gt0 + (tot >> 16) + min(eq0 + (tot & 0xffff), r.need), k);
   for (int j = o0 + (int)threadIdx.x; j < o1; j += blockDim.x) out[j] = stage[j];
@@ -1036,6 +1038,7 @@ __device__ __forceinline__ void count_bin(uint32_t* hist, bool valid, int bin) {
 
 // Fewer than k candidates passed: rescore the whole head with the score
 // kernel's table and arithmetic, in order, and select over all of it.
+template <int P>  // one copy per select kernel (one shared by several cost them SGPR spills)
 __device__ __noinline__ void select_exact_head(
     const uint8_t* __restrict__ codes, const float* __restrict__ alpha, RowMap rm, int Hkv,
     int bh, int n, int top_k, const int* __restrict__ sel_lut, const float* __restrict__ sel_inv,
@@ -1065,6 +1068,7 @@ __device__ __noinline__ void select_exact_head(
 // More candidates than the LDS list holds: the ordered list goes to the
 // workspace (tile by tile, wave w taking tiles w, w + 16, ...; an appended
 // token last) and radix rounds select over it.
+template <int P>
 __device__ __noinline__ bool select_workspace(
     const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_t, int chunk,
     int n_chunks, const int* off, int C, int top_k, bool extra, uint32_t extra_key,
@@ -1099,6 +1103,7 @@ __device__ __noinline__ bool select_workspace(
 
 // The k-th's bin holds too many keys (e.g. no usable bin scale): radix rounds
 // over the whole LDS list.
+template <int P>
 __device__ __noinline__ Kth select_degenerate(const uint32_t* lkey, int C, int top_k,
                                               uint32_t* hist, int* tmp, uint32_t* sub,
                                               int* scount, uint32_t* mm) {
@@ -1111,6 +1116,7 @@ __device__ __noinline__ Kth select_degenerate(const uint32_t* lkey, int C, int t
   return block_kth(lkey, C, top_k, lo, hi, hist, tmp, sub, scount);
 }
 
+template <int kParts>
 __global__ __launch_bounds__(1024) void select_kernel(
     const uint8_t* __restrict__ codes, const float* __restrict__ alpha, RowMap rm,
     int n_tokens, int Hkv, const int32_t* __restrict__ seq_lens,
@@ -1121,6 +1127,7 @@ __global__ __launch_bounds__(1024) void select_kernel(
     const float* __restrict__ bin_scale, const uint32_t* __restrict__ app_key,
     uint32_t* __restrict__ comp_key, int32_t* __restrict__ comp_t, int32_t* __restrict__ idx,
     ScoreArgs ta) {
+  constexpr int n_parts = kParts;
   __shared__ int off[kMaxChunks + 1];
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t lkey[kSelectLds];
@@ -1129,14 +1136,15 @@ __global__ __launch_bounds__(1024) void select_kernel(
   __shared__ int tmp[32];
   __shared__ uint32_t mm[32];
   __shared__ int scount;
-  if ((int)blockIdx.x >= 2 * ta.n_heads) {  // the last third of the grid: attention tables
-    if (threadIdx.x < 256) attention_tables(ta, blockIdx.x - 2 * ta.n_heads);
+  if ((int)blockIdx.x >= n_parts * ta.n_heads) {  // the grid's tail: attention tables
+    if (threadIdx.x < 256) attention_tables(ta, blockIdx.x - n_parts * ta.n_heads);
     return;
   }
-  // Two blocks per head, which build the same list and find the same k-th;
-  // each then emits half of the ordered selection.  The rare paths (the
-  // whole-head rescan, the list in the workspace) are the first block's alone.
-  const int bh = blockIdx.x >> 1, half = blockIdx.x & 1;
+  // n_parts (1..4) blocks per head, which build the same list and find the
+  // same k-th; each then emits its part of the ordered selection.  The rare
+  // paths (the whole-head rescan, the list in the workspace) are the first
+  // block's alone.
+  const int bh = blockIdx.x / n_parts, part = blockIdx.x % n_parts;
   const int tid = threadIdx.x;
   const int nt = seq_len(seq_lens, bh / Hkv, n_tokens);
   const int n = nt - kSink;
@@ -1147,13 +1155,13 @@ __global__ __launch_bounds__(1024) void select_kernel(
   const uint32_t thb = __float_as_uint(bin_scale[ta.n_heads + bh]);
   int32_t* out = idx + (int64_t)bh * top_k_max;
   if (top_k >= n) {  // every candidate is kept
-    if (half == 0) {
+    if (part == 0) {
       if (tid == 0) tau_word[bh] = 0ull;
       for (int j = tid; j < top_k_max; j += blockDim.x) out[j] = j < top_k ? kSink + j : -1;
     }
     return;
   }
-  if (half == 0)
+  if (part == 0)
     for (int j = top_k + tid; j < top_k_max; j += blockDim.x) out[j] = -1;
   for (int i = tid; i < 2048; i += blockDim.x) hist[i] = 0u;  // published by the scan's barriers
   // Tile counts -> offsets of each tile's candidates in the ordered list.  The
@@ -1219,7 +1227,7 @@ __global__ __launch_bounds__(1024) void select_kernel(
     any_bad = bad_any ? 1 : 0;
     __syncthreads();  // off
   }
-  if (half == 0 && tid == 0) tau_word[bh] = 0ull;  // every tile read it in the score kernel
+  if (part == 0 && tid == 0) tau_word[bh] = 0ull;  // every tile read it in the score kernel
   // An appended token (scored by the leader; the tiles stop before it) is the
   // head's last position: it follows every tile's candidates in the list.
   const int Ct = off[n_chunks];
@@ -1228,10 +1236,11 @@ __global__ __launch_bounds__(1024) void select_kernel(
   const bool ap = app_key != nullptr && akey >= thk;
   const int C = Ct + (ap ? 1 : 0);
   if (C < top_k || any_bad) {  // the LDS list is unused: it holds the table
-    if (half) return;
-    select_exact_head(codes, alpha, rm, Hkv, bh, n, top_k, sel_lut, sel_inv, comp_key + cbase,
-                      comp_t + cbase, reinterpret_cast<int*>(lkey), hist, tmp, sub, &scount, mm,
-                      out);
+    if (part) return;
+    select_exact_head<kParts>(codes, alpha, rm, Hkv, bh, n, top_k, sel_lut, sel_inv,
+                              comp_key + cbase, comp_t + cbase,
+                              reinterpret_cast<int*>(lkey), hist, tmp, sub, &scount, mm,
+                              out);
     return;
   }
   // Gather the candidates into one ordered list.  Wave w copies tiles w, w+nw,
@@ -1324,14 +1333,14 @@ __global__ __launch_bounds__(1024) void select_kernel(
   };
 
   if (!in_lds) {
-    if (half) return;
-    if (!select_workspace(cand_key + cbase, cand_t + cbase, chunk, n_chunks, off, C, top_k, ap,
-                          akey, nt - 1, thk, comp_key + cbase, comp_t + cbase, hist, tmp, sub,
-                          &scount, mm, out)) {
+    if (part) return;
+    if (!select_workspace<kParts>(cand_key + cbase, cand_t + cbase, chunk, n_chunks, off, C,
+                                  top_k, ap, akey, nt - 1, thk, comp_key + cbase,
+                                  comp_t + cbase, hist, tmp, sub, &scount, mm, out)) {
       __syncthreads();
-      select_exact_head(codes, alpha, rm, Hkv, bh, n, top_k, sel_lut, sel_inv, comp_key + cbase,
-                        comp_t + cbase, reinterpret_cast<int*>(lkey), hist, tmp, sub, &scount,
-                        mm, out);
+      select_exact_head<kParts>(codes, alpha, rm, Hkv, bh, n, top_k, sel_lut, sel_inv,
+                                comp_key + cbase, comp_t + cbase,
+                                reinterpret_cast<int*>(lkey), hist, tmp, sub, &scount, mm, out);
     }
     return;
   }
@@ -1408,21 +1417,24 @@ __global__ __launch_bounds__(1024) void select_kernel(
         r = Kth{rs.key, rb.above + rs.above, rs.need};
       }
     } else {  // degenerate spread (e.g. no usable bin scale): radix over the whole list
-      r = select_degenerate(lkey, C, top_k, hist, tmp, sub, &scount, mm);
+      r = select_degenerate<kParts>(lkey, C, top_k, hist, tmp, sub, &scount, mm);
     }
     // The list holds every token at or above the published threshold (tiles
     // that gave up waiting kept more); its k-th is the head's k-th only if it
     // is not below that threshold (else some of the top k may be missing).
     if (r.key < thk) {
-      if (half) return;
+      if (part) return;
       __syncthreads();  // the LDS list is reused by the exact path
-      select_exact_head(codes, alpha, rm, Hkv, bh, n, top_k, sel_lut, sel_inv, comp_key + cbase,
-                        comp_t + cbase, reinterpret_cast<int*>(lkey), hist, tmp, sub, &scount,
-                        mm, out);
+      select_exact_head<kParts>(codes, alpha, rm, Hkv, bh, n, top_k, sel_lut, sel_inv,
+                                comp_key + cbase, comp_t + cbase,
+                                reinterpret_cast<int*>(lkey), hist, tmp, sub, &scount, mm, out);
       return;
     }
-    list_emit(lkey, lofs, C, half, off, n_chunks, chunk, nt - 1, top_k, r,
-              reinterpret_cast<int32_t*>(lkey), out, tmp);
+    int32_t* stage = reinterpret_cast<int32_t*>(lkey);
+    // runs of at most (kSelectLds / n_parts) / 1024 entries, odd
+    constexpr int kRun = (((kSelectLds + n_parts - 1) / n_parts + 1023) / 1024) | 1;
+    list_emit<kRun>(lkey, lofs, C, part, n_parts, off, n_chunks, chunk, nt - 1, top_k, r, stage,
+                    out, tmp);
   }
 }
 
@@ -1463,10 +1475,20 @@ hipError_t launch_select(int B, int Hkv, const uint8_t* codes, const float* alph
                          const uint32_t* app_key, uint32_t* comp_key, int32_t* comp_t,
                          int32_t* idx, const ScoreArgs& ta, const Launch& s) {
   if (n_chunks > kMaxChunks) return hipErrorInvalidValue;
-  return launch_k(KID_SELECT, select_kernel, dim3(3 * B * Hkv), dim3(1024), 0, s, codes, alpha,
-                  rm, n_tokens, Hkv, seq_lens, sel_lut, sel_inv, top_k, chunk, n_chunks,
-                  cand_key, cand_t,
-                  chunk_count, tau_word, bin_scale, app_key, comp_key, comp_t, idx, ta);
+  // Blocks per head: up to four, while the grid (plus one block per head for
+  // the attention tables) stays within one 1024-thread block per CU.
+  int n_parts = 4;
+  while (n_parts > 1 && (int64_t)(n_parts + 1) * B * Hkv > kSelectBlocks) --n_parts;
+#define SIKV_SELECT(P)                                                                         \
+  launch_k(KID_SELECT, select_kernel<P>, dim3((P + 1) * B * Hkv), dim3(1024), 0, s, codes, alpha, \
+           rm, n_tokens, Hkv, seq_lens, sel_lut, sel_inv, top_k, chunk, n_chunks, cand_key,     \
+           cand_t, chunk_count, tau_word, bin_scale, app_key, comp_key, comp_t, idx, ta)
+  const hipError_t e = n_parts == 4   ? SIKV_SELECT(4)
+                       : n_parts == 3 ? SIKV_SELECT(3)
+                       : n_parts == 2 ? SIKV_SELECT(2)
+                                      : SIKV_SELECT(1);
+#undef SIKV_SELECT
+  return e;
 }
 
 }  // namespace sikv

@@ -325,6 +325,28 @@ def test_select_list_in_workspace():
     check_rows(out[0, :G], ref, "big_k decode")
 
 
+@pytest.mark.parametrize("B,Hkv,parts", [(2, 32, 3), (10, 8, 2), (1, 16, 4), (11, 8, 1)],
+                         ids=["3_parts", "2_parts", "4_parts", "1_part"])
+def test_select_parts(B, Hkv, parts):
+    """The select kernel splits a head's ordered emit over up to four blocks, as
+    many as keep its grid (plus one table block per head) within 256 blocks:
+    64 heads take 3 parts, 80 take 2, 16 take 4, 88 take 1.  Every head's
+    selection must equal the exact whole-head path's and follow the oracle."""
+    w = S.custom(f"parts{parts}", B, Hkv, Hkv, 12000, 1100, n_planted=8, cfg_id=230 + parts)
+    say(f"[parity] case=select_parts B={B} Hkv={Hkv} parts={parts}")
+    d = S.draw(w)
+    q = dev_bf16(d["q"])
+    cache = sk.Cache(w.batch, w.n_kv_heads, w.n_tokens, v=dev_bf16(d["V"]))
+    sk.sikv_encode(cache, dev_bf16(d["K"]))
+    gi = sk.sikv_score_topk(cache, q, w.top_k).cpu().numpy()
+    ge = sk.sikv_score_topk(cache, q, w.top_k, exact_select=True).cpu().numpy()
+    assert np.array_equal(gi, ge)
+    for b, h in [(0, 0), (B - 1, Hkv - 1), (B // 2, Hkv // 2)]:
+        o = oracle_head(d["K"][b, h], w.n_tokens)
+        s = oracle_scores(d["q"], o["codes"], o["alpha"], b, h, w.n_kv_heads, w.n_tokens)
+        check_topk(gi[b, h], s, w.top_k, w.n_tokens, f"parts {parts} topk b={b} h={h}")
+
+
 @pytest.mark.parametrize("stale", ["high", "neg_inf", "zero"])
 def test_stale_threshold_word(stale):
     """A tagged threshold word left in the caller's workspace (a fresh buffer may
