@@ -347,6 +347,46 @@ def test_select_parts(B, Hkv, parts):
         check_topk(gi[b, h], s, w.top_k, w.n_tokens, f"parts {parts} topk b={b} h={h}")
 
 
+@pytest.mark.parametrize("n_tied", [40, 100])
+def test_tied_keys_at_the_kth(n_tied):
+    """n_tied tokens share the key row of the token whose score is the k-th
+    largest, so the k-th's histogram bin holds about n_tied keys (40: ranked by
+    one wave; 100: more than its 64 lanes, by radix rounds).  The selection takes
+    the tied tokens with the smallest positions first, like the oracle's, and
+    equals the exact whole-head path's."""
+    w = S.custom(f"tied{n_tied}", 1, 4, 1, 9000, 600, n_planted=0, cfg_id=240 + n_tied)
+    say(f"[parity] case=tied_keys_at_the_kth n_tied={n_tied}")
+    d = S.draw(w)
+    K = d["K"].copy()
+    N, k = w.n_tokens, w.top_k
+    o = oracle_head(K[0, 0], N)
+    s = oracle_scores(d["q"], o["codes"], o["alpha"], 0, 0, 1, N)
+    t_k = 64 + int(np.argsort(-s, kind="stable")[k - 1])
+    rng = np.random.default_rng(7 + n_tied)
+    others = rng.choice(np.setdiff1d(np.arange(64, N), [t_k]), n_tied - 1, replace=False)
+    K[0, 0, others] = K[0, 0, t_k]
+    o = oracle_head(K[0, 0], N)
+    s = oracle_scores(d["q"], o["codes"], o["alpha"], 0, 0, 1, N)
+    # (the copies move the channel mean a little: take k so that the tied
+    # tokens straddle the k-th rank)
+    s_tie = s[t_k - 64]
+    tied = np.nonzero(s == s_tie)[0] + 64
+    assert len(tied) >= n_tied
+    k = int((s > s_tie).sum()) + n_tied // 2
+    q = dev_bf16(d["q"])
+    cache = sk.Cache(w.batch, w.n_kv_heads, N, v=dev_bf16(d["V"]))
+    sk.sikv_encode(cache, dev_bf16(K))
+    gi = sk.sikv_score_topk(cache, q, k).cpu().numpy()[0, 0]
+    ge = sk.sikv_score_topk(cache, q, k, exact_select=True).cpu().numpy()[0, 0]
+    assert np.array_equal(gi, ge)
+    check_topk(gi, s, k, N, f"tied {n_tied}")
+    # the tie rule: of the tied tokens, exactly the smallest positions are taken
+    ref = O.select_topk(s, k)
+    assert np.array_equal(np.intersect1d(gi, tied), np.intersect1d(ref, tied))
+    taken = np.intersect1d(gi, tied)
+    assert len(taken) == n_tied // 2 and np.array_equal(taken, tied[:len(taken)])
+
+
 @pytest.mark.parametrize("stale", ["high", "neg_inf", "zero"])
 def test_stale_threshold_word(stale):
     """A tagged threshold word left in the caller's workspace (a fresh buffer may
