@@ -22,7 +22,10 @@ from . import _abi
 
 HEAD_DIM = 128
 N_SINK = 64
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsikv.so")
+# SIKV_LIBRARY: another build of the same library to load instead (a host-side
+# sanitised one, say); by default the in-tree libsikv.so.
+LIB_PATH = os.environ.get("SIKV_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libsikv.so")
 
 OP_ENCODE, OP_SCORE_TOPK, OP_SPARSE_ATTN, OP_DECODE_STEP, OP_KMEANS = 0, 1, 2, 3, 4
 FLAG_EXACT_SELECT = _abi.FLAG_EXACT_SELECT
