@@ -1150,8 +1150,8 @@ __global__ __launch_bounds__(1024) void select_kernel(
   const int n = nt - kSink;
   const int top_k = seq_topk(top_k_max, nt);  // this sequence's k; the rest of its row is -1
   // The threshold the head's leader published, from its untagged copy (never
-  // cleared, so both blocks read the same value); the first block clears the
-  // tagged word for the next call's tiles.
+  // cleared, so all of the head's blocks read the same value); the first block
+  // clears the tagged word for the next call's tiles.
   const uint32_t thb = __float_as_uint(bin_scale[ta.n_heads + bh]);
   int32_t* out = idx + (int64_t)bh * top_k_max;
   if (top_k >= n) {  // every candidate is kept
