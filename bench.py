@@ -235,6 +235,11 @@ COUNTER_RATIOS = {
                           "TCC_EA0_RDREQ_128B_sum: bytes the L2 requested from memory, by size",
                           lambda c: 32 * c["TCC_EA0_RDREQ_32B_sum"] + 64 * c["TCC_EA0_RDREQ_64B_sum"]
                           + 128 * c["TCC_EA0_RDREQ_128B_sum"]),
+    "mfma_busy_frac": ("SQ_VALU_MFMA_BUSY_CYCLES / (1024 * GRBM_GUI_ACTIVE / 8): share of the "
+                       "SIMDs' cycles with the matrix core busy",
+                       lambda c: c["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * c["GRBM_GUI_ACTIVE"] / 8)),
+    "mfma_f16_flop": ("512 * SQ_INSTS_VALU_MFMA_MOPS_F16: fp16 matrix-core flops",
+                      lambda c: 512 * c["SQ_INSTS_VALU_MFMA_MOPS_F16"]),
 }
 
 
