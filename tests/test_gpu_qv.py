@@ -146,3 +146,47 @@ def test_quantised_value_fused_append():
                                          vq=(oqa[b, h], osza[b, h]))
                 got = res[1][3].view(np.float32)[b, h * G:(h + 1) * G]
                 check_rows(got, ref, f"{w.name} out b={b} h={h}")
+
+
+GROUPS = [(g, qv) for g in range(1, 9) for qv in (False, True)]
+
+
+@pytest.mark.parametrize("G,quant_v", GROUPS,
+                         ids=[f"g{g}_{'2bit' if qv else 'bf16'}" for g, qv in GROUPS])
+def test_every_group_size(G, quant_v):
+    """Every query-group size the attention kernel is built for (1 to 8 query
+    heads per KV head), with either value layout: attention on the oracle's
+    selection and the decode step, against the oracle."""
+    w = S.custom(f"grp{G}", 2, 2 * G, 2, 2600, 257, n_planted=4, cfg_id=250 + 2 * G + quant_v)
+    say(f"[qv] case=group G={G} quant_v={quant_v} B={w.batch} Hq={w.n_q_heads} N={w.n_tokens}")
+    d = S.draw(w)
+    N = w.n_tokens
+    K, V, q = dev_bf16(d["K"]), dev_bf16(d["V"]), dev_bf16(d["q"])
+    if quant_v:
+        cache = sk.Cache(w.batch, w.n_kv_heads, N, quant_v=True)
+        sk.sikv_encode(cache, K)
+        sk.sikv_encode_v(cache, V)
+        vq = O.quantize_v(d["V"])
+    else:
+        cache = sk.Cache(w.batch, w.n_kv_heads, N, v=V)
+        sk.sikv_encode(cache, K)
+    oc = [[oracle_head(d["K"][b, h], N) for h in range(w.n_kv_heads)] for b in range(w.batch)]
+    oidx = np.zeros((w.batch, w.n_kv_heads, w.top_k), np.int32)
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            s = oracle_scores(d["q"], oc[b][h]["codes"], oc[b][h]["alpha"], b, h, w.n_kv_heads, N)
+            oidx[b, h] = O.select_topk(s, w.top_k)
+    out = sk.sikv_sparse_attn(cache, q, torch.from_numpy(oidx).cuda(), SM).cpu().numpy()
+    idx_out = torch.empty((w.batch, w.n_kv_heads, w.top_k), dtype=torch.int32, device="cuda")
+    out2 = sk.sikv_decode_step(cache, q, w.top_k, SM, idx_out=idx_out).cpu().numpy()
+    di = idx_out.cpu().numpy()
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            o = oc[b][h]
+            s = oracle_scores(d["q"], o["codes"], o["alpha"], b, h, w.n_kv_heads, N)
+            check_topk(di[b, h], s, w.top_k, N, f"G={G} topk b={b} h={h}")
+            vkw = {"vq": (vq[0][b, h], vq[1][b, h])} if quant_v else {}
+            for sel, res, what in ((oidx[b, h], out, "attn"), (di[b, h], out2, "decode")):
+                ref = O.sparse_attention(d["q"][b, h * G:(h + 1) * G], sel, o["k_sink"],
+                                         o["codes"], o["alpha"], o["mu"], d["V"][b, h], SM, **vkw)
+                check_rows(res[b, h * G:(h + 1) * G], ref, f"G={G} {what} b={b} h={h}")
