@@ -193,37 +193,42 @@ __global__ __launch_bounds__(256) void codes_kernel(const uint16_t* __restrict__
   }
 }
 
-// Value codes: one block per (128-row tile, b*h); 16 lanes per row, 8 rows per
-// thread (quantize_vrow16); lane pairs write one code word, group leaders the
-// (scale, zero) word; rows below 64 are also kept whole in v_sink.
+// Value codes: one block per (128-row tile, b*h); 4 lanes per row, each with
+// one 32-channel group (quantize_vgroup32), so that a group's scale and
+// thresholds are made once per lane and no lane exchanges anything; thread
+// (rs, g) takes rows rs and rs + 64 of the tile, all of their loads issued
+// first.  Each lane writes its group's 8 code bytes and (scale, zero) word;
+// rows below 64 are also kept whole in v_sink.
 __global__ __launch_bounds__(256) void vcodes_kernel(const uint16_t* __restrict__ v, int64_t sb,
                                                      int64_t sh, int64_t st, int Hkv, int t_begin,
                                                      int t_end, RowMap rm,
                                                      uint8_t* __restrict__ vrec,
                                                      uint16_t* __restrict__ v_sink) {
   const int bh = blockIdx.y, b = bh / Hkv, h = bh - b * Hkv;
-  const int tid = threadIdx.x, cg = tid & 15, rs = tid >> 4;
+  const int tid = threadIdx.x, g = tid & 3, rs = tid >> 2;
   const int tb = t_begin + blockIdx.x * 128;
-  const uint16_t* base = v + (int64_t)b * sb + (int64_t)h * sh + cg * 8;
-  uint4 w[8];
+  const uint16_t* base = v + (int64_t)b * sb + (int64_t)h * sh + g * 32;
+  uint4 w[2][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int t = tb + i * 16 + rs;
-    w[i] = (t < t_end) ? *reinterpret_cast<const uint4*>(base + (int64_t)(t - t_begin) * st)
-                       : make_uint4(0u, 0u, 0u, 0u);
+  for (int i = 0; i < 2; ++i) {
+    const int t = tb + i * 64 + rs;
+    const uint4* p = reinterpret_cast<const uint4*>(base + (int64_t)(t - t_begin) * st);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) w[i][u] = (t < t_end) ? p[u] : make_uint4(0u, 0u, 0u, 0u);
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int t = tb + i * 16 + rs;
-    const VRowCode rc = quantize_vrow16(w[i]);
-    const uint32_t pair = rc.bits | (__shfl_down(rc.bits, 1, 16) << 16);
+  for (int i = 0; i < 2; ++i) {
+    const int t = tb + i * 64 + rs;
+    const VGroupCode gc = quantize_vgroup32(w[i]);
     if (t < t_end) {
-      const int64_t row = rm.row(b, h, t);
-      uint8_t* rec = vrec + row * kVRecBytes;
-      if ((cg & 1) == 0) *reinterpret_cast<uint32_t*>(rec + 2 * cg) = pair;
-      if ((cg & 3) == 0) *reinterpret_cast<uint32_t*>(rec + kVRecSz + cg) = rc.sz;
-      if (t < kSink)
-        *reinterpret_cast<uint4*>(v_sink + ((int64_t)bh * kSink + t) * kD + cg * 8) = w[i];
+      uint8_t* rec = vrec + rm.row(b, h, t) * kVRecBytes;
+      *reinterpret_cast<uint2*>(rec + 8 * g) = make_uint2(gc.lo, gc.hi);
+      *reinterpret_cast<uint32_t*>(rec + kVRecSz + 4 * g) = gc.sz;
+      if (t < kSink) {
+        uint4* dst = reinterpret_cast<uint4*>(v_sink + ((int64_t)bh * kSink + t) * kD + g * 32);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) dst[u] = w[i][u];
+      }
     }
   }
 }

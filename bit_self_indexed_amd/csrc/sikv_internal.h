@@ -98,12 +98,59 @@ __device__ __forceinline__ RowCode encode_row16(const uint4& w, const float (&m)
   return RowCode{v32, s * 0.0078125f, byte};
 }
 
-// 2-bit value code of one bf16 value row held by 16 consecutive lanes (lane cg:
-// channels 8cg..8cg+7 in w; groups of 32 channels = 4 lanes).  Per group: zero
-// point z = min, scale s = fl32((max - z) / 3), both rounded to fp16; code
-// q_c = clamp(rint(fl32(fl32(v_c - z16) / s16)), 0, 3) (0 if s16 = 0).  Returns
-// the lane's 16 code bits (channel 8cg+i at bits 2i) and its group's (scale,
-// zero) fp16 bits as one word.
+// 2-bit values, per group of 32 channels of a bf16 value row: zero point
+// z = min, scale s = fl32((max - z) / 3), both rounded to fp16; code
+// q_c = clamp(rint(fl32(fl32(v_c - z16) / s16)), 0, 3) (0 unless s16 is positive
+// and finite).
+//
+// The code is found without dividing: with d = fl32(v_c - z16) and s = s16 > 0,
+// rint (ties to even) gives q >= 1 iff r = fl32(d / s) > 1/2, q >= 2 iff r >= 3/2
+// and q >= 3 iff r > 5/2.  r reaches a float F iff d / s passes the midpoint
+// between F and the float below it (at the midpoint itself, iff F is even), so
+// the three conditions are d / s > 1/2 + 2^-25, d / s >= 3/2 - 2^-24 and
+// d / s > 5/2 + 2^-23.  Each midpoint times s is exact in fp64 (25 by 11
+// significant bits); the smallest float that satisfies the condition is the
+// group's threshold, and q is the number of thresholds d reaches.  A NaN d
+// reaches none, as a NaN quotient clamps to 0; s16 = 0, inf or NaN makes every
+// threshold NaN.
+__device__ __forceinline__ float vq_next_up(float t) {  // t positive and finite
+  return __uint_as_float(__float_as_uint(t) + 1u);
+}
+__device__ __forceinline__ float vq_least_ge(double p) {  // smallest float >= p > 0
+  const float t = (float)p;
+  return (double)t < p ? vq_next_up(t) : t;
+}
+__device__ __forceinline__ float vq_least_gt(double p) {  // smallest float > p > 0
+  const float t = (float)p;
+  return (double)t <= p ? vq_next_up(t) : t;
+}
+struct VqRule {
+  float zf, t1, t2, t3;
+  uint32_t sz;  // the (scale, zero) fp16 bits as one word
+};
+__device__ __forceinline__ VqRule vq_rule(float lo, float hi) {
+  lo = lo == 0.0f ? 0.0f : lo;  // a zero minimum is stored as +0
+  const __half z16 = __float2half_rn(lo);
+  const __half s16 = __float2half_rn(__fdiv_rn(hi - lo, 3.0f));
+  const float sf = __half2float(s16);
+  const double s64 = (double)sf;
+  const bool ok = sf > 0.0f && sf < INFINITY;
+  VqRule r;
+  r.zf = __half2float(z16);
+  r.t1 = ok ? vq_least_gt((0.5 + 0x1p-25) * s64) : __builtin_nanf("");
+  r.t2 = ok ? vq_least_ge((1.5 - 0x1p-24) * s64) : __builtin_nanf("");
+  r.t3 = ok ? vq_least_gt((2.5 + 0x1p-23) * s64) : __builtin_nanf("");
+  r.sz = (uint32_t)__half_as_ushort(s16) | ((uint32_t)__half_as_ushort(z16) << 16);
+  return r;
+}
+__device__ __forceinline__ uint32_t vq_code(const VqRule& r, float x) {
+  const float d = x - r.zf;
+  return (uint32_t)(d >= r.t1) + (uint32_t)(d >= r.t2) + (uint32_t)(d >= r.t3);
+}
+
+// One value row held by 16 consecutive lanes (lane cg: channels 8cg..8cg+7 in
+// w; a group = 4 lanes): the lane's 16 code bits (channel 8cg+i at bits 2i) and
+// its group's (scale, zero) word.
 struct VRowCode {
   uint32_t bits;
   uint32_t sz;
@@ -121,17 +168,39 @@ __device__ __forceinline__ VRowCode quantize_vrow16(const uint4& w) {
   hi = fmaxf(hi, __shfl_xor(hi, 1));
   lo = fminf(lo, __shfl_xor(lo, 2));
   hi = fmaxf(hi, __shfl_xor(hi, 2));
-  lo = lo == 0.0f ? 0.0f : lo;  // a zero minimum is stored as +0
-  const __half z16 = __float2half_rn(lo);
-  const __half s16 = __float2half_rn(__fdiv_rn(hi - lo, 3.0f));
-  const float zf = __half2float(z16), sf = __half2float(s16);
+  const VqRule r = vq_rule(lo, hi);
   uint32_t bits = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float q = sf > 0.0f ? fminf(fmaxf(rintf(__fdiv_rn(x[i] - zf, sf)), 0.0f), 3.0f) : 0.0f;
-    bits |= (uint32_t)q << (2 * i);
+  for (int i = 0; i < 8; ++i) bits |= vq_code(r, x[i]) << (2 * i);
+  return VRowCode{bits, r.sz};
+}
+
+// One whole group held by one lane (w[u]: channels 8u..8u+7 of the group): its
+// 64 code bits (channel j at bits 2j of lo / hi for j < 16 / j >= 16) and its
+// (scale, zero) word.
+struct VGroupCode {
+  uint32_t lo, hi, sz;
+};
+__device__ __forceinline__ VGroupCode quantize_vgroup32(const uint4 (&w)[4]) {
+  float x[32];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[8 * u + i] = chan(w[u], i);
+  float lo = x[0], hi = x[0];
+#pragma unroll
+  for (int j = 1; j < 32; ++j) {
+    lo = fminf(lo, x[j]);
+    hi = fmaxf(hi, x[j]);
   }
-  return VRowCode{bits, (uint32_t)__half_as_ushort(s16) | ((uint32_t)__half_as_ushort(z16) << 16)};
+  const VqRule r = vq_rule(lo, hi);
+  VGroupCode c{0u, 0u, r.sz};
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    c.lo |= vq_code(r, x[j]) << (2 * j);
+    c.hi |= vq_code(r, x[16 + j]) << (2 * j);
+  }
+  return c;
 }
 
 // Where token t of (batch b, KV head h) lives in the per-token arrays (codes,
@@ -327,7 +396,7 @@ hipError_t launch_mu_final(const float* partial, int BH, int nblk, int n_tokens,
 hipError_t launch_codes(const uint16_t* k, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
                         int t_begin, int t_end, const RowMap& rm, const float* mu, uint8_t* codes,
                         float* alpha, uint16_t* k_sink, uint8_t* vrec, const Launch& s);
-// 2-bit value codes of rows t_begin..t_end-1 (quantize_vrow16) into bytes 0..47 of
+// 2-bit value codes of rows t_begin..t_end-1 (quantize_vgroup32) into bytes 0..47 of
 // their records vrec [B*Hkv][cap][64]; rows below 64 are also copied to v_sink.
 hipError_t launch_vcodes(const uint16_t* v, int64_t sb, int64_t sh, int64_t st, int B, int Hkv,
                          int t_begin, int t_end, const RowMap& rm, uint8_t* vrec,

@@ -190,3 +190,57 @@ def test_every_group_size(G, quant_v):
                 ref = O.sparse_attention(d["q"][b, h * G:(h + 1) * G], sel, o["k_sink"],
                                          o["codes"], o["alpha"], o["mu"], d["V"][b, h], SM, **vkw)
                 check_rows(res[b, h * G:(h + 1) * G], ref, f"G={G} {what} b={b} h={h}")
+
+
+def _midpoint_rows(rng, n_rows):
+    """Value rows whose groups put most entries on or beside the rounding
+    midpoints z16 + (j + 1/2) s16 of their own group (the bf16 values nearest to
+    them and up to two steps either side), over scales from fp16 subnormals to
+    a few thousand; a third of the groups have z = 0 and a power-of-two scale,
+    where the midpoints are exact bf16 values (ties)."""
+    shape = (n_rows, 4)
+    e = rng.integers(-26, 12, size=shape).astype(np.float64)
+    ties = rng.random(shape) < 1 / 3
+    z = np.where(ties, 0.0, rng.normal(size=shape) * 4.0 * 2.0 ** e)
+    mx = np.where(ties, 3.0 * 2.0 ** e, z + rng.uniform(0.3, 3.0, size=shape) * 3.0 * 2.0 ** e)
+    zb = S.bf16_bits_to_f32(S.f32_to_bf16_bits(z.astype(np.float32)))
+    mb = S.bf16_bits_to_f32(S.f32_to_bf16_bits(mx.astype(np.float32)))
+    mb = np.maximum(mb, zb)
+    # the group's stored zero and scale, as the quantiser defines them
+    s = ((mb - zb) / np.float32(3)).astype(np.float32)
+    z16 = zb.astype(np.float16).astype(np.float64)
+    s16 = s.astype(np.float16).astype(np.float64)
+    j = rng.integers(0, 3, size=shape + (30,))
+    mid = z16[..., None] + (j + 0.5) * s16[..., None]
+    mid = np.where(np.isfinite(mid), mid, zb[..., None])
+    b0 = S.f32_to_bf16_bits(mid.astype(np.float32)).astype(np.int32)
+    nb = b0 + rng.integers(-2, 3, size=b0.shape)
+    # a step that would change the sign or leave the finite values (at +-0 or
+    # next to inf) keeps the midpoint itself: the inputs hold no NaN
+    keep = ((nb >> 15) == (b0 >> 15)) & (((nb >> 7) & 0xFF) != 0xFF) & (nb >= 0)
+    bits = np.where(keep, nb, b0).astype(np.uint16)
+    vals = np.clip(S.bf16_bits_to_f32(bits), zb[..., None], mb[..., None])
+    g = np.concatenate([zb[..., None], mb[..., None], vals], axis=-1)  # [rows, 4, 32]
+    perm = rng.permuted(np.broadcast_to(np.arange(32), g.shape), axis=-1)
+    g = np.take_along_axis(g, perm, axis=-1)
+    return S.f32_to_bf16_bits(g.reshape(n_rows, 128).astype(np.float32))
+
+
+def test_value_codes_at_rounding_midpoints():
+    """Value codes and (scale, zero) words bit-exact against the oracle where the
+    rounding decides: entries on and beside the midpoints between code levels,
+    exact ties included, at scales from fp16 subnormals up."""
+    B, Hkv, N = 1, 2, 64 + 6000
+    rng = np.random.default_rng(np.random.SeedSequence([2024, 12, 3]))
+    V = np.stack([_midpoint_rows(rng, N) for _ in range(B * Hkv)]).reshape(B, Hkv, N, 128)
+    K = S.f32_to_bf16_bits(rng.normal(size=(B, Hkv, N, 128)).astype(np.float32))
+    say(f"[qv] case=midpoints B={B} Hkv={Hkv} N={N}")
+    cache = sk.Cache(B, Hkv, N, quant_v=True)
+    sk.sikv_encode(cache, dev_bf16(K))
+    sk.sikv_encode_v(cache, dev_bf16(V))
+    torch.cuda.synchronize()
+    oq, osz = O.quantize_v(V)
+    gq, gsz = _vq_host(cache, N)
+    assert np.array_equal(gsz[:, :, 64:], osz[:, :, 64:]), "scale/zero words differ"
+    bad = np.argwhere(gq[:, :, 64:] != oq[:, :, 64:])
+    assert bad.size == 0, f"value codes differ at {len(bad)} bytes, first {bad[:4].tolist()}"
