@@ -129,7 +129,11 @@ __global__ __launch_bounds__(256) void codes_kernel(const uint16_t* __restrict__
                                                     long long* __restrict__ cb_part) {
   __shared__ unsigned long long cbs[CB ? kSub * 16 * 4 : 1];
   __shared__ int cbn[CB ? kSub * 16 : 1];
-  const int bh = blockIdx.y, b = bh / Hkv, h = bh - b * Hkv;
+  // Blocks walk the keys backwards (last head and tile first): right after the
+  // mean pass, whose last-read rows are the likeliest to still sit in the
+  // memory-side cache.
+  const int bh = gridDim.y - 1 - blockIdx.y, b = bh / Hkv, h = bh - b * Hkv;
+  const int bx = gridDim.x - 1 - blockIdx.x;
   const int tid = threadIdx.x, cg = tid & 15, rs = tid >> 4;
   if (CB) {
     for (int i = tid; i < kSub * 16 * 4; i += 256) cbs[i] = 0ull;
@@ -145,8 +149,8 @@ __global__ __launch_bounds__(256) void codes_kernel(const uint16_t* __restrict__
   }
   const uint16_t* base = k + (int64_t)b * sb + (int64_t)h * sh + cg * 8;
   const int n_tiles = (t_end - t_begin + 127) / 128;
-  const int tile_end = min(n_tiles, (int)(blockIdx.x + 1) * tpb);
-  for (int tile = blockIdx.x * tpb; tile < tile_end; ++tile) {
+  const int tile_end = min(n_tiles, (int)(bx + 1) * tpb);
+  for (int tile = bx * tpb; tile < tile_end; ++tile) {
     const int tb = t_begin + tile * 128;
     uint4 w[8];
 #pragma unroll
@@ -187,7 +191,7 @@ __global__ __launch_bounds__(256) void codes_kernel(const uint16_t* __restrict__
   }
   if (CB) {
     __syncthreads();
-    long long* out = cb_part + ((int64_t)bh * gridDim.x + blockIdx.x) * kCbStride;
+    long long* out = cb_part + ((int64_t)bh * gridDim.x + bx) * kCbStride;
     for (int i = tid; i < kSub * 16 * 4; i += 256) out[i] = (long long)cbs[i];
     for (int i = tid; i < kSub * 16; i += 256) out[kSub * 16 * 4 + i] = cbn[i];
   }
