@@ -211,22 +211,33 @@ __device__ __forceinline__ void process_chunk(Acc<G>& st, const Chunk<G>& x, boo
     cm[i] = half ? h1 : h0;
     co[i] = half ? h0 : h1;
   }
-  float sc[G];
+  // The running maxima are the same in every lane (lane reads), so whether a
+  // chunk raises any of them is a wave-wide branch; one that raises none keeps
+  // the accumulators as they are (its factors would all be exactly 1).
+  float sc[G], mn[G];
+  bool grow = false;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const float mx = ((g & 1) == half) ? cm[g >> 1] : co[g >> 1];
-    const float mn = fmaxf(st.m[g], mx);
-    sc[g] = exp2f(st.m[g] - mn);
-    st.m[g] = mn;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) st.acc[g][i] *= sc[g];
-    if (QV) st.zacc[g] *= sc[g];
+    mn[g] = fmaxf(st.m[g], mx);
+    grow |= mn[g] != st.m[g];
+    sc[g] = 1.0f;
   }
-  if constexpr (kMf) {  // output rows 4 * (lane / 16) + j are head j of a channel group
+  if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb)
+    for (int g = 0; g < G; ++g) {
+      sc[g] = exp2f(st.m[g] - mn[g]);
+      st.m[g] = mn[g];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) st.d[nb][j] *= j < G ? sc[j] : 0.0f;
+      for (int i = 0; i < 8; ++i) st.acc[g][i] *= sc[g];
+      if (QV) st.zacc[g] *= sc[g];
+    }
+    if constexpr (kMf) {  // output rows 4 * (lane / 16) + j are head j of a channel group
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) st.d[nb][j] *= j < G ? sc[j] : 0.0f;
+    }
   }
 #pragma unroll
   for (int i = 0; i < GH; ++i) {
