@@ -156,6 +156,13 @@ RowMap rows_of(const sikv_cache_desc* c) {
   return m;
 }
 
+// Rows the attention can address from its per-head bases: a head's capacity
+// (contiguous), or the whole pool (paged: its rows are pool rows).
+int64_t attn_rows(const sikv_cache_desc* c) {
+  return c->page_table != nullptr ? (int64_t)c->n_pages * c->n_kv_heads * c->page_size
+                                  : c->capacity;
+}
+
 sikv_status check_desc(const sikv_cache_desc* c) {
   if (c == nullptr) return SIKV_ERR_INVALID_ARG;
   if (c->head_dim != kD || c->n_sink != kSink) return SIKV_ERR_UNSUPPORTED;
@@ -305,7 +312,8 @@ sikv_status run_attn(const sikv_cache_desc* c, const uint16_t* q, int n_q_heads,
   }
   SIKV_TRY(launch_attn(n_q_heads, c->batch, c->n_kv_heads, c->codes, c->alpha, c->v,
                        c->v_stride_b, c->v_stride_h, c->v_stride_t, c->vrec, c->v_sink,
-                       rows_of(c), c->n_tokens, c->seq_lens, idx, top_k, tab->lut, tab->qmu, tab->slog, sm_scale, ap.cpb, ap.n_splits, po,
+                       rows_of(c), attn_rows(c), c->n_tokens, c->seq_lens, idx, top_k, tab->lut,
+                       tab->qmu, tab->slog, sm_scale, ap.cpb, ap.n_splits, po,
                        pml, s));
   SIKV_TRY(launch_combine(po, pml, c->batch * n_q_heads, ap.n_splits, out, s));
   return SIKV_OK;

@@ -91,7 +91,18 @@ struct Src {
   int64_t vst;
   const uint8_t* vrec;    // quantised values: the head's 64-byte value records
   const uint16_t* vsk;
+  const char* vbase;      // bf16 V rows without the lane's column offset
+  uint32_t vstb, vlane;   // row stride and the lane's column offset, in bytes
 };
+
+// A load at a 32-bit byte offset from a block-uniform base: one scalar base
+// plus one VGPR per load, where a 64-bit row times stride product costs four
+// multiplies.  Used when every row the kernel can address lies within 2^24
+// rows and 4 GiB of its base (checked on the host).
+template <typename T>
+__device__ __forceinline__ T ld32(const void* base, uint32_t off) {
+  return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + off);
+}
 
 // Registers of one chunk for one lane: the logit inputs of entry (lane & 31)
 // and the V data of the 16-lane group's 8 rows (entries grp, grp+4, ...).
@@ -109,7 +120,7 @@ struct Chunk {
 // block's entries, relative to the Src bases (entries past the list end repeat
 // its last), so every address is a real row.  A sink chunk reads the sink
 // logits (and, quantised, the bf16 sink rows) by entry index instead.
-template <int G, bool QV>
+template <int G, bool QV, bool kO32>
 __device__ __forceinline__ void load_chunk(Chunk<G>& x, int c, int lc, bool sink,
                                            const int* sidx, int lane, const Src& src) {
   const int el = lane & 31, half = lane >> 5, grp = lane >> 4, seg = lane & 15;
@@ -123,9 +134,16 @@ __device__ __forceinline__ void load_chunk(Chunk<G>& x, int c, int lc, bool sink
   } else {
     // quantised values: the key code copy in the token's value record, which the
     // V loads below fetch anyway
-    x.code = QV ? *reinterpret_cast<const uint4*>(src.vrec + (int64_t)t * kVRecBytes + kVRecCode)
-                : *reinterpret_cast<const uint4*>(src.codes + (int64_t)t * kCodeBytes);
-    x.a = src.alpha[t];
+    if constexpr (kO32) {
+      const uint32_t ut = (uint32_t)t;
+      x.code = QV ? ld32<uint4>(src.vrec, ut * kVRecBytes + kVRecCode)
+                  : ld32<uint4>(src.codes, ut * kCodeBytes);
+      x.a = ld32<float>(src.alpha, ut * 4u);
+    } else {
+      x.code = QV ? *reinterpret_cast<const uint4*>(src.vrec + (int64_t)t * kVRecBytes + kVRecCode)
+                  : *reinterpret_cast<const uint4*>(src.codes + (int64_t)t * kCodeBytes);
+      x.a = src.alpha[t];
+    }
 #pragma unroll
     for (int i = 0; i < (G + 1) / 2; ++i) x.sl[i] = 0.0f;
   }
@@ -133,13 +151,22 @@ __device__ __forceinline__ void load_chunk(Chunk<G>& x, int c, int lc, bool sink
   for (int u = 0; u < kRows; ++u) {
     const int tu = sidx[lc * kAttnChunk + grp + 4 * u];
     if (!QV) {
-      x.v[u] = *reinterpret_cast<const uint4*>(src.vb + (int64_t)tu * src.vst);
+      if constexpr (kO32)
+        x.v[u] = ld32<uint4>(src.vbase, __umul24((uint32_t)tu, src.vstb) + src.vlane);
+      else
+        x.v[u] = *reinterpret_cast<const uint4*>(src.vb + (int64_t)tu * src.vst);
     } else if (sink) {
       x.v[u] = *reinterpret_cast<const uint4*>(src.vsk + (int64_t)(c * kAttnChunk + grp + 4 * u) * kD);
     } else {
-      const uint8_t* rec = src.vrec + (int64_t)tu * kVRecBytes;
-      x.v[u].x = *reinterpret_cast<const uint16_t*>(rec + 2 * seg);
-      x.v[u].y = *reinterpret_cast<const uint32_t*>(rec + kVRecSz + 4 * (seg >> 2));
+      if constexpr (kO32) {
+        const uint32_t r = (uint32_t)tu * kVRecBytes;
+        x.v[u].x = ld32<uint16_t>(src.vrec, r + 2 * seg);
+        x.v[u].y = ld32<uint32_t>(src.vrec, r + kVRecSz + 4 * (seg >> 2));
+      } else {
+        const uint8_t* rec = src.vrec + (int64_t)tu * kVRecBytes;
+        x.v[u].x = *reinterpret_cast<const uint16_t*>(rec + 2 * seg);
+        x.v[u].y = *reinterpret_cast<const uint32_t*>(rec + kVRecSz + 4 * (seg >> 2));
+      }
       x.v[u].z = 0u;
       x.v[u].w = 0u;
     }
@@ -339,7 +366,7 @@ __device__ __forceinline__ void process_chunk(Acc<G>& st, const Chunk<G>& x, boo
   wave_sync_lds();
 }
 
-template <int G, bool QV>
+template <int G, bool QV, bool kO32>
 __global__ __launch_bounds__(256, 2) void attn_kernel(
     int n_q_heads, int Hkv, const uint8_t* __restrict__ codes, const float* __restrict__ alpha,
     const uint16_t* __restrict__ v, int64_t vsb, int64_t vsh, int64_t vst,
@@ -378,6 +405,10 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(
   src.slog = att_slog + hq0 * kSink;
   src.vb = QV ? nullptr : (paged ? v : v + (int64_t)b * vsb + (int64_t)h * vsh) + seg * 8;
   src.vst = vst;
+  src.vbase = QV ? nullptr
+                 : reinterpret_cast<const char*>(paged ? v : v + (int64_t)b * vsb + (int64_t)h * vsh);
+  src.vstb = (uint32_t)(vst * 2);
+  src.vlane = (uint32_t)seg * 16u;
   src.vrec = QV ? vrec + row0 * kVRecBytes : nullptr;
   src.vsk = QV ? vsink + (int64_t)bh * kSink * kD + seg * 8 : nullptr;
 
@@ -452,17 +483,17 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(
   int c = c0 + wave;
   if (c < c_end && c * kAttnChunk < kSink) {
     Chunk<G> sk;
-    load_chunk<G, QV>(sk, c, c - c0, true, sidx, lane, src);
+    load_chunk<G, QV, kO32>(sk, c, c - c0, true, sidx, lane, src);
     process_chunk<G, QV>(st, sk, true, true, lutq, qmu, sm_log2, pb[wave], mfw, lane);
     c += 4;
   }
   if (c < c_end) {
     const int c_last = c + ((c_end - 1 - c) & ~3);
     Chunk<G> nx;
-    load_chunk<G, QV>(nx, c, c - c0, false, sidx, lane, src);
+    load_chunk<G, QV, kO32>(nx, c, c - c0, false, sidx, lane, src);
     for (; c < c_last; c += 4) {
       const Chunk<G> cur = nx;
-      load_chunk<G, QV>(nx, c + 4, c + 4 - c0, false, sidx, lane, src);
+      load_chunk<G, QV, kO32>(nx, c + 4, c + 4 - c0, false, sidx, lane, src);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the chunk's work
       process_chunk<G, QV>(st, cur, false, c * kAttnChunk + el < L, lutq, qmu, sm_log2, pb[wave],
                            mfw, lane);
@@ -619,8 +650,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 hipError_t launch_attn(int n_q_heads, int B, int Hkv, const uint8_t* codes, const float* alpha,
                        const uint16_t* v, int64_t vsb, int64_t vsh, int64_t vst,
                        const uint8_t* vrec, const uint16_t* vsink, const RowMap& rm,
-                       int n_tokens, const int32_t* seq_lens, const int32_t* idx, int top_k,
-                       const float* att_lut,
+                       int64_t n_rows, int n_tokens, const int32_t* seq_lens,
+                       const int32_t* idx, int top_k, const float* att_lut,
                        const float* att_qmu, const float* att_slog, float sm_scale,
                        int chunks_per_block, int n_splits, float* part_o, float* part_ml,
                        const Launch& s) {
@@ -631,19 +662,23 @@ hipError_t launch_attn(int n_q_heads, int B, int Hkv, const uint8_t* codes, cons
     return hipErrorInvalidValue;
   const float sm_log2 = sm_scale * 1.4426950408889634f;
   const dim3 grid(n_splits, B * Hkv), block(256);
+  // 32-bit offsets: rows below 2^24 (the 24-bit multiply), and for bf16 values
+  // a row stride below 2^24 bytes with the last row's end within 4 GiB
+  const int64_t kRowLim = int64_t(1) << 24;
+  const bool o32 = n_rows > 0 && n_rows <= kRowLim &&
+                   (vrec != nullptr || (vst > 0 && 2 * vst < kRowLim &&
+                                        n_rows * 2 * vst <= (int64_t(1) << 32) - 256));
+#define SIKV_ATTN_ARGS                                                                         \
+  grid, block, 0, s, n_q_heads, Hkv, codes, alpha, v, vsb, vsh, vst, vrec, vsink, rm, n_tokens,  \
+      seq_lens, idx, top_k, att_lut, att_qmu, att_slog, sm_log2, chunks_per_block, n_splits,   \
+      part_o, part_ml
 #define SIKV_ATTN_CASE(GG)                                                                     \
   case GG:                                                                                     \
     if (vrec != nullptr)                                                                       \
-      return launch_k(KID_ATTN, attn_kernel<GG, true>, grid, block, 0, s, n_q_heads, Hkv,      \
-                      codes, alpha, v, vsb, vsh, vst, vrec, vsink, rm, n_tokens,                \
-                      seq_lens, idx,                                                           \
-                      top_k, att_lut, att_qmu, att_slog, sm_log2, chunks_per_block, n_splits,  \
-                      part_o, part_ml);                                                        \
-    return launch_k(KID_ATTN, attn_kernel<GG, false>, grid, block, 0, s, n_q_heads, Hkv,       \
-                    codes, alpha, v, vsb, vsh, vst, vrec, vsink, rm, n_tokens,                \
-                    seq_lens, idx,                                                             \
-                    top_k, att_lut, att_qmu, att_slog, sm_log2, chunks_per_block, n_splits,    \
-                    part_o, part_ml);
+      return o32 ? launch_k(KID_ATTN, attn_kernel<GG, true, true>, SIKV_ATTN_ARGS)             \
+                 : launch_k(KID_ATTN, attn_kernel<GG, true, false>, SIKV_ATTN_ARGS);           \
+    return o32 ? launch_k(KID_ATTN, attn_kernel<GG, false, true>, SIKV_ATTN_ARGS)              \
+               : launch_k(KID_ATTN, attn_kernel<GG, false, false>, SIKV_ATTN_ARGS);
   switch (n_q_heads / Hkv) {
     SIKV_ATTN_CASE(1)
     SIKV_ATTN_CASE(2)
@@ -657,6 +692,7 @@ hipError_t launch_attn(int n_q_heads, int B, int Hkv, const uint8_t* codes, cons
       return hipErrorInvalidValue;
   }
 #undef SIKV_ATTN_CASE
+#undef SIKV_ATTN_ARGS
 }
 
 hipError_t launch_combine(const float* part_o, const float* part_ml, int BHq, int n_splits,

@@ -507,8 +507,8 @@ constexpr int kAttnMaxCpb = 64;  // chunks per block at most (the block's positi
 hipError_t launch_attn(int n_q_heads, int B, int Hkv, const uint8_t* codes, const float* alpha,
                        const uint16_t* v, int64_t vsb, int64_t vsh, int64_t vst,
                        const uint8_t* vrec, const uint16_t* vsink, const RowMap& rm,
-                       int n_tokens, const int32_t* seq_lens, const int32_t* idx, int top_k,
-                       const float* att_lut,
+                       int64_t n_rows, int n_tokens, const int32_t* seq_lens,
+                       const int32_t* idx, int top_k, const float* att_lut,
                        const float* att_qmu, const float* att_slog, float sm_scale,
                        int chunks_per_block, int n_splits, float* part_o, float* part_ml,
                        const Launch& s);

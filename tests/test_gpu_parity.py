@@ -166,6 +166,40 @@ def test_append_and_strided_inputs():
             check_rows(out[b, h * G:(h + 1) * G], ref, f"append attn b={b} h={h}")
 
 
+
+def test_value_rows_beyond_32bit_offsets():
+    """V rows 16 MB apart (a row stride too wide for the attention's 32-bit
+    offsets): the kernels' 64-bit addressing form, against the oracle and
+    bit-identical to the same values in a compact layout."""
+    w = S.custom("wide_v", 1, 8, 2, 160, 64, n_planted=4, cfg_id=111)
+    say(f"[parity] case=wide_value_stride N={w.n_tokens}")
+    d = S.draw(w)
+    N, G = w.n_tokens, w.group
+    vst = (1 << 23) + 128                       # elements: 2 * vst bytes >= 2^24
+    buf = torch.empty(N * vst, dtype=torch.bfloat16, device="cuda")  # ~2.7 GB
+    Vwide = buf.as_strided((1, w.n_kv_heads, N, 128), (N * vst, 128, vst, 1))
+    V = dev_bf16(d["V"])
+    Vwide.copy_(V)
+    K, q = dev_bf16(d["K"]), dev_bf16(d["q"])
+    outs, idxs = [], []
+    for vv in (Vwide, V):
+        cache = sk.Cache(w.batch, w.n_kv_heads, N, v=vv)
+        sk.sikv_encode(cache, K)
+        idx_out = torch.empty((w.batch, w.n_kv_heads, w.top_k), dtype=torch.int32, device="cuda")
+        outs.append(sk.sikv_decode_step(cache, q, w.top_k, SM, idx_out=idx_out).cpu().numpy())
+        idxs.append(idx_out.cpu().numpy())
+        torch.cuda.synchronize()
+    del buf, Vwide
+    assert np.array_equal(idxs[0], idxs[1])
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    for h in range(w.n_kv_heads):
+        pre = oracle_head(d["K"][0, h], N)
+        s = oracle_scores(d["q"], pre["codes"], pre["alpha"], 0, h, w.n_kv_heads, N)
+        check_topk(idxs[0][0, h], s, w.top_k, N, f"wide_v h={h}")
+        ref = O.sparse_attention(d["q"][0, h * G:(h + 1) * G], idxs[0][0, h], pre["k_sink"],
+                                 pre["codes"], pre["alpha"], pre["mu"], d["V"][0, h], SM)
+        check_rows(outs[0][0, h * G:(h + 1) * G], ref, f"wide_v attn h={h}")
+
 CB_CASES = [
     ("cb_tiny_4k", None),
     ("cb_g5_multi_tile", S.custom("cb_g5", 2, 10, 2, 20123, 1500, n_planted=16, cfg_id=130)),
