@@ -80,6 +80,34 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Logit tables of a pair of query heads (2i, 2i + 1), interleaved: entry e of
+// head 2i + par at float 2e + par, so sub-vector j's 16 entries span 128 bytes.
+// The two halves of a wave serve the two heads of a pair: a lane's offset into
+// the pair table (par * 4 bytes) is set into the nibbles' byte offsets
+// (nibble * 8) by the same and-or that masks them, and each look-up's address
+// is then one byte extract with the rest an immediate offset.  Same look-ups
+// and the same order of additions as lut_word / lut_dot.
+__device__ __forceinline__ float lut_word_pair(const float* __restrict__ lutw, uint32_t d,
+                                               uint32_t par4) {
+  const uint32_t e = ((d << 3) & 0x78787878u) | par4;
+  const uint32_t o = ((d >> 1) & 0x78787878u) | par4;
+  const char* L = reinterpret_cast<const char*>(lutw);
+  float a = *reinterpret_cast<const float*>(L + 0 * 128 + byte_of(e, 0));
+  float c = *reinterpret_cast<const float*>(L + 1 * 128 + byte_of(o, 0));
+  a += *reinterpret_cast<const float*>(L + 2 * 128 + byte_of(e, 1));
+  c += *reinterpret_cast<const float*>(L + 3 * 128 + byte_of(o, 1));
+  a += *reinterpret_cast<const float*>(L + 4 * 128 + byte_of(e, 2));
+  c += *reinterpret_cast<const float*>(L + 5 * 128 + byte_of(o, 2));
+  a += *reinterpret_cast<const float*>(L + 6 * 128 + byte_of(e, 3));
+  c += *reinterpret_cast<const float*>(L + 7 * 128 + byte_of(o, 3));
+  return a + c;
+}
+__device__ __forceinline__ float lut_dot_pair(const float* __restrict__ lutp, uint4 c,
+                                              uint32_t par4) {
+  return (lut_word_pair(lutp, c.x, par4) + lut_word_pair(lutp + 256, c.y, par4)) +
+         (lut_word_pair(lutp + 512, c.z, par4) + lut_word_pair(lutp + 768, c.w, par4));
+}
+
 // Where a lane finds its inputs: codes / scales of the head, bf16 V at this
 // lane's channels (row stride vst), or (quantised values) the head's 2-bit
 // codes (32 B per token), (scale, zero) words (4 per token) and bf16 sink rows.
@@ -182,7 +210,7 @@ struct Acc {
 
 template <int G, bool QV>
 __device__ __forceinline__ void process_chunk(Acc<G>& st, const Chunk<G>& x, bool sink, bool live,
-                                              const float (*lutq)[kLut], const float* qmu,
+                                              const float (*lutp)[2 * kLut], const float* qmu,
                                               float sm_log2, float (*pbw)[G], MfLds* mf,
                                               int lane) {
   constexpr int GH = (G + 1) / 2;
@@ -219,12 +247,13 @@ __device__ __forceinline__ void process_chunk(Acc<G>& st, const Chunk<G>& x, boo
       }
     }
   }
-  // logits (log2 domain) of this lane's heads g = 2i + half
+  // logits (log2 domain) of this lane's heads g = 2i + half (with G odd, the
+  // last pair's second slot is a zero table whose logits are masked)
   float lg[GH];
+  const uint32_t par4 = half ? 0x04040404u : 0u;
 #pragma unroll
   for (int i = 0; i < GH; ++i) {
-    const int g = min(2 * i + half, G - 1);
-    const float dot = sink ? x.sl[i] : fmaf(x.a, lut_dot(lutq[g], x.code), qmu[i]);
+    const float dot = sink ? x.sl[i] : fmaf(x.a, lut_dot_pair(lutp[i], x.code, par4), qmu[i]);
     lg[i] = (live && 2 * i + half < G) ? dot * sm_log2 : -INFINITY;
   }
   // chunk max per head: heads of parity `half` live in this half of the wave
@@ -377,7 +406,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(
     const float* __restrict__ att_qmu, const float* __restrict__ att_slog, float sm_log2,
     int cpb, int n_splits, float* __restrict__ part_o, float* __restrict__ part_ml) {
   constexpr int GH = (G + 1) / 2;
-  __shared__ float lutq[G][kLut];
+  __shared__ float lutp[GH][2 * kLut];  // head pairs, interleaved (lut_word_pair)
   __shared__ int sidx[kAttnMaxCpb * kAttnChunk];
   __shared__ __align__(16) float pb[4][kAttnChunk][G];
   __shared__ float mo[4][G][kD];
@@ -436,10 +465,20 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(
 #pragma unroll
     for (int i = 0; i < GH; ++i) qmu[i] = (2 * i + half < G) ? att_qmu[hq0 + 2 * i + half] : 0.0f;
     __builtin_amdgcn_sched_barrier(0);  // all of the round's loads are out
-    float4* dst = reinterpret_cast<float4*>(&lutq[0][0]);
 #pragma unroll
-    for (int u = 0; u < kLutPer; ++u)  // (threads past the end rewrite the last entry's value)
-      dst[min(tid + 256 * u, G * kLut / 4 - 1)] = lv[u];
+    for (int u = 0; u < kLutPer; ++u) {  // (threads past the end rewrite the last entries)
+      const int f = min(tid + 256 * u, G * kLut / 4 - 1);  // float4 f: head g, entries 4r..
+      const int g = f / (kLut / 4), r = f - g * (kLut / 4);
+      float* d = &lutp[g >> 1][8 * r + (g & 1)];
+      d[0] = lv[u].x;
+      d[2] = lv[u].y;
+      d[4] = lv[u].z;
+      d[6] = lv[u].w;
+    }
+    if constexpr (G & 1) {  // the last pair's second slot
+#pragma unroll
+      for (int e = tid; e < kLut; e += 256) lutp[GH - 1][2 * e + 1] = 0.0f;
+    }
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int e = min(e0 + tid + 256 * u, L - 1);
@@ -484,7 +523,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(
   if (c < c_end && c * kAttnChunk < kSink) {
     Chunk<G> sk;
     load_chunk<G, QV, kO32>(sk, c, c - c0, true, sidx, lane, src);
-    process_chunk<G, QV>(st, sk, true, true, lutq, qmu, sm_log2, pb[wave], mfw, lane);
+    process_chunk<G, QV>(st, sk, true, true, lutp, qmu, sm_log2, pb[wave], mfw, lane);
     c += 4;
   }
   if (c < c_end) {
@@ -495,10 +534,10 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(
       const Chunk<G> cur = nx;
       load_chunk<G, QV, kO32>(nx, c + 4, c + 4 - c0, false, sidx, lane, src);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the chunk's work
-      process_chunk<G, QV>(st, cur, false, c * kAttnChunk + el < L, lutq, qmu, sm_log2, pb[wave],
+      process_chunk<G, QV>(st, cur, false, c * kAttnChunk + el < L, lutp, qmu, sm_log2, pb[wave],
                            mfw, lane);
     }
-    process_chunk<G, QV>(st, nx, false, c * kAttnChunk + el < L, lutq, qmu, sm_log2, pb[wave],
+    process_chunk<G, QV>(st, nx, false, c * kAttnChunk + el < L, lutp, qmu, sm_log2, pb[wave],
                          mfw, lane);
   }
 
