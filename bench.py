@@ -166,8 +166,8 @@ def short_kernel_name(name: str) -> str:
 def library_kernel(name: str):
     short = short_kernel_name(name)
     base = short.split("<")[0]
-    if base == "attn_kernel" and ", true>" in short:  # the 2-bit-value variant
-        return "attn_qv"
+    if base == "attn_kernel":  # attn_kernel<G, 2-bit values?, 32-bit offsets?>
+        return "attn_qv" if short.split(",")[1].strip() == "true" else "attn"
     return base[:-len("_kernel")] if base.endswith("_kernel") and base[:-len("_kernel")] in KERNEL_SOURCES else None
 
 
