@@ -24,12 +24,13 @@
 // The block first copies its slice of the position list into LDS (one round
 // trip), so a wave can issue all loads of its next chunk (codes, scales and V
 // rows) right after the current chunk's have arrived, before computing it.
-// Measured on the 128K shape (random positions, 8 rotating layers): ~25 us per
-// block of 5 chunks per wave; contiguous positions take ~8 us less and a
+// Measured on the 128K shape (random positions, 8 rotating layers): ~25 us for
+// blocks of 10 chunks per wave; contiguous positions take ~8 us less and a
 // single resident layer another ~5 us less, so the time is set by the random
-// gathers themselves (DRAM pages, translation), with the VALU work (~750
-// instructions per chunk, two waves per SIMD) as the floor underneath.  The
-// combine kernel then merges the blocks' partials.
+// gathers themselves (DRAM pages, translation); without the P.V arithmetic or
+// without the logit look-ups (timing-only builds) it is ~1.5 us shorter each,
+// and fewer, longer-lived blocks are slower by ~1.7 us per extra chunk per
+// wave.  The combine kernel then merges the blocks' partials.
 // (A last-block-merges variant needs device-scope fences, which on gfx950 write
 // back and invalidate the whole L2 of the XCD in every block: far slower than
 // one more launch.)
