@@ -27,13 +27,17 @@ def _pool_gather(pool, table, B):
     return torch.stack(out)
 
 
-def _caches(w, d, quant_v, codebook, seed):
+def _caches(w, d, quant_v, codebook, seed, n_pages=None):
     B, Hkv = w.batch, w.n_kv_heads
     pps = (w.n_tokens + 16 + P - 1) // P
     cap = pps * P
-    n_pages = B * pps + 5
-    rng = np.random.default_rng(seed)
-    perm = rng.permutation(n_pages)[:B * pps].reshape(B, pps)
+    if n_pages is None:
+        n_pages = B * pps + 5
+        rng = np.random.default_rng(seed)
+        perm = rng.permutation(n_pages)[:B * pps].reshape(B, pps)
+    else:  # a large pool: the sequences' pages shuffled among its last ones
+        rng = np.random.default_rng(seed)
+        perm = (n_pages - 1 - rng.permutation(B * pps)).reshape(B, pps)
     table = torch.tensor(perm, dtype=torch.int32, device="cuda")
     Vc = torch.zeros((B, Hkv, cap, 128), dtype=torch.bfloat16, device="cuda")
     Vc[:, :, :w.n_tokens] = dev_bf16(d["V"])
@@ -113,3 +117,32 @@ def test_paged_ragged_and_kmeans():
         res.append((idx.cpu(), out.cpu(), c.codebook.cpu()))
     for a, b, what in zip(res[0], res[1], ("idx", "out", "K-means codebook")):
         assert torch.equal(a, b), what
+
+
+@pytest.mark.parametrize("quant_v", [False, True], ids=["bf16_v", "2bit_v"])
+def test_pool_beyond_32bit_offsets(quant_v):
+    """A pool of more than 2^24 rows (33000 pages of 2 heads x 256 tokens), the
+    sequences in its last pages: the attention's 64-bit addressing form, which
+    must give the contiguous cache's results bit for bit."""
+    w = S.custom("big_pool", 2, 8, 2, 3000, 200, n_planted=8, cfg_id=194)
+    n_pages = 33000  # rows 33000 * 2 * 256 > 2^24
+    say(f"[paged] pool of {n_pages} pages, quant_v={quant_v}")
+    d = S.draw(w)
+    N = w.n_tokens
+    cont, paged, perm, Vc = _caches(w, d, quant_v, False, 195, n_pages=n_pages)
+    assert int(perm.min()) * w.n_kv_heads * P >= 1 << 24
+    K, q = dev_bf16(d["K"]), dev_bf16(d["q"])
+    res = []
+    for c in (cont, paged):
+        sk.sikv_encode(c, K[:, :, :N - 1])
+        if quant_v:
+            sk.sikv_encode_v(c, Vc[:, :, :N - 1])
+        idx = torch.empty((w.batch, w.n_kv_heads, w.top_k), dtype=torch.int32, device="cuda")
+        c.n_tokens = N - 1
+        out = sk.sikv_append_decode_step(c, K[:, :, N - 1:N], q, w.top_k, SM, idx_out=idx,
+                                         v_new=Vc[:, :, N - 1:N] if quant_v else None)
+        torch.cuda.synchronize()
+        res.append((idx.cpu(), out.cpu()))
+    del paged
+    assert torch.equal(res[0][0], res[1][0]), "idx"
+    assert torch.equal(res[0][1], res[1][1]), "out"
